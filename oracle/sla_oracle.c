@@ -1,0 +1,214 @@
+/*
+ * sla_oracle.c -- plain, slow, sequential CPU oracle for the sparse CG solve and
+ * its adjoint backward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  The product path (the HIP library and
+ * its Python binding) never calls it and shares no code with it.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC (see oracle/build.py).
+ * Contraction is off so every product is rounded before it is added: the row
+ * sums and dot products below are plain sequential fp64 sums in ascending index
+ * order, with no fused multiply-add.
+ *
+ * Sources (torch-sla: Differentiable Sparse Linear Algebra with Adjoint Solvers
+ * and Sparse Tensor Parallelism for PyTorch):
+ *   - CG (Hestenes and Stiefel) as the pytorch-native iterative backend:
+ *     paperpeel page, section 1 "Introduction" and section 3.1 "Five backends
+ *     and auto-dispatch"; one SpMV and the inner products <r,r>, <p,Ap> per
+ *     iteration: section 3.3 "Distributed Krylov solvers".
+ *   - Linear adjoint: for A x = b the backward pass solves A^T lambda = dL/dx and
+ *     the matrix gradient is -lambda_i x_j on the sparsity pattern only:
+ *     gist.science Hindi and Japanese summaries, Methodology item 2
+ *     ("Adjoint Differentiation Framework"), linear-systems bullet.
+ *     dL/db = lambda follows from x = A^{-1} b (implicit function theorem,
+ *     paperpeel section 3.2 "Adjoint Differentiation Framework").
+ *   - Stopping tests, breakdown and iteration counting are not printed on the
+ *     pages; the readings used here are listed with the parity tests.
+ *
+ * Parity pins (see tests/test_oracle_pins.py): dense LU solves on small grids,
+ * the closed-form eigenpairs of the 5-point Laplacian, manufactured solutions,
+ * one-iteration convergence on an eigenvector, homogeneity invariants of the
+ * gradients, central finite differences, scipy.sparse products and transposes,
+ * and exact rational solutions of a 2 x 2 grid (tests/golden).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Per-system outcome codes; the HIP library uses the same numbers. */
+enum { ORC_CONVERGED = 0, ORC_MAX_ITER = 1, ORC_NOT_SPD = 2, ORC_NAN = 3 };
+
+/* y = A x, one row at a time; row i sums val[k] * x[col[k]] for k ascending. */
+void orc_spmv(int64_t n_rows, const int64_t* row_ptr, const int32_t* col,
+              const double* val, const double* x, double* y)
+{
+    for (int64_t i = 0; i < n_rows; ++i) {
+        double s = 0.0;
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+            double t = val[k] * x[col[k]];
+            s = s + t;
+        }
+        y[i] = s;
+    }
+}
+
+/* y = A^T x by scattering each row: y[col[k]] += val[k] * x[i], rows ascending. */
+void orc_spmv_transposed(int64_t n_rows, int64_t n_cols, const int64_t* row_ptr,
+                         const int32_t* col, const double* val, const double* x, double* y)
+{
+    for (int64_t j = 0; j < n_cols; ++j) y[j] = 0.0;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+            double t = val[k] * x[i];
+            y[col[k]] = y[col[k]] + t;
+        }
+    }
+}
+
+double orc_dot(int64_t n, const double* a, const double* b)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double t = a[i] * b[i];
+        s = s + t;
+    }
+    return s;
+}
+
+/*
+ * Conjugate gradients for A x = b with x0 = 0, no preconditioner.
+ *
+ *   r = b, p = r, rho = <r,r>, threshold = max(rtol * |b|, atol)
+ *   repeat:  q = A p;  sigma = <p,q>;  alpha = rho / sigma
+ *            x = x + alpha p;  r = r - alpha q;  rho' = <r,r>
+ *            stop when |r| <= threshold (|r| from the recurrence, no extra SpMV)
+ *            beta = rho' / rho;  p = r + beta p
+ *
+ * The iteration count is the number of products A p (b = 0 stops at 0).
+ * sigma <= 0 stops with NOT_SPD, a NaN sigma with NAN; x is left as it was
+ * before that iteration.  max_iter reached: MAX_ITER with the last x.  With
+ * fixed != 0 the residual test is skipped and exactly max_iter iterations run
+ * (unless a breakdown stops them first).
+ *
+ * work: 3 * n doubles (r, p, q).  hist (nullable, max_iter + 1 entries) receives
+ * |r_k| for k = 0 .. iterations.
+ */
+int orc_cg(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
+           const double* b, double* x, double rtol, double atol, int64_t max_iter,
+           int fixed, double* work, int64_t* iters_out, double* res_out,
+           double* rhs_out, double* hist)
+{
+    double* r = work;
+    double* p = work + n;
+    double* q = work + 2 * n;
+    for (int64_t i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; p[i] = b[i]; }
+    double rho = orc_dot(n, r, r);
+    double bnorm = sqrt(rho);
+    double thr = rtol * bnorm;
+    if (atol > thr) thr = atol;
+    *rhs_out = bnorm;
+    if (hist) hist[0] = bnorm;
+    int64_t k = 0;
+    int state = ORC_MAX_ITER;
+    if (!fixed && sqrt(rho) <= thr) { state = ORC_CONVERGED; goto done; }
+    while (k < max_iter) {
+        orc_spmv(n, row_ptr, col, val, p, q);
+        double sigma = orc_dot(n, p, q);
+        if (!(sigma > 0.0)) { state = (sigma != sigma) ? ORC_NAN : ORC_NOT_SPD; goto done; }
+        double alpha = rho / sigma;
+        for (int64_t i = 0; i < n; ++i) {
+            double t = alpha * p[i];
+            x[i] = x[i] + t;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            double t = alpha * q[i];
+            r[i] = r[i] - t;
+        }
+        double rho1 = orc_dot(n, r, r);
+        k = k + 1;
+        if (hist) hist[k] = sqrt(rho1);
+        if (!fixed && sqrt(rho1) <= thr) { rho = rho1; state = ORC_CONVERGED; goto done; }
+        double beta = rho1 / rho;
+        for (int64_t i = 0; i < n; ++i) {
+            double t = beta * p[i];
+            p[i] = r[i] + t;
+        }
+        rho = rho1;
+    }
+done:
+    *iters_out = k;
+    *res_out = sqrt(rho);
+    return state;
+}
+
+/*
+ * Transpose of an n_rows x n_cols CSR pattern by a stable counting sort on the
+ * column index.  Row j of A^T lists the entries of column j of A in ascending
+ * row order; perm[kT] is the position in A of entry kT of A^T, so
+ * valT[kT] = val[perm[kT]].  row_ptr_t has n_cols + 1 entries.
+ */
+void orc_transpose(int64_t n_rows, int64_t n_cols, const int64_t* row_ptr, const int32_t* col,
+                   int64_t* row_ptr_t, int32_t* col_t, int64_t* perm)
+{
+    int64_t nnz = row_ptr[n_rows];
+    for (int64_t j = 0; j <= n_cols; ++j) row_ptr_t[j] = 0;
+    for (int64_t k = 0; k < nnz; ++k) row_ptr_t[col[k] + 1] += 1;
+    for (int64_t j = 0; j < n_cols; ++j) row_ptr_t[j + 1] += row_ptr_t[j];
+    int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_cols > 0 ? n_cols : 1));
+    for (int64_t j = 0; j < n_cols; ++j) next[j] = row_ptr_t[j];
+    for (int64_t i = 0; i < n_rows; ++i) {
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+            int64_t dst = next[col[k]]++;
+            col_t[dst] = (int32_t)i;
+            perm[dst] = k;
+        }
+    }
+    free(next);
+}
+
+/* gvals[k] = sign * u[row(k)] * v[col(k)] for every stored entry k. */
+void orc_pattern_outer(int64_t n_rows, const int64_t* row_ptr, const int32_t* col,
+                       double sign, const double* u, const double* v, double* gvals)
+{
+    for (int64_t i = 0; i < n_rows; ++i) {
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+            double t = u[i] * v[col[k]];
+            gvals[k] = sign * t;
+        }
+    }
+}
+
+/*
+ * Adjoint backward pass of x = A^{-1} b for a loss L(x) with g = dL/dx:
+ *   solve A^T lambda = g by the same CG (x0 = 0, same rtol / atol / budget,
+ *   threshold relative to |g|), then dL/db = lambda and
+ *   dL/dA_ij = -lambda_i x_j on the stored entries only.
+ * symmetric != 0: A^T is A (same arrays).  Otherwise A^T is formed by
+ * orc_transpose.  lam and gvals (nullable) are outputs; work: 3 n doubles.
+ */
+int orc_solve_backward(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
+                       int symmetric, const double* x, const double* g, double rtol, double atol,
+                       int64_t max_iter, int fixed, double* lam, double* gvals, double* work,
+                       int64_t* iters_out, double* res_out, double* rhs_out)
+{
+    int state;
+    if (symmetric) {
+        state = orc_cg(n, row_ptr, col, val, g, lam, rtol, atol, max_iter, fixed, work,
+                       iters_out, res_out, rhs_out, NULL);
+    } else {
+        int64_t nnz = row_ptr[n];
+        int64_t* rpt = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+        int32_t* ct = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+        int64_t* perm = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nnz > 0 ? nnz : 1));
+        double* vt = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
+        orc_transpose(n, n, row_ptr, col, rpt, ct, perm);
+        for (int64_t k = 0; k < nnz; ++k) vt[k] = val[perm[k]];
+        state = orc_cg(n, rpt, ct, vt, g, lam, rtol, atol, max_iter, fixed, work,
+                       iters_out, res_out, rhs_out, NULL);
+        free(rpt); free(ct); free(perm); free(vt);
+    }
+    if (gvals) orc_pattern_outer(n, row_ptr, col, -1.0, lam, x, gvals);
+    return state;
+}

@@ -1,0 +1,47 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each case compiles a copy of oracle/sla_oracle.c with one plausible mistake
+(a dropped term, a wrong sign, a wrong or transposed index) into a temporary
+directory and runs tests/test_oracle_pins.py against it in a subprocess.  CPU
+only; nothing here touches a GPU or the HIP library.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "sla_oracle.c")
+
+MUTANTS = {
+    "gradient sign": ("gvals[k] = sign * t;", "gvals[k] = -sign * t;"),
+    "gradient orientation": ("double t = u[i] * v[col[k]];", "double t = u[col[k]] * v[i];"),
+    "spmv column index": ("double t = val[k] * x[col[k]];\n            s = s + t;",
+                          "double t = val[k] * x[col[k] > 0 ? col[k] - 1 : 0];\n            s = s + t;"),
+    "beta inverted": ("double beta = rho1 / rho;", "double beta = rho / rho1;"),
+    "residual sign": ("r[i] = r[i] - t;", "r[i] = r[i] + t;"),
+    "beta term dropped": ("p[i] = r[i] + t;", "p[i] = r[i];"),
+    "alpha perturbed": ("double alpha = rho / sigma;", "double alpha = rho / sigma * 1.0000001;"),
+    "transpose permutation": ("perm[dst] = k;", "perm[dst] = k ^ 1;"),
+    "threshold not relative": ("double thr = rtol * bnorm;", "double thr = rtol;"),
+    "adjoint ignores transpose": ("if (symmetric) {", "if (1) {"),
+    "transposed spmv is forward": ("y[col[k]] = y[col[k]] + t;", "y[i] = y[i] + val[k] * x[col[k]];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(SRC).read()
+    a, b = MUTANTS[name]
+    assert a in src, "mutation anchor vanished from the oracle source"
+    mut = tmp_path / "mut.c"
+    mut.write_text(src.replace(a, b, 1))
+    so = tmp_path / "mut.so"
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-shared", "-fPIC", str(mut),
+                           "-o", str(so), "-lm"])
+    env = dict(os.environ, SLA_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "pins missed the planted mistake: " + name
