@@ -1,0 +1,17 @@
+"""MI355X-native differentiable sparse CG: CSR SpMV, conjugate-gradient solve and
+its adjoint backward pass, as HIP kernels for gfx950 behind a C ABI
+(include/sla.h, libsla.so).
+
+Importing the package loads libsla.so and fails loudly if it is missing: there
+is no CPU path.
+"""
+from . import _lib
+from ._lib import SlaError
+
+_lib.load()
+
+from .sparse import (SparseTensor, cg_opts, csr_create, csr_destroy, csr_info,  # noqa: E402
+                     matvec, matvec_backward, read_info, solve, solve_backward, timing)
+
+__all__ = ["SparseTensor", "SlaError", "cg_opts", "csr_create", "csr_destroy", "csr_info",
+           "matvec", "matvec_backward", "read_info", "solve", "solve_backward", "timing"]

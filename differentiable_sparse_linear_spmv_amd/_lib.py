@@ -1,0 +1,110 @@
+"""ctypes binding of libsla.so (include/sla.h): argument marshalling only.
+
+Every numerical step runs in the HIP kernels behind the C ABI.  Tensors are
+passed as raw device pointers with torch's current HIP stream; this module never
+computes anything itself and has no CPU fallback: if the library is missing it
+raises at import.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsla.so")
+
+SLA_OK, SLA_ERR_INVALID_ARG, SLA_ERR_INVALID_CSR, SLA_ERR_UNSUPPORTED, SLA_ERR_OOM, SLA_ERR_HIP = range(6)
+SLA_CONVERGED, SLA_MAX_ITER, SLA_NOT_SPD, SLA_NAN = range(4)
+STATE_NAMES = {0: "CONVERGED", 1: "MAX_ITER", 2: "NOT_SPD", 3: "NAN"}
+SLA_SYMMETRIC = 1
+SLA_EAGER_TRANSPOSE = 2
+SLA_FIXED_ITERS = 1
+(SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
+ SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_COUNT) = range(8)
+KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "gather_vals",
+                "transpose"]
+
+EXPORTS = [
+    "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_matvec", "sla_matvec_backward",
+    "sla_solve", "sla_solve_backward", "sla_timing_enable", "sla_timing_reset",
+    "sla_timing_collect", "sla_timing_query", "sla_status_string", "sla_last_error", "sla_version",
+]
+
+
+class SlaCgOpts(C.Structure):
+    _fields_ = [("rtol", C.c_double), ("atol", C.c_double), ("max_iter", C.c_int64),
+                ("check_every", C.c_int32), ("flags", C.c_uint32),
+                ("residual_history", C.c_void_p)]
+
+
+class SlaCgInfo(C.Structure):
+    _fields_ = [("iterations", C.c_int64), ("res_norm", C.c_double), ("rhs_norm", C.c_double),
+                ("state", C.c_int32), ("reserved", C.c_int32)]
+
+
+assert C.sizeof(SlaCgInfo) == 32
+
+
+class SlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def _status_name(s: int) -> str:
+    return ["SLA_OK", "SLA_ERR_INVALID_ARG", "SLA_ERR_INVALID_CSR", "SLA_ERR_UNSUPPORTED",
+            "SLA_ERR_OOM", "SLA_ERR_HIP"][s] if 0 <= s < 6 else f"status {s}"
+
+
+def load():
+    """Load libsla.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m differentiable_sparse_linear_spmv_amd.build` "
+                          "(there is no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    P, i64, i32, u32 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint32
+    st = C.c_int
+    L.sla_csr_create.argtypes = [C.POINTER(P), i64, i64, i64, P, i32, P, u32, P]
+    L.sla_csr_create.restype = st
+    L.sla_csr_destroy.argtypes = [P]
+    L.sla_csr_destroy.restype = st
+    L.sla_csr_info.argtypes = [P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64),
+                               C.POINTER(i32), C.POINTER(u32), C.POINTER(i64)]
+    L.sla_csr_info.restype = st
+    L.sla_matvec.argtypes = [P, i64, P, P, P, P]
+    L.sla_matvec.restype = st
+    L.sla_matvec_backward.argtypes = [P, i64, P, P, P, P, P, P]
+    L.sla_matvec_backward.restype = st
+    L.sla_solve.argtypes = [P, i64, P, P, P, C.POINTER(SlaCgOpts), P, P]
+    L.sla_solve.restype = st
+    L.sla_solve_backward.argtypes = [P, i64, P, P, P, P, P, C.POINTER(SlaCgOpts), P, P]
+    L.sla_solve_backward.restype = st
+    L.sla_timing_enable.argtypes = [i32]
+    L.sla_timing_enable.restype = st
+    L.sla_timing_reset.argtypes = []
+    L.sla_timing_reset.restype = st
+    L.sla_timing_collect.argtypes = []
+    L.sla_timing_collect.restype = st
+    L.sla_timing_query.argtypes = [i32, C.POINTER(i64), C.POINTER(C.c_double)]
+    L.sla_timing_query.restype = st
+    L.sla_status_string.argtypes = [st]
+    L.sla_status_string.restype = C.c_char_p
+    L.sla_last_error.argtypes = []
+    L.sla_last_error.restype = C.c_char_p
+    L.sla_version.argtypes = []
+    L.sla_version.restype = i32
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != SLA_OK:
+        msg = load().sla_last_error().decode(errors="replace")
+        raise SlaError(status, msg)

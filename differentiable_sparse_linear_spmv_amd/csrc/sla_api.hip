@@ -1,0 +1,660 @@
+// sla_api.hip -- the C ABI declared in include/sla.h: handles, argument checks,
+// workspace, and the host drivers that enqueue the CG and adjoint kernels.
+//
+// The solve loop follows the conjugate-gradient method of torch-sla's
+// pytorch-native backend (paperpeel page, sections 1 and 3.1), driven from the
+// device: the host enqueues chunks of iterations without reading any scalar, and
+// polls a device counter of still-running systems once per chunk (two chunks are
+// kept in flight, so the GPU never waits on the host).  The backward pass is the
+// linear adjoint of the gist.science summaries (Methodology item 2): a second CG
+// on A^T (A itself when the caller declares it symmetric), then an O(nnz) outer
+// product on the pattern (paperpeel section 3.2.3).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "sla.h"
+#include "sla_internal.h"
+
+using namespace sla;
+
+struct sla_csr {
+    int64_t n_rows = 0, n_cols = 0, nnz = 0;
+    int32_t rp_bits = 32;
+    uint32_t flags = 0;
+    const void* row_ptr = nullptr;
+    const int32_t* col = nullptr;
+    int device = 0;
+    int n_cu = 256;
+    int cap = kCapSmall;        // LDS variant for A
+    int32_t tile_max = 0;
+    // transposed pattern (lazily built unless SLA_SYMMETRIC)
+    bool has_t = false;
+    void* row_ptr_t = nullptr;
+    int32_t* col_t = nullptr;
+    int64_t* perm_t = nullptr;
+    int cap_t = kCapSmall;
+    // workspace
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    double* vals_t = nullptr;   // [batch][nnz] transposed values
+    size_t vals_t_bytes = 0;
+    int32_t* flag_host = nullptr;   // pinned, 2 slots for the polling copies
+    hipEvent_t poll_ev[2] = {nullptr, nullptr};
+    std::mutex mu;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sla_status fail(sla_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+#define HIP_TRY(expr)                                                                    \
+    do {                                                                                 \
+        hipError_t e_ = (expr);                                                          \
+        if (e_ != hipSuccess)                                                            \
+            return fail(SLA_ERR_HIP, "%s: %s (%s:%d)", #expr, hipGetErrorString(e_),     \
+                        __FILE__, __LINE__);                                             \
+    } while (0)
+
+// ---------------------------------------------------------------- kernel timing
+struct Pending {
+    int kid;
+    hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_pool;
+int64_t g_launches[SLA_K_COUNT] = {};
+double g_ms[SLA_K_COUNT] = {};
+
+hipEvent_t pool_get()
+{
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(int kid, hipStream_t s, F&& f)
+{
+    bool on;
+    {
+        std::lock_guard<std::mutex> lk(g_tmu);
+        on = g_timing;
+    }
+    if (!on) return f();
+    hipEvent_t a, b;
+    {
+        std::lock_guard<std::mutex> lk(g_tmu);
+        a = pool_get();
+        b = pool_get();
+    }
+    if (!a || !b) return f();
+    (void)hipEventRecord(a, s);
+    hipError_t e = f();
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pending.push_back({kid, a, b});
+    return e;
+}
+
+hipError_t timing_collect()
+{
+    std::vector<Pending> todo;
+    {
+        std::lock_guard<std::mutex> lk(g_tmu);
+        todo.swap(g_pending);
+    }
+    hipError_t first = hipSuccess;
+    for (auto& p : todo) {
+        hipError_t e = hipEventSynchronize(p.b);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.a, p.b);
+        if (e != hipSuccess && first == hipSuccess) first = e;
+        std::lock_guard<std::mutex> lk(g_tmu);
+        if (e == hipSuccess) {
+            g_launches[p.kid] += 1;
+            g_ms[p.kid] += ms;
+        }
+        g_pool.push_back(p.a);
+        g_pool.push_back(p.b);
+    }
+    return first;
+}
+
+// ---------------------------------------------------------------- helpers
+sla_status check_device(const sla_csr* A)
+{
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != A->device)
+        return fail(SLA_ERR_INVALID_ARG, "handle was created on device %d, current device is %d", A->device, dev);
+    return SLA_OK;
+}
+
+sla_status dev_alloc(void** p, size_t bytes)
+{
+    *p = nullptr;
+    if (bytes == 0) return SLA_OK;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        return fail(SLA_ERR_OOM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+    }
+    return SLA_OK;
+}
+
+int choose_cap(int32_t tile_max)
+{
+    if (tile_max <= kCapSmall) return kCapSmall;
+    if (tile_max <= kCapMid) return kCapMid;
+    return kCapLarge;
+}
+
+constexpr size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Workgroups per system: about 8 resident workgroups per CU over the whole grid.
+int blocks_per_system(const sla_csr* A, int64_t ntiles, int64_t batch)
+{
+    int64_t target = static_cast<int64_t>(A->n_cu) * 8;
+    int64_t g = (target + batch - 1) / batch;
+    if (g >= 8) g &= ~int64_t(7);   // a multiple of 8 enables the XCD band mapping
+    g = std::min<int64_t>(g, std::max<int64_t>(ntiles, 1));
+    return static_cast<int>(std::max<int64_t>(g, 1));
+}
+
+struct Workspace {
+    double *r, *p0, *p1, *q, *part_sigma, *part_rho;
+    SysState* st;
+    int32_t* n_active;
+};
+
+size_t workspace_bytes(int64_t n, int64_t batch, int G)
+{
+    const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
+    const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
+    return 4 * vec + 2 * part + align256(sizeof(SysState) * batch) + 256;
+}
+
+sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w)
+{
+    const int64_t n = A->n_rows;
+    const size_t need = workspace_bytes(n, batch, G);
+    if (need > A->ws_bytes) {
+        if (A->ws) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipFree(A->ws));
+            A->ws = nullptr;
+            A->ws_bytes = 0;
+        }
+        sla_status s = dev_alloc(&A->ws, need);
+        if (s != SLA_OK) return s;
+        A->ws_bytes = need;
+    }
+    char* p = static_cast<char*>(A->ws);
+    const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
+    const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
+    w->r = reinterpret_cast<double*>(p);
+    w->p0 = reinterpret_cast<double*>(p + vec);
+    w->p1 = reinterpret_cast<double*>(p + 2 * vec);
+    w->q = reinterpret_cast<double*>(p + 3 * vec);
+    w->part_sigma = reinterpret_cast<double*>(p + 4 * vec);
+    w->part_rho = reinterpret_cast<double*>(p + 4 * vec + part);
+    w->st = reinterpret_cast<SysState*>(p + 4 * vec + 2 * part);
+    w->n_active = reinterpret_cast<int32_t*>(p + 4 * vec + 2 * part + align256(sizeof(SysState) * batch));
+    return SLA_OK;
+}
+
+sla_status check_opts(const sla_cg_opts* o)
+{
+    if (!o) return fail(SLA_ERR_INVALID_ARG, "opts is NULL");
+    if (!(o->rtol >= 0.0) || !(o->atol >= 0.0))
+        return fail(SLA_ERR_INVALID_ARG, "rtol and atol must be >= 0 (got %g, %g)", o->rtol, o->atol);
+    if (o->max_iter < 0) return fail(SLA_ERR_INVALID_ARG, "max_iter must be >= 0");
+    if (o->check_every < 0) return fail(SLA_ERR_INVALID_ARG, "check_every must be >= 0");
+    if (o->flags & ~SLA_FIXED_ITERS) return fail(SLA_ERR_INVALID_ARG, "unknown cg flags 0x%x", o->flags);
+    return SLA_OK;
+}
+
+sla_status ensure_transpose(sla_csr* A, hipStream_t s)
+{
+    if (A->has_t) return SLA_OK;
+    void* scratch = nullptr;
+    sla_status st;
+    const size_t rpt_bytes = static_cast<size_t>(A->n_cols + 1) * (A->rp_bits == 64 ? 8 : 4);
+    if ((st = dev_alloc(&A->row_ptr_t, std::max<size_t>(rpt_bytes, 8))) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&A->col_t), std::max<size_t>(4 * A->nnz, 4))) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&A->perm_t), std::max<size_t>(8 * A->nnz, 8))) != SLA_OK) return st;
+    if ((st = dev_alloc(&scratch, transpose_scratch_bytes(A->n_rows, A->n_cols, A->nnz))) != SLA_OK) return st;
+    hipError_t e = timed(SLA_K_TRANSPOSE, s, [&] {
+        return launch_transpose(A->row_ptr, A->rp_bits, A->col, A->n_rows, A->n_cols, A->nnz, A->row_ptr_t,
+                                A->col_t, A->perm_t, scratch, s);
+    });
+    if (e != hipSuccess) {
+        (void)hipFree(scratch);
+        return fail(SLA_ERR_HIP, "transpose: %s", hipGetErrorString(e));
+    }
+    // analysis of the transposed pattern (also re-checks it)
+    int32_t* d_chk = static_cast<int32_t*>(scratch);   // reuse: the scan data is no longer needed
+    HIP_TRY(hipStreamSynchronize(s));
+    int32_t zero2[2] = {0, 0};
+    HIP_TRY(hipMemcpyAsync(d_chk, zero2, sizeof(zero2), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    e = launch_validate(A->row_ptr_t, A->rp_bits, A->col_t, A->n_cols, A->n_rows, A->nnz, d_chk, d_chk + 1, s);
+    if (e != hipSuccess) {
+        (void)hipFree(scratch);
+        return fail(SLA_ERR_HIP, "transpose analysis: %s", hipGetErrorString(e));
+    }
+    int32_t h[2];
+    HIP_TRY(hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    (void)hipFree(scratch);
+    if (h[0] != 0) return fail(SLA_ERR_HIP, "internal error: transposed pattern failed validation (%d)", h[0]);
+    A->cap_t = choose_cap(h[1]);
+    A->has_t = true;
+    return SLA_OK;
+}
+
+sla_status ensure_vals_t(sla_csr* A, int64_t batch, const double* vals, hipStream_t s, const double** out)
+{
+    const size_t need = sizeof(double) * static_cast<size_t>(A->nnz) * batch;
+    if (need > A->vals_t_bytes) {
+        if (A->vals_t) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipFree(A->vals_t));
+            A->vals_t = nullptr;
+            A->vals_t_bytes = 0;
+        }
+        sla_status st = dev_alloc(reinterpret_cast<void**>(&A->vals_t), need);
+        if (st != SLA_OK) return st;
+        A->vals_t_bytes = need;
+    }
+    hipError_t e = timed(SLA_K_GATHER_VALS, s, [&] {
+        return launch_gather_vals(A->perm_t, vals, A->vals_t, A->nnz, static_cast<int>(batch), s);
+    });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "gather of transposed values: %s", hipGetErrorString(e));
+    *out = A->vals_t;
+    return SLA_OK;
+}
+
+// One CG solve (batch systems) on the pattern (row_ptr, col, cap) with values vals.
+sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t batch, const double* vals,
+                  const double* b, double* x, const sla_cg_opts* o, sla_cg_info* info, hipStream_t s)
+{
+    const int64_t n = A->n_rows;
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    const int G = blocks_per_system(A, ntiles, batch);
+    Workspace w;
+    sla_status st = ensure_workspace(A, batch, G, &w);
+    if (st != SLA_OK) return st;
+
+    CgArgs a;
+    a.row_ptr = row_ptr;
+    a.col = col;
+    a.vals = vals;
+    a.b = b;
+    a.x = x;
+    a.r = w.r;
+    a.p0 = w.p0;
+    a.p1 = w.p1;
+    a.q = w.q;
+    a.part_sigma = w.part_sigma;
+    a.part_rho = w.part_rho;
+    a.st = w.st;
+    a.info = info;
+    a.hist = o->residual_history;
+    a.n_active = w.n_active;
+    a.n = n;
+    a.nnz = A->nnz;
+    a.ntiles = ntiles;
+    a.max_iter = o->max_iter;
+    a.rtol = o->rtol;
+    a.atol = o->atol;
+    a.fixed = (o->flags & SLA_FIXED_ITERS) ? 1 : 0;
+    a.G = G;
+    a.batch = static_cast<int32_t>(batch);
+    a.xcd_remap = 1;
+    const int rp_bits = A->rp_bits;
+
+    hipError_t e = timed(SLA_K_CG_INIT, s, [&] { return launch_cg_init(a, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "cg init launch: %s", hipGetErrorString(e));
+
+    auto step = [&](int64_t k) -> hipError_t {
+        hipError_t e1 = timed(SLA_K_CG_SPMV, s, [&] { return launch_cg_spmv(a, k, rp_bits, cap, s); });
+        if (e1 != hipSuccess || k >= a.max_iter) return e1;
+        return timed(SLA_K_CG_UPDATE, s, [&] { return launch_cg_update(a, k, s); });
+    };
+
+    if (a.fixed) {
+        for (int64_t k = 0; k <= a.max_iter; ++k) {
+            if ((e = step(k)) != hipSuccess) return fail(SLA_ERR_HIP, "cg launch: %s", hipGetErrorString(e));
+        }
+        return SLA_OK;
+    }
+    const int64_t chunk = o->check_every > 0 ? o->check_every : 32;
+    int64_t k = 0;
+    for (int64_t c = 0; k <= a.max_iter; ++c) {
+        const int64_t kend = std::min<int64_t>(k + chunk, a.max_iter + 1);
+        for (; k < kend; ++k) {
+            if ((e = step(k)) != hipSuccess) return fail(SLA_ERR_HIP, "cg launch: %s", hipGetErrorString(e));
+        }
+        const int slot = static_cast<int>(c & 1);
+        HIP_TRY(hipMemcpyAsync(A->flag_host + slot, w.n_active, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipEventRecord(A->poll_ev[slot], s));
+        if (c > 0) {
+            HIP_TRY(hipEventSynchronize(A->poll_ev[slot ^ 1]));
+            if (A->flag_host[slot ^ 1] == 0) break;   // every system has stopped
+        }
+    }
+    return SLA_OK;
+}
+
+sla_status check_common(const sla_csr* A, int64_t batch)
+{
+    if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
+    if (batch < 1 || batch > 65535) return fail(SLA_ERR_INVALID_ARG, "batch must be in [1, 65535] (got %lld)",
+                                               static_cast<long long>(batch));
+    return check_device(A);
+}
+
+}  // namespace
+
+// =====================================================================================
+extern "C" {
+
+const char* sla_status_string(sla_status s)
+{
+    switch (s) {
+    case SLA_OK: return "SLA_OK";
+    case SLA_ERR_INVALID_ARG: return "SLA_ERR_INVALID_ARG";
+    case SLA_ERR_INVALID_CSR: return "SLA_ERR_INVALID_CSR";
+    case SLA_ERR_UNSUPPORTED: return "SLA_ERR_UNSUPPORTED";
+    case SLA_ERR_OOM: return "SLA_ERR_OOM";
+    case SLA_ERR_HIP: return "SLA_ERR_HIP";
+    }
+    return "SLA_UNKNOWN_STATUS";
+}
+
+const char* sla_last_error(void) { return g_err; }
+
+int32_t sla_version(void) { return 100; }
+
+sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t nnz, const void* d_row_ptr,
+                          int32_t row_ptr_bits, const int32_t* d_col_idx, uint32_t flags, void* stream)
+{
+    if (!out) return fail(SLA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (n_rows < 0 || n_cols < 0 || nnz < 0) return fail(SLA_ERR_INVALID_ARG, "negative size");
+    if (n_rows >= (int64_t(1) << 31) || n_cols >= (int64_t(1) << 31))
+        return fail(SLA_ERR_INVALID_ARG, "n_rows and n_cols must be < 2^31");
+    if (row_ptr_bits != 32 && row_ptr_bits != 64)
+        return fail(SLA_ERR_INVALID_ARG, "row_ptr_bits must be 32 or 64 (got %d)", row_ptr_bits);
+    if (row_ptr_bits == 32 && nnz >= (int64_t(1) << 31))
+        return fail(SLA_ERR_INVALID_ARG, "nnz >= 2^31 needs 64-bit row pointers");
+    if (!d_row_ptr) return fail(SLA_ERR_INVALID_ARG, "row_ptr is NULL");
+    if (!d_col_idx && nnz > 0) return fail(SLA_ERR_INVALID_ARG, "col_idx is NULL");
+    if (flags & ~(SLA_SYMMETRIC | SLA_EAGER_TRANSPOSE)) return fail(SLA_ERR_INVALID_ARG, "unknown csr flags 0x%x", flags);
+    if ((flags & SLA_SYMMETRIC) && n_rows != n_cols)
+        return fail(SLA_ERR_INVALID_ARG, "SLA_SYMMETRIC needs a square matrix");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    sla_csr* A = new (std::nothrow) sla_csr();
+    if (!A) return fail(SLA_ERR_OOM, "host allocation failed");
+    A->n_rows = n_rows;
+    A->n_cols = n_cols;
+    A->nnz = nnz;
+    A->rp_bits = row_ptr_bits;
+    A->flags = flags;
+    A->row_ptr = d_row_ptr;
+    A->col = d_col_idx;
+    auto bail = [&](sla_status st) {
+        sla_csr_destroy(A);
+        return st;
+    };
+    if (hipGetDevice(&A->device) != hipSuccess) return bail(fail(SLA_ERR_HIP, "hipGetDevice failed"));
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, A->device) == hipSuccess && ncu > 0)
+        A->n_cu = ncu;
+    if (hipHostMalloc(reinterpret_cast<void**>(&A->flag_host), 2 * sizeof(int32_t), hipHostMallocDefault) !=
+        hipSuccess)
+        return bail(fail(SLA_ERR_OOM, "pinned host allocation failed"));
+    A->flag_host[0] = A->flag_host[1] = -1;
+    for (int i = 0; i < 2; ++i)
+        if (hipEventCreateWithFlags(&A->poll_ev[i], hipEventDisableTiming) != hipSuccess)
+            return bail(fail(SLA_ERR_HIP, "hipEventCreate failed"));
+
+    // Validation and tile analysis: one device pass, one synchronisation.
+    int32_t* d_chk = nullptr;
+    sla_status st = dev_alloc(reinterpret_cast<void**>(&d_chk), 2 * sizeof(int32_t));
+    if (st != SLA_OK) return bail(st);
+    int32_t h[2] = {0, 0};
+    hipError_t e = hipMemcpyAsync(d_chk, h, sizeof(h), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess)
+        e = launch_validate(d_row_ptr, row_ptr_bits, d_col_idx, n_rows, n_cols, nnz, d_chk, d_chk + 1, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    (void)hipFree(d_chk);
+    if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "CSR validation: %s", hipGetErrorString(e)));
+    if (h[0] != 0) {
+        const char* why = (h[0] & 1) ? "row_ptr[0] != 0 or row_ptr[n_rows] != nnz"
+                          : (h[0] & 2) ? "row_ptr is not non-decreasing within [0, nnz]"
+                          : (h[0] & 4) ? "a column index is out of [0, n_cols)"
+                                       : "columns are not strictly ascending within a row";
+        return bail(fail(SLA_ERR_INVALID_CSR, "invalid CSR: %s (code %d)", why, h[0]));
+    }
+    A->tile_max = h[1];
+    A->cap = choose_cap(h[1]);
+    if ((flags & SLA_EAGER_TRANSPOSE) && !(flags & SLA_SYMMETRIC)) {
+        std::lock_guard<std::mutex> lk(A->mu);
+        if ((st = ensure_transpose(A, s)) != SLA_OK) return bail(st);
+    }
+    *out = A;
+    return SLA_OK;
+}
+
+sla_status sla_csr_destroy(sla_csr* A)
+{
+    if (!A) return SLA_OK;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (prev != A->device) (void)hipSetDevice(A->device);
+    (void)hipDeviceSynchronize();
+    if (A->ws) (void)hipFree(A->ws);
+    if (A->vals_t) (void)hipFree(A->vals_t);
+    if (A->row_ptr_t) (void)hipFree(A->row_ptr_t);
+    if (A->col_t) (void)hipFree(A->col_t);
+    if (A->perm_t) (void)hipFree(A->perm_t);
+    if (A->flag_host) (void)hipHostFree(A->flag_host);
+    for (int i = 0; i < 2; ++i)
+        if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);
+    if (prev >= 0 && prev != A->device) (void)hipSetDevice(prev);
+    delete A;
+    return SLA_OK;
+}
+
+sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int64_t* nnz, int32_t* row_ptr_bits,
+                        uint32_t* flags, int64_t* workspace_bytes_out)
+{
+    if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
+    if (n_rows) *n_rows = A->n_rows;
+    if (n_cols) *n_cols = A->n_cols;
+    if (nnz) *nnz = A->nnz;
+    if (row_ptr_bits) *row_ptr_bits = A->rp_bits;
+    if (flags) *flags = A->flags;
+    if (workspace_bytes_out) {
+        int64_t tb = 0;
+        if (A->has_t)
+            tb = (A->n_cols + 1) * (A->rp_bits == 64 ? 8 : 4) + 12 * A->nnz;
+        *workspace_bytes_out = static_cast<int64_t>(A->ws_bytes + A->vals_t_bytes) + tb;
+    }
+    return SLA_OK;
+}
+
+sla_status sla_matvec(const sla_csr* Ac, int64_t batch, const double* d_vals, const double* d_x, double* d_y,
+                      void* stream)
+{
+    sla_status st = check_common(Ac, batch);
+    if (st != SLA_OK) return st;
+    if ((!d_vals && Ac->nnz > 0) || (!d_x && Ac->n_cols > 0) || (!d_y && Ac->n_rows > 0))
+        return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(SLA_K_MATVEC, s, [&] {
+        return launch_matvec(Ac->row_ptr, Ac->rp_bits, Ac->col, d_vals, d_x, d_y, Ac->n_rows, Ac->nnz, Ac->n_cols,
+                             static_cast<int>(batch), Ac->cap, s);
+    });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "matvec launch: %s", hipGetErrorString(e));
+    return SLA_OK;
+}
+
+sla_status sla_matvec_backward(const sla_csr* Ac, int64_t batch, const double* d_vals, const double* d_x,
+                               const double* d_gy, double* d_gx, double* d_gvals, void* stream)
+{
+    sla_status st = check_common(Ac, batch);
+    if (st != SLA_OK) return st;
+    if (!d_gy && Ac->n_rows > 0) return fail(SLA_ERR_INVALID_ARG, "gy is NULL");
+    if (d_gx && !d_vals && Ac->nnz > 0) return fail(SLA_ERR_INVALID_ARG, "vals is NULL");
+    if (d_gvals && !d_x && Ac->n_cols > 0) return fail(SLA_ERR_INVALID_ARG, "x is NULL");
+    sla_csr* A = const_cast<sla_csr*>(Ac);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(A->mu);
+    if (d_gx) {
+        hipError_t e;
+        if (A->flags & SLA_SYMMETRIC) {
+            e = timed(SLA_K_MATVEC, s, [&] {
+                return launch_matvec(A->row_ptr, A->rp_bits, A->col, d_vals, d_gy, d_gx, A->n_rows, A->nnz,
+                                     A->n_cols, static_cast<int>(batch), A->cap, s);
+            });
+        } else {
+            if ((st = ensure_transpose(A, s)) != SLA_OK) return st;
+            const double* vt = nullptr;
+            if ((st = ensure_vals_t(A, batch, d_vals, s, &vt)) != SLA_OK) return st;
+            e = timed(SLA_K_MATVEC, s, [&] {
+                return launch_matvec(A->row_ptr_t, A->rp_bits, A->col_t, vt, d_gy, d_gx, A->n_cols, A->nnz,
+                                     A->n_rows, static_cast<int>(batch), A->cap_t, s);
+            });
+        }
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "matvec_backward launch: %s", hipGetErrorString(e));
+    }
+    if (d_gvals) {
+        hipError_t e = timed(SLA_K_PATTERN_OUTER, s, [&] {
+            return launch_pattern_outer(A->row_ptr, A->rp_bits, A->col, 1.0, d_gy, A->n_rows, d_x, A->n_cols,
+                                        d_gvals, A->n_rows, A->nnz, static_cast<int>(batch), s);
+        });
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "pattern outer launch: %s", hipGetErrorString(e));
+    }
+    return SLA_OK;
+}
+
+sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, const double* d_b, double* d_x,
+                     const sla_cg_opts* opts, sla_cg_info* d_info, void* stream)
+{
+    sla_status st = check_common(Ac, batch);
+    if (st != SLA_OK) return st;
+    if (Ac->n_rows != Ac->n_cols) return fail(SLA_ERR_UNSUPPORTED, "solve needs a square matrix");
+    if ((st = check_opts(opts)) != SLA_OK) return st;
+    if ((!d_vals && Ac->nnz > 0) || !d_b || !d_x || !d_info) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    sla_csr* A = const_cast<sla_csr*>(Ac);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(A->mu);
+    st = run_cg(A, A->row_ptr, A->col, A->cap, batch, d_vals, d_b, d_x, opts, d_info, s);
+    if (st == SLA_OK && !(opts->flags & SLA_FIXED_ITERS)) {
+        hipError_t e = timing_collect();
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
+    }
+    return st;
+}
+
+sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_vals, const double* d_x,
+                              const double* d_gx, double* d_gb, double* d_gvals, const sla_cg_opts* opts,
+                              sla_cg_info* d_info, void* stream)
+{
+    sla_status st = check_common(Ac, batch);
+    if (st != SLA_OK) return st;
+    if (Ac->n_rows != Ac->n_cols) return fail(SLA_ERR_UNSUPPORTED, "solve_backward needs a square matrix");
+    if ((st = check_opts(opts)) != SLA_OK) return st;
+    if ((!d_vals && Ac->nnz > 0) || !d_gx || !d_gb || !d_info || (d_gvals && !d_x))
+        return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    sla_csr* A = const_cast<sla_csr*>(Ac);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(A->mu);
+    if (A->flags & SLA_SYMMETRIC) {
+        st = run_cg(A, A->row_ptr, A->col, A->cap, batch, d_vals, d_gx, d_gb, opts, d_info, s);
+    } else {
+        if ((st = ensure_transpose(A, s)) != SLA_OK) return st;
+        const double* vt = nullptr;
+        if ((st = ensure_vals_t(A, batch, d_vals, s, &vt)) != SLA_OK) return st;
+        st = run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, batch, vt, d_gx, d_gb, opts, d_info, s);
+    }
+    if (st != SLA_OK) return st;
+    if (d_gvals) {
+        hipError_t e = timed(SLA_K_PATTERN_OUTER, s, [&] {
+            return launch_pattern_outer(A->row_ptr, A->rp_bits, A->col, -1.0, d_gb, A->n_rows, d_x, A->n_cols,
+                                        d_gvals, A->n_rows, A->nnz, static_cast<int>(batch), s);
+        });
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "gradient scatter launch: %s", hipGetErrorString(e));
+    }
+    if (!(opts->flags & SLA_FIXED_ITERS)) {
+        hipError_t e = timing_collect();
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
+    }
+    return SLA_OK;
+}
+
+sla_status sla_timing_enable(int32_t enable)
+{
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing = enable != 0;
+    return SLA_OK;
+}
+
+sla_status sla_timing_reset(void)
+{
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (int i = 0; i < SLA_K_COUNT; ++i) {
+        g_launches[i] = 0;
+        g_ms[i] = 0.0;
+    }
+    return SLA_OK;
+}
+
+sla_status sla_timing_collect(void)
+{
+    hipError_t e = timing_collect();
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
+    return SLA_OK;
+}
+
+sla_status sla_timing_query(int32_t kernel, int64_t* launches, double* total_ms)
+{
+    if (kernel < 0 || kernel >= SLA_K_COUNT) return fail(SLA_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (launches) *launches = g_launches[kernel];
+    if (total_ms) *total_ms = g_ms[kernel];
+    return SLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// sla_internal.h -- shared declarations between the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sla.h"
+
+namespace sla {
+
+constexpr int kBlock = 256;   // threads per workgroup (4 waves of 64)
+constexpr int kTile = 256;    // CSR rows per tile: one row per lane
+
+// LDS capacities (stored entries per tile) of the staged SpMV variants.  The
+// handle picks the smallest that holds its largest tile; tiles above the cap
+// take the wave-per-row path inside the same kernel.
+constexpr int kCapSmall = 1280;   // 5 entries per row
+constexpr int kCapMid = 2048;     // 8 per row
+constexpr int kCapLarge = 4096;   // 16 per row
+
+// Per-system CG state in device memory (64 bytes).  Double-buffered by the
+// parity of the iteration index so that a kernel reads the previous value while
+// its first workgroup writes the new one.
+struct SysState {
+    int64_t stop_iter;   // INT64_MAX while running; else the iteration at which it stopped
+    double rho[2];       // rho_k = r_k^T r_k, slot k & 1
+    double alpha[2];     // alpha_k, slot k & 1
+    double thr;          // stop threshold max(rtol |rhs|, atol)
+    double rhs;          // |rhs|
+    double pad;
+};
+static_assert(sizeof(SysState) == 64, "SysState layout");
+
+// Arguments of the fused CG kernels (passed by value).
+struct CgArgs {
+    const void* row_ptr;     // int32 or int64 [n + 1]
+    const int32_t* col;      // [nnz]
+    const double* vals;      // [batch][nnz]
+    const double* b;         // [batch][n]   right-hand side (r_0)
+    double* x;               // [batch][n]
+    double* r;               // [batch][n]
+    double* p0;              // [batch][n]   p_k for even k
+    double* p1;              // [batch][n]   p_k for odd k
+    double* q;               // [batch][n]   A p_k
+    double* part_sigma;      // [batch][G]
+    double* part_rho;        // [batch][G]
+    SysState* st;            // [batch]
+    sla_cg_info* info;       // [batch]
+    double* hist;            // nullable, [batch][max_iter + 1]
+    int32_t* n_active;       // systems still running
+    int64_t n;
+    int64_t nnz;
+    int64_t ntiles;
+    int64_t max_iter;
+    double rtol;
+    double atol;
+    int32_t fixed;
+    int32_t G;               // workgroups per system
+    int32_t batch;
+    int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
+};
+
+// Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.
+hipError_t launch_cg_init(const CgArgs& a, hipStream_t s);
+hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s);
+hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s);
+
+hipError_t launch_matvec(const void* row_ptr, int rp_bits, const int32_t* col, const double* vals,
+                         const double* x, double* y, int64_t n_rows, int64_t nnz, int64_t n_cols,
+                         int batch, int cap, hipStream_t s);
+
+hipError_t launch_pattern_outer(const void* row_ptr, int rp_bits, const int32_t* col, double sign,
+                                const double* u, int64_t u_stride, const double* v,
+                                int64_t v_stride, double* g, int64_t n_rows, int64_t nnz,
+                                int batch, hipStream_t s);
+
+hipError_t launch_gather_vals(const int64_t* perm, const double* vals, double* out, int64_t nnz,
+                              int batch, hipStream_t s);
+
+// CSR checks: writes err[0] != 0 on the first problem found (no early exit) and
+// max entries per tile into tile_max[0].
+hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col, int64_t n_rows,
+                           int64_t n_cols, int64_t nnz, int32_t* err, int32_t* tile_max,
+                           hipStream_t s);
+
+// Transposed pattern: row_ptr_t (same width as rp_bits) [n_cols + 1], col_t [nnz],
+// perm [nnz] (position in A of each entry of A^T).  scratch: see transpose_scratch_bytes.
+size_t transpose_scratch_bytes(int64_t n_rows, int64_t n_cols, int64_t nnz);
+hipError_t launch_transpose(const void* row_ptr, int rp_bits, const int32_t* col, int64_t n_rows,
+                            int64_t n_cols, int64_t nnz, void* row_ptr_t, int32_t* col_t,
+                            int64_t* perm, void* scratch, hipStream_t s);
+
+}  // namespace sla

@@ -1,0 +1,313 @@
+"""Python surface of the HIP library: C-ABI calls with the same names, and the
+SparseTensor / autograd wrappers of torch-sla's API (.matvec, .solve with
+gradients to the values and to b).
+
+torch-sla (Differentiable Sparse Linear Algebra with Adjoint Solvers and Sparse
+Tensor Parallelism for PyTorch), paperpeel page, section 3.1: every operation is
+one torch.autograd.Function whose forward calls the solver under no_grad and
+stashes (A, x), and whose backward runs the adjoint solve -- one graph node and
+O(n + nnz) memory whatever the iteration count (section 3.2).  A SparseTensor is
+one matrix or a batch of matrices that share one pattern ("Typed sparse-tensor
+hierarchy").  Here the forward and backward are the C-ABI calls sla_solve and
+sla_solve_backward; this module only marshals tensors (device pointers, sizes,
+torch's current HIP stream) and never computes on the host.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import warnings
+
+import torch
+
+from . import _lib as L
+from ._lib import SlaCgInfo, SlaCgOpts, check
+
+__all__ = [
+    "csr_create", "csr_destroy", "csr_info", "matvec", "matvec_backward", "solve",
+    "solve_backward", "cg_opts", "read_info", "SparseTensor", "timing",
+]
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: int, device) -> None:
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+class Handle:
+    """Owns an sla_csr* and keeps the borrowed row_ptr / col tensors alive."""
+
+    def __init__(self, ptr: int, row_ptr: torch.Tensor, col: torch.Tensor, n_rows: int,
+                 n_cols: int, symmetric: bool):
+        self.ptr = C.c_void_p(ptr)
+        self.row_ptr, self.col = row_ptr, col
+        self.n_rows, self.n_cols, self.nnz = n_rows, n_cols, int(col.numel())
+        self.symmetric = symmetric
+        self.device = row_ptr.device
+
+    def __del__(self):
+        p = getattr(self, "ptr", None)
+        if p is not None and p.value:
+            try:
+                L.load().sla_csr_destroy(p)
+            except Exception:
+                pass
+            self.ptr = C.c_void_p(0)
+
+
+def csr_create(row_ptr: torch.Tensor, col: torch.Tensor, n_cols: int | None = None,
+               symmetric: bool = False, eager_transpose: bool = False) -> Handle:
+    """sla_csr_create: validate the pattern on the device and analyse it."""
+    lib = L.load()
+    if row_ptr.dtype not in (torch.int32, torch.int64):
+        raise ValueError("row_ptr must be int32 or int64")
+    if col.dtype != torch.int32:
+        raise ValueError("col must be int32")
+    if not row_ptr.is_cuda or col.device != row_ptr.device:
+        raise ValueError("row_ptr and col must be on the same GPU")
+    row_ptr, col = row_ptr.contiguous(), col.contiguous()
+    n_rows = row_ptr.numel() - 1
+    n_cols = n_rows if n_cols is None else int(n_cols)
+    flags = (L.SLA_SYMMETRIC if symmetric else 0) | (L.SLA_EAGER_TRANSPOSE if eager_transpose else 0)
+    out = C.c_void_p()
+    with torch.cuda.device(row_ptr.device):
+        check(lib.sla_csr_create(C.byref(out), n_rows, n_cols, col.numel(), row_ptr.data_ptr(),
+                                 32 if row_ptr.dtype == torch.int32 else 64,
+                                 col.data_ptr() if col.numel() else None, flags,
+                                 _stream(row_ptr.device)))
+    return Handle(out.value, row_ptr, col, n_rows, n_cols, symmetric)
+
+
+def csr_destroy(h: Handle) -> None:
+    h.__del__()
+
+
+def csr_info(h: Handle) -> dict:
+    lib = L.load()
+    a, b, c, w = C.c_int64(), C.c_int64(), C.c_int64(), C.c_int64()
+    bits, fl = C.c_int32(), C.c_uint32()
+    check(lib.sla_csr_info(h.ptr, C.byref(a), C.byref(b), C.byref(c), C.byref(bits),
+                           C.byref(fl), C.byref(w)))
+    return dict(n_rows=a.value, n_cols=b.value, nnz=c.value, row_ptr_bits=bits.value,
+                flags=fl.value, workspace_bytes=w.value)
+
+
+def _batch_of(vals: torch.Tensor, nnz: int) -> int:
+    if vals.dim() == 1:
+        return 1
+    if vals.dim() == 2 and vals.shape[1] == nnz:
+        return int(vals.shape[0])
+    raise ValueError(f"vals must be [nnz] or [batch, nnz] (got {tuple(vals.shape)})")
+
+
+def matvec(h: Handle, vals: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None):
+    """sla_matvec: y = A x for every system of the batch."""
+    B = _batch_of(vals, h.nnz)
+    _need(vals, "vals", torch.float64, B * h.nnz, h.device)
+    _need(x, "x", torch.float64, B * h.n_cols, h.device)
+    if y is None:
+        y = torch.empty((B, h.n_rows) if vals.dim() == 2 else (h.n_rows,), dtype=torch.float64,
+                        device=h.device)
+    _need(y, "y", torch.float64, B * h.n_rows, h.device)
+    check(L.load().sla_matvec(h.ptr, B, _ptr(vals), _ptr(x), _ptr(y), _stream(h.device)))
+    return y
+
+
+def matvec_backward(h: Handle, vals: torch.Tensor, x: torch.Tensor, gy: torch.Tensor,
+                    need_gx: bool = True, need_gvals: bool = True):
+    """sla_matvec_backward: (gx = A^T gy, gvals = gy[row] * x[col])."""
+    B = _batch_of(vals, h.nnz)
+    _need(gy, "gy", torch.float64, B * h.n_rows, h.device)
+    gx = gv = None
+    if need_gx:
+        _need(vals, "vals", torch.float64, B * h.nnz, h.device)
+        gx = torch.empty((B, h.n_cols) if vals.dim() == 2 else (h.n_cols,), dtype=torch.float64,
+                         device=h.device)
+    if need_gvals:
+        _need(x, "x", torch.float64, B * h.n_cols, h.device)
+        gv = torch.empty_like(vals)
+    check(L.load().sla_matvec_backward(h.ptr, B, _ptr(vals), _ptr(x), _ptr(gy), _ptr(gx),
+                                       _ptr(gv), _stream(h.device)))
+    return gx, gv
+
+
+def cg_opts(rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, check_every=0,
+            residual_history: torch.Tensor | None = None) -> SlaCgOpts:
+    return SlaCgOpts(float(rtol), float(atol), int(max_iter), int(check_every),
+                     L.SLA_FIXED_ITERS if fixed else 0,
+                     residual_history.data_ptr() if residual_history is not None else None)
+
+
+def _info_buffer(B: int, device) -> torch.Tensor:
+    return torch.empty(B * C.sizeof(SlaCgInfo), dtype=torch.uint8, device=device)
+
+
+def read_info(info: torch.Tensor) -> list[dict]:
+    """Copy a device sla_cg_info array to the host (synchronises the stream)."""
+    raw = info.cpu().numpy().tobytes()
+    n = len(raw) // C.sizeof(SlaCgInfo)
+    out = []
+    for i in range(n):
+        s = SlaCgInfo.from_buffer_copy(raw[i * 32:(i + 1) * 32])
+        out.append(dict(iterations=s.iterations, res_norm=s.res_norm, rhs_norm=s.rhs_norm,
+                        state=s.state, state_name=L.STATE_NAMES.get(s.state, str(s.state))))
+    return out
+
+
+def solve(h: Handle, vals: torch.Tensor, b: torch.Tensor, opts: SlaCgOpts,
+          x: torch.Tensor | None = None, info: torch.Tensor | None = None):
+    """sla_solve: CG from x0 = 0.  Returns (x, info) with info a device byte buffer."""
+    B = _batch_of(vals, h.nnz)
+    _need(vals, "vals", torch.float64, B * h.nnz, h.device)
+    _need(b, "b", torch.float64, B * h.n_rows, h.device)
+    if x is None:
+        x = torch.empty_like(b)
+    _need(x, "x", torch.float64, B * h.n_rows, h.device)
+    if info is None:
+        info = _info_buffer(B, h.device)
+    check(L.load().sla_solve(h.ptr, B, _ptr(vals), _ptr(b), _ptr(x), C.byref(opts), _ptr(info),
+                             _stream(h.device)))
+    return x, info
+
+
+def solve_backward(h: Handle, vals: torch.Tensor, x: torch.Tensor, gx: torch.Tensor,
+                   opts: SlaCgOpts, need_gvals: bool = True, gb: torch.Tensor | None = None,
+                   gvals: torch.Tensor | None = None, info: torch.Tensor | None = None):
+    """sla_solve_backward: returns (gb = lambda, gvals = -lambda[row] x[col], info)."""
+    B = _batch_of(vals, h.nnz)
+    _need(vals, "vals", torch.float64, B * h.nnz, h.device)
+    _need(gx, "gx", torch.float64, B * h.n_rows, h.device)
+    if gb is None:
+        gb = torch.empty_like(gx)
+    _need(gb, "gb", torch.float64, B * h.n_rows, h.device)
+    if need_gvals:
+        _need(x, "x", torch.float64, B * h.n_rows, h.device)
+        if gvals is None:
+            gvals = torch.empty_like(vals)
+        _need(gvals, "gvals", torch.float64, B * h.nnz, h.device)
+    else:
+        gvals = None
+    if info is None:
+        info = _info_buffer(B, h.device)
+    check(L.load().sla_solve_backward(h.ptr, B, _ptr(vals), _ptr(x), _ptr(gx), _ptr(gb),
+                                      _ptr(gvals), C.byref(opts), _ptr(info), _stream(h.device)))
+    return gb, gvals, info
+
+
+class timing:
+    """Per-kernel HIP-event timing inside the library (for measurement only)."""
+
+    @staticmethod
+    def enable(on: bool = True):
+        check(L.load().sla_timing_enable(1 if on else 0))
+
+    @staticmethod
+    def reset():
+        check(L.load().sla_timing_reset())
+
+    @staticmethod
+    def collect():
+        check(L.load().sla_timing_collect())
+
+    @staticmethod
+    def query() -> dict:
+        lib = L.load()
+        out = {}
+        for k, name in enumerate(L.KERNEL_NAMES):
+            n, ms = C.c_int64(), C.c_double()
+            check(lib.sla_timing_query(k, C.byref(n), C.byref(ms)))
+            out[name] = dict(launches=n.value, total_ms=ms.value)
+        return out
+
+
+# ------------------------------------------------------------------------------ autograd
+class _SolveFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, A, vals, b, opts_kw):
+        opts = cg_opts(**opts_kw)
+        x, info = solve(A.handle, vals.detach(), b.detach(), opts)
+        A.last_info = info
+        ctx.A, ctx.opts_kw = A, opts_kw
+        ctx.save_for_backward(vals, x)
+        return x
+
+    @staticmethod
+    def backward(ctx, gx):
+        vals, x = ctx.saved_tensors
+        A = ctx.A
+        opts = cg_opts(**ctx.opts_kw)
+        gb, gvals, info = solve_backward(A.handle, vals.detach(), x, gx.contiguous(), opts,
+                                         need_gvals=ctx.needs_input_grad[1])
+        A.last_backward_info = info
+        return None, gvals, (gb if ctx.needs_input_grad[2] else None), None
+
+
+class _MatvecFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, A, vals, x):
+        y = matvec(A.handle, vals.detach(), x.detach())
+        ctx.A = A
+        ctx.save_for_backward(vals, x)
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        vals, x = ctx.saved_tensors
+        gx, gv = matvec_backward(ctx.A.handle, vals.detach(), x.detach(), gy.contiguous(),
+                                 need_gx=ctx.needs_input_grad[2],
+                                 need_gvals=ctx.needs_input_grad[1])
+        return None, gv, gx
+
+
+class SparseTensor:
+    """One CSR matrix, or a batch of matrices sharing one pattern (vals [B, nnz]).
+
+    ``matvec(x)`` and ``solve(b)`` are differentiable with respect to ``vals`` and
+    to ``x`` / ``b``; each is one autograd node.
+    """
+
+    def __init__(self, row_ptr: torch.Tensor, col: torch.Tensor, vals: torch.Tensor,
+                 shape: tuple[int, int] | None = None, symmetric: bool = False):
+        n_cols = None if shape is None else shape[1]
+        self.handle = csr_create(row_ptr, col, n_cols=n_cols, symmetric=symmetric)
+        self.vals = vals
+        self.shape = (self.handle.n_rows, self.handle.n_cols)
+        self.last_info = None
+        self.last_backward_info = None
+
+    @property
+    def batch(self) -> int:
+        return _batch_of(self.vals, self.handle.nnz)
+
+    def matvec(self, x: torch.Tensor) -> torch.Tensor:
+        return _MatvecFn.apply(self, self.vals, x)
+
+    def solve(self, b: torch.Tensor, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False,
+              check: bool = False) -> torch.Tensor:
+        kw = dict(rtol=rtol, atol=atol, max_iter=max_iter, fixed=fixed)
+        x = _SolveFn.apply(self, self.vals, b, kw)
+        if check:
+            for i, s in enumerate(read_info(self.last_info)):
+                if s["state"] in (L.SLA_NOT_SPD, L.SLA_NAN):
+                    raise FloatingPointError(f"system {i}: CG stopped with {s['state_name']}")
+                if s["state"] == L.SLA_MAX_ITER and not fixed:
+                    warnings.warn(f"system {i}: CG reached max_iter={max_iter} "
+                                  f"(|r|/|b| = {s['res_norm'] / max(s['rhs_norm'], 1e-300):.3e})")
+        return x
+
+    def info(self, backward: bool = False) -> list[dict]:
+        buf = self.last_backward_info if backward else self.last_info
+        return [] if buf is None else read_info(buf)

@@ -1,0 +1,201 @@
+/*
+ * sla.h -- C ABI of the MI355X (gfx950) sparse CG solve and its adjoint.
+ *
+ * The operations follow torch-sla: Differentiable Sparse Linear Algebra with
+ * Adjoint Solvers and Sparse Tensor Parallelism for PyTorch:
+ *   - the API calls .matvec and .solve(b), with gradients flowing to the matrix
+ *     values and to b (paperpeel page, section 3.1 "API" and "Bridging backends
+ *     into autograd"; gist.science summaries, Methodology item 1);
+ *   - an explicit val/row/col operator (paperpeel, section "Operator
+ *     representation: explicit vs. implicit"), stored here as CSR;
+ *   - a SparseTensor is one matrix or a batch sharing one pattern (gist.science
+ *     summaries, Methodology item 1; paperpeel section 3.1 "Typed sparse-tensor
+ *     hierarchy"): every call below takes `batch` systems whose values are
+ *     [batch][nnz] over one pattern -- the batched shared-pattern variants;
+ *   - the solve is the pytorch-native backend's conjugate gradient, here
+ *     without preconditioner (paperpeel sections 1 and 3.1; section 3.3
+ *     "Distributed Krylov solvers" for one SpMV and the inner products <r,r>,
+ *     <p,Ap> per iteration);
+ *   - the backward pass solves A^T lambda = dL/dx and returns dL/db = lambda and
+ *     dL/dA_ij = -lambda_i x_j on the stored entries only (gist.science Hindi and
+ *     Japanese summaries, Methodology item 2, linear-systems bullet; paperpeel
+ *     section 3.2.3 "Complexity": one adjoint solve of the same size and pattern
+ *     plus an O(nnz) outer product).
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* or documented "device" are device pointers on the
+ *     current HIP device; everything else is host memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued on it.  sla_solve / sla_solve_backward with a residual
+ *     test block the calling host thread until the iterations have finished on
+ *     the stream (they poll a device counter once per chunk of iterations);
+ *     everything else returns after enqueueing.
+ *   - The caller owns every array it passes.  A handle borrows row_ptr and
+ *     col_idx: they must stay valid and unchanged until sla_csr_destroy.  The
+ *     library owns the handle's analysis data, an optional transposed pattern,
+ *     and a per-handle workspace (CG vectors and reduction partials, O(n + nnz)
+ *     per system, independent of the iteration count) which it allocates on
+ *     first use and frees in sla_csr_destroy.
+ *   - Calls that share one handle must not overlap in time (use one stream per
+ *     handle, or serialise): they share its workspace.
+ *   - Errors: argument problems are returned as sla_status before anything is
+ *     enqueued.  Numerical outcomes of a solve (converged, budget reached,
+ *     breakdown) are per-system states written into the device info array,
+ *     never return codes.  sla_last_error() gives a message for the calling
+ *     thread's most recent non-OK status.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SLA_OK = 0,
+    SLA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad flag, batch < 1, ... */
+    SLA_ERR_INVALID_CSR = 2,   /* row_ptr not monotone / not starting at 0 / not ending at nnz,
+                                  a column out of range, or columns not strictly ascending */
+    SLA_ERR_UNSUPPORTED = 3,   /* e.g. a solve on a non-square matrix */
+    SLA_ERR_OOM = 4,           /* device allocation of library-owned memory failed */
+    SLA_ERR_HIP = 5            /* a HIP runtime call failed; see sla_last_error() */
+} sla_status;
+
+/* Per-system outcome of a solve, in sla_cg_info.state (same numbers as the oracle). */
+enum {
+    SLA_CONVERGED = 0,   /* |r_k| <= max(rtol |rhs|, atol) with r_k the recurrence residual */
+    SLA_MAX_ITER = 1,    /* iteration budget reached (always the outcome with SLA_FIXED_ITERS) */
+    SLA_NOT_SPD = 2,     /* p^T A p <= 0: A is not symmetric positive definite */
+    SLA_NAN = 3          /* p^T A p is NaN */
+};
+
+/* sla_csr_create flags */
+#define SLA_SYMMETRIC        1u  /* caller asserts A == A^T exactly: the adjoint reuses A */
+#define SLA_EAGER_TRANSPOSE  2u  /* build the transposed pattern now instead of on first need */
+
+/* sla_cg_opts.flags */
+#define SLA_FIXED_ITERS      1u  /* skip the residual test: run exactly max_iter iterations */
+
+typedef struct sla_csr sla_csr;   /* opaque handle: one sparsity pattern */
+
+typedef struct {
+    double rtol;                 /* relative tolerance on |r| / |rhs| (>= 0) */
+    double atol;                 /* absolute tolerance on |r| (>= 0) */
+    int64_t max_iter;            /* iteration budget (>= 0) */
+    int32_t check_every;         /* iterations between host polls of the stop counter (0 = default 32) */
+    uint32_t flags;              /* SLA_FIXED_ITERS */
+    double* residual_history;    /* device, nullable: [batch][max_iter + 1], entry k = |r_k| */
+} sla_cg_opts;
+
+typedef struct {
+    int64_t iterations;          /* number of products A p performed */
+    double res_norm;             /* |r| of the recurrence residual at exit */
+    double rhs_norm;             /* |b| (forward) or |dL/dx| (backward) */
+    int32_t state;               /* SLA_CONVERGED, SLA_MAX_ITER, SLA_NOT_SPD or SLA_NAN */
+    int32_t reserved;
+} sla_cg_info;                   /* 32 bytes; device arrays of these have one entry per system */
+
+/*
+ * Create a handle for an n_rows x n_cols CSR pattern (paperpeel section
+ * "Operator representation": explicit val/row/col storage).
+ *   d_row_ptr  device, n_rows + 1 entries of int32 (row_ptr_bits = 32) or int64 (64);
+ *              d_row_ptr[0] = 0, non-decreasing, d_row_ptr[n_rows] = nnz.
+ *   d_col_idx  device int32 [nnz], strictly ascending within each row, in [0, n_cols).
+ * The pattern is validated on the device (one pass and one host synchronisation
+ * on `stream`); a malformed pattern returns SLA_ERR_INVALID_CSR and no handle.
+ * The analysis (per-tile entry counts that pick the SpMV variant) is computed here.
+ * n_rows, n_cols < 2^31; nnz < 2^31 with 32-bit row pointers.  nnz may be 0.
+ */
+sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                          const void* d_row_ptr, int32_t row_ptr_bits, const int32_t* d_col_idx,
+                          uint32_t flags, void* stream);
+
+/* Destroy a handle and free everything the library allocated for it (synchronises the device). */
+sla_status sla_csr_destroy(sla_csr* A);
+
+/* Shape and workspace queries (host outputs; any pointer may be NULL). */
+sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int64_t* nnz,
+                        int32_t* row_ptr_bits, uint32_t* flags, int64_t* workspace_bytes);
+
+/*
+ * y = A x for `batch` systems sharing the pattern (paperpeel section 3.3: the
+ * SpMV; section 3.1: .matvec).
+ *   d_vals [batch][nnz], d_x [batch][n_cols], d_y [batch][n_rows] (device, fp64).
+ * Row i is summed over its stored entries in ascending position order.
+ */
+sla_status sla_matvec(const sla_csr* A, int64_t batch, const double* d_vals, const double* d_x,
+                      double* d_y, void* stream);
+
+/*
+ * Backward of y = A x: d_gx = A^T gy (nullable) and d_gvals[k] = gy[row(k)] * x[col(k)]
+ * (nullable), per system.  A^T is A when the handle is SLA_SYMMETRIC, otherwise the
+ * transposed pattern (built on first need).
+ *   d_gy [batch][n_rows], d_gx [batch][n_cols], d_gvals [batch][nnz].
+ */
+sla_status sla_matvec_backward(const sla_csr* A, int64_t batch, const double* d_vals,
+                               const double* d_x, const double* d_gy, double* d_gx,
+                               double* d_gvals, void* stream);
+
+/*
+ * Solve A x = b by unpreconditioned conjugate gradients from x0 = 0, for `batch`
+ * independent systems sharing the pattern (paperpeel sections 1, 3.1, 3.3).
+ *   d_vals [batch][nnz], d_b [batch][n], d_x [batch][n] (output), d_info [batch] (output).
+ * Each iteration: q = A p, sigma = p^T q, alpha = rho / sigma, x += alpha p,
+ * r -= alpha q, rho' = r^T r, stop test, beta = rho' / rho, p = r + beta p.
+ * Each system stops on its own test (|r| <= max(rtol |b|, atol)), at max_iter, or
+ * on a breakdown (sigma <= 0 or NaN: x is the iterate before that step).  No host
+ * synchronisation happens inside an iteration: scalars and stop decisions live on
+ * the device.  Requires n_rows == n_cols.  b = 0 gives x = 0 after 0 iterations.
+ */
+sla_status sla_solve(const sla_csr* A, int64_t batch, const double* d_vals, const double* d_b,
+                     double* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
+
+/*
+ * Adjoint backward pass of x = A^{-1} b (gist.science summaries, Methodology item 2;
+ * paperpeel section 3.2.3): solve A^T lambda = dL/dx with the same CG and options
+ * (threshold relative to |dL/dx|), then
+ *   d_gb[b][i]    = lambda_b[i]                       (dL/db)
+ *   d_gvals[b][k] = -lambda_b[row(k)] * x_b[col(k)]   (dL/dA on the pattern; nullable)
+ *   d_x  [batch][n]  the forward solution (saved by the caller)
+ *   d_gx [batch][n]  dL/dx
+ * A^T is A for SLA_SYMMETRIC handles, else the transposed pattern with gathered values.
+ * Memory: O(n + nnz) per system, whatever the iteration count.
+ */
+sla_status sla_solve_backward(const sla_csr* A, int64_t batch, const double* d_vals,
+                              const double* d_x, const double* d_gx, double* d_gb,
+                              double* d_gvals, const sla_cg_opts* opts, sla_cg_info* d_info,
+                              void* stream);
+
+/*
+ * Kernel timing for measurement: while enabled, every kernel the library launches
+ * is bracketed by HIP events on its stream; the elapsed times are accumulated per
+ * kernel when the enclosing call synchronises (sla_solve / sla_solve_backward with
+ * a residual test, or sla_timing_collect).  Disabled by default; enabling it adds
+ * event records between launches.
+ */
+enum {
+    SLA_K_CG_INIT = 0,      /* r0 partial norms, x = 0, per-system state reset */
+    SLA_K_CG_SPMV = 1,      /* p = r + beta p (on the fly), x update, q = A p, partial p^T q */
+    SLA_K_CG_UPDATE = 2,    /* alpha, r -= alpha q, partial r^T r */
+    SLA_K_MATVEC = 3,       /* y = A x */
+    SLA_K_PATTERN_OUTER = 4,/* gvals = s * u[row] * v[col] */
+    SLA_K_GATHER_VALS = 5,  /* transposed values */
+    SLA_K_TRANSPOSE = 6,    /* pattern transpose (all its kernels) */
+    SLA_K_COUNT = 7
+};
+sla_status sla_timing_enable(int32_t enable);
+sla_status sla_timing_reset(void);
+sla_status sla_timing_collect(void);    /* synchronises pending timed launches */
+sla_status sla_timing_query(int32_t kernel, int64_t* launches, double* total_ms);
+
+const char* sla_status_string(sla_status s);
+const char* sla_last_error(void);
+int32_t sla_version(void);             /* 100 * major + minor */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLA_H */

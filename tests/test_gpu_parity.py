@@ -1,0 +1,364 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (from the parity contract of this library):
+  SpMV                 bit-exact with the oracle where both sum a row in ascending
+                       entry order (every LDS-staged tile); tiles above the LDS cap
+                       use a tree order and must sit within the rounding bound.
+  CG solution          relative L2 difference <= 1e-9; iteration count within 2 %.
+  lambda, dL/dvals     relative L2 difference <= 1e-8.
+  integer / index work bit-exact (transposed pattern, gradient scatter from equal inputs).
+Sizes span several 256-row tiles with a ragged tail; the 64 x 64 Poisson case is the
+small benchmark workload itself.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+EPS = np.finfo(np.float64).eps
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import differentiable_sparse_linear_spmv_amd as S
+    return S
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def handle(S, A, symmetric=True, index64=False):
+    rp = A.row_ptr.astype(np.int64 if index64 else np.int32)
+    return S.csr_create(dev(rp), dev(A.col.astype(np.int32)), n_cols=A.n_cols, symmetric=symmetric)
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def iters_close(k_gpu, k_orc):
+    return abs(k_gpu - k_orc) <= math.floor(0.02 * k_orc)
+
+
+def rows_of(A):
+    return np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+
+
+# ------------------------------------------------------------------------------------- SpMV
+CASES = {
+    "poisson64": lambda: W.poisson5(64),
+    "poisson37_ragged": lambda: W.poisson5(37),
+    "varcoef50": lambda: W.varcoef_poisson5(50, seed=3)[0],
+    "fem30x3": lambda: W.fem_p1_batched(nv=30, B=3, seed=2)[0],
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("index64", [False, True])
+def test_spmv_bitexact(S, name, index64):
+    A = CASES[name]()
+    rng = np.random.default_rng(7)
+    B = A.batch
+    h = handle(S, A, symmetric=True, index64=index64)
+    for kind in ("integer", "normal"):
+        if kind == "integer":
+            x = rng.integers(-2 ** 20, 2 ** 20, (B, A.n_cols)).astype(np.float64)
+        else:
+            x = rng.standard_normal((B, A.n_cols))
+        vals = A.vals.reshape(B, A.nnz)
+        y = host(S.matvec(h, dev(vals), dev(x)))
+        for s in range(B):
+            ref = O.spmv(A, x[s], vals=vals[s])
+            assert np.array_equal(y[s], ref), (name, kind, s)
+
+
+def irregular_matrix(n=1500, long_row=700, long_len=5000, seed=0):
+    """Random pattern with empty rows, a ragged tail and one row far above the LDS cap."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 9, n)
+    lens[rng.choice(n, 40, replace=False)] = 0
+    lens[long_row] = long_len
+    cols = [np.sort(rng.choice(max(n, long_len + 1), ln, replace=False)) for ln in lens]
+    n_cols = max(n, long_len + 1)
+    row_ptr = np.zeros(n + 1, np.int64)
+    np.cumsum(lens, out=row_ptr[1:])
+    col = np.concatenate(cols).astype(np.int32)
+    vals = rng.standard_normal(col.shape[0])
+    return W.CSR(n, n_cols, row_ptr.astype(np.int32), col, vals)
+
+
+def test_spmv_irregular_and_long_rows(S):
+    A = irregular_matrix()
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(A.n_cols)
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), n_cols=A.n_cols)
+    y = host(S.matvec(h, dev(A.vals), dev(x)))
+    ref = O.spmv(A, x)
+    rows = rows_of(A)
+    absum = np.bincount(rows, weights=np.abs(A.vals * x[A.col]), minlength=A.n_rows)
+    lens = np.diff(A.row_ptr)
+    tile_nnz = np.add.reduceat(lens, np.arange(0, A.n_rows, 256))
+    for t, cnt in enumerate(tile_nnz):
+        sl = slice(t * 256, min((t + 1) * 256, A.n_rows))
+        if cnt <= 4096:
+            assert np.array_equal(y[sl], ref[sl]), t
+        else:
+            bound = (lens[sl] + 64) * EPS * absum[sl]
+            assert np.all(np.abs(y[sl] - ref[sl]) <= bound), t
+    assert tile_nnz.max() > 4096   # the wave-per-row path was exercised
+
+
+def test_matvec_backward_nonsymmetric(S):
+    A = W.poisson5(33)
+    rng = np.random.default_rng(2)
+    vals = rng.standard_normal((2, A.nnz))
+    x = rng.standard_normal((2, A.n_cols))
+    gy = rng.standard_normal((2, A.n_rows))
+    for sym in (False,):
+        h = handle(S, A, symmetric=sym)
+        gx, gv = S.matvec_backward(h, dev(vals), dev(x), dev(gy))
+        gx, gv = host(gx), host(gv)
+        for s in range(2):
+            rgx, rgv = O.matvec_backward(A, x[s], gy[s], vals=vals[s])
+            assert np.array_equal(gx[s], rgx)
+            assert np.array_equal(gv[s], rgv)
+    # irregular rectangular pattern through the device transpose
+    I = irregular_matrix(n=900, long_row=10, long_len=50, seed=4)
+    h = S.csr_create(dev(I.row_ptr), dev(I.col), n_cols=I.n_cols)
+    x = rng.standard_normal(I.n_cols)
+    gy = rng.standard_normal(I.n_rows)
+    gx, gv = S.matvec_backward(h, dev(I.vals), dev(x), dev(gy))
+    rgx, rgv = O.matvec_backward(I, x, gy)
+    assert np.array_equal(host(gx), rgx)
+    assert np.array_equal(host(gv), rgv)
+
+
+# ------------------------------------------------------------------------------------- CG
+def run_pair(S, A, b, g_fn, rtol, symmetric=True, max_iter=100000, fixed=False, batch_vals=None):
+    """GPU solve + backward and the oracle's, for every system of the batch."""
+    B = 1 if batch_vals is None else batch_vals.shape[0]
+    vals = A.vals.reshape(B, A.nnz) if batch_vals is None else batch_vals
+    b = b.reshape(B, A.n_rows)
+    h = handle(S, A, symmetric=symmetric)
+    opts = S.cg_opts(rtol=rtol, max_iter=max_iter, fixed=fixed)
+    dv = dev(vals)
+    x, info = S.solve(h, dv, dev(b), opts)
+    xg = host(x)
+    g = np.stack([g_fn(xg[s]) for s in range(B)])
+    gb, gv, binfo = S.solve_backward(h, dv, x, dev(g), opts)
+    out = dict(x=xg, lam=host(gb), gvals=host(gv), info=S.read_info(info),
+               binfo=S.read_info(binfo), vals=vals, b=b, g=g)
+    ref = []
+    for s in range(B):
+        f = O.cg(A, b[s], rtol=rtol, max_iter=max_iter, fixed=fixed, vals=vals[s])
+        # the oracle's backward takes the GPU's x and g so the comparison isolates the adjoint
+        bw = O.solve_backward(A, xg[s], g[s], symmetric=True, rtol=rtol, max_iter=max_iter,
+                              fixed=fixed, vals=vals[s])
+        ref.append((f, bw))
+    return out, ref
+
+
+def check_pair(out, ref, tol_x=1e-9, tol_adj=1e-8):
+    for s, (f, bw) in enumerate(ref):
+        gi, bi = out["info"][s], out["binfo"][s]
+        assert gi["state"] == f["state"], (s, gi, f["state"])
+        assert iters_close(gi["iterations"], f["iterations"]), (s, gi["iterations"], f["iterations"])
+        assert rel(out["x"][s], f["x"]) <= tol_x, (s, rel(out["x"][s], f["x"]))
+        assert bi["state"] == bw["state"]
+        assert iters_close(bi["iterations"], bw["iterations"]), (s, bi["iterations"], bw["iterations"])
+        assert rel(out["lam"][s], bw["lam"]) <= tol_adj, (s, rel(out["lam"][s], bw["lam"]))
+        assert rel(out["gvals"][s], bw["gvals"]) <= tol_adj
+        assert abs(gi["rhs_norm"] - f["rhs_norm"]) <= 1e-13 * f["rhs_norm"]
+
+
+def test_cg_poisson64_config(S):
+    c = W.config("poisson64")
+    out, ref = run_pair(S, c["A"], c["b"], lambda x: x, rtol=c["rtol"])
+    check_pair(out, ref)
+    f = ref[0][0]
+    assert 200 <= f["iterations"] <= 250
+    assert out["info"][0]["res_norm"] <= c["rtol"] * out["info"][0]["rhs_norm"]
+
+
+def test_cg_poisson_ragged_tolerance_1e10(S):
+    A = W.poisson5(45)                        # 2025 rows: 7 full tiles and a ragged tail
+    b = W.rhs_uniform(A.n_rows, 3)
+    out, ref = run_pair(S, A, b, lambda x: x, rtol=1e-10)
+    check_pair(out, ref)
+
+
+def test_cg_varcoef_target_loss(S):
+    A, b, _ = W.varcoef_poisson5(40, seed=0)
+    t = np.random.default_rng(1).uniform(0, 1, A.n_rows)
+    out, ref = run_pair(S, A, b, lambda x: 2.0 * (x - t), rtol=1e-10)
+    check_pair(out, ref)
+
+
+def test_cg_fem_batched(S):
+    A, b = W.fem_p1_batched(nv=20, B=6, seed=0)
+    out, ref = run_pair(S, A, b, lambda x: x, rtol=1e-8, batch_vals=A.vals)
+    check_pair(out, ref)
+    its = [i["iterations"] for i in out["info"]]
+    assert len(set(its)) > 1   # systems stop independently
+
+
+def test_transpose_path_is_bit_identical_on_symmetric_matrix(S):
+    A, b, _ = W.varcoef_poisson5(30, seed=5)
+    x_ = dev(b)
+    res = {}
+    for sym in (True, False):
+        h = handle(S, A, symmetric=sym)
+        opts = S.cg_opts(rtol=1e-10)
+        dv = dev(A.vals)
+        x, _ = S.solve(h, dv, x_, opts)
+        gb, gv, info = S.solve_backward(h, dv, x, x.clone(), opts)
+        res[sym] = (host(x), host(gb), host(gv), S.read_info(info)[0]["iterations"])
+    for a, b2 in zip(res[True], res[False]):
+        assert np.array_equal(np.asarray(a), np.asarray(b2))
+
+
+def test_determinism(S):
+    A, b = W.fem_p1_batched(nv=24, B=3, seed=1)
+    outs = []
+    for _ in range(2):
+        o, _ = run_pair_gpu_only(S, A, b)
+        outs.append(o)
+    for k in ("x", "lam", "gvals"):
+        assert np.array_equal(outs[0][k], outs[1][k])
+
+
+def run_pair_gpu_only(S, A, b):
+    h = handle(S, A)
+    opts = S.cg_opts(rtol=1e-8)
+    dv = dev(A.vals)
+    x, info = S.solve(h, dv, dev(b), opts)
+    gb, gv, _ = S.solve_backward(h, dv, x, x.clone(), opts)
+    return dict(x=host(x), lam=host(gb), gvals=host(gv)), S.read_info(info)
+
+
+# ------------------------------------------------------------------------------ edge cases
+def test_zero_rhs_and_zero_gradient(S):
+    A = W.poisson5(20)
+    h = handle(S, A)
+    opts = S.cg_opts(rtol=1e-10)
+    dv = dev(A.vals)
+    x, info = S.solve(h, dv, dev(np.zeros(A.n_rows)), opts)
+    inf = S.read_info(info)[0]
+    assert inf["iterations"] == 0 and inf["state"] == O.CONVERGED
+    assert not np.any(host(x))
+    gb, gv, binfo = S.solve_backward(h, dv, x, dev(np.zeros(A.n_rows)), opts)
+    assert S.read_info(binfo)[0]["iterations"] == 0
+    assert not np.any(host(gb)) and not np.any(host(gv))
+
+
+def test_budget_and_fixed_iterations(S):
+    A = W.poisson5(24)
+    b = W.rhs_uniform(A.n_rows, 1)
+    h = handle(S, A)
+    dv = dev(A.vals)
+    x, info = S.solve(h, dv, dev(b), S.cg_opts(rtol=1e-10, max_iter=1))
+    inf = S.read_info(info)[0]
+    assert inf["iterations"] == 1 and inf["state"] == O.MAX_ITER
+    ref = O.cg(A, b, rtol=1e-10, max_iter=1)
+    assert rel(host(x), ref["x"]) <= 1e-14
+    hist = torch.full((38,), float("nan"), dtype=torch.float64, device="cuda")
+    x, info = S.solve(h, dv, dev(b), S.cg_opts(rtol=0.0, max_iter=37, fixed=True,
+                                               residual_history=hist))
+    inf = S.read_info(info)[0]
+    assert inf["iterations"] == 37 and inf["state"] == O.MAX_ITER
+    ref = O.cg(A, b, rtol=0.0, max_iter=37, fixed=True, history=True)
+    assert rel(host(x), ref["x"]) <= 1e-12
+    assert np.allclose(host(hist), ref["history"], rtol=1e-10, atol=0)
+
+
+def test_breakdowns(S):
+    A = W.poisson5(16)
+    b = W.rhs_uniform(A.n_rows, 2)
+    h = handle(S, A)
+    opts = S.cg_opts(rtol=1e-10, max_iter=500)
+    x, info = S.solve(h, dev(-A.vals), dev(b), opts)
+    inf = S.read_info(info)[0]
+    assert inf["state"] == O.NOT_SPD and inf["iterations"] == 0 and not np.any(host(x))
+    bad = A.vals.copy()
+    bad[11] = np.nan
+    x, info = S.solve(h, dev(bad), dev(b), opts)
+    assert S.read_info(info)[0]["state"] == O.NAN
+    sh = A.vals.copy()
+    sh[rows_of(A) == A.col] -= 4.0   # indefinite
+    x, info = S.solve(h, dev(sh), dev(b), opts)
+    inf = S.read_info(info)[0]
+    ref = O.cg(A, b, rtol=1e-10, max_iter=500, vals=sh)
+    assert inf["state"] == ref["state"] == O.NOT_SPD
+
+
+def test_batched_mixed_outcomes(S):
+    # one batch, four systems: converges, b = 0, not SPD, and an eigenvector (1 step)
+    A = W.poisson5(16)
+    n = A.n_rows
+    vals = np.stack([A.vals, A.vals, -A.vals, A.vals])
+    i = np.arange(1, 17)
+    v = np.outer(np.sin(2 * np.pi * i / 17), np.sin(3 * np.pi * i / 17)).reshape(-1)
+    b = np.stack([W.rhs_uniform(n, 0), np.zeros(n), W.rhs_uniform(n, 1), v])
+    h = handle(S, A)
+    x, info = S.solve(h, dev(vals), dev(b), S.cg_opts(rtol=1e-10))
+    inf = S.read_info(info)
+    assert [s["state"] for s in inf] == [O.CONVERGED, O.CONVERGED, O.NOT_SPD, O.CONVERGED]
+    assert inf[1]["iterations"] == 0 and inf[2]["iterations"] == 0 and inf[3]["iterations"] == 1
+    ref = O.cg(A, b[0], rtol=1e-10)
+    assert rel(host(x)[0], ref["x"]) <= 1e-9
+
+
+def test_invalid_csr_is_rejected(S):
+    A = W.poisson5(8)
+    bad_col = A.col.copy()
+    bad_col[5] = 10 ** 6
+    with pytest.raises(S.SlaError, match="INVALID_CSR"):
+        S.csr_create(dev(A.row_ptr), dev(bad_col))
+    unsorted = A.col.copy()
+    unsorted[[0, 1]] = unsorted[[1, 0]]
+    with pytest.raises(S.SlaError, match="INVALID_CSR"):
+        S.csr_create(dev(A.row_ptr), dev(unsorted))
+    rp = A.row_ptr.copy()
+    rp[-1] += 1
+    with pytest.raises(S.SlaError, match="INVALID_CSR"):
+        S.csr_create(dev(rp), dev(A.col))
+
+
+# ------------------------------------------------------------------------------- autograd
+def test_autograd_solve_and_matvec(S):
+    A, b, _ = W.varcoef_poisson5(24, seed=2)
+    t = np.random.default_rng(3).uniform(0, 1, A.n_rows)
+    vals = dev(A.vals).requires_grad_(True)
+    bb = dev(b).requires_grad_(True)
+    T = S.SparseTensor(dev(A.row_ptr), dev(A.col), vals, symmetric=True)
+    x = T.solve(bb, rtol=1e-12, check=True)
+    loss = ((x - dev(t)) ** 2).sum()
+    loss.backward()
+    f = O.cg(A, b, rtol=1e-12)
+    bw = O.solve_backward(A, f["x"], 2 * (f["x"] - t), rtol=1e-12)
+    assert rel(host(bb.grad), bw["lam"]) <= 1e-8
+    assert rel(host(vals.grad), bw["gvals"]) <= 1e-8
+    # matvec: y = A x, L = <w, y>
+    w = np.random.default_rng(4).standard_normal(A.n_rows)
+    xv = dev(t).requires_grad_(True)
+    vals.grad = None
+    y = T.matvec(xv)
+    (y * dev(w)).sum().backward()
+    gx, gv = O.matvec_backward(A, t, w)
+    assert np.array_equal(host(xv.grad), gx)
+    assert np.array_equal(host(vals.grad), gv)
