@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark: fp64 CG iterations/s and achieved HBM bandwidth of the sparse CG
+solve + adjoint backward on one MI355X.
+
+One step = one pass of the whole hot path on one batch of synthetic input:
+    x = A^{-1} b by conjugate gradients (sla_solve), then the adjoint backward of
+    L = 0.5 |x|^2 (sla_solve_backward: A^T lambda = x, dL/db = lambda,
+    dL/dA_ij = -lambda_i x_j on the pattern).
+The default workload is the 1024 x 1024 5-point Poisson system (n = 1,048,576,
+nnz = 5,238,784, b ~ N(0, 1) seed 0, relative residual 1e-8), a stand-in for the
+1M-DOF 2-D Poisson benchmark of the torch-sla paper (paperpeel page, section 4.1,
+Table 3).  Inputs are resident in HBM before the timed region starts.
+
+Printed: one JSON line with value = CG iterations per second (forward + adjoint
+iterations of all timed steps / wall time), the roofline of the dominant kernel
+(algorithmic bytes per launch / HIP-event-timed average launch duration), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+Profiling helpers (used to make the summaries under profiles/):
+    --calibrate-copy      also run a plain device copy of known size (counter scaling)
+    --summarize-pmc DIR   turn rocprofv3 counter CSVs under DIR into a traffic summary
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "fp64 CG iters/s + achieved HBM GB/s, Poisson 1M/169M DOF; solve+adjoint ms"
+COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "differentiable_sparse_linear_spmv_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------------------ bytes model
+def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
+    """Algorithmic HBM bytes of the kernels, per launch (all systems of the batch).
+
+    rp_bytes is the width of the row pointers the kernels read: 4 whenever nnz < 2^31
+    (the library keeps a 32-bit copy of 64-bit row pointers that fit).
+
+    cg_spmv : values 8 nnz B + columns 4 nnz + row pointers rp (n + 1)
+              + vectors: read r, p_{k-1}, x; write p_k, q, x  -> 6 x 8 n B
+    cg_update: read r, q; write r                             -> 3 x 8 n B
+    One CG iteration = both (nine vector passes).
+    """
+    spmv = 8 * nnz * batch + 4 * nnz + rp_bytes * (n + 1) + 6 * 8 * n * batch
+    upd = 3 * 8 * n * batch
+    return dict(cg_spmv=spmv, cg_update=upd, iteration=spmv + upd,
+                flops_iteration=(2 * nnz + 10 * n) * batch)
+
+
+# ------------------------------------------------------------------------------ workloads
+def make_workload(name: str, device):
+    import numpy as np
+    import torch
+    import workloads as W
+
+    if name == "poisson13000":
+        c = W.config(name)
+        N = c["N"]
+        rp, col, vals = W.poisson5_torch(N, device, index64=True)
+        b = torch.from_numpy(W.rhs_normal(N * N, 0)).to(device)
+        return dict(name=name, n=N * N, nnz=col.numel(), batch=1, rp=rp, col=col, vals=vals, b=b,
+                    rtol=0.0, max_iter=c["max_iter"], fixed=True, loss="half_sq", host=None,
+                    desc=f"5-point Poisson {N}x{N}, int64 row_ptr, b~N(0,1) seed 0, "
+                         f"{c['max_iter']} fixed CG iterations + {c['max_iter']} adjoint")
+    c = W.config(name)
+    A = c["A"]
+    B = A.batch
+    vals = torch.from_numpy(np.ascontiguousarray(A.vals.reshape(B, A.nnz) if B > 1 else A.vals))
+    b = torch.from_numpy(np.ascontiguousarray(c["b"]))
+    out = dict(name=name, n=A.n_rows, nnz=A.nnz, batch=B,
+               rp=torch.from_numpy(A.row_ptr).to(device), col=torch.from_numpy(A.col).to(device),
+               vals=vals.to(device), b=b.to(device), rtol=c["rtol"], max_iter=c["max_iter"],
+               fixed=False, loss=c["loss"], host=c)
+    out["x_target"] = (torch.from_numpy(c["x_target"]).to(device) if "x_target" in c else None)
+    descs = {
+        "poisson64": "5-point Poisson 64x64 (n=4096), b~U[-1,1] seed 0, CG to 1e-10 + adjoint",
+        "poisson1024": "5-point Poisson 1024x1024 (n=1048576, nnz=5238784), b~N(0,1) seed 0, "
+                       "CG to 1e-8 + adjoint of 0.5|x|^2",
+        "varcoef2048": "variable-coefficient Poisson 2048x2048, kappa=exp(GRF), CG to 1e-8 + adjoint",
+        "fem256x256": "256 P1 FEM systems on a jittered 256x256-vertex mesh, CG to 1e-8 + adjoint",
+    }
+    out["desc"] = descs[name]
+    return out
+
+
+def loss_grad(w, x):
+    if w["loss"] == "sq_target":
+        return 2.0 * (x - w["x_target"])
+    return x.clone()
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, iters: int) -> dict:
+    """The oracle as it stands (single-threaded C), on a bounded sample of the workload."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+
+    if w["host"] is None:      # the 169M case: sample a 2048 x 2048 grid of the same stencil
+        A = W.poisson5(2048)
+        b = W.rhs_normal(A.n_rows, 0)
+        vals = None
+        sample = (f"oracle CG on the same 5-point stencil at 2048x2048 (169M rows do not fit a "
+                  f"bounded CPU sample), {iters} fixed iterations + {iters} adjoint")
+    else:
+        A = w["host"]["A"]
+        b = w["host"]["b"].reshape(A.batch, A.n_rows)[0]
+        vals = A.vals.reshape(A.batch, A.nnz)[0]
+        sample = (f"oracle CG on system 0 of this workload, {iters} fixed iterations + "
+                  f"{iters} adjoint iterations (single thread)")
+    t0 = time.perf_counter()
+    f = O.cg(A, b, rtol=0.0, max_iter=iters, fixed=True, vals=vals)
+    O.solve_backward(A, f["x"], f["x"], symmetric=True, rtol=0.0, max_iter=iters, fixed=True,
+                     vals=vals)
+    dt = time.perf_counter() - t0
+    return dict(value=round(2 * iters / dt, 3), unit="CG iters/s", cores=1, kind="oracle",
+                sample=sample, seconds=round(dt, 2))
+
+
+# ------------------------------------------------------------------------------ traffic
+def read_traffic(workload: str):
+    p = os.path.join(ROOT, "profiles", f"cg_spmv_{workload}_traffic.txt")
+    if not os.path.exists(p):
+        return None, "no counter summary"
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return t.get("bytes_per_launch"), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the calibration copy.
+
+    Per kernel, the median over its dispatches (a fixed-iteration run: every dispatch
+    but the final stop one does the same work).  The copy is the last three
+    __amd_rocclr_copyBuffer dispatches: the --calibrate-copy device copies of 1 GiB
+    (run after everything else).
+    """
+    import csv
+    import statistics
+
+    def load(d, counter):
+        rows = []
+        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(p) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return sorted(rows)
+
+    def per_kernel(rows, key):
+        v = [val for _, name, val in rows if key in name]
+        return (statistics.median(v), len(v)) if v else (None, 0)
+
+    def copy_of(rows):
+        # the calibration copies are the last three device copies of the run
+        v = [val for _, name, val in rows if "copyBuffer" in name][-3:]
+        return statistics.median(v) if v else None
+
+    fr, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_f, copy_w = copy_of(fr), copy_of(wr)
+    spmv_f, nf = per_kernel(fr, "k_cg_spmv")
+    spmv_w, nw = per_kernel(wr, "k_cg_spmv")
+    upd_f, _ = per_kernel(fr, "k_cg_update")
+    upd_w, _ = per_kernel(wr, "k_cg_update")
+    kib = 1024.0
+    sf = COPY_BYTES / (copy_f * kib) if copy_f else 1.0
+    sw = COPY_BYTES / (copy_w * kib) if copy_w else 1.0
+    cmd = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o p --output-format csv -- "
+           f"python -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
+           "--calibrate-copy --fixed-iters 12; then python bench.py --workload "
+           f"{workload} --summarize-pmc <fetch dir> <write dir>")
+    out = dict(workload=workload, command=cmd, kernel_source_hash=kernel_source_hash(),
+               fetch_kib_per_launch=spmv_f, write_kib_per_launch=spmv_w, launches=[nf, nw],
+               copy_fetch_kib=copy_f, copy_write_kib=copy_w, fetch_scale=sf, write_scale=sw,
+               bytes_per_launch=(spmv_f * kib * sf + spmv_w * kib * sw) if spmv_f and spmv_w else None,
+               update_bytes_per_launch=(upd_f * kib * sf + upd_w * kib * sw) if upd_f and upd_w else None)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    p = os.path.join(ROOT, "profiles", f"cg_spmv_{workload}_traffic.txt")
+    with open(p, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+# ------------------------------------------------------------------------------ main
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="poisson1024",
+                    choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000"])
+    ap.add_argument("--cpu-iters", type=int, default=300)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--fixed-iters", type=int, default=0,
+                    help="profiling runs: exactly this many CG iterations per solve")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import differentiable_sparse_linear_spmv_amd as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(args.workload, dev)
+    n, nnz, B = w["n"], w["nnz"], w["batch"]
+    rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
+    h = S.csr_create(w["rp"], w["col"], symmetric=True)
+    if args.fixed_iters > 0:
+        w["max_iter"], w["fixed"], w["rtol"] = args.fixed_iters, True, 0.0
+    opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"])
+    vals, b = w["vals"], w["b"]
+
+    def step():
+        x, info = S.solve(h, vals, b, opts)
+        g = loss_grad(w, x)
+        gb, gv, binfo = S.solve_backward(h, vals, x, g, opts)
+        return x, gb, gv, info, binfo
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    infos = []
+    for _ in range(args.steps):
+        _, _, _, info, binfo = step()
+        infos.append((info, binfo))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    fwd_it = [sum(s["iterations"] for s in S.read_info(i)) for i, _ in infos]
+    bwd_it = [sum(s["iterations"] for s in S.read_info(bi)) for _, bi in infos]
+    max_fwd = max(s["iterations"] for s in S.read_info(infos[-1][0]))
+    max_bwd = max(s["iterations"] for s in S.read_info(infos[-1][1]))
+    total_it = sum(fwd_it) + sum(bwd_it)
+    # iterations of the batch advance together: count per-system iterations for batch > 1
+    value = total_it / wall
+    ms_step = 1e3 * wall / args.steps
+
+    # Dominant-kernel timing: the same solve + backward once more with per-launch HIP
+    # events on the library's stream, fixed at the measured iteration counts so every
+    # timed launch is a working one.
+    S.timing.reset()
+    S.timing.enable(True)
+    fo = S.cg_opts(rtol=0.0, max_iter=max_fwd, fixed=True)
+    bo = S.cg_opts(rtol=0.0, max_iter=max_bwd, fixed=True)
+    x, _ = S.solve(h, vals, b, fo)
+    S.solve_backward(h, vals, x, loss_grad(w, x), bo)
+    S.timing.collect()
+    S.timing.enable(False)
+    tq = S.timing.query()
+    torch.cuda.synchronize()
+
+    bm = bytes_model(n, nnz, B, rp_bytes)
+    spmv_ms = tq["cg_spmv"]["total_ms"] / max(tq["cg_spmv"]["launches"], 1)
+    upd_ms = tq["cg_update"]["total_ms"] / max(tq["cg_update"]["launches"], 1)
+    achieved = bm["cg_spmv"] / (spmv_ms * 1e-3) / 1e9
+    traffic, traffic_src = read_traffic(args.workload)
+    iter_gbps = bm["iteration"] / ((spmv_ms + upd_ms) * 1e-3) / 1e9
+    wall_gbps = bm["iteration"] * (total_it / B) / wall / 1e9
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if rank == 0 and not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_iters)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "CG iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w["desc"], "n": n, "nnz": nnz, "batch": B,
+                   "row_ptr": f"int{8 * rp_bytes}", "rtol": w["rtol"],
+                   "fixed_iterations": w["fixed"], "parallelism": "none (1 GPU)"},
+        "iterations_per_step": {"forward": fwd_it[-1], "adjoint": bwd_it[-1]},
+        "solve_adjoint_ms": round(ms_step, 4),
+        "hbm_gbps_per_iteration": round(iter_gbps, 1),
+        "hbm_gbps_wall": round(wall_gbps, 1),
+        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),
+        "kernels": {k: {"launches": v["launches"],
+                        "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
+                    for k, v in tq.items() if v["launches"]},
+        "bytes_model": bm,
+        "roofline": {"bound": "hbm", "kernel": "k_cg_spmv", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "traffic_source": traffic_src,
+                     "bytes_per_launch": bm["cg_spmv"], "avg_launch_us": round(1e3 * spmv_ms, 3)},
+        "cpu_baseline": cpu,
+    }
+    if rank == 0:
+        print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

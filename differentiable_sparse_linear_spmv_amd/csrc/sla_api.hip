@@ -31,6 +31,11 @@ struct sla_csr {
     uint32_t flags = 0;
     const void* row_ptr = nullptr;
     const int32_t* col = nullptr;
+    // Row pointers the kernels read: the caller's, or an owned 32-bit copy of 64-bit
+    // row pointers when nnz < 2^31 (4 bytes per row less traffic in every SpMV).
+    const void* krp = nullptr;
+    int32_t krp_bits = 32;
+    void* rp_owned = nullptr;
     int device = 0;
     int n_cu = 256;
     int cap = kCapSmall;        // LDS variant for A
@@ -96,8 +101,10 @@ hipEvent_t pool_get()
     return e;
 }
 
+// Time what f() enqueues.  single: f launches exactly one kernel, whose own start
+// and end are recorded (hipExtLaunchKernelGGL events); otherwise events bracket f.
 template <class F>
-hipError_t timed(int kid, hipStream_t s, F&& f)
+hipError_t timed(int kid, hipStream_t s, F&& f, bool single = true)
 {
     bool on;
     {
@@ -112,9 +119,16 @@ hipError_t timed(int kid, hipStream_t s, F&& f)
         b = pool_get();
     }
     if (!a || !b) return f();
-    (void)hipEventRecord(a, s);
-    hipError_t e = f();
-    (void)hipEventRecord(b, s);
+    hipError_t e;
+    if (single) {
+        launch_events() = LaunchEvents{a, b};
+        e = f();
+        launch_events() = LaunchEvents{};
+    } else {
+        (void)hipEventRecord(a, s);
+        e = f();
+        (void)hipEventRecord(b, s);
+    }
     std::lock_guard<std::mutex> lk(g_tmu);
     g_pending.push_back({kid, a, b});
     return e;
@@ -176,10 +190,12 @@ int choose_cap(int32_t tile_max)
 
 constexpr size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// Workgroups per system: about 8 resident workgroups per CU over the whole grid.
-int blocks_per_system(const sla_csr* A, int64_t ntiles, int64_t batch)
+// Workgroups per system: the grid of the CG kernels fills every CU exactly once
+// (resident workgroups per CU from the occupancy of the SpMV variant in use), so the
+// grid-stride loops have no second, partial wave of workgroups.
+int blocks_per_system(const sla_csr* A, int64_t ntiles, int64_t batch, int per_cu)
 {
-    int64_t target = static_cast<int64_t>(A->n_cu) * 8;
+    int64_t target = static_cast<int64_t>(A->n_cu) * per_cu;
     int64_t g = (target + batch - 1) / batch;
     if (g >= 8) g &= ~int64_t(7);   // a multiple of 8 enables the XCD band mapping
     g = std::min<int64_t>(g, std::max<int64_t>(ntiles, 1));
@@ -244,15 +260,18 @@ sla_status ensure_transpose(sla_csr* A, hipStream_t s)
     if (A->has_t) return SLA_OK;
     void* scratch = nullptr;
     sla_status st;
-    const size_t rpt_bytes = static_cast<size_t>(A->n_cols + 1) * (A->rp_bits == 64 ? 8 : 4);
+    const size_t rpt_bytes = static_cast<size_t>(A->n_cols + 1) * (A->krp_bits == 64 ? 8 : 4);
     if ((st = dev_alloc(&A->row_ptr_t, std::max<size_t>(rpt_bytes, 8))) != SLA_OK) return st;
     if ((st = dev_alloc(reinterpret_cast<void**>(&A->col_t), std::max<size_t>(4 * A->nnz, 4))) != SLA_OK) return st;
     if ((st = dev_alloc(reinterpret_cast<void**>(&A->perm_t), std::max<size_t>(8 * A->nnz, 8))) != SLA_OK) return st;
     if ((st = dev_alloc(&scratch, transpose_scratch_bytes(A->n_rows, A->n_cols, A->nnz))) != SLA_OK) return st;
-    hipError_t e = timed(SLA_K_TRANSPOSE, s, [&] {
-        return launch_transpose(A->row_ptr, A->rp_bits, A->col, A->n_rows, A->n_cols, A->nnz, A->row_ptr_t,
-                                A->col_t, A->perm_t, scratch, s);
-    });
+    hipError_t e = timed(
+        SLA_K_TRANSPOSE, s,
+        [&] {
+            return launch_transpose(A->krp, A->krp_bits, A->col, A->n_rows, A->n_cols, A->nnz, A->row_ptr_t,
+                                    A->col_t, A->perm_t, scratch, s);
+        },
+        false);
     if (e != hipSuccess) {
         (void)hipFree(scratch);
         return fail(SLA_ERR_HIP, "transpose: %s", hipGetErrorString(e));
@@ -263,7 +282,7 @@ sla_status ensure_transpose(sla_csr* A, hipStream_t s)
     int32_t zero2[2] = {0, 0};
     HIP_TRY(hipMemcpyAsync(d_chk, zero2, sizeof(zero2), hipMemcpyHostToDevice, s));
     HIP_TRY(hipStreamSynchronize(s));
-    e = launch_validate(A->row_ptr_t, A->rp_bits, A->col_t, A->n_cols, A->n_rows, A->nnz, d_chk, d_chk + 1, s);
+    e = launch_validate(A->row_ptr_t, A->krp_bits, A->col_t, A->n_cols, A->n_rows, A->nnz, d_chk, d_chk + 1, s);
     if (e != hipSuccess) {
         (void)hipFree(scratch);
         return fail(SLA_ERR_HIP, "transpose analysis: %s", hipGetErrorString(e));
@@ -306,7 +325,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
 {
     const int64_t n = A->n_rows;
     const int64_t ntiles = (n + kTile - 1) / kTile;
-    const int G = blocks_per_system(A, ntiles, batch);
+    const int G = blocks_per_system(A, ntiles, batch, cg_blocks_per_cu(A->krp_bits, cap, n));
     Workspace w;
     sla_status st = ensure_workspace(A, batch, G, &w);
     if (st != SLA_OK) return st;
@@ -337,7 +356,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.G = G;
     a.batch = static_cast<int32_t>(batch);
     a.xcd_remap = 1;
-    const int rp_bits = A->rp_bits;
+    const int rp_bits = A->krp_bits;   // A and its transpose use the same row-pointer width
 
     hipError_t e = timed(SLA_K_CG_INIT, s, [&] { return launch_cg_init(a, s); });
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "cg init launch: %s", hipGetErrorString(e));
@@ -468,6 +487,17 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
     }
     A->tile_max = h[1];
     A->cap = choose_cap(h[1]);
+    A->krp = d_row_ptr;
+    A->krp_bits = row_ptr_bits;
+    if (row_ptr_bits == 64 && nnz < (int64_t(1) << 31)) {
+        if ((st = dev_alloc(&A->rp_owned, sizeof(int32_t) * static_cast<size_t>(n_rows + 1))) != SLA_OK)
+            return bail(st);
+        e = launch_narrow_rp(static_cast<const int64_t*>(d_row_ptr), static_cast<int32_t*>(A->rp_owned), n_rows + 1,
+                             s);
+        if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "row pointer copy: %s", hipGetErrorString(e)));
+        A->krp = A->rp_owned;
+        A->krp_bits = 32;
+    }
     if ((flags & SLA_EAGER_TRANSPOSE) && !(flags & SLA_SYMMETRIC)) {
         std::lock_guard<std::mutex> lk(A->mu);
         if ((st = ensure_transpose(A, s)) != SLA_OK) return bail(st);
@@ -488,6 +518,7 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->row_ptr_t) (void)hipFree(A->row_ptr_t);
     if (A->col_t) (void)hipFree(A->col_t);
     if (A->perm_t) (void)hipFree(A->perm_t);
+    if (A->rp_owned) (void)hipFree(A->rp_owned);
     if (A->flag_host) (void)hipHostFree(A->flag_host);
     for (int i = 0; i < 2; ++i)
         if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);
@@ -508,7 +539,8 @@ sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int6
     if (workspace_bytes_out) {
         int64_t tb = 0;
         if (A->has_t)
-            tb = (A->n_cols + 1) * (A->rp_bits == 64 ? 8 : 4) + 12 * A->nnz;
+            tb = (A->n_cols + 1) * (A->krp_bits == 64 ? 8 : 4) + 12 * A->nnz;
+        if (A->rp_owned) tb += 4 * (A->n_rows + 1);
         *workspace_bytes_out = static_cast<int64_t>(A->ws_bytes + A->vals_t_bytes) + tb;
     }
     return SLA_OK;
@@ -523,7 +555,7 @@ sla_status sla_matvec(const sla_csr* Ac, int64_t batch, const double* d_vals, co
         return fail(SLA_ERR_INVALID_ARG, "NULL array");
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed(SLA_K_MATVEC, s, [&] {
-        return launch_matvec(Ac->row_ptr, Ac->rp_bits, Ac->col, d_vals, d_x, d_y, Ac->n_rows, Ac->nnz, Ac->n_cols,
+        return launch_matvec(Ac->krp, Ac->krp_bits, Ac->col, d_vals, d_x, d_y, Ac->n_rows, Ac->nnz, Ac->n_cols,
                              static_cast<int>(batch), Ac->cap, s);
     });
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "matvec launch: %s", hipGetErrorString(e));
@@ -545,7 +577,7 @@ sla_status sla_matvec_backward(const sla_csr* Ac, int64_t batch, const double* d
         hipError_t e;
         if (A->flags & SLA_SYMMETRIC) {
             e = timed(SLA_K_MATVEC, s, [&] {
-                return launch_matvec(A->row_ptr, A->rp_bits, A->col, d_vals, d_gy, d_gx, A->n_rows, A->nnz,
+                return launch_matvec(A->krp, A->krp_bits, A->col, d_vals, d_gy, d_gx, A->n_rows, A->nnz,
                                      A->n_cols, static_cast<int>(batch), A->cap, s);
             });
         } else {
@@ -553,7 +585,7 @@ sla_status sla_matvec_backward(const sla_csr* Ac, int64_t batch, const double* d
             const double* vt = nullptr;
             if ((st = ensure_vals_t(A, batch, d_vals, s, &vt)) != SLA_OK) return st;
             e = timed(SLA_K_MATVEC, s, [&] {
-                return launch_matvec(A->row_ptr_t, A->rp_bits, A->col_t, vt, d_gy, d_gx, A->n_cols, A->nnz,
+                return launch_matvec(A->row_ptr_t, A->krp_bits, A->col_t, vt, d_gy, d_gx, A->n_cols, A->nnz,
                                      A->n_rows, static_cast<int>(batch), A->cap_t, s);
             });
         }
@@ -561,7 +593,7 @@ sla_status sla_matvec_backward(const sla_csr* Ac, int64_t batch, const double* d
     }
     if (d_gvals) {
         hipError_t e = timed(SLA_K_PATTERN_OUTER, s, [&] {
-            return launch_pattern_outer(A->row_ptr, A->rp_bits, A->col, 1.0, d_gy, A->n_rows, d_x, A->n_cols,
+            return launch_pattern_outer(A->krp, A->krp_bits, A->col, 1.0, d_gy, A->n_rows, d_x, A->n_cols,
                                         d_gvals, A->n_rows, A->nnz, static_cast<int>(batch), s);
         });
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "pattern outer launch: %s", hipGetErrorString(e));
@@ -580,7 +612,7 @@ sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, con
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
-    st = run_cg(A, A->row_ptr, A->col, A->cap, batch, d_vals, d_b, d_x, opts, d_info, s);
+    st = run_cg(A, A->krp, A->col, A->cap, batch, d_vals, d_b, d_x, opts, d_info, s);
     if (st == SLA_OK && !(opts->flags & SLA_FIXED_ITERS)) {
         hipError_t e = timing_collect();
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
@@ -602,7 +634,7 @@ sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
     if (A->flags & SLA_SYMMETRIC) {
-        st = run_cg(A, A->row_ptr, A->col, A->cap, batch, d_vals, d_gx, d_gb, opts, d_info, s);
+        st = run_cg(A, A->krp, A->col, A->cap, batch, d_vals, d_gx, d_gb, opts, d_info, s);
     } else {
         if ((st = ensure_transpose(A, s)) != SLA_OK) return st;
         const double* vt = nullptr;
@@ -612,7 +644,7 @@ sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_
     if (st != SLA_OK) return st;
     if (d_gvals) {
         hipError_t e = timed(SLA_K_PATTERN_OUTER, s, [&] {
-            return launch_pattern_outer(A->row_ptr, A->rp_bits, A->col, -1.0, d_gb, A->n_rows, d_x, A->n_cols,
+            return launch_pattern_outer(A->krp, A->krp_bits, A->col, -1.0, d_gb, A->n_rows, d_x, A->n_cols,
                                         d_gvals, A->n_rows, A->nnz, static_cast<int>(batch), s);
         });
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "gradient scatter launch: %s", hipGetErrorString(e));

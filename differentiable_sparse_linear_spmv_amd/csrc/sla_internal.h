@@ -61,6 +61,18 @@ struct CgArgs {
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
 };
 
+// Optional timing events for the next single-kernel launch: when set, launchers use
+// hipExtLaunchKernelGGL so the events carry the kernel's own start and end times.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+// Resident workgroups per CU of the CG kernels for this pattern variant (the grid
+// of the CG kernels is sized to exactly fill the GPU once).
+int cg_blocks_per_cu(int rp_bits, int cap, int64_t n);
+
 // Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s);
 hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s);
@@ -78,11 +90,13 @@ hipError_t launch_pattern_outer(const void* row_ptr, int rp_bits, const int32_t*
 hipError_t launch_gather_vals(const int64_t* perm, const double* vals, double* out, int64_t nnz,
                               int batch, hipStream_t s);
 
-// CSR checks: writes err[0] != 0 on the first problem found (no early exit) and
-// max entries per tile into tile_max[0].
+// CSR checks: ORs a nonzero code into err[0] on any problem, and records the most
+// entries of any 256-row tile in tile_max[0].  Both counters must be zero on entry.
 hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col, int64_t n_rows,
-                           int64_t n_cols, int64_t nnz, int32_t* err, int32_t* tile_max,
-                           hipStream_t s);
+                           int64_t n_cols, int64_t nnz, int32_t* err, int32_t* tile_max, hipStream_t s);
+
+// out[i] = (int32) in[i] for i < n: 32-bit copy of 64-bit row pointers whose values fit.
+hipError_t launch_narrow_rp(const int64_t* in, int32_t* out, int64_t n, hipStream_t s);
 
 // Transposed pattern: row_ptr_t (same width as rp_bits) [n_cols + 1], col_t [nnz],
 // perm [nnz] (position in A of each entry of A^T).  scratch: see transpose_scratch_bytes.

@@ -29,14 +29,38 @@
 // All arithmetic is built with -ffp-contract=off: every product is rounded before
 // it is added, as in the oracle, so elementwise updates match it exactly and only
 // the order of the dot-product sums differs.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "sla_internal.h"
 
 namespace sla {
+
+LaunchEvents& launch_events()
+{
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+
+// Launch through hipExtLaunchKernelGGL when timing events are armed for this launch.
+#define SLA_LAUNCH(kernel, grid, block, shmem, stream, ...)                                          \
+    do {                                                                                             \
+        LaunchEvents& le_ = launch_events();                                                         \
+        if (le_.start)                                                                               \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, le_.start, le_.stop, 0,        \
+                                  __VA_ARGS__);                                                      \
+        else                                                                                         \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                     \
+    } while (0)
+
 namespace {
+
+// Gathers kept in flight per row: the variant for <= 5 entries per row on average
+// takes 5 (one round for 5-point stencils), the wider variants 8.
+constexpr int row_chunk(int cap) { return cap <= kCapSmall ? 5 : 8; }
 
 __device__ __forceinline__ double wave_sum(double v)
 {
@@ -65,14 +89,24 @@ __device__ __forceinline__ double reduce_partials(const double* part, int G, dou
     return block_sum(v, s_red);
 }
 
-// Workgroup -> logical block.  Workgroups are dispatched round-robin over the 8
-// XCDs; with G a multiple of 8, XCD x gets logical blocks [x G/8, (x+1) G/8), so
-// at every grid-stride step it streams one contiguous band of tiles.
-__device__ __forceinline__ int logical_block(int G, int remap)
+// Tiles of one workgroup.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup b runs on XCD b % 8).  With the XCD mapping each XCD owns one contiguous
+// eighth [lo, lo + len) of the tiles, and its G/8 workgroups take the positions
+// first, first + step, ... < len of that range, so they sweep through it together.
+struct TileRange {
+    int64_t lo, len, first, step;
+};
+
+__device__ __forceinline__ TileRange tile_range(int G, int64_t ntiles, int remap)
 {
     const int bx = blockIdx.x;
-    if (remap && (G & 7) == 0) return (bx & 7) * (G >> 3) + (bx >> 3);
-    return bx;
+    if (remap && (G & 7) == 0 && G >= 16) {
+        const int x = bx & 7;
+        const int64_t lo = (ntiles * x) >> 3;
+        const int64_t hi = (ntiles * (x + 1)) >> 3;
+        return TileRange{lo, hi - lo, bx >> 3, G >> 3};
+    }
+    return TileRange{0, ntiles, bx, G};
 }
 
 template <typename RP>
@@ -81,29 +115,56 @@ __device__ __forceinline__ int64_t ld_rp(const RP* rp, int64_t i)
     return static_cast<int64_t>(rp[i]);
 }
 
-// Gathered operand of the CG SpMV: p_k[c] = r_k[c] + beta * p_{k-1}[c]; p_0 = b.
+// Row pointer at a workgroup-uniform index, read through the constant address space
+// so it becomes a scalar load: its wait counts on the scalar counter and does not
+// drain the vector loads in flight.  The row pointers are never written by a kernel.
+template <typename RP>
+__device__ __forceinline__ int64_t ld_rp_uniform(const RP* rp, int64_t i)
+{
+    typedef const __attribute__((address_space(4))) RP* cptr;
+    return static_cast<int64_t>(((cptr)(rp))[i]);
+}
+
+// Element c of a vector.  With OFF32 (vectors shorter than 2^29 entries) the address
+// is a uniform 64-bit base plus a 32-bit byte offset, which the compiler maps to one
+// VGPR per gather instead of a 64-bit address pair.
+template <bool OFF32>
+__device__ __forceinline__ double ldv(const double* __restrict__ base, int64_t c)
+{
+    if constexpr (OFF32)
+        return *reinterpret_cast<const double*>(reinterpret_cast<const char*>(base) +
+                                                (static_cast<uint32_t>(c) << 3));
+    else
+        return base[c];
+}
+
+// Gathered operand of the CG SpMV: p_k[c] = r_k[c] + beta * p_{k-1}[c].  For k = 0,
+// r_0 = b, beta = 0 and p_{-1} = 0 (zeroed by k_cg_init), which gives p_0 = b exactly.
+template <bool OFF32>
 struct GatherCG {
     const double* __restrict__ rin;
     const double* __restrict__ pprev;
     double beta;
-    bool first;
     __device__ __forceinline__ double operator()(int64_t c) const
     {
-        const double rv = rin[c];
-        if (first) return rv;
-        const double t = beta * pprev[c];
+        const double rv = ldv<OFF32>(rin, c);
+        const double t = beta * ldv<OFF32>(pprev, c);
         return rv + t;
     }
 };
 
+template <bool OFF32>
 struct GatherX {
     const double* __restrict__ x;
-    __device__ __forceinline__ double operator()(int64_t c) const { return x[c]; }
+    __device__ __forceinline__ double operator()(int64_t c) const { return ldv<OFF32>(x, c); }
 };
 
 // Row sums of one tile [row0, row0 + nr) for lane tid (0 for tid >= nr).  Contains
 // the workgroup barriers of the LDS staging; every thread of the workgroup must call it.
-template <typename RP, int CAP, typename G>
+// Loads are never behind a divergent branch: out-of-range slots re-read a valid
+// address (clamped index) and their contribution is masked, so all loads of a phase
+// are in flight together instead of one memory round trip per entry.
+template <typename RP, int CAP, int RC, typename G>
 __device__ __forceinline__ double tile_rowsum(const RP* __restrict__ rp, const int32_t* __restrict__ col,
                                               const double* __restrict__ vals, int64_t row0, int nr,
                                               const G& g, double* s_val, int32_t* s_col)
@@ -114,47 +175,46 @@ __device__ __forceinline__ double tile_rowsum(const RP* __restrict__ rp, const i
     const int64_t cnt = k1 - k0;
     double s = 0.0;
     if (cnt <= CAP) {
-        constexpr int U = CAP / kBlock;
-        double v[U];
-        int32_t c[U];
+        const int tl = min(tid, nr - 1);
+        const int rs = static_cast<int>(ld_rp(rp, row0 + tl) - k0);
+        const int re = (tid < nr) ? static_cast<int>(ld_rp(rp, row0 + tl + 1) - k0) : rs;
+        if (cnt > 0) {
+            constexpr int U = CAP / kBlock;
+            const double* __restrict__ vb = vals + k0;
+            const int32_t* __restrict__ cb = col + k0;
+            const int last = static_cast<int>(cnt) - 1;
+            double v[U];
+            int32_t c[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = tid + u * kBlock;
-            if (j < cnt) {
-                v[u] = vals[k0 + j];
-                c[u] = col[k0 + j];
+            for (int u = 0; u < U; ++u) {
+                const int j = min(tid + u * kBlock, last);
+                v[u] = vb[j];
+                c[u] = cb[j];
             }
-        }
-        int rs = 0, re = 0;
-        if (tid < nr) {
-            rs = static_cast<int>(ld_rp(rp, row0 + tid) - k0);
-            re = static_cast<int>(ld_rp(rp, row0 + tid + 1) - k0);
-        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = tid + u * kBlock;
-            if (j < cnt) {
-                s_val[j] = v[u];
-                s_col[j] = c[u];
+            for (int u = 0; u < U; ++u) {
+                const int j = tid + u * kBlock;
+                if (j < cnt) {
+                    s_val[j] = v[u];
+                    s_col[j] = c[u];
+                }
             }
         }
         __syncthreads();
-        for (int j0 = rs; j0 < re; j0 += 8) {
-            double av[8], pv[8];
+        for (int j0 = rs; j0 < re; j0 += RC) {
+            double pv[RC];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u;
-                if (j < re) {
-                    av[u] = s_val[j];
-                    pv[u] = g(s_col[j]);
-                }
+            for (int u = 0; u < RC; ++u) {
+                const int j = (j0 + u < re) ? j0 + u : j0;
+                pv[u] = g(s_col[j]);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (j0 + u < re) {
-                    const double t = av[u] * pv[u];
-                    s = s + t;
-                }
+            for (int u = 0; u < RC; ++u) {
+                const bool ok = j0 + u < re;
+                const int j = ok ? j0 + u : j0;
+                const double t = s_val[j] * pv[u];
+                const double sn = s + t;
+                s = ok ? sn : s;
             }
         }
         __syncthreads();
@@ -181,39 +241,135 @@ __device__ __forceinline__ double tile_rowsum(const RP* __restrict__ rp, const i
     return s;
 }
 
+// Row sums of a tile whose entries exceed the LDS cap: wave per row, lanes stride
+// over the row's entries, fixed-order shuffle sum.  Contains workgroup barriers.
+template <typename RP, typename G>
+__device__ __forceinline__ double tile_rowsum_long(const RP* __restrict__ rp, const int32_t* __restrict__ col,
+                                                const double* __restrict__ vals, int64_t row0, int nr,
+                                                const G& g, double* s_q)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    for (int rr = w; rr < nr; rr += kBlock / 64) {
+        const int64_t a = ld_rp(rp, row0 + rr);
+        const int64_t e = ld_rp(rp, row0 + rr + 1);
+        double acc = 0.0;
+        for (int64_t kk = a + lane; kk < e; kk += 64) {
+            const double t = vals[kk] * g(col[kk]);
+            acc = acc + t;
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) s_q[rr] = acc;
+    }
+    __syncthreads();
+    const double s = (tid < nr) ? s_q[tid] : 0.0;
+    __syncthreads();
+    return s;
+}
+
 // ----------------------------------------------------------------------------------
-// CG kernels.  Grid: (G, batch) workgroups of kBlock threads; logical block lb of
-// system `sys` owns tiles lb, lb + G, lb + 2G, ...
+// CG kernels.  Grid: (G, batch) workgroups of kBlock threads; workgroup b of system
+// `sys` owns the tiles of tile_range(); it writes partial sums into slot b.
 // ----------------------------------------------------------------------------------
+constexpr int kStreamUnroll = 4;   // tiles per loop trip of the streaming kernels
+
 __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
 {
     __shared__ double s_red[kBlock / 64];
     const int sys = blockIdx.y;
-    const int lb = logical_block(a.G, a.xcd_remap);
+    const int tid = threadIdx.x;
+    const int lb = blockIdx.x;
+    const TileRange tr = tile_range(a.G, a.ntiles, a.xcd_remap);
     const int64_t off = static_cast<int64_t>(sys) * a.n;
     const double* __restrict__ b = a.b + off;
     double* __restrict__ x = a.x + off;
+    double* __restrict__ pm1 = a.p1 + off;   // p_{-1} = 0
     double rr = 0.0;
-    for (int64_t t = lb; t < a.ntiles; t += a.G) {
-        const int64_t i = t * kTile + threadIdx.x;
-        if (i < a.n) {
-            const double bv = b[i];
-            x[i] = 0.0;
-            const double u = bv * bv;
-            rr = rr + u;
+    for (int64_t m0 = tr.first; m0 < tr.len; m0 += kStreamUnroll * tr.step) {
+        double bv[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t i = (tr.lo + m0 + u * tr.step) * kTile + tid;
+            bv[u] = b[min(i, a.n - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t m = m0 + u * tr.step;
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (m < tr.len && i < a.n) {
+                x[i] = 0.0;
+                pm1[i] = 0.0;
+                const double w = bv[u] * bv[u];
+                rr = rr + w;
+            }
         }
     }
     rr = block_sum(rr, s_red);
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         a.part_rho[static_cast<int64_t>(sys) * a.G + lb] = rr;
         if (lb == 0) a.st[sys].stop_iter = INT64_MAX;
         if (lb == 0 && sys == 0) *a.n_active = a.batch;
     }
 }
 
-template <typename RP, int CAP>
+// Staged data of one tile, held in registers until the tile is processed: its
+// entries (written to LDS then), this lane's row bounds, and this lane's row of the
+// vectors the update needs.  Nothing derived from these loads is computed at staging
+// time, so no wait is forced until the tile is consumed.
+template <typename RP, int U>
+struct TileStage {
+    double v[U];
+    int32_t c[U];
+    RP a0, a1;            // row_ptr[row], row_ptr[row + 1] of this lane's (clamped) row
+    double ri, ppi, xi;   // r_k, p_{k-1}, x_{k-1} at this lane's row
+};
+
+// Issue (without waiting) the loads of tile t.  k0 / k1 are the tile's first and
+// end entry positions (known two tiles ahead).  Indices are clamped so no load sits
+// behind a branch; the tile's entries are staged only if they fit the LDS cap.
+template <typename RP, int CAP, bool OFF32>
+__device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const RP* __restrict__ rp,
+                                           const int32_t* __restrict__ col, const double* __restrict__ vals,
+                                           const double* __restrict__ rin, const double* __restrict__ pprev,
+                                           const double* __restrict__ x, int64_t t, int64_t n, int64_t k0,
+                                           int64_t k1)
+{
+    constexpr int U = CAP / kBlock;
+    const int tid = threadIdx.x;
+    const int64_t row0 = t * kTile;
+    const int nr = static_cast<int>(min(static_cast<int64_t>(kTile), n - row0));
+    const int64_t i = row0 + min(tid, nr - 1);
+    S.a0 = rp[i];
+    S.a1 = rp[i + 1];
+    S.ri = ldv<OFF32>(rin, i);
+    S.ppi = ldv<OFF32>(pprev, i);
+    S.xi = x[i];
+    const int64_t cnt = k1 - k0;
+    if (cnt <= CAP && cnt > 0) {
+        const double* __restrict__ vb = vals + k0;
+        const int32_t* __restrict__ cb = col + k0;
+        const int last = static_cast<int>(cnt) - 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(tid + u * kBlock, last);
+            S.v[u] = vb[j];
+            S.c[u] = cb[j];
+        }
+    }
+}
+
+// k_cg_spmv: one CG iteration's SpMV with everything fused around it.  Tiles are
+// software-pipelined: while the gathers of tile t are in flight, the row pointers
+// and entries of the workgroup's next tile are already loading (and the bounds of
+// the one after), so each tile costs about one memory round trip instead of four.
+// The first tile is staged before the stop check and the reduction of the rho
+// partials, which overlaps the kernel's start-up latency with useful loads.
+template <typename RP, int CAP, bool OFF32>
 __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
 {
+    constexpr int U = CAP / kBlock;
+    constexpr int RC = row_chunk(CAP);
     __shared__ double s_val[CAP];
     __shared__ int32_t s_col[CAP];
     __shared__ double s_red[kBlock / 64];
@@ -221,16 +377,46 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     const int sys = blockIdx.y;
     SysState* st = a.st + sys;
     const int tid = threadIdx.x;
-    // One read per workgroup, so the exit decision is uniform even while this
-    // kernel's leading workgroup may be writing stop_iter = k.
-    if (tid == 0) s_stop = st->stop_iter;
-    __syncthreads();
-    if (s_stop < k) return;   // stopped in an earlier kernel
-    const int lb = logical_block(a.G, a.xcd_remap);
+    const int lb = blockIdx.x;
+    const TileRange tr = tile_range(a.G, a.ntiles, a.xcd_remap);
     const bool lead = (lb == 0 && tid == 0);
     const bool first = (k == 0);
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t n = a.n;
+    const RP* __restrict__ rp = static_cast<const RP*>(a.row_ptr);
+    const int32_t* __restrict__ col = a.col;
+    const double* __restrict__ vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
+    const int64_t ntiles = tr.len;   // positions of this workgroup: tr.first + j * step, below tr.len
+    const int64_t Gs = tr.step;
+    auto tile_of = [&](int64_t m) { return tr.lo + m; };
+    auto tile_k0 = [&](int64_t m) { return ld_rp_uniform(rp, tile_of(m) * kTile); };
+    auto tile_k1 = [&](int64_t m) { return ld_rp_uniform(rp, min((tile_of(m) + 1) * kTile, n)); };
+    const double* __restrict__ rin = (first ? a.b : a.r) + off;          // r_k (r_0 = b)
+    const double* __restrict__ pprev = ((k & 1) ? a.p0 : a.p1) + off;   // p_{k-1}
+    double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;          // p_k
+    double* __restrict__ x = a.x + off;
 
+    int64_t t = tr.first;
+    int64_t k0 = 0, k1 = 0, k0n = 0, k1n = 0;
+    // Two stage buffers used alternately (the loop is unrolled by two), so the
+    // registers of a staged tile are never copied from one buffer to the other.
+    TileStage<RP, U> SA, SB;
+    if (t < ntiles) {
+        k0 = tile_k0(t);
+        k1 = tile_k1(t);
+        stage_tile<RP, CAP, OFF32>(SA, rp, col, vals, rin, pprev, x, tile_of(t), n, k0, k1);
+    }
+    if (t + Gs < ntiles) {
+        k0n = tile_k0(t + Gs);
+        k1n = tile_k1(t + Gs);
+    }
+
+    // One read of the stop word per workgroup (published by the barriers of the
+    // reduction), so the exit decision is uniform even while this kernel's leading
+    // workgroup may be writing stop_iter = k.
+    if (tid == 0) s_stop = st->stop_iter;
     const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.G, a.G, s_red);
+    if (s_stop < k) return;   // stopped in an earlier kernel
     const double res = sqrt(rho_k);
     double thr, rhs;
     if (first) {
@@ -243,10 +429,6 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     }
     if (lead && a.hist) a.hist[static_cast<int64_t>(sys) * (a.max_iter + 1) + k] = res;
 
-    const int64_t off = static_cast<int64_t>(sys) * a.n;
-    const double* __restrict__ pprev = ((k & 1) ? a.p0 : a.p1) + off;   // p_{k-1}
-    double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;          // p_k
-    double* __restrict__ x = a.x + off;
     const double alpha_prev = first ? 0.0 : st->alpha[(k - 1) & 1];
 
     int code = -1;
@@ -255,9 +437,9 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     if (code >= 0) {
         // Stop: apply the deferred update x_k = x_{k-1} + alpha_{k-1} p_{k-1}.
         if (!first) {
-            for (int64_t t = lb; t < a.ntiles; t += a.G) {
-                const int64_t i = t * kTile + tid;
-                if (i < a.n) {
+            for (int64_t m = tr.first; m < tr.len; m += tr.step) {
+                const int64_t i = (tr.lo + m) * kTile + tid;
+                if (i < n) {
                     const double tx = alpha_prev * pprev[i];
                     x[i] = x[i] + tx;
                 }
@@ -283,33 +465,118 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         if (first) { st->thr = thr; st->rhs = rhs; }
     }
 
-    const RP* __restrict__ rp = static_cast<const RP*>(a.row_ptr);
-    const double* __restrict__ vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
-    const double* __restrict__ rin = (first ? a.b : a.r) + off;
     double* __restrict__ q = a.q + off;
-    GatherCG g{rin, pprev, beta, first};
+    GatherCG<OFF32> g{rin, pprev, beta};
     double sig = 0.0;
-    for (int64_t t = lb; t < a.ntiles; t += a.G) {
-        const int64_t row0 = t * kTile;
-        const int nr = static_cast<int>(min(static_cast<int64_t>(kTile), a.n - row0));
-        const double s = tile_rowsum<RP, CAP>(rp, a.col, vals, row0, nr, g, s_val, s_col);
+    // Process tile t from stage `cur` while staging the next tile into `nxt`.
+    auto process = [&](TileStage<RP, U>& cur, TileStage<RP, U>& nxt) {
+        const int64_t tn = t + Gs;
+        const int64_t row0 = tile_of(t) * kTile;
+        const int nr = static_cast<int>(min(static_cast<int64_t>(kTile), n - row0));
+        const int64_t i = row0 + min(tid, nr - 1);
+        const int64_t cnt = k1 - k0;
+        int64_t k0nn = 0, k1nn = 0;
+        if (tn + Gs < ntiles) {
+            k0nn = tile_k0(tn + Gs);
+            k1nn = tile_k1(tn + Gs);
+        }
+        double s = 0.0;
+        const double ri = cur.ri, ppi = cur.ppi, xi = cur.xi;
+        if (cnt <= CAP) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = tid + u * kBlock;
+                if (j < cnt) {
+                    s_val[j] = cur.v[u];
+                    s_col[j] = cur.c[u];
+                }
+            }
+            const int rs = static_cast<int>(static_cast<int64_t>(cur.a0) - k0);
+            const int re = (tid < nr) ? static_cast<int>(static_cast<int64_t>(cur.a1) - k0) : rs;
+            __syncthreads();
+            // Gathers of the row's first RC entries are issued before the next tile's
+            // prefetch: the vector-memory counter completes in order, so waiting for
+            // them does not wait for the prefetch.  Slots past the row's end gather
+            // the lane's own row (a valid address) and are masked below.
+            double pv[RC];
+#pragma unroll
+            for (int u = 0; u < RC; ++u) {
+                const int64_t c = (rs + u < re) ? static_cast<int64_t>(s_col[rs + u]) : i;
+                pv[u] = g(c);
+            }
+            if (tn < ntiles) stage_tile<RP, CAP, OFF32>(nxt, rp, col, vals, rin, pprev, x, tile_of(tn), n, k0n, k1n);
+#pragma unroll
+            for (int u = 0; u < RC; ++u) {
+                const bool ok = rs + u < re;
+                const double tt = s_val[ok ? rs + u : rs] * pv[u];
+                const double sn = s + tt;
+                s = ok ? sn : s;
+            }
+#pragma unroll 1
+            for (int j0 = rs + RC; j0 < re; j0 += RC) {   // rows longer than RC entries
+                double pw[RC];
+#pragma unroll
+                for (int u = 0; u < RC; ++u) {
+                    const int j = (j0 + u < re) ? j0 + u : j0;
+                    pw[u] = g(s_col[j]);
+                }
+#pragma unroll
+                for (int u = 0; u < RC; ++u) {
+                    const bool ok = j0 + u < re;
+                    const int j = ok ? j0 + u : j0;
+                    const double tt = s_val[j] * pw[u];
+                    const double sn = s + tt;
+                    s = ok ? sn : s;
+                }
+            }
+            __syncthreads();
+        } else {
+            s = tile_rowsum_long(rp, col, vals, row0, nr, g, s_val);
+            if (tn < ntiles) stage_tile<RP, CAP, OFF32>(nxt, rp, col, vals, rin, pprev, x, tile_of(tn), n, k0n, k1n);
+        }
         if (tid < nr) {
-            const int64_t i = row0 + tid;
-            const double pi = g(i);
+            const double tp = beta * ppi;
+            const double pi = ri + tp;           // same expression as the gathered p_k
             pcur[i] = pi;
             q[i] = s;
-            if (!first) {
-                const double tx = alpha_prev * pprev[i];
-                x[i] = x[i] + tx;
-            }
+            const double tx = alpha_prev * ppi;   // alpha_{-1} = 0 for k = 0
+            x[i] = xi + tx;
             const double u = pi * s;
             sig = sig + u;
         }
+        k0 = k0n;
+        k1 = k1n;
+        k0n = k0nn;
+        k1n = k1nn;
+        t = tn;
+    };
+#pragma unroll 1
+    while (t < ntiles) {
+        process(SA, SB);
+        if (t >= ntiles) break;
+        process(SB, SA);
     }
     sig = block_sum(sig, s_red);
     if (tid == 0) a.part_sigma[static_cast<int64_t>(sys) * a.G + lb] = sig;
 }
 
+// Loads of one trip of the update kernel: kStreamUnroll tiles t0, t0 + step, ...
+// (clamped indices; masked on use).
+__device__ __forceinline__ void load_trip(const TileRange& tr, int64_t m0, int64_t n, const double* __restrict__ q,
+                                          const double* __restrict__ rin, double* qv, double* rv)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+        const int64_t i = min((tr.lo + m0 + u * tr.step) * kTile + tid, n - 1);
+        qv[u] = q[i];
+        rv[u] = rin[i];
+    }
+}
+
+// k_cg_update: alpha = rho / sigma, r -= alpha q, partial r^T r.  The first trip's
+// loads are issued before the stop check and the reduction of the sigma partials;
+// later trips are double-buffered so each trip's loads overlap the previous one.
 __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 {
     __shared__ double s_red[kBlock / 64];
@@ -317,12 +584,21 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     const int sys = blockIdx.y;
     SysState* st = a.st + sys;
     const int tid = threadIdx.x;
-    if (tid == 0) s_stop = st->stop_iter;
-    __syncthreads();
-    if (s_stop <= k) return;
-    const int lb = logical_block(a.G, a.xcd_remap);
+    const int lb = blockIdx.x;
+    const TileRange tr = tile_range(a.G, a.ntiles, a.xcd_remap);
     const bool lead = (lb == 0 && tid == 0);
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t n = a.n;
+    const double* __restrict__ rin = (k == 0 ? a.b : a.r) + off;
+    const double* __restrict__ q = a.q + off;
+    double* __restrict__ r = a.r + off;
+    const int64_t trip = kStreamUnroll * tr.step;
+    double qa[kStreamUnroll], ra[kStreamUnroll], qb[kStreamUnroll], rb[kStreamUnroll];
+    if (tr.first < tr.len) load_trip(tr, tr.first, n, q, rin, qa, ra);
+
+    if (tid == 0) s_stop = st->stop_iter;
     const double sigma = reduce_partials(a.part_sigma + static_cast<int64_t>(sys) * a.G, a.G, s_red);
+    if (s_stop <= k) return;
     const double rho_k = st->rho[k & 1];
     if (!(sigma > 0.0)) {
         if (lead) {
@@ -340,20 +616,28 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     }
     const double alpha = rho_k / sigma;
     if (lead) st->alpha[k & 1] = alpha;
-    const int64_t off = static_cast<int64_t>(sys) * a.n;
-    const double* __restrict__ rin = (k == 0 ? a.b : a.r) + off;
-    const double* __restrict__ q = a.q + off;
-    double* __restrict__ r = a.r + off;
     double rr = 0.0;
-    for (int64_t t = lb; t < a.ntiles; t += a.G) {
-        const int64_t i = t * kTile + tid;
-        if (i < a.n) {
-            const double tq = alpha * q[i];
-            const double rn = rin[i] - tq;
-            r[i] = rn;
-            const double u = rn * rn;
-            rr = rr + u;
+    auto apply = [&](int64_t m0, const double* qv, const double* rv) {
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t m = m0 + u * tr.step;
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (m < tr.len && i < n) {
+                const double tq = alpha * qv[u];
+                const double rn = rv[u] - tq;
+                r[i] = rn;
+                const double w = rn * rn;
+                rr = rr + w;
+            }
         }
+    };
+#pragma unroll 1
+    for (int64_t m0 = tr.first; m0 < tr.len; m0 += 2 * trip) {
+        if (m0 + trip < tr.len) load_trip(tr, m0 + trip, n, q, rin, qb, rb);
+        apply(m0, qa, ra);
+        if (m0 + trip >= tr.len) break;
+        if (m0 + 2 * trip < tr.len) load_trip(tr, m0 + 2 * trip, n, q, rin, qa, ra);
+        apply(m0 + trip, qb, rb);
     }
     rr = block_sum(rr, s_red);
     if (tid == 0) a.part_rho[static_cast<int64_t>(sys) * a.G + lb] = rr;
@@ -362,7 +646,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 // ----------------------------------------------------------------------------------
 // y = A x (one tile per workgroup; grid (ntiles, batch))
 // ----------------------------------------------------------------------------------
-template <typename RP, int CAP>
+template <typename RP, int CAP, bool OFF32>
 __global__ __launch_bounds__(kBlock) void k_matvec(const RP* __restrict__ rp, const int32_t* __restrict__ col,
                                                    const double* __restrict__ vals, const double* __restrict__ x,
                                                    double* __restrict__ y, int64_t n_rows, int64_t nnz,
@@ -373,9 +657,9 @@ __global__ __launch_bounds__(kBlock) void k_matvec(const RP* __restrict__ rp, co
     const int sys = blockIdx.y;
     const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kTile;
     const int nr = static_cast<int>(min(static_cast<int64_t>(kTile), n_rows - row0));
-    GatherX g{x + static_cast<int64_t>(sys) * n_cols};
-    const double s = tile_rowsum<RP, CAP>(rp, col, vals + static_cast<int64_t>(sys) * nnz, row0, nr, g,
-                                          s_val, s_col);
+    GatherX<OFF32> g{x + static_cast<int64_t>(sys) * n_cols};
+    const double s = tile_rowsum<RP, CAP, row_chunk(CAP)>(rp, col, vals + static_cast<int64_t>(sys) * nnz, row0,
+                                                          nr, g, s_val, s_col);
     if (static_cast<int>(threadIdx.x) < nr) y[static_cast<int64_t>(sys) * n_rows + row0 + threadIdx.x] = s;
 }
 
@@ -582,29 +866,46 @@ hipError_t scan_exclusive(int64_t* data, int64_t n, int64_t* scratch, hipStream_
     return hipGetLastError();
 }
 
-template <typename RP>
-hipError_t launch_spmv_rp(const CgArgs& a, int64_t k, int cap, hipStream_t s)
+using CgKernel = void (*)(CgArgs, int64_t);
+
+template <typename RP, bool O>
+CgKernel spmv_kernel_rp(int cap)
 {
-    const dim3 grid(a.G, a.batch), block(kBlock);
-    if (cap <= kCapSmall) hipLaunchKernelGGL((k_cg_spmv<RP, kCapSmall>), grid, block, 0, s, a, k);
-    else if (cap <= kCapMid) hipLaunchKernelGGL((k_cg_spmv<RP, kCapMid>), grid, block, 0, s, a, k);
-    else hipLaunchKernelGGL((k_cg_spmv<RP, kCapLarge>), grid, block, 0, s, a, k);
-    return hipGetLastError();
+    if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O>;
+    if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O>;
+    return k_cg_spmv<RP, kCapLarge, O>;
 }
 
-template <typename RP>
+CgKernel spmv_kernel(int rp_bits, int cap, bool off32)
+{
+    if (rp_bits == 64) return off32 ? spmv_kernel_rp<int64_t, true>(cap) : spmv_kernel_rp<int64_t, false>(cap);
+    return off32 ? spmv_kernel_rp<int32_t, true>(cap) : spmv_kernel_rp<int32_t, false>(cap);
+}
+
+inline bool off32_ok(int64_t n) { return n < (int64_t(1) << 29); }
+
+template <typename RP, bool O>
 hipError_t launch_matvec_rp(const RP* rp, const int32_t* col, const double* vals, const double* x, double* y,
                             int64_t n_rows, int64_t nnz, int64_t n_cols, int batch, int cap, hipStream_t s)
 {
     const int64_t ntiles = (n_rows + kTile - 1) / kTile;
     const dim3 grid(static_cast<unsigned>(ntiles), batch), block(kBlock);
     if (cap <= kCapSmall)
-        hipLaunchKernelGGL((k_matvec<RP, kCapSmall>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
+        SLA_LAUNCH((k_matvec<RP, kCapSmall, O>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
     else if (cap <= kCapMid)
-        hipLaunchKernelGGL((k_matvec<RP, kCapMid>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
+        SLA_LAUNCH((k_matvec<RP, kCapMid, O>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
     else
-        hipLaunchKernelGGL((k_matvec<RP, kCapLarge>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
+        SLA_LAUNCH((k_matvec<RP, kCapLarge, O>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
     return hipGetLastError();
+}
+
+template <typename RP>
+hipError_t launch_matvec_any(const RP* rp, const int32_t* col, const double* vals, const double* x, double* y,
+                             int64_t n_rows, int64_t nnz, int64_t n_cols, int batch, int cap, hipStream_t s)
+{
+    if (off32_ok(n_cols))
+        return launch_matvec_rp<RP, true>(rp, col, vals, x, y, n_rows, nnz, n_cols, batch, cap, s);
+    return launch_matvec_rp<RP, false>(rp, col, vals, x, y, n_rows, nnz, n_cols, batch, cap, s);
 }
 
 }  // namespace
@@ -612,20 +913,38 @@ hipError_t launch_matvec_rp(const RP* rp, const int32_t* col, const double* vals
 // ----------------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------------
+int cg_blocks_per_cu(int rp_bits, int cap, int64_t n)
+{
+    static int cache[2][3][2] = {};   // occupancy is fixed per variant: query once
+    const int ri = rp_bits == 64 ? 1 : 0;
+    const int ci = cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : 2);
+    const bool o = off32_ok(n);
+    int& c = cache[ri][ci][o ? 1 : 0];
+    if (c > 0) return c;
+    int a = 0, b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, spmv_kernel(rp_bits, cap, o), kBlock, 0) != hipSuccess ||
+        a < 1)
+        a = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_cg_update, kBlock, 0) != hipSuccess || b < 1) b = 1;
+    c = std::max(1, std::min(a, b));
+    return c;
+}
+
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_cg_init, dim3(a.G, a.batch), dim3(kBlock), 0, s, a);
+    SLA_LAUNCH(k_cg_init, dim3(a.G, a.batch), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s)
 {
-    return rp_bits == 64 ? launch_spmv_rp<int64_t>(a, k, cap, s) : launch_spmv_rp<int32_t>(a, k, cap, s);
+    SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n)), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
+    return hipGetLastError();
 }
 
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_cg_update, dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
+    SLA_LAUNCH(k_cg_update, dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
     return hipGetLastError();
 }
 
@@ -635,10 +954,10 @@ hipError_t launch_matvec(const void* row_ptr, int rp_bits, const int32_t* col, c
 {
     if (n_rows == 0) return hipSuccess;
     if (rp_bits == 64)
-        return launch_matvec_rp(static_cast<const int64_t*>(row_ptr), col, vals, x, y, n_rows, nnz, n_cols, batch,
-                                cap, s);
-    return launch_matvec_rp(static_cast<const int32_t*>(row_ptr), col, vals, x, y, n_rows, nnz, n_cols, batch,
-                            cap, s);
+        return launch_matvec_any(static_cast<const int64_t*>(row_ptr), col, vals, x, y, n_rows, nnz, n_cols, batch,
+                                 cap, s);
+    return launch_matvec_any(static_cast<const int32_t*>(row_ptr), col, vals, x, y, n_rows, nnz, n_cols, batch,
+                             cap, s);
 }
 
 hipError_t launch_pattern_outer(const void* row_ptr, int rp_bits, const int32_t* col, double sign,
@@ -649,10 +968,10 @@ hipError_t launch_pattern_outer(const void* row_ptr, int rp_bits, const int32_t*
     const int64_t ntiles = (n_rows + kTile - 1) / kTile;
     const dim3 grid(static_cast<unsigned>(ntiles), batch), block(kBlock);
     if (rp_bits == 64)
-        hipLaunchKernelGGL(k_pattern_outer<int64_t>, grid, block, 0, s, static_cast<const int64_t*>(row_ptr), col,
+        SLA_LAUNCH(k_pattern_outer<int64_t>, grid, block, 0, s, static_cast<const int64_t*>(row_ptr), col,
                            sign, u, us, v, vs, g, n_rows, nnz);
     else
-        hipLaunchKernelGGL(k_pattern_outer<int32_t>, grid, block, 0, s, static_cast<const int32_t*>(row_ptr), col,
+        SLA_LAUNCH(k_pattern_outer<int32_t>, grid, block, 0, s, static_cast<const int32_t*>(row_ptr), col,
                            sign, u, us, v, vs, g, n_rows, nnz);
     return hipGetLastError();
 }
@@ -661,7 +980,7 @@ hipError_t launch_gather_vals(const int64_t* perm, const double* vals, double* o
                               hipStream_t s)
 {
     if (nnz == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gather_vals, dim3(grid_for(nnz, kBlock, 4096), batch), dim3(kBlock), 0, s, perm, vals,
+    SLA_LAUNCH(k_gather_vals, dim3(grid_for(nnz, kBlock, 4096), batch), dim3(kBlock), 0, s, perm, vals,
                        out, nnz);
     return hipGetLastError();
 }
@@ -677,6 +996,12 @@ hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col,
     else
         hipLaunchKernelGGL(k_validate<int32_t>, grid, block, 0, s, static_cast<const int32_t*>(row_ptr), col, n_rows,
                            n_cols, nnz, err, tile_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_narrow_rp(const int64_t* in, int32_t* out, int64_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_narrow_i32, dim3(grid_for(n, kBlock, 8192)), dim3(kBlock), 0, s, in, out, n);
     return hipGetLastError();
 }
 

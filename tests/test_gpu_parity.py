@@ -202,6 +202,16 @@ def test_cg_poisson_ragged_tolerance_1e10(S):
     check_pair(out, ref)
 
 
+def test_cg_poisson520_fixed_iterations(S):
+    # 520 x 520 grid (1057 tiles, neighbours two tiles away, every XCD range in use);
+    # fixed iterations keep the oracle run short and make the two runs comparable step
+    # by step, so the bar is tighter than the converged one.
+    A = W.poisson5(520)
+    b = W.rhs_normal(A.n_rows, 4)
+    out, ref = run_pair(S, A, b, lambda x: x, rtol=0.0, max_iter=120, fixed=True)
+    check_pair(out, ref, tol_x=1e-12, tol_adj=1e-12)
+
+
 def test_cg_varcoef_target_loss(S):
     A, b, _ = W.varcoef_poisson5(40, seed=0)
     t = np.random.default_rng(1).uniform(0, 1, A.n_rows)
