@@ -195,6 +195,12 @@ constexpr size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // grid-stride loops have no second, partial wave of workgroups.
 int blocks_per_system(const sla_csr* A, int64_t ntiles, int64_t batch, int per_cu)
 {
+    if (batch >= 8 && batch % 8 == 0) {
+        // one XCD per system: about 8 tiles per workgroup, a multiple of 8 workgroups
+        int64_t g = (ntiles + 7) / 8;
+        g = std::max<int64_t>(8, std::min<int64_t>(256, (g + 7) & ~int64_t(7)));
+        return static_cast<int>(g);
+    }
     int64_t target = static_cast<int64_t>(A->n_cu) * per_cu;
     int64_t g = (target + batch - 1) / batch;
     if (g >= 8) g &= ~int64_t(7);   // a multiple of 8 enables the XCD band mapping
@@ -356,6 +362,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.G = G;
     a.batch = static_cast<int32_t>(batch);
     a.xcd_remap = 1;
+    a.sys_per_xcd = (batch >= 8 && batch % 8 == 0) ? 1 : 0;
     const int rp_bits = A->krp_bits;   // A and its transpose use the same row-pointer width
 
     hipError_t e = timed(SLA_K_CG_INIT, s, [&] { return launch_cg_init(a, s); });

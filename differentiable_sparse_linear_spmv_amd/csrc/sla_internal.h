@@ -59,6 +59,7 @@ struct CgArgs {
     int32_t G;               // workgroups per system
     int32_t batch;
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
+    int32_t sys_per_xcd;     // 1: batch % 8 == 0; every system runs on one XCD
 };
 
 // Optional timing events for the next single-kernel launch: when set, launchers use

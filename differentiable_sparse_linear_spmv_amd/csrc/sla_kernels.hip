@@ -109,6 +109,32 @@ __device__ __forceinline__ TileRange tile_range(int G, int64_t ntiles, int remap
     return TileRange{0, ntiles, bx, G};
 }
 
+// Which system and which of its workgroups this is, and its tiles.  For batches of
+// 8 or more systems (batch % 8 == 0) the grid is read as one linear sequence and
+// every system is pinned to one XCD: XCD x runs systems x, x + 8, x + 16, ... one
+// after the other, all G workgroups of a system on that XCD.  The gathered vectors of
+// the systems in flight then stay in that XCD's L2 instead of being spread over all
+// eight (each XCD would otherwise hold a slice of every running system).
+struct BlockCoord {
+    int sys;
+    int lb;      // workgroup index within the system: its partial-sum slot
+    TileRange tr;
+};
+
+__device__ __forceinline__ BlockCoord block_coord(const CgArgs& a)
+{
+    if (a.sys_per_xcd) {
+        const int64_t L = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+        const int x = static_cast<int>(L & 7);
+        const int64_t slot = L >> 3;
+        const int sys = x + 8 * static_cast<int>(slot / a.G);
+        const int lb = static_cast<int>(slot % a.G);
+        return BlockCoord{sys, lb, TileRange{0, a.ntiles, lb, a.G}};
+    }
+    return BlockCoord{static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.x),
+                      tile_range(a.G, a.ntiles, a.xcd_remap)};
+}
+
 template <typename RP>
 __device__ __forceinline__ int64_t ld_rp(const RP* rp, int64_t i)
 {
@@ -277,10 +303,11 @@ constexpr int kStreamUnroll = 4;   // tiles per loop trip of the streaming kerne
 __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
 {
     __shared__ double s_red[kBlock / 64];
-    const int sys = blockIdx.y;
+    const BlockCoord bc = block_coord(a);
+    const int sys = bc.sys;
     const int tid = threadIdx.x;
-    const int lb = blockIdx.x;
-    const TileRange tr = tile_range(a.G, a.ntiles, a.xcd_remap);
+    const int lb = bc.lb;
+    const TileRange tr = bc.tr;
     const int64_t off = static_cast<int64_t>(sys) * a.n;
     const double* __restrict__ b = a.b + off;
     double* __restrict__ x = a.x + off;
@@ -374,11 +401,12 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     __shared__ int32_t s_col[CAP];
     __shared__ double s_red[kBlock / 64];
     __shared__ int64_t s_stop;
-    const int sys = blockIdx.y;
+    const BlockCoord bc = block_coord(a);
+    const int sys = bc.sys;
     SysState* st = a.st + sys;
     const int tid = threadIdx.x;
-    const int lb = blockIdx.x;
-    const TileRange tr = tile_range(a.G, a.ntiles, a.xcd_remap);
+    const int lb = bc.lb;
+    const TileRange tr = bc.tr;
     const bool lead = (lb == 0 && tid == 0);
     const bool first = (k == 0);
     const int64_t off = static_cast<int64_t>(sys) * a.n;
@@ -581,11 +609,12 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 {
     __shared__ double s_red[kBlock / 64];
     __shared__ int64_t s_stop;
-    const int sys = blockIdx.y;
+    const BlockCoord bc = block_coord(a);
+    const int sys = bc.sys;
     SysState* st = a.st + sys;
     const int tid = threadIdx.x;
-    const int lb = blockIdx.x;
-    const TileRange tr = tile_range(a.G, a.ntiles, a.xcd_remap);
+    const int lb = bc.lb;
+    const TileRange tr = bc.tr;
     const bool lead = (lb == 0 && tid == 0);
     const int64_t off = static_cast<int64_t>(sys) * a.n;
     const int64_t n = a.n;

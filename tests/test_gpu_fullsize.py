@@ -1,0 +1,190 @@
+"""GPU parity at the benchmark sizes, through the C ABI.
+
+* poisson1024, varcoef2048, fem256x256: the full solve + adjoint against the
+  oracle's values stored in tests/golden/*.json (written by
+  tests/golden/make_golden.py, which calls only the oracle): iteration counts within
+  2 %, x within 1e-9, lambda and dL/dvals within 1e-8 (relative, on seeded samples
+  and on the norms).
+* poisson13000 (169M unknowns, int64 row pointers), in the launch configuration the
+  benchmark uses:
+    - the first 20 fixed iterations against the oracle's residual history and
+      samples (stored);
+    - the 500 + 500 run by properties that hold at any size: SpMV rows recomputed
+      by the oracle one row at a time (bit-exact), recurrence vs true residual, the
+      exact identity <dL/dvals, vals> + <dL/db, b> = lambda^T (b - A x), and
+      dL/dvals = -lambda_i x_j on sampled entries (bit-exact).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import differentiable_sparse_linear_spmv_amd as S
+    return S
+
+
+def golden(name):
+    with open(os.path.join(HERE, "golden", f"{name}.json")) as f:
+        return json.load(f)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def rel(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def iters_close(k_gpu, k_orc):
+    return abs(k_gpu - k_orc) <= math.floor(0.02 * k_orc)
+
+
+def check_system(out, g, tag):
+    assert out["state"] == g["state"], tag
+    assert iters_close(out["iterations"], g["iterations"]), (tag, out["iterations"], g["iterations"])
+    assert iters_close(out["adj_iterations"], g["adj_iterations"]), (tag, out["adj_iterations"],
+                                                                      g["adj_iterations"])
+    ix, ik = np.array(g["ix"]), np.array(g["ik"])
+    assert rel(out["x"][ix], g["x"]) <= 1e-9, (tag, rel(out["x"][ix], g["x"]))
+    assert abs(np.linalg.norm(out["x"]) - g["x_norm"]) <= 1e-9 * g["x_norm"], tag
+    assert rel(out["lam"][ix], g["lam"]) <= 1e-8, (tag, rel(out["lam"][ix], g["lam"]))
+    assert abs(np.linalg.norm(out["lam"]) - g["lam_norm"]) <= 1e-8 * g["lam_norm"], tag
+    assert rel(out["gvals"][ik], g["gvals"]) <= 1e-8, (tag, rel(out["gvals"][ik], g["gvals"]))
+    assert abs(out["rhs_norm"] - g["rhs_norm"]) <= 1e-12 * g["rhs_norm"], tag
+
+
+def solve_and_backward(S, c, vals, b, g_fn):
+    A = c["A"]
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=True)
+    opts = S.cg_opts(rtol=c["rtol"], atol=c["atol"], max_iter=c["max_iter"])
+    dv, db = dev(vals), dev(b)
+    x, info = S.solve(h, dv, db, opts)
+    gb, gv, binfo = S.solve_backward(h, dv, x, g_fn(x), opts)
+    return host(x), host(gb), host(gv), S.read_info(info), S.read_info(binfo)
+
+
+@pytest.mark.parametrize("name", ["poisson1024", "varcoef2048"])
+def test_fullsize_single_system(S, name):
+    g = golden(name)
+    c = W.config(name)
+    A = c["A"]
+    if c["loss"] == "sq_target":
+        xt = dev(c["x_target"])
+        g_fn = lambda x: 2.0 * (x - xt)
+    else:
+        g_fn = lambda x: x.clone()
+    x, lam, gv, info, binfo = solve_and_backward(S, c, A.vals, c["b"], g_fn)
+    out = dict(x=x, lam=lam, gvals=gv, iterations=info[0]["iterations"], state=info[0]["state"],
+               adj_iterations=binfo[0]["iterations"], rhs_norm=info[0]["rhs_norm"])
+    check_system(out, g, name)
+
+
+def test_fullsize_fem_batched(S):
+    g = golden("fem256x256")
+    c = W.config("fem256x256")
+    A = c["A"]
+    x, lam, gv, info, binfo = solve_and_backward(S, c, A.vals, c["b"], lambda x: x.clone())
+    its = [s["iterations"] for s in info]
+    adj = [s["iterations"] for s in binfo]
+    assert all(s["state"] == O.CONVERGED for s in info)
+    for s in range(A.batch):
+        assert iters_close(its[s], g["iterations"][s]), (s, its[s], g["iterations"][s])
+        assert iters_close(adj[s], g["adj_iterations"][s]), (s, adj[s], g["adj_iterations"][s])
+    for key, gs in g["systems"].items():
+        s = int(key)
+        out = dict(x=x[s], lam=lam[s], gvals=gv[s], iterations=its[s], state=info[s]["state"],
+                   adj_iterations=adj[s], rhs_norm=info[s]["rhs_norm"])
+        check_system(out, gs, f"system {s}")
+
+
+# ------------------------------------------------------------------------------ 169M rows
+@pytest.fixture(scope="module")
+def big(S):
+    N = 13000
+    rp, col, vals = W.poisson5_torch(N, torch.device("cuda"), index64=True)
+    b = dev(W.rhs_normal(N * N, 0))
+    h = S.csr_create(rp, col, symmetric=True)
+    yield dict(N=N, rp=rp, col=col, vals=vals, b=b, h=h)
+    del h
+    torch.cuda.empty_cache()
+
+
+def test_poisson13000_first_iterations_match_oracle(S, big):
+    g = golden("poisson13000")
+    K = g["fixed_iterations"]
+    hist = torch.full((K + 1,), float("nan"), dtype=torch.float64, device="cuda")
+    opts = S.cg_opts(rtol=0.0, max_iter=K, fixed=True, residual_history=hist)
+    x, info = S.solve(big["h"], big["vals"], big["b"], opts)
+    gb, gv, _ = S.solve_backward(big["h"], big["vals"], x, x.clone(), S.cg_opts(rtol=0.0, max_iter=K,
+                                                                                  fixed=True))
+    assert S.read_info(info)[0]["iterations"] == K
+    assert rel(host(hist), g["history"]) <= 1e-12
+    ix, ik = torch.tensor(g["ix"], device="cuda"), torch.tensor(g["ik"], device="cuda")
+    assert rel(host(x[ix]), g["x"]) <= 1e-12
+    assert rel(host(gb[ix]), g["lam"]) <= 1e-12
+    assert rel(host(gv[ik]), g["gvals"]) <= 1e-12
+
+
+def test_poisson13000_benchmark_run_properties(S, big):
+    N, h, vals, b = big["N"], big["h"], big["vals"], big["b"]
+    opts = S.cg_opts(rtol=0.0, max_iter=500, fixed=True)
+    x, info = S.solve(h, vals, b, opts)
+    gb, gv, binfo = S.solve_backward(h, vals, x, x.clone(), opts)
+    inf, binf = S.read_info(info)[0], S.read_info(binfo)[0]
+    assert inf["iterations"] == 500 and binf["iterations"] == 500
+    assert inf["state"] == O.MAX_ITER
+
+    # (1) A x on sampled rows: the oracle recomputes each sampled row from the stored
+    #     pattern and values (the same ascending order) and must agree bit for bit.
+    Ax = S.matvec(h, vals, x)
+    rows = np.sort(np.random.default_rng(5).choice(N * N, 512, replace=False))
+    rp_h = big["rp"][torch.from_numpy(np.stack([rows, rows + 1]).T.reshape(-1)).cuda()]
+    rp_h = host(rp_h).reshape(-1, 2)
+    starts, ends = rp_h[:, 0], rp_h[:, 1]
+    pos = np.concatenate([np.arange(s0, e0) for s0, e0 in zip(starts, ends)])
+    cols = host(big["col"][torch.from_numpy(pos).cuda()])
+    vv = host(vals[torch.from_numpy(pos).cuda()])
+    sub_rp = np.zeros(len(rows) + 1, np.int64)
+    np.cumsum(ends - starts, out=sub_rp[1:])
+    uniq, inv = np.unique(cols, return_inverse=True)
+    xs = host(x[torch.from_numpy(uniq).cuda()])
+    sub = W.CSR(len(rows), len(uniq), sub_rp, inv.astype(np.int32), vv)
+    assert np.array_equal(O.spmv(sub, xs), host(Ax[torch.from_numpy(rows).cuda()]))
+
+    # (2) the recurrence residual tracks the true residual
+    true_res = float(torch.linalg.vector_norm(b - Ax))
+    assert abs(true_res - inf["res_norm"]) <= 1e-6 * inf["res_norm"] + 1e-12 * inf["rhs_norm"]
+
+    # (3) exact identity of the pattern gradient: <g_vals, vals> + <g_b, b> = lambda^T (b - A x)
+    lhs = float(torch.dot(gv, vals) + torch.dot(gb, b))
+    rhs = float(torch.dot(gb, b - Ax))
+    scale = float(torch.dot(gv.abs(), vals.abs()) + torch.dot(gb.abs(), b.abs()))
+    assert abs(lhs - rhs) <= 1e-12 * scale
+
+    # (4) g_vals = -lambda_i x_j on sampled stored entries, bit for bit
+    ks = np.sort(np.random.default_rng(6).choice(vals.numel(), 4096, replace=False))
+    kt = torch.from_numpy(ks).cuda()
+    row_of = torch.searchsorted(big["rp"], kt, right=True) - 1
+    expect = -(gb[row_of] * x[big["col"][kt].long()])
+    assert np.array_equal(host(gv[kt]), host(expect))

@@ -227,6 +227,13 @@ def test_cg_fem_batched(S):
     assert len(set(its)) > 1   # systems stop independently
 
 
+def test_cg_fem_batched_one_xcd_per_system(S):
+    # 16 systems (a multiple of 8): every system's workgroups run on one XCD
+    A, b = W.fem_p1_batched(nv=24, B=16, seed=3)
+    out, ref = run_pair(S, A, b, lambda x: x, rtol=1e-8, batch_vals=A.vals)
+    check_pair(out, ref)
+
+
 def test_transpose_path_is_bit_identical_on_symmetric_matrix(S):
     A, b, _ = W.varcoef_poisson5(30, seed=5)
     x_ = dev(b)
