@@ -221,6 +221,7 @@ size_t workspace_bytes(int64_t n, int64_t batch, int G)
     return 4 * vec + 2 * part + align256(sizeof(SysState) * batch) + 256;
 }
 
+// G: the larger of the two grids (both partial arrays get room for it).
 sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w)
 {
     const int64_t n = A->n_rows;
@@ -332,8 +333,17 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     const int64_t n = A->n_rows;
     const int64_t ntiles = (n + kTile - 1) / kTile;
     const int G = blocks_per_system(A, ntiles, batch, cg_blocks_per_cu(A->krp_bits, cap, n));
+    // The update kernel streams 24 B per row and starts by summing all of the SpMV's
+    // partials: about 16 tiles per workgroup balances its start-up cost against the
+    // memory parallelism it needs (a smaller grid for small systems, G for large ones).
+    int Gu = G;
+    if (batch < 8 || batch % 8 != 0) {
+        int64_t g = ((ntiles + 15) / 16 + 7) & ~int64_t(7);
+        Gu = static_cast<int>(std::max<int64_t>(8, std::min<int64_t>(G, g)));
+        if (Gu > ntiles) Gu = G;
+    }
     Workspace w;
-    sla_status st = ensure_workspace(A, batch, G, &w);
+    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w);
     if (st != SLA_OK) return st;
 
     CgArgs a;
@@ -360,6 +370,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.atol = o->atol;
     a.fixed = (o->flags & SLA_FIXED_ITERS) ? 1 : 0;
     a.G = G;
+    a.Gu = Gu;
     a.batch = static_cast<int32_t>(batch);
     a.xcd_remap = 1;
     a.sys_per_xcd = (batch >= 8 && batch % 8 == 0) ? 1 : 0;

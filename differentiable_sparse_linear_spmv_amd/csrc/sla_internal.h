@@ -43,8 +43,8 @@ struct CgArgs {
     double* p0;              // [batch][n]   p_k for even k
     double* p1;              // [batch][n]   p_k for odd k
     double* q;               // [batch][n]   A p_k
-    double* part_sigma;      // [batch][G]
-    double* part_rho;        // [batch][G]
+    double* part_sigma;      // [batch][G]   written by k_cg_spmv
+    double* part_rho;        // [batch][Gu]  written by k_cg_init / k_cg_update
     SysState* st;            // [batch]
     sla_cg_info* info;       // [batch]
     double* hist;            // nullable, [batch][max_iter + 1]
@@ -56,7 +56,8 @@ struct CgArgs {
     double rtol;
     double atol;
     int32_t fixed;
-    int32_t G;               // workgroups per system
+    int32_t G;               // workgroups per system of k_cg_spmv
+    int32_t Gu;              // workgroups per system of k_cg_init and k_cg_update
     int32_t batch;
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
     int32_t sys_per_xcd;     // 1: batch % 8 == 0; every system runs on one XCD
@@ -70,8 +71,8 @@ struct LaunchEvents {
 };
 LaunchEvents& launch_events();
 
-// Resident workgroups per CU of the CG kernels for this pattern variant (the grid
-// of the CG kernels is sized to exactly fill the GPU once).
+// Resident workgroups per CU of the SpMV kernel variant for this pattern (its grid is
+// sized to fill the GPU exactly once).
 int cg_blocks_per_cu(int rp_bits, int cap, int64_t n);
 
 // Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.

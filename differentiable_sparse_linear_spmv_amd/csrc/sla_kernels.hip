@@ -121,18 +121,18 @@ struct BlockCoord {
     TileRange tr;
 };
 
-__device__ __forceinline__ BlockCoord block_coord(const CgArgs& a)
+__device__ __forceinline__ BlockCoord block_coord(const CgArgs& a, int G)
 {
     if (a.sys_per_xcd) {
         const int64_t L = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
         const int x = static_cast<int>(L & 7);
         const int64_t slot = L >> 3;
-        const int sys = x + 8 * static_cast<int>(slot / a.G);
-        const int lb = static_cast<int>(slot % a.G);
-        return BlockCoord{sys, lb, TileRange{0, a.ntiles, lb, a.G}};
+        const int sys = x + 8 * static_cast<int>(slot / G);
+        const int lb = static_cast<int>(slot % G);
+        return BlockCoord{sys, lb, TileRange{0, a.ntiles, lb, G}};
     }
     return BlockCoord{static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.x),
-                      tile_range(a.G, a.ntiles, a.xcd_remap)};
+                      tile_range(G, a.ntiles, a.xcd_remap)};
 }
 
 template <typename RP>
@@ -303,7 +303,7 @@ constexpr int kStreamUnroll = 4;   // tiles per loop trip of the streaming kerne
 __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
 {
     __shared__ double s_red[kBlock / 64];
-    const BlockCoord bc = block_coord(a);
+    const BlockCoord bc = block_coord(a, a.Gu);
     const int sys = bc.sys;
     const int tid = threadIdx.x;
     const int lb = bc.lb;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
     }
     rr = block_sum(rr, s_red);
     if (tid == 0) {
-        a.part_rho[static_cast<int64_t>(sys) * a.G + lb] = rr;
+        a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
         if (lb == 0) a.st[sys].stop_iter = INT64_MAX;
         if (lb == 0 && sys == 0) *a.n_active = a.batch;
     }
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     __shared__ int32_t s_col[CAP];
     __shared__ double s_red[kBlock / 64];
     __shared__ int64_t s_stop;
-    const BlockCoord bc = block_coord(a);
+    const BlockCoord bc = block_coord(a, a.G);
     const int sys = bc.sys;
     SysState* st = a.st + sys;
     const int tid = threadIdx.x;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     // reduction), so the exit decision is uniform even while this kernel's leading
     // workgroup may be writing stop_iter = k.
     if (tid == 0) s_stop = st->stop_iter;
-    const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.G, a.G, s_red);
+    const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
     if (s_stop < k) return;   // stopped in an earlier kernel
     const double res = sqrt(rho_k);
     double thr, rhs;
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 {
     __shared__ double s_red[kBlock / 64];
     __shared__ int64_t s_stop;
-    const BlockCoord bc = block_coord(a);
+    const BlockCoord bc = block_coord(a, a.Gu);
     const int sys = bc.sys;
     SysState* st = a.st + sys;
     const int tid = threadIdx.x;
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
         apply(m0 + trip, qb, rb);
     }
     rr = block_sum(rr, s_red);
-    if (tid == 0) a.part_rho[static_cast<int64_t>(sys) * a.G + lb] = rr;
+    if (tid == 0) a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
 }
 
 // ----------------------------------------------------------------------------------
@@ -950,18 +950,17 @@ int cg_blocks_per_cu(int rp_bits, int cap, int64_t n)
     const bool o = off32_ok(n);
     int& c = cache[ri][ci][o ? 1 : 0];
     if (c > 0) return c;
-    int a = 0, b = 0;
+    int a = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, spmv_kernel(rp_bits, cap, o), kBlock, 0) != hipSuccess ||
         a < 1)
         a = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k_cg_update, kBlock, 0) != hipSuccess || b < 1) b = 1;
-    c = std::max(1, std::min(a, b));
+    c = a;
     return c;
 }
 
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s)
 {
-    SLA_LAUNCH(k_cg_init, dim3(a.G, a.batch), dim3(kBlock), 0, s, a);
+    SLA_LAUNCH(k_cg_init, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
@@ -973,7 +972,7 @@ hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipS
 
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s)
 {
-    SLA_LAUNCH(k_cg_update, dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
+    SLA_LAUNCH(k_cg_update, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
     return hipGetLastError();
 }
 
