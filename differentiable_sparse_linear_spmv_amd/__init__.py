@@ -10,8 +10,8 @@ from ._lib import SlaError
 
 _lib.load()
 
-from .sparse import (SparseTensor, cg_opts, csr_create, csr_destroy, csr_info,  # noqa: E402
-                     matvec, matvec_backward, read_info, solve, solve_backward, timing)
+from .sparse import (SparseTensor, cg_opts, csr_analysis, csr_create, csr_destroy,  # noqa: E402
+                     csr_info, matvec, matvec_backward, read_info, solve, solve_backward, timing)
 
-__all__ = ["SparseTensor", "SlaError", "cg_opts", "csr_create", "csr_destroy", "csr_info",
+__all__ = ["SparseTensor", "SlaError", "cg_opts", "csr_analysis", "csr_create", "csr_destroy", "csr_info",
            "matvec", "matvec_backward", "read_info", "solve", "solve_backward", "timing"]

@@ -25,7 +25,7 @@ KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "g
                 "transpose"]
 
 EXPORTS = [
-    "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_matvec", "sla_matvec_backward",
+    "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
     "sla_solve", "sla_solve_backward", "sla_timing_enable", "sla_timing_reset",
     "sla_timing_collect", "sla_timing_query", "sla_status_string", "sla_last_error", "sla_version",
 ]
@@ -66,7 +66,7 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m differentiable_sparse_linear_spmv_amd.build` "
+                          "`python differentiable_sparse_linear_spmv_amd/build.py` "
                           "(there is no CPU fallback)")
     L = C.CDLL(LIB_PATH)
     P, i64, i32, u32 = C.c_void_p, C.c_int64, C.c_int32, C.c_uint32
@@ -78,6 +78,8 @@ def load():
     L.sla_csr_info.argtypes = [P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64),
                                C.POINTER(i32), C.POINTER(u32), C.POINTER(i64)]
     L.sla_csr_info.restype = st
+    L.sla_csr_analysis.argtypes = [P, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32), C.POINTER(i64)]
+    L.sla_csr_analysis.restype = st
     L.sla_matvec.argtypes = [P, i64, P, P, P, P]
     L.sla_matvec.restype = st
     L.sla_matvec_backward.argtypes = [P, i64, P, P, P, P, P, P]

@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -40,6 +41,10 @@ struct sla_csr {
     int n_cu = 256;
     int cap = kCapSmall;        // LDS variant for A
     int32_t tile_max = 0;
+    int32_t row_max = 0;
+    // Banded pattern (line-walking SpMV): line stride S, 0 if the plain SpMV is used.
+    int64_t band = 0;
+    int band_cap = kCapSmall;
     // transposed pattern (lazily built unless SLA_SYMMETRIC)
     bool has_t = false;
     void* row_ptr_t = nullptr;
@@ -286,20 +291,20 @@ sla_status ensure_transpose(sla_csr* A, hipStream_t s)
     // analysis of the transposed pattern (also re-checks it)
     int32_t* d_chk = static_cast<int32_t*>(scratch);   // reuse: the scan data is no longer needed
     HIP_TRY(hipStreamSynchronize(s));
-    int32_t zero2[2] = {0, 0};
-    HIP_TRY(hipMemcpyAsync(d_chk, zero2, sizeof(zero2), hipMemcpyHostToDevice, s));
+    int32_t h[kChkCount] = {0, 0, 0, INT32_MAX, 0};
+    HIP_TRY(hipMemcpyAsync(d_chk, h, sizeof(h), hipMemcpyHostToDevice, s));
     HIP_TRY(hipStreamSynchronize(s));
-    e = launch_validate(A->row_ptr_t, A->krp_bits, A->col_t, A->n_cols, A->n_rows, A->nnz, d_chk, d_chk + 1, s);
+    e = launch_validate(A->row_ptr_t, A->krp_bits, A->col_t, A->n_cols, A->n_rows, A->nnz, d_chk, s);
     if (e != hipSuccess) {
         (void)hipFree(scratch);
         return fail(SLA_ERR_HIP, "transpose analysis: %s", hipGetErrorString(e));
     }
-    int32_t h[2];
     HIP_TRY(hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
     (void)hipFree(scratch);
-    if (h[0] != 0) return fail(SLA_ERR_HIP, "internal error: transposed pattern failed validation (%d)", h[0]);
-    A->cap_t = choose_cap(h[1]);
+    if (h[kChkErr] != 0)
+        return fail(SLA_ERR_HIP, "internal error: transposed pattern failed validation (%d)", h[kChkErr]);
+    A->cap_t = choose_cap(h[kChkTileMax]);
     A->has_t = true;
     return SLA_OK;
 }
@@ -327,20 +332,43 @@ sla_status ensure_vals_t(sla_csr* A, int64_t batch, const double* vals, hipStrea
 }
 
 // One CG solve (batch systems) on the pattern (row_ptr, col, cap) with values vals.
-sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t batch, const double* vals,
-                  const double* b, double* x, const sla_cg_opts* o, sla_cg_info* info, hipStream_t s)
+// band > 0: the pattern is banded with line stride `band` and takes the line-walking
+// SpMV (LDS variant band_cap) on a persistent grid over blocks of lines of one strip.
+sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t band, int band_cap,
+                  int64_t batch, const double* vals, const double* b, double* x, const sla_cg_opts* o,
+                  sla_cg_info* info, hipStream_t s)
 {
     const int64_t n = A->n_rows;
     const int64_t ntiles = (n + kTile - 1) / kTile;
-    const int G = blocks_per_system(A, ntiles, batch, cg_blocks_per_cu(A->krp_bits, cap, n));
+    // Grid of the plain SpMV (also the base of the update kernel's grid).
+    const int Gp = blocks_per_system(A, ntiles, batch, cg_blocks_per_cu(A->krp_bits, cap, n));
+    int G = Gp, band_block = 0;
+    int64_t band_lines = 0;
+    if (band > 0) {
+        // Persistent grid over blocks of band_block lines of one strip (k_cg_spmv_band):
+        // blocks of up to kBandBlockLines lines, shorter when needed to give every
+        // workgroup of the grid a block.
+        const int64_t strips = (band + kTile - 1) / kTile;
+        band_lines = (n + band - 1) / band;
+        const int64_t spmv_bytes = (12 * A->nnz + 52 * n) * batch;   // values, columns, rows, six vectors
+        int per_cu = cg_band_blocks_per_cu(band_cap);
+        if (spmv_bytes > kBandStreamBytes) per_cu = std::min(per_cu, kBandBlocksPerCu);
+        const int64_t target = std::max<int64_t>(1, (static_cast<int64_t>(A->n_cu) * per_cu) / batch);
+        const int64_t bl = std::max<int64_t>(4, std::min<int64_t>(kBandBlockLines, strips * band_lines / target));
+        band_block = static_cast<int>(std::min<int64_t>(band_lines, bl));
+        const int64_t nblk = strips * ((band_lines + band_block - 1) / band_block);
+        G = static_cast<int>(std::min<int64_t>(nblk, target));
+        cap = band_cap;
+    }
     // The update kernel streams 24 B per row and starts by summing all of the SpMV's
     // partials: about 16 tiles per workgroup balances its start-up cost against the
-    // memory parallelism it needs (a smaller grid for small systems, G for large ones).
-    int Gu = G;
+    // memory parallelism it needs (a smaller grid for small systems, the plain SpMV's
+    // full-occupancy grid for large ones).
+    int Gu = Gp;
     if (batch < 8 || batch % 8 != 0) {
         int64_t g = ((ntiles + 15) / 16 + 7) & ~int64_t(7);
-        Gu = static_cast<int>(std::max<int64_t>(8, std::min<int64_t>(G, g)));
-        if (Gu > ntiles) Gu = G;
+        Gu = static_cast<int>(std::max<int64_t>(8, std::min<int64_t>(Gp, g)));
+        if (Gu > ntiles) Gu = Gp;
     }
     Workspace w;
     sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w);
@@ -374,6 +402,9 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.batch = static_cast<int32_t>(batch);
     a.xcd_remap = 1;
     a.sys_per_xcd = (batch >= 8 && batch % 8 == 0) ? 1 : 0;
+    a.band_block = band_block;
+    a.band_stride = band;
+    a.band_lines = band_lines;
     const int rp_bits = A->krp_bits;   // A and its transpose use the same row-pointer width
 
     hipError_t e = timed(SLA_K_CG_INIT, s, [&] { return launch_cg_init(a, s); });
@@ -407,6 +438,29 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         }
     }
     return SLA_OK;
+}
+
+// Line stride of a banded pattern, or 0.  Banded: square with n < 2^29 and nnz < 2^31
+// (the kernel uses 32-bit offsets and the 32-bit row pointers), every entry within
+// kBandHalo of the diagonal or within kBandHalo below the largest distance S, whole
+// windows of kTile rows fit the largest LDS variant, and S at least the minimum stride
+// (default 2048; environment SLA_BAND_MIN_STRIDE overrides it, read at each create).
+// Below that stride the plain SpMV's gathers already stay in L2.
+int64_t band_stride_of(int64_t n_rows, int64_t n_cols, int64_t nnz, int32_t row_max, int32_t far_min,
+                       int32_t far_max)
+{
+    int64_t min_stride = 2048;
+    if (const char* env = std::getenv("SLA_BAND_MIN_STRIDE")) {
+        char* end = nullptr;
+        const long long v = std::strtoll(env, &end, 10);
+        if (end != env && v > 0) min_stride = v;
+    }
+    const int64_t S = far_max;
+    if (n_rows != n_cols || n_rows >= (int64_t(1) << 29) || nnz >= (int64_t(1) << 31) || S <= 0) return 0;
+    if (far_min < S - kBandHalo) return 0;
+    if (S < kTile + 2 * kBandHalo || S < min_stride) return 0;
+    if (static_cast<int64_t>(kTile) * row_max > kCapLarge) return 0;
+    return S;
 }
 
 sla_status check_common(const sla_csr* A, int64_t batch)
@@ -483,28 +537,31 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
         if (hipEventCreateWithFlags(&A->poll_ev[i], hipEventDisableTiming) != hipSuccess)
             return bail(fail(SLA_ERR_HIP, "hipEventCreate failed"));
 
-    // Validation and tile analysis: one device pass, one synchronisation.
+    // Validation and pattern analysis: one device pass, one synchronisation.
     int32_t* d_chk = nullptr;
-    sla_status st = dev_alloc(reinterpret_cast<void**>(&d_chk), 2 * sizeof(int32_t));
+    sla_status st = dev_alloc(reinterpret_cast<void**>(&d_chk), kChkCount * sizeof(int32_t));
     if (st != SLA_OK) return bail(st);
-    int32_t h[2] = {0, 0};
+    int32_t h[kChkCount] = {0, 0, 0, INT32_MAX, 0};
     hipError_t e = hipMemcpyAsync(d_chk, h, sizeof(h), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e == hipSuccess)
-        e = launch_validate(d_row_ptr, row_ptr_bits, d_col_idx, n_rows, n_cols, nnz, d_chk, d_chk + 1, s);
+    if (e == hipSuccess) e = launch_validate(d_row_ptr, row_ptr_bits, d_col_idx, n_rows, n_cols, nnz, d_chk, s);
     if (e == hipSuccess) e = hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     (void)hipFree(d_chk);
     if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "CSR validation: %s", hipGetErrorString(e)));
-    if (h[0] != 0) {
-        const char* why = (h[0] & 1) ? "row_ptr[0] != 0 or row_ptr[n_rows] != nnz"
-                          : (h[0] & 2) ? "row_ptr is not non-decreasing within [0, nnz]"
-                          : (h[0] & 4) ? "a column index is out of [0, n_cols)"
-                                       : "columns are not strictly ascending within a row";
-        return bail(fail(SLA_ERR_INVALID_CSR, "invalid CSR: %s (code %d)", why, h[0]));
+    if (h[kChkErr] != 0) {
+        const int c = h[kChkErr];
+        const char* why = (c & 1) ? "row_ptr[0] != 0 or row_ptr[n_rows] != nnz"
+                          : (c & 2) ? "row_ptr is not non-decreasing within [0, nnz]"
+                          : (c & 4) ? "a column index is out of [0, n_cols)"
+                                    : "columns are not strictly ascending within a row";
+        return bail(fail(SLA_ERR_INVALID_CSR, "invalid CSR: %s (code %d)", why, c));
     }
-    A->tile_max = h[1];
-    A->cap = choose_cap(h[1]);
+    A->tile_max = h[kChkTileMax];
+    A->row_max = h[kChkRowMax];
+    A->cap = choose_cap(h[kChkTileMax]);
+    A->band = band_stride_of(n_rows, n_cols, nnz, h[kChkRowMax], h[kChkFarMin], h[kChkFarMax]);
+    A->band_cap = choose_cap(kTile * std::max<int32_t>(h[kChkRowMax], 1));
     A->krp = d_row_ptr;
     A->krp_bits = row_ptr_bits;
     if (row_ptr_bits == 64 && nnz < (int64_t(1) << 31)) {
@@ -542,6 +599,17 @@ sla_status sla_csr_destroy(sla_csr* A)
         if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);
     if (prev >= 0 && prev != A->device) (void)hipSetDevice(prev);
     delete A;
+    return SLA_OK;
+}
+
+sla_status sla_csr_analysis(const sla_csr* A, int32_t* row_max, int32_t* tile_max, int32_t* spmv_cap,
+                            int64_t* band_stride)
+{
+    if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
+    if (row_max) *row_max = A->row_max;
+    if (tile_max) *tile_max = A->tile_max;
+    if (spmv_cap) *spmv_cap = A->band > 0 ? A->band_cap : A->cap;
+    if (band_stride) *band_stride = A->band;
     return SLA_OK;
 }
 
@@ -630,7 +698,7 @@ sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, con
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
-    st = run_cg(A, A->krp, A->col, A->cap, batch, d_vals, d_b, d_x, opts, d_info, s);
+    st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, batch, d_vals, d_b, d_x, opts, d_info, s);
     if (st == SLA_OK && !(opts->flags & SLA_FIXED_ITERS)) {
         hipError_t e = timing_collect();
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
@@ -652,12 +720,12 @@ sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
     if (A->flags & SLA_SYMMETRIC) {
-        st = run_cg(A, A->krp, A->col, A->cap, batch, d_vals, d_gx, d_gb, opts, d_info, s);
+        st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, batch, d_vals, d_gx, d_gb, opts, d_info, s);
     } else {
         if ((st = ensure_transpose(A, s)) != SLA_OK) return st;
         const double* vt = nullptr;
         if ((st = ensure_vals_t(A, batch, d_vals, s, &vt)) != SLA_OK) return st;
-        st = run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, batch, vt, d_gx, d_gb, opts, d_info, s);
+        st = run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, 0, 0, batch, vt, d_gx, d_gb, opts, d_info, s);
     }
     if (st != SLA_OK) return st;
     if (d_gvals) {

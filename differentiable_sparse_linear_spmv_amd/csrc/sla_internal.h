@@ -19,6 +19,19 @@ constexpr int kCapSmall = 1280;   // 5 entries per row
 constexpr int kCapMid = 2048;     // 8 per row
 constexpr int kCapLarge = 4096;   // 16 per row
 
+// Banded patterns (every entry within kBandHalo of the diagonal or of distance S from
+// it) take the line-walking SpMV; its segments extend kBandHalo past each strip end.
+constexpr int kBandHalo = 8;
+// Lines per block of work of the banded SpMV, at most (each block starts its LDS ring
+// afresh, reading two segments more than it uses: 1/16 more operand reads at 32 lines).
+constexpr int kBandBlockLines = 32;
+// Resident workgroups per CU of the banded SpMV when one SpMV streams more than
+// kBandStreamBytes: with few workgroups sweeping one front, HBM sees the longest
+// sequential runs (measured on 169M rows: 2 per CU beat 1 and 4).  Smaller systems,
+// served largely from the 256 MB Infinity Cache, run at full occupancy.
+constexpr int kBandBlocksPerCu = 2;
+constexpr int64_t kBandStreamBytes = int64_t(1) << 30;
+
 // Per-system CG state in device memory (64 bytes).  Double-buffered by the
 // parity of the iteration index so that a kernel reads the previous value while
 // its first workgroup writes the new one.
@@ -61,6 +74,9 @@ struct CgArgs {
     int32_t batch;
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
     int32_t sys_per_xcd;     // 1: batch % 8 == 0; every system runs on one XCD
+    int32_t band_block;      // banded SpMV: lines per block of work
+    int64_t band_stride;     // banded SpMV: line length S (0: plain SpMV)
+    int64_t band_lines;      // banded SpMV: ceil(n / S)
 };
 
 // Optional timing events for the next single-kernel launch: when set, launchers use
@@ -74,6 +90,7 @@ LaunchEvents& launch_events();
 // Resident workgroups per CU of the SpMV kernel variant for this pattern (its grid is
 // sized to fill the GPU exactly once).
 int cg_blocks_per_cu(int rp_bits, int cap, int64_t n);
+int cg_band_blocks_per_cu(int cap);   // the banded SpMV (32-bit row pointers only)
 
 // Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s);
@@ -92,10 +109,14 @@ hipError_t launch_pattern_outer(const void* row_ptr, int rp_bits, const int32_t*
 hipError_t launch_gather_vals(const int64_t* perm, const double* vals, double* out, int64_t nnz,
                               int batch, hipStream_t s);
 
-// CSR checks: ORs a nonzero code into err[0] on any problem, and records the most
-// entries of any 256-row tile in tile_max[0].  Both counters must be zero on entry.
+// CSR checks and pattern analysis.  out[kChkCount] on entry: {0, 0, 0, INT32_MAX, 0}.
+// out[kChkErr] gets a nonzero code ORed in on any problem; out[kChkTileMax] the most
+// entries of any 256-row tile; out[kChkRowMax] the most entries of any row;
+// out[kChkFarMin] / out[kChkFarMax] the least / largest |c - i| over the entries with
+// |c - i| > kBandHalo (the band analysis).
+constexpr int kChkErr = 0, kChkTileMax = 1, kChkRowMax = 2, kChkFarMin = 3, kChkFarMax = 4, kChkCount = 5;
 hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col, int64_t n_rows,
-                           int64_t n_cols, int64_t nnz, int32_t* err, int32_t* tile_max, hipStream_t s);
+                           int64_t n_cols, int64_t nnz, int32_t* out, hipStream_t s);
 
 // out[i] = (int32) in[i] for i < n: 32-bit copy of 64-bit row pointers whose values fit.
 hipError_t launch_narrow_rp(const int64_t* in, int32_t* out, int64_t n, hipStream_t s);

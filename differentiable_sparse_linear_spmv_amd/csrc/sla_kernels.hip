@@ -340,6 +340,70 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
     }
 }
 
+// Start of a CG SpMV launch for system sys at iteration k: read the stop word, sum
+// the rho partials (rho_k = r_k^T r_k), and decide.  Returns kStepStopped if the
+// system stopped in an earlier launch, kStepStopNow if it stops at k (the info record
+// and the stop word are written here; the caller applies the deferred x update), else
+// kStepRun with beta_k = rho_k / rho_{k-1} (0 for k = 0) and alpha_{k-1} (0 for
+// k = 0).  Contains workgroup barriers: every thread of the workgroup calls it.
+constexpr int kStepRun = 0;
+constexpr int kStepStopped = 1;
+constexpr int kStepStopNow = 2;
+
+__device__ __forceinline__ int cg_step_begin(const CgArgs& a, int sys, int lb, int64_t k, double* s_red,
+                                             int64_t* s_stop, double& beta, double& alpha_prev)
+{
+    SysState* st = a.st + sys;
+    const int tid = threadIdx.x;
+    const bool lead = (lb == 0 && tid == 0);
+    const bool first = (k == 0);
+    // One read of the stop word per workgroup (published by the barriers of the
+    // reduction), so the exit decision is uniform even while this kernel's leading
+    // workgroup may be writing stop_iter = k.
+    if (tid == 0) *s_stop = st->stop_iter;
+    const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
+    beta = 0.0;
+    alpha_prev = 0.0;
+    if (*s_stop < k) return kStepStopped;
+    const double res = sqrt(rho_k);
+    double thr, rhs;
+    if (first) {
+        rhs = res;
+        thr = a.rtol * rhs;
+        if (a.atol > thr) thr = a.atol;
+    } else {
+        thr = st->thr;
+        rhs = st->rhs;
+    }
+    if (lead && a.hist) a.hist[static_cast<int64_t>(sys) * (a.max_iter + 1) + k] = res;
+    alpha_prev = first ? 0.0 : st->alpha[(k - 1) & 1];
+
+    int code = -1;
+    if (!a.fixed && res <= thr) code = SLA_CONVERGED;
+    else if (k >= a.max_iter) code = SLA_MAX_ITER;
+    if (code >= 0) {
+        if (lead) {
+            st->stop_iter = k;
+            if (first) { st->rhs = rhs; st->thr = thr; }
+            sla_cg_info inf;
+            inf.iterations = k;
+            inf.res_norm = res;
+            inf.rhs_norm = rhs;
+            inf.state = code;
+            inf.reserved = 0;
+            a.info[sys] = inf;
+            atomicSub(a.n_active, 1);
+        }
+        return kStepStopNow;
+    }
+    beta = first ? 0.0 : rho_k / st->rho[(k - 1) & 1];
+    if (lead) {
+        st->rho[k & 1] = rho_k;
+        if (first) { st->thr = thr; st->rhs = rhs; }
+    }
+    return kStepRun;
+}
+
 // Staged data of one tile, held in registers until the tile is processed: its
 // entries (written to LDS then), this lane's row bounds, and this lane's row of the
 // vectors the update needs.  Nothing derived from these loads is computed at staging
@@ -403,11 +467,9 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     __shared__ int64_t s_stop;
     const BlockCoord bc = block_coord(a, a.G);
     const int sys = bc.sys;
-    SysState* st = a.st + sys;
     const int tid = threadIdx.x;
     const int lb = bc.lb;
     const TileRange tr = bc.tr;
-    const bool lead = (lb == 0 && tid == 0);
     const bool first = (k == 0);
     const int64_t off = static_cast<int64_t>(sys) * a.n;
     const int64_t n = a.n;
@@ -439,30 +501,10 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         k1n = tile_k1(t + Gs);
     }
 
-    // One read of the stop word per workgroup (published by the barriers of the
-    // reduction), so the exit decision is uniform even while this kernel's leading
-    // workgroup may be writing stop_iter = k.
-    if (tid == 0) s_stop = st->stop_iter;
-    const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
-    if (s_stop < k) return;   // stopped in an earlier kernel
-    const double res = sqrt(rho_k);
-    double thr, rhs;
-    if (first) {
-        rhs = res;
-        thr = a.rtol * rhs;
-        if (a.atol > thr) thr = a.atol;
-    } else {
-        thr = st->thr;
-        rhs = st->rhs;
-    }
-    if (lead && a.hist) a.hist[static_cast<int64_t>(sys) * (a.max_iter + 1) + k] = res;
-
-    const double alpha_prev = first ? 0.0 : st->alpha[(k - 1) & 1];
-
-    int code = -1;
-    if (!a.fixed && res <= thr) code = SLA_CONVERGED;
-    else if (k >= a.max_iter) code = SLA_MAX_ITER;
-    if (code >= 0) {
+    double beta, alpha_prev;
+    const int run = cg_step_begin(a, sys, lb, k, s_red, &s_stop, beta, alpha_prev);
+    if (run == kStepStopped) return;
+    if (run == kStepStopNow) {
         // Stop: apply the deferred update x_k = x_{k-1} + alpha_{k-1} p_{k-1}.
         if (!first) {
             for (int64_t m = tr.first; m < tr.len; m += tr.step) {
@@ -473,24 +515,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
                 }
             }
         }
-        if (lead) {
-            st->stop_iter = k;
-            if (first) { st->rhs = rhs; st->thr = thr; }
-            sla_cg_info inf;
-            inf.iterations = k;
-            inf.res_norm = res;
-            inf.rhs_norm = rhs;
-            inf.state = code;
-            inf.reserved = 0;
-            a.info[sys] = inf;
-            atomicSub(a.n_active, 1);
-        }
         return;
-    }
-    const double beta = first ? 0.0 : rho_k / st->rho[(k - 1) & 1];
-    if (lead) {
-        st->rho[k & 1] = rho_k;
-        if (first) { st->thr = thr; st->rhs = rhs; }
     }
 
     double* __restrict__ q = a.q + off;
@@ -583,6 +608,427 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         process(SA, SB);
         if (t >= ntiles) break;
         process(SB, SA);
+    }
+    sig = block_sum(sig, s_red);
+    if (tid == 0) a.part_sigma[static_cast<int64_t>(sys) * a.G + lb] = sig;
+}
+
+// ----------------------------------------------------------------------------------
+// Banded patterns: the CG SpMV with its gathered operand held in LDS.
+//
+// A pattern is banded with stride S when every stored entry (i, c) has |c - i| <= kBandHalo
+// or S - kBandHalo <= |c - i| <= S: 5- and 9-point stencils on a grid whose lines hold S
+// (or S - 1) unknowns.  The rows are read as lines of S rows, each cut into strips of
+// kTile positions; workgroup (strip, chunk) walks its strip down a range of lines.
+// The row window of line l (rows l S + pos0 + [0, w)) reads the operand only inside
+// three segments, lines l - 1, l and l + 1 of the strip widened by kBandHalo on each
+// side.  Those live in an LDS ring of three segments, so each value of
+// p_k = r_k + beta p_{k-1} is loaded from HBM and formed once, then serves all three
+// windows that read it.  The plain kernel instead re-gathers rows S apart through the
+// L2, which cannot hold them when S is large.  Each row still sums its entries in
+// ascending order with the same rounded products, so q and p_k are bit-identical to
+// the plain kernel's.
+// ----------------------------------------------------------------------------------
+constexpr int kSeg = kTile + 2 * kBandHalo;   // positions per segment
+
+// Element e (0 <= e < 2^29) of a vector: uniform base plus a 32-bit byte offset.
+__device__ __forceinline__ double ld32(const double* __restrict__ base, int32_t e)
+{
+    return *reinterpret_cast<const double*>(reinterpret_cast<const char*>(base) + (static_cast<uint32_t>(e) << 3));
+}
+
+__device__ __forceinline__ void st32(double* __restrict__ base, int32_t e, double v)
+{
+    *reinterpret_cast<double*>(reinterpret_cast<char*>(base) + (static_cast<uint32_t>(e) << 3)) = v;
+}
+
+#ifndef SLA_BAND_NT
+#define SLA_BAND_NT 1
+#endif
+// Streaming accesses of the banded SpMV (entries read once, outputs written once) carry
+// the non-temporal hint.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p)
+{
+#if SLA_BAND_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st32_stream(double* __restrict__ base, int32_t e, double v)
+{
+    double* p = reinterpret_cast<double*>(reinterpret_cast<char*>(base) + (static_cast<uint32_t>(e) << 3));
+#if SLA_BAND_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// Raw loads of one segment (positions tid, and tid + kTile for tid < 2 kBandHalo).
+struct SegLoad {
+    double r0, pp0, r1, pp1;
+};
+
+// Every lane issues the same number of loads (the lanes past the segment's end re-read
+// its last position), so the compiler's counts of loads in flight are exact.
+__device__ __forceinline__ void seg_issue(SegLoad& L, const double* __restrict__ rin,
+                                          const double* __restrict__ pprev, int32_t e0, int32_t n)
+{
+    const int tid = threadIdx.x;
+    const int32_t e = min(max(e0 + tid, 0), n - 1);
+    L.r0 = ld32(rin, e);
+    L.pp0 = ld32(pprev, e);
+    const int32_t e1 = min(max(e0 + kTile + min(tid, 2 * kBandHalo - 1), 0), n - 1);
+    L.r1 = ld32(rin, e1);
+    L.pp1 = ld32(pprev, e1);
+}
+
+// Form p_k on the segment and store it (positions outside [0, n) hold 0; no column
+// points there).  The segment's own positions [kBandHalo, kBandHalo + kTile) also keep
+// p_{k-1} in s_pp (when given), for the deferred x update of that line's rows.
+__device__ __forceinline__ void seg_commit(const SegLoad& L, double* s_seg, double* s_pp, double beta, int32_t e0,
+                                           int32_t n)
+{
+    const int tid = threadIdx.x;
+    const int32_t e = e0 + tid;
+    const double t0 = beta * L.pp0;
+    const double v0 = L.r0 + t0;
+    s_seg[tid] = (e >= 0 && e < n) ? v0 : 0.0;
+    if (s_pp && tid >= kBandHalo) s_pp[tid - kBandHalo] = L.pp0;
+    if (tid < 2 * kBandHalo) {
+        const int32_t e1 = e + kTile;
+        const double t1 = beta * L.pp1;
+        const double v1 = L.r1 + t1;
+        s_seg[tid + kTile] = (e1 >= 0 && e1 < n) ? v1 : 0.0;
+        if (s_pp && tid < kBandHalo) s_pp[tid + kTile - kBandHalo] = L.pp1;
+    }
+}
+
+// Registers of one staged window: its entries, this lane's row bounds and x, and the
+// raw loads of the segment one line further down.
+template <int U>
+struct BandStage {
+    double v[U];
+    int32_t c[U];
+    int32_t a0, a1;
+    double xi;
+    SegLoad seg;
+};
+
+// Workgroup-uniform view of the band walk of one system (all indices < 2^29 and the
+// row pointers 32-bit: the band analysis admits only such patterns).
+struct BandWalk {
+    const int32_t* __restrict__ rp;
+    const int32_t* __restrict__ col;
+    const double* __restrict__ vals;
+    const double* __restrict__ rin;     // r_k
+    const double* __restrict__ pprev;   // p_{k-1}
+    const double* __restrict__ x;
+    int32_t n;
+    int32_t nnz;    // > 0
+    int32_t S;      // line stride
+    int32_t pos0;   // first position of this strip within a line
+    int32_t w;      // positions of the strip
+
+    __device__ __forceinline__ int32_t base(int32_t l) const { return l * S + pos0; }
+    __device__ __forceinline__ int rows(int32_t l) const   // rows of window l that exist
+    {
+        const int32_t m = n - base(l);
+        return m <= 0 ? 0 : (m < w ? m : w);
+    }
+    // first / end entry of window l (uniform scalar loads)
+    __device__ __forceinline__ int32_t k0(int32_t l) const { return ld_rp_uniform(rp, min(base(l), n)); }
+    __device__ __forceinline__ int32_t k1(int32_t l) const { return ld_rp_uniform(rp, min(base(l) + rows(l), n)); }
+};
+
+// Issue the loads of window l (entries [k0, k1), row bounds, x) and of segment l + 1.
+template <int U>
+__device__ __forceinline__ void band_stage(const BandWalk& W, BandStage<U>& B, int32_t l, int32_t k0, int32_t k1)
+{
+    const int tid = threadIdx.x;
+    const int nr = W.rows(l);
+    const int32_t i = min(W.base(l) + min(tid, max(nr - 1, 0)), W.n - 1);
+    const int32_t* __restrict__ rpi = W.rp + i;
+    B.a0 = rpi[0];
+    B.a1 = rpi[1];
+    B.xi = ld32(W.x, i);
+    // unconditional (clamped) loads: an empty window re-reads entry min(k0, nnz - 1)
+    const int32_t cnt = k1 - k0;
+    const int32_t kb = cnt > 0 ? k0 : min(k0, W.nnz - 1);
+    const double* __restrict__ vb = W.vals + kb;
+    const int32_t* __restrict__ cb = W.col + kb;
+    const int last = max(cnt - 1, 0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = min(tid + u * kBlock, last);
+        B.v[u] = ld_stream(vb + j);
+        B.c[u] = ld_stream(cb + j);
+    }
+    seg_issue(B.seg, W.rin, W.pprev, W.base(l + 1) - kBandHalo, W.n);
+}
+
+// LDS of one staged window besides its entries: this lane's row bounds (relative to
+// the window's first entry) and x.  Kept in LDS rather than in the registers the loads
+// wrote, so that summing the window never waits on the vector-memory counter while the
+// next window's loads are in flight.
+struct BandRows {
+    int32_t rs[kTile];
+    int32_t re[kTile];
+    double xi[kTile];
+};
+
+// Write stage B (window l's entries [k0, k0 + cnt), segment l + 1) into LDS.
+template <int U>
+__device__ __forceinline__ void band_commit(const BandWalk& W, const BandStage<U>& B, int32_t l, int32_t k0,
+                                            int32_t cnt, double* s_val, int32_t* s_col, BandRows* s_rows,
+                                            double* s_seg, double* s_pp, double beta)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = tid + u * kBlock;
+        if (j < cnt) {
+            s_val[j] = B.v[u];
+            s_col[j] = B.c[u];
+        }
+    }
+    const int nr = W.rows(l);
+    s_rows->rs[tid] = B.a0 - k0;
+    s_rows->re[tid] = (tid < nr) ? B.a1 - k0 : B.a0 - k0;
+    s_rows->xi[tid] = B.xi;
+    seg_commit(B.seg, s_seg, s_pp, beta, W.base(l + 1) - kBandHalo, W.n);
+}
+
+// Operand p_k at column c for window base b, from the segment holding it (slots sp,
+// so, sn hold lines l - 1, l, l + 1).  The band analysis admits a pattern only if every
+// column of every window falls in one of the three segments (an entry at distance
+// |d| <= kBandHalo lands in segment l, one at S - kBandHalo <= |d| <= S in segment
+// l +- 1), so no column is gathered from memory.  The position is clamped into the
+// segment all the same, so LDS reads stay inside the ring whatever the pattern.
+__device__ __forceinline__ double band_operand(int32_t c, int32_t b, int32_t S, const double* s_p, int sp, int so,
+                                               int sn)
+{
+    const int32_t d = c - b + kBandHalo + S;   // 0 at the first position of segment l - 1
+    const int32_t o = d - S * ((d >= S) + (d >= 2 * S));
+    const int slot = d >= 2 * S ? sn : (d >= S ? so : sp);
+    return s_p[slot * kSeg + min(max(o, 0), kSeg - 1)];
+}
+
+// Outputs of this lane's row of one window, held until they are stored.
+struct BandOut {
+    int32_t i;   // row, or -1 if the lane has none
+    double p, q, x;
+};
+
+// Row sum of this lane's row in window l (entries staged in LDS), and the row's
+// outputs: p_k, q = (A p_k)_i and the deferred update x_k = x_{k-1} + alpha_{k-1} p_{k-1}.
+template <int CAP>
+__device__ __forceinline__ BandOut band_window(const BandWalk& W, int32_t l, const double* s_val,
+                                               const int32_t* s_col, const BandRows* s_rows, const double* s_p,
+                                               const double* s_pp, int sp, int so, int sn, int po, double alpha_prev)
+{
+    constexpr int RC = row_chunk(CAP);
+    const int tid = threadIdx.x;
+    const int32_t base = W.base(l);
+    const int nr = W.rows(l);
+    const int rs = s_rows->rs[tid];
+    const int re = s_rows->re[tid];
+    double s = 0.0;
+    for (int j0 = rs; j0 < re; j0 += RC) {
+        double pv[RC];
+#pragma unroll
+        for (int u = 0; u < RC; ++u) {
+            const int j = (j0 + u < re) ? j0 + u : j0;
+            pv[u] = band_operand(s_col[j], base, W.S, s_p, sp, so, sn);
+        }
+#pragma unroll
+        for (int u = 0; u < RC; ++u) {
+            const bool ok = j0 + u < re;
+            const int j = ok ? j0 + u : j0;
+            const double tt = s_val[j] * pv[u];
+            const double sn2 = s + tt;
+            s = ok ? sn2 : s;
+        }
+    }
+    BandOut o;
+    o.i = tid < nr ? base + tid : -1;
+    o.p = s_p[so * kSeg + kBandHalo + tid];
+    o.q = s;
+    const double tx = alpha_prev * s_pp[po * kTile + tid];   // alpha_{-1} = 0 for k = 0
+    o.x = s_rows->xi[tid] + tx;
+    return o;
+}
+
+__device__ __forceinline__ void band_store(const BandOut& o, double* __restrict__ pcur, double* __restrict__ q,
+                                           double* __restrict__ x, double& sig)
+{
+    if (o.i >= 0) {
+        st32_stream(pcur, o.i, o.p);
+        st32_stream(q, o.i, o.q);
+        st32_stream(x, o.i, o.x);
+        const double u = o.p * o.q;
+        sig = sig + u;
+    }
+}
+
+// LDS of the banded SpMV.
+template <int CAP>
+struct BandLds {
+    double val[CAP];
+    int32_t col[CAP];
+    double p[3 * kSeg];     // p_k on lines l-1, l, l+1 (ring)
+    double pp[2 * kTile];   // p_{k-1} at the rows of lines l, l+1 (ring)
+    BandRows rows;
+};
+
+// One block: lines [l0, l1) of the strip W describes.  Pipeline: while window l is
+// summed from LDS, the loads of windows l + 1 and l + 2 (entries, bounds, x, segments
+// l + 2 and l + 3) are in flight in registers and the entry range of window l + 3 is
+// being read, so no load waits on another load's result.  Every load is unconditional
+// and every path that continues the loop passes a commit, so the compiler's wait counts
+// are exact and a commit leaves the newer window's loads in flight.
+template <int CAP>
+__device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_t l1, BandLds<CAP>& L, double beta,
+                                           double alpha_prev, double* __restrict__ pcur, double* __restrict__ q,
+                                           double* __restrict__ x, double& sig)
+{
+    constexpr int U = CAP / kBlock;
+    const int32_t n = W.n;
+    BandStage<U> SA, SB;
+    SegLoad Em, E0;   // segments of lines l0 - 1 and l0
+    // entry ranges [k0, k1) of windows l, l + 1, l + 2
+    int32_t k0a = W.k0(l0), k1a = W.k1(l0), k0b = 0, k1b = 0, k0c = 0, k1c = 0;
+    band_stage(W, SA, l0, k0a, k1a);
+    seg_issue(Em, W.rin, W.pprev, W.base(l0 - 1) - kBandHalo, n);
+    seg_issue(E0, W.rin, W.pprev, W.base(l0) - kBandHalo, n);
+    if (l0 + 1 < l1) {
+        k0b = W.k0(l0 + 1);
+        k1b = W.k1(l0 + 1);
+    }
+    band_stage(W, SB, l0 + 1, k0b, k1b);
+    if (l0 + 2 < l1) {
+        k0c = W.k0(l0 + 2);
+        k1c = W.k1(l0 + 2);
+    }
+    // Ring slots: line l - 1 in sp, l in so, l + 1 in sn; p_{k-1} of line l in po.
+    int sp = 0, so = 1, sn = 2, po = 0;
+    seg_commit(Em, L.p + sp * kSeg, nullptr, beta, W.base(l0 - 1) - kBandHalo, n);
+    seg_commit(E0, L.p + so * kSeg, L.pp + po * kTile, beta, W.base(l0) - kBandHalo, n);
+    band_commit(W, SA, l0, k0a, k1a - k0a, L.val, L.col, &L.rows, L.p + sn * kSeg, L.pp + (po ^ 1) * kTile, beta);
+    __syncthreads();
+    int32_t l = l0;
+    // One window l, with window l + 1's loads already in flight in `nb`: issue window
+    // l + 2's loads into `na` (free: its window l was committed), read the range of
+    // window l + 3, sum window l, commit `nb`, then store window l's rows (after the
+    // commit's wait, so that wait never includes them).  Two windows per trip so the
+    // stage buffers alternate in place.
+#define SLA_BAND_WINDOW(na, nb)                                                                            \
+    {                                                                                                      \
+        int32_t k0d = 0, k1d = 0;                                                                          \
+        band_stage(W, na, l + 2, k0c, k1c); /* past l1: harmless clamped loads, keeps counts exact */     \
+        if (l + 3 < l1) {                                                                                  \
+            k0d = W.k0(l + 3);                                                                             \
+            k1d = W.k1(l + 3);                                                                             \
+        }                                                                                                  \
+        const BandOut o = band_window<CAP>(W, l, L.val, L.col, &L.rows, L.p, L.pp, sp, so, sn, po, alpha_prev); \
+        __syncthreads(); /* window l's LDS reads are done: rotate the rings */                            \
+        const int t3 = sp;                                                                                 \
+        sp = so;                                                                                           \
+        so = sn;                                                                                           \
+        sn = t3;                                                                                           \
+        po ^= 1;                                                                                           \
+        ++l;                                                                                               \
+        k0a = k0b;                                                                                         \
+        k1a = k1b;                                                                                         \
+        k0b = k0c;                                                                                         \
+        k1b = k1c;                                                                                         \
+        k0c = k0d;                                                                                         \
+        k1c = k1d;                                                                                         \
+        if (l >= l1) {                                                                                     \
+            band_store(o, pcur, q, x, sig);                                                                \
+            break;                                                                                         \
+        }                                                                                                  \
+        band_commit(W, nb, l, k0a, k1a - k0a, L.val, L.col, &L.rows, L.p + sn * kSeg,                      \
+                    L.pp + (po ^ 1) * kTile, beta);                                                        \
+        band_store(o, pcur, q, x, sig);                                                                    \
+        __syncthreads();                                                                                   \
+    }
+#pragma unroll 1
+    while (l < l1) {
+        SLA_BAND_WINDOW(SA, SB)
+        SLA_BAND_WINDOW(SB, SA)
+    }
+#undef SLA_BAND_WINDOW
+}
+
+// Grid: (G, batch).  The blocks (strip j, lines [c B, c B + B)) are numbered
+// c * strips + j, and workgroup lb takes blocks lb, lb + G, ...: the workgroups in flight
+// cover consecutive blocks, so they stream one front of about G / strips * B lines
+// through memory together.
+template <int CAP>
+__global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
+{
+    __shared__ BandLds<CAP> L;
+    __shared__ double s_red[kBlock / 64];
+    __shared__ int64_t s_stop;
+    const int sys = blockIdx.y;
+    const int lb = blockIdx.x;
+    const int tid = threadIdx.x;
+    const bool first = (k == 0);
+    const int32_t n = static_cast<int32_t>(a.n);
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int32_t S = static_cast<int32_t>(a.band_stride);
+    const int32_t lines = static_cast<int32_t>(a.band_lines);
+    const int32_t B = a.band_block;
+    const int32_t strips = (S + kTile - 1) / kTile;
+    const int32_t nblk = strips * ((lines + B - 1) / B);
+    BandWalk W;
+    W.rp = static_cast<const int32_t*>(a.row_ptr);
+    W.col = a.col;
+    W.vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
+    W.rin = (first ? a.b : a.r) + off;              // r_k (r_0 = b)
+    W.pprev = ((k & 1) ? a.p0 : a.p1) + off;       // p_{k-1}
+    double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;   // p_k
+    double* __restrict__ x = a.x + off;
+    W.x = x;
+    W.n = n;
+    W.nnz = static_cast<int32_t>(a.nnz);
+    W.S = S;
+
+    double beta, alpha_prev;
+    const int run = cg_step_begin(a, sys, lb, k, s_red, &s_stop, beta, alpha_prev);
+    if (run == kStepStopped) return;
+    if (run == kStepStopNow) {
+        if (!first) {
+            for (int32_t b = lb; b < nblk; b += a.G) {
+                const int32_t j = b % strips;
+                const int32_t l0 = (b / strips) * B;
+                const int32_t l1 = min(l0 + B, lines);
+                const int32_t w = min(kTile, S - j * kTile);
+                for (int32_t m = l0; m < l1; ++m) {
+                    const int32_t i = m * S + j * kTile + tid;
+                    if (tid < w && i < n) {
+                        const double tx = alpha_prev * ld32(W.pprev, i);
+                        st32(x, i, ld32(x, i) + tx);
+                    }
+                }
+            }
+        }
+        return;
+    }
+    double* __restrict__ q = a.q + off;
+    double sig = 0.0;
+#pragma unroll 1
+    for (int32_t b = lb; b < nblk; b += a.G) {
+        const int32_t j = b % strips;
+        const int32_t l0 = (b / strips) * B;
+        W.pos0 = j * kTile;
+        W.w = min(kTile, S - W.pos0);
+        band_block<CAP>(W, l0, min(l0 + B, lines), L, beta, alpha_prev, pcur, q, x, sig);
+        __syncthreads();   // the next block refills the LDS
     }
     sig = block_sum(sig, s_red);
     if (tid == 0) a.part_sigma[static_cast<int64_t>(sys) * a.G + lb] = sig;
@@ -738,33 +1184,64 @@ __global__ __launch_bounds__(kBlock) void k_gather_vals(const int64_t* __restric
 // ----------------------------------------------------------------------------------
 // CSR validation and tile analysis
 // ----------------------------------------------------------------------------------
+__device__ __forceinline__ int32_t wave_max_i32(int32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ int32_t wave_min_i32(int32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
 template <typename RP>
 __global__ __launch_bounds__(kBlock) void k_validate(const RP* __restrict__ rp, const int32_t* __restrict__ col,
-                                                     int64_t n_rows, int64_t n_cols, int64_t nnz,
-                                                     int32_t* err, int32_t* tile_max)
+                                                     int64_t n_rows, int64_t n_cols, int64_t nnz, int32_t* out)
 {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
     if (i == 0) {
-        if (ld_rp(rp, 0) != 0 || ld_rp(rp, n_rows) != nnz) atomicOr(err, 1);
+        if (ld_rp(rp, 0) != 0 || ld_rp(rp, n_rows) != nnz) atomicOr(out + kChkErr, 1);
     }
+    int32_t row_len = 0, far_min = 0x7fffffff, far_max = 0;
     if (i < n_rows) {
         const int64_t a = ld_rp(rp, i), e = ld_rp(rp, i + 1);
         if (a > e || a < 0 || e > nnz) {
-            atomicOr(err, 2);
+            atomicOr(out + kChkErr, 2);
         } else {
             int64_t prev = -1;
             for (int64_t kk = a; kk < e; ++kk) {
                 const int64_t c = col[kk];
-                if (c < 0 || c >= n_cols) atomicOr(err, 4);
-                if (c <= prev) atomicOr(err, 8);
+                if (c < 0 || c >= n_cols) atomicOr(out + kChkErr, 4);
+                if (c <= prev) atomicOr(out + kChkErr, 8);
                 prev = c;
+                const int64_t d = min(c > i ? c - i : i - c, int64_t(0x7fffffff));
+                if (d > kBandHalo) {
+                    far_min = min(far_min, static_cast<int32_t>(d));
+                    far_max = max(far_max, static_cast<int32_t>(d));
+                }
             }
+            row_len = static_cast<int32_t>(min(e - a, int64_t(0x7fffffff)));
         }
         if ((i % kTile) == 0) {
             const int64_t last = min(i + kTile, n_rows);
             int64_t cnt = ld_rp(rp, last) - a;
             if (cnt > 0x7fffffff) cnt = 0x7fffffff;
-            if (cnt > 0) atomicMax(tile_max, static_cast<int32_t>(cnt));
+            if (cnt > 0) atomicMax(out + kChkTileMax, static_cast<int32_t>(cnt));
+        }
+    }
+    // one atomic per wave for the maxima / minima over rows
+    row_len = wave_max_i32(row_len);
+    far_min = wave_min_i32(far_min);
+    far_max = wave_max_i32(far_max);
+    if ((threadIdx.x & 63) == 0) {
+        if (row_len > 0) atomicMax(out + kChkRowMax, row_len);
+        if (far_max > 0) {
+            atomicMin(out + kChkFarMin, far_min);
+            atomicMax(out + kChkFarMax, far_max);
         }
     }
 }
@@ -913,6 +1390,13 @@ CgKernel spmv_kernel(int rp_bits, int cap, bool off32)
 
 inline bool off32_ok(int64_t n) { return n < (int64_t(1) << 29); }
 
+CgKernel band_kernel(int cap)
+{
+    if (cap <= kCapSmall) return k_cg_spmv_band<kCapSmall>;
+    if (cap <= kCapMid) return k_cg_spmv_band<kCapMid>;
+    return k_cg_spmv_band<kCapLarge>;
+}
+
 template <typename RP, bool O>
 hipError_t launch_matvec_rp(const RP* rp, const int32_t* col, const double* vals, const double* x, double* y,
                             int64_t n_rows, int64_t nnz, int64_t n_cols, int batch, int cap, hipStream_t s)
@@ -958,6 +1442,17 @@ int cg_blocks_per_cu(int rp_bits, int cap, int64_t n)
     return c;
 }
 
+int cg_band_blocks_per_cu(int cap)
+{
+    static int cache[3] = {};
+    int& c = cache[cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : 2)];
+    if (c > 0) return c;
+    int a = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, band_kernel(cap), kBlock, 0) != hipSuccess || a < 1) a = 1;
+    c = a;
+    return c;
+}
+
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s)
 {
     SLA_LAUNCH(k_cg_init, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a);
@@ -966,7 +1461,10 @@ hipError_t launch_cg_init(const CgArgs& a, hipStream_t s)
 
 hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s)
 {
-    SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n)), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
+    if (a.band_stride > 0)
+        SLA_LAUNCH(band_kernel(cap), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
+    else
+        SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n)), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
     return hipGetLastError();
 }
 
@@ -1014,16 +1512,16 @@ hipError_t launch_gather_vals(const int64_t* perm, const double* vals, double* o
 }
 
 hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col, int64_t n_rows, int64_t n_cols,
-                           int64_t nnz, int32_t* err, int32_t* tile_max, hipStream_t s)
+                           int64_t nnz, int32_t* out, hipStream_t s)
 {
     const int64_t nb = n_rows / kBlock + 1;   // covers row n_rows's checks via i == 0 as well
     const dim3 grid(static_cast<unsigned>(nb)), block(kBlock);
     if (rp_bits == 64)
         hipLaunchKernelGGL(k_validate<int64_t>, grid, block, 0, s, static_cast<const int64_t*>(row_ptr), col, n_rows,
-                           n_cols, nnz, err, tile_max);
+                           n_cols, nnz, out);
     else
         hipLaunchKernelGGL(k_validate<int32_t>, grid, block, 0, s, static_cast<const int32_t*>(row_ptr), col, n_rows,
-                           n_cols, nnz, err, tile_max);
+                           n_cols, nnz, out);
     return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ from . import _lib as L
 from ._lib import SlaCgInfo, SlaCgOpts, check
 
 __all__ = [
-    "csr_create", "csr_destroy", "csr_info", "matvec", "matvec_backward", "solve",
+    "csr_create", "csr_destroy", "csr_info", "csr_analysis", "matvec", "matvec_backward", "solve",
     "solve_backward", "cg_opts", "read_info", "SparseTensor", "timing",
 ]
 
@@ -103,6 +103,13 @@ def csr_info(h: Handle) -> dict:
                            C.byref(fl), C.byref(w)))
     return dict(n_rows=a.value, n_cols=b.value, nnz=c.value, row_ptr_bits=bits.value,
                 flags=fl.value, workspace_bytes=w.value)
+
+
+def csr_analysis(h: Handle) -> dict:
+    lib = L.load()
+    rm, tm, cap, band = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int64()
+    check(lib.sla_csr_analysis(h.ptr, C.byref(rm), C.byref(tm), C.byref(cap), C.byref(band)))
+    return dict(row_max=rm.value, tile_max=tm.value, spmv_cap=cap.value, band_stride=band.value)
 
 
 def _batch_of(vals: torch.Tensor, nnz: int) -> int:

@@ -106,8 +106,18 @@ typedef struct {
  *   d_col_idx  device int32 [nnz], strictly ascending within each row, in [0, n_cols).
  * The pattern is validated on the device (one pass and one host synchronisation
  * on `stream`); a malformed pattern returns SLA_ERR_INVALID_CSR and no handle.
- * The analysis (per-tile entry counts that pick the SpMV variant) is computed here.
+ * The analysis (per-tile entry counts that pick the SpMV variant, and the band test
+ * below) is computed here.
  * n_rows, n_cols < 2^31; nnz < 2^31 with 32-bit row pointers.  nnz may be 0.
+ *
+ * Band test: a square pattern with n_rows < 2^29 and nnz < 2^31 is banded with line
+ * stride S when every stored entry (i, c) has |c - i| <= 8 or S - 8 <= |c - i| <= S, where S is the
+ * largest |c - i| (5- and 9-point stencils of a grid in natural order, S = line length
+ * or line length + 1), S >= 272, rows hold at most 16 entries, and S is at least the
+ * minimum stride: 2048 by default, or the value of the environment variable
+ * SLA_BAND_MIN_STRIDE (read at each create).  The CG SpMV of a banded pattern walks
+ * the rows line by line and reads the operand from LDS; results are the same to the
+ * last bit per row as the plain SpMV's.
  */
 sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t nnz,
                           const void* d_row_ptr, int32_t row_ptr_bits, const int32_t* d_col_idx,
@@ -119,6 +129,15 @@ sla_status sla_csr_destroy(sla_csr* A);
 /* Shape and workspace queries (host outputs; any pointer may be NULL). */
 sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int64_t* nnz,
                         int32_t* row_ptr_bits, uint32_t* flags, int64_t* workspace_bytes);
+
+/*
+ * Results of the pattern analysis done at create (host outputs; any pointer may be
+ * NULL): the most entries of any row and of any 256-row tile, the LDS capacity (in
+ * entries) of the SpMV variant the CG solve uses, and the line stride S of a banded
+ * pattern (0 if the pattern is not banded, see sla_csr_create).
+ */
+sla_status sla_csr_analysis(const sla_csr* A, int32_t* row_max, int32_t* tile_max, int32_t* spmv_cap,
+                            int64_t* band_stride);
 
 /*
  * y = A x for `batch` systems sharing the pattern (paperpeel section 3.3: the
