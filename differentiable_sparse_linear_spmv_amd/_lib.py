@@ -20,9 +20,9 @@ SLA_SYMMETRIC = 1
 SLA_EAGER_TRANSPOSE = 2
 SLA_FIXED_ITERS = 1
 (SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
- SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_COUNT) = range(8)
+ SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_COUNT) = range(9)
 KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "gather_vals",
-                "transpose"]
+                "transpose", "cg_pupd"]
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
@@ -78,7 +78,8 @@ def load():
     L.sla_csr_info.argtypes = [P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64),
                                C.POINTER(i32), C.POINTER(u32), C.POINTER(i64)]
     L.sla_csr_info.restype = st
-    L.sla_csr_analysis.argtypes = [P, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32), C.POINTER(i64)]
+    L.sla_csr_analysis.argtypes = [P, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32), C.POINTER(i64),
+                                   C.POINTER(i32)]
     L.sla_csr_analysis.restype = st
     L.sla_matvec.argtypes = [P, i64, P, P, P, P]
     L.sla_matvec.restype = st

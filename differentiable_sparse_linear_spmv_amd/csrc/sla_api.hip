@@ -45,6 +45,8 @@ struct sla_csr {
     // Banded pattern (line-walking SpMV): line stride S, 0 if the plain SpMV is used.
     int64_t band = 0;
     int band_cap = kCapSmall;
+    // Split CG schedule (unstructured patterns); the transposed pattern has the same span.
+    bool split = false;
     // transposed pattern (lazily built unless SLA_SYMMETRIC)
     bool has_t = false;
     void* row_ptr_t = nullptr;
@@ -335,13 +337,14 @@ sla_status ensure_vals_t(sla_csr* A, int64_t batch, const double* vals, hipStrea
 // band > 0: the pattern is banded with line stride `band` and takes the line-walking
 // SpMV (LDS variant band_cap) on a persistent grid over blocks of lines of one strip.
 sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t band, int band_cap,
-                  int64_t batch, const double* vals, const double* b, double* x, const sla_cg_opts* o,
+                  bool split, int64_t batch, const double* vals, const double* b, double* x, const sla_cg_opts* o,
                   sla_cg_info* info, hipStream_t s)
 {
     const int64_t n = A->n_rows;
     const int64_t ntiles = (n + kTile - 1) / kTile;
     // Grid of the plain SpMV (also the base of the update kernel's grid).
-    const int Gp = blocks_per_system(A, ntiles, batch, cg_blocks_per_cu(A->krp_bits, cap, n));
+    if (band > 0) split = false;
+    const int Gp = blocks_per_system(A, ntiles, batch, cg_blocks_per_cu(A->krp_bits, cap, n, split));
     int G = Gp, band_block = 0;
     int64_t band_lines = 0;
     if (band > 0) {
@@ -402,6 +405,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.batch = static_cast<int32_t>(batch);
     a.xcd_remap = 1;
     a.sys_per_xcd = (batch >= 8 && batch % 8 == 0) ? 1 : 0;
+    a.split = split ? 1 : 0;
     a.band_block = band_block;
     a.band_stride = band;
     a.band_lines = band_lines;
@@ -411,6 +415,10 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "cg init launch: %s", hipGetErrorString(e));
 
     auto step = [&](int64_t k) -> hipError_t {
+        if (a.split) {
+            hipError_t e0 = timed(SLA_K_CG_PUPD, s, [&] { return launch_cg_pupd(a, k, s); });
+            if (e0 != hipSuccess) return e0;
+        }
         hipError_t e1 = timed(SLA_K_CG_SPMV, s, [&] { return launch_cg_spmv(a, k, rp_bits, cap, s); });
         if (e1 != hipSuccess || k >= a.max_iter) return e1;
         return timed(SLA_K_CG_UPDATE, s, [&] { return launch_cg_update(a, k, s); });
@@ -562,6 +570,11 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
     A->cap = choose_cap(h[kChkTileMax]);
     A->band = band_stride_of(n_rows, n_cols, nnz, h[kChkRowMax], h[kChkFarMin], h[kChkFarMax]);
     A->band_cap = choose_cap(kTile * std::max<int32_t>(h[kChkRowMax], 1));
+    A->split = A->band == 0 && h[kChkFarMax] >= kSplitMinSpan;
+    if (const char* env = std::getenv("SLA_CG_SCHEDULE")) {   // "fused" or "split" overrides the choice
+        if (std::strcmp(env, "fused") == 0) A->split = false;
+        if (std::strcmp(env, "split") == 0) A->split = A->band == 0;
+    }
     A->krp = d_row_ptr;
     A->krp_bits = row_ptr_bits;
     if (row_ptr_bits == 64 && nnz < (int64_t(1) << 31)) {
@@ -603,13 +616,14 @@ sla_status sla_csr_destroy(sla_csr* A)
 }
 
 sla_status sla_csr_analysis(const sla_csr* A, int32_t* row_max, int32_t* tile_max, int32_t* spmv_cap,
-                            int64_t* band_stride)
+                            int64_t* band_stride, int32_t* cg_split)
 {
     if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
     if (row_max) *row_max = A->row_max;
     if (tile_max) *tile_max = A->tile_max;
     if (spmv_cap) *spmv_cap = A->band > 0 ? A->band_cap : A->cap;
     if (band_stride) *band_stride = A->band;
+    if (cg_split) *cg_split = A->split ? 1 : 0;
     return SLA_OK;
 }
 
@@ -698,7 +712,8 @@ sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, con
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
-    st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, batch, d_vals, d_b, d_x, opts, d_info, s);
+    st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_b, d_x, opts, d_info,
+                s);
     if (st == SLA_OK && !(opts->flags & SLA_FIXED_ITERS)) {
         hipError_t e = timing_collect();
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
@@ -720,12 +735,13 @@ sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
     if (A->flags & SLA_SYMMETRIC) {
-        st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, batch, d_vals, d_gx, d_gb, opts, d_info, s);
+        st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_gx, d_gb, opts,
+                    d_info, s);
     } else {
         if ((st = ensure_transpose(A, s)) != SLA_OK) return st;
         const double* vt = nullptr;
         if ((st = ensure_vals_t(A, batch, d_vals, s, &vt)) != SLA_OK) return st;
-        st = run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, 0, 0, batch, vt, d_gx, d_gb, opts, d_info, s);
+        st = run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, 0, 0, A->split, batch, vt, d_gx, d_gb, opts, d_info, s);
     }
     if (st != SLA_OK) return st;
     if (d_gvals) {

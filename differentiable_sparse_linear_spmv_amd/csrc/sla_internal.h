@@ -32,6 +32,11 @@ constexpr int kBandBlockLines = 32;
 constexpr int kBandBlocksPerCu = 2;
 constexpr int64_t kBandStreamBytes = int64_t(1) << 30;
 
+// Patterns that are not banded but reach columns at least this far from the diagonal
+// gather from all over the operand: they take the split CG schedule (p_k formed by its
+// own pass, then gathered alone), which halves the gathers' cache requests.
+constexpr int64_t kSplitMinSpan = 4096;
+
 // Per-system CG state in device memory (64 bytes).  Double-buffered by the
 // parity of the iteration index so that a kernel reads the previous value while
 // its first workgroup writes the new one.
@@ -74,6 +79,7 @@ struct CgArgs {
     int32_t batch;
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
     int32_t sys_per_xcd;     // 1: batch % 8 == 0; every system runs on one XCD
+    int32_t split;           // 1: split schedule (k_cg_pupd forms p_k, the SpMV gathers it)
     int32_t band_block;      // banded SpMV: lines per block of work
     int64_t band_stride;     // banded SpMV: line length S (0: plain SpMV)
     int64_t band_lines;      // banded SpMV: ceil(n / S)
@@ -89,13 +95,14 @@ LaunchEvents& launch_events();
 
 // Resident workgroups per CU of the SpMV kernel variant for this pattern (its grid is
 // sized to fill the GPU exactly once).
-int cg_blocks_per_cu(int rp_bits, int cap, int64_t n);
+int cg_blocks_per_cu(int rp_bits, int cap, int64_t n, bool split);
 int cg_band_blocks_per_cu(int cap);   // the banded SpMV (32-bit row pointers only)
 
 // Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s);
 hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s);
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s);
+hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s);   // split schedule
 
 hipError_t launch_matvec(const void* row_ptr, int rp_bits, const int32_t* col, const double* vals,
                          const double* x, double* y, int64_t n_rows, int64_t nnz, int64_t n_cols,

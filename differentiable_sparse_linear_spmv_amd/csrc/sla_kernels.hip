@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "sla_internal.h"
 
@@ -419,7 +420,7 @@ struct TileStage {
 // Issue (without waiting) the loads of tile t.  k0 / k1 are the tile's first and
 // end entry positions (known two tiles ahead).  Indices are clamped so no load sits
 // behind a branch; the tile's entries are staged only if they fit the LDS cap.
-template <typename RP, int CAP, bool OFF32>
+template <typename RP, int CAP, bool OFF32, bool SPLIT>
 __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const RP* __restrict__ rp,
                                            const int32_t* __restrict__ col, const double* __restrict__ vals,
                                            const double* __restrict__ rin, const double* __restrict__ pprev,
@@ -433,9 +434,11 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
     const int64_t i = row0 + min(tid, nr - 1);
     S.a0 = rp[i];
     S.a1 = rp[i + 1];
-    S.ri = ldv<OFF32>(rin, i);
-    S.ppi = ldv<OFF32>(pprev, i);
-    S.xi = x[i];
+    S.ri = ldv<OFF32>(rin, i);   // with SPLIT: p_k (rin is the formed operand)
+    if constexpr (!SPLIT) {
+        S.ppi = ldv<OFF32>(pprev, i);
+        S.xi = x[i];
+    }
     const int64_t cnt = k1 - k0;
     if (cnt <= CAP && cnt > 0) {
         const double* __restrict__ vb = vals + k0;
@@ -456,7 +459,12 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
 // the one after), so each tile costs about one memory round trip instead of four.
 // The first tile is staged before the stop check and the reduction of the rho
 // partials, which overlaps the kernel's start-up latency with useful loads.
-template <typename RP, int CAP, bool OFF32>
+//
+// SPLIT: the split schedule for unstructured patterns.  k_cg_pupd has already taken
+// the step's decisions and formed p_k (and the x update); this kernel gathers p_k
+// alone, one load per stored entry instead of two (r_k and p_{k-1}), and computes q
+// and the partial p^T q.  The row sums are the same to the last bit.
+template <typename RP, int CAP, bool OFF32, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
 {
     constexpr int U = CAP / kBlock;
@@ -494,14 +502,20 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     if (t < ntiles) {
         k0 = tile_k0(t);
         k1 = tile_k1(t);
-        stage_tile<RP, CAP, OFF32>(SA, rp, col, vals, rin, pprev, x, tile_of(t), n, k0, k1);
+        stage_tile<RP, CAP, OFF32, SPLIT>(SA, rp, col, vals, SPLIT ? pcur : rin, pprev, x, tile_of(t), n, k0, k1);
     }
     if (t + Gs < ntiles) {
         k0n = tile_k0(t + Gs);
         k1n = tile_k1(t + Gs);
     }
 
-    double beta, alpha_prev;
+    double beta = 0.0, alpha_prev = 0.0;
+    if constexpr (SPLIT) {
+        // k_cg_pupd of this step wrote stop_iter = k if the system stops here
+        if (tid == 0) s_stop = a.st[sys].stop_iter;
+        __syncthreads();
+        if (s_stop <= k) return;
+    } else {
     const int run = cg_step_begin(a, sys, lb, k, s_red, &s_stop, beta, alpha_prev);
     if (run == kStepStopped) return;
     if (run == kStepStopNow) {
@@ -517,9 +531,14 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         }
         return;
     }
+    }
 
     double* __restrict__ q = a.q + off;
-    GatherCG<OFF32> g{rin, pprev, beta};
+    // the gathered operand: p_k formed on the fly, or (SPLIT) read as formed
+    using Gather = std::conditional_t<SPLIT, GatherX<OFF32>, GatherCG<OFF32>>;
+    Gather g;
+    if constexpr (SPLIT) g = GatherX<OFF32>{pcur};
+    else g = GatherCG<OFF32>{rin, pprev, beta};
     double sig = 0.0;
     // Process tile t from stage `cur` while staging the next tile into `nxt`.
     auto process = [&](TileStage<RP, U>& cur, TileStage<RP, U>& nxt) {
@@ -557,7 +576,9 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
                 const int64_t c = (rs + u < re) ? static_cast<int64_t>(s_col[rs + u]) : i;
                 pv[u] = g(c);
             }
-            if (tn < ntiles) stage_tile<RP, CAP, OFF32>(nxt, rp, col, vals, rin, pprev, x, tile_of(tn), n, k0n, k1n);
+            if (tn < ntiles)
+                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? pcur : rin, pprev, x, tile_of(tn), n,
+                                                  k0n, k1n);
 #pragma unroll
             for (int u = 0; u < RC; ++u) {
                 const bool ok = rs + u < re;
@@ -585,17 +606,25 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
             __syncthreads();
         } else {
             s = tile_rowsum_long(rp, col, vals, row0, nr, g, s_val);
-            if (tn < ntiles) stage_tile<RP, CAP, OFF32>(nxt, rp, col, vals, rin, pprev, x, tile_of(tn), n, k0n, k1n);
+            if (tn < ntiles)
+                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? pcur : rin, pprev, x, tile_of(tn), n,
+                                                  k0n, k1n);
         }
         if (tid < nr) {
-            const double tp = beta * ppi;
-            const double pi = ri + tp;           // same expression as the gathered p_k
-            pcur[i] = pi;
-            q[i] = s;
-            const double tx = alpha_prev * ppi;   // alpha_{-1} = 0 for k = 0
-            x[i] = xi + tx;
-            const double u = pi * s;
-            sig = sig + u;
+            if constexpr (SPLIT) {
+                q[i] = s;
+                const double u = ri * s;          // ri holds p_k here
+                sig = sig + u;
+            } else {
+                const double tp = beta * ppi;
+                const double pi = ri + tp;           // same expression as the gathered p_k
+                pcur[i] = pi;
+                q[i] = s;
+                const double tx = alpha_prev * ppi;   // alpha_{-1} = 0 for k = 0
+                x[i] = xi + tx;
+                const double u = pi * s;
+                sig = sig + u;
+            }
         }
         k0 = k0n;
         k1 = k1n;
@@ -1034,6 +1063,55 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
     if (tid == 0) a.part_sigma[static_cast<int64_t>(sys) * a.G + lb] = sig;
 }
 
+// k_cg_pupd (split schedule): the step's decisions (cg_step_begin), then for the
+// workgroup's rows p_k = r_k + beta_k p_{k-1} and the deferred x_k = x_{k-1} +
+// alpha_{k-1} p_{k-1}, the same expressions the fused SpMV evaluates.  Grid (Gu, batch).
+__global__ __launch_bounds__(kBlock) void k_cg_pupd(CgArgs a, int64_t k)
+{
+    __shared__ double s_red[kBlock / 64];
+    __shared__ int64_t s_stop;
+    const BlockCoord bc = block_coord(a, a.Gu);
+    const int sys = bc.sys;
+    const int tid = threadIdx.x;
+    const TileRange tr = bc.tr;
+    const bool first = (k == 0);
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t n = a.n;
+    const double* __restrict__ rin = (first ? a.b : a.r) + off;
+    const double* __restrict__ pprev = ((k & 1) ? a.p0 : a.p1) + off;
+    double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;
+    double* __restrict__ x = a.x + off;
+    double beta, alpha_prev;
+    const int run = cg_step_begin(a, sys, bc.lb, k, s_red, &s_stop, beta, alpha_prev);
+    if (run == kStepStopped) return;
+    const bool stop = (run == kStepStopNow);
+    if (stop && first) return;
+#pragma unroll 1
+    for (int64_t m0 = tr.first; m0 < tr.len; m0 += kStreamUnroll * tr.step) {
+        double rv[kStreamUnroll], pv[kStreamUnroll], xv[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t i = min((tr.lo + m0 + u * tr.step) * kTile + tid, n - 1);
+            rv[u] = rin[i];
+            pv[u] = pprev[i];
+            xv[u] = x[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t m = m0 + u * tr.step;
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (m < tr.len && i < n) {
+                const double tx = alpha_prev * pv[u];   // alpha_{-1} = 0 for k = 0
+                x[i] = xv[u] + tx;
+                if (!stop) {
+                    const double tp = beta * pv[u];
+                    pcur[i] = rv[u] + tp;
+                }
+            }
+        }
+    }
+}
+
 // Loads of one trip of the update kernel: kStreamUnroll tiles t0, t0 + step, ...
 // (clamped indices; masked on use).
 __device__ __forceinline__ void load_trip(const TileRange& tr, int64_t m0, int64_t n, const double* __restrict__ q,
@@ -1374,18 +1452,25 @@ hipError_t scan_exclusive(int64_t* data, int64_t n, int64_t* scratch, hipStream_
 
 using CgKernel = void (*)(CgArgs, int64_t);
 
-template <typename RP, bool O>
+template <typename RP, bool O, bool SPLIT>
 CgKernel spmv_kernel_rp(int cap)
 {
-    if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O>;
-    if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O>;
-    return k_cg_spmv<RP, kCapLarge, O>;
+    if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O, SPLIT>;
+    if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O, SPLIT>;
+    return k_cg_spmv<RP, kCapLarge, O, SPLIT>;
 }
 
-CgKernel spmv_kernel(int rp_bits, int cap, bool off32)
+template <bool SPLIT>
+CgKernel spmv_kernel_split(int rp_bits, int cap, bool off32)
 {
-    if (rp_bits == 64) return off32 ? spmv_kernel_rp<int64_t, true>(cap) : spmv_kernel_rp<int64_t, false>(cap);
-    return off32 ? spmv_kernel_rp<int32_t, true>(cap) : spmv_kernel_rp<int32_t, false>(cap);
+    if (rp_bits == 64)
+        return off32 ? spmv_kernel_rp<int64_t, true, SPLIT>(cap) : spmv_kernel_rp<int64_t, false, SPLIT>(cap);
+    return off32 ? spmv_kernel_rp<int32_t, true, SPLIT>(cap) : spmv_kernel_rp<int32_t, false, SPLIT>(cap);
+}
+
+CgKernel spmv_kernel(int rp_bits, int cap, bool off32, bool split = false)
+{
+    return split ? spmv_kernel_split<true>(rp_bits, cap, off32) : spmv_kernel_split<false>(rp_bits, cap, off32);
 }
 
 inline bool off32_ok(int64_t n) { return n < (int64_t(1) << 29); }
@@ -1426,16 +1511,17 @@ hipError_t launch_matvec_any(const RP* rp, const int32_t* col, const double* val
 // ----------------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------------
-int cg_blocks_per_cu(int rp_bits, int cap, int64_t n)
+int cg_blocks_per_cu(int rp_bits, int cap, int64_t n, bool split)
 {
-    static int cache[2][3][2] = {};   // occupancy is fixed per variant: query once
+    static int cache[2][3][2][2] = {};   // occupancy is fixed per variant: query once
     const int ri = rp_bits == 64 ? 1 : 0;
     const int ci = cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : 2);
     const bool o = off32_ok(n);
-    int& c = cache[ri][ci][o ? 1 : 0];
+    int& c = cache[ri][ci][o ? 1 : 0][split ? 1 : 0];
     if (c > 0) return c;
     int a = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, spmv_kernel(rp_bits, cap, o), kBlock, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, spmv_kernel(rp_bits, cap, o, split), kBlock, 0) !=
+            hipSuccess ||
         a < 1)
         a = 1;
     c = a;
@@ -1464,7 +1550,14 @@ hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipS
     if (a.band_stride > 0)
         SLA_LAUNCH(band_kernel(cap), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
     else
-        SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n)), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
+        SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n), a.split != 0), dim3(a.G, a.batch), dim3(kBlock), 0, s,
+                   a, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s)
+{
+    SLA_LAUNCH(k_cg_pupd, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
     return hipGetLastError();
 }
 

@@ -107,9 +107,11 @@ def csr_info(h: Handle) -> dict:
 
 def csr_analysis(h: Handle) -> dict:
     lib = L.load()
-    rm, tm, cap, band = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int64()
-    check(lib.sla_csr_analysis(h.ptr, C.byref(rm), C.byref(tm), C.byref(cap), C.byref(band)))
-    return dict(row_max=rm.value, tile_max=tm.value, spmv_cap=cap.value, band_stride=band.value)
+    rm, tm, cap, band, split = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int64(), C.c_int32()
+    check(lib.sla_csr_analysis(h.ptr, C.byref(rm), C.byref(tm), C.byref(cap), C.byref(band),
+                               C.byref(split)))
+    return dict(row_max=rm.value, tile_max=tm.value, spmv_cap=cap.value, band_stride=band.value,
+                split=bool(split.value))
 
 
 def _batch_of(vals: torch.Tensor, nnz: int) -> int:

@@ -133,11 +133,21 @@ sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int6
 /*
  * Results of the pattern analysis done at create (host outputs; any pointer may be
  * NULL): the most entries of any row and of any 256-row tile, the LDS capacity (in
- * entries) of the SpMV variant the CG solve uses, and the line stride S of a banded
- * pattern (0 if the pattern is not banded, see sla_csr_create).
+ * entries) of the SpMV variant the CG solve uses, the line stride S of a banded
+ * pattern (0 if the pattern is not banded, see sla_csr_create), and whether the CG
+ * solve uses the split schedule (1) or the fused one (0).
+ *
+ * Schedules.  Fused: one SpMV kernel forms p_k = r_k + beta p_{k-1} at every gathered
+ * column, applies the deferred x update and computes q = A p_k and p_k^T q; then one
+ * update kernel.  Split: a streaming kernel first forms p_k and the x update, so the
+ * SpMV gathers p_k alone (half the gather requests, one more vector pass).  A pattern
+ * that is not banded but has an entry at |c - i| >= 4096 takes the split schedule
+ * (unstructured gathers); the environment variable SLA_CG_SCHEDULE ("fused" or
+ * "split", read at each create) overrides the choice.  Banded patterns use their own
+ * SpMV.  The schedules give the same row sums to the last bit.
  */
 sla_status sla_csr_analysis(const sla_csr* A, int32_t* row_max, int32_t* tile_max, int32_t* spmv_cap,
-                            int64_t* band_stride);
+                            int64_t* band_stride, int32_t* cg_split);
 
 /*
  * y = A x for `batch` systems sharing the pattern (paperpeel section 3.3: the
@@ -197,13 +207,14 @@ sla_status sla_solve_backward(const sla_csr* A, int64_t batch, const double* d_v
  */
 enum {
     SLA_K_CG_INIT = 0,      /* r0 partial norms, x = 0, per-system state reset */
-    SLA_K_CG_SPMV = 1,      /* p = r + beta p (on the fly), x update, q = A p, partial p^T q */
+    SLA_K_CG_SPMV = 1,      /* q = A p, partial p^T q (fused schedule: p = r + beta p on the fly, x update) */
     SLA_K_CG_UPDATE = 2,    /* alpha, r -= alpha q, partial r^T r */
     SLA_K_MATVEC = 3,       /* y = A x */
     SLA_K_PATTERN_OUTER = 4,/* gvals = s * u[row] * v[col] */
     SLA_K_GATHER_VALS = 5,  /* transposed values */
     SLA_K_TRANSPOSE = 6,    /* pattern transpose (all its kernels) */
-    SLA_K_COUNT = 7
+    SLA_K_CG_PUPD = 7,      /* split schedule: step decisions, p = r + beta p, x update */
+    SLA_K_COUNT = 8
 };
 sla_status sla_timing_enable(int32_t enable);
 sla_status sla_timing_reset(void);

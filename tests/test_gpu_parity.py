@@ -8,7 +8,8 @@ Bars (from the parity contract of this library):
   lambda, dL/dvals     relative L2 difference <= 1e-8.
   integer / index work bit-exact (transposed pattern, gradient scatter from equal inputs).
 Sizes span several 256-row tiles with a ragged tail; the 64 x 64 Poisson case is the
-small benchmark workload itself.
+small benchmark workload itself.  Each test runs under both CG schedules (fused and
+split, see sla_csr_analysis) and under the automatic choice.
 """
 import math
 
@@ -30,6 +31,18 @@ def S():
         pytest.skip("no GPU")
     import differentiable_sparse_linear_spmv_amd as S
     return S
+
+
+# Every test runs under the CG schedule the analysis picks and under each one forced
+# (the split schedule is the automatic choice for the FEM meshes, the fused one for
+# the grids): same bars for both.
+@pytest.fixture(autouse=True, params=["auto", "fused", "split"])
+def schedule(request, monkeypatch):
+    if request.param == "auto":
+        monkeypatch.delenv("SLA_CG_SCHEDULE", raising=False)
+    else:
+        monkeypatch.setenv("SLA_CG_SCHEDULE", request.param)
+    return request.param
 
 
 def dev(a):
@@ -379,3 +392,12 @@ def test_autograd_solve_and_matvec(S):
     gx, gv = O.matvec_backward(A, t, w)
     assert np.array_equal(host(xv.grad), gx)
     assert np.array_equal(host(vals.grad), gv)
+
+
+def test_schedule_choice(S, schedule):
+    fem, _ = W.fem_p1_batched(nv=100, B=2, seed=2)   # permuted: entries up to n apart
+    grid = W.poisson5(40)
+    a_fem, a_grid = S.csr_analysis(handle(S, fem)), S.csr_analysis(handle(S, grid))
+    expect_fem = {"auto": True, "fused": False, "split": True}[schedule]
+    expect_grid = {"auto": False, "fused": False, "split": True}[schedule]
+    assert a_fem["split"] == expect_fem and a_grid["split"] == expect_grid
