@@ -8,8 +8,10 @@
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC (see oracle/build.py).
  * Contraction is off so every product is rounded before it is added: the row
- * sums and dot products below are plain sequential fp64 sums in ascending index
- * order, with no fused multiply-add.
+ * sums of the SpMV below are plain sequential fp64 sums in ascending entry order,
+ * with no fused multiply-add.  Inner products are the exact sums rounded once (to
+ * within a unit in the last place; see orc_dot), so that the reference does not
+ * carry the rounding error of one particular summation order.
  *
  * Sources (torch-sla: Differentiable Sparse Linear Algebra with Adjoint Solvers
  * and Sparse Tensor Parallelism for PyTorch):
@@ -67,14 +69,29 @@ void orc_spmv_transposed(int64_t n_rows, int64_t n_cols, const int64_t* row_ptr,
     }
 }
 
+/*
+ * Inner product <a, b> = sum_i a_i b_i, computed as the exact sum rounded once to
+ * fp64, up to the last bit: the compensated dot product "Dot2" of Ogita, Rump and
+ * Oishi (Accurate sum and dot product, SIAM J. Sci. Comput. 26(6), 2005), whose result
+ * is as accurate as if it had been accumulated in twice the working precision and
+ * then rounded.  Every product is split exactly into its rounded value h and the
+ * remainder r (r by fma, which rounds a_i b_i - h once, and that is exact), every
+ * running addition exactly into its rounded sum and remainder q (Knuth's two-sum),
+ * and the remainders are added up beside the main sum.
+ */
 double orc_dot(int64_t n, const double* a, const double* b)
 {
-    double s = 0.0;
+    double s = 0.0, c = 0.0;
     for (int64_t i = 0; i < n; ++i) {
-        double t = a[i] * b[i];
-        s = s + t;
+        double h = a[i] * b[i];
+        double r = fma(a[i], b[i], -h);          /* a_i b_i = h + r exactly */
+        double t = s + h;
+        double z = t - s;
+        double q = (s - (t - z)) + (h - z);      /* s + h = t + q exactly */
+        s = t;
+        c = c + (q + r);
     }
-    return s;
+    return s + c;
 }
 
 /*

@@ -3,8 +3,8 @@
 * poisson1024, varcoef2048, fem256x256: the full solve + adjoint against the
   oracle's values stored in tests/golden/*.json (written by
   tests/golden/make_golden.py, which calls only the oracle): iteration counts within
-  2 % (4 % for the FEM batch, see ITER_BAR), x within 1e-9, lambda and dL/dvals
-  within 1e-8 (relative, on seeded samples and on the norms).
+  2 % (every system of the FEM batch), x within 1e-9, lambda and dL/dvals within 1e-8
+  (relative, on seeded samples and on the norms).
 * poisson13000 (169M unknowns, int64 row pointers), in the launch configuration the
   benchmark uses:
     - the first 20 fixed iterations against the oracle's residual history and
@@ -56,13 +56,13 @@ def rel(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-# Iteration-count bars.  2 % for the Poisson systems.  The FEM systems converge on a
-# nearly flat stretch of the residual curve, where the crossing of 1e-8 moves with
-# the summation order of the dot products alone: on system 0 the oracle (sequential
-# sums) and a numpy CG (pairwise sums) on identical inputs stop 4662 vs 4523 adjoint
-# iterations apart (3.0 %) while their solutions agree to 2e-12.  No reduction order
-# other than the oracle's can meet 2 % there, so the FEM bar is 4 %.
-ITER_BAR = {"poisson1024": 0.02, "varcoef2048": 0.02, "fem256x256": 0.04}
+# Iteration-count bar: 2 % everywhere.  The FEM systems converge on a nearly flat
+# stretch of the residual curve, where the crossing of 1e-8 moves with the rounding of
+# the inner products alone; the oracle therefore takes each inner product as the exact
+# sum rounded once (not a sequential sum, which alone moves the FEM counts by up to
+# 4.4 % against an extended-precision reference), and against that the GPU's tree sums
+# stay within about 1 %.
+ITER_BAR = {"poisson1024": 0.02, "varcoef2048": 0.02, "fem256x256": 0.02}
 
 
 def iters_close(k_gpu, k_orc, bar=0.02):

@@ -27,6 +27,8 @@ MUTANTS = {
     "threshold not relative": ("double thr = rtol * bnorm;", "double thr = rtol;"),
     "adjoint ignores transpose": ("if (symmetric) {", "if (1) {"),
     "transposed spmv is forward": ("y[col[k]] = y[col[k]] + t;", "y[i] = y[i] + val[k] * x[col[k]];"),
+    "dot drops the product remainders": ("c = c + (q + r);", "c = c + q;"),
+    "dot is a plain sequential sum": ("return s + c;", "return s;"),
 }
 
 

@@ -99,14 +99,30 @@ def test_spmv_transposed_matches_dense_on_nonsymmetric():
     assert not np.allclose(D, D.T)
 
 
-def test_dot_is_plain_sum():
+def exact_dot(a, b):
+    """sum a_i b_i in exact rational arithmetic, rounded once (float(Fraction) rounds
+    correctly)."""
+    from fractions import Fraction
+    return float(sum((Fraction(x) * Fraction(y) for x, y in zip(a.tolist(), b.tolist())), Fraction(0)))
+
+
+def test_dot_is_the_exact_sum_rounded():
+    # the inner product is the exact sum rounded once, not one summation order's result
     a = np.array([1e16, 1.0, -1e16, 1.0])
     b = np.ones(4)
-    # sequential left-to-right: ((1e16 + 1) - 1e16) + 1 = 0 + 1 = 1 in fp64
-    assert O.dot(a, b) == 1.0
+    assert O.dot(a, b) == 2.0            # sequential fp64 gives 1.0, pairwise 0.0
+    a = np.array([1.0 + 2.0 ** -30, 1.0])
+    b = np.array([1.0 - 2.0 ** -30, -1.0])
+    assert O.dot(a, b) == -(2.0 ** -60)  # needs the product's rounding error
     rng = np.random.default_rng(0)
-    a, b = rng.standard_normal(1000), rng.standard_normal(1000)
-    assert abs(O.dot(a, b) - float(np.dot(a, b))) <= 1000 * EPS * float(np.abs(a) @ np.abs(b))
+    for trial in range(20):
+        n = int(rng.integers(1, 2000))
+        a = rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 6, n)
+        b = rng.standard_normal(n)
+        if trial % 2:                    # heavy cancellation: append the negated products
+            a, b = np.concatenate([a, -a * (1 + 2.0 ** -40)]), np.concatenate([b, b])
+        e = exact_dot(a, b)
+        assert abs(O.dot(a, b) - e) <= np.spacing(abs(e)), trial
 
 
 # ----------------------------------------------------------------------------- CG
