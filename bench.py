@@ -48,19 +48,31 @@ def kernel_source_hash() -> str:
 
 
 # ------------------------------------------------------------------------------ bytes model
-def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
+def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False) -> dict:
     """Algorithmic HBM bytes of the kernels, per launch (all systems of the batch).
 
     rp_bytes is the width of the row pointers the kernels read: 4 whenever nnz < 2^31
     (the library keeps a 32-bit copy of 64-bit row pointers that fit).
 
-    cg_spmv : values 8 nnz B + columns 4 nnz + row pointers rp (n + 1)
-              + vectors: read r, p_{k-1}, x; write p_k, q, x  -> 6 x 8 n B
-    cg_update: read r, q; write r                             -> 3 x 8 n B
-    One CG iteration = both (nine vector passes).
+    Fused schedule (plain or banded SpMV):
+      cg_spmv  : values 8 nnz B + columns 4 nnz + row pointers rp (n + 1)
+                 + vectors: read r, p_{k-1}, x; write p_k, q, x   -> 6 x 8 n B
+      cg_update: read r, q; write r                              -> 3 x 8 n B
+      one CG iteration = both (nine vector passes).
+    Split schedule (unstructured patterns):
+      cg_pupd  : read r, p_{k-1}, x; write p_k, x                 -> 5 x 8 n B
+      cg_spmv  : values, columns, row pointers + read p_k (own row; the gathers are
+                 cache traffic), write q                          -> 2 x 8 n B
+      cg_update: as above; one iteration = ten vector passes.
     """
-    spmv = 8 * nnz * batch + 4 * nnz + rp_bytes * (n + 1) + 6 * 8 * n * batch
+    mat = 8 * nnz * batch + 4 * nnz + rp_bytes * (n + 1)
     upd = 3 * 8 * n * batch
+    if split:
+        pupd = 5 * 8 * n * batch
+        spmv = mat + 2 * 8 * n * batch
+        return dict(cg_pupd=pupd, cg_spmv=spmv, cg_update=upd, iteration=pupd + spmv + upd,
+                    flops_iteration=(2 * nnz + 10 * n) * batch)
+    spmv = mat + 6 * 8 * n * batch
     return dict(cg_spmv=spmv, cg_update=upd, iteration=spmv + upd,
                 flops_iteration=(2 * nnz + 10 * n) * batch)
 
@@ -178,10 +190,19 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
 
     fr, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
     copy_f, copy_w = copy_of(fr), copy_of(wr)
-    spmv_f, nf = per_kernel(fr, "k_cg_spmv")
-    spmv_w, nw = per_kernel(wr, "k_cg_spmv")
-    upd_f, _ = per_kernel(fr, "k_cg_update")
-    upd_w, _ = per_kernel(wr, "k_cg_update")
+    def pick(rows, names):
+        for nm in names:
+            v = per_kernel(rows, nm)
+            if v[0] is not None:
+                return v
+        return None, 0
+
+    spmv_f, nf = pick(fr, ["k_cg_spmv", "k_gcg_spmv"])
+    spmv_w, nw = pick(wr, ["k_cg_spmv", "k_gcg_spmv"])
+    upd_f, _ = pick(fr, ["k_cg_update", "k_gcg_update"])
+    upd_w, _ = pick(wr, ["k_cg_update", "k_gcg_update"])
+    pupd_f, _ = pick(fr, ["k_cg_pupd", "k_gcg_pupd"])
+    pupd_w, _ = pick(wr, ["k_cg_pupd", "k_gcg_pupd"])
     kib = 1024.0
     sf = COPY_BYTES / (copy_f * kib) if copy_f else 1.0
     sw = COPY_BYTES / (copy_w * kib) if copy_w else 1.0
@@ -193,7 +214,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
                fetch_kib_per_launch=spmv_f, write_kib_per_launch=spmv_w, launches=[nf, nw],
                copy_fetch_kib=copy_f, copy_write_kib=copy_w, fetch_scale=sf, write_scale=sw,
                bytes_per_launch=(spmv_f * kib * sf + spmv_w * kib * sw) if spmv_f and spmv_w else None,
-               update_bytes_per_launch=(upd_f * kib * sf + upd_w * kib * sw) if upd_f and upd_w else None)
+               update_bytes_per_launch=(upd_f * kib * sf + upd_w * kib * sw) if upd_f and upd_w else None,
+               pupd_bytes_per_launch=(pupd_f * kib * sf + pupd_w * kib * sw) if pupd_f and pupd_w else None)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     p = os.path.join(ROOT, "profiles", f"cg_spmv_{workload}_traffic.txt")
     with open(p, "w") as f:
@@ -235,6 +257,16 @@ def main() -> int:
     n, nnz, B = w["n"], w["nnz"], w["batch"]
     rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
     h = S.csr_create(w["rp"], w["col"], symmetric=True)
+    an = S.csr_analysis(h)
+    if an["band_stride"] > 0:
+        spmv_kernel, schedule = "k_cg_spmv_band", f"fused, banded SpMV (line stride {an['band_stride']})"
+    elif an["split"] and B >= 8 and B % 4 == 0 and nnz < 2 ** 31:
+        spmv_kernel = "k_gcg_spmv"
+        schedule = "split, grouped batch (4 systems interleaved per element; k_gcg_pupd, k_gcg_spmv)"
+    elif an["split"]:
+        spmv_kernel, schedule = "k_cg_spmv", "split (k_cg_pupd forms p_k, the SpMV gathers it)"
+    else:
+        spmv_kernel, schedule = "k_cg_spmv", "fused"
     if args.fixed_iters > 0:
         w["max_iter"], w["fixed"], w["rtol"] = args.fixed_iters, True, 0.0
     opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"])
@@ -285,12 +317,13 @@ def main() -> int:
     tq = S.timing.query()
     torch.cuda.synchronize()
 
-    bm = bytes_model(n, nnz, B, rp_bytes)
+    bm = bytes_model(n, nnz, B, rp_bytes, split=an["split"])
     spmv_ms = tq["cg_spmv"]["total_ms"] / max(tq["cg_spmv"]["launches"], 1)
     upd_ms = tq["cg_update"]["total_ms"] / max(tq["cg_update"]["launches"], 1)
+    pupd_ms = tq["cg_pupd"]["total_ms"] / max(tq["cg_pupd"]["launches"], 1) if an["split"] else 0.0
     achieved = bm["cg_spmv"] / (spmv_ms * 1e-3) / 1e9
     traffic, traffic_src = read_traffic(args.workload)
-    iter_gbps = bm["iteration"] / ((spmv_ms + upd_ms) * 1e-3) / 1e9
+    iter_gbps = bm["iteration"] / ((spmv_ms + upd_ms + pupd_ms) * 1e-3) / 1e9
     wall_gbps = bm["iteration"] * (total_it / B) / wall / 1e9
 
     if args.calibrate_copy:
@@ -320,7 +353,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w["desc"], "n": n, "nnz": nnz, "batch": B,
                    "row_ptr": f"int{8 * rp_bytes}", "rtol": w["rtol"],
-                   "fixed_iterations": w["fixed"], "parallelism": "none (1 GPU)"},
+                   "fixed_iterations": w["fixed"], "parallelism": "none (1 GPU)",
+                   "cg_schedule": schedule},
         "iterations_per_step": {"forward": fwd_it[-1], "adjoint": bwd_it[-1]},
         "solve_adjoint_ms": round(ms_step, 4),
         "hbm_gbps_per_iteration": round(iter_gbps, 1),
@@ -330,7 +364,7 @@ def main() -> int:
                         "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
                     for k, v in tq.items() if v["launches"]},
         "bytes_model": bm,
-        "roofline": {"bound": "hbm", "kernel": "k_cg_spmv", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": spmv_kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "traffic_source": traffic_src,
                      "bytes_per_launch": bm["cg_spmv"], "avg_launch_us": round(1e3 * spmv_ms, 3)},

@@ -20,9 +20,9 @@ SLA_SYMMETRIC = 1
 SLA_EAGER_TRANSPOSE = 2
 SLA_FIXED_ITERS = 1
 (SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
- SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_COUNT) = range(9)
+ SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_GROUP_LAYOUT, SLA_K_COUNT) = range(10)
 KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "gather_vals",
-                "transpose", "cg_pupd"]
+                "transpose", "cg_pupd", "group_layout"]
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",

@@ -47,6 +47,8 @@ struct sla_csr {
     int band_cap = kCapSmall;
     // Split CG schedule (unstructured patterns); the transposed pattern has the same span.
     bool split = false;
+    // Grouped kernels for batches of split-schedule patterns (SLA_CG_GROUPED=0 turns them off).
+    bool group_ok = true;
     // transposed pattern (lazily built unless SLA_SYMMETRIC)
     bool has_t = false;
     void* row_ptr_t = nullptr;
@@ -57,6 +59,9 @@ struct sla_csr {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     double* vals_t = nullptr;   // [batch][nnz] transposed values
+    // grouped batches: x and the values in the grouped layout
+    void* gws = nullptr;
+    size_t gws_bytes = 0;
     size_t vals_t_bytes = 0;
     int32_t* flag_host = nullptr;   // pinned, 2 slots for the polling copies
     hipEvent_t poll_ev[2] = {nullptr, nullptr};
@@ -334,12 +339,131 @@ sla_status ensure_vals_t(sla_csr* A, int64_t batch, const double* vals, hipStrea
 }
 
 // One CG solve (batch systems) on the pattern (row_ptr, col, cap) with values vals.
+// Enqueue the iterations k = 0 .. max_iter (step(k) launches one iteration's kernels).
+// Fixed-iteration mode enqueues them all.  Otherwise chunks of check_every (default
+// 32) iterations go out with a copy of the device's running-systems counter after each
+// chunk; two chunks are kept in flight and the loop ends once a copy reads 0.
+template <class Step>
+sla_status drive_cg(sla_csr* A, const CgArgs& a, const Workspace& w, const sla_cg_opts* o, hipStream_t s,
+                    Step&& step)
+{
+    hipError_t e;
+    if (a.fixed) {
+        for (int64_t k = 0; k <= a.max_iter; ++k) {
+            if ((e = step(k)) != hipSuccess) return fail(SLA_ERR_HIP, "cg launch: %s", hipGetErrorString(e));
+        }
+        return SLA_OK;
+    }
+    const int64_t chunk = o->check_every > 0 ? o->check_every : 32;
+    int64_t k = 0;
+    for (int64_t c = 0; k <= a.max_iter; ++c) {
+        const int64_t kend = std::min<int64_t>(k + chunk, a.max_iter + 1);
+        for (; k < kend; ++k) {
+            if ((e = step(k)) != hipSuccess) return fail(SLA_ERR_HIP, "cg launch: %s", hipGetErrorString(e));
+        }
+        const int slot = static_cast<int>(c & 1);
+        HIP_TRY(hipMemcpyAsync(A->flag_host + slot, w.n_active, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipEventRecord(A->poll_ev[slot], s));
+        if (c > 0) {
+            HIP_TRY(hipEventSynchronize(A->poll_ev[slot ^ 1]));
+            if (A->flag_host[slot ^ 1] == 0) break;   // every system has stopped
+        }
+    }
+    return SLA_OK;
+}
+
+// Grouped batch (kGroup systems interleaved per element): values into the grouped
+// layout, then init / (p update, SpMV, update) per iteration / x back to the caller's
+// layout.  The polling is run_cg's.
+sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, int64_t batch, const double* vals,
+                          const double* b, double* x, const sla_cg_opts* o, sla_cg_info* info, hipStream_t s)
+{
+    const int64_t n = A->n_rows;
+    const int groups = static_cast<int>(batch / kGroup);
+    const int64_t gtiles = std::max<int64_t>(1, (n + kBlock / kGroup - 1) / (kBlock / kGroup));
+    // SpMV grid per group: with groups pinned to XCDs (groups % 8 == 0), the resident
+    // workgroups of one XCD; otherwise an equal share of the GPU.
+    const int gcap = static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapSmall ? kGCapSmall : kGCapLarge;
+    const int occ = cg_group_blocks_per_cu(gcap);
+    const bool pinned = groups >= 8 && groups % 8 == 0;
+    int64_t P = pinned ? static_cast<int64_t>(A->n_cu / 8) * occ : (static_cast<int64_t>(A->n_cu) * occ) / groups;
+    P = std::max<int64_t>(1, std::min<int64_t>(P, gtiles));
+    // streaming kernels: about 16 tiles per workgroup (their start sums the partials)
+    const int64_t Pu = std::max<int64_t>(1, std::min<int64_t>(64, (gtiles + 15) / 16));
+    Workspace w;
+    sla_status st = ensure_workspace(A, batch, static_cast<int>(std::max(P, Pu)), &w);
+    if (st != SLA_OK) return st;
+    const size_t xb = align256(sizeof(double) * static_cast<size_t>(n) * batch);
+    const size_t need = xb + sizeof(double) * static_cast<size_t>(A->nnz) * batch;
+    if (need > A->gws_bytes) {
+        if (A->gws) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipFree(A->gws));
+            A->gws = nullptr;
+            A->gws_bytes = 0;
+        }
+        if ((st = dev_alloc(&A->gws, need)) != SLA_OK) return st;
+        A->gws_bytes = need;
+    }
+    double* xg = static_cast<double*>(A->gws);
+    double* vg = reinterpret_cast<double*>(static_cast<char*>(A->gws) + xb);
+
+    CgArgs a{};
+    a.row_ptr = row_ptr;
+    a.col = col;
+    a.vals = vg;
+    a.b = b;
+    a.x = x;
+    a.r = w.r;
+    a.p0 = w.p0;
+    a.p1 = w.p1;
+    a.q = w.q;
+    a.part_sigma = w.part_sigma;
+    a.part_rho = w.part_rho;
+    a.st = w.st;
+    a.info = info;
+    a.hist = o->residual_history;
+    a.n_active = w.n_active;
+    a.n = n;
+    a.nnz = A->nnz;
+    a.ntiles = gtiles;
+    a.max_iter = o->max_iter;
+    a.rtol = o->rtol;
+    a.atol = o->atol;
+    a.fixed = (o->flags & SLA_FIXED_ITERS) ? 1 : 0;
+    a.G = static_cast<int32_t>(P);
+    a.Gu = static_cast<int32_t>(Pu);
+    a.batch = static_cast<int32_t>(batch);
+    a.split = 1;
+    a.groups = groups;
+    a.cap = gcap;
+    a.xg = xg;
+
+    hipError_t e = timed(SLA_K_GROUP_LAYOUT, s, [&] { return launch_group_vals(vals, vg, A->nnz, groups, s); });
+    if (e == hipSuccess) e = timed(SLA_K_CG_INIT, s, [&] { return launch_gcg(0, a, 0, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "grouped cg init: %s", hipGetErrorString(e));
+    auto step = [&](int64_t k) -> hipError_t {
+        hipError_t e0 = timed(SLA_K_CG_PUPD, s, [&] { return launch_gcg(1, a, k, s); });
+        if (e0 != hipSuccess) return e0;
+        e0 = timed(SLA_K_CG_SPMV, s, [&] { return launch_gcg(2, a, k, s); });
+        if (e0 != hipSuccess || k >= a.max_iter) return e0;
+        return timed(SLA_K_CG_UPDATE, s, [&] { return launch_gcg(3, a, k, s); });
+    };
+    if ((st = drive_cg(A, a, w, o, s, step)) != SLA_OK) return st;
+    e = timed(SLA_K_GROUP_LAYOUT, s, [&] { return launch_gcg(4, a, 0, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "grouped cg finish: %s", hipGetErrorString(e));
+    return SLA_OK;
+}
+
 // band > 0: the pattern is banded with line stride `band` and takes the line-walking
 // SpMV (LDS variant band_cap) on a persistent grid over blocks of lines of one strip.
 sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t band, int band_cap,
                   bool split, int64_t batch, const double* vals, const double* b, double* x, const sla_cg_opts* o,
                   sla_cg_info* info, hipStream_t s)
 {
+    if (split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 && A->krp_bits == 32 && A->group_ok &&
+        static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapLarge && row_ptr == A->krp)
+        return run_cg_grouped(A, row_ptr, col, batch, vals, b, x, o, info, s);
     const int64_t n = A->n_rows;
     const int64_t ntiles = (n + kTile - 1) / kTile;
     // Grid of the plain SpMV (also the base of the update kernel's grid).
@@ -423,29 +547,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         if (e1 != hipSuccess || k >= a.max_iter) return e1;
         return timed(SLA_K_CG_UPDATE, s, [&] { return launch_cg_update(a, k, s); });
     };
-
-    if (a.fixed) {
-        for (int64_t k = 0; k <= a.max_iter; ++k) {
-            if ((e = step(k)) != hipSuccess) return fail(SLA_ERR_HIP, "cg launch: %s", hipGetErrorString(e));
-        }
-        return SLA_OK;
-    }
-    const int64_t chunk = o->check_every > 0 ? o->check_every : 32;
-    int64_t k = 0;
-    for (int64_t c = 0; k <= a.max_iter; ++c) {
-        const int64_t kend = std::min<int64_t>(k + chunk, a.max_iter + 1);
-        for (; k < kend; ++k) {
-            if ((e = step(k)) != hipSuccess) return fail(SLA_ERR_HIP, "cg launch: %s", hipGetErrorString(e));
-        }
-        const int slot = static_cast<int>(c & 1);
-        HIP_TRY(hipMemcpyAsync(A->flag_host + slot, w.n_active, sizeof(int32_t), hipMemcpyDeviceToHost, s));
-        HIP_TRY(hipEventRecord(A->poll_ev[slot], s));
-        if (c > 0) {
-            HIP_TRY(hipEventSynchronize(A->poll_ev[slot ^ 1]));
-            if (A->flag_host[slot ^ 1] == 0) break;   // every system has stopped
-        }
-    }
-    return SLA_OK;
+    return drive_cg(A, a, w, o, s, step);
 }
 
 // Line stride of a banded pattern, or 0.  Banded: square with n < 2^29 and nnz < 2^31
@@ -575,6 +677,7 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
         if (std::strcmp(env, "fused") == 0) A->split = false;
         if (std::strcmp(env, "split") == 0) A->split = A->band == 0;
     }
+    if (const char* env = std::getenv("SLA_CG_GROUPED")) A->group_ok = std::strcmp(env, "0") != 0;
     A->krp = d_row_ptr;
     A->krp_bits = row_ptr_bits;
     if (row_ptr_bits == 64 && nnz < (int64_t(1) << 31)) {
@@ -602,6 +705,7 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (prev != A->device) (void)hipSetDevice(A->device);
     (void)hipDeviceSynchronize();
     if (A->ws) (void)hipFree(A->ws);
+    if (A->gws) (void)hipFree(A->gws);
     if (A->vals_t) (void)hipFree(A->vals_t);
     if (A->row_ptr_t) (void)hipFree(A->row_ptr_t);
     if (A->col_t) (void)hipFree(A->col_t);

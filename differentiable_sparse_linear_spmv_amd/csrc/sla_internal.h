@@ -37,6 +37,15 @@ constexpr int64_t kBandStreamBytes = int64_t(1) << 30;
 // own pass, then gathered alone), which halves the gathers' cache requests.
 constexpr int64_t kSplitMinSpan = 4096;
 
+// Grouped batches: systems interleaved per element in groups of kGroup (a 32-byte
+// piece per gathered element).  Batches of at least kGroupMinBatch systems, a
+// multiple of kGroup, on split-schedule patterns use the grouped kernels.
+constexpr int kGroup = 4;
+constexpr int kGroupMinBatch = 8;
+// Entries per 64-row tile staged by the grouped SpMV: rows of at most 8 or 16 entries.
+constexpr int kGCapSmall = 512;
+constexpr int kGCapLarge = 1024;
+
 // Per-system CG state in device memory (64 bytes).  Double-buffered by the
 // parity of the iteration index so that a kernel reads the previous value while
 // its first workgroup writes the new one.
@@ -80,6 +89,9 @@ struct CgArgs {
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
     int32_t sys_per_xcd;     // 1: batch % 8 == 0; every system runs on one XCD
     int32_t split;           // 1: split schedule (k_cg_pupd forms p_k, the SpMV gathers it)
+    int32_t groups;          // grouped batch: number of groups (r, p0, p1, q, vals, xg grouped)
+    int32_t cap;             // grouped batch: entries per tile staged (kGCapSmall or kGCapLarge)
+    double* xg;              // grouped batch: x in the grouped layout
     int32_t band_block;      // banded SpMV: lines per block of work
     int64_t band_stride;     // banded SpMV: line length S (0: plain SpMV)
     int64_t band_lines;      // banded SpMV: ceil(n / S)
@@ -97,12 +109,17 @@ LaunchEvents& launch_events();
 // sized to fill the GPU exactly once).
 int cg_blocks_per_cu(int rp_bits, int cap, int64_t n, bool split);
 int cg_band_blocks_per_cu(int cap);   // the banded SpMV (32-bit row pointers only)
+int cg_group_blocks_per_cu(int cap);   // the grouped SpMV
 
 // Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s);
 hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s);
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s);
 hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s);   // split schedule
+// Grouped batch: values into the grouped layout, and the CG kernels
+// (which: 0 init, 1 p update, 2 SpMV, 3 update, 4 x back to the caller's layout).
+hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, hipStream_t s);
+hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s);
 
 hipError_t launch_matvec(const void* row_ptr, int rp_bits, const int32_t* col, const double* vals,
                          const double* x, double* y, int64_t n_rows, int64_t nnz, int64_t n_cols,

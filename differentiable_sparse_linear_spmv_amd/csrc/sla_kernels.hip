@@ -1197,6 +1197,446 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 }
 
 // ----------------------------------------------------------------------------------
+// Grouped batch (shared-pattern batches on unstructured patterns).  kGroup systems
+// are interleaved element by element: vectors [group][n][kGroup], values
+// [group][nnz][kGroup].  Lane t works on row t / kGroup of its tile for system
+// t % kGroup, so one gathered element of all kGroup systems is one 32-byte piece of
+// a cache line: the random gathers cost one cache request per kGroup systems instead
+// of one per system.  Every lane sums its row in ascending entry order with rounded
+// products, as the other SpMV kernels do, and the elementwise steps use the same
+// expressions, so each system follows the same arithmetic as on its own.
+// Grid (P, groups); with groups % 8 == 0 every group runs on one XCD (workgroup b
+// runs on XCD b % 8), so the XCD's L2 holds that group's operand.
+// ----------------------------------------------------------------------------------
+constexpr int kGRows = kBlock / kGroup;   // rows per tile
+
+struct GroupCoord {
+    int grp;
+    int lb;
+};
+
+__device__ __forceinline__ GroupCoord group_coord(const CgArgs& a, int P)
+{
+    if (a.groups >= 8 && (a.groups & 7) == 0) {
+        const int64_t L = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+        const int x = static_cast<int>(L & 7);
+        const int64_t slot = L >> 3;
+        return GroupCoord{x + 8 * static_cast<int>(slot / P), static_cast<int>(slot % P)};
+    }
+    return GroupCoord{static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.x)};
+}
+
+// Per-system sum over the workgroup: lane t contributes v to system t % kGroup; every
+// lane gets its system's total.  Fixed order (deterministic).  s_red: 4 * kGroup doubles.
+__device__ __forceinline__ double group_block_sum(double v, double* s_red)
+{
+#pragma unroll
+    for (int off = 32; off >= kGroup; off >>= 1) v = v + __shfl_xor(v, off, 64);
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    if (lane < kGroup) s_red[w * kGroup + lane] = v;
+    __syncthreads();
+    const int sy = threadIdx.x % kGroup;
+    const double t = (s_red[sy] + s_red[kGroup + sy]) + (s_red[2 * kGroup + sy] + s_red[3 * kGroup + sy]);
+    __syncthreads();
+    return t;
+}
+
+// Per-system sum of the P partials part[sys][P] of the group's systems.
+__device__ __forceinline__ double group_reduce_partials(const double* part, int sys0, int P, double* s_red)
+{
+    const int sy = threadIdx.x % kGroup;
+    double v = 0.0;
+    for (int j = threadIdx.x / kGroup; j < P; j += kBlock / kGroup)
+        v = v + part[static_cast<int64_t>(sys0 + sy) * P + j];
+    return group_block_sum(v, s_red);
+}
+
+// cg_step_begin for the group's systems: each lane decides for system sys0 + t % kGroup
+// (the lane t < kGroup of workgroup 0 writes that system's records).  s_stop[kGroup]
+// receives the stop words read at entry.  Contains barriers.
+__device__ __forceinline__ int group_step_begin(const CgArgs& a, int sys0, int lb, int64_t k, double* s_red,
+                                                int64_t* s_stop, double& beta, double& alpha_prev)
+{
+    const int sy = threadIdx.x % kGroup;
+    const int sys = sys0 + sy;
+    SysState* st = a.st + sys;
+    const bool lead = (lb == 0 && threadIdx.x < kGroup);
+    const bool first = (k == 0);
+    if (threadIdx.x < kGroup) s_stop[threadIdx.x] = a.st[sys0 + threadIdx.x].stop_iter;
+    const double rho_k = group_reduce_partials(a.part_rho, sys0, a.Gu, s_red);
+    beta = 0.0;
+    alpha_prev = 0.0;
+    if (s_stop[sy] < k) return kStepStopped;
+    const double res = sqrt(rho_k);
+    double thr, rhs;
+    if (first) {
+        rhs = res;
+        thr = a.rtol * rhs;
+        if (a.atol > thr) thr = a.atol;
+    } else {
+        thr = st->thr;
+        rhs = st->rhs;
+    }
+    if (lead && a.hist) a.hist[static_cast<int64_t>(sys) * (a.max_iter + 1) + k] = res;
+    alpha_prev = first ? 0.0 : st->alpha[(k - 1) & 1];
+    int code = -1;
+    if (!a.fixed && res <= thr) code = SLA_CONVERGED;
+    else if (k >= a.max_iter) code = SLA_MAX_ITER;
+    if (code >= 0) {
+        if (lead) {
+            st->stop_iter = k;
+            if (first) { st->rhs = rhs; st->thr = thr; }
+            sla_cg_info inf;
+            inf.iterations = k;
+            inf.res_norm = res;
+            inf.rhs_norm = rhs;
+            inf.state = code;
+            inf.reserved = 0;
+            a.info[sys] = inf;
+            atomicSub(a.n_active, 1);
+        }
+        return kStepStopNow;
+    }
+    beta = first ? 0.0 : rho_k / st->rho[(k - 1) & 1];
+    if (lead) {
+        st->rho[k & 1] = rho_k;
+        if (first) { st->thr = thr; st->rhs = rhs; }
+    }
+    return kStepRun;
+}
+
+__device__ __forceinline__ bool group_any_running(const int64_t* s_stop, int64_t after)
+{
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) any = any || (s_stop[j] > after);
+    return any;
+}
+
+// Grouped layout of the values: out[g][k][s] = vals[g * kGroup + s][k].
+__global__ __launch_bounds__(kBlock) void k_group_vals(const double* __restrict__ vals, double* __restrict__ out,
+                                                       int64_t nnz, int groups)
+{
+    const int64_t total = nnz * kGroup;
+    const int g = blockIdx.y;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; e < total;
+         e += static_cast<int64_t>(gridDim.x) * kBlock) {
+        const int64_t kk = e / kGroup;
+        const int sy = static_cast<int>(e - kk * kGroup);
+        out[static_cast<int64_t>(g) * total + e] = vals[(static_cast<int64_t>(g) * kGroup + sy) * nnz + kk];
+    }
+}
+
+// x = 0, p_{-1} = 0, r_0 = b (into the grouped layout), partial r_0^T r_0, state reset.
+__global__ __launch_bounds__(kBlock) void k_gcg_init(CgArgs a)
+{
+    __shared__ double s_red[4 * kGroup];
+    const GroupCoord gc = group_coord(a, a.Gu);
+    const int tid = threadIdx.x;
+    const int sy = tid % kGroup;
+    const int sys0 = gc.grp * kGroup;
+    const int64_t n = a.n;
+    const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
+    const double* __restrict__ b = a.b + static_cast<int64_t>(sys0 + sy) * n;
+    const int64_t gtiles = (n + kGRows - 1) / kGRows;
+    double rr = 0.0;
+    for (int64_t t = gc.lb; t < gtiles; t += a.Gu) {
+        const int64_t i = t * kGRows + tid / kGroup;
+        if (i < n) {
+            const int64_t e = goff + i * kGroup + sy;
+            const double bv = b[i];
+            a.r[e] = bv;
+            a.xg[e] = 0.0;
+            a.p1[e] = 0.0;
+            const double w = bv * bv;
+            rr = rr + w;
+        }
+    }
+    rr = group_block_sum(rr, s_red);
+    if (tid < kGroup) {
+        a.part_rho[static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb] = rr;
+        if (gc.lb == 0) a.st[sys0 + tid].stop_iter = INT64_MAX;
+    }
+    if (gc.lb == 0 && gc.grp == 0 && tid == 0) *a.n_active = a.batch;
+}
+
+// The step's decisions, p_k = r_k + beta p_{k-1} and x_k = x_{k-1} + alpha_{k-1} p_{k-1}.
+__global__ __launch_bounds__(kBlock) void k_gcg_pupd(CgArgs a, int64_t k)
+{
+    __shared__ double s_red[4 * kGroup];
+    __shared__ int64_t s_stop[kGroup];
+    const GroupCoord gc = group_coord(a, a.Gu);
+    const int tid = threadIdx.x;
+    const int sy = tid % kGroup;
+    const int sys0 = gc.grp * kGroup;
+    double beta, alpha_prev;
+    const int run = group_step_begin(a, sys0, gc.lb, k, s_red, s_stop, beta, alpha_prev);
+    if (!group_any_running(s_stop, k - 1)) return;   // every system stopped earlier
+    if (run == kStepStopped || (run == kStepStopNow && k == 0)) return;
+    const bool stop = (run == kStepStopNow);
+    const int64_t n = a.n;
+    const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
+    const double* __restrict__ rg = a.r + goff;
+    const double* __restrict__ pp = ((k & 1) ? a.p0 : a.p1) + goff;
+    double* __restrict__ pc = ((k & 1) ? a.p1 : a.p0) + goff;
+    double* __restrict__ xg = a.xg + goff;
+    const int64_t gtiles = (n + kGRows - 1) / kGRows;
+    (void)sy;
+#pragma unroll 1
+    for (int64_t t0 = gc.lb; t0 < gtiles; t0 += kStreamUnroll * static_cast<int64_t>(a.Gu)) {
+        double rv[kStreamUnroll], pv[kStreamUnroll], xv[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t i = min((t0 + u * static_cast<int64_t>(a.Gu)) * kGRows + tid / kGroup, n - 1);
+            const int64_t e = i * kGroup + tid % kGroup;
+            rv[u] = rg[e];
+            pv[u] = pp[e];
+            xv[u] = xg[e];
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t t = t0 + u * static_cast<int64_t>(a.Gu);
+            const int64_t i = t * kGRows + tid / kGroup;
+            if (t < gtiles && i < n) {
+                const int64_t e = i * kGroup + tid % kGroup;
+                const double tx = alpha_prev * pv[u];
+                xg[e] = xv[u] + tx;
+                if (!stop) {
+                    const double tp = beta * pv[u];
+                    pc[e] = rv[u] + tp;
+                }
+            }
+        }
+    }
+}
+
+// q = A p_k for the group's systems (p_k formed by k_gcg_pupd), partial p_k^T q.
+// Tiles of kGRows rows: the tile's entries (values of all kGroup systems, columns) are
+// one contiguous range, loaded coalesced and staged through LDS (the lanes of one row
+// read its entries there); only the operand is gathered from memory.  Pipelined like
+// the banded kernel: while tile t is summed, tile t + P's loads are in flight, every
+// load unconditional (clamped), and the outputs are stored after the next commit.
+template <int CAPG>   // entries per tile (kGRows rows of at most CAPG / kGRows entries)
+struct GStage {
+    double v[CAPG * kGroup / kBlock];
+    int32_t c[CAPG / kBlock];
+    int32_t a0, a1;
+};
+
+template <int CAPG>
+__global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
+{
+    constexpr int UV = CAPG * kGroup / kBlock;
+    constexpr int UC = CAPG / kBlock;
+    constexpr int RC = 8;
+    __shared__ double s_val[CAPG * kGroup];
+    __shared__ int32_t s_col[CAPG];
+    __shared__ int32_t s_rs[kBlock], s_re[kBlock];
+    __shared__ double s_red[4 * kGroup];
+    __shared__ int64_t s_stop[kGroup];
+    const GroupCoord gc = group_coord(a, a.G);
+    const int tid = threadIdx.x;
+    const int sy = tid % kGroup;
+    const int sys0 = gc.grp * kGroup;
+    if (tid < kGroup) s_stop[tid] = a.st[sys0 + tid].stop_iter;
+    __syncthreads();
+    if (!group_any_running(s_stop, k)) return;   // k_gcg_pupd stopped all of them at k or before
+    const bool run = s_stop[sy] > k;
+    const int32_t n = static_cast<int32_t>(a.n);
+    const int64_t goff = static_cast<int64_t>(gc.grp) * a.n * kGroup;
+    const int32_t* __restrict__ rp = static_cast<const int32_t*>(a.row_ptr);
+    const int32_t* __restrict__ col = a.col;
+    const double* __restrict__ vg = a.vals + static_cast<int64_t>(gc.grp) * a.nnz * kGroup;
+    const double* __restrict__ pg = ((k & 1) ? a.p1 : a.p0) + goff;
+    double* __restrict__ qg = a.q + goff;
+    const int32_t gtiles = (n + kGRows - 1) / kGRows;
+    const int32_t P = a.G;
+    const int32_t nnz = static_cast<int32_t>(a.nnz);
+    auto tk0 = [&](int32_t t) { return static_cast<int32_t>(ld_rp_uniform(rp, min(t * kGRows, n))); };
+    auto tk1 = [&](int32_t t) { return static_cast<int32_t>(ld_rp_uniform(rp, min((t + 1) * kGRows, n))); };
+    // issue the loads of tile t (entries [k0, k1)); clamped, so every lane issues them all
+    auto stage = [&](GStage<CAPG>& S, int32_t t, int32_t k0, int32_t k1) __attribute__((always_inline)) {
+        const int32_t i = min(t * kGRows + tid / kGroup, n - 1);
+        S.a0 = rp[i];
+        S.a1 = rp[i + 1];
+        const int32_t cnt = k1 - k0;
+        const int32_t kb = cnt > 0 ? k0 : min(k0, nnz - 1);
+        const double* __restrict__ vb = vg + static_cast<int64_t>(kb) * kGroup;
+        const int32_t* __restrict__ cb = col + kb;
+        const int lastv = max(cnt * kGroup - 1, 0), lastc = max(cnt - 1, 0);
+#pragma unroll
+        for (int u = 0; u < UV; ++u) S.v[u] = vb[min(tid + u * kBlock, lastv)];
+#pragma unroll
+        for (int u = 0; u < UC; ++u) S.c[u] = cb[min(tid + u * kBlock, lastc)];
+    };
+    auto commit = [&](const GStage<CAPG>& S, int32_t t, int32_t k0, int32_t k1) __attribute__((always_inline)) {
+        const int32_t cnt = k1 - k0;
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int e = tid + u * kBlock;
+            if (e < cnt * kGroup) s_val[e] = S.v[u];
+        }
+#pragma unroll
+        for (int u = 0; u < UC; ++u) {
+            const int e = tid + u * kBlock;
+            if (e < cnt) s_col[e] = S.c[u];
+        }
+        const bool has = t * kGRows + tid / kGroup < n;
+        s_rs[tid] = S.a0 - k0;
+        s_re[tid] = has ? S.a1 - k0 : S.a0 - k0;
+    };
+
+    double sig = 0.0;
+    int32_t t = gc.lb;
+    if (t >= gtiles) {
+        sig = group_block_sum(sig, s_red);
+        if (tid < kGroup) a.part_sigma[static_cast<int64_t>(sys0 + tid) * a.G + gc.lb] = sig;
+        return;
+    }
+    GStage<CAPG> SA, SB;
+    int32_t k0a = tk0(t), k1a = tk1(t), k0b = 0, k1b = 0;
+    stage(SA, t, k0a, k1a);
+    if (t + P < gtiles) {
+        k0b = tk0(t + P);
+        k1b = tk1(t + P);
+    }
+    commit(SA, t, k0a, k1a);
+    __syncthreads();
+#define SLA_GCG_TILE(nxt)                                                                                  \
+    {                                                                                                      \
+        stage(nxt, t + P, k0b, k1b); /* past the end: clamped loads, keeps the wait counts exact */       \
+        int32_t k0c = 0, k1c = 0;                                                                          \
+        if (t + 2 * P < gtiles) {                                                                          \
+            k0c = tk0(t + 2 * P);                                                                          \
+            k1c = tk1(t + 2 * P);                                                                          \
+        }                                                                                                  \
+        const int rs = s_rs[tid], re = s_re[tid];                                                          \
+        double sum = 0.0;                                                                                  \
+        for (int j0 = rs; j0 < re; j0 += RC) {                                                             \
+            double pv[RC];                                                                                 \
+            _Pragma("unroll") for (int u = 0; u < RC; ++u) {                                               \
+                const int j = (j0 + u < re) ? j0 + u : j0;                                                 \
+                pv[u] = pg[static_cast<int64_t>(s_col[j]) * kGroup + sy];                                  \
+            }                                                                                              \
+            _Pragma("unroll") for (int u = 0; u < RC; ++u) {                                               \
+                const bool ok = j0 + u < re;                                                               \
+                const int j = ok ? j0 + u : j0;                                                            \
+                const double tt = s_val[j * kGroup + sy] * pv[u];                                          \
+                const double sn = sum + tt;                                                                \
+                sum = ok ? sn : sum;                                                                       \
+            }                                                                                              \
+        }                                                                                                  \
+        const int32_t i = t * kGRows + tid / kGroup;                                                       \
+        __syncthreads(); /* tile t's LDS reads are done */                                                 \
+        t += P;                                                                                            \
+        const int32_t k0n = k0b, k1n = k1b;                                                                \
+        k0b = k0c;                                                                                         \
+        k1b = k1c;                                                                                         \
+        if (t < gtiles) commit(nxt, t, k0n, k1n);                                                          \
+        if (run && i < n) {                                                                                \
+            const int64_t e = static_cast<int64_t>(i) * kGroup + sy;                                      \
+            qg[e] = sum;                                                                                   \
+            const double w = pg[e] * sum;                                                                  \
+            sig = sig + w;                                                                                 \
+        }                                                                                                  \
+        if (t >= gtiles) break;                                                                            \
+        __syncthreads();                                                                                   \
+    }
+#pragma unroll 1
+    while (true) {
+        SLA_GCG_TILE(SB)
+        SLA_GCG_TILE(SA)
+    }
+#undef SLA_GCG_TILE
+    sig = group_block_sum(sig, s_red);
+    if (tid < kGroup) a.part_sigma[static_cast<int64_t>(sys0 + tid) * a.G + gc.lb] = sig;
+}
+
+// alpha = rho / sigma per system, r -= alpha q, partial r^T r.
+__global__ __launch_bounds__(kBlock) void k_gcg_update(CgArgs a, int64_t k)
+{
+    __shared__ double s_red[4 * kGroup];
+    __shared__ int64_t s_stop[kGroup];
+    const GroupCoord gc = group_coord(a, a.Gu);
+    const int tid = threadIdx.x;
+    const int sy = tid % kGroup;
+    const int sys0 = gc.grp * kGroup;
+    const int sys = sys0 + sy;
+    SysState* st = a.st + sys;
+    if (tid < kGroup) s_stop[tid] = a.st[sys0 + tid].stop_iter;
+    const double sigma = group_reduce_partials(a.part_sigma, sys0, a.G, s_red);
+    if (!group_any_running(s_stop, k)) return;
+    bool run = s_stop[sy] > k;
+    const double rho_k = st->rho[k & 1];
+    if (run && !(sigma > 0.0)) {
+        if (gc.lb == 0 && tid < kGroup) {
+            st->stop_iter = k;
+            sla_cg_info inf;
+            inf.iterations = k;
+            inf.res_norm = sqrt(rho_k);
+            inf.rhs_norm = st->rhs;
+            inf.state = (sigma != sigma) ? SLA_NAN : SLA_NOT_SPD;
+            inf.reserved = 0;
+            a.info[sys] = inf;
+            atomicSub(a.n_active, 1);
+        }
+        run = false;
+    }
+    const double alpha = rho_k / sigma;
+    if (run && gc.lb == 0 && tid < kGroup) st->alpha[k & 1] = alpha;
+    const int64_t n = a.n;
+    const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
+    const double* __restrict__ qg = a.q + goff;
+    double* __restrict__ rg = a.r + goff;
+    const int64_t gtiles = (n + kGRows - 1) / kGRows;
+    double rr = 0.0;
+    if (run) {
+#pragma unroll 1
+        for (int64_t t0 = gc.lb; t0 < gtiles; t0 += kStreamUnroll * static_cast<int64_t>(a.Gu)) {
+            double qv[kStreamUnroll], rv[kStreamUnroll];
+#pragma unroll
+            for (int u = 0; u < kStreamUnroll; ++u) {
+                const int64_t i = min((t0 + u * static_cast<int64_t>(a.Gu)) * kGRows + tid / kGroup, n - 1);
+                const int64_t e = i * kGroup + sy;
+                qv[u] = qg[e];
+                rv[u] = rg[e];
+            }
+#pragma unroll
+            for (int u = 0; u < kStreamUnroll; ++u) {
+                const int64_t t = t0 + u * static_cast<int64_t>(a.Gu);
+                const int64_t i = t * kGRows + tid / kGroup;
+                if (t < gtiles && i < n) {
+                    const double tq = alpha * qv[u];
+                    const double rn = rv[u] - tq;
+                    rg[i * kGroup + sy] = rn;
+                    const double w = rn * rn;
+                    rr = rr + w;
+                }
+            }
+        }
+    }
+    rr = group_block_sum(rr, s_red);
+    if (tid < kGroup) a.part_rho[static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb] = rr;
+}
+
+// x[s][i] = xg[i][s]: the solutions back in the caller's layout.
+__global__ __launch_bounds__(kBlock) void k_gcg_finish(CgArgs a)
+{
+    const GroupCoord gc = group_coord(a, a.Gu);
+    const int tid = threadIdx.x;
+    const int sy = tid % kGroup;
+    const int64_t n = a.n;
+    const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
+    double* __restrict__ x = a.x + static_cast<int64_t>(gc.grp * kGroup + sy) * n;
+    const int64_t gtiles = (n + kGRows - 1) / kGRows;
+    for (int64_t t = gc.lb; t < gtiles; t += a.Gu) {
+        const int64_t i = t * kGRows + tid / kGroup;
+        if (i < n) x[i] = a.xg[goff + i * kGroup + sy];
+    }
+}
+
+// ----------------------------------------------------------------------------------
 // y = A x (one tile per workgroup; grid (ntiles, batch))
 // ----------------------------------------------------------------------------------
 template <typename RP, int CAP, bool OFF32>
@@ -1276,51 +1716,71 @@ __device__ __forceinline__ int32_t wave_min_i32(int32_t v)
     return v;
 }
 
+// Grid-stride over 256-row tiles; each workgroup folds its maxima / minima in
+// registers and LDS and issues one atomic per counter at the end (a per-row or
+// per-tile atomic on one address serialises at the L2 for large patterns).
 template <typename RP>
 __global__ __launch_bounds__(kBlock) void k_validate(const RP* __restrict__ rp, const int32_t* __restrict__ col,
                                                      int64_t n_rows, int64_t n_cols, int64_t nnz, int32_t* out)
 {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (i == 0) {
+    __shared__ int32_t s_m[3][kBlock / 64];
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid == 0) {
         if (ld_rp(rp, 0) != 0 || ld_rp(rp, n_rows) != nnz) atomicOr(out + kChkErr, 1);
     }
-    int32_t row_len = 0, far_min = 0x7fffffff, far_max = 0;
-    if (i < n_rows) {
-        const int64_t a = ld_rp(rp, i), e = ld_rp(rp, i + 1);
-        if (a > e || a < 0 || e > nnz) {
-            atomicOr(out + kChkErr, 2);
-        } else {
-            int64_t prev = -1;
-            for (int64_t kk = a; kk < e; ++kk) {
-                const int64_t c = col[kk];
-                if (c < 0 || c >= n_cols) atomicOr(out + kChkErr, 4);
-                if (c <= prev) atomicOr(out + kChkErr, 8);
-                prev = c;
-                const int64_t d = min(c > i ? c - i : i - c, int64_t(0x7fffffff));
-                if (d > kBandHalo) {
-                    far_min = min(far_min, static_cast<int32_t>(d));
-                    far_max = max(far_max, static_cast<int32_t>(d));
+    const int64_t ntiles = (n_rows + kTile - 1) / kTile;
+    int32_t err = 0, row_len = 0, far_min = 0x7fffffff, far_max = 0, tile_max = 0;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t i = t * kTile + tid;
+        if (i < n_rows) {
+            const int64_t a = ld_rp(rp, i), e = ld_rp(rp, i + 1);
+            if (a > e || a < 0 || e > nnz) {
+                err |= 2;
+            } else {
+                int64_t prev = -1;
+                for (int64_t kk = a; kk < e; ++kk) {
+                    const int64_t c = col[kk];
+                    if (c < 0 || c >= n_cols) err |= 4;
+                    if (c <= prev) err |= 8;
+                    prev = c;
+                    const int64_t d = min(c > i ? c - i : i - c, int64_t(0x7fffffff));
+                    if (d > kBandHalo) {
+                        far_min = min(far_min, static_cast<int32_t>(d));
+                        far_max = max(far_max, static_cast<int32_t>(d));
+                    }
                 }
+                row_len = max(row_len, static_cast<int32_t>(min(e - a, int64_t(0x7fffffff))));
             }
-            row_len = static_cast<int32_t>(min(e - a, int64_t(0x7fffffff)));
-        }
-        if ((i % kTile) == 0) {
-            const int64_t last = min(i + kTile, n_rows);
-            int64_t cnt = ld_rp(rp, last) - a;
-            if (cnt > 0x7fffffff) cnt = 0x7fffffff;
-            if (cnt > 0) atomicMax(out + kChkTileMax, static_cast<int32_t>(cnt));
+            if (tid == 0) {
+                const int64_t last = min(i + kTile, n_rows);
+                const int64_t cnt = ld_rp(rp, last) - a;
+                if (cnt > 0) tile_max = max(tile_max, static_cast<int32_t>(min(cnt, int64_t(0x7fffffff))));
+            }
         }
     }
-    // one atomic per wave for the maxima / minima over rows
+    if (err) atomicOr(out + kChkErr, err);
     row_len = wave_max_i32(row_len);
     far_min = wave_min_i32(far_min);
     far_max = wave_max_i32(far_max);
-    if ((threadIdx.x & 63) == 0) {
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) {
+        s_m[0][w] = row_len;
+        s_m[1][w] = far_min;
+        s_m[2][w] = far_max;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int v = 1; v < kBlock / 64; ++v) {
+            row_len = max(row_len, s_m[0][v]);
+            far_min = min(far_min, s_m[1][v]);
+            far_max = max(far_max, s_m[2][v]);
+        }
         if (row_len > 0) atomicMax(out + kChkRowMax, row_len);
         if (far_max > 0) {
             atomicMin(out + kChkFarMin, far_min);
             atomicMax(out + kChkFarMax, far_max);
         }
+        if (tile_max > 0) atomicMax(out + kChkTileMax, tile_max);
     }
 }
 
@@ -1539,6 +1999,21 @@ int cg_band_blocks_per_cu(int cap)
     return c;
 }
 
+int cg_group_blocks_per_cu(int cap)
+{
+    static int cache[2] = {};
+    int& c = cache[cap <= kGCapSmall ? 0 : 1];
+    if (c > 0) return c;
+    int a = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, cap <= kGCapSmall ? k_gcg_spmv<kGCapSmall>
+                                                                            : k_gcg_spmv<kGCapLarge>,
+                                                    kBlock, 0) != hipSuccess ||
+        a < 1)
+        a = 1;
+    c = a;
+    return c;
+}
+
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s)
 {
     SLA_LAUNCH(k_cg_init, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a);
@@ -1558,6 +2033,29 @@ hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipS
 hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s)
 {
     SLA_LAUNCH(k_cg_pupd, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, hipStream_t s)
+{
+    SLA_LAUNCH(k_group_vals, dim3(grid_for(nnz * kGroup, kBlock, 2048), groups), dim3(kBlock), 0, s, vals, out, nnz,
+               groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s)
+{
+    const dim3 gu(a.Gu, a.groups), gs(a.G, a.groups), blk(kBlock);
+    switch (which) {
+    case 0: SLA_LAUNCH(k_gcg_init, gu, blk, 0, s, a); break;
+    case 1: SLA_LAUNCH(k_gcg_pupd, gu, blk, 0, s, a, k); break;
+    case 2:
+        if (a.cap <= kGCapSmall) SLA_LAUNCH(k_gcg_spmv<kGCapSmall>, gs, blk, 0, s, a, k);
+        else SLA_LAUNCH(k_gcg_spmv<kGCapLarge>, gs, blk, 0, s, a, k);
+        break;
+    case 3: SLA_LAUNCH(k_gcg_update, gu, blk, 0, s, a, k); break;
+    default: SLA_LAUNCH(k_gcg_finish, gu, blk, 0, s, a); break;
+    }
     return hipGetLastError();
 }
 
@@ -1607,8 +2105,8 @@ hipError_t launch_gather_vals(const int64_t* perm, const double* vals, double* o
 hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col, int64_t n_rows, int64_t n_cols,
                            int64_t nnz, int32_t* out, hipStream_t s)
 {
-    const int64_t nb = n_rows / kBlock + 1;   // covers row n_rows's checks via i == 0 as well
-    const dim3 grid(static_cast<unsigned>(nb)), block(kBlock);
+    const int64_t ntiles = (n_rows + kTile - 1) / kTile;
+    const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(ntiles, 8192)))), block(kBlock);
     if (rp_bits == 64)
         hipLaunchKernelGGL(k_validate<int64_t>, grid, block, 0, s, static_cast<const int64_t*>(row_ptr), col, n_rows,
                            n_cols, nnz, out);

@@ -214,7 +214,8 @@ enum {
     SLA_K_GATHER_VALS = 5,  /* transposed values */
     SLA_K_TRANSPOSE = 6,    /* pattern transpose (all its kernels) */
     SLA_K_CG_PUPD = 7,      /* split schedule: step decisions, p = r + beta p, x update */
-    SLA_K_COUNT = 8
+    SLA_K_GROUP_LAYOUT = 8, /* grouped batches: values and x between layouts */
+    SLA_K_COUNT = 9
 };
 sla_status sla_timing_enable(int32_t enable);
 sla_status sla_timing_reset(void);

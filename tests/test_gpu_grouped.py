@@ -1,0 +1,161 @@
+"""GPU parity of the grouped batch kernels, through the C ABI.
+
+Shared-pattern batches of at least 8 systems (a multiple of 4) on unstructured
+patterns (the split schedule) run with the systems interleaved in groups of 4: lane
+(row, system), one cache piece per gathered element for four systems.  The bars are
+those of the single-system path against the oracle: iterations within 2 %, x within
+1e-9, lambda and dL/dvals within 1e-8, and 1e-12 over fixed iterations.  Cases: 32
+systems (8 groups: every group pinned to one XCD), 12 systems (3 groups, not pinned),
+a batch of 8 whose systems start from b = 0, are not SPD, hold a NaN or run out of
+budget, and the residual histories of a fixed run.
+
+The fixed-iteration comparisons stop at 6 iterations.  On these FEM systems the early
+CG iterates amplify rounding differences about tenfold per iteration: on the CPU, the
+oracle and a CG that differs from it only in the summation order of its dot products
+(numpy's) agree to 7e-16 after 5 iterations, 3e-14 after 8, 2e-12 after 10 and 4e-11
+after 12 (worst of the first 8 systems), and to 8e-9 after 20 and 6e-6 after 40 on
+system 0, before both converge to the same solution.  A 1e-12 bar is therefore only
+meaningful over the first few iterations; the converged runs carry the usual bars.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import differentiable_sparse_linear_spmv_amd as S
+    return S
+
+
+@pytest.fixture(scope="module")
+def mesh():
+    # 100 x 100 vertices: permuted ids put entries up to n apart, so the analysis picks
+    # the split schedule; 32 systems with their own kappa and b
+    return W.fem_p1_batched(nv=100, B=32, seed=5)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def iters_close(k_gpu, k_orc):
+    return abs(k_gpu - k_orc) <= math.floor(0.02 * k_orc)
+
+
+def handle(S, A):
+    return S.csr_create(dev(A.row_ptr.astype(np.int32)), dev(A.col.astype(np.int32)), n_cols=A.n_cols,
+                        symmetric=True)
+
+
+def solve_pair(S, A, vals, b, rtol, max_iter=100000, fixed=False):
+    h = handle(S, A)
+    assert S.csr_analysis(h)["split"]
+    opts = S.cg_opts(rtol=rtol, max_iter=max_iter, fixed=fixed)
+    dv = dev(vals)
+    x, info = S.solve(h, dv, dev(b), opts)
+    gb, gv, binfo = S.solve_backward(h, dv, x, x.clone(), opts)
+    return host(x), host(gb), host(gv), S.read_info(info), S.read_info(binfo)
+
+
+def check_against_oracle(A, vals, b, out, rtol, max_iter=100000, fixed=False, systems=None):
+    x, lam, gv, info, binfo = out
+    tol_x, tol_adj = (1e-12, 1e-12) if fixed else (1e-9, 1e-8)
+    for s in (range(vals.shape[0]) if systems is None else systems):
+        f = O.cg(A, b[s], rtol=rtol, max_iter=max_iter, fixed=fixed, vals=vals[s])
+        assert info[s]["state"] == f["state"], (s, info[s], f["state"])
+        assert iters_close(info[s]["iterations"], f["iterations"]), (s, info[s]["iterations"], f["iterations"])
+        assert rel(x[s], f["x"]) <= tol_x, (s, rel(x[s], f["x"]))
+        bw = O.solve_backward(A, x[s], x[s], symmetric=True, rtol=rtol, max_iter=max_iter, fixed=fixed,
+                              vals=vals[s])
+        assert binfo[s]["state"] == bw["state"]
+        assert iters_close(binfo[s]["iterations"], bw["iterations"]), (s, binfo[s]["iterations"],
+                                                                       bw["iterations"])
+        assert rel(lam[s], bw["lam"]) <= tol_adj, (s, rel(lam[s], bw["lam"]))
+        assert rel(gv[s], bw["gvals"]) <= tol_adj, (s, rel(gv[s], bw["gvals"]))
+
+
+def test_grouped_32_systems_pinned(S, mesh):
+    A, b = mesh
+    out = solve_pair(S, A, A.vals, b, rtol=1e-8)
+    check_against_oracle(A, A.vals, b, out, rtol=1e-8, systems=[0, 5, 13, 22, 31])
+    its = [i["iterations"] for i in out[3]]
+    assert len(set(its)) > 1   # systems stop independently
+
+
+def test_grouped_12_systems(S, mesh):
+    A, b = mesh
+    out = solve_pair(S, A, A.vals[:12], b[:12], rtol=1e-8)
+    check_against_oracle(A, A.vals[:12], b[:12], out, rtol=1e-8, systems=[0, 7, 11])
+
+
+def test_grouped_fixed_iterations_tight(S, mesh):
+    A, b = mesh
+    out = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
+    check_against_oracle(A, A.vals[:8], b[:8], out, rtol=0.0, max_iter=6, fixed=True, systems=[0, 3, 6])
+
+
+def test_grouped_mixed_outcomes(S, mesh):
+    A, b0 = mesh
+    vals = A.vals[:8].copy()
+    b = b0[:8].copy()
+    b[1] = 0.0                       # converged at 0 iterations
+    vals[2] = -vals[2]               # not SPD at the first step
+    vals[3][17] = np.nan             # NaN
+    h = handle(S, A)
+    K = 6                            # budget far below what the others need (see the header)
+    opts = S.cg_opts(rtol=1e-8, max_iter=K)
+    x, info = S.solve(h, dev(vals), dev(b), opts)
+    inf = S.read_info(info)
+    xs = host(x)
+    for s in range(8):
+        f = O.cg(A, b[s], rtol=1e-8, max_iter=K, vals=vals[s])
+        assert inf[s]["state"] == f["state"], (s, inf[s], f["state"])
+        if f["state"] == O.MAX_ITER:
+            assert inf[s]["iterations"] == K
+            assert rel(xs[s], f["x"]) <= 1e-12, (s, rel(xs[s], f["x"]))
+    assert inf[1]["iterations"] == 0 and not np.any(xs[1])
+    assert inf[2]["state"] == O.NOT_SPD and inf[2]["iterations"] == 0 and not np.any(xs[2])
+    assert inf[3]["state"] == O.NAN
+
+
+def test_grouped_residual_histories(S, mesh):
+    A, b = mesh
+    K = 6
+    h = handle(S, A)
+    hist = torch.full((8, K + 1), float("nan"), dtype=torch.float64, device="cuda")
+    x, info = S.solve(h, dev(A.vals[:8]), dev(b[:8]), S.cg_opts(rtol=0.0, max_iter=K, fixed=True,
+                                                                 residual_history=hist))
+    hh = host(hist)
+    for s in (0, 4, 7):
+        f = O.cg(A, b[s], rtol=0.0, max_iter=K, fixed=True, vals=A.vals[s], history=True)
+        assert rel(hh[s], f["history"]) <= 1e-12, s
+
+
+def test_grouped_matches_ungrouped(S, mesh, monkeypatch):
+    # same inputs through the per-system split kernels (grouping switched off)
+    A, b = mesh
+    out_g = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
+    monkeypatch.setenv("SLA_CG_GROUPED", "0")
+    out_u = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
+    for a_, b_ in zip(out_g[:3], out_u[:3]):
+        assert rel(a_, b_) <= 1e-12
