@@ -501,7 +501,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w);
     if (st != SLA_OK) return st;
 
-    CgArgs a;
+    CgArgs a{};
     a.row_ptr = row_ptr;
     a.col = col;
     a.vals = vals;
@@ -530,6 +530,10 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.xcd_remap = 1;
     a.sys_per_xcd = (batch >= 8 && batch % 8 == 0) ? 1 : 0;
     a.split = split ? 1 : 0;
+    // systems far beyond the caches: the update pass streams with the non-temporal
+    // hint (measured 5 % faster at 169M rows; slower where the 256 MB cache holds the
+    // working set across iterations)
+    a.stream_nt = (12 * A->nnz + 52 * n) * batch > kBandStreamBytes ? 1 : 0;
     a.band_block = band_block;
     a.band_stride = band;
     a.band_lines = band_lines;

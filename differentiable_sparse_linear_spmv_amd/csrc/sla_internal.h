@@ -89,6 +89,7 @@ struct CgArgs {
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
     int32_t sys_per_xcd;     // 1: batch % 8 == 0; every system runs on one XCD
     int32_t split;           // 1: split schedule (k_cg_pupd forms p_k, the SpMV gathers it)
+    int32_t stream_nt;       // 1: the update kernel streams with the non-temporal hint
     int32_t groups;          // grouped batch: number of groups (r, p0, p1, q, vals, xg grouped)
     int32_t cap;             // grouped batch: entries per tile staged (kGCapSmall or kGCapLarge)
     double* xg;              // grouped batch: x in the grouped layout

@@ -1113,7 +1113,9 @@ __global__ __launch_bounds__(kBlock) void k_cg_pupd(CgArgs a, int64_t k)
 }
 
 // Loads of one trip of the update kernel: kStreamUnroll tiles t0, t0 + step, ...
-// (clamped indices; masked on use).
+// (clamped indices; masked on use).  NT: with the non-temporal hint (systems far
+// larger than the caches, where nothing of q or r is reused before the next pass).
+template <bool NT>
 __device__ __forceinline__ void load_trip(const TileRange& tr, int64_t m0, int64_t n, const double* __restrict__ q,
                                           const double* __restrict__ rin, double* qv, double* rv)
 {
@@ -1121,14 +1123,20 @@ __device__ __forceinline__ void load_trip(const TileRange& tr, int64_t m0, int64
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) {
         const int64_t i = min((tr.lo + m0 + u * tr.step) * kTile + tid, n - 1);
-        qv[u] = q[i];
-        rv[u] = rin[i];
+        if constexpr (NT) {
+            qv[u] = __builtin_nontemporal_load(q + i);
+            rv[u] = __builtin_nontemporal_load(rin + i);
+        } else {
+            qv[u] = q[i];
+            rv[u] = rin[i];
+        }
     }
 }
 
 // k_cg_update: alpha = rho / sigma, r -= alpha q, partial r^T r.  The first trip's
 // loads are issued before the stop check and the reduction of the sigma partials;
 // later trips are double-buffered so each trip's loads overlap the previous one.
+template <bool NT>
 __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 {
     __shared__ double s_red[kBlock / 64];
@@ -1147,7 +1155,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     double* __restrict__ r = a.r + off;
     const int64_t trip = kStreamUnroll * tr.step;
     double qa[kStreamUnroll], ra[kStreamUnroll], qb[kStreamUnroll], rb[kStreamUnroll];
-    if (tr.first < tr.len) load_trip(tr, tr.first, n, q, rin, qa, ra);
+    if (tr.first < tr.len) load_trip<NT>(tr, tr.first, n, q, rin, qa, ra);
 
     if (tid == 0) s_stop = st->stop_iter;
     const double sigma = reduce_partials(a.part_sigma + static_cast<int64_t>(sys) * a.G, a.G, s_red);
@@ -1178,7 +1186,8 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
             if (m < tr.len && i < n) {
                 const double tq = alpha * qv[u];
                 const double rn = rv[u] - tq;
-                r[i] = rn;
+                if constexpr (NT) __builtin_nontemporal_store(rn, r + i);
+                else r[i] = rn;
                 const double w = rn * rn;
                 rr = rr + w;
             }
@@ -1186,10 +1195,10 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     };
 #pragma unroll 1
     for (int64_t m0 = tr.first; m0 < tr.len; m0 += 2 * trip) {
-        if (m0 + trip < tr.len) load_trip(tr, m0 + trip, n, q, rin, qb, rb);
+        if (m0 + trip < tr.len) load_trip<NT>(tr, m0 + trip, n, q, rin, qb, rb);
         apply(m0, qa, ra);
         if (m0 + trip >= tr.len) break;
-        if (m0 + 2 * trip < tr.len) load_trip(tr, m0 + 2 * trip, n, q, rin, qa, ra);
+        if (m0 + 2 * trip < tr.len) load_trip<NT>(tr, m0 + 2 * trip, n, q, rin, qa, ra);
         apply(m0 + trip, qb, rb);
     }
     rr = block_sum(rr, s_red);
@@ -2061,7 +2070,10 @@ hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s)
 
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s)
 {
-    SLA_LAUNCH(k_cg_update, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
+    if (a.stream_nt)
+        SLA_LAUNCH(k_cg_update<true>, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
+    else
+        SLA_LAUNCH(k_cg_update<false>, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
     return hipGetLastError();
 }
 
