@@ -51,11 +51,13 @@ def lib():
         L.orc_dot.restype = f64
         L.orc_cg.argtypes = [i64, P, P, P, P, P, f64, f64, i64, i32, P, P, P, P, P]
         L.orc_cg.restype = i32
+        L.orc_pcg_jacobi.argtypes = [i64, P, P, P, P, P, f64, f64, i64, i32, P, P, P, P, P]
+        L.orc_pcg_jacobi.restype = i32
         L.orc_transpose.argtypes = [i64, i64, P, P, P, P, P]
         L.orc_transpose.restype = None
         L.orc_pattern_outer.argtypes = [i64, P, P, f64, P, P, P]
         L.orc_pattern_outer.restype = None
-        L.orc_solve_backward.argtypes = [i64, P, P, P, i32, P, P, f64, f64, i64, i32, P, P, P,
+        L.orc_solve_backward.argtypes = [i64, P, P, P, i32, P, P, f64, f64, i64, i32, i32, P, P, P,
                                          P, P, P]
         L.orc_solve_backward.restype = i32
         _lib = L
@@ -99,17 +101,20 @@ def dot(a, b) -> float:
     return float(lib().orc_dot(a.shape[0], _p(a), _p(b)))
 
 
-def cg(A, b, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, vals=None, history=False):
-    """Returns dict(x, iterations, state, res_norm, rhs_norm[, history])."""
+def cg(A, b, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, vals=None, history=False,
+       jacobi=False):
+    """Returns dict(x, iterations, state, res_norm, rhs_norm[, history]).  jacobi: the
+    Jacobi-preconditioned variant (orc_pcg_jacobi)."""
     rp, col = _pattern(A)
     v = _f64(A.vals if vals is None else vals)
     b = _f64(b)
     n = A.n_rows
     x = np.empty(n, np.float64)
-    work = np.empty(3 * max(n, 1), np.float64)
+    work = np.empty(5 * max(n, 1), np.float64)
     it, res, rhs = C.c_int64(0), C.c_double(0), C.c_double(0)
     hist = np.full(max_iter + 1, np.nan) if history else None
-    st = lib().orc_cg(n, _p(rp), _p(col), _p(v), _p(b), _p(x), rtol, atol, max_iter,
+    fn = lib().orc_pcg_jacobi if jacobi else lib().orc_cg
+    st = fn(n, _p(rp), _p(col), _p(v), _p(b), _p(x), rtol, atol, max_iter,
                       1 if fixed else 0, _p(work), C.byref(it), C.byref(res), C.byref(rhs),
                       _p(hist) if history else None)
     out = dict(x=x, iterations=int(it.value), state=int(st), res_norm=float(res.value),
@@ -139,7 +144,7 @@ def pattern_outer(A, u, v, sign=1.0) -> np.ndarray:
 
 
 def solve_backward(A, x, g, symmetric=True, rtol=1e-10, atol=0.0, max_iter=100000,
-                   fixed=False, vals=None):
+                   fixed=False, vals=None, jacobi=False):
     """Returns dict(lam (= dL/db), gvals (= dL/dvals), iterations, state, res_norm, rhs_norm)."""
     rp, col = _pattern(A)
     v = _f64(A.vals if vals is None else vals)
@@ -147,10 +152,11 @@ def solve_backward(A, x, g, symmetric=True, rtol=1e-10, atol=0.0, max_iter=10000
     n = A.n_rows
     lam = np.empty(n, np.float64)
     gv = np.empty(A.nnz, np.float64)
-    work = np.empty(3 * max(n, 1), np.float64)
+    work = np.empty(5 * max(n, 1), np.float64)
     it, res, rhs = C.c_int64(0), C.c_double(0), C.c_double(0)
     st = lib().orc_solve_backward(n, _p(rp), _p(col), _p(v), 1 if symmetric else 0, _p(x),
-                                  _p(g), rtol, atol, max_iter, 1 if fixed else 0, _p(lam),
+                                  _p(g), rtol, atol, max_iter, 1 if fixed else 0,
+                                  1 if jacobi else 0, _p(lam),
                                   _p(gv), _p(work), C.byref(it), C.byref(res), C.byref(rhs))
     return dict(lam=lam, gvals=gv, iterations=int(it.value), state=int(st),
                 res_norm=float(res.value), rhs_norm=float(rhs.value))

@@ -161,6 +161,89 @@ done:
 }
 
 /*
+ * Jacobi-preconditioned conjugate gradients, M = diag(A), x0 = 0 (the pages'
+ * pytorch-native backend: paperpeel page, section 4.1, Table 3, which runs CG with
+ * a Jacobi preconditioner):
+ *
+ *   r = b, z = M^{-1} r, p = z, rho = <r,z>, threshold = max(rtol * |b|, atol)
+ *   repeat:  q = A p;  sigma = <p,q>;  alpha = rho / sigma
+ *            x = x + alpha p;  r = r - alpha q;  z = M^{-1} r;  rho' = <r,z>
+ *            stop when |r| <= threshold (|r| = sqrt(<r,r>) of the recurrence
+ *            residual, the same test as orc_cg)
+ *            beta = rho' / rho;  p = z + beta p
+ *
+ * M^{-1} r is the solution of the diagonal system: z_i = r_i / a_ii (a division,
+ * not a multiplication by a stored reciprocal).  a_ii is the stored entry (i, i);
+ * a row without one has a_ii = 0.  If some a_ii is NaN the solve stops with NAN, if
+ * some a_ii <= 0 (M is not positive definite) with NOT_SPD, both before any
+ * iteration with x = 0.  Iteration count, budget, fixed mode and breakdowns as in
+ * orc_cg.  work: 5 n doubles (r, z, p, q, diagonal).
+ */
+int orc_pcg_jacobi(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
+                   const double* b, double* x, double rtol, double atol, int64_t max_iter,
+                   int fixed, double* work, int64_t* iters_out, double* res_out,
+                   double* rhs_out, double* hist)
+{
+    double* r = work;
+    double* z = work + n;
+    double* p = work + 2 * n;
+    double* q = work + 3 * n;
+    double* d = work + 4 * n;
+    int bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        d[i] = 0.0;
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k)
+            if (col[k] == i) d[i] = val[k];
+        if (d[i] != d[i]) bad |= 2;
+        else if (!(d[i] > 0.0)) bad |= 1;
+    }
+    for (int64_t i = 0; i < n; ++i) x[i] = 0.0;
+    double rr = orc_dot(n, b, b);
+    double bnorm = sqrt(rr);
+    double thr = rtol * bnorm;
+    if (atol > thr) thr = atol;
+    *rhs_out = bnorm;
+    if (hist) hist[0] = bnorm;
+    int64_t k = 0;
+    int state = ORC_MAX_ITER;
+    double rho = 0.0;
+    if (!fixed && bnorm <= thr) { state = ORC_CONVERGED; goto done; }
+    if (bad) { state = (bad & 2) ? ORC_NAN : ORC_NOT_SPD; goto done; }
+    for (int64_t i = 0; i < n; ++i) { r[i] = b[i]; z[i] = r[i] / d[i]; p[i] = z[i]; }
+    rho = orc_dot(n, r, z);
+    while (k < max_iter) {
+        orc_spmv(n, row_ptr, col, val, p, q);
+        double sigma = orc_dot(n, p, q);
+        if (!(sigma > 0.0)) { state = (sigma != sigma) ? ORC_NAN : ORC_NOT_SPD; goto done; }
+        double alpha = rho / sigma;
+        for (int64_t i = 0; i < n; ++i) {
+            double t = alpha * p[i];
+            x[i] = x[i] + t;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            double t = alpha * q[i];
+            r[i] = r[i] - t;
+            z[i] = r[i] / d[i];
+        }
+        rr = orc_dot(n, r, r);
+        double rho1 = orc_dot(n, r, z);
+        k = k + 1;
+        if (hist) hist[k] = sqrt(rr);
+        if (!fixed && sqrt(rr) <= thr) { state = ORC_CONVERGED; goto done; }
+        double beta = rho1 / rho;
+        for (int64_t i = 0; i < n; ++i) {
+            double t = beta * p[i];
+            p[i] = z[i] + t;
+        }
+        rho = rho1;
+    }
+done:
+    *iters_out = k;
+    *res_out = sqrt(rr);
+    return state;
+}
+
+/*
  * Transpose of an n_rows x n_cols CSR pattern by a stable counting sort on the
  * column index.  Row j of A^T lists the entries of column j of A in ascending
  * row order; perm[kT] is the position in A of entry kT of A^T, so
@@ -200,20 +283,33 @@ void orc_pattern_outer(int64_t n_rows, const int64_t* row_ptr, const int32_t* co
 /*
  * Adjoint backward pass of x = A^{-1} b for a loss L(x) with g = dL/dx:
  *   solve A^T lambda = g by the same CG (x0 = 0, same rtol / atol / budget,
- *   threshold relative to |g|), then dL/db = lambda and
- *   dL/dA_ij = -lambda_i x_j on the stored entries only.
+ *   threshold relative to |g|; Jacobi-preconditioned if jacobi != 0, A^T has the
+ *   same diagonal), then dL/db = lambda and dL/dA_ij = -lambda_i x_j on the stored
+ *   entries only.
  * symmetric != 0: A^T is A (same arrays).  Otherwise A^T is formed by
- * orc_transpose.  lam and gvals (nullable) are outputs; work: 3 n doubles.
+ * orc_transpose.  lam and gvals (nullable) are outputs; work: 5 n doubles.
  */
+static int orc_solve_either(int jacobi, int64_t n, const int64_t* row_ptr, const int32_t* col,
+                            const double* val, const double* b, double* x, double rtol, double atol,
+                            int64_t max_iter, int fixed, double* work, int64_t* iters_out,
+                            double* res_out, double* rhs_out)
+{
+    if (jacobi)
+        return orc_pcg_jacobi(n, row_ptr, col, val, b, x, rtol, atol, max_iter, fixed, work, iters_out,
+                              res_out, rhs_out, NULL);
+    return orc_cg(n, row_ptr, col, val, b, x, rtol, atol, max_iter, fixed, work, iters_out, res_out,
+                  rhs_out, NULL);
+}
+
 int orc_solve_backward(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
                        int symmetric, const double* x, const double* g, double rtol, double atol,
-                       int64_t max_iter, int fixed, double* lam, double* gvals, double* work,
+                       int64_t max_iter, int fixed, int jacobi, double* lam, double* gvals, double* work,
                        int64_t* iters_out, double* res_out, double* rhs_out)
 {
     int state;
     if (symmetric) {
-        state = orc_cg(n, row_ptr, col, val, g, lam, rtol, atol, max_iter, fixed, work,
-                       iters_out, res_out, rhs_out, NULL);
+        state = orc_solve_either(jacobi, n, row_ptr, col, val, g, lam, rtol, atol, max_iter, fixed, work,
+                                 iters_out, res_out, rhs_out);
     } else {
         int64_t nnz = row_ptr[n];
         int64_t* rpt = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
@@ -222,8 +318,8 @@ int orc_solve_backward(int64_t n, const int64_t* row_ptr, const int32_t* col, co
         double* vt = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
         orc_transpose(n, n, row_ptr, col, rpt, ct, perm);
         for (int64_t k = 0; k < nnz; ++k) vt[k] = val[perm[k]];
-        state = orc_cg(n, rpt, ct, vt, g, lam, rtol, atol, max_iter, fixed, work,
-                       iters_out, res_out, rhs_out, NULL);
+        state = orc_solve_either(jacobi, n, rpt, ct, vt, g, lam, rtol, atol, max_iter, fixed, work,
+                                 iters_out, res_out, rhs_out);
         free(rpt); free(ct); free(perm); free(vt);
     }
     if (gvals) orc_pattern_outer(n, row_ptr, col, -1.0, lam, x, gvals);

@@ -29,6 +29,9 @@ MUTANTS = {
     "transposed spmv is forward": ("y[col[k]] = y[col[k]] + t;", "y[i] = y[i] + val[k] * x[col[k]];"),
     "dot drops the product remainders": ("c = c + (q + r);", "c = c + q;"),
     "dot is a plain sequential sum": ("return s + c;", "return s;"),
+    "pcg without the preconditioner": ("            z[i] = r[i] / d[i];", "            z[i] = r[i];"),
+    "pcg beta from <r,r>": ("double rho1 = orc_dot(n, r, z);", "double rho1 = orc_dot(n, r, r);"),
+    "pcg direction from r": ("            p[i] = z[i] + t;", "            p[i] = r[i] + t;"),
 }
 
 

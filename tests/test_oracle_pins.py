@@ -31,6 +31,10 @@ EPS = np.finfo(np.float64).eps
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
+def rel_err(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(b))
+
+
 def dense(A, vals=None):
     v = A.vals if vals is None else vals
     return sp.csr_matrix((v, A.col, A.row_ptr.astype(np.int64)), shape=(A.n_rows, A.n_cols)).toarray()
@@ -123,6 +127,85 @@ def test_dot_is_the_exact_sum_rounded():
             a, b = np.concatenate([a, -a * (1 + 2.0 ** -40)]), np.concatenate([b, b])
         e = exact_dot(a, b)
         assert abs(O.dot(a, b) - e) <= np.spacing(abs(e)), trial
+
+
+# ----------------------------------------------------------------------------- Jacobi PCG
+def scaled(A, s):
+    """S A S for S = diag(s): entry (i, j) times s_i s_j."""
+    rows = np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+    return W.CSR(A.n_rows, A.n_cols, A.row_ptr, A.col, A.vals * s[rows] * s[A.col])
+
+
+def test_pcg_is_cg_bit_for_bit_on_a_constant_diagonal():
+    # diagonal 4: z = r / 4 and every scaling by a power of two is exact, so PCG and CG
+    # produce the same iterates to the last bit
+    A = W.poisson5(20)
+    b = W.rhs_uniform(A.n_rows, 3)
+    f = O.cg(A, b, rtol=1e-10, history=True)
+    g = O.cg(A, b, rtol=1e-10, history=True, jacobi=True)
+    assert g["iterations"] == f["iterations"] and g["state"] == f["state"]
+    assert np.array_equal(g["x"], f["x"]) and np.array_equal(g["history"], f["history"])
+
+
+def test_pcg_on_a_diagonal_matrix_takes_one_iteration():
+    n = 300
+    d = np.random.default_rng(4).uniform(0.1, 10.0, n)
+    A = W.CSR(n, n, np.arange(n + 1, dtype=np.int64), np.arange(n, dtype=np.int32), d)
+    b = W.rhs_normal(n, 5)
+    g = O.cg(A, b, rtol=1e-12, jacobi=True)
+    assert g["iterations"] == 1 and g["state"] == O.CONVERGED
+    assert np.allclose(g["x"], b / d, rtol=1e-15, atol=0)
+    f = O.cg(A, b, rtol=1e-12)                 # plain CG needs many more
+    assert f["iterations"] > 20
+
+
+@pytest.mark.parametrize("N", [12, 20])
+def test_pcg_on_a_rescaled_matrix_follows_cg(N):
+    # PCG with M = diag(S A S) on S A S x' = S b is CG on A / 4 (A = 5-point Poisson,
+    # diagonal 4): the same Krylov iterates, x' = S^-1 x, iteration for iteration
+    A = W.poisson5(N)
+    s = np.random.default_rng(N).uniform(0.3, 3.0, A.n_rows)
+    b = W.rhs_normal(A.n_rows, 6)
+    f = O.cg(A, b, rtol=1e-10, history=True)
+    g = O.cg(scaled(A, s), s * b, rtol=0.0, max_iter=f["iterations"], fixed=True, jacobi=True)
+    assert rel_err(g["x"] * s, f["x"]) <= 1e-8
+    # the preconditioned residual norms <r', M^-1 r'> = <r, r> / 4 track CG's
+    h = O.cg(scaled(A, s), s * b, rtol=1e-10, jacobi=True)
+    assert abs(h["iterations"] - f["iterations"]) <= 2
+    # plain CG on the rescaled matrix is far slower
+    assert O.cg(scaled(A, s), s * b, rtol=1e-10)["iterations"] > 1.5 * f["iterations"]
+
+
+def test_pcg_vs_dense_lu_varcoef():
+    A, b, _ = W.varcoef_poisson5(14, seed=2)
+    D = dense(A)
+    xs = np.linalg.solve(D, b)
+    g = O.cg(A, b, rtol=1e-12, jacobi=True)
+    assert g["state"] == O.CONVERGED
+    assert rel_err(g["x"], xs) <= np.linalg.cond(D) * 1e-12
+    f = O.cg(A, b, rtol=1e-12)
+    assert g["iterations"] < f["iterations"]   # the coefficient jumps make Jacobi pay
+
+
+def test_pcg_invalid_diagonal_and_adjoint():
+    A = W.poisson5(10)
+    b = W.rhs_uniform(A.n_rows, 1)
+    rows = np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+    v = A.vals.copy()
+    v[np.nonzero(rows == A.col)[0][7]] = 0.0
+    g = O.cg(A, b, vals=v, jacobi=True)
+    assert g["state"] == O.NOT_SPD and g["iterations"] == 0 and not np.any(g["x"])
+    v[np.nonzero(rows == A.col)[0][7]] = np.nan
+    assert O.cg(A, b, vals=v, jacobi=True)["state"] == O.NAN
+    assert O.cg(A, np.zeros(A.n_rows), vals=v, jacobi=True)["state"] == O.CONVERGED   # b = 0 first
+    # the adjoint with Jacobi solves the same system: lambda = A^-1 g
+    A2, b2, _ = W.varcoef_poisson5(10, seed=4)
+    x = O.cg(A2, b2, rtol=1e-12, jacobi=True)["x"]
+    bw = O.solve_backward(A2, x, x, symmetric=True, rtol=1e-12, jacobi=True)
+    lam = np.linalg.solve(dense(A2), x)
+    assert rel_err(bw["lam"], lam) <= 1e-9
+    rows2 = np.repeat(np.arange(A2.n_rows), np.diff(A2.row_ptr.astype(np.int64)))
+    assert np.array_equal(bw["gvals"], -(bw["lam"][rows2] * x[A2.col]))
 
 
 # ----------------------------------------------------------------------------- CG
