@@ -234,6 +234,8 @@ def main() -> int:
     ap.add_argument("--cpu-iters", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--jacobi", action="store_true",
+                    help="Jacobi-preconditioned CG (SLA_JACOBI) instead of the plain CG of the metric")
     ap.add_argument("--fixed-iters", type=int, default=0,
                     help="profiling runs: exactly this many CG iterations per solve")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -269,7 +271,7 @@ def main() -> int:
         spmv_kernel, schedule = "k_cg_spmv", "fused"
     if args.fixed_iters > 0:
         w["max_iter"], w["fixed"], w["rtol"] = args.fixed_iters, True, 0.0
-    opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"])
+    opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"], jacobi=args.jacobi)
     vals, b = w["vals"], w["b"]
 
     def step():
@@ -308,8 +310,8 @@ def main() -> int:
     # timed launch is a working one.
     S.timing.reset()
     S.timing.enable(True)
-    fo = S.cg_opts(rtol=0.0, max_iter=max_fwd, fixed=True)
-    bo = S.cg_opts(rtol=0.0, max_iter=max_bwd, fixed=True)
+    fo = S.cg_opts(rtol=0.0, max_iter=max_fwd, fixed=True, jacobi=args.jacobi)
+    bo = S.cg_opts(rtol=0.0, max_iter=max_bwd, fixed=True, jacobi=args.jacobi)
     x, _ = S.solve(h, vals, b, fo)
     S.solve_backward(h, vals, x, loss_grad(w, x), bo)
     S.timing.collect()
@@ -354,7 +356,7 @@ def main() -> int:
         "config": {"workload": w["desc"], "n": n, "nnz": nnz, "batch": B,
                    "row_ptr": f"int{8 * rp_bytes}", "rtol": w["rtol"],
                    "fixed_iterations": w["fixed"], "parallelism": "none (1 GPU)",
-                   "cg_schedule": schedule},
+                   "cg_schedule": schedule, "preconditioner": "jacobi" if args.jacobi else "none"},
         "iterations_per_step": {"forward": fwd_it[-1], "adjoint": bwd_it[-1]},
         "solve_adjoint_ms": round(ms_step, 4),
         "hbm_gbps_per_iteration": round(iter_gbps, 1),

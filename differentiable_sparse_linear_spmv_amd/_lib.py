@@ -19,6 +19,7 @@ STATE_NAMES = {0: "CONVERGED", 1: "MAX_ITER", 2: "NOT_SPD", 3: "NAN"}
 SLA_SYMMETRIC = 1
 SLA_EAGER_TRANSPOSE = 2
 SLA_FIXED_ITERS = 1
+SLA_JACOBI = 2
 (SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
  SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_GROUP_LAYOUT, SLA_K_COUNT) = range(10)
 KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "gather_vals",

@@ -221,23 +221,24 @@ int blocks_per_system(const sla_csr* A, int64_t ntiles, int64_t batch, int per_c
 }
 
 struct Workspace {
-    double *r, *p0, *p1, *q, *part_sigma, *part_rho;
+    double *r, *p0, *p1, *q, *z, *dg, *part_sigma, *part_rho, *part_rr, *part_aux;
     SysState* st;
     int32_t* n_active;
 };
 
-size_t workspace_bytes(int64_t n, int64_t batch, int G)
+// vectors r, p0, p1, q (+ z, dg with Jacobi); partials sigma, rho (+ rr, aux)
+size_t workspace_bytes(int64_t n, int64_t batch, int G, bool jacobi)
 {
     const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
-    return 4 * vec + 2 * part + align256(sizeof(SysState) * batch) + 256;
+    return (jacobi ? 6 : 4) * vec + (jacobi ? 4 : 2) * part + align256(sizeof(SysState) * batch) + 256;
 }
 
-// G: the larger of the two grids (both partial arrays get room for it).
-sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w)
+// G: the larger of the two grids (every partial array gets room for it).
+sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, bool jacobi = false)
 {
     const int64_t n = A->n_rows;
-    const size_t need = workspace_bytes(n, batch, G);
+    const size_t need = workspace_bytes(n, batch, G, jacobi);
     if (need > A->ws_bytes) {
         if (A->ws) {
             HIP_TRY(hipDeviceSynchronize());
@@ -252,14 +253,19 @@ sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w)
     char* p = static_cast<char*>(A->ws);
     const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
+    const int nv = jacobi ? 6 : 4, np = jacobi ? 4 : 2;
     w->r = reinterpret_cast<double*>(p);
     w->p0 = reinterpret_cast<double*>(p + vec);
     w->p1 = reinterpret_cast<double*>(p + 2 * vec);
     w->q = reinterpret_cast<double*>(p + 3 * vec);
-    w->part_sigma = reinterpret_cast<double*>(p + 4 * vec);
-    w->part_rho = reinterpret_cast<double*>(p + 4 * vec + part);
-    w->st = reinterpret_cast<SysState*>(p + 4 * vec + 2 * part);
-    w->n_active = reinterpret_cast<int32_t*>(p + 4 * vec + 2 * part + align256(sizeof(SysState) * batch));
+    w->z = jacobi ? reinterpret_cast<double*>(p + 4 * vec) : nullptr;
+    w->dg = jacobi ? reinterpret_cast<double*>(p + 5 * vec) : nullptr;
+    w->part_sigma = reinterpret_cast<double*>(p + nv * vec);
+    w->part_rho = reinterpret_cast<double*>(p + nv * vec + part);
+    w->part_rr = jacobi ? reinterpret_cast<double*>(p + nv * vec + 2 * part) : nullptr;
+    w->part_aux = jacobi ? reinterpret_cast<double*>(p + nv * vec + 3 * part) : nullptr;
+    w->st = reinterpret_cast<SysState*>(p + nv * vec + np * part);
+    w->n_active = reinterpret_cast<int32_t*>(p + nv * vec + np * part + align256(sizeof(SysState) * batch));
     return SLA_OK;
 }
 
@@ -270,7 +276,7 @@ sla_status check_opts(const sla_cg_opts* o)
         return fail(SLA_ERR_INVALID_ARG, "rtol and atol must be >= 0 (got %g, %g)", o->rtol, o->atol);
     if (o->max_iter < 0) return fail(SLA_ERR_INVALID_ARG, "max_iter must be >= 0");
     if (o->check_every < 0) return fail(SLA_ERR_INVALID_ARG, "check_every must be >= 0");
-    if (o->flags & ~SLA_FIXED_ITERS) return fail(SLA_ERR_INVALID_ARG, "unknown cg flags 0x%x", o->flags);
+    if (o->flags & ~(SLA_FIXED_ITERS | SLA_JACOBI)) return fail(SLA_ERR_INVALID_ARG, "unknown cg flags 0x%x", o->flags);
     return SLA_OK;
 }
 
@@ -461,7 +467,9 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
                   bool split, int64_t batch, const double* vals, const double* b, double* x, const sla_cg_opts* o,
                   sla_cg_info* info, hipStream_t s)
 {
-    if (split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 && A->krp_bits == 32 && A->group_ok &&
+    const bool jacobi = (o->flags & SLA_JACOBI) != 0;
+    if (!jacobi && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 && A->krp_bits == 32 &&
+        A->group_ok &&
         static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapLarge && row_ptr == A->krp)
         return run_cg_grouped(A, row_ptr, col, batch, vals, b, x, o, info, s);
     const int64_t n = A->n_rows;
@@ -498,7 +506,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         if (Gu > ntiles) Gu = Gp;
     }
     Workspace w;
-    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w);
+    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi);
     if (st != SLA_OK) return st;
 
     CgArgs a{};
@@ -513,6 +521,11 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.q = w.q;
     a.part_sigma = w.part_sigma;
     a.part_rho = w.part_rho;
+    a.part_rr = w.part_rr;
+    a.part_aux = w.part_aux;
+    a.z = w.z;
+    a.dg = w.dg;
+    a.jacobi = jacobi ? 1 : 0;
     a.st = w.st;
     a.info = info;
     a.hist = o->residual_history;
@@ -539,7 +552,9 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.band_lines = band_lines;
     const int rp_bits = A->krp_bits;   // A and its transpose use the same row-pointer width
 
-    hipError_t e = timed(SLA_K_CG_INIT, s, [&] { return launch_cg_init(a, s); });
+    hipError_t e = hipSuccess;
+    if (a.jacobi) e = timed(SLA_K_CG_INIT, s, [&] { return launch_cg_diag(a, rp_bits, s); });
+    if (e == hipSuccess) e = timed(SLA_K_CG_INIT, s, [&] { return launch_cg_init(a, s); });
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "cg init launch: %s", hipGetErrorString(e));
 
     auto step = [&](int64_t k) -> hipError_t {

@@ -51,11 +51,11 @@ constexpr int kGCapLarge = 1024;
 // its first workgroup writes the new one.
 struct SysState {
     int64_t stop_iter;   // INT64_MAX while running; else the iteration at which it stopped
-    double rho[2];       // rho_k = r_k^T r_k, slot k & 1
+    double rho[2];       // rho_k = r_k^T r_k (with Jacobi r_k^T z_k), slot k & 1
     double alpha[2];     // alpha_k, slot k & 1
     double thr;          // stop threshold max(rtol |rhs|, atol)
     double rhs;          // |rhs|
-    double pad;
+    double rr;           // Jacobi: |r_k|^2 of the last step (rho holds r^T z)
 };
 static_assert(sizeof(SysState) == 64, "SysState layout");
 
@@ -71,7 +71,11 @@ struct CgArgs {
     double* p1;              // [batch][n]   p_k for odd k
     double* q;               // [batch][n]   A p_k
     double* part_sigma;      // [batch][G]   written by k_cg_spmv
-    double* part_rho;        // [batch][Gu]  written by k_cg_init / k_cg_update
+    double* part_rho;        // [batch][Gu]  written by k_cg_init / k_cg_update (rho_k partials)
+    double* part_rr;         // [batch][Gu]  Jacobi: r^T r partials (the stop test)
+    double* part_aux;        // [batch][Gu]  Jacobi: bad-diagonal flags of k_cg_init
+    double* z;               // [batch][n]   Jacobi: z_k = M^{-1} r_k
+    double* dg;              // [batch][n]   Jacobi: the diagonal of A
     SysState* st;            // [batch]
     sla_cg_info* info;       // [batch]
     double* hist;            // nullable, [batch][max_iter + 1]
@@ -89,6 +93,7 @@ struct CgArgs {
     int32_t xcd_remap;       // 1: map workgroups so each XCD streams contiguous tiles
     int32_t sys_per_xcd;     // 1: batch % 8 == 0; every system runs on one XCD
     int32_t split;           // 1: split schedule (k_cg_pupd forms p_k, the SpMV gathers it)
+    int32_t jacobi;          // 1: Jacobi-preconditioned CG
     int32_t stream_nt;       // 1: the update kernel streams with the non-temporal hint
     int32_t groups;          // grouped batch: number of groups (r, p0, p1, q, vals, xg grouped)
     int32_t cap;             // grouped batch: entries per tile staged (kGCapSmall or kGCapLarge)
@@ -114,6 +119,7 @@ int cg_group_blocks_per_cu(int cap);   // the grouped SpMV
 
 // Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s);
+hipError_t launch_cg_diag(const CgArgs& a, int rp_bits, hipStream_t s);   // Jacobi: diagonal, before init
 hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s);
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s);
 hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s);   // split schedule

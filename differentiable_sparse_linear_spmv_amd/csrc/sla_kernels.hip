@@ -301,6 +301,13 @@ __device__ __forceinline__ double tile_rowsum_long(const RP* __restrict__ rp, co
 // ----------------------------------------------------------------------------------
 constexpr int kStreamUnroll = 4;   // tiles per loop trip of the streaming kernels
 
+// Jacobi: k_cg_diag stores one flag per workgroup, kDiagNaN if some diagonal entry of
+// its rows is NaN, else kDiagNonPos if one is <= 0 or missing, else 0.  Summed over
+// the (at most 65535) workgroups of a system, the total reaches kDiagNaN exactly when
+// some entry is NaN.
+constexpr double kDiagNonPos = 1.0;
+constexpr double kDiagNaN = 65536.0;
+
 __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
 {
     __shared__ double s_red[kBlock / 64];
@@ -313,13 +320,15 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
     const double* __restrict__ b = a.b + off;
     double* __restrict__ x = a.x + off;
     double* __restrict__ pm1 = a.p1 + off;   // p_{-1} = 0
-    double rr = 0.0;
+    const bool jac = a.jacobi != 0;
+    double rr = 0.0, rz = 0.0;
     for (int64_t m0 = tr.first; m0 < tr.len; m0 += kStreamUnroll * tr.step) {
-        double bv[kStreamUnroll];
+        double bv[kStreamUnroll], dv[kStreamUnroll];
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) {
-            const int64_t i = (tr.lo + m0 + u * tr.step) * kTile + tid;
-            bv[u] = b[min(i, a.n - 1)];
+            const int64_t i = min((tr.lo + m0 + u * tr.step) * kTile + tid, a.n - 1);
+            bv[u] = b[i];
+            dv[u] = jac ? a.dg[off + i] : 1.0;
         }
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) {
@@ -330,15 +339,73 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
                 pm1[i] = 0.0;
                 const double w = bv[u] * bv[u];
                 rr = rr + w;
+                if (jac) {                       // z_0 = M^{-1} b
+                    const double zv = bv[u] / dv[u];
+                    a.z[off + i] = zv;
+                    const double wz = bv[u] * zv;
+                    rz = rz + wz;
+                }
             }
         }
     }
     rr = block_sum(rr, s_red);
+    if (jac) rz = block_sum(rz, s_red);
     if (tid == 0) {
-        a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+        if (jac) {
+            a.part_rr[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+            a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rz;
+        } else {
+            a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+        }
         if (lb == 0) a.st[sys].stop_iter = INT64_MAX;
         if (lb == 0 && sys == 0) *a.n_active = a.batch;
     }
+}
+
+__device__ __forceinline__ double block_max(double v, double* s_red)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) s_red[w] = v;
+    __syncthreads();
+    const double t = fmax(fmax(s_red[0], s_red[1]), fmax(s_red[2], s_red[3]));
+    __syncthreads();
+    return t;
+}
+
+// Jacobi: the diagonal of A (entry (i, i) found by binary search in the ascending
+// columns of row i; 0 if not stored) into dg, and the workgroup's flag partial (see
+// kDiagNaN).  Same grid and partial slots as k_cg_init, which runs after it.
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_cg_diag(CgArgs a)
+{
+    __shared__ double s_red[kBlock / 64];
+    const BlockCoord bc = block_coord(a, a.Gu);
+    const int sys = bc.sys;
+    const int tid = threadIdx.x;
+    const TileRange tr = bc.tr;
+    const RP* __restrict__ rp = static_cast<const RP*>(a.row_ptr);
+    const double* __restrict__ vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
+    double* __restrict__ dg = a.dg + static_cast<int64_t>(sys) * a.n;
+    double flag = 0.0;
+    for (int64_t m = tr.first; m < tr.len; m += tr.step) {
+        const int64_t i = (tr.lo + m) * kTile + tid;
+        if (i < a.n) {
+            int64_t lo = ld_rp(rp, i), hi = ld_rp(rp, i + 1);
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (a.col[mid] < i) lo = mid + 1;
+                else hi = mid;
+            }
+            const double d = (lo < ld_rp(rp, i + 1) && a.col[lo] == i) ? vals[lo] : 0.0;
+            dg[i] = d;
+            if (d != d) flag = kDiagNaN;
+            else if (!(d > 0.0)) flag = fmax(flag, kDiagNonPos);
+        }
+    }
+    flag = block_max(flag, s_red);
+    if (tid == 0) a.part_aux[static_cast<int64_t>(sys) * a.Gu + bc.lb] = flag;
 }
 
 // Start of a CG SpMV launch for system sys at iteration k: read the stop word, sum
@@ -350,6 +417,13 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
 constexpr int kStepRun = 0;
 constexpr int kStepStopped = 1;
 constexpr int kStepStopNow = 2;
+
+// The vector p_k is formed from: r_k (r_0 = b, never copied) or, with Jacobi, z_k.
+__device__ __forceinline__ const double* gathered_r(const CgArgs& a, bool first)
+{
+    return a.jacobi ? a.z : (first ? a.b : a.r);
+}
+
 
 __device__ __forceinline__ int cg_step_begin(const CgArgs& a, int sys, int lb, int64_t k, double* s_red,
                                              int64_t* s_stop, double& beta, double& alpha_prev)
@@ -363,10 +437,15 @@ __device__ __forceinline__ int cg_step_begin(const CgArgs& a, int sys, int lb, i
     // workgroup may be writing stop_iter = k.
     if (tid == 0) *s_stop = st->stop_iter;
     const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
+    // |r_k|: from rho_k itself, or (Jacobi, rho_k = r^T z) from its own partials
+    const double rr_k =
+        a.jacobi ? reduce_partials(a.part_rr + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red) : rho_k;
+    const double diag_flags =
+        (a.jacobi && first) ? reduce_partials(a.part_aux + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red) : 0.0;
     beta = 0.0;
     alpha_prev = 0.0;
     if (*s_stop < k) return kStepStopped;
-    const double res = sqrt(rho_k);
+    const double res = sqrt(rr_k);
     double thr, rhs;
     if (first) {
         rhs = res;
@@ -381,6 +460,8 @@ __device__ __forceinline__ int cg_step_begin(const CgArgs& a, int sys, int lb, i
 
     int code = -1;
     if (!a.fixed && res <= thr) code = SLA_CONVERGED;
+    else if (diag_flags >= kDiagNaN) code = SLA_NAN;        // Jacobi, k = 0: unusable diagonal
+    else if (diag_flags > 0.0) code = SLA_NOT_SPD;
     else if (k >= a.max_iter) code = SLA_MAX_ITER;
     if (code >= 0) {
         if (lead) {
@@ -400,6 +481,7 @@ __device__ __forceinline__ int cg_step_begin(const CgArgs& a, int sys, int lb, i
     beta = first ? 0.0 : rho_k / st->rho[(k - 1) & 1];
     if (lead) {
         st->rho[k & 1] = rho_k;
+        st->rr = rr_k;
         if (first) { st->thr = thr; st->rhs = rhs; }
     }
     return kStepRun;
@@ -489,7 +571,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     auto tile_of = [&](int64_t m) { return tr.lo + m; };
     auto tile_k0 = [&](int64_t m) { return ld_rp_uniform(rp, tile_of(m) * kTile); };
     auto tile_k1 = [&](int64_t m) { return ld_rp_uniform(rp, min((tile_of(m) + 1) * kTile, n)); };
-    const double* __restrict__ rin = (first ? a.b : a.r) + off;          // r_k (r_0 = b)
+    const double* __restrict__ rin = gathered_r(a, first) + off;         // r_k (r_0 = b), or z_k
     const double* __restrict__ pprev = ((k & 1) ? a.p0 : a.p1) + off;   // p_{k-1}
     double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;          // p_k
     double* __restrict__ x = a.x + off;
@@ -1018,7 +1100,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
     W.rp = static_cast<const int32_t*>(a.row_ptr);
     W.col = a.col;
     W.vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
-    W.rin = (first ? a.b : a.r) + off;              // r_k (r_0 = b)
+    W.rin = gathered_r(a, first) + off;             // r_k (r_0 = b), or z_k
     W.pprev = ((k & 1) ? a.p0 : a.p1) + off;       // p_{k-1}
     double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;   // p_k
     double* __restrict__ x = a.x + off;
@@ -1077,7 +1159,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_pupd(CgArgs a, int64_t k)
     const bool first = (k == 0);
     const int64_t off = static_cast<int64_t>(sys) * a.n;
     const int64_t n = a.n;
-    const double* __restrict__ rin = (first ? a.b : a.r) + off;
+    const double* __restrict__ rin = gathered_r(a, first) + off;
     const double* __restrict__ pprev = ((k & 1) ? a.p0 : a.p1) + off;
     double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;
     double* __restrict__ x = a.x + off;
@@ -1115,9 +1197,10 @@ __global__ __launch_bounds__(kBlock) void k_cg_pupd(CgArgs a, int64_t k)
 // Loads of one trip of the update kernel: kStreamUnroll tiles t0, t0 + step, ...
 // (clamped indices; masked on use).  NT: with the non-temporal hint (systems far
 // larger than the caches, where nothing of q or r is reused before the next pass).
-template <bool NT>
+template <bool NT, bool JAC>
 __device__ __forceinline__ void load_trip(const TileRange& tr, int64_t m0, int64_t n, const double* __restrict__ q,
-                                          const double* __restrict__ rin, double* qv, double* rv)
+                                          const double* __restrict__ rin, const double* __restrict__ dg, double* qv,
+                                          double* rv, double* dv)
 {
     const int tid = threadIdx.x;
 #pragma unroll
@@ -1126,9 +1209,11 @@ __device__ __forceinline__ void load_trip(const TileRange& tr, int64_t m0, int64
         if constexpr (NT) {
             qv[u] = __builtin_nontemporal_load(q + i);
             rv[u] = __builtin_nontemporal_load(rin + i);
+            if constexpr (JAC) dv[u] = __builtin_nontemporal_load(dg + i);
         } else {
             qv[u] = q[i];
             rv[u] = rin[i];
+            if constexpr (JAC) dv[u] = dg[i];
         }
     }
 }
@@ -1136,7 +1221,7 @@ __device__ __forceinline__ void load_trip(const TileRange& tr, int64_t m0, int64
 // k_cg_update: alpha = rho / sigma, r -= alpha q, partial r^T r.  The first trip's
 // loads are issued before the stop check and the reduction of the sigma partials;
 // later trips are double-buffered so each trip's loads overlap the previous one.
-template <bool NT>
+template <bool NT, bool JAC>
 __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 {
     __shared__ double s_red[kBlock / 64];
@@ -1153,9 +1238,12 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     const double* __restrict__ rin = (k == 0 ? a.b : a.r) + off;
     const double* __restrict__ q = a.q + off;
     double* __restrict__ r = a.r + off;
+    const double* __restrict__ dg = JAC ? a.dg + off : nullptr;
+    double* __restrict__ z = JAC ? a.z + off : nullptr;
     const int64_t trip = kStreamUnroll * tr.step;
     double qa[kStreamUnroll], ra[kStreamUnroll], qb[kStreamUnroll], rb[kStreamUnroll];
-    if (tr.first < tr.len) load_trip<NT>(tr, tr.first, n, q, rin, qa, ra);
+    double da[JAC ? kStreamUnroll : 1], db[JAC ? kStreamUnroll : 1];
+    if (tr.first < tr.len) load_trip<NT, JAC>(tr, tr.first, n, q, rin, dg, qa, ra, da);
 
     if (tid == 0) s_stop = st->stop_iter;
     const double sigma = reduce_partials(a.part_sigma + static_cast<int64_t>(sys) * a.G, a.G, s_red);
@@ -1166,7 +1254,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
             st->stop_iter = k;
             sla_cg_info inf;
             inf.iterations = k;
-            inf.res_norm = sqrt(rho_k);
+            inf.res_norm = sqrt(JAC ? st->rr : rho_k);
             inf.rhs_norm = st->rhs;
             inf.state = (sigma != sigma) ? SLA_NAN : SLA_NOT_SPD;
             inf.reserved = 0;
@@ -1177,8 +1265,8 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     }
     const double alpha = rho_k / sigma;
     if (lead) st->alpha[k & 1] = alpha;
-    double rr = 0.0;
-    auto apply = [&](int64_t m0, const double* qv, const double* rv) {
+    double rr = 0.0, rz = 0.0;
+    auto apply = [&](int64_t m0, const double* qv, const double* rv, const double* dv) {
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) {
             const int64_t m = m0 + u * tr.step;
@@ -1190,19 +1278,34 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
                 else r[i] = rn;
                 const double w = rn * rn;
                 rr = rr + w;
+                if constexpr (JAC) {
+                    const double zn = rn / dv[u];   // z = M^{-1} r
+                    if constexpr (NT) __builtin_nontemporal_store(zn, z + i);
+                    else z[i] = zn;
+                    const double wz = rn * zn;
+                    rz = rz + wz;
+                }
             }
         }
     };
 #pragma unroll 1
     for (int64_t m0 = tr.first; m0 < tr.len; m0 += 2 * trip) {
-        if (m0 + trip < tr.len) load_trip<NT>(tr, m0 + trip, n, q, rin, qb, rb);
-        apply(m0, qa, ra);
+        if (m0 + trip < tr.len) load_trip<NT, JAC>(tr, m0 + trip, n, q, rin, dg, qb, rb, db);
+        apply(m0, qa, ra, da);
         if (m0 + trip >= tr.len) break;
-        if (m0 + 2 * trip < tr.len) load_trip<NT>(tr, m0 + 2 * trip, n, q, rin, qa, ra);
-        apply(m0 + trip, qb, rb);
+        if (m0 + 2 * trip < tr.len) load_trip<NT, JAC>(tr, m0 + 2 * trip, n, q, rin, dg, qa, ra, da);
+        apply(m0 + trip, qb, rb, db);
     }
     rr = block_sum(rr, s_red);
-    if (tid == 0) a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+    if constexpr (JAC) {
+        rz = block_sum(rz, s_red);
+        if (tid == 0) {
+            a.part_rr[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+            a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rz;
+        }
+    } else {
+        if (tid == 0) a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+    }
 }
 
 // ----------------------------------------------------------------------------------
@@ -2023,6 +2126,13 @@ int cg_group_blocks_per_cu(int cap)
     return c;
 }
 
+hipError_t launch_cg_diag(const CgArgs& a, int rp_bits, hipStream_t s)
+{
+    if (rp_bits == 64) SLA_LAUNCH(k_cg_diag<int64_t>, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a);
+    else SLA_LAUNCH(k_cg_diag<int32_t>, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s)
 {
     SLA_LAUNCH(k_cg_init, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a);
@@ -2070,10 +2180,14 @@ hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s)
 
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s)
 {
-    if (a.stream_nt)
-        SLA_LAUNCH(k_cg_update<true>, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
-    else
-        SLA_LAUNCH(k_cg_update<false>, dim3(a.Gu, a.batch), dim3(kBlock), 0, s, a, k);
+    const dim3 grid(a.Gu, a.batch), blk(kBlock);
+    if (a.jacobi) {
+        if (a.stream_nt) SLA_LAUNCH((k_cg_update<true, true>), grid, blk, 0, s, a, k);
+        else SLA_LAUNCH((k_cg_update<false, true>), grid, blk, 0, s, a, k);
+    } else {
+        if (a.stream_nt) SLA_LAUNCH((k_cg_update<true, false>), grid, blk, 0, s, a, k);
+        else SLA_LAUNCH((k_cg_update<false, false>), grid, blk, 0, s, a, k);
+    }
     return hipGetLastError();
 }
 

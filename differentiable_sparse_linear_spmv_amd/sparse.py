@@ -154,9 +154,9 @@ def matvec_backward(h: Handle, vals: torch.Tensor, x: torch.Tensor, gy: torch.Te
 
 
 def cg_opts(rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, check_every=0,
-            residual_history: torch.Tensor | None = None) -> SlaCgOpts:
-    return SlaCgOpts(float(rtol), float(atol), int(max_iter), int(check_every),
-                     L.SLA_FIXED_ITERS if fixed else 0,
+            residual_history: torch.Tensor | None = None, jacobi: bool = False) -> SlaCgOpts:
+    flags = (L.SLA_FIXED_ITERS if fixed else 0) | (L.SLA_JACOBI if jacobi else 0)
+    return SlaCgOpts(float(rtol), float(atol), int(max_iter), int(check_every), flags,
                      residual_history.data_ptr() if residual_history is not None else None)
 
 
@@ -305,8 +305,8 @@ class SparseTensor:
         return _MatvecFn.apply(self, self.vals, x)
 
     def solve(self, b: torch.Tensor, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False,
-              check: bool = False) -> torch.Tensor:
-        kw = dict(rtol=rtol, atol=atol, max_iter=max_iter, fixed=fixed)
+              check: bool = False, jacobi: bool = False) -> torch.Tensor:
+        kw = dict(rtol=rtol, atol=atol, max_iter=max_iter, fixed=fixed, jacobi=jacobi)
         x = _SolveFn.apply(self, self.vals, b, kw)
         if check:
             for i, s in enumerate(read_info(self.last_info)):

@@ -68,8 +68,8 @@ typedef enum {
 enum {
     SLA_CONVERGED = 0,   /* |r_k| <= max(rtol |rhs|, atol) with r_k the recurrence residual */
     SLA_MAX_ITER = 1,    /* iteration budget reached (always the outcome with SLA_FIXED_ITERS) */
-    SLA_NOT_SPD = 2,     /* p^T A p <= 0: A is not symmetric positive definite */
-    SLA_NAN = 3          /* p^T A p is NaN */
+    SLA_NOT_SPD = 2,     /* p^T A p <= 0 (or, with SLA_JACOBI, a diagonal entry <= 0 or missing) */
+    SLA_NAN = 3          /* p^T A p is NaN (or, with SLA_JACOBI, a NaN diagonal entry) */
 };
 
 /* sla_csr_create flags */
@@ -78,6 +78,17 @@ enum {
 
 /* sla_cg_opts.flags */
 #define SLA_FIXED_ITERS      1u  /* skip the residual test: run exactly max_iter iterations */
+/*
+ * Jacobi-preconditioned CG, M = diag(A) (paperpeel page, section 4.1, Table 3: the
+ * pages' CG runs with a Jacobi preconditioner).  Per iteration z = M^{-1} r (a
+ * division by the stored diagonal entry), rho = <r, z>, p = z + beta p; the stop test
+ * stays |r| <= max(rtol |rhs|, atol) on the recurrence residual, and
+ * residual_history still records |r_k|.  A missing or non-positive diagonal entry
+ * stops the system with SLA_NOT_SPD before the first iteration, a NaN one with
+ * SLA_NAN (a zero right-hand side stops first, converged).  The adjoint solve uses
+ * the same preconditioner (A^T has the same diagonal).
+ */
+#define SLA_JACOBI           2u
 
 typedef struct sla_csr sla_csr;   /* opaque handle: one sparsity pattern */
 
@@ -86,7 +97,7 @@ typedef struct {
     double atol;                 /* absolute tolerance on |r| (>= 0) */
     int64_t max_iter;            /* iteration budget (>= 0) */
     int32_t check_every;         /* iterations between host polls of the stop counter (0 = default 32) */
-    uint32_t flags;              /* SLA_FIXED_ITERS */
+    uint32_t flags;              /* SLA_FIXED_ITERS | SLA_JACOBI */
     double* residual_history;    /* device, nullable: [batch][max_iter + 1], entry k = |r_k| */
 } sla_cg_opts;
 
