@@ -11,7 +11,12 @@ Adjoint Solvers and Sparse Tensor Parallelism for PyTorch):
   * ``spmv``              y = A x (paperpeel page, section 3.3: SpMV).
   * ``cg``                unpreconditioned Hestenes-Stiefel CG, x0 = 0
                           (paperpeel section 1; section 3.3 "Distributed Krylov
-                          solvers" for the two inner products per iteration).
+                          solvers" for the two inner products per iteration), or
+                          with ``jacobi=True`` Jacobi-preconditioned CG (section
+                          4.1, Table 3).
+  * ``bicgstab``          van der Vorst's BiCGStab, x0 = 0, shadow residual b
+                          (paperpeel sections 1 and 3.1: the nonsymmetric solver of
+                          the iterative backends).
   * ``solve_backward``    A^T lambda = dL/dx, dL/db = lambda,
                           dL/dA_ij = -lambda_i x_j on the pattern (gist.science
                           Hindi / Japanese summaries, Methodology item 2,
@@ -29,7 +34,8 @@ import numpy as np
 
 from . import build as _build
 
-CONVERGED, MAX_ITER, NOT_SPD, NAN = 0, 1, 2, 3
+CONVERGED, MAX_ITER, NOT_SPD, NAN, BREAKDOWN = 0, 1, 2, 3, 4
+METHODS = {"cg": 0, "jacobi": 1, "bicgstab": 2}
 _lib = None
 
 
@@ -53,6 +59,8 @@ def lib():
         L.orc_cg.restype = i32
         L.orc_pcg_jacobi.argtypes = [i64, P, P, P, P, P, f64, f64, i64, i32, P, P, P, P, P]
         L.orc_pcg_jacobi.restype = i32
+        L.orc_bicgstab.argtypes = [i64, P, P, P, P, P, f64, f64, i64, i32, P, P, P, P, P]
+        L.orc_bicgstab.restype = i32
         L.orc_transpose.argtypes = [i64, i64, P, P, P, P, P]
         L.orc_transpose.restype = None
         L.orc_pattern_outer.argtypes = [i64, P, P, f64, P, P, P]
@@ -102,9 +110,10 @@ def dot(a, b) -> float:
 
 
 def cg(A, b, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, vals=None, history=False,
-       jacobi=False):
+       jacobi=False, method=None):
     """Returns dict(x, iterations, state, res_norm, rhs_norm[, history]).  jacobi: the
-    Jacobi-preconditioned variant (orc_pcg_jacobi)."""
+    Jacobi-preconditioned variant (orc_pcg_jacobi); method="bicgstab": orc_bicgstab."""
+    method = method or ("jacobi" if jacobi else "cg")
     rp, col = _pattern(A)
     v = _f64(A.vals if vals is None else vals)
     b = _f64(b)
@@ -113,7 +122,7 @@ def cg(A, b, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, vals=None, hist
     work = np.empty(5 * max(n, 1), np.float64)
     it, res, rhs = C.c_int64(0), C.c_double(0), C.c_double(0)
     hist = np.full(max_iter + 1, np.nan) if history else None
-    fn = lib().orc_pcg_jacobi if jacobi else lib().orc_cg
+    fn = {"cg": lib().orc_cg, "jacobi": lib().orc_pcg_jacobi, "bicgstab": lib().orc_bicgstab}[method]
     st = fn(n, _p(rp), _p(col), _p(v), _p(b), _p(x), rtol, atol, max_iter,
                       1 if fixed else 0, _p(work), C.byref(it), C.byref(res), C.byref(rhs),
                       _p(hist) if history else None)
@@ -122,6 +131,11 @@ def cg(A, b, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, vals=None, hist
     if history:
         out["history"] = hist[: it.value + 1].copy()
     return out
+
+
+def bicgstab(A, b, **kw):
+    """BiCGStab (orc_bicgstab); same arguments and result as :func:`cg`."""
+    return cg(A, b, method="bicgstab", **kw)
 
 
 def transpose(A):
@@ -144,8 +158,10 @@ def pattern_outer(A, u, v, sign=1.0) -> np.ndarray:
 
 
 def solve_backward(A, x, g, symmetric=True, rtol=1e-10, atol=0.0, max_iter=100000,
-                   fixed=False, vals=None, jacobi=False):
-    """Returns dict(lam (= dL/db), gvals (= dL/dvals), iterations, state, res_norm, rhs_norm)."""
+                   fixed=False, vals=None, jacobi=False, method=None):
+    """Returns dict(lam (= dL/db), gvals (= dL/dvals), iterations, state, res_norm, rhs_norm).
+    The adjoint solve uses the forward's method: "cg", "jacobi" or "bicgstab"."""
+    method = method or ("jacobi" if jacobi else "cg")
     rp, col = _pattern(A)
     v = _f64(A.vals if vals is None else vals)
     x, g = _f64(x), _f64(g)
@@ -156,7 +172,7 @@ def solve_backward(A, x, g, symmetric=True, rtol=1e-10, atol=0.0, max_iter=10000
     it, res, rhs = C.c_int64(0), C.c_double(0), C.c_double(0)
     st = lib().orc_solve_backward(n, _p(rp), _p(col), _p(v), 1 if symmetric else 0, _p(x),
                                   _p(g), rtol, atol, max_iter, 1 if fixed else 0,
-                                  1 if jacobi else 0, _p(lam),
+                                  METHODS[method], _p(lam),
                                   _p(gv), _p(work), C.byref(it), C.byref(res), C.byref(rhs))
     return dict(lam=lam, gvals=gv, iterations=int(it.value), state=int(st),
                 res_norm=float(res.value), rhs_norm=float(rhs.value))

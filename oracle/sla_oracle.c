@@ -25,11 +25,15 @@
  *     ("Adjoint Differentiation Framework"), linear-systems bullet.
  *     dL/db = lambda follows from x = A^{-1} b (implicit function theorem,
  *     paperpeel section 3.2 "Adjoint Differentiation Framework").
+ *   - BiCGStab (van der Vorst, 1992) for nonsymmetric systems, the pages' second
+ *     iterative method (paperpeel section 1; section 3.1 "Five backends and
+ *     auto-dispatch"), with the same adjoint on A^T.
  *   - Stopping tests, breakdown and iteration counting are not printed on the
  *     pages; the readings used here are listed with the parity tests.
  *
- * Parity pins (see tests/test_oracle_pins.py): dense LU solves on small grids,
- * the closed-form eigenpairs of the 5-point Laplacian, manufactured solutions,
+ * Parity pins (tests/test_oracle_pins.py, tests/test_oracle_bicgstab.py): dense LU
+ * solves on small grids, the closed-form eigenpairs of the 5-point Laplacian,
+ * manufactured solutions,
  * one-iteration convergence on an eigenvector, homogeneity invariants of the
  * gradients, central finite differences, scipy.sparse products and transposes,
  * and exact rational solutions of a 2 x 2 grid (tests/golden).
@@ -40,7 +44,7 @@
 #include <string.h>
 
 /* Per-system outcome codes; the HIP library uses the same numbers. */
-enum { ORC_CONVERGED = 0, ORC_MAX_ITER = 1, ORC_NOT_SPD = 2, ORC_NAN = 3 };
+enum { ORC_CONVERGED = 0, ORC_MAX_ITER = 1, ORC_NOT_SPD = 2, ORC_NAN = 3, ORC_BREAKDOWN = 4 };
 
 /* y = A x, one row at a time; row i sums val[k] * x[col[k]] for k ascending. */
 void orc_spmv(int64_t n_rows, const int64_t* row_ptr, const int32_t* col,
@@ -244,6 +248,118 @@ done:
 }
 
 /*
+ * BiCGStab (van der Vorst, Bi-CGSTAB: a fast and smoothly converging variant of Bi-CG
+ * for the solution of nonsymmetric linear systems, SIAM J. Sci. Stat. Comput. 13(2),
+ * 1992; cited by the paperpeel page, section 1, and listed there in section 3.1 as
+ * the second iterative method of the scipy, eigen and pytorch-native backends) for
+ * A x = b with x0 = 0, no preconditioner, shadow residual rh = r0 = b:
+ *
+ *   r = b, p = r, rho = <rh, r>, threshold = max(rtol * |b|, atol)
+ *   iteration k = 0, 1, ...:
+ *     stop when |r| <= threshold (recurrence residual), or at the budget
+ *     k > 0:  rho' = <rh, r>;  beta = (rho' / rho) (alpha / omega);
+ *             p = r + beta (p - omega v);  rho = rho'
+ *     v = A p;  alpha = rho / <rh, v>
+ *     s = r - alpha v
+ *     t = A s;  omega = <t, s> / <t, t>
+ *     if |s| <= threshold: x = x + alpha p, stop (converged half-way, k + 1)
+ *     x = x + alpha p + omega s;  r = s - omega t
+ *
+ * The half-way test on s is the customary safeguard (Barrett et al., Templates for
+ * the Solution of Linear Systems, 1994, section 2.3.8): without it an exactly
+ * converged s gives t = 0 and omega = 0 / 0.  t = A s is formed before that test.
+ * The iteration count is the number of products A p.  Breakdowns stop the solve with
+ * x as it was before the failing iteration: <rh, v> = 0 or <t, t> = 0 (BREAKDOWN),
+ * either of them or <t, s> NaN (NAN), and rho' = 0 or omega = 0 at the start of an
+ * iteration (BREAKDOWN: beta would divide by zero).  The tests run in the order
+ * written: residual, budget, then the breakdowns.  With fixed != 0 neither residual
+ * test runs and exactly max_iter iterations are made unless a breakdown stops them.
+ *
+ * work: 5 n doubles (r, p, v, s, t).  hist (nullable, max_iter + 1 entries) receives
+ * |r_k| for k = 0 .. iterations (|s| for a half-way stop).
+ */
+int orc_bicgstab(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
+                 const double* b, double* x, double rtol, double atol, int64_t max_iter,
+                 int fixed, double* work, int64_t* iters_out, double* res_out,
+                 double* rhs_out, double* hist)
+{
+    double* r = work;
+    double* p = work + n;
+    double* v = work + 2 * n;
+    double* s = work + 3 * n;
+    double* t = work + 4 * n;
+    const double* rh = b;
+    for (int64_t i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; p[i] = b[i]; v[i] = 0.0; }
+    double rr = orc_dot(n, r, r);
+    double bnorm = sqrt(rr);
+    double thr = rtol * bnorm;
+    if (atol > thr) thr = atol;
+    *rhs_out = bnorm;
+    double rho = orc_dot(n, rh, r);
+    double alpha = 0.0, omega = 0.0, res = bnorm;
+    int64_t k = 0;
+    int state;
+    for (;;) {
+        res = sqrt(rr);
+        if (hist) hist[k] = res;
+        if (!fixed && res <= thr) { state = ORC_CONVERGED; break; }
+        if (k >= max_iter) { state = ORC_MAX_ITER; break; }
+        if (k > 0) {
+            double rho1 = orc_dot(n, rh, r);
+            if (rho1 == 0.0 || omega == 0.0) { state = ORC_BREAKDOWN; break; }
+            double beta = (rho1 / rho) * (alpha / omega);
+            for (int64_t i = 0; i < n; ++i) {
+                double tv = omega * v[i];
+                double d = p[i] - tv;
+                double tb = beta * d;
+                p[i] = r[i] + tb;
+            }
+            rho = rho1;
+        }
+        orc_spmv(n, row_ptr, col, val, p, v);
+        double rv = orc_dot(n, rh, v);
+        if (rv != rv) { state = ORC_NAN; break; }
+        if (rv == 0.0) { state = ORC_BREAKDOWN; break; }
+        alpha = rho / rv;
+        for (int64_t i = 0; i < n; ++i) {
+            double tv = alpha * v[i];
+            s[i] = r[i] - tv;
+        }
+        double ss = orc_dot(n, s, s);
+        orc_spmv(n, row_ptr, col, val, s, t);
+        double ts = orc_dot(n, t, s);
+        double tt = orc_dot(n, t, t);
+        if (!fixed && sqrt(ss) <= thr) {
+            for (int64_t i = 0; i < n; ++i) {
+                double tp = alpha * p[i];
+                x[i] = x[i] + tp;
+            }
+            k = k + 1;
+            res = sqrt(ss);
+            if (hist) hist[k] = res;
+            state = ORC_CONVERGED;
+            break;
+        }
+        if (tt != tt || ts != ts) { state = ORC_NAN; break; }
+        if (tt == 0.0) { state = ORC_BREAKDOWN; break; }
+        omega = ts / tt;
+        for (int64_t i = 0; i < n; ++i) {
+            double tp = alpha * p[i];
+            double x1 = x[i] + tp;
+            double ts_ = omega * s[i];
+            x[i] = x1 + ts_;
+            double tt_ = omega * t[i];
+            r[i] = s[i] - tt_;
+        }
+        rr = orc_dot(n, r, r);
+        k = k + 1;
+    }
+    *iters_out = k;
+    *res_out = res;
+    return state;
+}
+
+/*
  * Transpose of an n_rows x n_cols CSR pattern by a stable counting sort on the
  * column index.  Row j of A^T lists the entries of column j of A in ascending
  * row order; perm[kT] is the position in A of entry kT of A^T, so
@@ -282,33 +398,36 @@ void orc_pattern_outer(int64_t n_rows, const int64_t* row_ptr, const int32_t* co
 
 /*
  * Adjoint backward pass of x = A^{-1} b for a loss L(x) with g = dL/dx:
- *   solve A^T lambda = g by the same CG (x0 = 0, same rtol / atol / budget,
- *   threshold relative to |g|; Jacobi-preconditioned if jacobi != 0, A^T has the
- *   same diagonal), then dL/db = lambda and dL/dA_ij = -lambda_i x_j on the stored
- *   entries only.
+ *   solve A^T lambda = g by the same method as the forward solve (x0 = 0, same
+ *   rtol / atol / budget, threshold relative to |g|), then dL/db = lambda and
+ *   dL/dA_ij = -lambda_i x_j on the stored entries only.
+ * method: 0 CG, 1 Jacobi-preconditioned CG (A^T has the same diagonal), 2 BiCGStab.
  * symmetric != 0: A^T is A (same arrays).  Otherwise A^T is formed by
  * orc_transpose.  lam and gvals (nullable) are outputs; work: 5 n doubles.
  */
-static int orc_solve_either(int jacobi, int64_t n, const int64_t* row_ptr, const int32_t* col,
+static int orc_solve_method(int method, int64_t n, const int64_t* row_ptr, const int32_t* col,
                             const double* val, const double* b, double* x, double rtol, double atol,
                             int64_t max_iter, int fixed, double* work, int64_t* iters_out,
                             double* res_out, double* rhs_out)
 {
-    if (jacobi)
+    if (method == 1)
         return orc_pcg_jacobi(n, row_ptr, col, val, b, x, rtol, atol, max_iter, fixed, work, iters_out,
                               res_out, rhs_out, NULL);
+    if (method == 2)
+        return orc_bicgstab(n, row_ptr, col, val, b, x, rtol, atol, max_iter, fixed, work, iters_out,
+                            res_out, rhs_out, NULL);
     return orc_cg(n, row_ptr, col, val, b, x, rtol, atol, max_iter, fixed, work, iters_out, res_out,
                   rhs_out, NULL);
 }
 
 int orc_solve_backward(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
                        int symmetric, const double* x, const double* g, double rtol, double atol,
-                       int64_t max_iter, int fixed, int jacobi, double* lam, double* gvals, double* work,
+                       int64_t max_iter, int fixed, int method, double* lam, double* gvals, double* work,
                        int64_t* iters_out, double* res_out, double* rhs_out)
 {
     int state;
     if (symmetric) {
-        state = orc_solve_either(jacobi, n, row_ptr, col, val, g, lam, rtol, atol, max_iter, fixed, work,
+        state = orc_solve_method(method, n, row_ptr, col, val, g, lam, rtol, atol, max_iter, fixed, work,
                                  iters_out, res_out, rhs_out);
     } else {
         int64_t nnz = row_ptr[n];
@@ -318,7 +437,7 @@ int orc_solve_backward(int64_t n, const int64_t* row_ptr, const int32_t* col, co
         double* vt = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
         orc_transpose(n, n, row_ptr, col, rpt, ct, perm);
         for (int64_t k = 0; k < nnz; ++k) vt[k] = val[perm[k]];
-        state = orc_solve_either(jacobi, n, rpt, ct, vt, g, lam, rtol, atol, max_iter, fixed, work,
+        state = orc_solve_method(method, n, rpt, ct, vt, g, lam, rtol, atol, max_iter, fixed, work,
                                  iters_out, res_out, rhs_out);
         free(rpt); free(ct); free(perm); free(vt);
     }

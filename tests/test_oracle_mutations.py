@@ -2,7 +2,8 @@
 
 Each case compiles a copy of oracle/sla_oracle.c with one plausible mistake
 (a dropped term, a wrong sign, a wrong or transposed index) into a temporary
-directory and runs tests/test_oracle_pins.py against it in a subprocess.  CPU
+directory and runs the pins of that part of the oracle (tests/test_oracle_pins.py,
+or tests/test_oracle_bicgstab.py for BiCGStab) against it in a subprocess.  CPU
 only; nothing here touches a GPU or the HIP library.
 """
 import os
@@ -14,6 +15,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "sla_oracle.c")
 
+PINS = "test_oracle_pins.py"
+BICG = "test_oracle_bicgstab.py"
 MUTANTS = {
     "gradient sign": ("gvals[k] = sign * t;", "gvals[k] = -sign * t;"),
     "gradient orientation": ("double t = u[i] * v[col[k]];", "double t = u[col[k]] * v[i];"),
@@ -32,13 +35,26 @@ MUTANTS = {
     "pcg without the preconditioner": ("            z[i] = r[i] / d[i];", "            z[i] = r[i];"),
     "pcg beta from <r,r>": ("double rho1 = orc_dot(n, r, z);", "double rho1 = orc_dot(n, r, r);"),
     "pcg direction from r": ("            p[i] = z[i] + t;", "            p[i] = r[i] + t;"),
+    # BiCGStab: caught by tests/test_oracle_bicgstab.py
+    "bicgstab beta without alpha/omega": ("double beta = (rho1 / rho) * (alpha / omega);",
+                                          "double beta = rho1 / rho;", BICG),
+    "bicgstab direction drops omega v": ("double d = p[i] - tv;", "double d = p[i];", BICG),
+    "bicgstab x update drops omega s": ("x[i] = x1 + ts_;", "x[i] = x1;", BICG),
+    "bicgstab residual sign": ("r[i] = s[i] - tt_;", "r[i] = s[i] + tt_;", BICG),
+    "bicgstab omega from <s,s>": ("omega = ts / tt;", "omega = ts / ss;", BICG),
+    "bicgstab shadow residual follows r": ("double rv = orc_dot(n, rh, v);", "double rv = orc_dot(n, r, v);",
+                                           BICG),
+    "bicgstab half-way stop skips x": ("                x[i] = x[i] + tp;", "                x[i] = x[i];",
+                                       BICG),
+    "bicgstab adjoint without transpose": ("    if (symmetric) {", "    if (symmetric || method == 2) {",
+                                           BICG),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     src = open(SRC).read()
-    a, b = MUTANTS[name]
+    a, b, pins = (MUTANTS[name] + (PINS,))[:3]
     assert a in src, "mutation anchor vanished from the oracle source"
     mut = tmp_path / "mut.c"
     mut.write_text(src.replace(a, b, 1))
@@ -47,6 +63,6 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                            "-o", str(so), "-lm"])
     env = dict(os.environ, SLA_ORACLE_LIB=str(so))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "pins missed the planted mistake: " + name

@@ -22,7 +22,7 @@ import numpy as np
 
 __all__ = [
     "CSR", "poisson5", "poisson5_torch", "varcoef_poisson5", "gaussian_random_field",
-    "fem_p1_batched", "rhs_uniform", "rhs_normal", "config",
+    "fem_p1_batched", "convdiff5", "rhs_uniform", "rhs_normal", "config",
 ]
 
 
@@ -274,6 +274,50 @@ def fem_p1_batched(nv: int = 256, B: int = 256, seed: int = 0, jitter: float = 0
     return csr, b
 
 
+def convdiff5(N: int, wind=100.0, shift: float = 0.0, index64: bool = False) -> CSR:
+    """Nonsymmetric 2-D convection-diffusion matrix: -Lap u + w . grad u on the unit
+    square, N x N interior grid (h = 1 / (N + 1)), homogeneous Dirichlet data, the
+    5-point Laplacian plus first-order upwind convection, scaled by h^2 like
+    :func:`poisson5` (kappa = 1 gives exactly that matrix when w = 0).
+
+    The pages support nonsymmetric systems through BiCGStab but name no nonsymmetric
+    workload; this is the textbook stand-in.  The wind is the recirculating flow
+    w = W (2 Y (1 - X^2), -2 X (1 - Y^2)) with X = 2 x - 1, Y = 2 y - 1, evaluated at
+    each unknown.  Upwinding gives, at unknown P with neighbours S, W, E, N,
+        A_PP = 4 + h (|w_x| + |w_y|),  A_PW = -1 - h max(w_x, 0),
+        A_PE = -1 - h max(-w_x, 0),     A_PS = -1 - h max(w_y, 0),
+        A_PN = -1 - h max(-w_y, 0),
+    an M-matrix (nonsingular, weakly diagonally dominant) whose nonsymmetric part
+    grows with W.  Same pattern and ordering as :func:`poisson5`.  ``wind``: W, or a
+    sequence of W values for a shared-pattern batch (vals [B, nnz]).  ``shift`` adds a
+    reaction term c u (c = shift, on the h^2-scaled diagonal): c >= 1 makes the matrix
+    strictly diagonally dominant and well conditioned (a few tens of iterations).
+    """
+    row_ptr, col, pos_of = _poisson5_pattern_np(N)
+    n = N * N
+    h = 1.0 / (N + 1)
+    idx = np.arange(n, dtype=np.int64)
+    a, c = idx // N, idx % N
+    X = 2.0 * (c + 1) * h - 1.0           # column index c runs along x
+    Y = 2.0 * (a + 1) * h - 1.0           # grid row a runs along y
+    winds = np.atleast_1d(np.asarray(wind, dtype=np.float64))
+    vals = np.empty((winds.shape[0], col.shape[0]), np.float64)
+    for bi, W in enumerate(winds):
+        wx = W * 2.0 * Y * (1.0 - X * X)
+        wy = -W * 2.0 * X * (1.0 - Y * Y)
+        # neighbour order of the pattern: S (i - N), W (i - 1), P, E (i + 1), N (i + N)
+        coef = [-1.0 - h * np.maximum(wy, 0.0), -1.0 - h * np.maximum(wx, 0.0),
+                (4.0 + shift) + h * (np.abs(wx) + np.abs(wy)),
+                -1.0 - h * np.maximum(-wx, 0.0), -1.0 - h * np.maximum(-wy, 0.0)]
+        for k, (m, pos) in enumerate(pos_of):
+            vals[bi, pos] = coef[k][m]
+    if np.ndim(wind) == 0:
+        vals = vals[0]
+    if not index64:
+        row_ptr = row_ptr.astype(np.int32)
+    return CSR(n, n, row_ptr, col, vals)
+
+
 def rhs_uniform(n: int, seed: int = 0, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
     return np.random.default_rng(seed).uniform(lo, hi, n)
 
@@ -301,6 +345,9 @@ def config(name: str, scale: int | None = None) -> dict:
     poisson13000   5-point Poisson on 13000 x 13000 (169M unknowns), int64 row
                    pointer, b ~ N(0, 1) (seed 0); 500 fixed CG iterations forward
                    and 500 in the adjoint, loss 0.5 |x|^2.
+    convdiff1024   nonsymmetric convection-diffusion (:func:`convdiff5`, W = 100) on
+                   1024 x 1024, b ~ N(0, 1) (seed 0), BiCGStab to rtol 1e-8 forward and
+                   on A^T in the adjoint, loss 0.5 |x|^2.
     """
     if name == "poisson64":
         N = scale or 64
@@ -325,6 +372,12 @@ def config(name: str, scale: int | None = None) -> dict:
         A, b = fem_p1_batched(nv=nv, B=B, seed=0)
         return dict(name=name, A=A, b=b, rtol=1e-8, atol=0.0, max_iter=100000,
                     fixed=False, loss="half_sq")
+    if name == "convdiff1024":
+        N = scale or 1024
+        A = convdiff5(N, wind=100.0)
+        return dict(name=name, A=A, b=rhs_normal(N * N, 0), rtol=1e-8, atol=0.0,
+                    max_iter=100000, fixed=False, loss="half_sq", method="bicgstab",
+                    symmetric=False)
     if name == "poisson13000":
         N = scale or 13000
         return dict(name=name, N=N, A=None, b=None, rtol=0.0, atol=0.0, max_iter=500,
