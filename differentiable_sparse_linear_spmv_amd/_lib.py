@@ -14,16 +14,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsla.so")
 
 SLA_OK, SLA_ERR_INVALID_ARG, SLA_ERR_INVALID_CSR, SLA_ERR_UNSUPPORTED, SLA_ERR_OOM, SLA_ERR_HIP = range(6)
-SLA_CONVERGED, SLA_MAX_ITER, SLA_NOT_SPD, SLA_NAN = range(4)
-STATE_NAMES = {0: "CONVERGED", 1: "MAX_ITER", 2: "NOT_SPD", 3: "NAN"}
+SLA_CONVERGED, SLA_MAX_ITER, SLA_NOT_SPD, SLA_NAN, SLA_BREAKDOWN = range(5)
+STATE_NAMES = {0: "CONVERGED", 1: "MAX_ITER", 2: "NOT_SPD", 3: "NAN", 4: "BREAKDOWN"}
 SLA_SYMMETRIC = 1
 SLA_EAGER_TRANSPOSE = 2
 SLA_FIXED_ITERS = 1
 SLA_JACOBI = 2
+SLA_BICGSTAB = 4
 (SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
- SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_GROUP_LAYOUT, SLA_K_COUNT) = range(10)
+ SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_GROUP_LAYOUT, SLA_K_BS_SPMV, SLA_K_BS_VEC,
+ SLA_K_COUNT) = range(12)
 KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "gather_vals",
-                "transpose", "cg_pupd", "group_layout"]
+                "transpose", "cg_pupd", "group_layout", "bs_spmv", "bs_vec"]
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",

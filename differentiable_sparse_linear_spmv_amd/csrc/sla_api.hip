@@ -221,24 +221,30 @@ int blocks_per_system(const sla_csr* A, int64_t ntiles, int64_t batch, int per_c
 }
 
 struct Workspace {
-    double *r, *p0, *p1, *q, *z, *dg, *part_sigma, *part_rho, *part_rr, *part_aux;
+    double *r, *p0, *p1, *q, *z, *dg, *part_sigma, *part_rho, *part_rr, *part_aux, *part_tt;
     SysState* st;
     int32_t* n_active;
 };
 
-// vectors r, p0, p1, q (+ z, dg with Jacobi); partials sigma, rho (+ rr, aux)
-size_t workspace_bytes(int64_t n, int64_t batch, int G, bool jacobi)
+// Solver methods and the workspace each needs.
+enum Method { kMethodCG = 0, kMethodJacobi = 1, kMethodBiCGStab = 2 };
+// vectors r, p0, p1, q (+ z, dg with Jacobi; + z with BiCGStab);
+// partials sigma, rho (+ rr, aux with Jacobi; + rr, aux, tt with BiCGStab)
+constexpr int kWsVectors[3] = {4, 6, 5};
+constexpr int kWsPartials[3] = {2, 4, 5};
+
+size_t workspace_bytes(int64_t n, int64_t batch, int G, int method)
 {
     const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
-    return (jacobi ? 6 : 4) * vec + (jacobi ? 4 : 2) * part + align256(sizeof(SysState) * batch) + 256;
+    return kWsVectors[method] * vec + kWsPartials[method] * part + align256(sizeof(SysState) * batch) + 256;
 }
 
 // G: the larger of the two grids (every partial array gets room for it).
-sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, bool jacobi = false)
+sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int method = kMethodCG)
 {
     const int64_t n = A->n_rows;
-    const size_t need = workspace_bytes(n, batch, G, jacobi);
+    const size_t need = workspace_bytes(n, batch, G, method);
     if (need > A->ws_bytes) {
         if (A->ws) {
             HIP_TRY(hipDeviceSynchronize());
@@ -253,17 +259,20 @@ sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, bool
     char* p = static_cast<char*>(A->ws);
     const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
-    const int nv = jacobi ? 6 : 4, np = jacobi ? 4 : 2;
-    w->r = reinterpret_cast<double*>(p);
-    w->p0 = reinterpret_cast<double*>(p + vec);
-    w->p1 = reinterpret_cast<double*>(p + 2 * vec);
-    w->q = reinterpret_cast<double*>(p + 3 * vec);
-    w->z = jacobi ? reinterpret_cast<double*>(p + 4 * vec) : nullptr;
-    w->dg = jacobi ? reinterpret_cast<double*>(p + 5 * vec) : nullptr;
-    w->part_sigma = reinterpret_cast<double*>(p + nv * vec);
-    w->part_rho = reinterpret_cast<double*>(p + nv * vec + part);
-    w->part_rr = jacobi ? reinterpret_cast<double*>(p + nv * vec + 2 * part) : nullptr;
-    w->part_aux = jacobi ? reinterpret_cast<double*>(p + nv * vec + 3 * part) : nullptr;
+    const int nv = kWsVectors[method], np = kWsPartials[method];
+    auto vec_at = [&](int i) { return i < nv ? reinterpret_cast<double*>(p + i * vec) : nullptr; };
+    auto part_at = [&](int i) { return i < np ? reinterpret_cast<double*>(p + nv * vec + i * part) : nullptr; };
+    w->r = vec_at(0);
+    w->p0 = vec_at(1);
+    w->p1 = vec_at(2);
+    w->q = vec_at(3);
+    w->z = vec_at(4);
+    w->dg = vec_at(5);
+    w->part_sigma = part_at(0);
+    w->part_rho = part_at(1);
+    w->part_rr = part_at(2);
+    w->part_aux = part_at(3);
+    w->part_tt = part_at(4);
     w->st = reinterpret_cast<SysState*>(p + nv * vec + np * part);
     w->n_active = reinterpret_cast<int32_t*>(p + nv * vec + np * part + align256(sizeof(SysState) * batch));
     return SLA_OK;
@@ -276,7 +285,10 @@ sla_status check_opts(const sla_cg_opts* o)
         return fail(SLA_ERR_INVALID_ARG, "rtol and atol must be >= 0 (got %g, %g)", o->rtol, o->atol);
     if (o->max_iter < 0) return fail(SLA_ERR_INVALID_ARG, "max_iter must be >= 0");
     if (o->check_every < 0) return fail(SLA_ERR_INVALID_ARG, "check_every must be >= 0");
-    if (o->flags & ~(SLA_FIXED_ITERS | SLA_JACOBI)) return fail(SLA_ERR_INVALID_ARG, "unknown cg flags 0x%x", o->flags);
+    if (o->flags & ~(SLA_FIXED_ITERS | SLA_JACOBI | SLA_BICGSTAB))
+        return fail(SLA_ERR_INVALID_ARG, "unknown cg flags 0x%x", o->flags);
+    if ((o->flags & SLA_JACOBI) && (o->flags & SLA_BICGSTAB))
+        return fail(SLA_ERR_INVALID_ARG, "SLA_JACOBI and SLA_BICGSTAB cannot be combined");
     return SLA_OK;
 }
 
@@ -506,7 +518,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         if (Gu > ntiles) Gu = Gp;
     }
     Workspace w;
-    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi);
+    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi ? kMethodJacobi : kMethodCG);
     if (st != SLA_OK) return st;
 
     CgArgs a{};
@@ -565,6 +577,78 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         hipError_t e1 = timed(SLA_K_CG_SPMV, s, [&] { return launch_cg_spmv(a, k, rp_bits, cap, s); });
         if (e1 != hipSuccess || k >= a.max_iter) return e1;
         return timed(SLA_K_CG_UPDATE, s, [&] { return launch_cg_update(a, k, s); });
+    };
+    return drive_cg(A, a, w, o, s, step);
+}
+
+// BiCGStab on the pattern (row_ptr, col; LDS variant cap) with values vals: init, then
+// per iteration the p update, v = A p, s, t = A s and the update.  The SpMV grid fills
+// the GPU once as the CG SpMV's does, the streaming kernels take about 16 tiles per
+// workgroup; the polling is run_cg's.
+sla_status run_bicgstab(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t batch,
+                        const double* vals, const double* b, double* x, const sla_cg_opts* o, sla_cg_info* info,
+                        hipStream_t s)
+{
+    const int64_t n = A->n_rows;
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    const int rp_bits = A->krp_bits;   // A and its transpose use the same row-pointer width
+    const int G = blocks_per_system(A, ntiles, batch, bs_blocks_per_cu(rp_bits, cap, n));
+    int Gu = G;
+    if (batch < 8 || batch % 8 != 0) {
+        int64_t g = ((ntiles + 15) / 16 + 7) & ~int64_t(7);
+        Gu = static_cast<int>(std::max<int64_t>(8, std::min<int64_t>(G, g)));
+        if (Gu > ntiles) Gu = G;
+    }
+    Workspace w;
+    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, kMethodBiCGStab);
+    if (st != SLA_OK) return st;
+
+    CgArgs a{};
+    a.row_ptr = row_ptr;
+    a.col = col;
+    a.vals = vals;
+    a.b = b;
+    a.x = x;
+    a.r = w.r;
+    a.p0 = w.p0;   // p
+    a.p1 = w.p1;   // s
+    a.q = w.q;     // v
+    a.z = w.z;     // t
+    a.part_sigma = w.part_sigma;
+    a.part_rho = w.part_rho;
+    a.part_rr = w.part_rr;
+    a.part_aux = w.part_aux;
+    a.part_tt = w.part_tt;
+    a.st = w.st;
+    a.info = info;
+    a.hist = o->residual_history;
+    a.n_active = w.n_active;
+    a.n = n;
+    a.nnz = A->nnz;
+    a.ntiles = ntiles;
+    a.max_iter = o->max_iter;
+    a.rtol = o->rtol;
+    a.atol = o->atol;
+    a.fixed = (o->flags & SLA_FIXED_ITERS) ? 1 : 0;
+    a.G = G;
+    a.Gu = Gu;
+    a.batch = static_cast<int32_t>(batch);
+    a.xcd_remap = 1;
+    a.sys_per_xcd = (batch >= 8 && batch % 8 == 0) ? 1 : 0;
+    a.split = 1;
+
+    hipError_t e = timed(SLA_K_BS_VEC, s, [&] { return launch_bs(0, a, 0, rp_bits, cap, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "bicgstab init launch: %s", hipGetErrorString(e));
+    auto step = [&](int64_t k) -> hipError_t {
+        hipError_t e0 = timed(SLA_K_BS_VEC, s, [&] { return launch_bs(1, a, k, rp_bits, cap, s); });
+        if (e0 != hipSuccess || k >= a.max_iter) return e0;
+        static const int kOrder[4] = {2, 3, 4, 5};
+        for (int which : kOrder) {
+            const int kid = (which == 2 || which == 4) ? SLA_K_BS_SPMV : SLA_K_BS_VEC;
+            e0 = timed(kid, s, [&] { return launch_bs(which, a, k, rp_bits, cap, s); });
+            if (e0 != hipSuccess) return e0;
+        }
+        return hipSuccess;
     };
     return drive_cg(A, a, w, o, s, step);
 }
@@ -835,8 +919,11 @@ sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, con
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
-    st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_b, d_x, opts, d_info,
-                s);
+    if (opts->flags & SLA_BICGSTAB)
+        st = run_bicgstab(A, A->krp, A->col, A->cap, batch, d_vals, d_b, d_x, opts, d_info, s);
+    else
+        st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_b, d_x, opts,
+                    d_info, s);
     if (st == SLA_OK && !(opts->flags & SLA_FIXED_ITERS)) {
         hipError_t e = timing_collect();
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
@@ -857,14 +944,18 @@ sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
+    const bool bicg = (opts->flags & SLA_BICGSTAB) != 0;
     if (A->flags & SLA_SYMMETRIC) {
-        st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_gx, d_gb, opts,
-                    d_info, s);
+        st = bicg ? run_bicgstab(A, A->krp, A->col, A->cap, batch, d_vals, d_gx, d_gb, opts, d_info, s)
+                  : run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_gx, d_gb,
+                           opts, d_info, s);
     } else {
         if ((st = ensure_transpose(A, s)) != SLA_OK) return st;
         const double* vt = nullptr;
         if ((st = ensure_vals_t(A, batch, d_vals, s, &vt)) != SLA_OK) return st;
-        st = run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, 0, 0, A->split, batch, vt, d_gx, d_gb, opts, d_info, s);
+        st = bicg ? run_bicgstab(A, A->row_ptr_t, A->col_t, A->cap_t, batch, vt, d_gx, d_gb, opts, d_info, s)
+                  : run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, 0, 0, A->split, batch, vt, d_gx, d_gb, opts,
+                           d_info, s);
     }
     if (st != SLA_OK) return st;
     if (d_gvals) {

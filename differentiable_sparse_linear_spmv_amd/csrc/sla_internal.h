@@ -46,18 +46,20 @@ constexpr int kGroupMinBatch = 8;
 constexpr int kGCapSmall = 512;
 constexpr int kGCapLarge = 1024;
 
-// Per-system CG state in device memory (64 bytes).  Double-buffered by the
+// Per-system solver state in device memory (80 bytes).  Double-buffered by the
 // parity of the iteration index so that a kernel reads the previous value while
 // its first workgroup writes the new one.
 struct SysState {
     int64_t stop_iter;   // INT64_MAX while running; else the iteration at which it stopped
-    double rho[2];       // rho_k = r_k^T r_k (with Jacobi r_k^T z_k), slot k & 1
+                         // (BiCGStab: the phase 5 k + position of the kernel that stopped it)
+    double rho[2];       // rho_k = r_k^T r_k (Jacobi r_k^T z_k, BiCGStab rh^T r_k), slot k & 1
     double alpha[2];     // alpha_k, slot k & 1
     double thr;          // stop threshold max(rtol |rhs|, atol)
     double rhs;          // |rhs|
-    double rr;           // Jacobi: |r_k|^2 of the last step (rho holds r^T z)
+    double rr;           // Jacobi, BiCGStab: |r_k|^2 of the last step (rho holds another product)
+    double omega[2];     // BiCGStab: omega_k, slot k & 1
 };
-static_assert(sizeof(SysState) == 64, "SysState layout");
+static_assert(sizeof(SysState) == 80, "SysState layout");
 
 // Arguments of the fused CG kernels (passed by value).
 struct CgArgs {
@@ -73,7 +75,8 @@ struct CgArgs {
     double* part_sigma;      // [batch][G]   written by k_cg_spmv
     double* part_rho;        // [batch][Gu]  written by k_cg_init / k_cg_update (rho_k partials)
     double* part_rr;         // [batch][Gu]  Jacobi: r^T r partials (the stop test)
-    double* part_aux;        // [batch][Gu]  Jacobi: bad-diagonal flags of k_cg_init
+    double* part_aux;        // [batch][Gu]  Jacobi: bad-diagonal flags of k_cg_init; BiCGStab: s^T s
+    double* part_tt;         // [batch][G]   BiCGStab: t^T t (t = A s), written by the SpMV
     double* z;               // [batch][n]   Jacobi: z_k = M^{-1} r_k
     double* dg;              // [batch][n]   Jacobi: the diagonal of A
     SysState* st;            // [batch]
@@ -127,6 +130,10 @@ hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s);   // split
 // (which: 0 init, 1 p update, 2 SpMV, 3 update, 4 x back to the caller's layout).
 hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, hipStream_t s);
 hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s);
+// BiCGStab (which: 0 init, 1 p update, 2 v = A p, 3 s, 4 t = A s, 5 update).  Vectors:
+// r in a.r, p in a.p0, v in a.q, s in a.p1, t in a.z; rh = b.
+hipError_t launch_bs(int which, const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s);
+int bs_blocks_per_cu(int rp_bits, int cap, int64_t n);   // the BiCGStab SpMV (t = A s variant)
 
 hipError_t launch_matvec(const void* row_ptr, int rp_bits, const int32_t* col, const double* vals,
                          const double* x, double* y, int64_t n_rows, int64_t nnz, int64_t n_cols,

@@ -418,6 +418,20 @@ constexpr int kStepRun = 0;
 constexpr int kStepStopped = 1;
 constexpr int kStepStopNow = 2;
 
+// Variants of the staged SpMV kernel k_cg_spmv.
+constexpr int kSpmvFused = 0;   // CG, p_k formed on the fly, deferred x update
+constexpr int kSpmvSplit = 1;   // CG, split schedule: p_k read as formed
+constexpr int kSpmvBsV = 2;     // BiCGStab: v = A p, partial <rh, v>
+constexpr int kSpmvBsT = 3;     // BiCGStab: t = A s, partials <t, s>, <t, t>
+
+// BiCGStab's kernels of iteration k run in the order p update, v = A p, s, t = A s,
+// update; the stop word of a system holds the phase (5 k + position) of the kernel
+// that stopped it.  A kernel returns at once if the word is below its own phase; the
+// workgroups of the deciding kernel, which may read the word their leader just wrote,
+// see it equal to their phase and take the same decision again.
+constexpr int kPhaseP = 0, kPhaseV = 1, kPhaseS = 2, kPhaseT = 3, kPhaseU = 4;
+__device__ __forceinline__ int64_t bs_phase(int64_t k, int pos) { return 5 * k + pos; }
+
 // The vector p_k is formed from: r_k (r_0 = b, never copied) or, with Jacobi, z_k.
 __device__ __forceinline__ const double* gathered_r(const CgArgs& a, bool first)
 {
@@ -542,13 +556,16 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
 // The first tile is staged before the stop check and the reduction of the rho
 // partials, which overlaps the kernel's start-up latency with useful loads.
 //
-// SPLIT: the split schedule for unstructured patterns.  k_cg_pupd has already taken
-// the step's decisions and formed p_k (and the x update); this kernel gathers p_k
-// alone, one load per stored entry instead of two (r_k and p_{k-1}), and computes q
-// and the partial p^T q.  The row sums are the same to the last bit.
-template <typename RP, int CAP, bool OFF32, bool SPLIT>
+// MODE kSpmvSplit: the split schedule for unstructured patterns.  k_cg_pupd has
+// already taken the step's decisions and formed p_k (and the x update); this kernel
+// gathers p_k alone, one load per stored entry instead of two (r_k and p_{k-1}), and
+// computes q and the partial p^T q.  The row sums are the same to the last bit.
+// MODE kSpmvBsV / kSpmvBsT: the two products of a BiCGStab iteration, v = A p with
+// the partial <rh, v> (rh = b), and t = A s with the partials <t, s> and <t, t>.
+template <typename RP, int CAP, bool OFF32, int MODE>
 __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
 {
+    constexpr bool SPLIT = MODE != kSpmvFused;
     constexpr int U = CAP / kBlock;
     constexpr int RC = row_chunk(CAP);
     __shared__ double s_val[CAP];
@@ -575,6 +592,12 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     const double* __restrict__ pprev = ((k & 1) ? a.p0 : a.p1) + off;   // p_{k-1}
     double* __restrict__ pcur = ((k & 1) ? a.p1 : a.p0) + off;          // p_k
     double* __restrict__ x = a.x + off;
+    // split modes: the gathered operand, the vector dotted with the product at each
+    // row (read with the row's staged data), and the product's destination
+    const double* __restrict__ opnd =
+        MODE == kSpmvBsV ? a.p0 + off : (MODE == kSpmvBsT ? a.p1 + off : pcur);   // p, s (BiCGStab)
+    const double* __restrict__ partner = MODE == kSpmvBsV ? a.b + off : opnd;     // rh = b, or the operand
+    double* __restrict__ out = (MODE == kSpmvBsT ? a.z : a.q) + off;              // q or v, t (BiCGStab)
 
     int64_t t = tr.first;
     int64_t k0 = 0, k1 = 0, k0n = 0, k1n = 0;
@@ -584,7 +607,8 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     if (t < ntiles) {
         k0 = tile_k0(t);
         k1 = tile_k1(t);
-        stage_tile<RP, CAP, OFF32, SPLIT>(SA, rp, col, vals, SPLIT ? pcur : rin, pprev, x, tile_of(t), n, k0, k1);
+        stage_tile<RP, CAP, OFF32, SPLIT>(SA, rp, col, vals, SPLIT ? partner : rin, pprev, x, tile_of(t), n, k0,
+                                          k1);
     }
     if (t + Gs < ntiles) {
         k0n = tile_k0(t + Gs);
@@ -592,11 +616,16 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     }
 
     double beta = 0.0, alpha_prev = 0.0;
-    if constexpr (SPLIT) {
+    if constexpr (MODE == kSpmvSplit) {
         // k_cg_pupd of this step wrote stop_iter = k if the system stops here
         if (tid == 0) s_stop = a.st[sys].stop_iter;
         __syncthreads();
         if (s_stop <= k) return;
+    } else if constexpr (SPLIT) {
+        // BiCGStab: stopped by a kernel of an earlier phase of the iteration sequence
+        if (tid == 0) s_stop = a.st[sys].stop_iter;
+        __syncthreads();
+        if (s_stop < bs_phase(k, MODE == kSpmvBsV ? kPhaseV : kPhaseT)) return;
     } else {
     const int run = cg_step_begin(a, sys, lb, k, s_red, &s_stop, beta, alpha_prev);
     if (run == kStepStopped) return;
@@ -619,9 +648,9 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     // the gathered operand: p_k formed on the fly, or (SPLIT) read as formed
     using Gather = std::conditional_t<SPLIT, GatherX<OFF32>, GatherCG<OFF32>>;
     Gather g;
-    if constexpr (SPLIT) g = GatherX<OFF32>{pcur};
+    if constexpr (SPLIT) g = GatherX<OFF32>{opnd};
     else g = GatherCG<OFF32>{rin, pprev, beta};
-    double sig = 0.0;
+    double sig = 0.0, tt2 = 0.0;
     // Process tile t from stage `cur` while staging the next tile into `nxt`.
     auto process = [&](TileStage<RP, U>& cur, TileStage<RP, U>& nxt) {
         const int64_t tn = t + Gs;
@@ -659,7 +688,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
                 pv[u] = g(c);
             }
             if (tn < ntiles)
-                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? pcur : rin, pprev, x, tile_of(tn), n,
+                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
                                                   k0n, k1n);
 #pragma unroll
             for (int u = 0; u < RC; ++u) {
@@ -689,14 +718,18 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         } else {
             s = tile_rowsum_long(rp, col, vals, row0, nr, g, s_val);
             if (tn < ntiles)
-                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? pcur : rin, pprev, x, tile_of(tn), n,
+                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
                                                   k0n, k1n);
         }
         if (tid < nr) {
             if constexpr (SPLIT) {
-                q[i] = s;
-                const double u = ri * s;          // ri holds p_k here
+                out[i] = s;
+                const double u = ri * s;          // ri holds the partner's row: p_k, rh or s
                 sig = sig + u;
+                if constexpr (MODE == kSpmvBsT) {
+                    const double w = s * s;
+                    tt2 = tt2 + w;
+                }
             } else {
                 const double tp = beta * ppi;
                 const double pi = ri + tp;           // same expression as the gathered p_k
@@ -721,7 +754,11 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         process(SB, SA);
     }
     sig = block_sum(sig, s_red);
-    if (tid == 0) a.part_sigma[static_cast<int64_t>(sys) * a.G + lb] = sig;
+    if constexpr (MODE == kSpmvBsT) tt2 = block_sum(tt2, s_red);
+    if (tid == 0) {
+        a.part_sigma[static_cast<int64_t>(sys) * a.G + lb] = sig;
+        if constexpr (MODE == kSpmvBsT) a.part_tt[static_cast<int64_t>(sys) * a.G + lb] = tt2;
+    }
 }
 
 // ----------------------------------------------------------------------------------
@@ -1305,6 +1342,301 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
         }
     } else {
         if (tid == 0) a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+    }
+}
+
+// ----------------------------------------------------------------------------------
+// BiCGStab (van der Vorst, 1992), the pages' iterative method for nonsymmetric systems
+// (paperpeel page, section 1; section 3.1 "Five backends and auto-dispatch").  x0 = 0,
+// shadow residual rh = r0 = b.  Iteration k runs five kernels: the stop tests and the
+// direction p = r + beta (p - omega v) (k_bs_pupd), v = A p with <rh, v>
+// (k_cg_spmv<..., kSpmvBsV>), alpha and s = r - alpha v with <s, s> (k_bs_s), t = A s
+// with <t, s> and <t, t> (k_cg_spmv<..., kSpmvBsT>), then omega, x and r (k_bs_update).
+// Grids, partial slots and the deterministic reductions are those of the CG kernels;
+// scalars and stop decisions stay in device memory.  Every elementwise step rounds
+// each product before the sum, in the order written.
+// ----------------------------------------------------------------------------------
+
+// Stop system sys from the leading thread of its workgroup 0: stop word = the deciding
+// kernel's phase, the info record, one less running system.
+__device__ __forceinline__ void bs_stop(const CgArgs& a, int sys, int64_t phase, int64_t iters, double res,
+                                        int state)
+{
+    SysState* st = a.st + sys;
+    st->stop_iter = phase;
+    sla_cg_info inf;
+    inf.iterations = iters;
+    inf.res_norm = res;
+    inf.rhs_norm = st->rhs;
+    inf.state = state;
+    inf.reserved = 0;
+    a.info[sys] = inf;
+    atomicSub(a.n_active, 1);
+}
+
+// x = 0, r = b, p = b, and the partials of <rh, r0> = <r0, r0> = <b, b>.
+__global__ __launch_bounds__(kBlock) void k_bs_init(CgArgs a)
+{
+    __shared__ double s_red[kBlock / 64];
+    const BlockCoord bc = block_coord(a, a.Gu);
+    const int sys = bc.sys;
+    const int tid = threadIdx.x;
+    const TileRange tr = bc.tr;
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t n = a.n;
+    const double* __restrict__ b = a.b + off;
+    double* __restrict__ x = a.x + off;
+    double* __restrict__ r = a.r + off;
+    double* __restrict__ p = a.p0 + off;
+    double bb = 0.0;
+#pragma unroll 1
+    for (int64_t m0 = tr.first; m0 < tr.len; m0 += kStreamUnroll * tr.step) {
+        double bv[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u)
+            bv[u] = b[min((tr.lo + m0 + u * tr.step) * kTile + tid, n - 1)];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t m = m0 + u * tr.step;
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (m < tr.len && i < n) {
+                x[i] = 0.0;
+                r[i] = bv[u];
+                p[i] = bv[u];
+                const double w = bv[u] * bv[u];
+                bb = bb + w;
+            }
+        }
+    }
+    bb = block_sum(bb, s_red);
+    if (tid == 0) {
+        a.part_rho[static_cast<int64_t>(sys) * a.Gu + bc.lb] = bb;
+        a.part_rr[static_cast<int64_t>(sys) * a.Gu + bc.lb] = bb;
+        if (bc.lb == 0) a.st[sys].stop_iter = INT64_MAX;
+        if (bc.lb == 0 && sys == 0) *a.n_active = a.batch;
+    }
+}
+
+// Start of iteration k: |r_k| and rho_k = <rh, r_k> from the partials, the stop tests
+// (residual, budget, then the breakdowns rho_k = 0 or omega_{k-1} = 0), and for k > 0
+// the direction p_k = r_k + beta (p_{k-1} - omega_{k-1} v_{k-1}) with
+// beta = (rho_k / rho_{k-1}) (alpha_{k-1} / omega_{k-1}).  p_0 = b needs no pass.
+__global__ __launch_bounds__(kBlock) void k_bs_pupd(CgArgs a, int64_t k)
+{
+    __shared__ double s_red[kBlock / 64];
+    __shared__ int64_t s_stop;
+    const BlockCoord bc = block_coord(a, a.Gu);
+    const int sys = bc.sys;
+    const int tid = threadIdx.x;
+    const TileRange tr = bc.tr;
+    SysState* st = a.st + sys;
+    const bool lead = (bc.lb == 0 && tid == 0);
+    const bool first = (k == 0);
+    const int64_t phase = bs_phase(k, kPhaseP);
+    if (tid == 0) s_stop = st->stop_iter;
+    const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
+    const double rr_k = reduce_partials(a.part_rr + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
+    if (s_stop < phase) return;
+    const double res = sqrt(rr_k);
+    double thr;
+    if (first) {
+        thr = a.rtol * res;
+        if (a.atol > thr) thr = a.atol;
+    } else {
+        thr = st->thr;
+    }
+    if (lead) {
+        if (first) {
+            st->rhs = res;
+            st->thr = thr;
+        }
+        if (a.hist) a.hist[static_cast<int64_t>(sys) * (a.max_iter + 1) + k] = res;
+    }
+    const double omega = first ? 0.0 : st->omega[(k - 1) & 1];
+    int code = -1;
+    if (!a.fixed && res <= thr) code = SLA_CONVERGED;
+    else if (k >= a.max_iter) code = SLA_MAX_ITER;
+    else if (!first && (rho_k == 0.0 || omega == 0.0)) code = SLA_BREAKDOWN;
+    if (code >= 0) {
+        if (lead) bs_stop(a, sys, phase, k, res, code);
+        return;
+    }
+    if (lead) {
+        st->rho[k & 1] = rho_k;
+        st->rr = rr_k;
+    }
+    if (first) return;
+    const double q1 = rho_k / st->rho[(k - 1) & 1];
+    const double q2 = st->alpha[(k - 1) & 1] / omega;
+    const double beta = q1 * q2;
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t n = a.n;
+    const double* __restrict__ r = a.r + off;
+    const double* __restrict__ v = a.q + off;
+    double* __restrict__ p = a.p0 + off;
+#pragma unroll 1
+    for (int64_t m0 = tr.first; m0 < tr.len; m0 += kStreamUnroll * tr.step) {
+        double rv[kStreamUnroll], pv[kStreamUnroll], vv[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t i = min((tr.lo + m0 + u * tr.step) * kTile + tid, n - 1);
+            rv[u] = r[i];
+            pv[u] = p[i];
+            vv[u] = v[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t m = m0 + u * tr.step;
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (m < tr.len && i < n) {
+                const double tv = omega * vv[u];
+                const double d = pv[u] - tv;
+                const double tb = beta * d;
+                p[i] = rv[u] + tb;
+            }
+        }
+    }
+}
+
+// alpha_k = rho_k / <rh, v> (zero: BREAKDOWN, NaN: NAN), s = r - alpha v, partial <s, s>.
+__global__ __launch_bounds__(kBlock) void k_bs_s(CgArgs a, int64_t k)
+{
+    __shared__ double s_red[kBlock / 64];
+    __shared__ int64_t s_stop;
+    const BlockCoord bc = block_coord(a, a.Gu);
+    const int sys = bc.sys;
+    const int tid = threadIdx.x;
+    const TileRange tr = bc.tr;
+    SysState* st = a.st + sys;
+    const bool lead = (bc.lb == 0 && tid == 0);
+    const int64_t phase = bs_phase(k, kPhaseS);
+    if (tid == 0) s_stop = st->stop_iter;
+    const double d = reduce_partials(a.part_sigma + static_cast<int64_t>(sys) * a.G, a.G, s_red);
+    if (s_stop < phase) return;
+    if (d != d || d == 0.0) {
+        if (lead) bs_stop(a, sys, phase, k, sqrt(st->rr), d != d ? SLA_NAN : SLA_BREAKDOWN);
+        return;
+    }
+    const double alpha = st->rho[k & 1] / d;
+    if (lead) st->alpha[k & 1] = alpha;
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t n = a.n;
+    const double* __restrict__ r = a.r + off;
+    const double* __restrict__ v = a.q + off;
+    double* __restrict__ sv = a.p1 + off;
+    double ss = 0.0;
+#pragma unroll 1
+    for (int64_t m0 = tr.first; m0 < tr.len; m0 += kStreamUnroll * tr.step) {
+        double rv[kStreamUnroll], vv[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t i = min((tr.lo + m0 + u * tr.step) * kTile + tid, n - 1);
+            rv[u] = r[i];
+            vv[u] = v[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t m = m0 + u * tr.step;
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (m < tr.len && i < n) {
+                const double tv = alpha * vv[u];
+                const double si = rv[u] - tv;
+                sv[i] = si;
+                const double w = si * si;
+                ss = ss + w;
+            }
+        }
+    }
+    ss = block_sum(ss, s_red);
+    if (tid == 0) a.part_aux[static_cast<int64_t>(sys) * a.Gu + bc.lb] = ss;
+}
+
+// End of iteration k.  |s| <= threshold: x += alpha p and stop (converged half-way,
+// k + 1 iterations).  Otherwise omega = <t, s> / <t, t> (NaN: NAN, <t, t> = 0:
+// BREAKDOWN), x = (x + alpha p) + omega s, r = s - omega t, partials <rh, r>, <r, r>.
+__global__ __launch_bounds__(kBlock) void k_bs_update(CgArgs a, int64_t k)
+{
+    __shared__ double s_red[kBlock / 64];
+    __shared__ int64_t s_stop;
+    const BlockCoord bc = block_coord(a, a.Gu);
+    const int sys = bc.sys;
+    const int tid = threadIdx.x;
+    const TileRange tr = bc.tr;
+    SysState* st = a.st + sys;
+    const bool lead = (bc.lb == 0 && tid == 0);
+    const int64_t phase = bs_phase(k, kPhaseU);
+    if (tid == 0) s_stop = st->stop_iter;
+    const double ts = reduce_partials(a.part_sigma + static_cast<int64_t>(sys) * a.G, a.G, s_red);
+    const double tt = reduce_partials(a.part_tt + static_cast<int64_t>(sys) * a.G, a.G, s_red);
+    const double ss = reduce_partials(a.part_aux + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
+    if (s_stop < phase) return;
+    const double alpha = st->alpha[k & 1];
+    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t n = a.n;
+    const double* __restrict__ p = a.p0 + off;
+    const double* __restrict__ sv = a.p1 + off;
+    const double* __restrict__ t = a.z + off;
+    const double* __restrict__ rh = a.b + off;
+    double* __restrict__ x = a.x + off;
+    double* __restrict__ r = a.r + off;
+    const double sres = sqrt(ss);
+    if (!a.fixed && sres <= st->thr) {
+        for (int64_t m = tr.first; m < tr.len; m += tr.step) {
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (i < n) {
+                const double tp = alpha * p[i];
+                x[i] = x[i] + tp;
+            }
+        }
+        if (lead) {
+            if (a.hist) a.hist[static_cast<int64_t>(sys) * (a.max_iter + 1) + k + 1] = sres;
+            bs_stop(a, sys, phase, k + 1, sres, SLA_CONVERGED);
+        }
+        return;
+    }
+    if (tt != tt || ts != ts || tt == 0.0) {
+        if (lead) bs_stop(a, sys, phase, k, sqrt(st->rr), tt == 0.0 ? SLA_BREAKDOWN : SLA_NAN);
+        return;
+    }
+    const double omega = ts / tt;
+    if (lead) st->omega[k & 1] = omega;
+    double rho1 = 0.0, rr1 = 0.0;
+#pragma unroll 1
+    for (int64_t m0 = tr.first; m0 < tr.len; m0 += kStreamUnroll * tr.step) {
+        double xv[kStreamUnroll], pv[kStreamUnroll], svv[kStreamUnroll], tv[kStreamUnroll], hv[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t i = min((tr.lo + m0 + u * tr.step) * kTile + tid, n - 1);
+            xv[u] = x[i];
+            pv[u] = p[i];
+            svv[u] = sv[i];
+            tv[u] = t[i];
+            hv[u] = rh[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) {
+            const int64_t m = m0 + u * tr.step;
+            const int64_t i = (tr.lo + m) * kTile + tid;
+            if (m < tr.len && i < n) {
+                const double tp = alpha * pv[u];
+                const double x1 = xv[u] + tp;
+                const double tsv = omega * svv[u];
+                x[i] = x1 + tsv;
+                const double ttv = omega * tv[u];
+                const double rn = svv[u] - ttv;
+                r[i] = rn;
+                const double w1 = hv[u] * rn;
+                rho1 = rho1 + w1;
+                const double w2 = rn * rn;
+                rr1 = rr1 + w2;
+            }
+        }
+    }
+    rho1 = block_sum(rho1, s_red);
+    rr1 = block_sum(rr1, s_red);
+    if (tid == 0) {
+        a.part_rho[static_cast<int64_t>(sys) * a.Gu + bc.lb] = rho1;
+        a.part_rr[static_cast<int64_t>(sys) * a.Gu + bc.lb] = rr1;
     }
 }
 
@@ -2024,25 +2356,26 @@ hipError_t scan_exclusive(int64_t* data, int64_t n, int64_t* scratch, hipStream_
 
 using CgKernel = void (*)(CgArgs, int64_t);
 
-template <typename RP, bool O, bool SPLIT>
+template <typename RP, bool O, int MODE>
 CgKernel spmv_kernel_rp(int cap)
 {
-    if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O, SPLIT>;
-    if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O, SPLIT>;
-    return k_cg_spmv<RP, kCapLarge, O, SPLIT>;
+    if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O, MODE>;
+    if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O, MODE>;
+    return k_cg_spmv<RP, kCapLarge, O, MODE>;
 }
 
-template <bool SPLIT>
-CgKernel spmv_kernel_split(int rp_bits, int cap, bool off32)
+template <int MODE>
+CgKernel spmv_kernel_mode(int rp_bits, int cap, bool off32)
 {
     if (rp_bits == 64)
-        return off32 ? spmv_kernel_rp<int64_t, true, SPLIT>(cap) : spmv_kernel_rp<int64_t, false, SPLIT>(cap);
-    return off32 ? spmv_kernel_rp<int32_t, true, SPLIT>(cap) : spmv_kernel_rp<int32_t, false, SPLIT>(cap);
+        return off32 ? spmv_kernel_rp<int64_t, true, MODE>(cap) : spmv_kernel_rp<int64_t, false, MODE>(cap);
+    return off32 ? spmv_kernel_rp<int32_t, true, MODE>(cap) : spmv_kernel_rp<int32_t, false, MODE>(cap);
 }
 
 CgKernel spmv_kernel(int rp_bits, int cap, bool off32, bool split = false)
 {
-    return split ? spmv_kernel_split<true>(rp_bits, cap, off32) : spmv_kernel_split<false>(rp_bits, cap, off32);
+    return split ? spmv_kernel_mode<kSpmvSplit>(rp_bits, cap, off32)
+                 : spmv_kernel_mode<kSpmvFused>(rp_bits, cap, off32);
 }
 
 inline bool off32_ok(int64_t n) { return n < (int64_t(1) << 29); }
@@ -2174,6 +2507,38 @@ hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s)
         break;
     case 3: SLA_LAUNCH(k_gcg_update, gu, blk, 0, s, a, k); break;
     default: SLA_LAUNCH(k_gcg_finish, gu, blk, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+int bs_blocks_per_cu(int rp_bits, int cap, int64_t n)
+{
+    static int cache[2][3][2] = {};
+    const int ri = rp_bits == 64 ? 1 : 0;
+    const int ci = cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : 2);
+    const bool o = off32_ok(n);
+    int& c = cache[ri][ci][o ? 1 : 0];
+    if (c > 0) return c;
+    int a = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, spmv_kernel_mode<kSpmvBsT>(rp_bits, cap, o), kBlock, 0) !=
+            hipSuccess ||
+        a < 1)
+        a = 1;
+    c = a;
+    return c;
+}
+
+hipError_t launch_bs(int which, const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s)
+{
+    const dim3 gu(a.Gu, a.batch), gs(a.G, a.batch), blk(kBlock);
+    const bool o = off32_ok(a.n);
+    switch (which) {
+    case 0: SLA_LAUNCH(k_bs_init, gu, blk, 0, s, a); break;
+    case 1: SLA_LAUNCH(k_bs_pupd, gu, blk, 0, s, a, k); break;
+    case 2: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsV>(rp_bits, cap, o), gs, blk, 0, s, a, k); break;
+    case 3: SLA_LAUNCH(k_bs_s, gu, blk, 0, s, a, k); break;
+    case 4: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsT>(rp_bits, cap, o), gs, blk, 0, s, a, k); break;
+    default: SLA_LAUNCH(k_bs_update, gu, blk, 0, s, a, k); break;
     }
     return hipGetLastError();
 }

@@ -154,8 +154,14 @@ def matvec_backward(h: Handle, vals: torch.Tensor, x: torch.Tensor, gy: torch.Te
 
 
 def cg_opts(rtol=1e-10, atol=0.0, max_iter=100000, fixed=False, check_every=0,
-            residual_history: torch.Tensor | None = None, jacobi: bool = False) -> SlaCgOpts:
-    flags = (L.SLA_FIXED_ITERS if fixed else 0) | (L.SLA_JACOBI if jacobi else 0)
+            residual_history: torch.Tensor | None = None, jacobi: bool = False,
+            method: str = "cg") -> SlaCgOpts:
+    """Solver options.  method: "cg" (with jacobi=True, Jacobi-preconditioned) or
+    "bicgstab" (nonsymmetric systems; the adjoint then runs BiCGStab on A^T)."""
+    if method not in ("cg", "bicgstab"):
+        raise ValueError(f"unknown method {method!r} (expected 'cg' or 'bicgstab')")
+    flags = ((L.SLA_FIXED_ITERS if fixed else 0) | (L.SLA_JACOBI if jacobi else 0)
+             | (L.SLA_BICGSTAB if method == "bicgstab" else 0))
     return SlaCgOpts(float(rtol), float(atol), int(max_iter), int(check_every), flags,
                      residual_history.data_ptr() if residual_history is not None else None)
 
@@ -305,15 +311,16 @@ class SparseTensor:
         return _MatvecFn.apply(self, self.vals, x)
 
     def solve(self, b: torch.Tensor, rtol=1e-10, atol=0.0, max_iter=100000, fixed=False,
-              check: bool = False, jacobi: bool = False) -> torch.Tensor:
-        kw = dict(rtol=rtol, atol=atol, max_iter=max_iter, fixed=fixed, jacobi=jacobi)
+              check: bool = False, jacobi: bool = False, method: str = "cg") -> torch.Tensor:
+        kw = dict(rtol=rtol, atol=atol, max_iter=max_iter, fixed=fixed, jacobi=jacobi, method=method)
         x = _SolveFn.apply(self, self.vals, b, kw)
         if check:
+            name = "BiCGStab" if method == "bicgstab" else "CG"
             for i, s in enumerate(read_info(self.last_info)):
-                if s["state"] in (L.SLA_NOT_SPD, L.SLA_NAN):
-                    raise FloatingPointError(f"system {i}: CG stopped with {s['state_name']}")
+                if s["state"] in (L.SLA_NOT_SPD, L.SLA_NAN, L.SLA_BREAKDOWN):
+                    raise FloatingPointError(f"system {i}: {name} stopped with {s['state_name']}")
                 if s["state"] == L.SLA_MAX_ITER and not fixed:
-                    warnings.warn(f"system {i}: CG reached max_iter={max_iter} "
+                    warnings.warn(f"system {i}: {name} reached max_iter={max_iter} "
                                   f"(|r|/|b| = {s['res_norm'] / max(s['rhs_norm'], 1e-300):.3e})")
         return x
 

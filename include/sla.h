@@ -69,7 +69,10 @@ enum {
     SLA_CONVERGED = 0,   /* |r_k| <= max(rtol |rhs|, atol) with r_k the recurrence residual */
     SLA_MAX_ITER = 1,    /* iteration budget reached (always the outcome with SLA_FIXED_ITERS) */
     SLA_NOT_SPD = 2,     /* p^T A p <= 0 (or, with SLA_JACOBI, a diagonal entry <= 0 or missing) */
-    SLA_NAN = 3          /* p^T A p is NaN (or, with SLA_JACOBI, a NaN diagonal entry) */
+    SLA_NAN = 3,         /* p^T A p is NaN (or, with SLA_JACOBI, a NaN diagonal entry;
+                            with SLA_BICGSTAB, <rh, A p>, <t, s> or <t, t> is NaN) */
+    SLA_BREAKDOWN = 4    /* SLA_BICGSTAB only: <rh, A p> = 0, <t, t> = 0, or a zero
+                            <rh, r> or omega at the start of an iteration */
 };
 
 /* sla_csr_create flags */
@@ -89,6 +92,24 @@ enum {
  * the same preconditioner (A^T has the same diagonal).
  */
 #define SLA_JACOBI           2u
+/*
+ * BiCGStab instead of CG, for nonsymmetric (and SPD) systems: van der Vorst's method
+ * (Bi-CGSTAB, SIAM J. Sci. Stat. Comput. 13(2), 1992), the second iterative method of
+ * the pages' backends (paperpeel page, section 1; section 3.1 "Five backends and
+ * auto-dispatch").  x0 = 0, shadow residual rh = b, no preconditioner (not combinable
+ * with SLA_JACOBI: SLA_ERR_INVALID_ARG).  Iteration k:
+ *   stop if |r| <= max(rtol |rhs|, atol) or k = max_iter;
+ *   k > 0: beta = (rho_k / rho_{k-1}) (alpha / omega), p = r + beta (p - omega v),
+ *          with rho_k = <rh, r>;
+ *   v = A p, alpha = rho_k / <rh, v>, s = r - alpha v, t = A s,
+ *   |s| <= threshold: x += alpha p, stop (converged; counts as iteration k + 1);
+ *   omega = <t, s> / <t, t>, x += alpha p + omega s, r = s - omega t.
+ * iterations counts the products A p; residual_history records |r_k| (|s| for a stop
+ * half-way).  Breakdowns stop with SLA_BREAKDOWN (or SLA_NAN) and the x before the
+ * failing iteration.  The adjoint solve of sla_solve_backward uses BiCGStab on A^T
+ * (on A for an SLA_SYMMETRIC handle).
+ */
+#define SLA_BICGSTAB         4u
 
 typedef struct sla_csr sla_csr;   /* opaque handle: one sparsity pattern */
 
@@ -97,7 +118,7 @@ typedef struct {
     double atol;                 /* absolute tolerance on |r| (>= 0) */
     int64_t max_iter;            /* iteration budget (>= 0) */
     int32_t check_every;         /* iterations between host polls of the stop counter (0 = default 32) */
-    uint32_t flags;              /* SLA_FIXED_ITERS | SLA_JACOBI */
+    uint32_t flags;              /* SLA_FIXED_ITERS | SLA_JACOBI | SLA_BICGSTAB */
     double* residual_history;    /* device, nullable: [batch][max_iter + 1], entry k = |r_k| */
 } sla_cg_opts;
 
@@ -105,7 +126,7 @@ typedef struct {
     int64_t iterations;          /* number of products A p performed */
     double res_norm;             /* |r| of the recurrence residual at exit */
     double rhs_norm;             /* |b| (forward) or |dL/dx| (backward) */
-    int32_t state;               /* SLA_CONVERGED, SLA_MAX_ITER, SLA_NOT_SPD or SLA_NAN */
+    int32_t state;               /* SLA_CONVERGED, SLA_MAX_ITER, SLA_NOT_SPD, SLA_NAN or SLA_BREAKDOWN */
     int32_t reserved;
 } sla_cg_info;                   /* 32 bytes; device arrays of these have one entry per system */
 
@@ -189,14 +210,17 @@ sla_status sla_matvec_backward(const sla_csr* A, int64_t batch, const double* d_
  * on a breakdown (sigma <= 0 or NaN: x is the iterate before that step).  No host
  * synchronisation happens inside an iteration: scalars and stop decisions live on
  * the device.  Requires n_rows == n_cols.  b = 0 gives x = 0 after 0 iterations.
+ * With SLA_JACOBI in opts->flags the CG is Jacobi-preconditioned; with SLA_BICGSTAB
+ * the method is BiCGStab (see the flags above).
  */
 sla_status sla_solve(const sla_csr* A, int64_t batch, const double* d_vals, const double* d_b,
                      double* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
 
 /*
  * Adjoint backward pass of x = A^{-1} b (gist.science summaries, Methodology item 2;
- * paperpeel section 3.2.3): solve A^T lambda = dL/dx with the same CG and options
- * (threshold relative to |dL/dx|), then
+ * paperpeel section 3.2.3): solve A^T lambda = dL/dx with the same method (CG,
+ * Jacobi CG or BiCGStab, from opts->flags) and options (threshold relative to
+ * |dL/dx|), then
  *   d_gb[b][i]    = lambda_b[i]                       (dL/db)
  *   d_gvals[b][k] = -lambda_b[row(k)] * x_b[col(k)]   (dL/dA on the pattern; nullable)
  *   d_x  [batch][n]  the forward solution (saved by the caller)
@@ -226,7 +250,9 @@ enum {
     SLA_K_TRANSPOSE = 6,    /* pattern transpose (all its kernels) */
     SLA_K_CG_PUPD = 7,      /* split schedule: step decisions, p = r + beta p, x update */
     SLA_K_GROUP_LAYOUT = 8, /* grouped batches: values and x between layouts */
-    SLA_K_COUNT = 9
+    SLA_K_BS_SPMV = 9,      /* BiCGStab: v = A p with <rh, v>, and t = A s with <t, s>, <t, t> */
+    SLA_K_BS_VEC = 10,      /* BiCGStab: init, p update, s = r - alpha v, x and r update */
+    SLA_K_COUNT = 11
 };
 sla_status sla_timing_enable(int32_t enable);
 sla_status sla_timing_reset(void);
