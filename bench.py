@@ -11,6 +11,10 @@ nnz = 5,238,784, b ~ N(0, 1) seed 0, relative residual 1e-8), a stand-in for the
 1M-DOF 2-D Poisson benchmark of the torch-sla paper (paperpeel page, section 4.1,
 Table 3).  Inputs are resident in HBM before the timed region starts.
 
+--workload convdiff1024 runs BiCGStab (forward, and on A^T in the adjoint) on a
+nonsymmetric convection-diffusion system instead; its line reports BiCGStab
+iterations per second under its own metric name.
+
 Printed: one JSON line with value = CG iterations per second (forward + adjoint
 iterations of all timed steps / wall time), the roofline of the dominant kernel
 (algorithmic bytes per launch / HIP-event-timed average launch duration), and the
@@ -36,6 +40,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "fp64 CG iters/s + achieved HBM GB/s, Poisson 1M/169M DOF; solve+adjoint ms"
+# the nonsymmetric widening (not the headline metric): BiCGStab on convection-diffusion
+METRIC_BICGSTAB = "fp64 BiCGStab iters/s + achieved HBM GB/s, convection-diffusion 1M DOF; solve+adjoint ms"
 COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written
 
 
@@ -77,6 +83,25 @@ def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False
                 flops_iteration=(2 * nnz + 10 * n) * batch)
 
 
+def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
+    """Algorithmic HBM bytes of the BiCGStab kernels, per launch (all systems).
+
+      v = A p  : values, columns, row pointers + read p (the gathers are cache traffic)
+                 and rh, write v                                    -> 3 x 8 n B
+      t = A s  : values, columns, row pointers + read s, write t    -> 2 x 8 n B
+      bs_spmv  : the mean of the two (the timing id covers both launches)
+      p update : read r, p, v; write p -> 4;  s: read r, v; write s -> 3;
+      update   : read x, p, s, t, rh; write x, r -> 7;  bs_vec: the mean of the three
+      one iteration = both products + 14 vector passes.
+    """
+    mat = 8 * nnz * batch + 4 * nnz + rp_bytes * (n + 1)
+    v = 8 * n * batch
+    spmv_v, spmv_t = mat + 3 * v, mat + 2 * v
+    vec = 14 * v
+    return dict(bs_spmv=(spmv_v + spmv_t) / 2, bs_vec=vec / 3, iteration=spmv_v + spmv_t + vec,
+                flops_iteration=(4 * nnz + 24 * n) * batch)
+
+
 # ------------------------------------------------------------------------------ workloads
 def make_workload(name: str, device):
     import numpy as np
@@ -90,6 +115,7 @@ def make_workload(name: str, device):
         b = torch.from_numpy(W.rhs_normal(N * N, 0)).to(device)
         return dict(name=name, n=N * N, nnz=col.numel(), batch=1, rp=rp, col=col, vals=vals, b=b,
                     rtol=0.0, max_iter=c["max_iter"], fixed=True, loss="half_sq", host=None,
+                    method="cg", symmetric=True,
                     desc=f"5-point Poisson {N}x{N}, int64 row_ptr, b~N(0,1) seed 0, "
                          f"{c['max_iter']} fixed CG iterations + {c['max_iter']} adjoint")
     c = W.config(name)
@@ -108,7 +134,11 @@ def make_workload(name: str, device):
                        "CG to 1e-8 + adjoint of 0.5|x|^2",
         "varcoef2048": "variable-coefficient Poisson 2048x2048, kappa=exp(GRF), CG to 1e-8 + adjoint",
         "fem256x256": "256 P1 FEM systems on a jittered 256x256-vertex mesh, CG to 1e-8 + adjoint",
+        "convdiff1024": "nonsymmetric convection-diffusion 1024x1024 (upwind, recirculating wind W=100), "
+                        "b~N(0,1) seed 0, BiCGStab to 1e-8 + BiCGStab adjoint on A^T",
     }
+    out["method"] = c.get("method", "cg")
+    out["symmetric"] = c.get("symmetric", True)
     out["desc"] = descs[name]
     return out
 
@@ -138,12 +168,16 @@ def cpu_baseline(w, iters: int) -> dict:
         vals = A.vals.reshape(A.batch, A.nnz)[0]
         sample = (f"oracle CG on system 0 of this workload, {iters} fixed iterations + "
                   f"{iters} adjoint iterations (single thread)")
+    method = w.get("method", "cg")
+    if method == "bicgstab":
+        sample = sample.replace("oracle CG", "oracle BiCGStab")
     t0 = time.perf_counter()
-    f = O.cg(A, b, rtol=0.0, max_iter=iters, fixed=True, vals=vals)
-    O.solve_backward(A, f["x"], f["x"], symmetric=True, rtol=0.0, max_iter=iters, fixed=True,
-                     vals=vals)
+    f = O.cg(A, b, rtol=0.0, max_iter=iters, fixed=True, vals=vals, method=method)
+    O.solve_backward(A, f["x"], f["x"], symmetric=w.get("symmetric", True), rtol=0.0, max_iter=iters,
+                     fixed=True, vals=vals, method=method)
     dt = time.perf_counter() - t0
-    return dict(value=round(2 * iters / dt, 3), unit="CG iters/s", cores=1, kind="oracle",
+    unit = "BiCGStab iters/s" if method == "bicgstab" else "CG iters/s"
+    return dict(value=round(2 * iters / dt, 3), unit=unit, cores=1, kind="oracle",
                 sample=sample, seconds=round(dt, 2))
 
 
@@ -201,8 +235,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
     spmv_w, nw = pick(wr, ["k_cg_spmv", "k_gcg_spmv"])
     upd_f, _ = pick(fr, ["k_cg_update", "k_gcg_update"])
     upd_w, _ = pick(wr, ["k_cg_update", "k_gcg_update"])
-    pupd_f, _ = pick(fr, ["k_cg_pupd", "k_gcg_pupd"])
-    pupd_w, _ = pick(wr, ["k_cg_pupd", "k_gcg_pupd"])
+    pupd_f, _ = pick(fr, ["k_cg_pupd", "k_gcg_pupd", "k_bs_pupd"])
+    pupd_w, _ = pick(wr, ["k_cg_pupd", "k_gcg_pupd", "k_bs_pupd"])
+    if upd_f is None:   # BiCGStab
+        upd_f, _ = pick(fr, ["k_bs_update"])
+        upd_w, _ = pick(wr, ["k_bs_update"])
     kib = 1024.0
     sf = COPY_BYTES / (copy_f * kib) if copy_f else 1.0
     sw = COPY_BYTES / (copy_w * kib) if copy_w else 1.0
@@ -230,7 +267,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="poisson1024",
-                    choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000"])
+                    choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000",
+                             "convdiff1024"])
     ap.add_argument("--cpu-iters", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -258,9 +296,14 @@ def main() -> int:
     w = make_workload(args.workload, dev)
     n, nnz, B = w["n"], w["nnz"], w["batch"]
     rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
-    h = S.csr_create(w["rp"], w["col"], symmetric=True)
+    method = w["method"]
+    bicg = method == "bicgstab"
+    h = S.csr_create(w["rp"], w["col"], symmetric=w["symmetric"])
     an = S.csr_analysis(h)
-    if an["band_stride"] > 0:
+    if bicg:
+        spmv_kernel = "k_cg_spmv (BiCGStab modes: v = A p, t = A s)"
+        schedule = "BiCGStab: p update, v = A p, s, t = A s, update (adjoint on the device transpose)"
+    elif an["band_stride"] > 0:
         spmv_kernel, schedule = "k_cg_spmv_band", f"fused, banded SpMV (line stride {an['band_stride']})"
     elif an["split"] and B >= 8 and B % 4 == 0 and nnz < 2 ** 31:
         spmv_kernel = "k_gcg_spmv"
@@ -271,7 +314,8 @@ def main() -> int:
         spmv_kernel, schedule = "k_cg_spmv", "fused"
     if args.fixed_iters > 0:
         w["max_iter"], w["fixed"], w["rtol"] = args.fixed_iters, True, 0.0
-    opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"], jacobi=args.jacobi)
+    opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"], jacobi=args.jacobi,
+                     method=method)
     vals, b = w["vals"], w["b"]
 
     def step():
@@ -310,8 +354,8 @@ def main() -> int:
     # timed launch is a working one.
     S.timing.reset()
     S.timing.enable(True)
-    fo = S.cg_opts(rtol=0.0, max_iter=max_fwd, fixed=True, jacobi=args.jacobi)
-    bo = S.cg_opts(rtol=0.0, max_iter=max_bwd, fixed=True, jacobi=args.jacobi)
+    fo = S.cg_opts(rtol=0.0, max_iter=max_fwd, fixed=True, jacobi=args.jacobi, method=method)
+    bo = S.cg_opts(rtol=0.0, max_iter=max_bwd, fixed=True, jacobi=args.jacobi, method=method)
     x, _ = S.solve(h, vals, b, fo)
     S.solve_backward(h, vals, x, loss_grad(w, x), bo)
     S.timing.collect()
@@ -319,13 +363,21 @@ def main() -> int:
     tq = S.timing.query()
     torch.cuda.synchronize()
 
-    bm = bytes_model(n, nnz, B, rp_bytes, split=an["split"])
-    spmv_ms = tq["cg_spmv"]["total_ms"] / max(tq["cg_spmv"]["launches"], 1)
-    upd_ms = tq["cg_update"]["total_ms"] / max(tq["cg_update"]["launches"], 1)
-    pupd_ms = tq["cg_pupd"]["total_ms"] / max(tq["cg_pupd"]["launches"], 1) if an["split"] else 0.0
-    achieved = bm["cg_spmv"] / (spmv_ms * 1e-3) / 1e9
+    def avg_ms(key):
+        return tq[key]["total_ms"] / max(tq[key]["launches"], 1)
+
+    if bicg:
+        bm = bytes_model_bicgstab(n, nnz, B, rp_bytes)
+        spmv_ms, spmv_bytes = avg_ms("bs_spmv"), bm["bs_spmv"]
+        # per iteration: two products and three streaming kernels (init excluded)
+        iter_ms = 2 * spmv_ms + 3 * avg_ms("bs_vec")
+    else:
+        bm = bytes_model(n, nnz, B, rp_bytes, split=an["split"])
+        spmv_ms, spmv_bytes = avg_ms("cg_spmv"), bm["cg_spmv"]
+        iter_ms = spmv_ms + avg_ms("cg_update") + (avg_ms("cg_pupd") if an["split"] else 0.0)
+    achieved = spmv_bytes / (spmv_ms * 1e-3) / 1e9
     traffic, traffic_src = read_traffic(args.workload)
-    iter_gbps = bm["iteration"] / ((spmv_ms + upd_ms + pupd_ms) * 1e-3) / 1e9
+    iter_gbps = bm["iteration"] / (iter_ms * 1e-3) / 1e9
     wall_gbps = bm["iteration"] * (total_it / B) / wall / 1e9
 
     if args.calibrate_copy:
@@ -338,12 +390,13 @@ def main() -> int:
 
     cpu = None
     if rank == 0 and not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_iters)
+        # a BiCGStab iteration is two products: half as many keep the sample's CPU time
+        cpu = cpu_baseline(w, max(1, args.cpu_iters // 2) if bicg else args.cpu_iters)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BICGSTAB if bicg else METRIC,
         "value": round(value, 2),
-        "unit": "CG iters/s",
+        "unit": "BiCGStab iters/s" if bicg else "CG iters/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -356,7 +409,8 @@ def main() -> int:
         "config": {"workload": w["desc"], "n": n, "nnz": nnz, "batch": B,
                    "row_ptr": f"int{8 * rp_bytes}", "rtol": w["rtol"],
                    "fixed_iterations": w["fixed"], "parallelism": "none (1 GPU)",
-                   "cg_schedule": schedule, "preconditioner": "jacobi" if args.jacobi else "none"},
+                   "cg_schedule": schedule, "preconditioner": "jacobi" if args.jacobi else "none",
+                   "method": method},
         "iterations_per_step": {"forward": fwd_it[-1], "adjoint": bwd_it[-1]},
         "solve_adjoint_ms": round(ms_step, 4),
         "hbm_gbps_per_iteration": round(iter_gbps, 1),
@@ -369,7 +423,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": spmv_kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "traffic_source": traffic_src,
-                     "bytes_per_launch": bm["cg_spmv"], "avg_launch_us": round(1e3 * spmv_ms, 3)},
+                     "bytes_per_launch": spmv_bytes, "avg_launch_us": round(1e3 * spmv_ms, 3)},
         "cpu_baseline": cpu,
     }
     if rank == 0:

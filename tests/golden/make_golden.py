@@ -15,6 +15,8 @@ fem256x256      256 systems to 1e-8 + adjoint of sum_b 0.5|x_b|^2 (iteration cou
                 every system; samples of 8 systems).
 poisson13000    the first 20 fixed iterations forward and adjoint (the full 500 are
                 beyond a CPU fixture): residual history and samples of x, lambda, grads.
+convdiff1024    BiCGStab to 1e-8 on the nonsymmetric convection-diffusion matrix and on
+                its transpose in the adjoint of 0.5|x|^2, with the true residuals.
 Runs take from seconds (poisson64) to tens of minutes (varcoef2048, fem256x256).
 """
 from __future__ import annotations
@@ -48,10 +50,11 @@ def loss_grad(c, x, s=0):
 
 
 def one_system(A, b, vals, c, want_full=False, g_of=None):
-    opts = dict(rtol=c["rtol"], atol=c["atol"], max_iter=c["max_iter"], fixed=c["fixed"])
+    opts = dict(rtol=c["rtol"], atol=c["atol"], max_iter=c["max_iter"], fixed=c["fixed"],
+                method=c.get("method", "cg"))
     f = O.cg(A, b, vals=vals, **opts)
     g = loss_grad(c, f["x"]) if g_of is None else g_of(f["x"])
-    bw = O.solve_backward(A, f["x"], g, symmetric=True, vals=vals, **opts)
+    bw = O.solve_backward(A, f["x"], g, symmetric=c.get("symmetric", True), vals=vals, **opts)
     out = dict(iterations=f["iterations"], state=f["state"], res_norm=f["res_norm"],
                rhs_norm=f["rhs_norm"], x_norm=float(np.linalg.norm(f["x"])),
                adj_iterations=bw["iterations"], adj_state=bw["state"], adj_res_norm=bw["res_norm"],
@@ -60,6 +63,10 @@ def one_system(A, b, vals, c, want_full=False, g_of=None):
     ix, ik = samples(A.n_rows, 11), samples(A.nnz, 12)
     out.update(ix=ix.tolist(), ik=ik.tolist(), x=f["x"][ix].tolist(), lam=bw["lam"][ix].tolist(),
                gvals=bw["gvals"][ik].tolist())
+    if c.get("method") == "bicgstab":
+        # true residuals of the oracle's solutions (the stop test is on the recurrence)
+        out.update(true_res=float(np.linalg.norm(b - O.spmv(A, f["x"], vals=vals))),
+                   adj_true_res=float(np.linalg.norm(g - O.spmv_transposed(A, bw["lam"], vals=vals))))
     if want_full:
         out.update(x_full=f["x"].tolist(), lam_full=bw["lam"].tolist())
     return out
@@ -123,5 +130,5 @@ def main(names):
 
 
 if __name__ == "__main__":
-    ALL = ["poisson64", "poisson1024", "fem256x256", "poisson13000", "varcoef2048"]
+    ALL = ["poisson64", "poisson1024", "fem256x256", "poisson13000", "varcoef2048", "convdiff1024"]
     main(sys.argv[1:] or ALL)

@@ -5,6 +5,8 @@
   tests/golden/make_golden.py, which calls only the oracle): iteration counts within
   2 % (every system of the FEM batch), x within 1e-9, lambda and dL/dvals within 1e-8
   (relative, on seeded samples and on the norms).
+* convdiff1024: BiCGStab and its adjoint on A^T, by the bounds its stop test fixes
+  (see the test's docstring).
 * poisson13000 (169M unknowns, int64 row pointers), in the launch configuration the
   benchmark uses:
     - the first 20 fixed iterations against the oracle's residual history and
@@ -211,3 +213,34 @@ def test_poisson13000_benchmark_run_properties(S, big):
     row_of = torch.searchsorted(big["rp"], kt, right=True) - 1
     expect = -(gb[row_of] * x[big["col"][kt].long()])
     assert np.array_equal(host(gv[kt]), host(expect))
+
+
+# --------------------------------------------------------------------- BiCGStab, 1M rows
+def test_fullsize_bicgstab_convdiff(S):
+    """convdiff1024: BiCGStab forward and on A^T in the adjoint, in the benchmark's launch
+    configuration.  BiCGStab's stop point and solution move with the summation order
+    alone (up to 13 % in iterations on smaller grids), so this is held to what the stop
+    test fixes, checked by the oracle at full size: the true residuals |b - A x| and
+    |x - A^T lambda| within 2 rtol, iteration counts within 20 % of the oracle's, and
+    dL/dvals = -lambda_i x_j bit for bit on every stored entry."""
+    g = golden("convdiff1024")
+    c = W.config("convdiff1024")
+    A = c["A"]
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=False)
+    opts = S.cg_opts(rtol=c["rtol"], atol=c["atol"], max_iter=c["max_iter"], method="bicgstab")
+    dv, db = dev(A.vals), dev(c["b"])
+    x, info = S.solve(h, dv, db, opts)
+    gb, gv, binfo = S.solve_backward(h, dv, x, x.clone(), opts)
+    x, lam, gv = host(x), host(gb), host(gv)
+    info, binfo = S.read_info(info)[0], S.read_info(binfo)[0]
+    assert info["state"] == binfo["state"] == g["state"] == g["adj_state"] == O.CONVERGED
+    assert iters_close(info["iterations"], g["iterations"], 0.20), (info["iterations"], g["iterations"])
+    assert iters_close(binfo["iterations"], g["adj_iterations"], 0.20), (binfo["iterations"],
+                                                                          g["adj_iterations"])
+    rtol, nb = c["rtol"], np.linalg.norm(c["b"])
+    assert abs(info["rhs_norm"] - g["rhs_norm"]) <= 1e-12 * g["rhs_norm"]
+    assert g["true_res"] <= 2 * rtol * nb                       # the oracle's own solution
+    assert np.linalg.norm(c["b"] - O.spmv(A, x)) <= 2 * rtol * nb
+    nx = np.linalg.norm(x)
+    assert np.linalg.norm(x - O.spmv_transposed(A, lam)) <= 2 * rtol * nx
+    assert np.array_equal(gv, O.pattern_outer(A, lam, x, sign=-1.0))
