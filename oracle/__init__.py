@@ -23,7 +23,10 @@ Adjoint Solvers and Sparse Tensor Parallelism for PyTorch):
                           linear-systems bullet).
   * ``matvec_backward``   for y = A x: dL/dx = A^T gy, dL/dA_ij = gy_i x_j.
   * ``transpose``         stable counting-sort transpose of the pattern.
-Every function is pinned by tests/test_oracle_pins.py; none is "parity unpinned".
+  * ``eigsh`` (module oracle/eigsh.py)  Lanczos eigenpairs and the Hellmann-Feynman
+                          gradient (paperpeel section 4.3, note to Table 5).
+Every function is pinned (tests/test_oracle_pins.py, test_oracle_bicgstab.py,
+test_oracle_eigsh.py); none is "parity unpinned".
 """
 from __future__ import annotations
 

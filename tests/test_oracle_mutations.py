@@ -66,3 +66,35 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                         os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "pins missed the planted mistake: " + name
+
+
+# The Lanczos eigensolver is Python (oracle/eigsh.py): mutated copies are loaded by
+# tests/test_oracle_eigsh.py through SLA_ORACLE_EIGSH.
+EIGSH = os.path.join(ROOT, "oracle", "eigsh.py")
+EIGSH_MUTANTS = {
+    # (a wrong sign in the three-term step is not a mistake in effect: the full
+    # reorthogonalization that follows removes any multiple of v_j and v_{j-1})
+    "lanczos alpha from v_0": ("a = dot(V[j], w)", "a = dot(V[0], w)"),
+    "lanczos without reorthogonalization": ("for _ in range(2):", "for _ in range(0):"),
+    "lanczos residual from the first component": ("res = b * np.abs(S[m - 1, idx])", "res = b * np.abs(S[0, idx])"),
+    "ritz vectors from a shifted basis": ("U = S[:, idx].T @ V[:m]", "U = S[:, idx].T @ V[1:m + 1]"),
+    "largest taken in ascending order": ("np.arange(m - 1, m - 1 - k, -1)", "np.arange(m - k, m)"),
+    "sign convention dropped": ("if dot(U[i], v) < 0.0:", "if False:"),
+    "gradient weights of the first eigenvalue": ("float(g_evals[m])", "float(g_evals[0])"),
+    "gradient of the first eigenvector only": ("pattern_outer(A, evecs[m], evecs[m], sign=1.0)",
+                                               "pattern_outer(A, evecs[0], evecs[0], sign=1.0)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EIGSH_MUTANTS))
+def test_eigsh_pins_catch_planted_mistake(name, tmp_path):
+    src = open(EIGSH).read()
+    a, b = EIGSH_MUTANTS[name]
+    assert a in src, "mutation anchor vanished from the oracle source"
+    mut = tmp_path / "eigsh_mut.py"
+    mut.write_text(src.replace(a, b, 1))
+    env = dict(os.environ, SLA_ORACLE_EIGSH=str(mut), OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_eigsh.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "pins missed the planted mistake: " + name
