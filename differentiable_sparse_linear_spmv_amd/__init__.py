@@ -1,6 +1,7 @@
-"""MI355X-native differentiable sparse CG: CSR SpMV, conjugate-gradient solve and
-its adjoint backward pass, as HIP kernels for gfx950 behind a C ABI
-(include/sla.h, libsla.so).
+"""MI355X-native differentiable sparse linear algebra: CSR SpMV, the
+conjugate-gradient solve (plain or Jacobi-preconditioned) and BiCGStab with their
+adjoint backward passes, and the Lanczos eigensolver with its Hellmann-Feynman
+gradient, as HIP kernels for gfx950 behind a C ABI (include/sla.h, libsla.so).
 
 Importing the package loads libsla.so and fails loudly if it is missing: there
 is no CPU path.
@@ -11,7 +12,9 @@ from ._lib import SlaError
 _lib.load()
 
 from .sparse import (SparseTensor, cg_opts, csr_analysis, csr_create, csr_destroy,  # noqa: E402
-                     csr_info, matvec, matvec_backward, read_info, solve, solve_backward, timing)
+                     csr_info, eigsh, eigsh_backward, matvec, matvec_backward, read_info, solve,
+                     solve_backward, timing)
 
 __all__ = ["SparseTensor", "SlaError", "cg_opts", "csr_analysis", "csr_create", "csr_destroy", "csr_info",
-           "matvec", "matvec_backward", "read_info", "solve", "solve_backward", "timing"]
+           "eigsh", "eigsh_backward", "matvec", "matvec_backward", "read_info", "solve", "solve_backward",
+           "timing"]

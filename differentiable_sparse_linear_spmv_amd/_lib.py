@@ -21,15 +21,18 @@ SLA_EAGER_TRANSPOSE = 2
 SLA_FIXED_ITERS = 1
 SLA_JACOBI = 2
 SLA_BICGSTAB = 4
+SLA_EIG_LARGEST, SLA_EIG_SMALLEST = 0, 1
+SLA_EIG_MAX_K = 32
 (SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
  SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_GROUP_LAYOUT, SLA_K_BS_SPMV, SLA_K_BS_VEC,
- SLA_K_COUNT) = range(12)
+ SLA_K_LZ_SPMV, SLA_K_LZ_ORTH, SLA_K_LZ_RITZ, SLA_K_COUNT) = range(15)
 KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "gather_vals",
-                "transpose", "cg_pupd", "group_layout", "bs_spmv", "bs_vec"]
+                "transpose", "cg_pupd", "group_layout", "bs_spmv", "bs_vec", "lz_spmv", "lz_orth",
+                "lz_ritz"]
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
-    "sla_solve", "sla_solve_backward", "sla_timing_enable", "sla_timing_reset",
+    "sla_solve", "sla_solve_backward", "sla_eigsh", "sla_eigsh_backward", "sla_timing_enable", "sla_timing_reset",
     "sla_timing_collect", "sla_timing_query", "sla_status_string", "sla_last_error", "sla_version",
 ]
 
@@ -46,6 +49,16 @@ class SlaCgInfo(C.Structure):
 
 
 assert C.sizeof(SlaCgInfo) == 32
+
+
+class SlaEigOpts(C.Structure):
+    _fields_ = [("tol", C.c_double), ("max_dim", C.c_int64), ("which", C.c_int32),
+                ("check_every", C.c_int32)]
+
+
+class SlaEigInfo(C.Structure):
+    _fields_ = [("iterations", C.c_int64), ("max_res", C.c_double), ("state", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class SlaError(RuntimeError):
@@ -92,6 +105,10 @@ def load():
     L.sla_solve.restype = st
     L.sla_solve_backward.argtypes = [P, i64, P, P, P, P, P, C.POINTER(SlaCgOpts), P, P]
     L.sla_solve_backward.restype = st
+    L.sla_eigsh.argtypes = [P, P, i32, P, P, P, C.POINTER(SlaEigOpts), C.POINTER(SlaEigInfo), P]
+    L.sla_eigsh.restype = st
+    L.sla_eigsh_backward.argtypes = [P, i32, P, P, P, P]
+    L.sla_eigsh_backward.restype = st
     L.sla_timing_enable.argtypes = [i32]
     L.sla_timing_enable.restype = st
     L.sla_timing_reset.argtypes = []

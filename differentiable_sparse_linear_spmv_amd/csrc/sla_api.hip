@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -64,6 +66,11 @@ struct sla_csr {
     size_t gws_bytes = 0;
     size_t vals_t_bytes = 0;
     int32_t* flag_host = nullptr;   // pinned, 2 slots for the polling copies
+    // Lanczos (sla_eigsh): device workspace and a pinned host staging area
+    void* eig_ws = nullptr;
+    size_t eig_ws_bytes = 0;
+    double* eig_host = nullptr;
+    size_t eig_host_bytes = 0;
     hipEvent_t poll_ev[2] = {nullptr, nullptr};
     std::mutex mu;
 };
@@ -815,6 +822,8 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->perm_t) (void)hipFree(A->perm_t);
     if (A->rp_owned) (void)hipFree(A->rp_owned);
     if (A->flag_host) (void)hipHostFree(A->flag_host);
+    if (A->eig_ws) (void)hipFree(A->eig_ws);
+    if (A->eig_host) (void)hipHostFree(A->eig_host);
     for (int i = 0; i < 2; ++i)
         if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);
     if (prev >= 0 && prev != A->device) (void)hipSetDevice(prev);
@@ -969,6 +978,251 @@ sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_
         hipError_t e = timing_collect();
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
     }
+    return SLA_OK;
+}
+
+sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const double* d_v0, double* d_evals,
+                     double* d_evecs, const sla_eig_opts* opts, sla_eig_info* info, void* stream)
+{
+    sla_status st = check_common(Ac, 1);
+    if (st != SLA_OK) return st;
+    if (Ac->n_rows != Ac->n_cols) return fail(SLA_ERR_UNSUPPORTED, "eigsh needs a square matrix");
+    if (!(Ac->flags & SLA_SYMMETRIC))
+        return fail(SLA_ERR_UNSUPPORTED, "eigsh needs a symmetric matrix (a handle created with SLA_SYMMETRIC)");
+    if (!opts || !info || !d_v0 || !d_evals || !d_evecs || (!d_vals && Ac->nnz > 0))
+        return fail(SLA_ERR_INVALID_ARG, "NULL argument");
+    const int64_t n = Ac->n_rows;
+    if (n < 1) return fail(SLA_ERR_INVALID_ARG, "eigsh of an empty matrix");
+    const int64_t max_dim = opts->max_dim > 0 ? opts->max_dim : std::min<int64_t>(n, 1000);
+    if (max_dim > n) return fail(SLA_ERR_INVALID_ARG, "max_dim %lld exceeds n %lld", (long long)max_dim, (long long)n);
+    if (k < 1 || k > SLA_EIG_MAX_K || k > max_dim)
+        return fail(SLA_ERR_INVALID_ARG, "k must be in [1, min(%d, max_dim)] (got %d)", SLA_EIG_MAX_K, k);
+    if (!(opts->tol > 0.0)) return fail(SLA_ERR_INVALID_ARG, "tol must be > 0");
+    if (opts->which != SLA_EIG_LARGEST && opts->which != SLA_EIG_SMALLEST)
+        return fail(SLA_ERR_INVALID_ARG, "which must be SLA_EIG_LARGEST or SLA_EIG_SMALLEST");
+    if (opts->check_every < 0) return fail(SLA_ERR_INVALID_ARG, "check_every must be >= 0");
+    sla_csr* A = const_cast<sla_csr*>(Ac);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(A->mu);
+    const bool largest = opts->which == SLA_EIG_LARGEST;
+    const int rp_bits = A->krp_bits;
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    const int G = blocks_per_system(A, ntiles, 1, bs_blocks_per_cu(rp_bits, A->cap, n));
+    const int Gu = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(1024, (n + kBlock - 1) / kBlock)));
+    const int Gd = static_cast<int>((n + kLzRows - 1) / kLzRows);
+
+    // device workspace
+    const size_t sz_V = align256(sizeof(double) * static_cast<size_t>(max_dim + 1) * n);
+    const size_t sz_w = align256(sizeof(double) * n);
+    const size_t sz_ph = align256(sizeof(double) * static_cast<size_t>(max_dim + 1) * Gd);
+    const size_t sz_md = align256(sizeof(double) * (max_dim + 1));
+    const size_t sz_G = align256(sizeof(double) * G);
+    const size_t sz_Gu = align256(sizeof(double) * Gu);
+    const size_t sz_S = align256(sizeof(double) * static_cast<size_t>(k) * max_dim);
+    const size_t sz_k = align256(sizeof(double) * k);
+    const size_t sz_pr = align256(sizeof(double) * 2 * k * Gu);
+    const size_t need = sz_V + sz_w + sz_ph + 3 * sz_md + 2 * sz_G + sz_Gu + sz_S + sz_k + sz_pr +
+                        align256(sizeof(SysState));
+    if (need > A->eig_ws_bytes) {
+        if (A->eig_ws) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipFree(A->eig_ws));
+            A->eig_ws = nullptr;
+            A->eig_ws_bytes = 0;
+        }
+        if ((st = dev_alloc(&A->eig_ws, need)) != SLA_OK) return st;
+        A->eig_ws_bytes = need;
+    }
+    // pinned host staging: alpha, beta, S, theta / scale, partials, state
+    const size_t hneed = sizeof(double) * (2 * max_dim + static_cast<size_t>(k) * max_dim + k + 2 * k * Gu + Gu) +
+                         sizeof(SysState);
+    if (hneed > A->eig_host_bytes) {
+        HIP_TRY(hipStreamSynchronize(s));
+        if (A->eig_host) HIP_TRY(hipHostFree(A->eig_host));
+        A->eig_host = nullptr;
+        A->eig_host_bytes = 0;
+        HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&A->eig_host), hneed, hipHostMallocDefault));
+        A->eig_host_bytes = hneed;
+    }
+    char* p = static_cast<char*>(A->eig_ws);
+    auto take = [&](size_t b) {
+        char* q = p;
+        p += b;
+        return reinterpret_cast<double*>(q);
+    };
+    LzArgs a{};
+    a.V = take(sz_V);
+    a.w = take(sz_w);
+    a.part_h = take(sz_ph);
+    a.h = take(sz_md);
+    a.alpha = take(sz_md);
+    a.beta = take(sz_md);
+    double* part_sigma = take(sz_G);
+    double* part_tt = take(sz_G);
+    a.part = take(sz_Gu);
+    double* d_S = take(sz_S);
+    double* d_scale = take(sz_k);
+    a.part_ritz = take(sz_pr);
+    SysState* d_st = reinterpret_cast<SysState*>(p);
+    a.v0 = d_v0;
+    a.part_sigma = part_sigma;
+    a.S = d_S;
+    a.U = d_evecs;
+    a.scale = d_scale;
+    a.n = n;
+    a.G = G;
+    a.Gu = Gu;
+    a.Gd = Gd;
+    a.k = k;
+    double* h_ab = A->eig_host;                 // alpha [max_dim], beta [max_dim]
+    double* h_S = h_ab + 2 * max_dim;           // [k][m]
+    double* h_theta = h_S + static_cast<size_t>(k) * max_dim;
+    double* h_part = h_theta + k;               // [2 k][Gu] (also the |v0|^2 partials)
+    SysState* h_st = reinterpret_cast<SysState*>(h_part + 2 * k * Gu + Gu);
+
+    // the SpMV (BiCGStab's t = A s mode): operand v_j, product w, partials <v_j, w>
+    CgArgs c{};
+    c.row_ptr = A->krp;
+    c.col = A->col;
+    c.vals = d_vals;
+    c.z = a.w;
+    c.part_sigma = part_sigma;
+    c.part_tt = part_tt;
+    c.st = d_st;
+    c.n = n;
+    c.nnz = A->nnz;
+    c.ntiles = ntiles;
+    c.G = G;
+    c.Gu = Gu;
+    c.batch = 1;
+    c.xcd_remap = 1;
+    c.split = 1;
+    *h_st = SysState{};
+    h_st->stop_iter = INT64_MAX;
+    HIP_TRY(hipMemcpyAsync(d_st, h_st, sizeof(SysState), hipMemcpyHostToDevice, s));
+
+    hipError_t e = timed(SLA_K_LZ_RITZ, s, [&] { return launch_lz(0, a, 0, 0.0, 0, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh start: %s", hipGetErrorString(e));
+    HIP_TRY(hipMemcpyAsync(h_part, a.part, sizeof(double) * Gu, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    double nn = 0.0;
+    for (int g = 0; g < Gu; ++g) nn += h_part[g];
+    const double nrm = std::sqrt(nn);
+    if (!(nrm > 0.0) || !std::isfinite(nrm)) return fail(SLA_ERR_INVALID_ARG, "start vector v0 is zero or not finite");
+    e = timed(SLA_K_LZ_RITZ, s, [&] { return launch_lz(1, a, 0, nrm, 0, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh start: %s", hipGetErrorString(e));
+
+    auto lanczos_step = [&](int64_t j) -> hipError_t {
+        c.p1 = a.V + j * n;
+        hipError_t e0 = timed(SLA_K_LZ_SPMV, s, [&] { return launch_bs(4, c, j, rp_bits, A->cap, s); });
+        if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(2, a, j, 0.0, 0, s); });
+        for (int pass = 0; pass < 2 && e0 == hipSuccess; ++pass) {
+            e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(3, a, j + 1, 0.0, 0, s); });
+            if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(4, a, j + 1, 0.0, 0, s); });
+            if (e0 == hipSuccess)
+                e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(5, a, j + 1, 0.0, pass == 1, s); });
+        }
+        if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(6, a, j, 0.0, 0, s); });
+        return e0;
+    };
+
+    const int64_t chunk = opts->check_every > 0 ? opts->check_every : 16;
+    // beta_j at the rounding level of the reorthogonalized w (<= sqrt(n) eps |T_j|, |T_j|
+    // the largest Gershgorin row sum) means the Krylov space is numerically invariant
+    const double inv_level = std::sqrt(static_cast<double>(n)) * DBL_EPSILON;
+    double tnorm = 0.0;
+    int64_t j = 0, m_stop = -1;
+    int state = SLA_MAX_ITER;
+    double max_res = 0.0;
+    std::vector<double> theta(k), res(k);
+    while (m_stop < 0) {
+        const int64_t j0 = j, jend = std::min<int64_t>(j + chunk, max_dim);
+        for (; j < jend; ++j) {
+            if ((e = lanczos_step(j)) != hipSuccess) return fail(SLA_ERR_HIP, "eigsh step: %s", hipGetErrorString(e));
+        }
+        HIP_TRY(hipMemcpyAsync(h_ab, a.alpha, sizeof(double) * jend, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipMemcpyAsync(h_ab + max_dim, a.beta, sizeof(double) * jend, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        const double* al = h_ab;
+        const double* be = h_ab + max_dim;
+        for (int64_t jj = j0; jj < jend && m_stop < 0; ++jj) {
+            const int64_t m = jj + 1;
+            double b = be[jj];
+            tnorm = std::max(tnorm, std::fabs(al[jj]) + std::fabs(b) + (jj > 0 ? std::fabs(be[jj - 1]) : 0.0));
+            if (b <= inv_level * tnorm) b = 0.0;
+            if (m < k) {
+                if (b == 0.0) {
+                    m_stop = m;
+                    state = SLA_BREAKDOWN;
+                }
+                continue;
+            }
+            tridiag_eigpairs(al, be, static_cast<int>(m), k, largest, theta.data(), h_S);
+            bool done = true;
+            max_res = 0.0;
+            for (int r = 0; r < k; ++r) {
+                res[r] = b * std::fabs(h_S[static_cast<size_t>(r) * m + m - 1]);
+                max_res = std::max(max_res, res[r]);
+                if (!(res[r] <= opts->tol * std::fabs(theta[r]))) done = false;
+            }
+            if (done || b == 0.0) {
+                m_stop = m;
+                state = SLA_CONVERGED;
+            } else if (m == max_dim) {
+                m_stop = m;
+                state = SLA_MAX_ITER;
+            }
+        }
+    }
+    info->iterations = m_stop;
+    info->state = state;
+    info->reserved = 0;
+    if (state == SLA_BREAKDOWN) {
+        info->max_res = 0.0;
+        return SLA_OK;   // d_evals / d_evecs untouched: fewer than k Ritz values exist
+    }
+    info->max_res = max_res;
+    // Ritz vectors of the stopping step: u_r = V_m s_r, then divided by their signed norms
+    a.m = m_stop;
+    HIP_TRY(hipMemcpyAsync(d_S, h_S, sizeof(double) * k * m_stop, hipMemcpyHostToDevice, s));
+    e = timed(SLA_K_LZ_RITZ, s, [&] { return launch_lz(7, a, 0, 0.0, 0, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh ritz: %s", hipGetErrorString(e));
+    HIP_TRY(hipMemcpyAsync(h_part, a.part_ritz, sizeof(double) * 2 * k * Gu, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    for (int r = 0; r < k; ++r) {
+        double uu = 0.0, uv = 0.0;
+        for (int g = 0; g < Gu; ++g) {
+            uu += h_part[static_cast<size_t>(2 * r) * Gu + g];
+            uv += h_part[static_cast<size_t>(2 * r + 1) * Gu + g];
+        }
+        const double nu = std::sqrt(uu);
+        h_theta[r] = uv < 0.0 ? -nu : nu;   // staged as the signed norms first
+    }
+    HIP_TRY(hipMemcpyAsync(d_scale, h_theta, sizeof(double) * k, hipMemcpyHostToDevice, s));
+    e = timed(SLA_K_LZ_RITZ, s, [&] { return launch_lz(8, a, 0, 0.0, 0, s); });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh scale: %s", hipGetErrorString(e));
+    HIP_TRY(hipStreamSynchronize(s));
+    for (int r = 0; r < k; ++r) h_theta[r] = theta[r];
+    HIP_TRY(hipMemcpyAsync(d_evals, h_theta, sizeof(double) * k, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    hipError_t te = timing_collect();
+    if (te != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(te));
+    return SLA_OK;
+}
+
+sla_status sla_eigsh_backward(const sla_csr* Ac, int32_t k, const double* d_evecs, const double* d_gevals,
+                              double* d_gvals, void* stream)
+{
+    sla_status st = check_common(Ac, 1);
+    if (st != SLA_OK) return st;
+    if (k < 1 || k > SLA_EIG_MAX_K) return fail(SLA_ERR_INVALID_ARG, "k must be in [1, %d]", SLA_EIG_MAX_K);
+    if (!d_evecs || !d_gevals || (!d_gvals && Ac->nnz > 0)) return fail(SLA_ERR_INVALID_ARG, "NULL argument");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed(SLA_K_LZ_RITZ, s, [&] {
+        return launch_eig_grad(Ac->krp, Ac->krp_bits, Ac->col, d_evecs, d_gevals, k, Ac->n_rows, Ac->nnz, d_gvals,
+                               s);
+    });
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh backward launch: %s", hipGetErrorString(e));
     return SLA_OK;
 }
 

@@ -106,6 +106,44 @@ struct CgArgs {
     int64_t band_lines;      // banded SpMV: ceil(n / S)
 };
 
+// Lanczos eigensolver (sla_eigsh).  V [max_dim + 1][n]: row j is the Lanczos vector
+// v_j; w [n] the vector being orthogonalized.  Grids: Gu workgroups for the streaming
+// kernels, Gd for the reorthogonalization dots (kLzRows rows each), G for the SpMV.
+constexpr int kLzRows = 1024;      // rows per workgroup of the reorthogonalization dots
+constexpr int kEigMaxK = 32;       // eigenpairs per call, at most
+struct LzArgs {
+    double* V;
+    double* w;
+    const double* v0;        // start vector (caller's)
+    double* part;            // [Gu] norm partials
+    double* part_h;          // [max_dim + 1][Gd] reorthogonalization dot partials
+    double* h;               // [max_dim + 1] reorthogonalization coefficients
+    double* alpha;           // [max_dim] diagonal of T
+    double* beta;            // [max_dim] off-diagonal of T (beta_j = |w| after step j)
+    const double* part_sigma;// [G] the SpMV's partials of <v_j, A v_j>
+    const double* S;         // [k][m] Ritz coefficients (row r: eigenvector r of T)
+    double* U;               // [k][n] Ritz vectors
+    const double* scale;     // [k] signed norms of the Ritz vectors (u_r is divided by it)
+    double* part_ritz;       // [2 k][Gu] partials of <u_r, u_r> and <u_r, v_0>
+    int64_t n;
+    int64_t m;               // Ritz vectors: Krylov dimension
+    int32_t G, Gu, Gd;
+    int32_t k;
+};
+// which: 0 |v0|^2 partials, 1 v_0 = v0 / nrm, 2 three-term step of column j (alpha_j from
+// the SpMV partials), 3 dots of w with columns 0 .. j, 4 their reduction into h, 5 w -=
+// V h (last: with |w|^2 partials), 6 beta_j and v_{j+1}, 7 Ritz vectors with partials,
+// 8 division of the Ritz vectors by their signed norms.
+hipError_t launch_lz(int which, const LzArgs& a, int64_t j, double nrm, int last, hipStream_t s);
+// dL/dvals[e] = sum_r g[r] U[r][row(e)] U[r][col(e)] (Hellmann-Feynman), g and U on the device.
+hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col, const double* U, const double* g,
+                           int k, int64_t n, int64_t nnz, double* gvals, hipStream_t s);
+
+// Wanted eigenpairs of a symmetric tridiagonal matrix (host code, sla_tridiag.hip):
+// diagonal a[0..m), off-diagonal b[0..m-1).  The k largest (descending) or smallest
+// (ascending) eigenvalues into theta[k], unit eigenvectors into S[k][m].
+void tridiag_eigpairs(const double* a, const double* b, int m, int k, bool largest, double* theta, double* S);
+
 // Optional timing events for the next single-kernel launch: when set, launchers use
 // hipExtLaunchKernelGGL so the events carry the kernel's own start and end times.
 struct LaunchEvents {

@@ -1641,6 +1641,222 @@ __global__ __launch_bounds__(kBlock) void k_bs_update(CgArgs a, int64_t k)
 }
 
 // ----------------------------------------------------------------------------------
+// Lanczos eigensolver (the pages' .eigsh: paperpeel page, section 4.3, note to Table 5)
+// with full reorthogonalization.  Step j: w = A v_j with <v_j, w> (the SpMV kernel in
+// its t = A s mode), the three-term step w -= alpha_j v_j + beta_{j-1} v_{j-1}, twice
+// the classical Gram-Schmidt pass w -= V (V^T w) over v_0 .. v_j (dots, their
+// deterministic reduction, the update), then beta_j = |w| and v_{j+1} = w / beta_j.
+// The eigenpairs of the small tridiagonal matrix are taken on the host; the Ritz
+// vectors u_r = sum_l S[r][l] v_l are formed here.  All vectors are rows of V, each
+// contiguous, so every pass is a coalesced stream.
+// ----------------------------------------------------------------------------------
+
+// Value at a workgroup-uniform address, read as a scalar load (read-only data).
+__device__ __forceinline__ double ld_uniform(const double* p, int64_t i)
+{
+    typedef const __attribute__((address_space(4))) double* cptr;
+    return ((cptr)(p))[i];
+}
+
+// Rows of this workgroup's grid-stride walk: i = blockIdx.x * kBlock + tid + t * stride.
+#define LZ_ROWS(i, n)                                                                          \
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < (n);       \
+         i += static_cast<int64_t>(gridDim.x) * kBlock)
+
+__global__ __launch_bounds__(kBlock) void k_lz_norm(LzArgs a)
+{
+    __shared__ double s_red[kBlock / 64];
+    double acc = 0.0;
+    LZ_ROWS(i, a.n) {
+        const double v = a.v0[i];
+        const double t = v * v;
+        acc = acc + t;
+    }
+    acc = block_sum(acc, s_red);
+    if (threadIdx.x == 0) a.part[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kBlock) void k_lz_start(LzArgs a, double nrm)
+{
+    LZ_ROWS(i, a.n) a.V[i] = a.v0[i] / nrm;
+}
+
+// alpha_j = sum of the SpMV partials; w = (w - alpha_j v_j) - beta_{j-1} v_{j-1}.
+__global__ __launch_bounds__(kBlock) void k_lz_three(LzArgs a, int64_t j)
+{
+    __shared__ double s_red[kBlock / 64];
+    const double alpha = reduce_partials(a.part_sigma, a.G, s_red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.alpha[j] = alpha;
+    const double beta = j > 0 ? a.beta[j - 1] : 0.0;
+    const double* __restrict__ vj = a.V + j * a.n;
+    const double* __restrict__ vp = a.V + (j > 0 ? j - 1 : 0) * a.n;
+    double* __restrict__ w = a.w;
+    LZ_ROWS(i, a.n) {
+        const double t1 = alpha * vj[i];
+        double wi = w[i] - t1;
+        if (j > 0) {
+            const double t2 = beta * vp[i];
+            wi = wi - t2;
+        }
+        w[i] = wi;
+    }
+}
+
+// Partial dots <v_c, w> for c < ncols over this workgroup's kLzRows rows: w's slice is
+// staged in LDS once; wave q takes the columns c = q, q + 4, ... and reduces each with
+// shuffles, so no workgroup barrier is paid per column.
+__global__ __launch_bounds__(kBlock) void k_lz_dots(LzArgs a, int64_t ncols)
+{
+    __shared__ double s_w[kLzRows];
+    const int tid = threadIdx.x;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kLzRows;
+    const int nr = static_cast<int>(min(static_cast<int64_t>(kLzRows), a.n - r0));
+    for (int t = tid; t < nr; t += kBlock) s_w[t] = a.w[r0 + t];
+    __syncthreads();
+    const int lane = tid & 63, q = tid >> 6;
+    for (int64_t c = q; c < ncols; c += kBlock / 64) {
+        const double* __restrict__ vc = a.V + c * a.n + r0;
+        double acc = 0.0;
+        for (int t = lane; t < nr; t += 64) {
+            const double p = vc[t] * s_w[t];
+            acc = acc + p;
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) a.part_h[c * a.Gd + blockIdx.x] = acc;
+    }
+}
+
+// h[c] = sum over the Gd partials of column c, in a fixed order.
+__global__ __launch_bounds__(kBlock) void k_lz_reduce(LzArgs a, int64_t ncols)
+{
+    __shared__ double s_red[kBlock / 64];
+    for (int64_t c = blockIdx.x; c < ncols; c += gridDim.x) {
+        const double v = reduce_partials(a.part_h + c * a.Gd, a.Gd, s_red);
+        if (threadIdx.x == 0) a.h[c] = v;
+    }
+}
+
+// w -= sum_c h[c] v_c (c ascending); with last, the partials of |w|^2.
+__global__ __launch_bounds__(kBlock) void k_lz_axpy(LzArgs a, int64_t ncols, int last)
+{
+    __shared__ double s_red[kBlock / 64];
+    double nrm = 0.0;
+    LZ_ROWS(i, a.n) {
+        double acc = 0.0;
+        const double* __restrict__ vc = a.V + i;
+        for (int64_t c = 0; c < ncols; ++c) {
+            const double p = ld_uniform(a.h, c) * vc[c * a.n];
+            acc = acc + p;
+        }
+        const double wi = a.w[i] - acc;
+        a.w[i] = wi;
+        const double t = wi * wi;
+        nrm = nrm + t;
+    }
+    if (last) {
+        nrm = block_sum(nrm, s_red);
+        if (threadIdx.x == 0) a.part[blockIdx.x] = nrm;
+    }
+}
+
+// beta_j = |w|, v_{j+1} = w / beta_j (0 when beta_j = 0: the Krylov space is invariant).
+__global__ __launch_bounds__(kBlock) void k_lz_next(LzArgs a, int64_t j)
+{
+    __shared__ double s_red[kBlock / 64];
+    const double beta = sqrt(reduce_partials(a.part, a.Gu, s_red));
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.beta[j] = beta;
+    double* __restrict__ vn = a.V + (j + 1) * a.n;
+    LZ_ROWS(i, a.n) vn[i] = beta > 0.0 ? a.w[i] / beta : 0.0;
+}
+
+// u_r = sum_l S[r][l] v_l (l ascending) for r < k, with partials of <u_r, u_r> and
+// <u_r, v_0>.  KK >= k accumulators in registers (rows r >= k compute nothing used).
+template <int KK>
+__global__ __launch_bounds__(kBlock) void k_lz_ritz(LzArgs a)
+{
+    __shared__ double s_red[kBlock / 64];
+    double uu[KK], uv[KK];
+#pragma unroll
+    for (int r = 0; r < KK; ++r) uu[r] = uv[r] = 0.0;
+    LZ_ROWS(i, a.n) {
+        double acc[KK];
+#pragma unroll
+        for (int r = 0; r < KK; ++r) acc[r] = 0.0;
+        for (int64_t l = 0; l < a.m; ++l) {
+            const double v = a.V[l * a.n + i];
+#pragma unroll
+            for (int r = 0; r < KK; ++r) {
+                const double p = ld_uniform(a.S, static_cast<int64_t>(r < a.k ? r : 0) * a.m + l) * v;
+                acc[r] = acc[r] + p;
+            }
+        }
+        const double v0 = a.V[i];
+#pragma unroll
+        for (int r = 0; r < KK; ++r) {
+            if (r < a.k) a.U[static_cast<int64_t>(r) * a.n + i] = acc[r];
+            const double t1 = acc[r] * acc[r];
+            uu[r] = uu[r] + t1;
+            const double t2 = acc[r] * v0;
+            uv[r] = uv[r] + t2;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
+        const double su = block_sum(uu[r], s_red);
+        const double sv = block_sum(uv[r], s_red);
+        if (threadIdx.x == 0 && r < a.k) {
+            a.part_ritz[static_cast<int64_t>(2 * r) * a.Gu + blockIdx.x] = su;
+            a.part_ritz[static_cast<int64_t>(2 * r + 1) * a.Gu + blockIdx.x] = sv;
+        }
+    }
+}
+
+// u_r /= scale[r] (the signed norm: normalization and sign in one rounding).
+__global__ __launch_bounds__(kBlock) void k_lz_scale(LzArgs a)
+{
+    LZ_ROWS(i, a.n) {
+        for (int r = 0; r < a.k; ++r) {
+            double* u = a.U + static_cast<int64_t>(r) * a.n + i;
+            *u = *u / ld_uniform(a.scale, r);
+        }
+    }
+}
+#undef LZ_ROWS
+
+// Hellmann-Feynman gradient on the stored entries: gvals[e] = sum_r g[r] U[r][i] U[r][c]
+// for entry e = (i, c), r ascending, each product rounded.  Tile of kTile rows per
+// workgroup, entries walked as in k_pattern_outer.
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_eig_grad(const RP* __restrict__ rp, const int32_t* __restrict__ col,
+                                                     const double* __restrict__ U, const double* __restrict__ g,
+                                                     int k, int64_t n, double* __restrict__ gvals)
+{
+    __shared__ int64_t s_rp[kTile + 1];
+    const int tid = threadIdx.x;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kTile;
+    const int nr = static_cast<int>(min(static_cast<int64_t>(kTile), n - row0));
+    for (int j = tid; j <= nr; j += kBlock) s_rp[j] = ld_rp(rp, row0 + j);
+    __syncthreads();
+    const int64_t k0 = s_rp[0], k1 = s_rp[nr];
+    for (int64_t kk = k0 + tid; kk < k1; kk += kBlock) {
+        int lo = 0, hi = nr;   // s_rp[lo] <= kk < s_rp[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_rp[mid] <= kk) lo = mid;
+            else hi = mid;
+        }
+        const int64_t i = row0 + lo, c = col[kk];
+        double acc = 0.0;
+        for (int r = 0; r < k; ++r) {
+            const double t = U[static_cast<int64_t>(r) * n + i] * U[static_cast<int64_t>(r) * n + c];
+            const double t2 = g[r] * t;
+            acc = acc + t2;
+        }
+        gvals[kk] = acc;
+    }
+}
+
+// ----------------------------------------------------------------------------------
 // Grouped batch (shared-pattern batches on unstructured patterns).  kGroup systems
 // are interleaved element by element: vectors [group][n][kGroup], values
 // [group][nnz][kGroup].  Lane t works on row t / kGroup of its tile for system
@@ -2540,6 +2756,45 @@ hipError_t launch_bs(int which, const CgArgs& a, int64_t k, int rp_bits, int cap
     case 4: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsT>(rp_bits, cap, o), gs, blk, 0, s, a, k); break;
     default: SLA_LAUNCH(k_bs_update, gu, blk, 0, s, a, k); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_lz(int which, const LzArgs& a, int64_t j, double nrm, int last, hipStream_t s)
+{
+    const dim3 gu(a.Gu), blk(kBlock);
+    switch (which) {
+    case 0: SLA_LAUNCH(k_lz_norm, gu, blk, 0, s, a); break;
+    case 1: SLA_LAUNCH(k_lz_start, gu, blk, 0, s, a, nrm); break;
+    case 2: SLA_LAUNCH(k_lz_three, gu, blk, 0, s, a, j); break;
+    case 3: SLA_LAUNCH(k_lz_dots, dim3(a.Gd), blk, 0, s, a, j); break;
+    case 4: SLA_LAUNCH(k_lz_reduce, dim3(static_cast<unsigned>(std::min<int64_t>(j, 1024))), blk, 0, s, a, j);
+        break;
+    case 5: SLA_LAUNCH(k_lz_axpy, gu, blk, 0, s, a, j, last); break;
+    case 6: SLA_LAUNCH(k_lz_next, gu, blk, 0, s, a, j); break;
+    case 7:
+        if (a.k <= 1) SLA_LAUNCH(k_lz_ritz<1>, gu, blk, 0, s, a);
+        else if (a.k <= 2) SLA_LAUNCH(k_lz_ritz<2>, gu, blk, 0, s, a);
+        else if (a.k <= 4) SLA_LAUNCH(k_lz_ritz<4>, gu, blk, 0, s, a);
+        else if (a.k <= 8) SLA_LAUNCH(k_lz_ritz<8>, gu, blk, 0, s, a);
+        else if (a.k <= 16) SLA_LAUNCH(k_lz_ritz<16>, gu, blk, 0, s, a);
+        else SLA_LAUNCH(k_lz_ritz<kEigMaxK>, gu, blk, 0, s, a);
+        break;
+    default: SLA_LAUNCH(k_lz_scale, gu, blk, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col, const double* U, const double* g,
+                           int k, int64_t n, int64_t nnz, double* gvals, hipStream_t s)
+{
+    if (n == 0 || nnz == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((n + kTile - 1) / kTile)), blk(kBlock);
+    if (rp_bits == 64)
+        SLA_LAUNCH(k_eig_grad<int64_t>, grid, blk, 0, s, static_cast<const int64_t*>(row_ptr), col, U, g, k, n,
+                   gvals);
+    else
+        SLA_LAUNCH(k_eig_grad<int32_t>, grid, blk, 0, s, static_cast<const int32_t*>(row_ptr), col, U, g, k, n,
+                   gvals);
     return hipGetLastError();
 }
 

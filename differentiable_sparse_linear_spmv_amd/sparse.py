@@ -20,11 +20,11 @@ import warnings
 import torch
 
 from . import _lib as L
-from ._lib import SlaCgInfo, SlaCgOpts, check
+from ._lib import SlaCgInfo, SlaCgOpts, SlaEigInfo, SlaEigOpts, check
 
 __all__ = [
     "csr_create", "csr_destroy", "csr_info", "csr_analysis", "matvec", "matvec_backward", "solve",
-    "solve_backward", "cg_opts", "read_info", "SparseTensor", "timing",
+    "solve_backward", "cg_opts", "read_info", "eigsh", "eigsh_backward", "SparseTensor", "timing",
 ]
 
 
@@ -222,6 +222,36 @@ def solve_backward(h: Handle, vals: torch.Tensor, x: torch.Tensor, gx: torch.Ten
     return gb, gvals, info
 
 
+def eigsh(h: Handle, vals: torch.Tensor, k: int, v0: torch.Tensor, which: str = "largest",
+          tol: float = 1e-10, max_dim: int = 0, check_every: int = 0):
+    """sla_eigsh: k extreme eigenpairs by Lanczos.  Returns (evals [k], evecs [k, n], info)."""
+    if which not in ("largest", "smallest"):
+        raise ValueError(f"which must be 'largest' or 'smallest' (got {which!r})")
+    _need(vals, "vals", torch.float64, h.nnz, h.device)
+    _need(v0, "v0", torch.float64, h.n_rows, h.device)
+    evals = torch.empty(k, dtype=torch.float64, device=h.device)
+    evecs = torch.empty((k, h.n_rows), dtype=torch.float64, device=h.device)
+    opts = SlaEigOpts(float(tol), int(max_dim), L.SLA_EIG_LARGEST if which == "largest" else L.SLA_EIG_SMALLEST,
+                      int(check_every))
+    info = SlaEigInfo()
+    check(L.load().sla_eigsh(h.ptr, _ptr(vals), int(k), _ptr(v0), _ptr(evals), _ptr(evecs), C.byref(opts),
+                             C.byref(info), _stream(h.device)))
+    return evals, evecs, dict(iterations=info.iterations, max_res=info.max_res, state=info.state,
+                              state_name=L.STATE_NAMES.get(info.state, str(info.state)))
+
+
+def eigsh_backward(h: Handle, evecs: torch.Tensor, gevals: torch.Tensor, gvals: torch.Tensor | None = None):
+    """sla_eigsh_backward: dL/dvals[e] = sum_r gevals[r] u_r[row(e)] u_r[col(e)]."""
+    k = int(gevals.numel())
+    _need(evecs, "evecs", torch.float64, k * h.n_rows, h.device)
+    _need(gevals, "gevals", torch.float64, k, h.device)
+    if gvals is None:
+        gvals = torch.empty(h.nnz, dtype=torch.float64, device=h.device)
+    _need(gvals, "gvals", torch.float64, h.nnz, h.device)
+    check(L.load().sla_eigsh_backward(h.ptr, k, _ptr(evecs), _ptr(gevals), _ptr(gvals), _stream(h.device)))
+    return gvals
+
+
 class timing:
     """Per-kernel HIP-event timing inside the library (for measurement only)."""
 
@@ -270,6 +300,26 @@ class _SolveFn(torch.autograd.Function):
         return None, gvals, (gb if ctx.needs_input_grad[2] else None), None
 
 
+class _EigshFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, A, vals, v0, kw):
+        evals, evecs, info = eigsh(A.handle, vals.detach(), kw["k"], v0.detach(), which=kw["which"],
+                                   tol=kw["tol"], max_dim=kw["max_dim"])
+        A.last_eig_info = info
+        ctx.A = A
+        ctx.save_for_backward(evecs)
+        ctx.mark_non_differentiable(evecs)
+        return evals, evecs
+
+    @staticmethod
+    def backward(ctx, gevals, _gevecs):
+        (evecs,) = ctx.saved_tensors
+        gvals = None
+        if ctx.needs_input_grad[1]:
+            gvals = eigsh_backward(ctx.A.handle, evecs, gevals.contiguous())
+        return None, gvals, None, None
+
+
 class _MatvecFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, A, vals, x):
@@ -302,6 +352,7 @@ class SparseTensor:
         self.shape = (self.handle.n_rows, self.handle.n_cols)
         self.last_info = None
         self.last_backward_info = None
+        self.last_eig_info = None
 
     @property
     def batch(self) -> int:
@@ -323,6 +374,18 @@ class SparseTensor:
                     warnings.warn(f"system {i}: {name} reached max_iter={max_iter} "
                                   f"(|r|/|b| = {s['res_norm'] / max(s['rhs_norm'], 1e-300):.3e})")
         return x
+
+    def eigsh(self, k: int = 6, which: str = "largest", tol: float = 1e-10, max_dim: int = 0,
+              v0: torch.Tensor | None = None):
+        """k extreme eigenpairs (Lanczos); the eigenvalues are differentiable with respect to
+        vals (Hellmann-Feynman), the eigenvectors carry no gradient.  v0: the start vector;
+        by default N(0, 1) from a generator seeded with 0 on the matrix's device.
+        Returns (evals [k], evecs [k, n])."""
+        if v0 is None:
+            gen = torch.Generator(device=self.handle.device).manual_seed(0)
+            v0 = torch.randn(self.handle.n_rows, dtype=torch.float64, device=self.handle.device, generator=gen)
+        kw = dict(k=k, which=which, tol=tol, max_dim=max_dim)
+        return _EigshFn.apply(self, self.vals, v0, kw)
 
     def info(self, backward: bool = False) -> list[dict]:
         buf = self.last_backward_info if backward else self.last_info

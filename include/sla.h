@@ -233,6 +233,64 @@ sla_status sla_solve_backward(const sla_csr* A, int64_t batch, const double* d_v
                               double* d_gvals, const sla_cg_opts* opts, sla_cg_info* d_info,
                               void* stream);
 
+/* ------------------------------------------------------------------ eigenvalues */
+#define SLA_EIG_LARGEST   0   /* the k largest eigenvalues (algebraic), descending */
+#define SLA_EIG_SMALLEST  1   /* the k smallest eigenvalues (algebraic), ascending */
+#define SLA_EIG_MAX_K     32  /* eigenpairs per call, at most */
+
+typedef struct {
+    double tol;                  /* stop when |A u - theta u| <= tol |theta| for every wanted pair (> 0) */
+    int64_t max_dim;             /* Krylov dimension cap, k <= max_dim <= n (0: min(n, 1000)) */
+    int32_t which;               /* SLA_EIG_LARGEST or SLA_EIG_SMALLEST */
+    int32_t check_every;         /* Lanczos steps between host checks (0: 16) */
+} sla_eig_opts;
+
+typedef struct {
+    int64_t iterations;          /* Lanczos steps taken = dimension of the Krylov space used */
+    double max_res;              /* largest residual estimate beta_j |s_r[j]| of the returned pairs */
+    int32_t state;               /* SLA_CONVERGED, SLA_MAX_ITER or SLA_BREAKDOWN */
+    int32_t reserved;
+} sla_eig_info;                  /* host struct */
+
+/*
+ * k extreme eigenpairs of a symmetric matrix by Lanczos with full reorthogonalization
+ * (the pages' .eigsh entry point and its Lanczos eigensolver: paperpeel page, section
+ * 3.1 "API"; section 4.3, note to Table 5).  Batch 1.
+ *   d_vals   [nnz]   values; the handle must be SLA_SYMMETRIC (else SLA_ERR_UNSUPPORTED)
+ *   k        1 <= k <= min(SLA_EIG_MAX_K, max_dim)
+ *   d_v0     [n]     start vector (nonzero; the caller draws it, e.g. N(0,1))
+ *   d_evals  [k]     output: the Ritz values, from the wanted end
+ *   d_evecs  [k][n]  output: unit Ritz vectors, signed so that <u_r, v0> >= 0
+ *   info     host output
+ * Step j: w = A v_j, alpha_j = <v_j, w>, w -= alpha_j v_j + beta_{j-1} v_{j-1}, then
+ * twice w -= V (V^T w) over v_0 .. v_j, beta_j = |w|, v_{j+1} = w / beta_j.  After
+ * every step j + 1 >= k the k wanted Ritz pairs (theta_r, s_r) of the tridiagonal
+ * T_j are tested: converged when every beta_j |s_r[j]| <= tol |theta_r| (or beta_j =
+ * 0: the Krylov space is invariant and the pairs are exact; beta_j counts as 0 when
+ * it is at most sqrt(n) eps |T_j|, |T_j| the largest Gershgorin row sum of T_j with
+ * beta_j, the rounding level of a reorthogonalized w).  The first step that
+ * passes ends the solve (the host checks chunks of steps; the steps past it are
+ * discarded).  max_dim steps without convergence: SLA_MAX_ITER with the current Ritz
+ * pairs.  An invariant Krylov space of dimension < k: SLA_BREAKDOWN.
+ * Memory: (max_dim + 1) n doubles for the Lanczos vectors, owned by the handle.
+ * Synchronises the calling thread with the stream once per chunk of steps.
+ */
+sla_status sla_eigsh(const sla_csr* A, const double* d_vals, int32_t k, const double* d_v0, double* d_evals,
+                     double* d_evecs, const sla_eig_opts* opts, sla_eig_info* info, void* stream);
+
+/*
+ * Backward of the eigenvalues of sla_eigsh by the Hellmann-Feynman theorem
+ * (dlambda / dA_ij = u_i u_j for a unit eigenvector u: gist.science Japanese summary,
+ * Methodology item 2, eigenvalue bullet; paperpeel section 4.3, Eq. (4)): an O(nnz)
+ * outer product on the stored entries, no linear solve.
+ *   d_evecs  [k][n]  the unit eigenvectors returned by sla_eigsh
+ *   d_gevals [k]     dL/dlambda_r
+ *   d_gvals  [nnz]   output: dL/dvals[e] = sum_r dL/dlambda_r u_r[row(e)] u_r[col(e)]
+ * Only eigenvalue gradients: eigenvector outputs carry none.
+ */
+sla_status sla_eigsh_backward(const sla_csr* A, int32_t k, const double* d_evecs, const double* d_gevals,
+                              double* d_gvals, void* stream);
+
 /*
  * Kernel timing for measurement: while enabled, every kernel the library launches
  * is bracketed by HIP events on its stream; the elapsed times are accumulated per
@@ -252,7 +310,10 @@ enum {
     SLA_K_GROUP_LAYOUT = 8, /* grouped batches: values and x between layouts */
     SLA_K_BS_SPMV = 9,      /* BiCGStab: v = A p with <rh, v>, and t = A s with <t, s>, <t, t> */
     SLA_K_BS_VEC = 10,      /* BiCGStab: init, p update, s = r - alpha v, x and r update */
-    SLA_K_COUNT = 11
+    SLA_K_LZ_SPMV = 11,     /* Lanczos: w = A v_j with <v_j, w> */
+    SLA_K_LZ_ORTH = 12,     /* Lanczos: three-term step, reorthogonalization dots and updates, next vector */
+    SLA_K_LZ_RITZ = 13,     /* Lanczos: start vector, Ritz vectors, eigenvalue gradient */
+    SLA_K_COUNT = 14
 };
 sla_status sla_timing_enable(int32_t enable);
 sla_status sla_timing_reset(void);
