@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "fp64 CG iters/s + achieved HBM GB/s, Poisson 1M/169M DOF; solve+adjoint ms"
 # the nonsymmetric widening (not the headline metric): BiCGStab on convection-diffusion
+METRIC_EIGSH = "fp64 Lanczos steps/s + achieved HBM GB/s, eigsh on a 1M-DOF Poisson-type matrix; eigsh+gradient ms"
 METRIC_BICGSTAB = "fp64 BiCGStab iters/s + achieved HBM GB/s, convection-diffusion 1M DOF; solve+adjoint ms"
 COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written
 
@@ -102,6 +103,72 @@ def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
                 flops_iteration=(4 * nnz + 24 * n) * batch)
 
 
+def eigsh_bytes(n: int, nnz: int, rp_bytes: int, steps: int) -> dict:
+    """Algorithmic HBM bytes of a Lanczos run of `steps` steps (Krylov dimension).
+
+      lz_spmv  (per step): values, columns, row pointers + read v_j (the gathers are
+               cache traffic), write w                              -> mat + 2 x 8 n
+      lz_orth  (step j): three-term step (read v_j, v_{j-1}, w; write w) 4 x 8 n;
+               two Gram-Schmidt passes, each: dots read V_{0..j} and w, (j + 2) x 8 n,
+               update read V_{0..j} and w, write w, (j + 3) x 8 n; next vector (read
+               w, write v_{j+1}) 2 x 8 n                            -> (4 j + 16) x 8 n
+      lz_ritz  u_r = V s_r: read V_{0..m-1} once, write k vectors (plus the start)
+    """
+    mat = 8 * nnz + 4 * nnz + rp_bytes * (n + 1)
+    spmv = mat + 2 * 8 * n
+    orth = sum((4 * j + 16) * 8 * n for j in range(steps))
+    return dict(lz_spmv=spmv, lz_orth_total=orth, run=steps * spmv + orth)
+
+
+def run_eigsh(args, w, S, torch) -> dict:
+    """One step = eigsh (k wanted pairs) + the gradient of sum(lambda)."""
+    h = S.csr_create(w["rp"], w["col"], symmetric=True)
+    vals, v0, k = w["vals"], w["v0"], w["k"]
+
+    def step():
+        ev, U, info = S.eigsh(h, vals, k, v0, which=w["which"], tol=w["tol"])
+        gv = S.eigsh_backward(h, U, torch.ones(k, dtype=torch.float64, device=vals.device))
+        return ev, U, gv, info
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    infos = [step()[3] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    steps_run = infos[-1]["iterations"]
+    # per-kernel HIP-event timing of one more run
+    S.timing.reset()
+    S.timing.enable(True)
+    step()
+    S.timing.collect()
+    S.timing.enable(False)
+    tq = S.timing.query()
+    n, nnz = w["n"], w["nnz"]
+    bm = eigsh_bytes(n, nnz, 4, steps_run)
+    orth_ms = tq["lz_orth"]["total_ms"]
+    spmv_ms = tq["lz_spmv"]["total_ms"] / max(tq["lz_spmv"]["launches"], 1)
+    achieved = bm["lz_orth_total"] / (orth_ms * 1e-3) / 1e9
+    return dict(value=sum(i["iterations"] for i in infos) / wall, wall=wall, tq=tq, bm=bm, achieved=achieved,
+                spmv_ms=spmv_ms, orth_ms=orth_ms, info=infos[-1],
+                spmv_gbps=bm["lz_spmv"] / (spmv_ms * 1e-3) / 1e9)
+
+
+def cpu_baseline_eigsh(w, steps: int) -> dict:
+    """The oracle's Lanczos (one thread) for a bounded number of steps of the same problem."""
+    import oracle.eigsh as OE
+    from threadpoolctl import threadpool_limits
+    A = w["host"]["A"]
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=steps)
+    dt = time.perf_counter() - t0
+    return dict(value=round(steps / dt, 3), unit="Lanczos steps/s", cores=1, kind="oracle",
+                sample=f"oracle Lanczos on this workload, the first {steps} steps (dimension cap), "
+                       f"single thread", seconds=round(dt, 2))
+
+
 # ------------------------------------------------------------------------------ workloads
 def make_workload(name: str, device):
     import numpy as np
@@ -120,6 +187,14 @@ def make_workload(name: str, device):
                          f"{c['max_iter']} fixed CG iterations + {c['max_iter']} adjoint")
     c = W.config(name)
     A = c["A"]
+    if c.get("method") == "eigsh":
+        return dict(name=name, n=A.n_rows, nnz=A.nnz, batch=1, rp=torch.from_numpy(A.row_ptr).to(device),
+                    col=torch.from_numpy(A.col).to(device), vals=torch.from_numpy(A.vals).to(device),
+                    v0=torch.from_numpy(c["v0"]).to(device), k=c["k"], which=c["which"], tol=c["tol"],
+                    method="eigsh", host=c,
+                    desc=f"Lanczos eigsh: {c['k']} {c['which']} eigenpairs of the variable-coefficient "
+                         f"Poisson matrix 1024x1024 (kappa=exp(GRF) seed 0), tol {c['tol']}, v0~N(0,1) "
+                         f"seed 3, + Hellmann-Feynman gradient of sum(lambda)")
     B = A.batch
     vals = torch.from_numpy(np.ascontiguousarray(A.vals.reshape(B, A.nnz) if B > 1 else A.vals))
     b = torch.from_numpy(np.ascontiguousarray(c["b"]))
@@ -268,7 +343,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="poisson1024",
                     choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000",
-                             "convdiff1024"])
+                             "convdiff1024", "eigsh_varcoef1024"])
     ap.add_argument("--cpu-iters", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -297,6 +372,35 @@ def main() -> int:
     n, nnz, B = w["n"], w["nnz"], w["batch"]
     rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
     method = w["method"]
+    if method == "eigsh":
+        r = run_eigsh(args, w, S, torch)
+        cpu = cpu_baseline_eigsh(w, 40) if (rank == 0 and not args.no_cpu_baseline) else None
+        out = {
+            "metric": METRIC_EIGSH, "value": round(r["value"], 2), "unit": "Lanczos steps/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * r["wall"] / args.steps, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+            "data": "synthetic",
+            "config": {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "k": w["k"], "which": w["which"],
+                       "tol": w["tol"], "parallelism": "none (1 GPU)", "method": "eigsh"},
+            "lanczos_steps": r["info"]["iterations"], "state": r["info"]["state_name"],
+            "kernels": {kk: {"launches": v["launches"],
+                             "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
+                        for kk, v in r["tq"].items() if v["launches"]},
+            "bytes_model": r["bm"],
+            "lz_spmv_gbps": round(r["spmv_gbps"], 1),
+            "roofline": {"bound": "hbm",
+                         "kernel": "Lanczos reorthogonalization (k_lz_three, k_lz_dots, k_lz_reduce, k_lz_axpy, "
+                                   "k_lz_next), all launches of one run",
+                         "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "traffic_source": "no counter summary",
+                         "bytes_per_launch": None, "bytes_per_run": r["bm"]["lz_orth_total"],
+                         "run_ms": round(r["orth_ms"], 3)},
+            "cpu_baseline": cpu,
+        }
+        if rank == 0:
+            print(json.dumps(out), flush=True)
+        return 0
     bicg = method == "bicgstab"
     h = S.csr_create(w["rp"], w["col"], symmetric=w["symmetric"])
     an = S.csr_analysis(h)

@@ -345,6 +345,9 @@ def config(name: str, scale: int | None = None) -> dict:
     poisson13000   5-point Poisson on 13000 x 13000 (169M unknowns), int64 row
                    pointer, b ~ N(0, 1) (seed 0); 500 fixed CG iterations forward
                    and 500 in the adjoint, loss 0.5 |x|^2.
+    eigsh_varcoef1024  the 8 largest eigenpairs of the varcoef matrix on 1024 x 1024
+                   (kappa = exp(GRF), seed 0) by Lanczos to tol 1e-10 from v0 ~ N(0, 1)
+                   (seed 3), and the Hellmann-Feynman gradient of sum(lambda).
     convdiff1024   nonsymmetric convection-diffusion (:func:`convdiff5`, W = 100) on
                    1024 x 1024, b ~ N(0, 1) (seed 0), BiCGStab to rtol 1e-8 forward and
                    on A^T in the adjoint, loss 0.5 |x|^2.
@@ -378,6 +381,11 @@ def config(name: str, scale: int | None = None) -> dict:
         return dict(name=name, A=A, b=rhs_normal(N * N, 0), rtol=1e-8, atol=0.0,
                     max_iter=100000, fixed=False, loss="half_sq", method="bicgstab",
                     symmetric=False)
+    if name == "eigsh_varcoef1024":
+        N = scale or 1024
+        A, _, _ = varcoef_poisson5(N, seed=0)
+        return dict(name=name, A=A, v0=rhs_normal(N * N, 3), k=8, which="largest", tol=1e-10,
+                    method="eigsh")
     if name == "poisson13000":
         N = scale or 13000
         return dict(name=name, N=N, A=None, b=None, rtol=0.0, atol=0.0, max_iter=500,
