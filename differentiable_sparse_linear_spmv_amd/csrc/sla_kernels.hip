@@ -1714,15 +1714,32 @@ __global__ __launch_bounds__(kBlock) void k_lz_dots(LzArgs a, int64_t ncols)
     for (int t = tid; t < nr; t += kBlock) s_w[t] = a.w[r0 + t];
     __syncthreads();
     const int lane = tid & 63, q = tid >> 6;
-    for (int64_t c = q; c < ncols; c += kBlock / 64) {
-        const double* __restrict__ vc = a.V + c * a.n + r0;
-        double acc = 0.0;
-        for (int t = lane; t < nr; t += 64) {
-            const double p = vc[t] * s_w[t];
-            acc = acc + p;
+    constexpr int kW = kBlock / 64;
+    // four columns per trip (c, c + 4, c + 8, c + 12): four independent load streams
+    constexpr int kC = 4;
+    for (int64_t c = q; c < ncols; c += kC * kW) {
+        const double* __restrict__ v[kC];
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+            const int64_t cu = c + u * kW;
+            v[u] = a.V + (cu < ncols ? cu : c) * a.n + r0;
         }
-        acc = wave_sum(acc);
-        if (lane == 0) a.part_h[c * a.Gd + blockIdx.x] = acc;
+        double acc[kC] = {};
+#pragma unroll 2
+        for (int t = lane; t < nr; t += 64) {
+            const double wt = s_w[t];
+#pragma unroll
+            for (int u = 0; u < kC; ++u) {
+                const double p = v[u][t] * wt;
+                acc[u] = acc[u] + p;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+            const double sum = wave_sum(acc[u]);
+            const int64_t cu = c + u * kW;
+            if (lane == 0 && cu < ncols) a.part_h[cu * a.Gd + blockIdx.x] = sum;
+        }
     }
 }
 
@@ -1741,10 +1758,22 @@ __global__ __launch_bounds__(kBlock) void k_lz_axpy(LzArgs a, int64_t ncols, int
 {
     __shared__ double s_red[kBlock / 64];
     double nrm = 0.0;
+    constexpr int kU = 16;   // loads issued together; the sum stays in ascending c
     LZ_ROWS(i, a.n) {
         double acc = 0.0;
         const double* __restrict__ vc = a.V + i;
-        for (int64_t c = 0; c < ncols; ++c) {
+        int64_t c = 0;
+        for (; c + kU <= ncols; c += kU) {
+            double v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) v[u] = vc[(c + u) * a.n];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const double p = ld_uniform(a.h, c + u) * v[u];
+                acc = acc + p;
+            }
+        }
+        for (; c < ncols; ++c) {
             const double p = ld_uniform(a.h, c) * vc[c * a.n];
             acc = acc + p;
         }
