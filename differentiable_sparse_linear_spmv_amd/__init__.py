@@ -11,10 +11,10 @@ from ._lib import SlaError
 
 _lib.load()
 
-from .sparse import (SparseTensor, cg_opts, csr_analysis, csr_create, csr_destroy,  # noqa: E402
-                     csr_info, eigsh, eigsh_backward, matvec, matvec_backward, read_info, solve,
-                     solve_backward, timing)
+from .sparse import (SparseTensor, SparseTensorList, cg_opts, csr_analysis, csr_create,  # noqa: E402
+                     csr_destroy, csr_info, eigsh, eigsh_backward, list_create, list_solve,
+                     list_solve_backward, matvec, matvec_backward, read_info, solve, solve_backward, timing)
 
-__all__ = ["SparseTensor", "SlaError", "cg_opts", "csr_analysis", "csr_create", "csr_destroy", "csr_info",
-           "eigsh", "eigsh_backward", "matvec", "matvec_backward", "read_info", "solve", "solve_backward",
-           "timing"]
+__all__ = ["SparseTensor", "SparseTensorList", "SlaError", "cg_opts", "csr_analysis", "csr_create", "csr_destroy",
+           "csr_info", "eigsh", "eigsh_backward", "list_create", "list_solve", "list_solve_backward", "matvec",
+           "matvec_backward", "read_info", "solve", "solve_backward", "timing"]

@@ -32,7 +32,8 @@ KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "g
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
-    "sla_solve", "sla_solve_backward", "sla_eigsh", "sla_eigsh_backward", "sla_timing_enable", "sla_timing_reset",
+    "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_solve",
+    "sla_list_solve_backward", "sla_eigsh", "sla_eigsh_backward", "sla_timing_enable", "sla_timing_reset",
     "sla_timing_collect", "sla_timing_query", "sla_status_string", "sla_last_error", "sla_version",
 ]
 
@@ -105,6 +106,16 @@ def load():
     L.sla_solve.restype = st
     L.sla_solve_backward.argtypes = [P, i64, P, P, P, P, P, C.POINTER(SlaCgOpts), P, P]
     L.sla_solve_backward.restype = st
+    L.sla_list_create.argtypes = [C.POINTER(P), i32, P, P, P, i32, P, u32, P]
+    L.sla_list_create.restype = st
+    L.sla_list_destroy.argtypes = [P]
+    L.sla_list_destroy.restype = st
+    L.sla_list_info.argtypes = [P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i32)]
+    L.sla_list_info.restype = st
+    L.sla_list_solve.argtypes = [P, P, P, P, C.POINTER(SlaCgOpts), P, P]
+    L.sla_list_solve.restype = st
+    L.sla_list_solve_backward.argtypes = [P, P, P, P, P, P, C.POINTER(SlaCgOpts), P, P]
+    L.sla_list_solve_backward.restype = st
     L.sla_eigsh.argtypes = [P, P, i32, P, P, P, C.POINTER(SlaEigOpts), C.POINTER(SlaEigInfo), P]
     L.sla_eigsh.restype = st
     L.sla_eigsh_backward.argtypes = [P, i32, P, P, P, P]

@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -72,6 +73,26 @@ struct sla_csr {
     double* eig_host = nullptr;
     size_t eig_host_bytes = 0;
     hipEvent_t poll_ev[2] = {nullptr, nullptr};
+    std::mutex mu;
+};
+
+// SparseTensorList: items with distinct patterns packed block-diagonally into one
+// pattern, each item's rows starting on a tile boundary.
+struct sla_list {
+    int32_t items = 0;
+    uint32_t flags = 0;
+    int device = 0;
+    std::vector<int64_t> n, nnz, r0, e0;   // per item: rows, entries, first packed row / entry
+    int64_t n_total = 0, nnz_total = 0;
+    sla_csr* packed = nullptr;             // handle of the packed pattern
+    void* rp = nullptr;                    // owned packed row pointers (32- or 64-bit)
+    int32_t* col = nullptr;                // owned packed columns
+    int32_t* d_wg = nullptr;               // per-system tables (ListPlan)
+    int64_t* d_tiles = nullptr;
+    int64_t* d_rend = nullptr;
+    int32_t total_wg = 0;
+    double* stage = nullptr;               // packed values, three packed vectors, packed gradient
+    size_t stage_bytes = 0;
     std::mutex mu;
 };
 
@@ -240,18 +261,21 @@ enum Method { kMethodCG = 0, kMethodJacobi = 1, kMethodBiCGStab = 2 };
 constexpr int kWsVectors[3] = {4, 6, 5};
 constexpr int kWsPartials[3] = {2, 4, 5};
 
-size_t workspace_bytes(int64_t n, int64_t batch, int G, int method)
+size_t workspace_bytes(int64_t n, int64_t batch, int G, int method, int64_t nstate)
 {
     const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
-    return kWsVectors[method] * vec + kWsPartials[method] * part + align256(sizeof(SysState) * batch) + 256;
+    return kWsVectors[method] * vec + kWsPartials[method] * part + align256(sizeof(SysState) * nstate) + 256;
 }
 
-// G: the larger of the two grids (every partial array gets room for it).
-sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int method = kMethodCG)
+// G: the larger of the two grids (every partial array gets room for it).  nstate: the
+// number of systems (batch, or the items of a SparseTensorList; < 0: batch).
+sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int method = kMethodCG,
+                            int64_t nstate = -1)
 {
     const int64_t n = A->n_rows;
-    const size_t need = workspace_bytes(n, batch, G, method);
+    if (nstate < 0) nstate = batch;
+    const size_t need = workspace_bytes(n, batch, G, method, nstate);
     if (need > A->ws_bytes) {
         if (A->ws) {
             HIP_TRY(hipDeviceSynchronize());
@@ -281,7 +305,7 @@ sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int 
     w->part_aux = part_at(3);
     w->part_tt = part_at(4);
     w->st = reinterpret_cast<SysState*>(p + nv * vec + np * part);
-    w->n_active = reinterpret_cast<int32_t*>(p + nv * vec + np * part + align256(sizeof(SysState) * batch));
+    w->n_active = reinterpret_cast<int32_t*>(p + nv * vec + np * part + align256(sizeof(SysState) * nstate));
     return SLA_OK;
 }
 
@@ -480,14 +504,27 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     return SLA_OK;
 }
 
+// SparseTensorList: per-system tables of the packed block-diagonal pattern (device
+// arrays) and its one-dimensional grid, shared by every kernel of the solve.
+struct ListPlan {
+    const int32_t* wg;      // [items + 1] first workgroup of each system
+    const int64_t* tiles;   // [items + 1] first tile of each system
+    const int64_t* rend;    // [items] end of each system's real rows
+    int32_t items;
+    int32_t total_wg;
+};
+
 // band > 0: the pattern is banded with line stride `band` and takes the line-walking
 // SpMV (LDS variant band_cap) on a persistent grid over blocks of lines of one strip.
+// list: a SparseTensorList solve on the packed pattern (batch 1, plain or split SpMV).
 sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t band, int band_cap,
                   bool split, int64_t batch, const double* vals, const double* b, double* x, const sla_cg_opts* o,
-                  sla_cg_info* info, hipStream_t s)
+                  sla_cg_info* info, hipStream_t s, const ListPlan* list = nullptr)
 {
     const bool jacobi = (o->flags & SLA_JACOBI) != 0;
-    if (!jacobi && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 && A->krp_bits == 32 &&
+    if (list) band = 0;
+    if (!list && !jacobi && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 &&
+        A->krp_bits == 32 &&
         A->group_ok &&
         static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapLarge && row_ptr == A->krp)
         return run_cg_grouped(A, row_ptr, col, batch, vals, b, x, o, info, s);
@@ -524,8 +561,10 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         Gu = static_cast<int>(std::max<int64_t>(8, std::min<int64_t>(Gp, g)));
         if (Gu > ntiles) Gu = Gp;
     }
+    if (list) G = Gu = list->total_wg;   // one grid and one partial slot per workgroup
     Workspace w;
-    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi ? kMethodJacobi : kMethodCG);
+    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi ? kMethodJacobi : kMethodCG,
+                                     list ? list->items : -1);
     if (st != SLA_OK) return st;
 
     CgArgs a{};
@@ -569,6 +608,14 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.band_block = band_block;
     a.band_stride = band;
     a.band_lines = band_lines;
+    if (list) {
+        a.list_wg = list->wg;
+        a.list_tiles = list->tiles;
+        a.list_rend = list->rend;
+        a.list_items = list->items;
+        a.sys_per_xcd = 0;
+        a.xcd_remap = 0;
+    }
     const int rp_bits = A->krp_bits;   // A and its transpose use the same row-pointer width
 
     hipError_t e = hipSuccess;
@@ -1223,6 +1270,278 @@ sla_status sla_eigsh_backward(const sla_csr* Ac, int32_t k, const double* d_evec
                                s);
     });
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh backward launch: %s", hipGetErrorString(e));
+    return SLA_OK;
+}
+
+sla_status sla_list_destroy(sla_list* L)
+{
+    if (!L) return SLA_OK;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (prev != L->device) (void)hipSetDevice(L->device);
+    (void)hipDeviceSynchronize();
+    if (L->packed) (void)sla_csr_destroy(L->packed);
+    if (L->rp) (void)hipFree(L->rp);
+    if (L->col) (void)hipFree(L->col);
+    if (L->d_wg) (void)hipFree(L->d_wg);
+    if (L->d_tiles) (void)hipFree(L->d_tiles);
+    if (L->d_rend) (void)hipFree(L->d_rend);
+    if (L->stage) (void)hipFree(L->stage);
+    if (prev >= 0 && prev != L->device) (void)hipSetDevice(prev);
+    delete L;
+    return SLA_OK;
+}
+
+sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, const int64_t* nnz,
+                           const void* const* d_row_ptr, int32_t row_ptr_bits, const int32_t* const* d_col,
+                           uint32_t flags, void* stream)
+{
+    if (!out) return fail(SLA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (items < 1 || items > (1 << 20)) return fail(SLA_ERR_INVALID_ARG, "items must be in [1, 2^20] (got %d)", items);
+    if (!n || !nnz || !d_row_ptr || !d_col) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    if (row_ptr_bits != 32 && row_ptr_bits != 64) return fail(SLA_ERR_INVALID_ARG, "row_ptr_bits must be 32 or 64");
+    if (flags & ~(SLA_SYMMETRIC | SLA_EAGER_TRANSPOSE)) return fail(SLA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_ptr<sla_list> L(new (std::nothrow) sla_list);
+    if (!L) return fail(SLA_ERR_OOM, "host allocation failed");
+    HIP_TRY(hipGetDevice(&L->device));
+    L->items = items;
+    L->flags = flags;
+    int64_t tiles = 0, ents = 0;
+    std::vector<int64_t> tile0(items + 1), rend(items);
+    for (int32_t i = 0; i < items; ++i) {
+        if (n[i] < 1 || nnz[i] < 0 || !d_row_ptr[i] || (nnz[i] > 0 && !d_col[i]))
+            return fail(SLA_ERR_INVALID_ARG, "item %d: n must be >= 1, nnz >= 0, arrays non-NULL", i);
+        if (row_ptr_bits == 32 && nnz[i] >= (int64_t(1) << 31))
+            return fail(SLA_ERR_INVALID_ARG, "item %d: nnz does not fit 32-bit row pointers", i);
+        L->n.push_back(n[i]);
+        L->nnz.push_back(nnz[i]);
+        L->r0.push_back(tiles * kTile);
+        L->e0.push_back(ents);
+        tile0[i] = tiles;
+        rend[i] = tiles * kTile + n[i];
+        tiles += (n[i] + kTile - 1) / kTile;
+        ents += nnz[i];
+    }
+    tile0[items] = tiles;
+    L->n_total = tiles * kTile;
+    L->nnz_total = ents;
+    if (L->n_total >= (int64_t(1) << 31)) return fail(SLA_ERR_UNSUPPORTED, "packed rows exceed 2^31");
+    // each item's own pattern is checked first: a column of one item must not reach
+    // into another item's rows
+    int32_t* d_chk = nullptr;
+    sla_status st = dev_alloc(reinterpret_cast<void**>(&d_chk), sizeof(int32_t) * kChkCount * items);
+    if (st != SLA_OK) return st;
+    std::vector<int32_t> h_chk(static_cast<size_t>(kChkCount) * items);
+    for (int32_t i = 0; i < items; ++i) {
+        int32_t* c = &h_chk[static_cast<size_t>(kChkCount) * i];
+        c[kChkErr] = 0, c[kChkTileMax] = 0, c[kChkRowMax] = 0, c[kChkFarMin] = INT32_MAX, c[kChkFarMax] = 0;
+    }
+    hipError_t e = hipMemcpyAsync(d_chk, h_chk.data(), sizeof(int32_t) * h_chk.size(), hipMemcpyHostToDevice, s);
+    for (int32_t i = 0; i < items && e == hipSuccess; ++i)
+        e = launch_validate(d_row_ptr[i], row_ptr_bits, d_col[i], n[i], n[i], nnz[i], d_chk + kChkCount * i, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h_chk.data(), d_chk, sizeof(int32_t) * h_chk.size(), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    (void)hipFree(d_chk);
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "list validation: %s", hipGetErrorString(e));
+    for (int32_t i = 0; i < items; ++i)
+        if (h_chk[static_cast<size_t>(kChkCount) * i + kChkErr] != 0)
+            return fail(SLA_ERR_INVALID_CSR, "item %d: malformed CSR pattern (code %d)", i,
+                        h_chk[static_cast<size_t>(kChkCount) * i + kChkErr]);
+    // packed pattern
+    const int out_bits = ents < (int64_t(1) << 31) ? 32 : 64;
+    if ((st = dev_alloc(&L->rp, static_cast<size_t>(L->n_total + 1) * (out_bits / 8))) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&L->col), std::max<size_t>(4, 4 * static_cast<size_t>(ents)))) !=
+        SLA_OK)
+        return st;
+    for (int32_t i = 0; i < items; ++i) {
+        const int64_t rows_padded = (tile0[i + 1] - tile0[i]) * kTile;
+        e = launch_pack_pattern(d_row_ptr[i], row_ptr_bits, d_col[i], n[i], nnz[i], L->r0[i], L->e0[i], rows_padded,
+                                L->rp, out_bits, L->col, s);
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "list packing: %s", hipGetErrorString(e));
+    }
+    if ((st = sla_csr_create(&L->packed, L->n_total, L->n_total, ents, L->rp, out_bits, L->col, flags, stream)) !=
+        SLA_OK)
+        return st;
+    L->packed->band = 0;          // the list solve runs the plain or split SpMV
+    L->packed->group_ok = false;
+    // workgroups per item, in proportion to its tiles (at least one each), for a grid
+    // that fills the GPU about once
+    const int per_cu = cg_blocks_per_cu(L->packed->krp_bits, L->packed->cap, L->n_total, L->packed->split);
+    const double target = static_cast<double>(L->packed->n_cu) * per_cu;
+    std::vector<int32_t> wg(items + 1);
+    int64_t acc = 0;
+    for (int32_t i = 0; i < items; ++i) {
+        wg[i] = static_cast<int32_t>(acc);
+        const int64_t ti = tile0[i + 1] - tile0[i];
+        const int64_t gi = std::max<int64_t>(
+            1, std::min<int64_t>(ti, static_cast<int64_t>(std::llround(target * ti / static_cast<double>(tiles)))));
+        acc += gi;
+    }
+    if (acc >= (int64_t(1) << 31)) return fail(SLA_ERR_UNSUPPORTED, "too many workgroups");
+    wg[items] = static_cast<int32_t>(acc);
+    L->total_wg = static_cast<int32_t>(acc);
+    if ((st = dev_alloc(reinterpret_cast<void**>(&L->d_wg), sizeof(int32_t) * (items + 1))) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&L->d_tiles), sizeof(int64_t) * (items + 1))) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&L->d_rend), sizeof(int64_t) * items)) != SLA_OK) return st;
+    HIP_TRY(hipMemcpyAsync(L->d_wg, wg.data(), sizeof(int32_t) * (items + 1), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(L->d_tiles, tile0.data(), sizeof(int64_t) * (items + 1), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(L->d_rend, rend.data(), sizeof(int64_t) * items, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    *out = L.release();
+    return SLA_OK;
+}
+
+sla_status sla_list_info(const sla_list* L, int64_t* n_total, int64_t* nnz_total, int32_t* workgroups)
+{
+    if (!L) return fail(SLA_ERR_INVALID_ARG, "list is NULL");
+    if (n_total) *n_total = L->n_total;
+    if (nnz_total) *nnz_total = L->nnz_total;
+    if (workgroups) *workgroups = L->total_wg;
+    return SLA_OK;
+}
+
+namespace {
+
+// Staging of a list solve: packed values, three packed vectors, packed gradient.
+sla_status list_stage(sla_list* L, bool want_grad, double** vals, double** v0, double** v1, double** v2,
+                      double** gv)
+{
+    const size_t sv = align256(sizeof(double) * std::max<int64_t>(L->nnz_total, 1));
+    const size_t sn = align256(sizeof(double) * L->n_total);
+    const size_t need = 2 * sv + 3 * sn;
+    if (need > L->stage_bytes) {
+        if (L->stage) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipFree(L->stage));
+            L->stage = nullptr;
+            L->stage_bytes = 0;
+        }
+        sla_status st = dev_alloc(reinterpret_cast<void**>(&L->stage), need);
+        if (st != SLA_OK) return st;
+        L->stage_bytes = need;
+    }
+    char* p = reinterpret_cast<char*>(L->stage);
+    *vals = reinterpret_cast<double*>(p);
+    *v0 = reinterpret_cast<double*>(p + sv);
+    *v1 = reinterpret_cast<double*>(p + sv + sn);
+    *v2 = reinterpret_cast<double*>(p + sv + 2 * sn);
+    *gv = want_grad ? reinterpret_cast<double*>(p + sv + 3 * sn) : nullptr;
+    return SLA_OK;
+}
+
+// Copy each item's values / vector into the packed layout (vectors zero-padded).
+sla_status list_pack(const sla_list* L, const double* const* items, double* out, bool values, hipStream_t s)
+{
+    if (!values) HIP_TRY(hipMemsetAsync(out, 0, sizeof(double) * L->n_total, s));
+    for (int32_t i = 0; i < L->items; ++i) {
+        const int64_t cnt = values ? L->nnz[i] : L->n[i];
+        if (cnt == 0) continue;
+        if (!items[i]) return fail(SLA_ERR_INVALID_ARG, "item %d: NULL array", i);
+        HIP_TRY(hipMemcpyAsync(out + (values ? L->e0[i] : L->r0[i]), items[i], sizeof(double) * cnt,
+                               hipMemcpyDeviceToDevice, s));
+    }
+    return SLA_OK;
+}
+
+sla_status list_unpack(const sla_list* L, const double* in, double* const* items, bool values, hipStream_t s)
+{
+    for (int32_t i = 0; i < L->items; ++i) {
+        const int64_t cnt = values ? L->nnz[i] : L->n[i];
+        if (cnt == 0) continue;
+        if (!items[i]) return fail(SLA_ERR_INVALID_ARG, "item %d: NULL output", i);
+        HIP_TRY(hipMemcpyAsync(items[i], in + (values ? L->e0[i] : L->r0[i]), sizeof(double) * cnt,
+                               hipMemcpyDeviceToDevice, s));
+    }
+    return SLA_OK;
+}
+
+ListPlan plan_of(const sla_list* L)
+{
+    return ListPlan{L->d_wg, L->d_tiles, L->d_rend, L->items, L->total_wg};
+}
+
+sla_status check_list(const sla_list* L, const sla_cg_opts* opts)
+{
+    if (!L) return fail(SLA_ERR_INVALID_ARG, "list is NULL");
+    sla_status st = check_opts(opts);
+    if (st != SLA_OK) return st;
+    if (opts->flags & SLA_BICGSTAB) return fail(SLA_ERR_UNSUPPORTED, "list solves take CG or Jacobi CG only");
+    return check_device(L->packed);
+}
+
+}  // namespace
+
+sla_status sla_list_solve(const sla_list* Lc, const double* const* d_vals, const double* const* d_b,
+                          double* const* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream)
+{
+    sla_status st = check_list(Lc, opts);
+    if (st != SLA_OK) return st;
+    if (!d_vals || !d_b || !d_x || !d_info) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    sla_list* L = const_cast<sla_list*>(Lc);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(L->mu);
+    std::lock_guard<std::mutex> lk2(L->packed->mu);
+    double *vals, *b, *x, *unused, *gv;
+    if ((st = list_stage(L, false, &vals, &b, &x, &unused, &gv)) != SLA_OK) return st;
+    if ((st = list_pack(L, d_vals, vals, true, s)) != SLA_OK) return st;
+    if ((st = list_pack(L, d_b, b, false, s)) != SLA_OK) return st;
+    sla_csr* A = L->packed;
+    const ListPlan plan = plan_of(L);
+    st = run_cg(A, A->krp, A->col, A->cap, 0, 0, A->split, 1, vals, b, x, opts, d_info, s, &plan);
+    if (st != SLA_OK) return st;
+    if ((st = list_unpack(L, x, d_x, false, s)) != SLA_OK) return st;
+    if (!(opts->flags & SLA_FIXED_ITERS)) {
+        hipError_t e = timing_collect();
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
+    }
+    return SLA_OK;
+}
+
+sla_status sla_list_solve_backward(const sla_list* Lc, const double* const* d_vals, const double* const* d_x,
+                                   const double* const* d_gx, double* const* d_gb, double* const* d_gvals,
+                                   const sla_cg_opts* opts, sla_cg_info* d_info, void* stream)
+{
+    sla_status st = check_list(Lc, opts);
+    if (st != SLA_OK) return st;
+    if (!d_vals || !d_gx || !d_gb || !d_info || (d_gvals && !d_x)) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    sla_list* L = const_cast<sla_list*>(Lc);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(L->mu);
+    std::lock_guard<std::mutex> lk2(L->packed->mu);
+    double *vals, *g, *lam, *xp, *gv;
+    if ((st = list_stage(L, d_gvals != nullptr, &vals, &g, &lam, &xp, &gv)) != SLA_OK) return st;
+    if ((st = list_pack(L, d_vals, vals, true, s)) != SLA_OK) return st;
+    if ((st = list_pack(L, d_gx, g, false, s)) != SLA_OK) return st;
+    sla_csr* A = L->packed;
+    const ListPlan plan = plan_of(L);
+    if (A->flags & SLA_SYMMETRIC) {
+        st = run_cg(A, A->krp, A->col, A->cap, 0, 0, A->split, 1, vals, g, lam, opts, d_info, s, &plan);
+    } else {
+        // the transpose of the block-diagonal packed pattern is block-diagonal on the
+        // same row blocks, so the same plan applies
+        if ((st = ensure_transpose(A, s)) != SLA_OK) return st;
+        const double* vt = nullptr;
+        if ((st = ensure_vals_t(A, 1, vals, s, &vt)) != SLA_OK) return st;
+        st = run_cg(A, A->row_ptr_t, A->col_t, A->cap_t, 0, 0, A->split, 1, vt, g, lam, opts, d_info, s, &plan);
+    }
+    if (st != SLA_OK) return st;
+    if ((st = list_unpack(L, lam, d_gb, false, s)) != SLA_OK) return st;
+    if (d_gvals) {
+        if ((st = list_pack(L, d_x, xp, false, s)) != SLA_OK) return st;
+        hipError_t e = timed(SLA_K_PATTERN_OUTER, s, [&] {
+            return launch_pattern_outer(A->krp, A->krp_bits, A->col, -1.0, lam, A->n_rows, xp, A->n_cols, gv,
+                                        A->n_rows, A->nnz, 1, s);
+        });
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "gradient scatter launch: %s", hipGetErrorString(e));
+        if ((st = list_unpack(L, gv, d_gvals, true, s)) != SLA_OK) return st;
+    }
+    if (!(opts->flags & SLA_FIXED_ITERS)) {
+        hipError_t e = timing_collect();
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
+    }
     return SLA_OK;
 }
 

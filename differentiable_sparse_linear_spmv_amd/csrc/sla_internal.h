@@ -101,6 +101,14 @@ struct CgArgs {
     int32_t groups;          // grouped batch: number of groups (r, p0, p1, q, vals, xg grouped)
     int32_t cap;             // grouped batch: entries per tile staged (kGCapSmall or kGCapLarge)
     double* xg;              // grouped batch: x in the grouped layout
+    // SparseTensorList (distinct patterns, packed block-diagonally; null otherwise):
+    // system s owns tiles [list_tiles[s], list_tiles[s + 1]) and workgroups
+    // [list_wg[s], list_wg[s + 1]) of a one-dimensional grid (the same for every kernel);
+    // its real rows end at list_rend[s] (the rest of its last tile is padding).
+    const int32_t* list_wg;
+    const int64_t* list_tiles;
+    const int64_t* list_rend;
+    int32_t list_items;
     int32_t band_block;      // banded SpMV: lines per block of work
     int64_t band_stride;     // banded SpMV: line length S (0: plain SpMV)
     int64_t band_lines;      // banded SpMV: ceil(n / S)
@@ -172,6 +180,13 @@ hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s);
 // r in a.r, p in a.p0, v in a.q, s in a.p1, t in a.z; rh = b.
 hipError_t launch_bs(int which, const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s);
 int bs_blocks_per_cu(int rp_bits, int cap, int64_t n);   // the BiCGStab SpMV (t = A s variant)
+
+// SparseTensorList packing: item pattern (row_ptr of rp_bits, col) with n rows and nnz
+// entries into the packed pattern at row r0 and entry e0, its rows padded with empty
+// rows up to r0 + rows_padded; columns shifted by r0.  out_rp has the packed width.
+hipError_t launch_pack_pattern(const void* rp, int rp_bits, const int32_t* col, int64_t n, int64_t nnz, int64_t r0,
+                               int64_t e0, int64_t rows_padded, void* out_rp, int out_bits, int32_t* out_col,
+                               hipStream_t s);
 
 hipError_t launch_matvec(const void* row_ptr, int rp_bits, const int32_t* col, const double* vals,
                          const double* x, double* y, int64_t n_rows, int64_t nnz, int64_t n_cols,

@@ -124,6 +124,19 @@ struct BlockCoord {
 
 __device__ __forceinline__ BlockCoord block_coord(const CgArgs& a, int G)
 {
+    if (a.list_wg) {
+        // SparseTensorList: system of workgroup L by binary search in the workgroup table
+        const int64_t L = blockIdx.x;
+        int lo = 0, hi = a.list_items;   // list_wg[lo] <= L < list_wg[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.list_wg[mid] <= L) lo = mid;
+            else hi = mid;
+        }
+        const int32_t g0 = a.list_wg[lo], gi = a.list_wg[lo + 1] - g0;
+        const int64_t t0 = a.list_tiles[lo];
+        return BlockCoord{lo, static_cast<int>(L - g0), TileRange{t0, a.list_tiles[lo + 1] - t0, L - g0, gi}};
+    }
     if (a.sys_per_xcd) {
         const int64_t L = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
         const int x = static_cast<int>(L & 7);
@@ -134,6 +147,33 @@ __device__ __forceinline__ BlockCoord block_coord(const CgArgs& a, int G)
     }
     return BlockCoord{static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.x),
                       tile_range(G, a.ntiles, a.xcd_remap)};
+}
+
+// Partial-sum slots of system sys when each system has G workgroups (a table in list
+// mode), and the offsets of its vectors and values.
+struct Parts {
+    int64_t base;
+    int count;
+};
+__device__ __forceinline__ Parts parts_of(const CgArgs& a, int sys, int G)
+{
+    if (a.list_wg) {
+        const int64_t lo = a.list_wg[sys];
+        return Parts{lo, static_cast<int>(a.list_wg[sys + 1] - lo)};
+    }
+    return Parts{static_cast<int64_t>(sys) * G, G};
+}
+__device__ __forceinline__ int64_t vec_off(const CgArgs& a, int sys)
+{
+    return a.list_wg ? 0 : static_cast<int64_t>(sys) * a.n;
+}
+__device__ __forceinline__ int64_t val_off(const CgArgs& a, int sys)
+{
+    return a.list_wg ? 0 : static_cast<int64_t>(sys) * a.nnz;
+}
+__device__ __forceinline__ double reduce_parts(const double* part, Parts p, double* s_red)
+{
+    return reduce_partials(part + p.base, p.count, s_red);
 }
 
 template <typename RP>
@@ -316,7 +356,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
     const int tid = threadIdx.x;
     const int lb = bc.lb;
     const TileRange tr = bc.tr;
-    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t off = vec_off(a, sys);
     const double* __restrict__ b = a.b + off;
     double* __restrict__ x = a.x + off;
     double* __restrict__ pm1 = a.p1 + off;   // p_{-1} = 0
@@ -350,15 +390,16 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(CgArgs a)
     }
     rr = block_sum(rr, s_red);
     if (jac) rz = block_sum(rz, s_red);
+    const int64_t slot = parts_of(a, sys, a.Gu).base + lb;
     if (tid == 0) {
         if (jac) {
-            a.part_rr[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
-            a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rz;
+            a.part_rr[slot] = rr;
+            a.part_rho[slot] = rz;
         } else {
-            a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+            a.part_rho[slot] = rr;
         }
         if (lb == 0) a.st[sys].stop_iter = INT64_MAX;
-        if (lb == 0 && sys == 0) *a.n_active = a.batch;
+        if (lb == 0 && sys == 0) *a.n_active = a.list_wg ? a.list_items : a.batch;
     }
 }
 
@@ -386,12 +427,15 @@ __global__ __launch_bounds__(kBlock) void k_cg_diag(CgArgs a)
     const int tid = threadIdx.x;
     const TileRange tr = bc.tr;
     const RP* __restrict__ rp = static_cast<const RP*>(a.row_ptr);
-    const double* __restrict__ vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
-    double* __restrict__ dg = a.dg + static_cast<int64_t>(sys) * a.n;
+    const double* __restrict__ vals = a.vals + val_off(a, sys);
+    double* __restrict__ dg = a.dg + vec_off(a, sys);
+    // list mode: the padding rows of the system's last tile take d = 1 (r = 0 there)
+    const int64_t rend = a.list_wg ? a.list_rend[sys] : a.n;
     double flag = 0.0;
     for (int64_t m = tr.first; m < tr.len; m += tr.step) {
         const int64_t i = (tr.lo + m) * kTile + tid;
-        if (i < a.n) {
+        if (i >= rend && i < a.n) dg[i] = 1.0;
+        if (i < rend) {
             int64_t lo = ld_rp(rp, i), hi = ld_rp(rp, i + 1);
             while (lo < hi) {
                 const int64_t mid = (lo + hi) >> 1;
@@ -405,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_diag(CgArgs a)
         }
     }
     flag = block_max(flag, s_red);
-    if (tid == 0) a.part_aux[static_cast<int64_t>(sys) * a.Gu + bc.lb] = flag;
+    if (tid == 0) a.part_aux[parts_of(a, sys, a.Gu).base + bc.lb] = flag;
 }
 
 // Start of a CG SpMV launch for system sys at iteration k: read the stop word, sum
@@ -450,12 +494,13 @@ __device__ __forceinline__ int cg_step_begin(const CgArgs& a, int sys, int lb, i
     // reduction), so the exit decision is uniform even while this kernel's leading
     // workgroup may be writing stop_iter = k.
     if (tid == 0) *s_stop = st->stop_iter;
-    const double rho_k = reduce_partials(a.part_rho + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red);
+    const Parts pu = parts_of(a, sys, a.Gu);
+    const double rho_k = reduce_parts(a.part_rho, pu, s_red);
     // |r_k|: from rho_k itself, or (Jacobi, rho_k = r^T z) from its own partials
     const double rr_k =
-        a.jacobi ? reduce_partials(a.part_rr + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red) : rho_k;
+        a.jacobi ? reduce_parts(a.part_rr, pu, s_red) : rho_k;
     const double diag_flags =
-        (a.jacobi && first) ? reduce_partials(a.part_aux + static_cast<int64_t>(sys) * a.Gu, a.Gu, s_red) : 0.0;
+        (a.jacobi && first) ? reduce_parts(a.part_aux, pu, s_red) : 0.0;
     beta = 0.0;
     alpha_prev = 0.0;
     if (*s_stop < k) return kStepStopped;
@@ -578,11 +623,11 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     const int lb = bc.lb;
     const TileRange tr = bc.tr;
     const bool first = (k == 0);
-    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t off = vec_off(a, sys);
     const int64_t n = a.n;
     const RP* __restrict__ rp = static_cast<const RP*>(a.row_ptr);
     const int32_t* __restrict__ col = a.col;
-    const double* __restrict__ vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
+    const double* __restrict__ vals = a.vals + val_off(a, sys);
     const int64_t ntiles = tr.len;   // positions of this workgroup: tr.first + j * step, below tr.len
     const int64_t Gs = tr.step;
     auto tile_of = [&](int64_t m) { return tr.lo + m; };
@@ -756,8 +801,9 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     sig = block_sum(sig, s_red);
     if constexpr (MODE == kSpmvBsT) tt2 = block_sum(tt2, s_red);
     if (tid == 0) {
-        a.part_sigma[static_cast<int64_t>(sys) * a.G + lb] = sig;
-        if constexpr (MODE == kSpmvBsT) a.part_tt[static_cast<int64_t>(sys) * a.G + lb] = tt2;
+        const int64_t slot = parts_of(a, sys, a.G).base + lb;
+        a.part_sigma[slot] = sig;
+        if constexpr (MODE == kSpmvBsT) a.part_tt[slot] = tt2;
     }
 }
 
@@ -1194,7 +1240,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_pupd(CgArgs a, int64_t k)
     const int tid = threadIdx.x;
     const TileRange tr = bc.tr;
     const bool first = (k == 0);
-    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t off = vec_off(a, sys);
     const int64_t n = a.n;
     const double* __restrict__ rin = gathered_r(a, first) + off;
     const double* __restrict__ pprev = ((k & 1) ? a.p0 : a.p1) + off;
@@ -1270,7 +1316,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     const int lb = bc.lb;
     const TileRange tr = bc.tr;
     const bool lead = (lb == 0 && tid == 0);
-    const int64_t off = static_cast<int64_t>(sys) * a.n;
+    const int64_t off = vec_off(a, sys);
     const int64_t n = a.n;
     const double* __restrict__ rin = (k == 0 ? a.b : a.r) + off;
     const double* __restrict__ q = a.q + off;
@@ -1283,7 +1329,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     if (tr.first < tr.len) load_trip<NT, JAC>(tr, tr.first, n, q, rin, dg, qa, ra, da);
 
     if (tid == 0) s_stop = st->stop_iter;
-    const double sigma = reduce_partials(a.part_sigma + static_cast<int64_t>(sys) * a.G, a.G, s_red);
+    const double sigma = reduce_parts(a.part_sigma, parts_of(a, sys, a.G), s_red);
     if (s_stop <= k) return;
     const double rho_k = st->rho[k & 1];
     if (!(sigma > 0.0)) {
@@ -1337,11 +1383,11 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     if constexpr (JAC) {
         rz = block_sum(rz, s_red);
         if (tid == 0) {
-            a.part_rr[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
-            a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rz;
+            a.part_rr[parts_of(a, sys, a.Gu).base + lb] = rr;
+            a.part_rho[parts_of(a, sys, a.Gu).base + lb] = rz;
         }
     } else {
-        if (tid == 0) a.part_rho[static_cast<int64_t>(sys) * a.Gu + lb] = rr;
+        if (tid == 0) a.part_rho[parts_of(a, sys, a.Gu).base + lb] = rr;
     }
 }
 
@@ -1883,6 +1929,24 @@ __global__ __launch_bounds__(kBlock) void k_eig_grad(const RP* __restrict__ rp, 
         }
         gvals[kk] = acc;
     }
+}
+
+// SparseTensorList packing: one item's pattern into the block-diagonal packed pattern
+// (the pages' second batching mode, distinct patterns per item: paperpeel page, section
+// 3.1 "Typed sparse-tensor hierarchy").
+template <typename RPI, typename RPO>
+__global__ __launch_bounds__(kBlock) void k_pack_pattern(const RPI* __restrict__ rp, const int32_t* __restrict__ col,
+                                                         int64_t n, int64_t nnz, int64_t r0, int64_t e0,
+                                                         int64_t rows_padded, RPO* __restrict__ out_rp,
+                                                         int32_t* __restrict__ out_col)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    // rows r0 .. r0 + rows_padded inclusive: the last value (e0 + nnz) is also the next
+    // item's first, written the same by both
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i <= rows_padded; i += stride)
+        out_rp[r0 + i] = static_cast<RPO>(e0 + (i <= n ? static_cast<int64_t>(rp[i]) : nnz));
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; e < nnz; e += stride)
+        out_col[e0 + e] = static_cast<int32_t>(r0 + col[e]);
 }
 
 // ----------------------------------------------------------------------------------
@@ -2824,6 +2888,26 @@ hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col,
     else
         SLA_LAUNCH(k_eig_grad<int32_t>, grid, blk, 0, s, static_cast<const int32_t*>(row_ptr), col, U, g, k, n,
                    gvals);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_pattern(const void* rp, int rp_bits, const int32_t* col, int64_t n, int64_t nnz, int64_t r0,
+                               int64_t e0, int64_t rows_padded, void* out_rp, int out_bits, int32_t* out_col,
+                               hipStream_t s)
+{
+    const dim3 grid(grid_for(std::max(rows_padded + 1, nnz), kBlock, 4096)), blk(kBlock);
+    if (rp_bits == 64 && out_bits == 64)
+        SLA_LAUNCH((k_pack_pattern<int64_t, int64_t>), grid, blk, 0, s, static_cast<const int64_t*>(rp), col, n, nnz,
+                   r0, e0, rows_padded, static_cast<int64_t*>(out_rp), out_col);
+    else if (rp_bits == 64)
+        SLA_LAUNCH((k_pack_pattern<int64_t, int32_t>), grid, blk, 0, s, static_cast<const int64_t*>(rp), col, n, nnz,
+                   r0, e0, rows_padded, static_cast<int32_t*>(out_rp), out_col);
+    else if (out_bits == 64)
+        SLA_LAUNCH((k_pack_pattern<int32_t, int64_t>), grid, blk, 0, s, static_cast<const int32_t*>(rp), col, n, nnz,
+                   r0, e0, rows_padded, static_cast<int64_t*>(out_rp), out_col);
+    else
+        SLA_LAUNCH((k_pack_pattern<int32_t, int32_t>), grid, blk, 0, s, static_cast<const int32_t*>(rp), col, n, nnz,
+                   r0, e0, rows_padded, static_cast<int32_t*>(out_rp), out_col);
     return hipGetLastError();
 }
 

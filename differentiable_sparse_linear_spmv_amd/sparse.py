@@ -24,7 +24,8 @@ from ._lib import SlaCgInfo, SlaCgOpts, SlaEigInfo, SlaEigOpts, check
 
 __all__ = [
     "csr_create", "csr_destroy", "csr_info", "csr_analysis", "matvec", "matvec_backward", "solve",
-    "solve_backward", "cg_opts", "read_info", "eigsh", "eigsh_backward", "SparseTensor", "timing",
+    "solve_backward", "cg_opts", "read_info", "eigsh", "eigsh_backward", "list_create", "list_solve",
+    "list_solve_backward", "SparseTensor", "SparseTensorList", "timing",
 ]
 
 
@@ -252,6 +253,80 @@ def eigsh_backward(h: Handle, evecs: torch.Tensor, gevals: torch.Tensor, gvals: 
     return gvals
 
 
+class ListHandle:
+    """Owns an sla_list* (items with distinct patterns, packed on the device)."""
+
+    def __init__(self, ptr: int, n: list[int], nnz: list[int], symmetric: bool, device):
+        self.ptr = C.c_void_p(ptr)
+        self.n, self.nnz = n, nnz
+        self.items = len(n)
+        self.symmetric = symmetric
+        self.device = device
+
+    def __del__(self):
+        try:
+            if self.ptr:
+                L.load().sla_list_destroy(self.ptr)
+                self.ptr = C.c_void_p(0)
+        except Exception:
+            pass
+
+
+def _ptr_array(ts) -> C.Array:
+    return (C.c_void_p * len(ts))(*[None if t is None else t.data_ptr() for t in ts])
+
+
+def list_create(row_ptrs: list[torch.Tensor], cols: list[torch.Tensor], symmetric: bool = False) -> ListHandle:
+    """sla_list_create: items with their own square CSR patterns (same row-pointer dtype)."""
+    if len(row_ptrs) != len(cols) or not row_ptrs:
+        raise ValueError("need as many row_ptr as col tensors, at least one")
+    dt = row_ptrs[0].dtype
+    if dt not in (torch.int32, torch.int64) or any(r.dtype != dt for r in row_ptrs):
+        raise ValueError("row pointers must all be int32 or all int64")
+    dev = row_ptrs[0].device
+    for r, c in zip(row_ptrs, cols):
+        if r.device != dev or c.device != dev or c.dtype != torch.int32 or not (r.is_contiguous() and c.is_contiguous()):
+            raise ValueError("row_ptr / col must be contiguous, on one device, col int32")
+    n = [int(r.numel()) - 1 for r in row_ptrs]
+    nnz = [int(c.numel()) for c in cols]
+    ns = (C.c_int64 * len(n))(*n)
+    zs = (C.c_int64 * len(nnz))(*nnz)
+    out = C.c_void_p()
+    flags = L.SLA_SYMMETRIC if symmetric else 0
+    check(L.load().sla_list_create(C.byref(out), len(n), ns, zs, _ptr_array(row_ptrs),
+                                   32 if dt == torch.int32 else 64, _ptr_array(cols), flags, _stream(dev)))
+    h = ListHandle(out.value, n, nnz, symmetric, dev)
+    h._keep = (row_ptrs, cols)
+    return h
+
+
+def list_solve(h: ListHandle, vals: list[torch.Tensor], b: list[torch.Tensor], opts: SlaCgOpts):
+    """sla_list_solve: returns ([x_i], info) with info a device byte buffer [items]."""
+    for i in range(h.items):
+        _need(vals[i], f"vals[{i}]", torch.float64, h.nnz[i], h.device)
+        _need(b[i], f"b[{i}]", torch.float64, h.n[i], h.device)
+    x = [torch.empty_like(bi) for bi in b]
+    info = _info_buffer(h.items, h.device)
+    check(L.load().sla_list_solve(h.ptr, _ptr_array(vals), _ptr_array(b), _ptr_array(x), C.byref(opts),
+                                  _ptr(info), _stream(h.device)))
+    return x, info
+
+
+def list_solve_backward(h: ListHandle, vals: list[torch.Tensor], x: list[torch.Tensor], gx: list[torch.Tensor],
+                        opts: SlaCgOpts, need_gvals: bool = True):
+    """sla_list_solve_backward: returns ([lambda_i], [gvals_i] or None, info)."""
+    for i in range(h.items):
+        _need(vals[i], f"vals[{i}]", torch.float64, h.nnz[i], h.device)
+        _need(gx[i], f"gx[{i}]", torch.float64, h.n[i], h.device)
+    gb = [torch.empty_like(g) for g in gx]
+    gv = [torch.empty_like(v) for v in vals] if need_gvals else None
+    info = _info_buffer(h.items, h.device)
+    check(L.load().sla_list_solve_backward(h.ptr, _ptr_array(vals), _ptr_array(x) if need_gvals else None,
+                                           _ptr_array(gx), _ptr_array(gb), _ptr_array(gv) if need_gvals else None,
+                                           C.byref(opts), _ptr(info), _stream(h.device)))
+    return gb, gv, info
+
+
 class timing:
     """Per-kernel HIP-event timing inside the library (for measurement only)."""
 
@@ -320,6 +395,32 @@ class _EigshFn(torch.autograd.Function):
         return None, gvals, None, None
 
 
+class _ListSolveFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, T, opts_kw, *tensors):
+        k = T.handle.items
+        vals, b = [t.detach() for t in tensors[:k]], [t.detach() for t in tensors[k:]]
+        x, info = list_solve(T.handle, vals, b, cg_opts(**opts_kw))
+        T.last_info = info
+        ctx.T, ctx.opts_kw = T, opts_kw
+        ctx.save_for_backward(*vals, *x)
+        return tuple(x)
+
+    @staticmethod
+    def backward(ctx, *gx):
+        T = ctx.T
+        k = T.handle.items
+        saved = ctx.saved_tensors
+        vals, x = list(saved[:k]), list(saved[k:])
+        need_v = any(ctx.needs_input_grad[2:2 + k])
+        gx = [g.contiguous() if g is not None else torch.zeros_like(xi) for g, xi in zip(gx, x)]
+        gb, gv, info = list_solve_backward(T.handle, vals, x, gx, cg_opts(**ctx.opts_kw), need_gvals=need_v)
+        T.last_backward_info = info
+        gvals = gv if need_v else [None] * k
+        gbs = [g if ctx.needs_input_grad[2 + k + i] else None for i, g in enumerate(gb)]
+        return (None, None, *gvals, *gbs)
+
+
 class _MatvecFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, A, vals, x):
@@ -386,6 +487,35 @@ class SparseTensor:
             v0 = torch.randn(self.handle.n_rows, dtype=torch.float64, device=self.handle.device, generator=gen)
         kw = dict(k=k, which=which, tol=tol, max_dim=max_dim)
         return _EigshFn.apply(self, self.vals, v0, kw)
+
+    def info(self, backward: bool = False) -> list[dict]:
+        buf = self.last_backward_info if backward else self.last_info
+        return [] if buf is None else read_info(buf)
+
+
+class SparseTensorList:
+    """A list of square sparse matrices with distinct patterns (the pages' SparseTensorList).
+
+    ``solve([b_i])`` solves every item in one packed CG run on the device and is one
+    autograd node, differentiable with respect to every ``vals_i`` and ``b_i``.
+    """
+
+    def __init__(self, row_ptrs: list[torch.Tensor], cols: list[torch.Tensor], vals: list[torch.Tensor],
+                 symmetric: bool = False):
+        self.handle = list_create(row_ptrs, cols, symmetric=symmetric)
+        self.vals = list(vals)
+        self.last_info = None
+        self.last_backward_info = None
+
+    def __len__(self) -> int:
+        return self.handle.items
+
+    def solve(self, b: list[torch.Tensor], rtol=1e-10, atol=0.0, max_iter=100000, fixed=False,
+              jacobi: bool = False) -> list[torch.Tensor]:
+        if len(b) != self.handle.items:
+            raise ValueError(f"need {self.handle.items} right-hand sides, got {len(b)}")
+        kw = dict(rtol=rtol, atol=atol, max_iter=max_iter, fixed=fixed, jacobi=jacobi)
+        return list(_ListSolveFn.apply(self, kw, *self.vals, *b))
 
     def info(self, backward: bool = False) -> list[dict]:
         buf = self.last_backward_info if backward else self.last_info

@@ -233,6 +233,58 @@ sla_status sla_solve_backward(const sla_csr* A, int64_t batch, const double* d_v
                               double* d_gvals, const sla_cg_opts* opts, sla_cg_info* d_info,
                               void* stream);
 
+/* ------------------------------------------------------------ SparseTensorList */
+/*
+ * A list of square systems with distinct sparsity patterns, solved together (the
+ * pages' second batching mode, SparseTensorList: paperpeel page, section 3.1 "Typed
+ * sparse-tensor hierarchy"; gist.science summaries, Methodology item 1).  The items
+ * are packed block-diagonally into one pattern, each item's rows starting on a
+ * 256-row tile boundary (the rest of its last tile is empty padding), and one grid of
+ * workgroups is split among them in proportion to their tiles.  Each item keeps its
+ * own scalars, stop test, iteration count and info record, exactly as the systems of
+ * a batch do; the arithmetic of every item is that of sla_solve on that item alone
+ * (its rows summed in the same order; inner products in a different tree).
+ */
+typedef struct sla_list sla_list;   /* opaque */
+
+/*
+ * Create a list of `items` patterns (1 <= items <= 2^20).  Host arrays [items]:
+ *   n[i] >= 1 rows (= columns), nnz[i] >= 0 entries, d_row_ptr[i] / d_col[i] device
+ *   pointers to item i's CSR (row_ptr_bits 32 or 64, columns int32 strictly ascending
+ *   within a row, in [0, n[i])).
+ * Every item is validated on the device (SLA_ERR_INVALID_CSR names the first bad one).
+ * The packed pattern and its per-item tables are owned by the list; the caller's
+ * arrays are only read during this call.  flags: SLA_SYMMETRIC (every item symmetric)
+ * and SLA_EAGER_TRANSPOSE as for sla_csr_create.  Synchronises the stream once.
+ */
+sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, const int64_t* nnz,
+                           const void* const* d_row_ptr, int32_t row_ptr_bits, const int32_t* const* d_col,
+                           uint32_t flags, void* stream);
+sla_status sla_list_destroy(sla_list* L);   /* synchronises the device */
+/* Packed sizes (rows with padding, entries) and the number of workgroups of the grid. */
+sla_status sla_list_info(const sla_list* L, int64_t* n_total, int64_t* nnz_total, int32_t* workgroups);
+
+/*
+ * Solve every item: x_i = A_i^{-1} b_i by CG (or Jacobi CG with SLA_JACOBI; SLA_BICGSTAB
+ * is SLA_ERR_UNSUPPORTED here), x0 = 0, the options and stop tests of sla_solve per item.
+ *   d_vals[i] [nnz[i]], d_b[i] [n[i]], d_x[i] [n[i]] (outputs): host arrays of device
+ *   pointers; d_info device [items].  opts->residual_history, if given, is
+ *   [items][max_iter + 1].
+ * The values and right-hand sides are copied into packed staging buffers owned by the
+ * list, and the solutions copied back.
+ */
+sla_status sla_list_solve(const sla_list* L, const double* const* d_vals, const double* const* d_b,
+                          double* const* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
+
+/*
+ * Adjoint backward of sla_list_solve, item by item as sla_solve_backward: A_i^T
+ * lambda_i = d_gx[i] (on the packed transpose unless SLA_SYMMETRIC), d_gb[i] = lambda_i,
+ * d_gvals[i][k] = -lambda_i[row(k)] x_i[col(k)] (d_gvals nullable; then d_x may be NULL).
+ */
+sla_status sla_list_solve_backward(const sla_list* L, const double* const* d_vals, const double* const* d_x,
+                                   const double* const* d_gx, double* const* d_gb, double* const* d_gvals,
+                                   const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
+
 /* ------------------------------------------------------------------ eigenvalues */
 #define SLA_EIG_LARGEST   0   /* the k largest eigenvalues (algebraic), descending */
 #define SLA_EIG_SMALLEST  1   /* the k smallest eigenvalues (algebraic), ascending */
