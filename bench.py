@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "fp64 CG iters/s + achieved HBM GB/s, Poisson 1M/169M DOF; solve+adjoint ms"
 # the nonsymmetric widening (not the headline metric): BiCGStab on convection-diffusion
+METRIC_LIST = "fp64 CG iters/s summed over items + achieved HBM GB/s, SparseTensorList of 64 Poisson grids; solve+adjoint ms"
 METRIC_EIGSH = "fp64 Lanczos steps/s + achieved HBM GB/s, eigsh on a 1M-DOF Poisson-type matrix; eigsh+gradient ms"
 METRIC_BICGSTAB = "fp64 BiCGStab iters/s + achieved HBM GB/s, convection-diffusion 1M DOF; solve+adjoint ms"
 COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written
@@ -153,6 +154,62 @@ def run_eigsh(args, w, S, torch) -> dict:
     return dict(value=sum(i["iterations"] for i in infos) / wall, wall=wall, tq=tq, bm=bm, achieved=achieved,
                 spmv_ms=spmv_ms, orth_ms=orth_ms, info=infos[-1],
                 spmv_gbps=bm["lz_spmv"] / (spmv_ms * 1e-3) / 1e9)
+
+
+def run_list(args, c, S, torch, dev) -> dict:
+    """One step = sla_list_solve + sla_list_solve_backward over every item."""
+    import numpy as np
+    items = c["items"]
+    h = S.list_create([torch.from_numpy(A.row_ptr).to(dev) for A in items],
+                      [torch.from_numpy(A.col).to(dev) for A in items], symmetric=True)
+    vals = [torch.from_numpy(A.vals).to(dev) for A in items]
+    bs = [torch.from_numpy(b).to(dev) for b in c["b"]]
+    opts = S.cg_opts(rtol=c["rtol"], max_iter=c["max_iter"])
+
+    def step():
+        x, info = S.list_solve(h, vals, bs, opts)
+        gb, gv, binfo = S.list_solve_backward(h, vals, x, [xi.clone() for xi in x], opts)
+        return info, binfo
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    infos = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fi = [s["iterations"] for s in S.read_info(infos[-1][0])]
+    bi = [s["iterations"] for s in S.read_info(infos[-1][1])]
+    S.timing.reset()
+    S.timing.enable(True)
+    step()
+    S.timing.collect()
+    S.timing.enable(False)
+    tq = S.timing.query()
+    # algorithmic bytes of every item-iteration of the fused CG SpMV, over its measured time
+    per_item = [bytes_model(A.n_rows, A.nnz, 1, 4)["cg_spmv"] for A in items]
+    spmv_bytes = float(np.dot(np.array(fi) + np.array(bi), per_item))
+    it_bytes = float(np.dot(np.array(fi) + np.array(bi), [bytes_model(A.n_rows, A.nnz, 1, 4)["iteration"]
+                                                          for A in items]))
+    spmv_ms = tq["cg_spmv"]["total_ms"]
+    iter_ms = spmv_ms + tq["cg_update"]["total_ms"] + tq["cg_pupd"]["total_ms"]
+    return dict(value=(sum(fi) + sum(bi)) * args.steps / wall, wall=wall, tq=tq, fi=fi, bi=bi,
+                achieved=spmv_bytes / (spmv_ms * 1e-3) / 1e9, spmv_bytes=spmv_bytes, spmv_ms=spmv_ms,
+                iter_gbps=it_bytes / (iter_ms * 1e-3) / 1e9, info=S.list_info if hasattr(S, "list_info") else None)
+
+
+def cpu_baseline_list(c, iters: int) -> dict:
+    """The oracle's CG (one thread) on every item of the list, a fixed number of iterations each."""
+    import oracle as O
+    t0 = time.perf_counter()
+    for A, b in zip(c["items"], c["b"]):
+        f = O.cg(A, b, rtol=0.0, max_iter=iters, fixed=True)
+        O.solve_backward(A, f["x"], f["x"], symmetric=True, rtol=0.0, max_iter=iters, fixed=True)
+    dt = time.perf_counter() - t0
+    k = len(c["items"])
+    return dict(value=round(2 * iters * k / dt, 3), unit="CG iters/s (summed over items)", cores=1, kind="oracle",
+                sample=f"oracle CG on each of the {k} items, {iters} fixed iterations + {iters} adjoint "
+                       f"(single thread)", seconds=round(dt, 2))
 
 
 def cpu_baseline_eigsh(w, steps: int) -> dict:
@@ -343,7 +400,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="poisson1024",
                     choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000",
-                             "convdiff1024", "eigsh_varcoef1024"])
+                             "convdiff1024", "eigsh_varcoef1024", "poisson_list64"])
     ap.add_argument("--cpu-iters", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -368,6 +425,37 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "poisson_list64":
+        import workloads as W
+        c = W.config(args.workload)
+        r = run_list(args, c, S, torch, dev)
+        cpu = cpu_baseline_list(c, 150) if (rank == 0 and not args.no_cpu_baseline) else None
+        n_tot = sum(A.n_rows for A in c["items"])
+        out = {
+            "metric": METRIC_LIST, "value": round(r["value"], 2), "unit": "CG iters/s (summed over items)",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(1e3 * r["wall"] / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+            "config": {"workload": "SparseTensorList of 64 five-point Poisson grids, sides 64, 67, ..., 253 "
+                                   "(distinct patterns), b_i~N(0,1) seed i, CG to 1e-8 + adjoint",
+                       "items": len(c["items"]), "rows": n_tot, "rtol": c["rtol"], "parallelism": "none (1 GPU)",
+                       "method": "list"},
+            "iterations_per_step": {"forward_sum": sum(r["fi"]), "adjoint_sum": sum(r["bi"]),
+                                    "forward_max": max(r["fi"]), "adjoint_max": max(r["bi"])},
+            "kernels": {kk: {"launches": v["launches"],
+                             "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
+                        for kk, v in r["tq"].items() if v["launches"]},
+            "hbm_gbps_per_iteration": round(r["iter_gbps"], 1),
+            "roofline": {"bound": "hbm", "kernel": "k_cg_spmv (list mode), all launches of one step",
+                         "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "traffic_source": "no counter summary", "bytes_per_launch": None,
+                         "bytes_per_step": r["spmv_bytes"], "spmv_ms_per_step": round(r["spmv_ms"], 3)},
+            "cpu_baseline": cpu,
+        }
+        if rank == 0:
+            print(json.dumps(out), flush=True)
+        return 0
     w = make_workload(args.workload, dev)
     n, nnz, B = w["n"], w["nnz"], w["batch"]
     rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read

@@ -348,6 +348,9 @@ def config(name: str, scale: int | None = None) -> dict:
     eigsh_varcoef1024  the 8 largest eigenpairs of the varcoef matrix on 1024 x 1024
                    (kappa = exp(GRF), seed 0) by Lanczos to tol 1e-10 from v0 ~ N(0, 1)
                    (seed 3), and the Hellmann-Feynman gradient of sum(lambda).
+    poisson_list64 a SparseTensorList of 64 five-point Poisson grids of sides 64, 67, ...,
+                   253 (distinct patterns, 1.7M rows in all), b_i ~ N(0, 1) seed i, CG to
+                   1e-8 + adjoint of sum_i 0.5 |x_i|^2.
     convdiff1024   nonsymmetric convection-diffusion (:func:`convdiff5`, W = 100) on
                    1024 x 1024, b ~ N(0, 1) (seed 0), BiCGStab to rtol 1e-8 forward and
                    on A^T in the adjoint, loss 0.5 |x|^2.
@@ -381,6 +384,12 @@ def config(name: str, scale: int | None = None) -> dict:
         return dict(name=name, A=A, b=rhs_normal(N * N, 0), rtol=1e-8, atol=0.0,
                     max_iter=100000, fixed=False, loss="half_sq", method="bicgstab",
                     symmetric=False)
+    if name == "poisson_list64":
+        sizes = [64 + 3 * i for i in range(64)]
+        items = [poisson5(N) for N in sizes]
+        return dict(name=name, items=items, b=[rhs_normal(A.n_rows, i) for i, A in enumerate(items)],
+                    sizes=sizes, rtol=1e-8, atol=0.0, max_iter=100000, fixed=False, loss="half_sq",
+                    method="list")
     if name == "eigsh_varcoef1024":
         N = scale or 1024
         A, _, _ = varcoef_poisson5(N, seed=0)
