@@ -439,8 +439,10 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     P = std::max<int64_t>(1, std::min<int64_t>(P, gtiles));
     // streaming kernels: about 16 tiles per workgroup (their start sums the partials)
     const int64_t Pu = std::max<int64_t>(1, std::min<int64_t>(64, (gtiles + 15) / 16));
+    const bool jacobi = (o->flags & SLA_JACOBI) != 0;
     Workspace w;
-    sla_status st = ensure_workspace(A, batch, static_cast<int>(std::max(P, Pu)), &w);
+    sla_status st = ensure_workspace(A, batch, static_cast<int>(std::max(P, Pu)), &w,
+                                     jacobi ? kMethodJacobi : kMethodCG);
     if (st != SLA_OK) return st;
     const size_t xb = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t need = xb + sizeof(double) * static_cast<size_t>(A->nnz) * batch;
@@ -469,6 +471,11 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     a.q = w.q;
     a.part_sigma = w.part_sigma;
     a.part_rho = w.part_rho;
+    a.part_rr = w.part_rr;
+    a.part_aux = w.part_aux;
+    a.z = w.z;       // Jacobi, grouped layout
+    a.dg = w.dg;
+    a.jacobi = jacobi ? 1 : 0;
     a.st = w.st;
     a.info = info;
     a.hist = o->residual_history;
@@ -489,6 +496,7 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     a.xg = xg;
 
     hipError_t e = timed(SLA_K_GROUP_LAYOUT, s, [&] { return launch_group_vals(vals, vg, A->nnz, groups, s); });
+    if (e == hipSuccess && jacobi) e = timed(SLA_K_CG_INIT, s, [&] { return launch_gcg(5, a, 0, s); });
     if (e == hipSuccess) e = timed(SLA_K_CG_INIT, s, [&] { return launch_gcg(0, a, 0, s); });
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "grouped cg init: %s", hipGetErrorString(e));
     auto step = [&](int64_t k) -> hipError_t {
@@ -523,7 +531,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
 {
     const bool jacobi = (o->flags & SLA_JACOBI) != 0;
     if (list) band = 0;
-    if (!list && !jacobi && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 &&
+    if (!list && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 &&
         A->krp_bits == 32 &&
         A->group_ok &&
         static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapLarge && row_ptr == A->krp)

@@ -173,7 +173,8 @@ hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipS
 hipError_t launch_cg_update(const CgArgs& a, int64_t k, hipStream_t s);
 hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s);   // split schedule
 // Grouped batch: values into the grouped layout, and the CG kernels
-// (which: 0 init, 1 p update, 2 SpMV, 3 update, 4 x back to the caller's layout).
+// (which: 0 init, 1 p update, 2 SpMV, 3 update, 4 x back to the caller's layout,
+// 5 the Jacobi diagonal in the grouped layout).
 hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, hipStream_t s);
 hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s);
 // BiCGStab (which: 0 init, 1 p update, 2 v = A p, 3 s, 4 t = A s, 5 update).  Vectors:

@@ -1995,6 +1995,21 @@ __device__ __forceinline__ double group_block_sum(double v, double* s_red)
     return t;
 }
 
+// Per-system maximum over the workgroup (as group_block_sum, with max).
+__device__ __forceinline__ double group_block_max(double v, double* s_red)
+{
+#pragma unroll
+    for (int off = 32; off >= kGroup; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    if (lane < kGroup) s_red[w * kGroup + lane] = v;
+    __syncthreads();
+    const int sy = threadIdx.x % kGroup;
+    const double t = fmax(fmax(s_red[sy], s_red[kGroup + sy]), fmax(s_red[2 * kGroup + sy], s_red[3 * kGroup + sy]));
+    __syncthreads();
+    return t;
+}
+
 // Per-system sum of the P partials part[sys][P] of the group's systems.
 __device__ __forceinline__ double group_reduce_partials(const double* part, int sys0, int P, double* s_red)
 {
@@ -2018,10 +2033,13 @@ __device__ __forceinline__ int group_step_begin(const CgArgs& a, int sys0, int l
     const bool first = (k == 0);
     if (threadIdx.x < kGroup) s_stop[threadIdx.x] = a.st[sys0 + threadIdx.x].stop_iter;
     const double rho_k = group_reduce_partials(a.part_rho, sys0, a.Gu, s_red);
+    // |r_k|: from rho_k, or (Jacobi, rho_k = r^T z) from its own partials
+    const double rr_k = a.jacobi ? group_reduce_partials(a.part_rr, sys0, a.Gu, s_red) : rho_k;
+    const double diag_flags = (a.jacobi && first) ? group_reduce_partials(a.part_aux, sys0, a.Gu, s_red) : 0.0;
     beta = 0.0;
     alpha_prev = 0.0;
     if (s_stop[sy] < k) return kStepStopped;
-    const double res = sqrt(rho_k);
+    const double res = sqrt(rr_k);
     double thr, rhs;
     if (first) {
         rhs = res;
@@ -2035,6 +2053,8 @@ __device__ __forceinline__ int group_step_begin(const CgArgs& a, int sys0, int l
     alpha_prev = first ? 0.0 : st->alpha[(k - 1) & 1];
     int code = -1;
     if (!a.fixed && res <= thr) code = SLA_CONVERGED;
+    else if (diag_flags >= kDiagNaN) code = SLA_NAN;        // Jacobi, k = 0: unusable diagonal
+    else if (diag_flags > 0.0) code = SLA_NOT_SPD;
     else if (k >= a.max_iter) code = SLA_MAX_ITER;
     if (code >= 0) {
         if (lead) {
@@ -2054,6 +2074,7 @@ __device__ __forceinline__ int group_step_begin(const CgArgs& a, int sys0, int l
     beta = first ? 0.0 : rho_k / st->rho[(k - 1) & 1];
     if (lead) {
         st->rho[k & 1] = rho_k;
+        st->rr = rr_k;
         if (first) { st->thr = thr; st->rhs = rhs; }
     }
     return kStepRun;
@@ -2093,7 +2114,8 @@ __global__ __launch_bounds__(kBlock) void k_gcg_init(CgArgs a)
     const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
     const double* __restrict__ b = a.b + static_cast<int64_t>(sys0 + sy) * n;
     const int64_t gtiles = (n + kGRows - 1) / kGRows;
-    double rr = 0.0;
+    const bool jac = a.jacobi != 0;
+    double rr = 0.0, rz = 0.0;
     for (int64_t t = gc.lb; t < gtiles; t += a.Gu) {
         const int64_t i = t * kGRows + tid / kGroup;
         if (i < n) {
@@ -2104,11 +2126,24 @@ __global__ __launch_bounds__(kBlock) void k_gcg_init(CgArgs a)
             a.p1[e] = 0.0;
             const double w = bv * bv;
             rr = rr + w;
+            if (jac) {                       // z_0 = M^{-1} b
+                const double zv = bv / a.dg[e];
+                a.z[e] = zv;
+                const double wz = bv * zv;
+                rz = rz + wz;
+            }
         }
     }
     rr = group_block_sum(rr, s_red);
+    if (jac) rz = group_block_sum(rz, s_red);
     if (tid < kGroup) {
-        a.part_rho[static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb] = rr;
+        const int64_t slot = static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb;
+        if (jac) {
+            a.part_rr[slot] = rr;
+            a.part_rho[slot] = rz;
+        } else {
+            a.part_rho[slot] = rr;
+        }
         if (gc.lb == 0) a.st[sys0 + tid].stop_iter = INT64_MAX;
     }
     if (gc.lb == 0 && gc.grp == 0 && tid == 0) *a.n_active = a.batch;
@@ -2130,7 +2165,7 @@ __global__ __launch_bounds__(kBlock) void k_gcg_pupd(CgArgs a, int64_t k)
     const bool stop = (run == kStepStopNow);
     const int64_t n = a.n;
     const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
-    const double* __restrict__ rg = a.r + goff;
+    const double* __restrict__ rg = (a.jacobi ? a.z : a.r) + goff;   // p_k = z_k + beta p_{k-1} with Jacobi
     const double* __restrict__ pp = ((k & 1) ? a.p0 : a.p1) + goff;
     double* __restrict__ pc = ((k & 1) ? a.p1 : a.p0) + goff;
     double* __restrict__ xg = a.xg + goff;
@@ -2327,7 +2362,7 @@ __global__ __launch_bounds__(kBlock) void k_gcg_update(CgArgs a, int64_t k)
             st->stop_iter = k;
             sla_cg_info inf;
             inf.iterations = k;
-            inf.res_norm = sqrt(rho_k);
+            inf.res_norm = sqrt(a.jacobi ? st->rr : rho_k);
             inf.rhs_norm = st->rhs;
             inf.state = (sigma != sigma) ? SLA_NAN : SLA_NOT_SPD;
             inf.reserved = 0;
@@ -2342,8 +2377,11 @@ __global__ __launch_bounds__(kBlock) void k_gcg_update(CgArgs a, int64_t k)
     const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
     const double* __restrict__ qg = a.q + goff;
     double* __restrict__ rg = a.r + goff;
+    const bool jac = a.jacobi != 0;
+    const double* __restrict__ dgg = jac ? a.dg + goff : nullptr;
+    double* __restrict__ zg = jac ? a.z + goff : nullptr;
     const int64_t gtiles = (n + kGRows - 1) / kGRows;
-    double rr = 0.0;
+    double rr = 0.0, rz = 0.0;
     if (run) {
 #pragma unroll 1
         for (int64_t t0 = gc.lb; t0 < gtiles; t0 += kStreamUnroll * static_cast<int64_t>(a.Gu)) {
@@ -2365,12 +2403,62 @@ __global__ __launch_bounds__(kBlock) void k_gcg_update(CgArgs a, int64_t k)
                     rg[i * kGroup + sy] = rn;
                     const double w = rn * rn;
                     rr = rr + w;
+                    if (jac) {
+                        const double zn = rn / dgg[i * kGroup + sy];   // z = M^{-1} r
+                        zg[i * kGroup + sy] = zn;
+                        const double wz = rn * zn;
+                        rz = rz + wz;
+                    }
                 }
             }
         }
     }
     rr = group_block_sum(rr, s_red);
-    if (tid < kGroup) a.part_rho[static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb] = rr;
+    if (jac) rz = group_block_sum(rz, s_red);
+    if (tid < kGroup) {
+        const int64_t slot = static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb;
+        if (jac) {
+            a.part_rr[slot] = rr;
+            a.part_rho[slot] = rz;
+        } else {
+            a.part_rho[slot] = rr;
+        }
+    }
+}
+
+// Jacobi: the diagonal in the grouped layout (entry (i, i) by binary search in row i of
+// the shared 32-bit pattern; 0 if not stored) and the flag partials of k_cg_diag.
+__global__ __launch_bounds__(kBlock) void k_gcg_diag(CgArgs a)
+{
+    __shared__ double s_red[4 * kGroup];
+    const GroupCoord gc = group_coord(a, a.Gu);
+    const int tid = threadIdx.x;
+    const int sy = tid % kGroup;
+    const int sys0 = gc.grp * kGroup;
+    const int64_t n = a.n;
+    const int64_t goff = static_cast<int64_t>(gc.grp) * n * kGroup;
+    const int32_t* __restrict__ rp = static_cast<const int32_t*>(a.row_ptr);
+    const double* __restrict__ vg = a.vals + static_cast<int64_t>(gc.grp) * a.nnz * kGroup;
+    const int64_t gtiles = (n + kGRows - 1) / kGRows;
+    double flag = 0.0;
+    for (int64_t t = gc.lb; t < gtiles; t += a.Gu) {
+        const int64_t i = t * kGRows + tid / kGroup;
+        if (i < n) {
+            int64_t lo = rp[i], hi = rp[i + 1];
+            const int64_t end = hi;
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (a.col[mid] < i) lo = mid + 1;
+                else hi = mid;
+            }
+            const double d = (lo < end && a.col[lo] == i) ? vg[lo * kGroup + sy] : 0.0;
+            a.dg[goff + i * kGroup + sy] = d;
+            if (d != d) flag = kDiagNaN;
+            else if (!(d > 0.0)) flag = fmax(flag, kDiagNonPos);
+        }
+    }
+    flag = group_block_max(flag, s_red);
+    if (tid < kGroup) a.part_aux[static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb] = flag;
 }
 
 // x[s][i] = xg[i][s]: the solutions back in the caller's layout.
@@ -2815,6 +2903,7 @@ hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s)
         else SLA_LAUNCH(k_gcg_spmv<kGCapLarge>, gs, blk, 0, s, a, k);
         break;
     case 3: SLA_LAUNCH(k_gcg_update, gu, blk, 0, s, a, k); break;
+    case 5: SLA_LAUNCH(k_gcg_diag, gu, blk, 0, s, a); break;
     default: SLA_LAUNCH(k_gcg_finish, gu, blk, 0, s, a); break;
     }
     return hipGetLastError();

@@ -130,11 +130,45 @@ def test_jacobi_varcoef_against_oracle(S, path):
     assert info[0]["iterations"] < 0.8 * plain["iterations"]
 
 
-def test_jacobi_fem_batch_against_oracle(S, monkeypatch):
+@pytest.mark.parametrize("grouped", ["1", "0"])
+def test_jacobi_fem_batch_against_oracle(S, monkeypatch, grouped):
+    # 16 systems on the split schedule: the grouped kernels (4 systems interleaved per
+    # element), or the per-system ones with grouping switched off
     monkeypatch.setenv("SLA_CG_SCHEDULE", "split")
+    monkeypatch.setenv("SLA_CG_GROUPED", grouped)
     A, b = W.fem_p1_batched(nv=24, B=16, seed=3)
     h = handle(S, A)
     check_pcg(S, h, A, A.vals, b, rtol=1e-8)
+
+
+def test_jacobi_grouped_invalid_diagonals_and_agreement(S, monkeypatch):
+    monkeypatch.setenv("SLA_CG_SCHEDULE", "split")
+    A, b = W.fem_p1_batched(nv=24, B=8, seed=4)
+    rows = np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+    diag = np.nonzero(rows == A.col)[0]
+    vals = A.vals.copy()
+    b = b.copy()
+    vals[1][diag[40]] = 0.0
+    vals[2][diag[7]] = np.nan
+    vals[3][diag[A.n_rows - 1]] = -2.0
+    b[4] = 0.0
+    h = handle(S, A)
+    x, info = solve(S, h, vals, b, True, rtol=1e-8)
+    inf = [i["state"] for i in info]
+    assert inf[1:5] == [O.NOT_SPD, O.NAN, O.NOT_SPD, O.CONVERGED]
+    xs = host(x).reshape(8, -1)
+    for s_ in range(8):
+        f = O.cg(A, b[s_], rtol=1e-8, vals=vals[s_], jacobi=True)
+        assert info[s_]["state"] == f["state"], (s_, info[s_], f["state"])
+        if f["state"] == O.CONVERGED:
+            assert iters_close(info[s_]["iterations"], f["iterations"])
+            assert rel(xs[s_], f["x"]) <= 1e-9, s_
+    # grouped vs per-system kernels over 6 fixed iterations (system 0)
+    xg, _ = solve(S, h, A.vals, b, True, rtol=0.0, max_iter=6, fixed=True)
+    monkeypatch.setenv("SLA_CG_GROUPED", "0")
+    h2 = handle(S, A)
+    xu, _ = solve(S, h2, A.vals, b, True, rtol=0.0, max_iter=6, fixed=True)
+    assert rel(host(xg), host(xu)) <= 1e-12
 
 
 def test_jacobi_invalid_diagonals(S, path):
