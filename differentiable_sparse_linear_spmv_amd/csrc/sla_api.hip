@@ -52,6 +52,12 @@ struct sla_csr {
     bool split = false;
     // Grouped kernels for batches of split-schedule patterns (SLA_CG_GROUPED=0 turns them off).
     bool group_ok = true;
+    // The grouped kernels run on a reverse Cuthill-McKee reordering of the pattern, built on
+    // the first grouped solve (SLA_CG_REORDER=0 turns it off): row pointers, columns, the
+    // entry permutation and the row permutation (new -> caller's), all int32.
+    bool reorder_ok = true;
+    bool g_reordered = false;
+    int32_t *g_rp = nullptr, *g_col = nullptr, *g_eperm = nullptr, *g_perm = nullptr;
     // transposed pattern (lazily built unless SLA_SYMMETRIC)
     bool has_t = false;
     void* row_ptr_t = nullptr;
@@ -421,9 +427,52 @@ sla_status drive_cg(sla_csr* A, const CgArgs& a, const Workspace& w, const sla_c
     return SLA_OK;
 }
 
+// The reordered pattern of the grouped kernels (once per handle; the pattern is 32-bit
+// there).  Host copies of the pattern, the reverse Cuthill-McKee order, each new row's
+// entries sorted by new column with the positions they came from.
+sla_status ensure_reorder(sla_csr* A, hipStream_t s)
+{
+    if (A->g_reordered) return SLA_OK;
+    const int64_t n = A->n_rows, nnz = A->nnz;
+    std::vector<int32_t> rp(n + 1), col(std::max<int64_t>(nnz, 1));
+    HIP_TRY(hipMemcpyAsync(rp.data(), A->krp, sizeof(int32_t) * (n + 1), hipMemcpyDeviceToHost, s));
+    if (nnz > 0) HIP_TRY(hipMemcpyAsync(col.data(), A->col, sizeof(int32_t) * nnz, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    std::vector<int32_t> perm(n), inv(n), rp2(n + 1), col2(std::max<int64_t>(nnz, 1)), ep(std::max<int64_t>(nnz, 1));
+    rcm_order(rp.data(), col.data(), n, perm.data());
+    for (int64_t i = 0; i < n; ++i) inv[perm[i]] = static_cast<int32_t>(i);
+    rp2[0] = 0;
+    std::vector<std::pair<int32_t, int32_t>> row;
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t o = perm[i];
+        row.clear();
+        for (int32_t k = rp[o]; k < rp[o + 1]; ++k) row.emplace_back(inv[col[k]], k);
+        std::sort(row.begin(), row.end());
+        for (size_t j = 0; j < row.size(); ++j) {
+            col2[rp2[i] + j] = row[j].first;
+            ep[rp2[i] + j] = row[j].second;
+        }
+        rp2[i + 1] = rp2[i] + static_cast<int32_t>(row.size());
+    }
+    sla_status st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_rp), sizeof(int32_t) * (n + 1))) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_col), sizeof(int32_t) * col2.size())) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_eperm), sizeof(int32_t) * ep.size())) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_perm), sizeof(int32_t) * n)) != SLA_OK) return st;
+    HIP_TRY(hipMemcpyAsync(A->g_rp, rp2.data(), sizeof(int32_t) * (n + 1), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(A->g_col, col2.data(), sizeof(int32_t) * col2.size(), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(A->g_eperm, ep.data(), sizeof(int32_t) * ep.size(), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(A->g_perm, perm.data(), sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    A->g_reordered = true;
+    return SLA_OK;
+}
+
 // Grouped batch (kGroup systems interleaved per element): values into the grouped
 // layout, then init / (p update, SpMV, update) per iteration / x back to the caller's
-// layout.  The polling is run_cg's.
+// layout.  The polling is run_cg's.  With the reordering on, the grouped kernels run on
+// the reordered pattern: the values are gathered through the entry permutation, b and
+// x through the row permutation, so the caller sees its own order.
 sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, int64_t batch, const double* vals,
                           const double* b, double* x, const sla_cg_opts* o, sla_cg_info* info, hipStream_t s)
 {
@@ -444,6 +493,8 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     sla_status st = ensure_workspace(A, batch, static_cast<int>(std::max(P, Pu)), &w,
                                      jacobi ? kMethodJacobi : kMethodCG);
     if (st != SLA_OK) return st;
+    const bool reorder = A->reorder_ok;
+    if (reorder && (st = ensure_reorder(A, s)) != SLA_OK) return st;
     const size_t xb = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t need = xb + sizeof(double) * static_cast<size_t>(A->nnz) * batch;
     if (need > A->gws_bytes) {
@@ -460,8 +511,9 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     double* vg = reinterpret_cast<double*>(static_cast<char*>(A->gws) + xb);
 
     CgArgs a{};
-    a.row_ptr = row_ptr;
-    a.col = col;
+    a.row_ptr = reorder ? static_cast<const void*>(A->g_rp) : row_ptr;
+    a.col = reorder ? A->g_col : col;
+    a.gperm = reorder ? A->g_perm : nullptr;
     a.vals = vg;
     a.b = b;
     a.x = x;
@@ -495,7 +547,9 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     a.cap = gcap;
     a.xg = xg;
 
-    hipError_t e = timed(SLA_K_GROUP_LAYOUT, s, [&] { return launch_group_vals(vals, vg, A->nnz, groups, s); });
+    hipError_t e = timed(SLA_K_GROUP_LAYOUT, s, [&] {
+        return launch_group_vals(vals, vg, A->nnz, groups, reorder ? A->g_eperm : nullptr, s);
+    });
     if (e == hipSuccess && jacobi) e = timed(SLA_K_CG_INIT, s, [&] { return launch_gcg(5, a, 0, s); });
     if (e == hipSuccess) e = timed(SLA_K_CG_INIT, s, [&] { return launch_gcg(0, a, 0, s); });
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "grouped cg init: %s", hipGetErrorString(e));
@@ -843,6 +897,7 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
         if (std::strcmp(env, "split") == 0) A->split = A->band == 0;
     }
     if (const char* env = std::getenv("SLA_CG_GROUPED")) A->group_ok = std::strcmp(env, "0") != 0;
+    if (const char* env = std::getenv("SLA_CG_REORDER")) A->reorder_ok = std::strcmp(env, "0") != 0;
     A->krp = d_row_ptr;
     A->krp_bits = row_ptr_bits;
     if (row_ptr_bits == 64 && nnz < (int64_t(1) << 31)) {
@@ -878,6 +933,10 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->rp_owned) (void)hipFree(A->rp_owned);
     if (A->flag_host) (void)hipHostFree(A->flag_host);
     if (A->eig_ws) (void)hipFree(A->eig_ws);
+    if (A->g_rp) (void)hipFree(A->g_rp);
+    if (A->g_col) (void)hipFree(A->g_col);
+    if (A->g_eperm) (void)hipFree(A->g_eperm);
+    if (A->g_perm) (void)hipFree(A->g_perm);
     if (A->eig_host) (void)hipHostFree(A->eig_host);
     for (int i = 0; i < 2; ++i)
         if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);

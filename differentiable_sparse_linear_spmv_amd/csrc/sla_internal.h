@@ -101,6 +101,7 @@ struct CgArgs {
     int32_t groups;          // grouped batch: number of groups (r, p0, p1, q, vals, xg grouped)
     int32_t cap;             // grouped batch: entries per tile staged (kGCapSmall or kGCapLarge)
     double* xg;              // grouped batch: x in the grouped layout
+    const int32_t* gperm;    // grouped batch on a reordered pattern: row i is the caller's row gperm[i]
     // SparseTensorList (distinct patterns, packed block-diagonally; null otherwise):
     // system s owns tiles [list_tiles[s], list_tiles[s + 1]) and workgroups
     // [list_wg[s], list_wg[s + 1]) of a one-dimensional grid (the same for every kernel);
@@ -147,6 +148,10 @@ hipError_t launch_lz(int which, const LzArgs& a, int64_t j, double nrm, int last
 hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col, const double* U, const double* g,
                            int k, int64_t n, int64_t nnz, double* gvals, hipStream_t s);
 
+// Bandwidth-reducing order of a square pattern (reverse Cuthill-McKee, host code,
+// sla_reorder.hip): perm[new] = old.  rp / col are host copies of the pattern.
+void rcm_order(const int32_t* rp, const int32_t* col, int64_t n, int32_t* perm);
+
 // Wanted eigenpairs of a symmetric tridiagonal matrix (host code, sla_tridiag.hip):
 // diagonal a[0..m), off-diagonal b[0..m-1).  The k largest (descending) or smallest
 // (ascending) eigenvalues into theta[k], unit eigenvectors into S[k][m].
@@ -175,7 +180,9 @@ hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s);   // split
 // Grouped batch: values into the grouped layout, and the CG kernels
 // (which: 0 init, 1 p update, 2 SpMV, 3 update, 4 x back to the caller's layout,
 // 5 the Jacobi diagonal in the grouped layout).
-hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, hipStream_t s);
+// eperm (nullable): entry k of the reordered pattern is entry eperm[k] of the caller's.
+hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, const int32_t* eperm,
+                             hipStream_t s);
 hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s);
 // BiCGStab (which: 0 init, 1 p update, 2 v = A p, 3 s, 4 t = A s, 5 update).  Vectors:
 // r in a.r, p in a.p0, v in a.q, s in a.p1, t in a.z; rh = b.

@@ -2090,7 +2090,7 @@ __device__ __forceinline__ bool group_any_running(const int64_t* s_stop, int64_t
 
 // Grouped layout of the values: out[g][k][s] = vals[g * kGroup + s][k].
 __global__ __launch_bounds__(kBlock) void k_group_vals(const double* __restrict__ vals, double* __restrict__ out,
-                                                       int64_t nnz, int groups)
+                                                       int64_t nnz, int groups, const int32_t* __restrict__ eperm)
 {
     const int64_t total = nnz * kGroup;
     const int g = blockIdx.y;
@@ -2098,7 +2098,8 @@ __global__ __launch_bounds__(kBlock) void k_group_vals(const double* __restrict_
          e += static_cast<int64_t>(gridDim.x) * kBlock) {
         const int64_t kk = e / kGroup;
         const int sy = static_cast<int>(e - kk * kGroup);
-        out[static_cast<int64_t>(g) * total + e] = vals[(static_cast<int64_t>(g) * kGroup + sy) * nnz + kk];
+        const int64_t src = eperm ? static_cast<int64_t>(eperm[kk]) : kk;   // reordered pattern: old entry
+        out[static_cast<int64_t>(g) * total + e] = vals[(static_cast<int64_t>(g) * kGroup + sy) * nnz + src];
     }
 }
 
@@ -2120,7 +2121,7 @@ __global__ __launch_bounds__(kBlock) void k_gcg_init(CgArgs a)
         const int64_t i = t * kGRows + tid / kGroup;
         if (i < n) {
             const int64_t e = goff + i * kGroup + sy;
-            const double bv = b[i];
+            const double bv = b[a.gperm ? a.gperm[i] : i];   // reordered pattern: row i was row gperm[i]
             a.r[e] = bv;
             a.xg[e] = 0.0;
             a.p1[e] = 0.0;
@@ -2461,7 +2462,7 @@ __global__ __launch_bounds__(kBlock) void k_gcg_diag(CgArgs a)
     if (tid < kGroup) a.part_aux[static_cast<int64_t>(sys0 + tid) * a.Gu + gc.lb] = flag;
 }
 
-// x[s][i] = xg[i][s]: the solutions back in the caller's layout.
+// x[s][i] = xg[i][s]: the solutions back in the caller's layout (and order).
 __global__ __launch_bounds__(kBlock) void k_gcg_finish(CgArgs a)
 {
     const GroupCoord gc = group_coord(a, a.Gu);
@@ -2473,7 +2474,7 @@ __global__ __launch_bounds__(kBlock) void k_gcg_finish(CgArgs a)
     const int64_t gtiles = (n + kGRows - 1) / kGRows;
     for (int64_t t = gc.lb; t < gtiles; t += a.Gu) {
         const int64_t i = t * kGRows + tid / kGroup;
-        if (i < n) x[i] = a.xg[goff + i * kGroup + sy];
+        if (i < n) x[a.gperm ? a.gperm[i] : i] = a.xg[goff + i * kGroup + sy];
     }
 }
 
@@ -2885,10 +2886,11 @@ hipError_t launch_cg_pupd(const CgArgs& a, int64_t k, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, hipStream_t s)
+hipError_t launch_group_vals(const double* vals, double* out, int64_t nnz, int groups, const int32_t* eperm,
+                             hipStream_t s)
 {
     SLA_LAUNCH(k_group_vals, dim3(grid_for(nnz * kGroup, kBlock, 2048), groups), dim3(kBlock), 0, s, vals, out, nnz,
-               groups);
+               groups, eperm);
     return hipGetLastError();
 }
 

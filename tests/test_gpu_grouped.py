@@ -2,7 +2,8 @@
 
 Shared-pattern batches of at least 8 systems (a multiple of 4) on unstructured
 patterns (the split schedule) run with the systems interleaved in groups of 4: lane
-(row, system), one cache piece per gathered element for four systems.  The bars are
+(row, system), one cache piece per gathered element for four systems, on a reverse
+Cuthill-McKee reordering of the pattern (values, b and x gathered through it).  The bars are
 those of the single-system path against the oracle: iterations within 2 %, x within
 1e-9, lambda and dL/dvals within 1e-8, and 1e-12 over fixed iterations.  Cases: 32
 systems (8 groups: every group pinned to one XCD), 12 systems (3 groups, not pinned),
@@ -159,3 +160,18 @@ def test_grouped_matches_ungrouped(S, mesh, monkeypatch):
     out_u = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
     for a_, b_ in zip(out_g[:3], out_u[:3]):
         assert rel(a_, b_) <= 1e-12
+
+
+def test_grouped_reordering_matches_the_original_order(S, mesh, monkeypatch):
+    # the grouped kernels run on a reverse Cuthill-McKee reordering of the pattern by
+    # default; with SLA_CG_REORDER=0 on the caller's order.  Only the order of the sums
+    # inside a row differs: the same iterates to rounding over 6 fixed iterations, and
+    # the converged solves both meet the oracle's bars.
+    A, b = mesh
+    out_r = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
+    monkeypatch.setenv("SLA_CG_REORDER", "0")
+    out_o = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
+    for a_, b_ in zip(out_r[:3], out_o[:3]):
+        assert rel(a_, b_) <= 1e-12
+    out = solve_pair(S, A, A.vals[:8], b[:8], rtol=1e-8)
+    check_against_oracle(A, A.vals[:8], b[:8], out, rtol=1e-8, systems=[0, 7])
