@@ -10,7 +10,7 @@ Workloads are stand-ins for the 2-D Poisson benchmarks of the torch-sla paper
 SparseTensor described in section 3.1 ("Typed sparse-tensor hierarchy").
 
 Readings where the pages are silent (stencil scale, ordering, coefficient
-field, mesh, loss) are listed in the design doc and restated in each docstring.
+field, mesh, loss) are stated in each generator's docstring.
 All randomness is ``numpy.random.default_rng(seed)`` (PCG64).
 """
 from __future__ import annotations
