@@ -454,11 +454,21 @@ sla_status ensure_reorder(sla_csr* A, hipStream_t s)
         }
         rp2[i + 1] = rp2[i] + static_cast<int32_t>(row.size());
     }
+    auto release = [&]() {
+        for (int32_t** q : {&A->g_rp, &A->g_col, &A->g_eperm, &A->g_perm}) {
+            if (*q) (void)hipFree(*q);
+            *q = nullptr;
+        }
+    };
+    release();   // nothing is left from an earlier attempt that failed
     sla_status st;
-    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_rp), sizeof(int32_t) * (n + 1))) != SLA_OK) return st;
-    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_col), sizeof(int32_t) * col2.size())) != SLA_OK) return st;
-    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_eperm), sizeof(int32_t) * ep.size())) != SLA_OK) return st;
-    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_perm), sizeof(int32_t) * n)) != SLA_OK) return st;
+    if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_rp), sizeof(int32_t) * (n + 1))) != SLA_OK ||
+        (st = dev_alloc(reinterpret_cast<void**>(&A->g_col), sizeof(int32_t) * col2.size())) != SLA_OK ||
+        (st = dev_alloc(reinterpret_cast<void**>(&A->g_eperm), sizeof(int32_t) * ep.size())) != SLA_OK ||
+        (st = dev_alloc(reinterpret_cast<void**>(&A->g_perm), sizeof(int32_t) * n)) != SLA_OK) {
+        release();
+        return st;
+    }
     HIP_TRY(hipMemcpyAsync(A->g_rp, rp2.data(), sizeof(int32_t) * (n + 1), hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(A->g_col, col2.data(), sizeof(int32_t) * col2.size(), hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(A->g_eperm, ep.data(), sizeof(int32_t) * ep.size(), hipMemcpyHostToDevice, s));
@@ -1370,7 +1380,12 @@ sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, cons
     if (row_ptr_bits != 32 && row_ptr_bits != 64) return fail(SLA_ERR_INVALID_ARG, "row_ptr_bits must be 32 or 64");
     if (flags & ~(SLA_SYMMETRIC | SLA_EAGER_TRANSPOSE)) return fail(SLA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    std::unique_ptr<sla_list> L(new (std::nothrow) sla_list);
+    // everything allocated below is released by sla_list_destroy if creation fails
+    struct Guard {
+        sla_list* p;
+        ~Guard() { if (p) (void)sla_list_destroy(p); }
+    } guard{new (std::nothrow) sla_list};
+    sla_list* const L = guard.p;
     if (!L) return fail(SLA_ERR_OOM, "host allocation failed");
     HIP_TRY(hipGetDevice(&L->device));
     L->items = items;
@@ -1457,7 +1472,8 @@ sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, cons
     HIP_TRY(hipMemcpyAsync(L->d_tiles, tile0.data(), sizeof(int64_t) * (items + 1), hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(L->d_rend, rend.data(), sizeof(int64_t) * items, hipMemcpyHostToDevice, s));
     HIP_TRY(hipStreamSynchronize(s));
-    *out = L.release();
+    *out = L;
+    guard.p = nullptr;
     return SLA_OK;
 }
 
