@@ -2254,8 +2254,10 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         const double* __restrict__ vb = vg + static_cast<int64_t>(kb) * kGroup;
         const int32_t* __restrict__ cb = col + kb;
         const int lastv = max(cnt * kGroup - 1, 0), lastc = max(cnt - 1, 0);
+        // the values (every system's, read once per SpMV) stream with the non-temporal
+        // hint, leaving the caches to the gathered operand
 #pragma unroll
-        for (int u = 0; u < UV; ++u) S.v[u] = vb[min(tid + u * kBlock, lastv)];
+        for (int u = 0; u < UV; ++u) S.v[u] = __builtin_nontemporal_load(vb + min(tid + u * kBlock, lastv));
 #pragma unroll
         for (int u = 0; u < UC; ++u) S.c[u] = cb[min(tid + u * kBlock, lastc)];
     };
