@@ -12,7 +12,8 @@ a dropped term, a wrong sign, a wrong or transposed index.
   adjoint    dense LU for lambda = A^-T g and -lambda_i x_j; closed forms on an
              eigenvector right-hand side; the homogeneity invariants; central
              finite differences under the pages' 1e-5 bar (torch-sla, paperpeel
-             section 4.3 "Gradient Verification").
+             section 4.3 "Gradient Verification"); reverse-mode differentiation
+             through the converged CG iterations themselves (section 4.2).
   transpose  involution, symmetric fixed point, scipy's transpose.
 """
 import json
@@ -449,6 +450,54 @@ def test_adjoint_entrywise_fd_nonsymmetric_orientation():
         h = 1e-6
         fd = (loss(h) - loss(-h)) / (2 * h)
         assert abs(fd - bw["gvals"][k]) <= 1e-5 * max(abs(fd), 1e-3 * np.max(np.abs(bw["gvals"])))
+
+
+def test_adjoint_matches_unrolled_reverse_mode():
+    """The pages' naive path (paperpeel section 4.2): backpropagating through the CG
+    iterations themselves, an O(k)-node graph built from a scatter-based SpMV
+    (val * x[col], index_add).  Once the iteration has converged it must give the
+    adjoint's gradients (with respect to A: along symmetric perturbations).  torch autograd on the CPU in float64, 16 x 16 variable-
+    coefficient grid, the same number of iterations as the oracle's solve to 1e-14."""
+    torch = pytest.importorskip("torch")
+    A, b, _ = W.varcoef_poisson5(16, seed=7)
+    f = O.cg(A, b, rtol=1e-14)
+    assert f["state"] == O.CONVERGED
+    K = f["iterations"]
+    rows = torch.from_numpy(np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64))))
+    cols = torch.from_numpy(A.col.astype(np.int64))
+    vals = torch.tensor(A.vals, dtype=torch.float64, requires_grad=True)
+    bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+
+    def spmv(p):
+        return torch.zeros(A.n_rows, dtype=torch.float64).index_add(0, rows, vals * p[cols])
+
+    x = torch.zeros(A.n_rows, dtype=torch.float64)
+    r = bt.clone()
+    p = r.clone()
+    rho = r @ r
+    for _ in range(K):
+        q = spmv(p)
+        alpha = rho / (p @ q)
+        x = x + alpha * p
+        r = r - alpha * q
+        rho1 = r @ r
+        p = r + (rho1 / rho) * p
+        rho = rho1
+    loss = 0.5 * (x @ x)
+    loss.backward()
+    bw = O.solve_backward(A, f["x"], f["x"], symmetric=True, rtol=1e-14)
+    assert abs(loss.item() - 0.5 * float(f["x"] @ f["x"])) <= 1e-13 * loss.item()
+    assert rel_err(bt.grad.numpy(), bw["lam"]) <= 1e-9
+    # CG's recurrence assumes A = A^T, so its derivative along one stored entry alone (a
+    # nonsymmetric perturbation) is not that of A^-1 b -- the pages see the same 1e-4
+    # gap on the matrix gradient.  Along symmetric perturbations both are derivatives
+    # of A^-1 b: the sums over each mirrored pair (i, j), (j, i) must agree.
+    _, _, mirror = O.transpose(A)          # entry of A^T at position e = entry (j, i) of A
+    sym_unrolled = vals.grad.numpy() + vals.grad.numpy()[mirror]
+    sym_adjoint = bw["gvals"] + bw["gvals"][mirror]
+    assert rel_err(sym_unrolled, sym_adjoint) <= 1e-9
+    # while the single-entry values differ at the pages' level
+    assert rel_err(vals.grad.numpy(), bw["gvals"]) <= 1e-2
 
 
 def test_matvec_backward_against_dense():
