@@ -9,7 +9,9 @@ Hellmann-Feynman eigenvalue gradient, against facts fixed by the mathematics.
               and BREAKDOWN when that subspace is smaller than k; the stop test's
               residual bound on the returned pairs, and the Lanczos identity that
               makes beta_m |s[m-1]| their true residual; orthonormal vectors with
-              <u, v0> >= 0; MAX_ITER at the dimension cap.
+              <u, v0> >= 0; MAX_ITER at the dimension cap; thick restart (a
+              basis of 12 or 30 vectors) reaching dense eigh's pairs, with the
+              Lanczos relation intact.
   gradient    central finite differences of dense eigenvalues under a symmetric
               perturbation of the stored values, under the pages' 1e-5 bar (torch-sla,
               paperpeel page, section 4.3, Table 5); the closed form u_i u_j on a
@@ -133,6 +135,28 @@ def test_eigsh_dimension_cap():
     w = np.linalg.eigvalsh(dense(A))
     assert np.all(r["evals"] >= w[0] - 1e-12) and np.all(r["evals"] <= w[-1] + 1e-12)
     assert np.all(r["evals"][:3] >= w[:3] - 1e-12)
+
+
+@pytest.mark.parametrize("which,m", [("smallest", 30), ("largest", 12)])
+def test_eigsh_thick_restart(which, m):
+    # a basis of m vectors restarted from the kept Ritz vectors: the same eigenpairs as
+    # dense eigh, and the Lanczos relation (true residual = beta |s[m-1]|) still holds
+    A, _, _ = W.varcoef_poisson5(20, seed=6)
+    M = dense(A)
+    w, V = np.linalg.eigh(M)
+    v0 = W.rhs_normal(A.n_rows, 9)
+    k = 4
+    r = E.eigsh(A, k, v0, which=which, tol=1e-11, max_dim=m, max_iter=20000)
+    assert r["state"] == O.CONVERGED and r["restarts"] > 0
+    idx = np.arange(A.n_rows - 1, A.n_rows - 1 - k, -1) if which == "largest" else np.arange(k)
+    assert np.abs(r["evals"] - w[idx]).max() <= 1e-12 * np.abs(w).max()
+    for i in range(k):
+        ref = V[:, idx[i]] * np.sign(V[:, idx[i]] @ v0)
+        assert np.linalg.norm(r["evecs"][i] - ref) <= 1e-8
+    check_pairs(A, r, 1e-11)
+    # without the budget to restart, the same basis size stops at MAX_ITER
+    r0 = E.eigsh(A, k, v0, which=which, tol=1e-11, max_dim=m)
+    assert r0["state"] == O.MAX_ITER and r0["iterations"] == m
 
 
 @pytest.mark.parametrize("which", ["largest", "smallest"])

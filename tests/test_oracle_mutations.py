@@ -78,11 +78,15 @@ EIGSH_MUTANTS = {
     "lanczos without reorthogonalization": ("for _ in range(2):", "for _ in range(0):"),
     "lanczos residual from the first component": ("res = b * np.abs(S[m - 1, idx])", "res = b * np.abs(S[0, idx])"),
     "ritz vectors from a shifted basis": ("U = S[:, idx].T @ V[:m]", "U = S[:, idx].T @ V[1:m + 1]"),
-    "largest taken in ascending order": ("np.arange(m - 1, m - 1 - k, -1)", "np.arange(m - k, m)"),
+    "largest taken in ascending order": ("order = np.arange(m - 1, -1, -1) if which", "order = np.arange(m) if which"),
     "sign convention dropped": ("if dot(U[i], v) < 0.0:", "if False:"),
     "gradient weights of the first eigenvalue": ("float(g_evals[m])", "float(g_evals[0])"),
     "gradient of the first eigenvector only": ("pattern_outer(A, evecs[m], evecs[m], sign=1.0)",
                                                "pattern_outer(A, evecs[0], evecs[0], sign=1.0)"),
+    "restart coupling from the first component": ("H[i, l_keep] = H[l_keep, i] = b * S[m - 1, c]",
+                                                  "H[i, l_keep] = H[l_keep, i] = b * S[0, c]"),
+    "restart keeps the wrong end": ("kept = order[:l_keep]", "kept = order[::-1][:l_keep]"),
+    "restart drops the next Lanczos vector": ("V[l_keep] = nxt", "V[l_keep] = 0.0 * nxt"),
 }
 
 
