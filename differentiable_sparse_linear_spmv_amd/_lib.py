@@ -54,12 +54,13 @@ assert C.sizeof(SlaCgInfo) == 32
 
 class SlaEigOpts(C.Structure):
     _fields_ = [("tol", C.c_double), ("max_dim", C.c_int64), ("which", C.c_int32),
-                ("check_every", C.c_int32)]
+                ("check_every", C.c_int32), ("max_iter", C.c_int64), ("keep", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class SlaEigInfo(C.Structure):
     _fields_ = [("iterations", C.c_int64), ("max_res", C.c_double), ("state", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("restarts", C.c_int32)]
 
 
 class SlaError(RuntimeError):

@@ -1125,9 +1125,24 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     if (opts->which != SLA_EIG_LARGEST && opts->which != SLA_EIG_SMALLEST)
         return fail(SLA_ERR_INVALID_ARG, "which must be SLA_EIG_LARGEST or SLA_EIG_SMALLEST");
     if (opts->check_every < 0) return fail(SLA_ERR_INVALID_ARG, "check_every must be >= 0");
+    if (opts->max_iter < 0 || opts->keep < 0) return fail(SLA_ERR_INVALID_ARG, "max_iter and keep must be >= 0");
+    // thick restart when the step budget exceeds the basis size
+    const int64_t total = std::max<int64_t>(max_dim, opts->max_iter);
+    const bool restart = total > max_dim;
+    const int64_t lk = opts->keep > 0 ? opts->keep
+                                      : std::min<int64_t>(max_dim - 1, std::max<int64_t>(k + 1, (max_dim + k) / 2));
+    if (restart) {
+        static_assert(kEigRestartMaxDim == SLA_EIG_RESTART_MAX_DIM && kEigRestartMaxDim <= kLzStage, "caps");
+        if (max_dim > kEigRestartMaxDim)
+            return fail(SLA_ERR_INVALID_ARG, "thick restart needs max_dim <= %lld (got %lld)",
+                        (long long)kEigRestartMaxDim, (long long)max_dim);
+        if (lk < k || lk >= max_dim)
+            return fail(SLA_ERR_INVALID_ARG, "thick restart needs k <= keep < max_dim (keep %lld)", (long long)lk);
+    }
+    const int64_t nS = restart ? std::max<int64_t>(k, lk) : k;   // Ritz coefficient rows
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    std::lock_guard<std::mutex> lk(A->mu);
+    std::lock_guard<std::mutex> guard(A->mu);
     const bool largest = opts->which == SLA_EIG_LARGEST;
     const int rp_bits = A->krp_bits;
     const int64_t ntiles = (n + kTile - 1) / kTile;
@@ -1142,7 +1157,7 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     const size_t sz_md = align256(sizeof(double) * (max_dim + 1));
     const size_t sz_G = align256(sizeof(double) * G);
     const size_t sz_Gu = align256(sizeof(double) * Gu);
-    const size_t sz_S = align256(sizeof(double) * static_cast<size_t>(k) * max_dim);
+    const size_t sz_S = align256(sizeof(double) * static_cast<size_t>(nS) * max_dim);
     const size_t sz_k = align256(sizeof(double) * k);
     const size_t sz_pr = align256(sizeof(double) * 2 * k * Gu);
     const size_t need = sz_V + sz_w + sz_ph + 3 * sz_md + 2 * sz_G + sz_Gu + sz_S + sz_k + sz_pr +
@@ -1157,8 +1172,9 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
         if ((st = dev_alloc(&A->eig_ws, need)) != SLA_OK) return st;
         A->eig_ws_bytes = need;
     }
-    // pinned host staging: alpha, beta, S, theta / scale, partials, state
-    const size_t hneed = sizeof(double) * (2 * max_dim + static_cast<size_t>(k) * max_dim + k + 2 * k * Gu + Gu) +
+    // pinned host staging: alpha, beta, S, theta / scale, partials, restart couplings, state
+    const size_t hneed = sizeof(double) * (2 * max_dim + static_cast<size_t>(nS) * max_dim + k + 2 * k * Gu + Gu +
+                                           max_dim) +
                          sizeof(SysState);
     if (hneed > A->eig_host_bytes) {
         HIP_TRY(hipStreamSynchronize(s));
@@ -1199,10 +1215,11 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     a.Gd = Gd;
     a.k = k;
     double* h_ab = A->eig_host;                 // alpha [max_dim], beta [max_dim]
-    double* h_S = h_ab + 2 * max_dim;           // [k][m]
-    double* h_theta = h_S + static_cast<size_t>(k) * max_dim;
+    double* h_S = h_ab + 2 * max_dim;           // [nS][m]
+    double* h_theta = h_S + static_cast<size_t>(nS) * max_dim;
     double* h_part = h_theta + k;               // [2 k][Gu] (also the |v0|^2 partials)
-    SysState* h_st = reinterpret_cast<SysState*>(h_part + 2 * k * Gu + Gu);
+    double* h_coup = h_part + 2 * k * Gu + Gu;  // [lk] couplings of the kept vectors
+    SysState* h_st = reinterpret_cast<SysState*>(h_coup + max_dim);
 
     // the SpMV (BiCGStab's t = A s mode): operand v_j, product w, partials <v_j, w>
     CgArgs c{};
@@ -1236,10 +1253,13 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     e = timed(SLA_K_LZ_RITZ, s, [&] { return launch_lz(1, a, 0, nrm, 0, s); });
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh start: %s", hipGetErrorString(e));
 
-    auto lanczos_step = [&](int64_t j) -> hipError_t {
+    // Step j.  couple: the first step after a restart, which removes the couplings of the
+    // kept vectors (staged in h) instead of beta_{j-1} v_{j-1} (beta[j-1] is 0 there).
+    auto lanczos_step = [&](int64_t j, bool couple) -> hipError_t {
         c.p1 = a.V + j * n;
         hipError_t e0 = timed(SLA_K_LZ_SPMV, s, [&] { return launch_bs(4, c, j, rp_bits, A->cap, s); });
         if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(2, a, j, 0.0, 0, s); });
+        if (e0 == hipSuccess && couple) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(5, a, j, 0.0, 0, s); });
         for (int pass = 0; pass < 2 && e0 == hipSuccess; ++pass) {
             e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(3, a, j + 1, 0.0, 0, s); });
             if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(4, a, j + 1, 0.0, 0, s); });
@@ -1251,37 +1271,76 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     };
 
     const int64_t chunk = opts->check_every > 0 ? opts->check_every : 16;
-    // beta_j at the rounding level of the reorthogonalized w (<= sqrt(n) eps |T_j|, |T_j|
-    // the largest Gershgorin row sum) means the Krylov space is numerically invariant
+    // beta_j at the rounding level of the reorthogonalized w (<= sqrt(n) eps |T|, |T| the
+    // largest row sum of the projected matrix with beta_j) means the Krylov space is
+    // numerically invariant
     const double inv_level = std::sqrt(static_cast<double>(n)) * DBL_EPSILON;
     double tnorm = 0.0;
-    int64_t j = 0, m_stop = -1;
+    int64_t j = 0, m_stop = -1, steps = 0, jcouple = -1;
+    int32_t restarts = 0;
     int state = SLA_MAX_ITER;
     double max_res = 0.0;
-    std::vector<double> theta(k), res(k);
+    std::vector<double> theta(nS), res(k);
+    // restart mode: the projected matrix of the current basis, [(max_dim + 1)]^2 row-major
+    // (tridiagonal until the first restart, then diag(theta) bordered by the couplings)
+    const int64_t ld = max_dim + 1;
+    std::vector<double> H, Hm;
+    if (restart) {
+        H.assign(static_cast<size_t>(ld) * ld, 0.0);
+        Hm.resize(static_cast<size_t>(max_dim) * max_dim);
+    }
+    auto Hat = [&](int64_t r, int64_t q) -> double& { return H[static_cast<size_t>(r) * ld + q]; };
     while (m_stop < 0) {
-        const int64_t j0 = j, jend = std::min<int64_t>(j + chunk, max_dim);
+        const int64_t j0 = j;
+        int64_t jend = std::min<int64_t>(j + chunk, max_dim);
+        if (restart) jend = std::min<int64_t>(jend, j + (total - steps));
         for (; j < jend; ++j) {
-            if ((e = lanczos_step(j)) != hipSuccess) return fail(SLA_ERR_HIP, "eigsh step: %s", hipGetErrorString(e));
+            if ((e = lanczos_step(j, j == jcouple)) != hipSuccess)
+                return fail(SLA_ERR_HIP, "eigsh step: %s", hipGetErrorString(e));
         }
-        HIP_TRY(hipMemcpyAsync(h_ab, a.alpha, sizeof(double) * jend, hipMemcpyDeviceToHost, s));
-        HIP_TRY(hipMemcpyAsync(h_ab + max_dim, a.beta, sizeof(double) * jend, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipMemcpyAsync(h_ab + j0, a.alpha + j0, sizeof(double) * (jend - j0), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipMemcpyAsync(h_ab + max_dim + j0, a.beta + j0, sizeof(double) * (jend - j0), hipMemcpyDeviceToHost,
+                               s));
         HIP_TRY(hipStreamSynchronize(s));
         const double* al = h_ab;
         const double* be = h_ab + max_dim;
         for (int64_t jj = j0; jj < jend && m_stop < 0; ++jj) {
             const int64_t m = jj + 1;
+            ++steps;
             double b = be[jj];
-            tnorm = std::max(tnorm, std::fabs(al[jj]) + std::fabs(b) + (jj > 0 ? std::fabs(be[jj - 1]) : 0.0));
-            if (b <= inv_level * tnorm) b = 0.0;
-            if (m < k) {
-                if (b == 0.0) {
+            if (!restart) {
+                tnorm = std::max(tnorm, std::fabs(al[jj]) + std::fabs(b) + (jj > 0 ? std::fabs(be[jj - 1]) : 0.0));
+                if (b <= inv_level * tnorm) b = 0.0;
+                if (m < k) {
+                    if (b == 0.0) {
+                        m_stop = m;
+                        state = SLA_BREAKDOWN;
+                    }
+                    continue;
+                }
+                tridiag_eigpairs(al, be, static_cast<int>(m), k, largest, theta.data(), h_S);
+            } else {
+                Hat(jj, jj) = al[jj];
+                Hat(jj, jj + 1) = Hat(jj + 1, jj) = b;
+                double row = 0.0;   // rows above jj keep their sums
+                for (int64_t q = 0; q <= m; ++q) row += std::fabs(Hat(jj, q));
+                tnorm = std::max(tnorm, row);
+                if (b <= inv_level * tnorm) {
+                    b = 0.0;
+                    Hat(jj, jj + 1) = Hat(jj + 1, jj) = 0.0;
+                }
+                if (!(m == max_dim || b == 0.0 || steps == total)) continue;
+                if (m < k) {   // invariant before k Ritz values exist
                     m_stop = m;
                     state = SLA_BREAKDOWN;
+                    continue;
                 }
-                continue;
+                for (int64_t r = 0; r < m; ++r)
+                    std::copy(&Hat(r, 0), &Hat(r, 0) + m, Hm.begin() + static_cast<size_t>(r) * m);
+                const bool may_restart = m == max_dim && b != 0.0 && steps < total;
+                sym_eigpairs(Hm.data(), static_cast<int>(m), static_cast<int>(may_restart ? lk : k), largest,
+                             theta.data(), h_S);
             }
-            tridiag_eigpairs(al, be, static_cast<int>(m), k, largest, theta.data(), h_S);
             bool done = true;
             max_res = 0.0;
             for (int r = 0; r < k; ++r) {
@@ -1292,15 +1351,38 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
             if (done || b == 0.0) {
                 m_stop = m;
                 state = SLA_CONVERGED;
-            } else if (m == max_dim) {
+            } else if (!restart ? m == max_dim : steps == total) {
                 m_stop = m;
                 state = SLA_MAX_ITER;
+            } else if (restart && m == max_dim) {
+                // thick restart: the lk wanted-end Ritz vectors V S^T, then v_m, start the
+                // new basis; the projected matrix becomes diag(theta) bordered by the
+                // couplings beta s_r[m-1] (Wu and Simon 2000)
+                a.m = m;
+                HIP_TRY(hipMemcpyAsync(d_S, h_S, sizeof(double) * lk * m, hipMemcpyHostToDevice, s));
+                e = timed(SLA_K_LZ_RITZ, s, [&] { return launch_lz_restart(a, m, lk, s); });
+                if (e != hipSuccess) return fail(SLA_ERR_HIP, "eigsh restart: %s", hipGetErrorString(e));
+                std::fill(H.begin(), H.end(), 0.0);
+                tnorm = 0.0;
+                for (int64_t r = 0; r < lk; ++r) {
+                    const double cr = b * h_S[static_cast<size_t>(r) * m + m - 1];
+                    Hat(r, r) = theta[r];
+                    Hat(r, lk) = Hat(lk, r) = cr;
+                    h_coup[r] = cr;
+                    tnorm = std::max(tnorm, std::fabs(theta[r]) + std::fabs(cr));
+                }
+                // the first step of the new basis subtracts sum_r c_r v_r through h, and
+                // no beta_{lk-1} v_{lk-1}
+                HIP_TRY(hipMemcpyAsync(a.h, h_coup, sizeof(double) * lk, hipMemcpyHostToDevice, s));
+                HIP_TRY(hipMemsetAsync(a.beta + (lk - 1), 0, sizeof(double), s));
+                j = jcouple = lk;
+                ++restarts;
             }
         }
     }
-    info->iterations = m_stop;
+    info->iterations = steps;
     info->state = state;
-    info->reserved = 0;
+    info->restarts = restarts;
     if (state == SLA_BREAKDOWN) {
         info->max_res = 0.0;
         return SLA_OK;   // d_evals / d_evecs untouched: fewer than k Ritz values exist

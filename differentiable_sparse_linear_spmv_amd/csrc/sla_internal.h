@@ -120,6 +120,7 @@ struct CgArgs {
 // kernels, Gd for the reorthogonalization dots (kLzRows rows each), G for the SpMV.
 constexpr int kLzRows = 1024;      // rows per workgroup of the reorthogonalization dots
 constexpr int kEigMaxK = 32;       // eigenpairs per call, at most
+constexpr int64_t kEigRestartMaxDim = 1024;   // basis size cap with thick restart
 struct LzArgs {
     double* V;
     double* w;
@@ -144,6 +145,10 @@ struct LzArgs {
 // V h (last: with |w|^2 partials), 6 beta_j and v_{j+1}, 7 Ritz vectors with partials,
 // 8 division of the Ritz vectors by their signed norms.
 hipError_t launch_lz(int which, const LzArgs& a, int64_t j, double nrm, int last, hipStream_t s);
+// Thick restart in place: V[r] = sum_{l<m} S[r][l] V[l] for r < lk (S [lk][m] on the
+// device), then V[lk] = V[m].  Needs 1 <= lk < m <= kLzStage.
+constexpr int64_t kLzStage = 8192;   // doubles of V staged in LDS per workgroup (64 KiB)
+hipError_t launch_lz_restart(const LzArgs& a, int64_t m, int64_t lk, hipStream_t s);
 // dL/dvals[e] = sum_r g[r] U[r][row(e)] U[r][col(e)] (Hellmann-Feynman), g and U on the device.
 hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col, const double* U, const double* g,
                            int k, int64_t n, int64_t nnz, double* gvals, hipStream_t s);
@@ -156,6 +161,9 @@ void rcm_order(const int32_t* rp, const int32_t* col, int64_t n, int32_t* perm);
 // diagonal a[0..m), off-diagonal b[0..m-1).  The k largest (descending) or smallest
 // (ascending) eigenvalues into theta[k], unit eigenvectors into S[k][m].
 void tridiag_eigpairs(const double* a, const double* b, int m, int k, bool largest, double* theta, double* S);
+// The same for a dense symmetric H [m][m] (row-major): Householder reduction to
+// tridiagonal form, then tridiag_eigpairs, then the back-transform.
+void sym_eigpairs(const double* H, int m, int k, bool largest, double* theta, double* S);
 
 // Optional timing events for the next single-kernel launch: when set, launchers use
 // hipExtLaunchKernelGGL so the events carry the kernel's own start and end times.

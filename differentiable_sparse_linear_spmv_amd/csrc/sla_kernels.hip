@@ -1845,7 +1845,7 @@ __global__ __launch_bounds__(kBlock) void k_lz_next(LzArgs a, int64_t j)
 }
 
 // u_r = sum_l S[r][l] v_l (l ascending) for r < k, with partials of <u_r, u_r> and
-// <u_r, v_0>.  KK >= k accumulators in registers (rows r >= k compute nothing used).
+// <u_r, v0> (the caller's start vector).  KK >= k accumulators in registers (rows r >= k compute nothing used).
 template <int KK>
 __global__ __launch_bounds__(kBlock) void k_lz_ritz(LzArgs a)
 {
@@ -1865,7 +1865,7 @@ __global__ __launch_bounds__(kBlock) void k_lz_ritz(LzArgs a)
                 acc[r] = acc[r] + p;
             }
         }
-        const double v0 = a.V[i];
+        const double v0 = a.v0[i];
 #pragma unroll
         for (int r = 0; r < KK; ++r) {
             if (r < a.k) a.U[static_cast<int64_t>(r) * a.n + i] = acc[r];
@@ -1884,6 +1884,39 @@ __global__ __launch_bounds__(kBlock) void k_lz_ritz(LzArgs a)
             a.part_ritz[static_cast<int64_t>(2 * r + 1) * a.Gu + blockIdx.x] = sv;
         }
     }
+}
+
+// Thick restart of the basis in place: V[r][i] = sum_{l < m} S[r][l] V[l][i] (l
+// ascending) for r < lk, then V[lk][i] = V[m][i] (the next Lanczos vector).  Each
+// workgroup owns a slice of `rows` consecutive i; it stages that slice of V[0..m) in LDS
+// ([m][rows], m * rows <= kLzStage doubles) before any row is overwritten, so the
+// product needs no second basis.
+__global__ __launch_bounds__(kBlock) void k_lz_restart(LzArgs a, int64_t m, int64_t lk, int rows)
+{
+    extern __shared__ double s_v[];
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * rows;
+    const int nr = static_cast<int>(min(static_cast<int64_t>(rows), a.n - i0));
+    const int64_t staged = m * rows;
+    for (int64_t t = threadIdx.x; t < staged; t += kBlock) {
+        const int64_t l = t / rows;
+        const int c = static_cast<int>(t - l * rows);
+        s_v[t] = c < nr ? a.V[l * a.n + i0 + c] : 0.0;
+    }
+    __syncthreads();
+    const int64_t outs = lk * rows;
+    for (int64_t t = threadIdx.x; t < outs; t += kBlock) {
+        const int64_t r = t / rows;
+        const int c = static_cast<int>(t - r * rows);
+        if (c >= nr) continue;
+        const double* __restrict__ sr = a.S + r * m;
+        double acc = 0.0;
+        for (int64_t l = 0; l < m; ++l) {
+            const double p = sr[l] * s_v[l * rows + c];
+            acc = acc + p;
+        }
+        a.V[r * a.n + i0 + c] = acc;
+    }
+    for (int c = threadIdx.x; c < nr; c += kBlock) a.V[lk * a.n + i0 + c] = a.V[m * a.n + i0 + c];
 }
 
 // u_r /= scale[r] (the signed norm: normalization and sign in one rounding).
@@ -2942,6 +2975,21 @@ hipError_t launch_bs(int which, const CgArgs& a, int64_t k, int rp_bits, int cap
     case 4: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsT>(rp_bits, cap, o), gs, blk, 0, s, a, k); break;
     default: SLA_LAUNCH(k_bs_update, gu, blk, 0, s, a, k); break;
     }
+    return hipGetLastError();
+}
+
+int lz_restart_rows(int64_t m)
+{
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(64, kLzStage / m)));
+}
+
+hipError_t launch_lz_restart(const LzArgs& a, int64_t m, int64_t lk, hipStream_t s)
+{
+    if (m < 1 || m > kLzStage || lk < 1 || lk >= m) return hipErrorInvalidValue;
+    const int rows = lz_restart_rows(m);
+    const dim3 grid(static_cast<unsigned>((a.n + rows - 1) / rows));
+    const size_t lds = sizeof(double) * static_cast<size_t>(m) * rows;
+    SLA_LAUNCH(k_lz_restart, grid, dim3(kBlock), lds, s, a, m, lk, rows);
     return hipGetLastError();
 }
 

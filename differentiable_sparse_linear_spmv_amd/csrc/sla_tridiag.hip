@@ -1,5 +1,6 @@
 // sla_tridiag.hip -- host code: wanted eigenpairs of the small symmetric tridiagonal
-// matrix T that the Lanczos eigensolver builds (sla_eigsh).
+// matrix T that the Lanczos eigensolver builds (sla_eigsh), and of the dense projected
+// matrix of a thick-restarted basis.
 //
 // Eigenvalues by bisection on the Sturm count (the number of negative pivots of the
 // LDL^T factorization of T - x I equals the number of eigenvalues below x), each to
@@ -12,6 +13,7 @@
 #include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <cstddef>
 #include <vector>
 
 #include "sla_internal.h"
@@ -148,6 +150,64 @@ void tridiag_eigpairs(const double* a, const double* b, int m, int k, bool large
         s = std::sqrt(s);
         for (int l = 0; l < m; ++l) y[l] /= s;
     }
+}
+
+// Dense symmetric H (m x m, row-major): Householder reduction H = Q T Q^T (for c = 0 ..
+// m - 3 the reflector I - 2 v v^T zeroes column c below its subdiagonal, applied from
+// both sides as H -= v q^T + q v^T with p = 2 H v, q = p - (v^T p) v, and accumulated
+// into Q; columns already zero there are skipped, so the tridiagonal part of a
+// restarted basis costs nothing), the wanted eigenpairs of T, and back to H's
+// eigenvectors Q y.  O(c m^2) for c columns to reduce.
+void sym_eigpairs(const double* Hm, int m, int k, bool largest, double* theta, double* S)
+{
+    std::vector<double> H(Hm, Hm + static_cast<size_t>(m) * m), Q(static_cast<size_t>(m) * m, 0.0);
+    for (int i = 0; i < m; ++i) Q[static_cast<size_t>(i) * m + i] = 1.0;
+    std::vector<double> v(m), p(m), q(m);
+    auto at = [&](std::vector<double>& X, int r, int c) -> double& { return X[static_cast<size_t>(r) * m + c]; };
+    for (int c = 0; c + 2 < m; ++c) {
+        double tail = 0.0;   // column c below its subdiagonal: already tridiagonal if zero
+        for (int r = c + 2; r < m; ++r) tail += at(H, r, c) * at(H, r, c);
+        if (tail == 0.0) continue;
+        const double nx = std::sqrt(at(H, c + 1, c) * at(H, c + 1, c) + tail);
+        const double x0 = at(H, c + 1, c);
+        const double alpha = x0 >= 0.0 ? -nx : nx;
+        double nv = 0.0;
+        for (int r = c + 1; r < m; ++r) {
+            v[r] = at(H, r, c) - (r == c + 1 ? alpha : 0.0);
+            nv += v[r] * v[r];
+        }
+        nv = std::sqrt(nv);
+        if (nv == 0.0) continue;
+        for (int r = c + 1; r < m; ++r) v[r] /= nv;
+        double K = 0.0;
+        for (int r = c + 1; r < m; ++r) {
+            double t = 0.0;
+            for (int s2 = c + 1; s2 < m; ++s2) t += at(H, r, s2) * v[s2];
+            p[r] = 2.0 * t;
+            K += v[r] * p[r];
+        }
+        for (int r = c + 1; r < m; ++r) q[r] = p[r] - K * v[r];
+        for (int r = c + 1; r < m; ++r)
+            for (int s2 = c + 1; s2 < m; ++s2) at(H, r, s2) -= v[r] * q[s2] + q[r] * v[s2];
+        at(H, c + 1, c) = at(H, c, c + 1) = alpha;
+        for (int r = c + 2; r < m; ++r) at(H, r, c) = at(H, c, r) = 0.0;
+        for (int r = 0; r < m; ++r) {   // Q (I - 2 v v^T)
+            double t = 0.0;
+            for (int s2 = c + 1; s2 < m; ++s2) t += at(Q, r, s2) * v[s2];
+            t *= 2.0;
+            for (int s2 = c + 1; s2 < m; ++s2) at(Q, r, s2) -= t * v[s2];
+        }
+    }
+    std::vector<double> d(m), e(m > 1 ? m - 1 : 1), Y(static_cast<size_t>(k) * m);
+    for (int i = 0; i < m; ++i) d[i] = at(H, i, i);
+    for (int i = 0; i + 1 < m; ++i) e[i] = at(H, i + 1, i);
+    tridiag_eigpairs(d.data(), e.data(), m, k, largest, theta, Y.data());
+    for (int r = 0; r < k; ++r)
+        for (int i = 0; i < m; ++i) {
+            double t = 0.0;
+            for (int c = 0; c < m; ++c) t += at(Q, i, c) * Y[static_cast<size_t>(r) * m + c];
+            S[static_cast<size_t>(r) * m + i] = t;
+        }
 }
 
 }  // namespace sla

@@ -224,8 +224,9 @@ def solve_backward(h: Handle, vals: torch.Tensor, x: torch.Tensor, gx: torch.Ten
 
 
 def eigsh(h: Handle, vals: torch.Tensor, k: int, v0: torch.Tensor, which: str = "largest",
-          tol: float = 1e-10, max_dim: int = 0, check_every: int = 0):
-    """sla_eigsh: k extreme eigenpairs by Lanczos.  Returns (evals [k], evecs [k, n], info)."""
+          tol: float = 1e-10, max_dim: int = 0, check_every: int = 0, max_iter: int = 0, keep: int = 0):
+    """sla_eigsh: k extreme eigenpairs by Lanczos (thick-restarted when max_iter > max_dim).
+    Returns (evals [k], evecs [k, n], info)."""
     if which not in ("largest", "smallest"):
         raise ValueError(f"which must be 'largest' or 'smallest' (got {which!r})")
     _need(vals, "vals", torch.float64, h.nnz, h.device)
@@ -233,12 +234,12 @@ def eigsh(h: Handle, vals: torch.Tensor, k: int, v0: torch.Tensor, which: str = 
     evals = torch.empty(k, dtype=torch.float64, device=h.device)
     evecs = torch.empty((k, h.n_rows), dtype=torch.float64, device=h.device)
     opts = SlaEigOpts(float(tol), int(max_dim), L.SLA_EIG_LARGEST if which == "largest" else L.SLA_EIG_SMALLEST,
-                      int(check_every))
+                      int(check_every), int(max_iter), int(keep), 0)
     info = SlaEigInfo()
     check(L.load().sla_eigsh(h.ptr, _ptr(vals), int(k), _ptr(v0), _ptr(evals), _ptr(evecs), C.byref(opts),
                              C.byref(info), _stream(h.device)))
     return evals, evecs, dict(iterations=info.iterations, max_res=info.max_res, state=info.state,
-                              state_name=L.STATE_NAMES.get(info.state, str(info.state)))
+                              restarts=info.restarts, state_name=L.STATE_NAMES.get(info.state, str(info.state)))
 
 
 def eigsh_backward(h: Handle, evecs: torch.Tensor, gevals: torch.Tensor, gvals: torch.Tensor | None = None):
@@ -379,7 +380,7 @@ class _EigshFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, A, vals, v0, kw):
         evals, evecs, info = eigsh(A.handle, vals.detach(), kw["k"], v0.detach(), which=kw["which"],
-                                   tol=kw["tol"], max_dim=kw["max_dim"])
+                                   tol=kw["tol"], max_dim=kw["max_dim"], max_iter=kw["max_iter"], keep=kw["keep"])
         A.last_eig_info = info
         ctx.A = A
         ctx.save_for_backward(evecs)
@@ -477,15 +478,16 @@ class SparseTensor:
         return x
 
     def eigsh(self, k: int = 6, which: str = "largest", tol: float = 1e-10, max_dim: int = 0,
-              v0: torch.Tensor | None = None):
+              v0: torch.Tensor | None = None, max_iter: int = 0, keep: int = 0):
         """k extreme eigenpairs (Lanczos); the eigenvalues are differentiable with respect to
         vals (Hellmann-Feynman), the eigenvectors carry no gradient.  v0: the start vector;
         by default N(0, 1) from a generator seeded with 0 on the matrix's device.
-        Returns (evals [k], evecs [k, n])."""
+        max_iter > max_dim: thick restart of a basis of max_dim vectors, keeping `keep`
+        Ritz vectors, up to max_iter steps in all.  Returns (evals [k], evecs [k, n])."""
         if v0 is None:
             gen = torch.Generator(device=self.handle.device).manual_seed(0)
             v0 = torch.randn(self.handle.n_rows, dtype=torch.float64, device=self.handle.device, generator=gen)
-        kw = dict(k=k, which=which, tol=tol, max_dim=max_dim)
+        kw = dict(k=k, which=which, tol=tol, max_dim=max_dim, max_iter=max_iter, keep=keep)
         return _EigshFn.apply(self, self.vals, v0, kw)
 
     def info(self, backward: bool = False) -> list[dict]:

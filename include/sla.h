@@ -289,19 +289,24 @@ sla_status sla_list_solve_backward(const sla_list* L, const double* const* d_val
 #define SLA_EIG_LARGEST   0   /* the k largest eigenvalues (algebraic), descending */
 #define SLA_EIG_SMALLEST  1   /* the k smallest eigenvalues (algebraic), ascending */
 #define SLA_EIG_MAX_K     32  /* eigenpairs per call, at most */
+#define SLA_EIG_RESTART_MAX_DIM 1024  /* basis size cap when thick restart is on */
 
 typedef struct {
     double tol;                  /* stop when |A u - theta u| <= tol |theta| for every wanted pair (> 0) */
-    int64_t max_dim;             /* Krylov dimension cap, k <= max_dim <= n (0: min(n, 1000)) */
+    int64_t max_dim;             /* basis size cap, k <= max_dim <= n (0: min(n, 1000)) */
     int32_t which;               /* SLA_EIG_LARGEST or SLA_EIG_SMALLEST */
     int32_t check_every;         /* Lanczos steps between host checks (0: 16) */
+    int64_t max_iter;            /* total Lanczos steps; > max_dim turns on thick restart (0: max_dim) */
+    int32_t keep;                /* Ritz vectors kept at a restart, k <= keep < max_dim
+                                    (0: min(max_dim - 1, max(k + 1, (max_dim + k) / 2))) */
+    int32_t reserved;            /* 0 */
 } sla_eig_opts;
 
 typedef struct {
-    int64_t iterations;          /* Lanczos steps taken = dimension of the Krylov space used */
+    int64_t iterations;          /* Lanczos steps taken (all bases: restarts included) */
     double max_res;              /* largest residual estimate beta_j |s_r[j]| of the returned pairs */
     int32_t state;               /* SLA_CONVERGED, SLA_MAX_ITER or SLA_BREAKDOWN */
-    int32_t reserved;
+    int32_t restarts;            /* thick restarts taken */
 } sla_eig_info;                  /* host struct */
 
 /*
@@ -324,6 +329,16 @@ typedef struct {
  * passes ends the solve (the host checks chunks of steps; the steps past it are
  * discarded).  max_dim steps without convergence: SLA_MAX_ITER with the current Ritz
  * pairs.  An invariant Krylov space of dimension < k: SLA_BREAKDOWN.
+ * Thick restart (Wu and Simon, "Thick-restart Lanczos method for large symmetric
+ * eigenvalue problems", 2000; the pages name Lanczos without a restart scheme), when
+ * max_iter > max_dim: the pairs are tested only when the basis is full (or invariant,
+ * or at max_iter steps); if they fail, the keep wanted-end Ritz vectors V s_r and the
+ * next Lanczos vector become the new basis (in place, on the device), whose projected
+ * matrix is diag(theta_r) bordered by the couplings beta s_r[m-1] (kept on the host,
+ * eigenpairs by Householder reduction); the first step of the new basis removes those
+ * couplings.  SLA_MAX_ITER after max_iter steps.  Needs max_dim <=
+ * SLA_EIG_RESTART_MAX_DIM (SLA_ERR_INVALID_ARG otherwise, and for keep outside
+ * [k, max_dim)).
  * Memory: (max_dim + 1) n doubles for the Lanczos vectors, owned by the handle.
  * Synchronises the calling thread with the stream once per chunk of steps.
  */
