@@ -104,21 +104,41 @@ def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
                 flops_iteration=(4 * nnz + 24 * n) * batch)
 
 
-def eigsh_bytes(n: int, nnz: int, rp_bytes: int, steps: int) -> dict:
-    """Algorithmic HBM bytes of a Lanczos run of `steps` steps (Krylov dimension).
+def lanczos_positions(steps: int, max_dim: int, keep: int) -> list:
+    """Basis position j of every Lanczos step: 0 .. max_dim - 1, then after each thick
+    restart keep .. max_dim - 1 again (no restart: 0 .. steps - 1)."""
+    if max_dim <= 0 or steps <= max_dim:
+        return list(range(steps))
+    pos, left = list(range(max_dim)), steps - max_dim
+    while left > 0:
+        c = min(left, max_dim - keep)
+        pos += list(range(keep, keep + c))
+        left -= c
+    return pos
+
+
+def eigsh_bytes(n: int, nnz: int, rp_bytes: int, steps: int, max_dim: int = 0, keep: int = 0,
+                restarts: int = 0) -> dict:
+    """Algorithmic HBM bytes of a Lanczos run of `steps` steps.
 
       lz_spmv  (per step): values, columns, row pointers + read v_j (the gathers are
                cache traffic), write w                              -> mat + 2 x 8 n
-      lz_orth  (step j): three-term step (read v_j, v_{j-1}, w; write w) 4 x 8 n;
-               two Gram-Schmidt passes, each: dots read V_{0..j} and w, (j + 2) x 8 n,
-               update read V_{0..j} and w, write w, (j + 3) x 8 n; next vector (read
-               w, write v_{j+1}) 2 x 8 n                            -> (4 j + 16) x 8 n
+      lz_orth  (step at basis position j): three-term step (read v_j, v_{j-1}, w; write
+               w) 4 x 8 n; two Gram-Schmidt passes, each: dots read V_{0..j} and w,
+               (j + 2) x 8 n, update read V_{0..j} and w, write w, (j + 3) x 8 n; next
+               vector (read w, write v_{j+1}) 2 x 8 n               -> (4 j + 16) x 8 n
+               plus, on the first step after a restart, the couplings: read V_{0..keep-1}
+               and w, write w                                       -> (keep + 2) x 8 n
+      restart  (per restart, timed with the Ritz kernels): read V_{0..m-1}, write
+               V_{0..keep-1}, copy v_m                               -> (m + keep + 2) x 8 n
       lz_ritz  u_r = V s_r: read V_{0..m-1} once, write k vectors (plus the start)
     """
     mat = 8 * nnz + 4 * nnz + rp_bytes * (n + 1)
     spmv = mat + 2 * 8 * n
-    orth = sum((4 * j + 16) * 8 * n for j in range(steps))
-    return dict(lz_spmv=spmv, lz_orth_total=orth, run=steps * spmv + orth)
+    pos = lanczos_positions(steps, max_dim, keep)
+    orth = sum((4 * j + 16) * 8 * n for j in pos) + restarts * (keep + 2) * 8 * n
+    rst = restarts * (max_dim + keep + 2) * 8 * n
+    return dict(lz_spmv=spmv, lz_orth_total=orth, restart_total=rst, run=steps * spmv + orth + rst)
 
 
 def run_eigsh(args, w, S, torch) -> dict:
@@ -127,7 +147,8 @@ def run_eigsh(args, w, S, torch) -> dict:
     vals, v0, k = w["vals"], w["v0"], w["k"]
 
     def step():
-        ev, U, info = S.eigsh(h, vals, k, v0, which=w["which"], tol=w["tol"])
+        ev, U, info = S.eigsh(h, vals, k, v0, which=w["which"], tol=w["tol"], max_dim=w["max_dim"],
+                              max_iter=w["max_iter"], keep=w["keep"])
         gv = S.eigsh_backward(h, U, torch.ones(k, dtype=torch.float64, device=vals.device))
         return ev, U, gv, info
 
@@ -147,7 +168,8 @@ def run_eigsh(args, w, S, torch) -> dict:
     S.timing.enable(False)
     tq = S.timing.query()
     n, nnz = w["n"], w["nnz"]
-    bm = eigsh_bytes(n, nnz, 4, steps_run)
+    keep = w["keep"] or min(w["max_dim"] - 1, max(k + 1, (w["max_dim"] + k) // 2))
+    bm = eigsh_bytes(n, nnz, 4, steps_run, w["max_dim"], keep, infos[-1]["restarts"])
     orth_ms = tq["lz_orth"]["total_ms"]
     spmv_ms = tq["lz_spmv"]["total_ms"] / max(tq["lz_spmv"]["launches"], 1)
     achieved = bm["lz_orth_total"] / (orth_ms * 1e-3) / 1e9
@@ -219,10 +241,16 @@ def cpu_baseline_eigsh(w, steps: int) -> dict:
     A = w["host"]["A"]
     t0 = time.perf_counter()
     with threadpool_limits(1):
-        OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=steps)
+        if w["max_dim"] and w["max_dim"] < steps:
+            OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=w["max_dim"],
+                     max_iter=steps, keep=w["keep"] or None)
+            how = f"step budget, basis of {w['max_dim']} with thick restart"
+        else:
+            OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=steps)
+            how = "dimension cap"
     dt = time.perf_counter() - t0
     return dict(value=round(steps / dt, 3), unit="Lanczos steps/s", cores=1, kind="oracle",
-                sample=f"oracle Lanczos on this workload, the first {steps} steps (dimension cap), "
+                sample=f"oracle Lanczos on this workload, the first {steps} steps ({how}), "
                        f"single thread", seconds=round(dt, 2))
 
 
@@ -248,10 +276,12 @@ def make_workload(name: str, device):
         return dict(name=name, n=A.n_rows, nnz=A.nnz, batch=1, rp=torch.from_numpy(A.row_ptr).to(device),
                     col=torch.from_numpy(A.col).to(device), vals=torch.from_numpy(A.vals).to(device),
                     v0=torch.from_numpy(c["v0"]).to(device), k=c["k"], which=c["which"], tol=c["tol"],
+                    max_dim=c["max_dim"], max_iter=c["max_iter"], keep=c["keep"],
                     method="eigsh", host=c,
                     desc=f"Lanczos eigsh: {c['k']} {c['which']} eigenpairs of the variable-coefficient "
                          f"Poisson matrix 1024x1024 (kappa=exp(GRF) seed 0), tol {c['tol']}, v0~N(0,1) "
-                         f"seed 3, + Hellmann-Feynman gradient of sum(lambda)")
+                         f"seed 3, + Hellmann-Feynman gradient of sum(lambda)"
+                         + (f"; thick restart, basis {c['max_dim']}" if c["max_iter"] > c["max_dim"] else ""))
     B = A.batch
     vals = torch.from_numpy(np.ascontiguousarray(A.vals.reshape(B, A.nnz) if B > 1 else A.vals))
     b = torch.from_numpy(np.ascontiguousarray(c["b"]))
@@ -400,7 +430,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="poisson1024",
                     choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000",
-                             "convdiff1024", "eigsh_varcoef1024", "poisson_list64"])
+                             "convdiff1024", "eigsh_varcoef1024", "eigsh_tr_varcoef1024", "poisson_list64"])
     ap.add_argument("--cpu-iters", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -469,8 +499,10 @@ def main() -> int:
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
             "data": "synthetic",
             "config": {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "k": w["k"], "which": w["which"],
-                       "tol": w["tol"], "parallelism": "none (1 GPU)", "method": "eigsh"},
-            "lanczos_steps": r["info"]["iterations"], "state": r["info"]["state_name"],
+                       "tol": w["tol"], "max_dim": w["max_dim"], "max_iter": w["max_iter"],
+                       "parallelism": "none (1 GPU)", "method": "eigsh"},
+            "lanczos_steps": r["info"]["iterations"], "restarts": r["info"]["restarts"],
+            "state": r["info"]["state_name"],
             "kernels": {kk: {"launches": v["launches"],
                              "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
                         for kk, v in r["tq"].items() if v["launches"]},

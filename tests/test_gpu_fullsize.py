@@ -244,3 +244,50 @@ def test_fullsize_bicgstab_convdiff(S):
     nx = np.linalg.norm(x)
     assert np.linalg.norm(x - O.spmv_transposed(A, lam)) <= 2 * rtol * nx
     assert np.array_equal(gv, O.pattern_outer(A, lam, x, sign=-1.0))
+
+
+def test_fullsize_eigsh_varcoef1024(S):
+    """eigsh_varcoef1024 and eigsh_tr_varcoef1024 (the 8 largest eigenpairs of the 1M-row
+    varcoef matrix, without and with thick restart of a 32-vector basis), as the
+    benchmark runs them, by what holds at any size: every returned pair's true residual
+    |A u - theta u| (scipy's SpMV on the host) within tol |theta| and equal to the
+    reported estimate (the Lanczos relation), Rayleigh quotients, orthonormal vectors
+    with <u, v0> >= 0, the two runs' eigenvalues within 1e-12 |A| of each other (both
+    converged), and the gradient of sum(lambda) on sampled entries against
+    sum_r u_r[i] u_r[j] taken one entry at a time."""
+    import scipy.sparse as sp
+    runs = {}
+    for name in ("eigsh_varcoef1024", "eigsh_tr_varcoef1024"):
+        c = W.config(name)
+        A = c["A"]
+        print(f"[eigsh full size] {name}", flush=True)
+        h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=True)
+        ev, U, info = S.eigsh(h, dev(A.vals), c["k"], dev(c["v0"]), which=c["which"], tol=c["tol"],
+                              max_dim=c["max_dim"], max_iter=c["max_iter"], keep=c["keep"])
+        gv = host(S.eigsh_backward(h, U, torch.ones(c["k"], dtype=torch.float64, device="cuda")))
+        ev, U = host(ev), host(U)
+        assert info["state"] == O.CONVERGED
+        assert (info["restarts"] > 0) == (c["max_iter"] > c["max_dim"])
+        M = sp.csr_matrix((A.vals, A.col, A.row_ptr.astype(np.int64)), shape=(A.n_rows, A.n_cols))
+        nA = float(np.add.reduceat(np.abs(A.vals), A.row_ptr[:-1].astype(np.int64)).max())
+        assert np.all(np.diff(ev) <= 0)                              # descending from the largest
+        assert np.allclose(U @ U.T, np.eye(c["k"]), atol=1e-12)
+        res = []
+        for r in range(c["k"]):
+            assert U[r] @ c["v0"] >= 0.0
+            Au = M @ U[r]
+            res.append(np.linalg.norm(Au - ev[r] * U[r]))
+            assert res[-1] <= c["tol"] * abs(ev[r]) * (1 + 1e-6) + 1e-12 * nA, (r, res[-1])
+            assert abs(U[r] @ Au - ev[r]) <= 1e-12 * nA
+        assert abs(max(res) - info["max_res"]) <= 1e-3 * info["max_res"] + 1e-12 * nA
+        rng = np.random.default_rng(17)
+        rows = np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+        for e in rng.integers(0, A.nnz, 2000):
+            i, j = rows[e], A.col[e]
+            want = 0.0
+            for r in range(c["k"]):
+                want = want + U[r, i] * U[r, j]
+            assert abs(gv[e] - want) <= 1e-15 * max(1.0, abs(want)), (e, gv[e], want)
+        runs[name] = (ev, nA)
+    (e0, nA), (e1, _) = runs["eigsh_varcoef1024"], runs["eigsh_tr_varcoef1024"]
+    assert np.abs(e0 - e1).max() <= 1e-12 * nA

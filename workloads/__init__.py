@@ -348,6 +348,8 @@ def config(name: str, scale: int | None = None) -> dict:
     eigsh_varcoef1024  the 8 largest eigenpairs of the varcoef matrix on 1024 x 1024
                    (kappa = exp(GRF), seed 0) by Lanczos to tol 1e-10 from v0 ~ N(0, 1)
                    (seed 3), and the Hellmann-Feynman gradient of sum(lambda).
+    eigsh_tr_varcoef1024  the same with thick restart: a basis of 32 vectors (keep 20)
+                   restarted until convergence.
     poisson_list64 a SparseTensorList of 64 five-point Poisson grids of sides 64, 67, ...,
                    253 (distinct patterns, 1.7M rows in all), b_i ~ N(0, 1) seed i, CG to
                    1e-8 + adjoint of sum_i 0.5 |x_i|^2.
@@ -390,11 +392,14 @@ def config(name: str, scale: int | None = None) -> dict:
         return dict(name=name, items=items, b=[rhs_normal(A.n_rows, i) for i, A in enumerate(items)],
                     sizes=sizes, rtol=1e-8, atol=0.0, max_iter=100000, fixed=False, loss="half_sq",
                     method="list")
-    if name == "eigsh_varcoef1024":
+    if name in ("eigsh_varcoef1024", "eigsh_tr_varcoef1024"):
         N = scale or 1024
         A, _, _ = varcoef_poisson5(N, seed=0)
-        return dict(name=name, A=A, v0=rhs_normal(N * N, 3), k=8, which="largest", tol=1e-10,
-                    method="eigsh")
+        c = dict(name=name, A=A, v0=rhs_normal(N * N, 3), k=8, which="largest", tol=1e-10,
+                 method="eigsh", max_dim=0, max_iter=0, keep=0)
+        if name == "eigsh_tr_varcoef1024":
+            c.update(max_dim=32, max_iter=100000)
+        return c
     if name == "poisson13000":
         N = scale or 13000
         return dict(name=name, N=N, A=None, b=None, rtol=0.0, atol=0.0, max_iter=500,
