@@ -102,3 +102,36 @@ def test_eigsh_pins_catch_planted_mistake(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_eigsh.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "pins missed the planted mistake: " + name
+
+
+# The LOBPCG eigensolver (oracle/lobpcg.py), loaded by tests/test_oracle_lobpcg.py
+# through SLA_ORACLE_LOBPCG.  (Leaving out the projection of W against X is not a
+# mistake in effect: the residuals of Ritz pairs are orthogonal to the Ritz space
+# already.)
+LOBPCG = os.path.join(ROOT, "oracle", "lobpcg.py")
+LOBPCG_MUTANTS = {
+    "residual with the wrong sign": ("R = AX - X * theta", "R = AX + X * theta"),
+    "AX not rotated with the Ritz vectors": ("X, AX = S @ Y, AS @ Y", "X, AX = S @ Y, AS[:, :k]"),
+    "largest taken from the smallest end": (
+        "idx = np.arange(len(w) - 1, len(w) - 1 - k, -1) if which == \"largest\" else np.arange(k)",
+        "idx = np.arange(k)"),
+    "cholesky factor not transposed": ("Rinv = np.linalg.inv(L.T)", "Rinv = np.linalg.inv(L)"),
+    "ritz values from the diagonal of H": ("theta, Y = _wanted(S.T @ AS, k, which)",
+                                           "theta, Y = np.diag(S.T @ AS)[:k].copy(), np.eye(S.shape[1])[:, :k]"),
+    "sign convention dropped": ("if U[r] @ X0[r] < 0.0:", "if False:"),
+    "stop test on the absolute residual": ("active = res > tol * np.abs(theta)", "active = res > tol"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LOBPCG_MUTANTS))
+def test_lobpcg_pins_catch_planted_mistake(name, tmp_path):
+    src = open(LOBPCG).read()
+    a, b = LOBPCG_MUTANTS[name]
+    assert a in src, "mutation anchor vanished from the oracle source"
+    mut = tmp_path / "lobpcg_mut.py"
+    mut.write_text(src.replace(a, b, 1))
+    env = dict(os.environ, SLA_ORACLE_LOBPCG=str(mut), OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_lobpcg.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "pins missed the planted mistake: " + name
