@@ -344,15 +344,30 @@ def cpu_baseline(w, iters: int) -> dict:
 
 
 # ------------------------------------------------------------------------------ traffic
-def read_traffic(workload: str):
-    p = os.path.join(ROOT, "profiles", f"cg_spmv_{workload}_traffic.txt")
+def traffic_file(workload: str) -> str:
+    kind = "lz_orth" if workload.startswith("eigsh") else "cg_spmv"
+    return os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.txt")
+
+
+def read_traffic(workload: str, key: str = "bytes_per_launch"):
+    p = traffic_file(workload)
     if not os.path.exists(p):
         return None, "no counter summary"
     with open(p) as f:
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
-    return t.get("bytes_per_launch"), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+    return t.get(key), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+
+
+def calibrate_copy(torch, dev) -> None:
+    """Three plain device copies of COPY_BYTES (the counters' scale), after the run."""
+    src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
@@ -393,6 +408,39 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
                 return v
         return None, 0
 
+    kib = 1024.0
+    sf = COPY_BYTES / (copy_f * kib) if copy_f else 1.0
+    sw = COPY_BYTES / (copy_w * kib) if copy_w else 1.0
+    if workload.startswith("eigsh") or workload == "poisson_list64":
+        # whole runs: the sum over the dispatches of the roofline's kernels, divided by
+        # the runs (a kernel launched a known number of times per run counts them)
+        if workload.startswith("eigsh"):
+            names, per, unit = ["k_lz_three", "k_lz_dots", "k_lz_reduce", "k_lz_axpy", "k_lz_next"], \
+                ("k_lz_norm", 1), "run"
+        else:
+            names, per, unit = ["k_cg_spmv"], ("k_cg_init", 2), "step"
+
+        def total(rows):
+            return sum(val for _, name, val in rows if any(nm in name for nm in names))
+
+        runs = sum(1 for _, name, _ in fr if per[0] in name) / per[1]
+        runs_w = sum(1 for _, name, _ in wr if per[0] in name) / per[1]
+        tf, tw = total(fr), total(wr)
+        cmd = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o p --output-format csv -- "
+               f"python -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
+               "--calibrate-copy; then python bench.py --workload "
+               f"{workload} --summarize-pmc <fetch dir> <write dir>")
+        out = dict(workload=workload, command=cmd, kernel_source_hash=kernel_source_hash(), kernels=names,
+                   unit=unit, runs=[runs, runs_w], fetch_kib_total=tf, write_kib_total=tw,
+                   copy_fetch_kib=copy_f, copy_write_kib=copy_w, fetch_scale=sf, write_scale=sw,
+                   **{f"bytes_per_{unit}": (tf * kib * sf / runs + tw * kib * sw / runs_w)
+                      if runs and runs_w else None})
+        p = traffic_file(workload)
+        with open(p, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out))
+        return
+
     spmv_f, nf = pick(fr, ["k_cg_spmv", "k_gcg_spmv"])
     spmv_w, nw = pick(wr, ["k_cg_spmv", "k_gcg_spmv"])
     upd_f, _ = pick(fr, ["k_cg_update", "k_gcg_update"])
@@ -402,9 +450,6 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
     if upd_f is None:   # BiCGStab
         upd_f, _ = pick(fr, ["k_bs_update"])
         upd_w, _ = pick(wr, ["k_bs_update"])
-    kib = 1024.0
-    sf = COPY_BYTES / (copy_f * kib) if copy_f else 1.0
-    sw = COPY_BYTES / (copy_w * kib) if copy_w else 1.0
     cmd = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o p --output-format csv -- "
            f"python -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
            "--calibrate-copy --fixed-iters 12; then python bench.py --workload "
@@ -415,8 +460,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
                bytes_per_launch=(spmv_f * kib * sf + spmv_w * kib * sw) if spmv_f and spmv_w else None,
                update_bytes_per_launch=(upd_f * kib * sf + upd_w * kib * sw) if upd_f and upd_w else None,
                pupd_bytes_per_launch=(pupd_f * kib * sf + pupd_w * kib * sw) if pupd_f and pupd_w else None)
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    p = os.path.join(ROOT, "profiles", f"cg_spmv_{workload}_traffic.txt")
+    p = traffic_file(workload)
     with open(p, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -459,6 +503,9 @@ def main() -> int:
         import workloads as W
         c = W.config(args.workload)
         r = run_list(args, c, S, torch, dev)
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
+        traffic, traffic_src = read_traffic(args.workload, "bytes_per_step")
         cpu = cpu_baseline_list(c, 150) if (rank == 0 and not args.no_cpu_baseline) else None
         n_tot = sum(A.n_rows for A in c["items"])
         out = {
@@ -478,8 +525,9 @@ def main() -> int:
             "hbm_gbps_per_iteration": round(r["iter_gbps"], 1),
             "roofline": {"bound": "hbm", "kernel": "k_cg_spmv (list mode), all launches of one step",
                          "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": None,
-                         "traffic_source": "no counter summary", "bytes_per_launch": None,
+                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                         "traffic_source": traffic_src, "traffic_unit": "bytes per step (all launches)",
+                         "bytes_per_launch": None,
                          "bytes_per_step": r["spmv_bytes"], "spmv_ms_per_step": round(r["spmv_ms"], 3)},
             "cpu_baseline": cpu,
         }
@@ -492,6 +540,9 @@ def main() -> int:
     method = w["method"]
     if method == "eigsh":
         r = run_eigsh(args, w, S, torch)
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
+        traffic, traffic_src = read_traffic(args.workload, "bytes_per_run")
         cpu = cpu_baseline_eigsh(w, 40) if (rank == 0 and not args.no_cpu_baseline) else None
         out = {
             "metric": METRIC_EIGSH, "value": round(r["value"], 2), "unit": "Lanczos steps/s", "n_gpus": 1,
@@ -512,8 +563,8 @@ def main() -> int:
                          "kernel": "Lanczos reorthogonalization (k_lz_three, k_lz_dots, k_lz_reduce, k_lz_axpy, "
                                    "k_lz_next), all launches of one run",
                          "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": None,
-                         "traffic_source": "no counter summary",
+                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                         "traffic_source": traffic_src, "traffic_unit": "bytes per run (all launches)",
                          "bytes_per_launch": None, "bytes_per_run": r["bm"]["lz_orth_total"],
                          "run_ms": round(r["orth_ms"], 3)},
             "cpu_baseline": cpu,
@@ -605,12 +656,7 @@ def main() -> int:
     wall_gbps = bm["iteration"] * (total_it / B) / wall / 1e9
 
     if args.calibrate_copy:
-        src = torch.empty(COPY_BYTES // 8, dtype=torch.float64, device=dev).normal_()
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate_copy(torch, dev)
 
     cpu = None
     if rank == 0 and not args.no_cpu_baseline:
