@@ -25,15 +25,16 @@ SLA_EIG_LARGEST, SLA_EIG_SMALLEST = 0, 1
 SLA_EIG_MAX_K = 32
 (SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
  SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_GROUP_LAYOUT, SLA_K_BS_SPMV, SLA_K_BS_VEC,
- SLA_K_LZ_SPMV, SLA_K_LZ_ORTH, SLA_K_LZ_RITZ, SLA_K_COUNT) = range(15)
+ SLA_K_LZ_SPMV, SLA_K_LZ_ORTH, SLA_K_LZ_RITZ, SLA_K_LOB_SPMM, SLA_K_LOB_GRAM, SLA_K_LOB_COMB,
+ SLA_K_COUNT) = range(18)
 KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "gather_vals",
                 "transpose", "cg_pupd", "group_layout", "bs_spmv", "bs_vec", "lz_spmv", "lz_orth",
-                "lz_ritz"]
+                "lz_ritz", "lob_spmm", "lob_gram", "lob_comb"]
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
     "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_solve",
-    "sla_list_solve_backward", "sla_eigsh", "sla_eigsh_backward", "sla_timing_enable", "sla_timing_reset",
+    "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable", "sla_timing_reset",
     "sla_timing_collect", "sla_timing_query", "sla_status_string", "sla_last_error", "sla_version",
 ]
 
@@ -119,6 +120,8 @@ def load():
     L.sla_list_solve_backward.restype = st
     L.sla_eigsh.argtypes = [P, P, i32, P, P, P, C.POINTER(SlaEigOpts), C.POINTER(SlaEigInfo), P]
     L.sla_eigsh.restype = st
+    L.sla_lobpcg.argtypes = [P, P, i32, P, P, P, C.POINTER(SlaEigOpts), C.POINTER(SlaEigInfo), P]
+    L.sla_lobpcg.restype = st
     L.sla_eigsh_backward.argtypes = [P, i32, P, P, P, P]
     L.sla_eigsh_backward.restype = st
     L.sla_timing_enable.argtypes = [i32]

@@ -78,6 +78,11 @@ struct sla_csr {
     size_t eig_ws_bytes = 0;
     double* eig_host = nullptr;
     size_t eig_host_bytes = 0;
+    // LOBPCG (sla_lobpcg): block vectors and scratch on the device, a pinned arena
+    void* lob_ws = nullptr;
+    size_t lob_ws_bytes = 0;
+    char* lob_host = nullptr;
+    size_t lob_host_bytes = 0;
     hipEvent_t poll_ev[2] = {nullptr, nullptr};
     std::mutex mu;
 };
@@ -948,6 +953,8 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->g_eperm) (void)hipFree(A->g_eperm);
     if (A->g_perm) (void)hipFree(A->g_perm);
     if (A->eig_host) (void)hipHostFree(A->eig_host);
+    if (A->lob_ws) (void)hipFree(A->lob_ws);
+    if (A->lob_host) (void)hipHostFree(A->lob_host);
     for (int i = 0; i < 2; ++i)
         if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);
     if (prev >= 0 && prev != A->device) (void)hipSetDevice(prev);
@@ -1411,6 +1418,428 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     for (int r = 0; r < k; ++r) h_theta[r] = theta[r];
     HIP_TRY(hipMemcpyAsync(d_evals, h_theta, sizeof(double) * k, hipMemcpyHostToDevice, s));
     HIP_TRY(hipStreamSynchronize(s));
+    hipError_t te = timing_collect();
+    if (te != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(te));
+    return SLA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Cholesky G = L L^T of the symmetrized m x m G (row-major) with the pivot test of the
+// block orthonormalization (every pivot above kOrthPivot times the largest diagonal
+// entry); on success Rinv = (L^T)^-1, upper triangular, by back substitution.
+constexpr double kOrthPivot = 1e-14;
+bool chol_rinv(const std::vector<double>& G0, int m, std::vector<double>& Rinv)
+{
+    std::vector<double> G(static_cast<size_t>(m) * m), L(static_cast<size_t>(m) * m, 0.0);
+    double gmax = 0.0;
+    for (int a = 0; a < m; ++a)
+        for (int b = 0; b < m; ++b) G[a * m + b] = 0.5 * (G0[a * m + b] + G0[b * m + a]);
+    for (int a = 0; a < m; ++a) gmax = std::max(gmax, G[a * m + a]);
+    for (int j = 0; j < m; ++j) {
+        double d = G[j * m + j];
+        for (int p = 0; p < j; ++p) d -= L[j * m + p] * L[j * m + p];
+        if (!(d > kOrthPivot * gmax)) return false;
+        L[j * m + j] = std::sqrt(d);
+        for (int i = j + 1; i < m; ++i) {
+            double t = G[i * m + j];
+            for (int p = 0; p < j; ++p) t -= L[i * m + p] * L[j * m + p];
+            L[i * m + j] = t / L[j * m + j];
+        }
+    }
+    // R = L^T upper; solve R X = I column by column
+    Rinv.assign(static_cast<size_t>(m) * m, 0.0);
+    for (int c = 0; c < m; ++c)
+        for (int i = c; i >= 0; --i) {
+            double t = (i == c) ? 1.0 : 0.0;
+            for (int p = i + 1; p <= c; ++p) t -= L[p * m + i] * Rinv[p * m + c];
+            Rinv[i * m + c] = t / L[i * m + i];
+        }
+    return true;
+}
+
+// Device-side staging of the small per-launch arrays (index lists, coefficient
+// matrices): appended to a pinned arena and copied in stream order; the arena is
+// reset only after the host has synchronized with the stream.
+struct Arena {
+    char* h = nullptr;
+    char* d = nullptr;
+    size_t cap = 0, off = 0;
+    template <class T>
+    const T* put(const T* src, size_t count, hipStream_t s, hipError_t& e)
+    {
+        const size_t bytes = sizeof(T) * count;
+        if (off + bytes > cap) {
+            e = hipErrorOutOfMemory;
+            return nullptr;
+        }
+        std::memcpy(h + off, src, bytes);
+        T* dst = reinterpret_cast<T*>(d + off);
+        e = hipMemcpyAsync(dst, h + off, bytes, hipMemcpyHostToDevice, s);
+        off = (off + bytes + 255) & ~static_cast<size_t>(255);
+        return dst;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const double* d_X0, double* d_evals,
+                      double* d_evecs, const sla_eig_opts* opts, sla_eig_info* info, void* stream)
+{
+    sla_status st = check_common(Ac, 1);
+    if (st != SLA_OK) return st;
+    if (Ac->n_rows != Ac->n_cols) return fail(SLA_ERR_UNSUPPORTED, "lobpcg needs a square matrix");
+    if (!(Ac->flags & SLA_SYMMETRIC))
+        return fail(SLA_ERR_UNSUPPORTED, "lobpcg needs a symmetric matrix (a handle created with SLA_SYMMETRIC)");
+    if (!opts || !info || !d_X0 || !d_evals || !d_evecs || (!d_vals && Ac->nnz > 0))
+        return fail(SLA_ERR_INVALID_ARG, "NULL argument");
+    const int64_t n = Ac->n_rows;
+    if (k < 1 || k > SLA_EIG_MAX_K || 3 * static_cast<int64_t>(k) > n)
+        return fail(SLA_ERR_INVALID_ARG, "k must be in [1, %d] with 3 k <= n (got k %d, n %lld)", SLA_EIG_MAX_K, k,
+                    (long long)n);
+    if (!(opts->tol > 0.0)) return fail(SLA_ERR_INVALID_ARG, "tol must be > 0");
+    if (opts->which != SLA_EIG_LARGEST && opts->which != SLA_EIG_SMALLEST)
+        return fail(SLA_ERR_INVALID_ARG, "which must be SLA_EIG_LARGEST or SLA_EIG_SMALLEST");
+    if (opts->max_iter < 0) return fail(SLA_ERR_INVALID_ARG, "max_iter must be >= 0");
+    static_assert(3 * SLA_EIG_MAX_K <= kBlkMaxCols, "block width");
+    const int64_t max_iter = opts->max_iter > 0 ? opts->max_iter : 1000;
+    const bool largest = opts->which == SLA_EIG_LARGEST;
+    sla_csr* A = const_cast<sla_csr*>(Ac);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> guard(A->mu);
+
+    // workspace: NC block columns, Gram partials and results, combination norm partials
+    const int NC = 14 * k;
+    const int Gg = blk_gram_groups(n), Gc = blk_comb_groups(n);
+    const size_t sz_pool = align256(sizeof(double) * static_cast<size_t>(NC) * n);
+    const size_t sz_gp = align256(sizeof(double) * static_cast<size_t>(Gg) * 9 * k * k);
+    const size_t sz_g = align256(sizeof(double) * 9 * k * k);
+    const size_t sz_cp = align256(sizeof(double) * static_cast<size_t>(Gc) * k);
+    const size_t sz_arena = 1 << 20;
+    const size_t need = sz_pool + sz_gp + sz_g + sz_cp + sz_arena;
+    if (need > A->lob_ws_bytes) {
+        if (A->lob_ws) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(hipFree(A->lob_ws));
+            A->lob_ws = nullptr;
+            A->lob_ws_bytes = 0;
+        }
+        if ((st = dev_alloc(&A->lob_ws, need)) != SLA_OK) return st;
+        A->lob_ws_bytes = need;
+    }
+    const size_t hneed = sz_arena + sz_g;
+    if (hneed > A->lob_host_bytes) {
+        HIP_TRY(hipStreamSynchronize(s));
+        if (A->lob_host) HIP_TRY(hipHostFree(A->lob_host));
+        A->lob_host = nullptr;
+        A->lob_host_bytes = 0;
+        HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&A->lob_host), hneed, hipHostMallocDefault));
+        A->lob_host_bytes = hneed;
+    }
+    char* p = static_cast<char*>(A->lob_ws);
+    double* pool = reinterpret_cast<double*>(p);
+    double* d_gpart = reinterpret_cast<double*>(p + sz_pool);
+    double* d_g = reinterpret_cast<double*>(p + sz_pool + sz_gp);
+    double* d_cpart = reinterpret_cast<double*>(p + sz_pool + sz_gp + sz_g);
+    Arena ar;
+    ar.d = p + sz_pool + sz_gp + sz_g + sz_cp;
+    ar.h = A->lob_host;
+    ar.cap = sz_arena;
+    double* h_g = reinterpret_cast<double*>(A->lob_host + sz_arena);
+
+    using Cols = std::vector<int32_t>;
+    std::vector<int32_t> free_cols;
+    for (int c = NC - 1; c >= 0; --c) free_cols.push_back(c);
+    auto take = [&](int w, Cols& out) -> bool {
+        if (static_cast<int>(free_cols.size()) < w) return false;
+        out.resize(w);
+        for (int i = 0; i < w; ++i) {
+            out[i] = free_cols.back();
+            free_cols.pop_back();
+        }
+        return true;
+    };
+    auto give = [&](const Cols& c) {
+        for (int32_t v : c) free_cols.push_back(v);
+    };
+    auto cat = [](std::initializer_list<const Cols*> parts) {
+        Cols o;
+        for (const Cols* q : parts) o.insert(o.end(), q->begin(), q->end());
+        return o;
+    };
+    hipError_t e = hipSuccess;
+    // Gram <a_i, b_j> of two column sets, read back to the host ([|a|][|b|])
+    auto gram = [&](const double* ba, const Cols& ia, const double* bb, const Cols& ib,
+                    std::vector<double>& out) -> hipError_t {
+        const int32_t* dia = ar.put(ia.data(), ia.size(), s, e);
+        if (e != hipSuccess) return e;
+        const int32_t* dib = ar.put(ib.data(), ib.size(), s, e);
+        if (e != hipSuccess) return e;
+        e = timed(SLA_K_LOB_GRAM, s, [&] {
+            return launch_blk_gram(ba, dia, static_cast<int>(ia.size()), bb, dib, static_cast<int>(ib.size()), n,
+                                   d_gpart, d_g, s);
+        }, false);
+        if (e != hipSuccess) return e;
+        const size_t np = ia.size() * ib.size();
+        if ((e = hipMemcpyAsync(h_g, d_g, sizeof(double) * np, hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+        if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+        ar.off = 0;
+        out.assign(h_g, h_g + np);
+        return hipSuccess;
+    };
+    // out = in Y (Y [|in|][|out|] on the host), optionally the squared column norms
+    auto comb = [&](const double* bin, const Cols& in, const std::vector<double>& Y, double* bout, const Cols& out,
+                    std::vector<double>* norms) -> hipError_t {
+        const int m = static_cast<int>(in.size()), q = static_cast<int>(out.size());
+        const int32_t* din = ar.put(in.data(), in.size(), s, e);
+        if (e != hipSuccess) return e;
+        for (int c0 = 0; c0 < q; c0 += 32) {
+            const int qc = std::min(32, q - c0);
+            std::vector<double> Yc(static_cast<size_t>(m) * qc);
+            for (int j = 0; j < m; ++j)
+                for (int c = 0; c < qc; ++c) Yc[j * qc + c] = Y[static_cast<size_t>(j) * q + c0 + c];
+            const double* dY = ar.put(Yc.data(), Yc.size(), s, e);
+            if (e != hipSuccess) return e;
+            const int32_t* dout = ar.put(out.data() + c0, qc, s, e);
+            if (e != hipSuccess) return e;
+            e = timed(SLA_K_LOB_COMB, s, [&] {
+                return launch_blk_comb(bin, din, m, dY, bout, dout, qc, n, norms ? d_cpart : nullptr, s);
+            });
+            if (e != hipSuccess) return e;
+            if (norms) {
+                e = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_reduce(d_cpart, Gc, qc, d_g, s); });
+                if (e != hipSuccess) return e;
+                if ((e = hipMemcpyAsync(h_g, d_g, sizeof(double) * qc, hipMemcpyDeviceToHost, s)) != hipSuccess)
+                    return e;
+                if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+                ar.off = 0;
+                norms->insert(norms->end(), h_g, h_g + qc);
+            }
+        }
+        return hipSuccess;
+    };
+    auto spmm = [&](const Cols& in, const Cols& out) -> hipError_t {
+        const int32_t* din = ar.put(in.data(), in.size(), s, e);
+        if (e != hipSuccess) return e;
+        const int32_t* dout = ar.put(out.data(), out.size(), s, e);
+        if (e != hipSuccess) return e;
+        return timed(SLA_K_LOB_SPMM, s, [&] {
+            return launch_blk_spmm(A->krp, A->krp_bits, A->col, d_vals, pool, din, pool, dout,
+                                   static_cast<int>(in.size()), n, s);
+        });
+    };
+    // Z (and AZ) orthonormal: unit-scaled columns, then Cholesky QR twice; false when a
+    // column is zero or a pivot fails.  On success Z, AZ name new columns (the inputs
+    // are released unless they live outside the pool).
+    auto orth = [&](const double* bz, Cols& Z, Cols* AZ, bool& ok) -> hipError_t {
+        const int w = static_cast<int>(Z.size());
+        std::vector<double> G, Rinv, T;
+        ok = false;
+        for (int pass = 0; pass < 2; ++pass) {
+            const double* base = pass == 0 ? bz : pool;
+            if ((e = gram(base, Z, base, Z, G)) != hipSuccess) return e;
+            std::vector<double> nrm(w, 1.0);
+            if (pass == 0) {
+                for (int c = 0; c < w; ++c) {
+                    nrm[c] = std::sqrt(G[c * w + c]);
+                    if (!(nrm[c] > 0.0)) return hipSuccess;
+                }
+                for (int a = 0; a < w; ++a)
+                    for (int b = 0; b < w; ++b) G[a * w + b] = G[a * w + b] / (nrm[a] * nrm[b]);
+            }
+            if (!chol_rinv(G, w, Rinv)) return hipSuccess;
+            T.assign(static_cast<size_t>(w) * w, 0.0);
+            for (int a = 0; a < w; ++a)
+                for (int b = 0; b < w; ++b) T[a * w + b] = Rinv[a * w + b] / nrm[a];
+            Cols Z2, AZ2;
+            if (!take(w, Z2)) return hipErrorOutOfMemory;
+            if ((e = comb(base, Z, T, pool, Z2, nullptr)) != hipSuccess) return e;
+            if (base == pool) give(Z);
+            Z = Z2;
+            if (AZ) {
+                if (!take(w, AZ2)) return hipErrorOutOfMemory;
+                if ((e = comb(pool, *AZ, T, pool, AZ2, nullptr)) != hipSuccess) return e;
+                give(*AZ);
+                *AZ = AZ2;
+            }
+        }
+        ok = true;
+        return hipSuccess;
+    };
+    // twice Z = Z - B (B^T Z) (AZ = AZ - AB (B^T Z)) against the orthonormal block B
+    auto project = [&](Cols& Z, Cols* AZ, const Cols& B, const Cols* AB) -> hipError_t {
+        const int w = static_cast<int>(Z.size()), b = static_cast<int>(B.size());
+        std::vector<double> C;
+        for (int pass = 0; pass < 2; ++pass) {
+            if ((e = gram(pool, B, pool, Z, C)) != hipSuccess) return e;   // [b][w]
+            std::vector<double> Y(static_cast<size_t>(w + b) * w, 0.0);
+            for (int c = 0; c < w; ++c) Y[c * w + c] = 1.0;
+            for (int j = 0; j < b; ++j)
+                for (int c = 0; c < w; ++c) Y[(w + j) * w + c] = -C[j * w + c];
+            Cols Z2;
+            if (!take(w, Z2)) return hipErrorOutOfMemory;
+            if ((e = comb(pool, cat({&Z, &B}), Y, pool, Z2, nullptr)) != hipSuccess) return e;
+            give(Z);
+            Z = Z2;
+            if (AZ) {
+                Cols AZ2;
+                if (!take(w, AZ2)) return hipErrorOutOfMemory;
+                if ((e = comb(pool, cat({AZ, AB}), Y, pool, AZ2, nullptr)) != hipSuccess) return e;
+                give(*AZ);
+                *AZ = AZ2;
+            }
+        }
+        return hipSuccess;
+    };
+    // Rayleigh-Ritz on the orthonormal S: theta (k), Y [|S|][k]
+    std::vector<double> theta(k), Ys, Y;
+    auto rayleigh_ritz = [&](const Cols& S, const Cols& AS) -> hipError_t {
+        const int m = static_cast<int>(S.size());
+        std::vector<double> H;
+        if ((e = gram(pool, S, pool, AS, H)) != hipSuccess) return e;
+        std::vector<double> Hs(static_cast<size_t>(m) * m);
+        for (int a = 0; a < m; ++a)
+            for (int b = 0; b < m; ++b) Hs[a * m + b] = 0.5 * (H[a * m + b] + H[b * m + a]);
+        Ys.assign(static_cast<size_t>(k) * m, 0.0);
+        sym_eigpairs(Hs.data(), m, k, largest, theta.data(), Ys.data());
+        Y.assign(static_cast<size_t>(m) * k, 0.0);
+        for (int r = 0; r < k; ++r)
+            for (int j = 0; j < m; ++j) Y[j * k + r] = Ys[static_cast<size_t>(r) * m + j];
+        return hipSuccess;
+    };
+    auto hip_fail = [&](const char* what) { return fail(SLA_ERR_HIP, "lobpcg %s: %s", what, hipGetErrorString(e)); };
+
+    // start: X = orth(X0), AX = A X, Rayleigh-Ritz on X
+    Cols X(k), AX, P, AP;
+    for (int r = 0; r < k; ++r) X[r] = r;   // rows of the caller's X0
+    bool ok = false;
+    if ((e = orth(d_X0, X, nullptr, ok)) != hipSuccess) return hip_fail("start");
+    if (!ok) return fail(SLA_ERR_INVALID_ARG, "start block X0 is rank deficient (or has a zero row)");
+    if (!take(k, AX)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
+    if ((e = spmm(X, AX)) != hipSuccess) return hip_fail("start");
+    if ((e = rayleigh_ritz(X, AX)) != hipSuccess) return hip_fail("start");
+    {
+        Cols X2, AX2;
+        if (!take(k, X2) || !take(k, AX2)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
+        if ((e = comb(pool, X, Y, pool, X2, nullptr)) != hipSuccess) return hip_fail("start");
+        if ((e = comb(pool, AX, Y, pool, AX2, nullptr)) != hipSuccess) return hip_fail("start");
+        give(X);
+        give(AX);
+        X = X2;
+        AX = AX2;
+    }
+    int64_t it = 0;
+    int state = SLA_MAX_ITER;
+    std::vector<double> res(k);
+    while (true) {
+        // residuals R = A X - X diag(theta) and their norms
+        Cols R;
+        if (!take(k, R)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
+        std::vector<double> Yr(static_cast<size_t>(2 * k) * k, 0.0), nr;
+        for (int r = 0; r < k; ++r) {
+            Yr[r * k + r] = 1.0;
+            Yr[(k + r) * k + r] = -theta[r];
+        }
+        if ((e = comb(pool, cat({&AX, &X}), Yr, pool, R, &nr)) != hipSuccess) return hip_fail("residual");
+        std::vector<int> active;
+        for (int r = 0; r < k; ++r) {
+            res[r] = std::sqrt(nr[r]);
+            if (res[r] > opts->tol * std::fabs(theta[r])) active.push_back(r);
+        }
+        if (active.empty() || it == max_iter) {
+            state = active.empty() ? SLA_CONVERGED : SLA_MAX_ITER;
+            give(R);
+            break;
+        }
+        ++it;
+        Cols W, AW, Pa, APa;
+        for (int r = 0; r < k; ++r) {
+            const bool act = std::find(active.begin(), active.end(), r) != active.end();
+            if (act) W.push_back(R[r]);
+            else free_cols.push_back(R[r]);
+            if (!P.empty()) {
+                if (act) {
+                    Pa.push_back(P[r]);
+                    APa.push_back(AP[r]);
+                } else {
+                    free_cols.push_back(P[r]);
+                    free_cols.push_back(AP[r]);
+                }
+            }
+        }
+        P.clear();
+        AP.clear();
+        if ((e = project(W, nullptr, X, nullptr)) != hipSuccess) return hip_fail("projection");
+        bool wok = false;
+        if ((e = orth(pool, W, nullptr, wok)) != hipSuccess) return hip_fail("orthonormalization");
+        if (!wok) {
+            give(W);
+            W.clear();
+        } else {
+            if (!take(static_cast<int>(W.size()), AW)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
+            if ((e = spmm(W, AW)) != hipSuccess) return hip_fail("spmm");
+        }
+        if (!Pa.empty()) {
+            const Cols B = cat({&X, &W}), AB = cat({&AX, &AW});
+            if ((e = project(Pa, &APa, B, &AB)) != hipSuccess) return hip_fail("projection");
+            bool pok = false;
+            if ((e = orth(pool, Pa, &APa, pok)) != hipSuccess) return hip_fail("orthonormalization");
+            if (!pok) {
+                give(Pa);
+                give(APa);
+                Pa.clear();
+                APa.clear();
+            }
+        }
+        const Cols S = cat({&X, &W, &Pa}), AS = cat({&AX, &AW, &APa});
+        const int m = static_cast<int>(S.size());
+        if ((e = rayleigh_ritz(S, AS)) != hipSuccess) return hip_fail("rayleigh-ritz");
+        Cols X2, AX2, P2, AP2;
+        if (!take(k, X2) || !take(k, AX2)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
+        if ((e = comb(pool, S, Y, pool, X2, nullptr)) != hipSuccess) return hip_fail("ritz vectors");
+        if ((e = comb(pool, AS, Y, pool, AX2, nullptr)) != hipSuccess) return hip_fail("ritz vectors");
+        if (m > k) {   // P = S[k:] Y[k:], AP = AS[k:] Y[k:]
+            const Cols Sk(S.begin() + k, S.end()), ASk(AS.begin() + k, AS.end());
+            std::vector<double> Yk(Y.begin() + static_cast<size_t>(k) * k, Y.end());
+            if (!take(k, P2) || !take(k, AP2)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
+            if ((e = comb(pool, Sk, Yk, pool, P2, nullptr)) != hipSuccess) return hip_fail("directions");
+            if ((e = comb(pool, ASk, Yk, pool, AP2, nullptr)) != hipSuccess) return hip_fail("directions");
+        }
+        give(S);
+        give(AS);
+        X = X2;
+        AX = AX2;
+        P = P2;
+        AP = AP2;
+    }
+    // unit Ritz vectors signed by <u_r, X0[r]>, written to d_evecs
+    std::vector<double> Gxx, Gx0;
+    Cols R0(k);
+    for (int r = 0; r < k; ++r) R0[r] = r;
+    if ((e = gram(pool, X, pool, X, Gxx)) != hipSuccess) return hip_fail("output");
+    if ((e = gram(pool, X, d_X0, R0, Gx0)) != hipSuccess) return hip_fail("output");
+    std::vector<double> Yo(static_cast<size_t>(k) * k, 0.0);
+    for (int r = 0; r < k; ++r) {
+        const double nu = std::sqrt(Gxx[r * k + r]);
+        const double sgn = Gx0[r * k + r] < 0.0 ? -1.0 : 1.0;
+        Yo[r * k + r] = 1.0 / (sgn * nu);
+    }
+    if ((e = comb(pool, X, Yo, d_evecs, R0, nullptr)) != hipSuccess) return hip_fail("output");
+    const double* dth = ar.put(theta.data(), theta.size(), s, e);
+    if (e != hipSuccess) return hip_fail("output");
+    HIP_TRY(hipMemcpyAsync(d_evals, dth, sizeof(double) * k, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    ar.off = 0;
+    info->iterations = it;
+    info->state = state;
+    info->restarts = 0;
+    double mr = 0.0;
+    for (int r = 0; r < k; ++r) mr = std::max(mr, res[r]);
+    info->max_res = mr;
     hipError_t te = timing_collect();
     if (te != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(te));
     return SLA_OK;

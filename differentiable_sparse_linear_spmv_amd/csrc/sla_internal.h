@@ -153,6 +153,27 @@ hipError_t launch_lz_restart(const LzArgs& a, int64_t m, int64_t lk, hipStream_t
 hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col, const double* U, const double* g,
                            int k, int64_t n, int64_t nnz, double* gvals, hipStream_t s);
 
+// Block kernels (LOBPCG).  A block is a set of n-vectors, column c at base + c n, named
+// by device index lists; coefficient matrices are device arrays.
+constexpr int kBlkMaxCols = 96;      // columns of a Gram operand (3 x SLA_EIG_MAX_K)
+constexpr int kBlkGramGroups = 512;  // workgroups of a Gram product (partials per pair)
+// out[idx_out[c]] = A in[idx_in[c]], c < q <= kBlkMaxCols.
+hipError_t launch_blk_spmm(const void* rp, int rp_bits, const int32_t* col, const double* vals, const double* in,
+                           const int32_t* idx_in, double* out, const int32_t* idx_out, int q, int64_t n,
+                           hipStream_t s);
+// out[a mv + b] = <A[ia[a]], B[ib[b]]> (a < mu, b < mv, both <= kBlkMaxCols), summed in
+// a fixed order; part: blk_gram_groups(n) * mu * mv doubles of scratch.
+int blk_gram_groups(int64_t n);
+hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib, int mv,
+                           int64_t n, double* part, double* out, hipStream_t s);
+// out[idx_out[c]] = sum_j Y[j][c] in[idx_in[j]] (c < q <= 32, Y [m][q]); part (nullable):
+// blk_comb_groups(n) * q partials of |out[c]|^2, [group][c].  out must not alias in.
+int blk_comb_groups(int64_t n);
+// out[p] = sum over g < G of part[g][p] (g ascending), p < np.
+hipError_t launch_blk_reduce(const double* part, int G, int np, double* out, hipStream_t s);
+hipError_t launch_blk_comb(const double* in, const int32_t* idx_in, int m, const double* Y, double* out,
+                           const int32_t* idx_out, int q, int64_t n, double* part, hipStream_t s);
+
 // Bandwidth-reducing order of a square pattern (reverse Cuthill-McKee, host code,
 // sla_reorder.hip): perm[new] = old.  rp / col are host copies of the pattern.
 void rcm_order(const int32_t* rp, const int32_t* col, int64_t n, int32_t* perm);

@@ -1704,6 +1704,12 @@ __device__ __forceinline__ double ld_uniform(const double* p, int64_t i)
     return ((cptr)(p))[i];
 }
 
+__device__ __forceinline__ int32_t ld_uniform_i(const int32_t* p, int64_t i)
+{
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    return ((cptr)(p))[i];
+}
+
 // Rows of this workgroup's grid-stride walk: i = blockIdx.x * kBlock + tid + t * stride.
 #define LZ_ROWS(i, n)                                                                          \
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < (n);       \
@@ -1903,18 +1909,31 @@ __global__ __launch_bounds__(kBlock) void k_lz_restart(LzArgs a, int64_t m, int6
         s_v[t] = c < nr ? a.V[l * a.n + i0 + c] : 0.0;
     }
     __syncthreads();
-    const int64_t outs = lk * rows;
-    for (int64_t t = threadIdx.x; t < outs; t += kBlock) {
-        const int64_t r = t / rows;
-        const int c = static_cast<int>(t - r * rows);
-        if (c >= nr) continue;
-        const double* __restrict__ sr = a.S + r * m;
-        double acc = 0.0;
-        for (int64_t l = 0; l < m; ++l) {
-            const double p = sr[l] * s_v[l * rows + c];
-            acc = acc + p;
+    if (rows == 64) {   // one output row per wave and trip: S[r][.] is wave-uniform
+        const int lane = threadIdx.x & 63;
+        for (int64_t r0 = threadIdx.x >> 6; r0 < lk; r0 += kBlock / 64) {
+            const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(r0));
+            double acc = 0.0;
+            for (int64_t l = 0; l < m; ++l) {
+                const double p = ld_uniform(a.S, r * m + l) * s_v[l * 64 + lane];
+                acc = acc + p;
+            }
+            if (lane < nr) a.V[r * a.n + i0 + lane] = acc;
         }
-        a.V[r * a.n + i0 + c] = acc;
+    } else {
+        const int64_t outs = lk * rows;
+        for (int64_t t = threadIdx.x; t < outs; t += kBlock) {
+            const int64_t r = t / rows;
+            const int c = static_cast<int>(t - r * rows);
+            if (c >= nr) continue;
+            const double* __restrict__ sr = a.S + r * m;
+            double acc = 0.0;
+            for (int64_t l = 0; l < m; ++l) {
+                const double p = sr[l] * s_v[l * rows + c];
+                acc = acc + p;
+            }
+            a.V[r * a.n + i0 + c] = acc;
+        }
     }
     for (int c = threadIdx.x; c < nr; c += kBlock) a.V[lk * a.n + i0 + c] = a.V[m * a.n + i0 + c];
 }
@@ -1929,6 +1948,155 @@ __global__ __launch_bounds__(kBlock) void k_lz_scale(LzArgs a)
         }
     }
 }
+// ------------------------------------------------------------------ block kernels (LOBPCG)
+// Blocks are sets of column vectors of length n, each contiguous, named by index lists
+// into a base array (column c at base + c n); the lists and the small coefficient
+// matrices live on the device and are read as scalar loads.
+
+// out[c] = A in[c] for c < q: every row's entries are read once per CH columns; each
+// sum runs over the row's entries in ascending order, products rounded.
+template <typename RP, int CH>
+__global__ __launch_bounds__(kBlock) void k_blk_spmm(const RP* __restrict__ rp, const int32_t* __restrict__ col,
+                                                     const double* __restrict__ vals, const double* __restrict__ in,
+                                                     const int32_t* __restrict__ idx_in, double* __restrict__ out,
+                                                     const int32_t* __restrict__ idx_out, int q, int64_t n)
+{
+    LZ_ROWS(i, n) {
+        const int64_t e0 = ld_rp(rp, i), e1 = ld_rp(rp, i + 1);
+        for (int c0 = 0; c0 < q; c0 += CH) {
+            const double* __restrict__ x[CH];
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                const int c = c0 + u < q ? c0 + u : c0;
+                x[u] = in + static_cast<int64_t>(ld_uniform_i(idx_in, c)) * n;
+            }
+            double acc[CH];
+#pragma unroll
+            for (int u = 0; u < CH; ++u) acc[u] = 0.0;
+            for (int64_t e = e0; e < e1; ++e) {
+                const double v = vals[e];
+                const int32_t j = col[e];
+#pragma unroll
+                for (int u = 0; u < CH; ++u) {
+                    const double p = v * x[u][j];
+                    acc[u] = acc[u] + p;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                if (c0 + u < q) out[static_cast<int64_t>(ld_uniform_i(idx_out, c0 + u)) * n + i] = acc[u];
+        }
+    }
+}
+
+// Partial Gram products part[g][a mv + b] = sum over this workgroup's row slices of
+// A_a[i] B_b[i] (a < mu, b < mv).  Slices of kGramRows rows, staged in LDS with a
+// padded stride (no bank conflicts); pair p = tid + s kBlock takes PP accumulators.
+constexpr int kGramRows = 32;
+constexpr int kGramPad = kGramRows + 1;
+template <int PP>
+__global__ __launch_bounds__(kBlock) void k_blk_gram(const double* __restrict__ A, const int32_t* __restrict__ ia,
+                                                     int mu, const double* __restrict__ B,
+                                                     const int32_t* __restrict__ ib, int mv, int64_t n,
+                                                     double* __restrict__ part)
+{
+    __shared__ double s_a[kBlkMaxCols * kGramPad];
+    __shared__ double s_b[kBlkMaxCols * kGramPad];
+    const int tid = threadIdx.x;
+    const int np = mu * mv;
+    double acc[PP];
+    int pa[PP], pb[PP];
+#pragma unroll
+    for (int u = 0; u < PP; ++u) {
+        acc[u] = 0.0;
+        const int p = min(tid + u * kBlock, np - 1);
+        pa[u] = p / mv;
+        pb[u] = p - pa[u] * mv;
+    }
+    const int64_t nslices = (n + kGramRows - 1) / kGramRows;
+    for (int64_t sl = blockIdx.x; sl < nslices; sl += gridDim.x) {
+        const int64_t r0 = sl * kGramRows;
+        const int nr = static_cast<int>(min(static_cast<int64_t>(kGramRows), n - r0));
+        for (int t = tid; t < mu * kGramRows; t += kBlock) {
+            const int c = t / kGramRows, r = t - c * kGramRows;
+            s_a[c * kGramPad + r] = r < nr ? A[static_cast<int64_t>(ld_uniform_i(ia, c)) * n + r0 + r] : 0.0;
+        }
+        for (int t = tid; t < mv * kGramRows; t += kBlock) {
+            const int c = t / kGramRows, r = t - c * kGramRows;
+            s_b[c * kGramPad + r] = r < nr ? B[static_cast<int64_t>(ld_uniform_i(ib, c)) * n + r0 + r] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < PP; ++u) {
+            const double* __restrict__ xa = s_a + pa[u] * kGramPad;
+            const double* __restrict__ xb = s_b + pb[u] * kGramPad;
+            double t = acc[u];
+            for (int r = 0; r < kGramRows; ++r) {
+                const double p = xa[r] * xb[r];
+                t = t + p;
+            }
+            acc[u] = t;
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < PP; ++u) {
+        const int p = tid + u * kBlock;
+        if (p < np) part[static_cast<int64_t>(blockIdx.x) * np + p] = acc[u];
+    }
+}
+
+// out[p] = sum over g < G of part[g][p] (g ascending), p < np.
+__global__ __launch_bounds__(kBlock) void k_blk_reduce(const double* __restrict__ part, int G, int np,
+                                                       double* __restrict__ out)
+{
+    const int p = blockIdx.x * kBlock + threadIdx.x;
+    if (p >= np) return;
+    double s = 0.0;
+    for (int g = 0; g < G; ++g) s = s + part[static_cast<int64_t>(g) * np + p];
+    out[p] = s;
+}
+
+// out[c] = sum_j Y[j][c] in[j] (j ascending) for c < q (q <= QQ), Y [m][q]; with part,
+// the partials part[g][c] of |out[c]|^2 over this workgroup's rows.
+template <int QQ>
+__global__ __launch_bounds__(kBlock) void k_blk_comb(const double* __restrict__ in, const int32_t* __restrict__ idx_in,
+                                                     int m, const double* __restrict__ Y, double* __restrict__ out,
+                                                     const int32_t* __restrict__ idx_out, int q, int64_t n,
+                                                     double* __restrict__ part)
+{
+    __shared__ double s_red[kBlock / 64];
+    double nrm[QQ];
+#pragma unroll
+    for (int u = 0; u < QQ; ++u) nrm[u] = 0.0;
+    LZ_ROWS(i, n) {
+        double acc[QQ];
+#pragma unroll
+        for (int u = 0; u < QQ; ++u) acc[u] = 0.0;
+        for (int j = 0; j < m; ++j) {
+            const double v = in[static_cast<int64_t>(ld_uniform_i(idx_in, j)) * n + i];
+#pragma unroll
+            for (int u = 0; u < QQ; ++u) {
+                const double p = ld_uniform(Y, static_cast<int64_t>(j) * q + (u < q ? u : 0)) * v;
+                acc[u] = acc[u] + p;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < QQ; ++u) {
+            if (u < q) out[static_cast<int64_t>(ld_uniform_i(idx_out, u)) * n + i] = acc[u];
+            const double t = acc[u] * acc[u];
+            nrm[u] = nrm[u] + t;
+        }
+    }
+    if (part) {
+#pragma unroll
+        for (int u = 0; u < QQ; ++u) {
+            const double sv = block_sum(nrm[u], s_red);
+            if (threadIdx.x == 0 && u < q) part[static_cast<int64_t>(blockIdx.x) * q + u] = sv;
+        }
+    }
+}
+
 #undef LZ_ROWS
 
 // Hellmann-Feynman gradient on the stored entries: gvals[e] = sum_r g[r] U[r][i] U[r][c]
@@ -2990,6 +3158,74 @@ hipError_t launch_lz_restart(const LzArgs& a, int64_t m, int64_t lk, hipStream_t
     const dim3 grid(static_cast<unsigned>((a.n + rows - 1) / rows));
     const size_t lds = sizeof(double) * static_cast<size_t>(m) * rows;
     SLA_LAUNCH(k_lz_restart, grid, dim3(kBlock), lds, s, a, m, lk, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_blk_spmm(const void* rp, int rp_bits, const int32_t* col, const double* vals, const double* in,
+                           const int32_t* idx_in, double* out, const int32_t* idx_out, int q, int64_t n,
+                           hipStream_t s)
+{
+    if (q < 1 || q > kBlkMaxCols || n < 1) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>((n + kBlock - 1) / kBlock, 4096))), blk(kBlock);
+    if (rp_bits == 64)
+        SLA_LAUNCH((k_blk_spmm<int64_t, 8>), grid, blk, 0, s, static_cast<const int64_t*>(rp), col, vals, in, idx_in,
+                   out, idx_out, q, n);
+    else
+        SLA_LAUNCH((k_blk_spmm<int32_t, 8>), grid, blk, 0, s, static_cast<const int32_t*>(rp), col, vals, in, idx_in,
+                   out, idx_out, q, n);
+    return hipGetLastError();
+}
+
+int blk_gram_groups(int64_t n)
+{
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kBlkGramGroups, (n + kGramRows - 1) / kGramRows)));
+}
+
+hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib, int mv,
+                           int64_t n, double* part, double* out, hipStream_t s)
+{
+    if (mu < 1 || mv < 1 || mu > kBlkMaxCols || mv > kBlkMaxCols || n < 1) return hipErrorInvalidValue;
+    const int np = mu * mv;
+    const int G = blk_gram_groups(n);
+    const dim3 grid(static_cast<unsigned>(G)), blk(kBlock);
+    const int pp = (np + kBlock - 1) / kBlock;
+    if (pp <= 1) SLA_LAUNCH(k_blk_gram<1>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
+    else if (pp <= 2) SLA_LAUNCH(k_blk_gram<2>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
+    else if (pp <= 4) SLA_LAUNCH(k_blk_gram<4>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
+    else if (pp <= 8) SLA_LAUNCH(k_blk_gram<8>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
+    else if (pp <= 16) SLA_LAUNCH(k_blk_gram<16>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
+    else SLA_LAUNCH(k_blk_gram<(kBlkMaxCols * kBlkMaxCols + kBlock - 1) / kBlock>, grid, blk, 0, s, A, ia, mu, B, ib,
+                    mv, n, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>((np + kBlock - 1) / kBlock)), blk, 0, s, part, G, np, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_blk_reduce(const double* part, int G, int np, double* out, hipStream_t s)
+{
+    if (G < 1 || np < 1) return hipErrorInvalidValue;
+    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>((np + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, part, G, np,
+               out);
+    return hipGetLastError();
+}
+
+int blk_comb_groups(int64_t n)
+{
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(1024, (n + kBlock - 1) / kBlock)));
+}
+
+hipError_t launch_blk_comb(const double* in, const int32_t* idx_in, int m, const double* Y, double* out,
+                           const int32_t* idx_out, int q, int64_t n, double* part, hipStream_t s)
+{
+    if (m < 1 || q < 1 || q > 32 || n < 1) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blk_comb_groups(n))), blk(kBlock);
+    if (q <= 1) SLA_LAUNCH(k_blk_comb<1>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+    else if (q <= 2) SLA_LAUNCH(k_blk_comb<2>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+    else if (q <= 4) SLA_LAUNCH(k_blk_comb<4>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+    else if (q <= 8) SLA_LAUNCH(k_blk_comb<8>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+    else if (q <= 16) SLA_LAUNCH(k_blk_comb<16>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+    else SLA_LAUNCH(k_blk_comb<32>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
     return hipGetLastError();
 }
 

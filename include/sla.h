@@ -346,7 +346,37 @@ sla_status sla_eigsh(const sla_csr* A, const double* d_vals, int32_t k, const do
                      double* d_evecs, const sla_eig_opts* opts, sla_eig_info* info, void* stream);
 
 /*
- * Backward of the eigenvalues of sla_eigsh by the Hellmann-Feynman theorem
+ * k extreme eigenpairs of a symmetric matrix by LOBPCG, the block eigensolver the pages
+ * name beside Lanczos (paperpeel page, section 4.3, note to Table 5; they give no
+ * steps).  Knyazev's locally optimal block preconditioned conjugate gradient method
+ * (SIAM J. Sci. Comput. 23(2), 2001), unpreconditioned, with an orthonormal
+ * Rayleigh-Ritz basis (Hetmaniuk and Lehoucq, J. Comput. Phys. 218, 2006):
+ *   X = orth(X0), Rayleigh-Ritz on X; then per iteration R = A X - X diag(theta), the
+ *   pairs with |R_r| <= tol |theta_r| are converged (all: SLA_CONVERGED); the others'
+ *   residuals W and conjugate directions P are made orthonormal against X (and P
+ *   against W) by two projections and Cholesky QR twice on unit-scaled columns (a
+ *   block whose Cholesky pivot falls to 1e-14 of the largest is left out of that
+ *   iteration); Rayleigh-Ritz on S = [X, W, P] gives the new X = S Y and P = the part
+ *   of S Y outside the old X.  A W is the only product with A per iteration.
+ *   d_vals   [nnz]   values; the handle must be SLA_SYMMETRIC (else SLA_ERR_UNSUPPORTED)
+ *   k        1 <= k <= SLA_EIG_MAX_K, 3 k <= n
+ *   d_X0     [k][n]  start block (linearly independent rows, e.g. N(0,1); else
+ *                    SLA_ERR_INVALID_ARG)
+ *   d_evals  [k]     output: the Ritz values, from the wanted end
+ *   d_evecs  [k][n]  output: unit Ritz vectors, signed so that <u_r, X0[r]> >= 0
+ *   opts     tol, which, max_iter (iterations; 0: 1000); max_dim, keep and check_every
+ *            are not used
+ *   info     host output: iterations, max_res (largest |A u - theta u| at the last
+ *            test), state (SLA_CONVERGED or SLA_MAX_ITER)
+ * Memory: 14 k n doubles of block vectors, owned by the handle.  Synchronises the
+ * calling thread with the stream several times per iteration (the small Gram
+ * matrices are factored and solved on the host).
+ */
+sla_status sla_lobpcg(const sla_csr* A, const double* d_vals, int32_t k, const double* d_X0, double* d_evals,
+                      double* d_evecs, const sla_eig_opts* opts, sla_eig_info* info, void* stream);
+
+/*
+ * Backward of the eigenvalues of sla_eigsh or sla_lobpcg by the Hellmann-Feynman theorem
  * (dlambda / dA_ij = u_i u_j for a unit eigenvector u: gist.science Japanese summary,
  * Methodology item 2, eigenvalue bullet; paperpeel section 4.3, Eq. (4)): an O(nnz)
  * outer product on the stored entries, no linear solve.
@@ -380,7 +410,10 @@ enum {
     SLA_K_LZ_SPMV = 11,     /* Lanczos: w = A v_j with <v_j, w> */
     SLA_K_LZ_ORTH = 12,     /* Lanczos: three-term step, reorthogonalization dots and updates, next vector */
     SLA_K_LZ_RITZ = 13,     /* Lanczos: start vector, Ritz vectors, eigenvalue gradient */
-    SLA_K_COUNT = 14
+    SLA_K_LOB_SPMM = 14,    /* LOBPCG: A W for a block W */
+    SLA_K_LOB_GRAM = 15,    /* LOBPCG: Gram products of blocks and their reduction */
+    SLA_K_LOB_COMB = 16,    /* LOBPCG: block combinations S Y (projections, Cholesky QR, Ritz vectors) */
+    SLA_K_COUNT = 17
 };
 sla_status sla_timing_enable(int32_t enable);
 sla_status sla_timing_reset(void);
