@@ -43,6 +43,8 @@ METRIC = "fp64 CG iters/s + achieved HBM GB/s, Poisson 1M/169M DOF; solve+adjoin
 # the nonsymmetric widening (not the headline metric): BiCGStab on convection-diffusion
 METRIC_LIST = "fp64 CG iters/s summed over items + achieved HBM GB/s, SparseTensorList of 64 Poisson grids; solve+adjoint ms"
 METRIC_EIGSH = "fp64 Lanczos steps/s + achieved HBM GB/s, eigsh on a 1M-DOF Poisson-type matrix; eigsh+gradient ms"
+METRIC_LOBPCG = "fp64 LOBPCG iterations/s + achieved HBM GB/s, eigsh on a 1M-DOF Poisson-type matrix; eigsh+gradient ms"
+LOBPCG_FAMILIES = {"lob_spmm": ["k_blk_spmm"], "lob_gram": ["k_blk_gram", "k_blk_reduce"], "lob_comb": ["k_blk_comb"]}
 METRIC_BICGSTAB = "fp64 BiCGStab iters/s + achieved HBM GB/s, convection-diffusion 1M DOF; solve+adjoint ms"
 COPY_BYTES = 1 << 30            # calibration copy: 1 GiB read + 1 GiB written
 
@@ -176,6 +178,54 @@ def run_eigsh(args, w, S, torch) -> dict:
     return dict(value=sum(i["iterations"] for i in infos) / wall, wall=wall, tq=tq, bm=bm, achieved=achieved,
                 spmv_ms=spmv_ms, orth_ms=orth_ms, info=infos[-1],
                 spmv_gbps=bm["lz_spmv"] / (spmv_ms * 1e-3) / 1e9)
+
+
+def run_lobpcg(args, c, S, torch, dev) -> dict:
+    """One step = LOBPCG (k wanted pairs) + the gradient of sum(lambda).  The roofline
+    kernel is the block-kernel family with the most time; its algorithmic bytes are
+    counted by the library per launch (each operand column read once, each output
+    written once, the matrix once per product)."""
+    A = c["A"]
+    h = S.csr_create(torch.from_numpy(A.row_ptr).to(dev), torch.from_numpy(A.col).to(dev), symmetric=True)
+    vals = torch.from_numpy(A.vals).to(dev)
+    X0 = torch.from_numpy(c["X0"]).to(dev)
+    k = c["k"]
+
+    def step():
+        ev, U, info = S.lobpcg(h, vals, k, X0, which=c["which"], tol=c["tol"], max_iter=c["max_iter"])
+        S.eigsh_backward(h, U, torch.ones(k, dtype=torch.float64, device=dev))
+        return info
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    infos = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    S.timing.reset()
+    S.timing.enable(True)
+    step()
+    S.timing.collect()
+    S.timing.enable(False)
+    tq = S.timing.query()
+    fam = max(LOBPCG_FAMILIES, key=lambda f: tq[f]["total_ms"])
+    achieved = tq[fam]["bytes"] / (tq[fam]["total_ms"] * 1e-3) / 1e9
+    return dict(value=sum(i["iterations"] for i in infos) / wall, wall=wall, tq=tq, info=infos[-1], fam=fam,
+                achieved=achieved)
+
+
+def cpu_baseline_lobpcg(c, iters: int) -> dict:
+    """The oracle's LOBPCG (one thread) for a bounded number of iterations."""
+    import oracle.lobpcg as OL
+    from threadpoolctl import threadpool_limits
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        OL.lobpcg(c["A"], c["k"], c["X0"], which=c["which"], tol=1e-300, max_iter=iters)
+    dt = time.perf_counter() - t0
+    return dict(value=round(iters / dt, 3), unit="LOBPCG iterations/s", cores=1, kind="oracle",
+                sample=f"oracle LOBPCG on this workload, the first {iters} iterations, single thread",
+                seconds=round(dt, 2))
 
 
 def run_list(args, c, S, torch, dev) -> dict:
@@ -345,7 +395,7 @@ def cpu_baseline(w, iters: int) -> dict:
 
 # ------------------------------------------------------------------------------ traffic
 def traffic_file(workload: str) -> str:
-    kind = "lz_orth" if workload.startswith("eigsh") else "cg_spmv"
+    kind = "lz_orth" if workload.startswith("eigsh") else "blk" if workload.startswith("lobpcg") else "cg_spmv"
     return os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.txt")
 
 
@@ -411,6 +461,28 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
     kib = 1024.0
     sf = COPY_BYTES / (copy_f * kib) if copy_f else 1.0
     sw = COPY_BYTES / (copy_w * kib) if copy_w else 1.0
+    if workload.startswith("lobpcg"):
+        # per family of block kernels, the sum over one run's dispatches (one gradient
+        # kernel per run counts the runs)
+        runs = sum(1 for _, name, _ in fr if "k_eig_grad" in name)
+        runs_w = sum(1 for _, name, _ in wr if "k_eig_grad" in name)
+        fams = {}
+        for fam, names in LOBPCG_FAMILIES.items():
+            tf = sum(val for _, name, val in fr if any(nm in name for nm in names))
+            tw = sum(val for _, name, val in wr if any(nm in name for nm in names))
+            fams[fam] = dict(kernels=names, fetch_kib_total=tf, write_kib_total=tw,
+                             bytes_per_run=(tf * kib * sf / runs + tw * kib * sw / runs_w) if runs and runs_w else None)
+        cmd = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o p --output-format csv -- "
+               f"python -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
+               "--calibrate-copy; then python bench.py --workload "
+               f"{workload} --summarize-pmc <fetch dir> <write dir>")
+        out = dict(workload=workload, command=cmd, kernel_source_hash=kernel_source_hash(), unit="run",
+                   runs=[runs, runs_w], copy_fetch_kib=copy_f, copy_write_kib=copy_w, fetch_scale=sf,
+                   write_scale=sw, families=fams)
+        with open(traffic_file(workload), "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out))
+        return
     if workload.startswith("eigsh") or workload == "poisson_list64":
         # whole runs: the sum over the dispatches of the roofline's kernels, divided by
         # the runs (a kernel launched a known number of times per run counts them)
@@ -474,7 +546,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="poisson1024",
                     choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000",
-                             "convdiff1024", "eigsh_varcoef1024", "eigsh_tr_varcoef1024", "poisson_list64"])
+                             "convdiff1024", "eigsh_varcoef1024", "eigsh_tr_varcoef1024", "lobpcg_varcoef1024",
+                             "poisson_list64"])
     ap.add_argument("--cpu-iters", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -499,6 +572,50 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "lobpcg_varcoef1024":
+        import workloads as W
+        c = W.config(args.workload)
+        r = run_lobpcg(args, c, S, torch, dev)
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
+        traffic, traffic_src = None, "no counter summary"
+        p = traffic_file(args.workload)
+        if os.path.exists(p):
+            with open(p) as f:
+                t = json.load(f)
+            if t.get("kernel_source_hash") != kernel_source_hash():
+                traffic_src = "kernel changed since the counters were taken"
+            else:
+                traffic = t["families"][r["fam"]]["bytes_per_run"]
+                traffic_src = "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+        cpu = cpu_baseline_lobpcg(c, 20) if (rank == 0 and not args.no_cpu_baseline) else None
+        A = c["A"]
+        fam = r["fam"]
+        out = {
+            "metric": METRIC_LOBPCG, "value": round(r["value"], 2), "unit": "LOBPCG iterations/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * r["wall"] / args.steps, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+            "config": {"workload": f"LOBPCG: {c['k']} {c['which']} eigenpairs of the variable-coefficient Poisson "
+                                   f"matrix 1024x1024 (kappa=exp(GRF) seed 0), tol {c['tol']}, X0[r]~N(0,1) "
+                                   "seed 3+r, + Hellmann-Feynman gradient of sum(lambda)",
+                       "n": A.n_rows, "nnz": A.nnz, "k": c["k"], "which": c["which"], "tol": c["tol"],
+                       "parallelism": "none (1 GPU)", "method": "lobpcg"},
+            "iterations": r["info"]["iterations"], "state": r["info"]["state_name"],
+            "kernels": {kk: {"launches": v["launches"], "total_ms": round(v["total_ms"], 3),
+                             "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None,
+                             "algorithmic_bytes": v["bytes"] or None}
+                        for kk, v in r["tq"].items() if v["launches"]},
+            "roofline": {"bound": "hbm", "kernel": f"{fam} ({', '.join(LOBPCG_FAMILIES[fam])}), all launches of one run",
+                         "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                         "traffic_source": traffic_src, "traffic_unit": "bytes per run (all launches)",
+                         "bytes_per_launch": None, "bytes_per_run": r["tq"][fam]["bytes"],
+                         "run_ms": round(r["tq"][fam]["total_ms"], 3)},
+            "cpu_baseline": cpu,
+        }
+        if rank == 0:
+            print(json.dumps(out), flush=True)
+        return 0
     if args.workload == "poisson_list64":
         import workloads as W
         c = W.config(args.workload)

@@ -34,8 +34,9 @@ KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "g
 EXPORTS = [
     "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
     "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_solve",
-    "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable", "sla_timing_reset",
-    "sla_timing_collect", "sla_timing_query", "sla_status_string", "sla_last_error", "sla_version",
+    "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable",
+    "sla_timing_reset", "sla_timing_collect", "sla_timing_query", "sla_timing_query_bytes", "sla_status_string",
+    "sla_last_error", "sla_version",
 ]
 
 
@@ -132,6 +133,8 @@ def load():
     L.sla_timing_collect.restype = st
     L.sla_timing_query.argtypes = [i32, C.POINTER(i64), C.POINTER(C.c_double)]
     L.sla_timing_query.restype = st
+    L.sla_timing_query_bytes.argtypes = [i32, C.POINTER(C.c_double)]
+    L.sla_timing_query_bytes.restype = st
     L.sla_status_string.argtypes = [st]
     L.sla_status_string.restype = C.c_char_p
     L.sla_last_error.argtypes = []

@@ -132,6 +132,7 @@ sla_status fail(sla_status s, const char* fmt, ...)
 struct Pending {
     int kid;
     hipEvent_t a, b;
+    double bytes;   // algorithmic bytes of what was timed (0 where not counted)
 };
 std::mutex g_tmu;
 bool g_timing = false;
@@ -139,6 +140,7 @@ std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
 int64_t g_launches[SLA_K_COUNT] = {};
 double g_ms[SLA_K_COUNT] = {};
+double g_bytes[SLA_K_COUNT] = {};
 
 hipEvent_t pool_get()
 {
@@ -155,7 +157,7 @@ hipEvent_t pool_get()
 // Time what f() enqueues.  single: f launches exactly one kernel, whose own start
 // and end are recorded (hipExtLaunchKernelGGL events); otherwise events bracket f.
 template <class F>
-hipError_t timed(int kid, hipStream_t s, F&& f, bool single = true)
+hipError_t timed(int kid, hipStream_t s, F&& f, bool single = true, double bytes = 0.0)
 {
     bool on;
     {
@@ -181,7 +183,7 @@ hipError_t timed(int kid, hipStream_t s, F&& f, bool single = true)
         (void)hipEventRecord(b, s);
     }
     std::lock_guard<std::mutex> lk(g_tmu);
-    g_pending.push_back({kid, a, b});
+    g_pending.push_back({kid, a, b, bytes});
     return e;
 }
 
@@ -202,6 +204,7 @@ hipError_t timing_collect()
         if (e == hipSuccess) {
             g_launches[p.kid] += 1;
             g_ms[p.kid] += ms;
+            g_bytes[p.kid] += p.bytes;
         }
         g_pool.push_back(p.a);
         g_pool.push_back(p.b);
@@ -1461,14 +1464,15 @@ bool chol_rinv(const std::vector<double>& G0, int m, std::vector<double>& Rinv)
 }
 
 // Device-side staging of the small per-launch arrays (index lists, coefficient
-// matrices): appended to a pinned arena and copied in stream order; the arena is
-// reset only after the host has synchronized with the stream.
+// matrices): appended to a pinned arena, then one copy in stream order per launch
+// (flush) for everything appended since the last; the arena is reset only after the
+// host has synchronized with the stream.
 struct Arena {
     char* h = nullptr;
     char* d = nullptr;
-    size_t cap = 0, off = 0;
+    size_t cap = 0, off = 0, sent = 0;
     template <class T>
-    const T* put(const T* src, size_t count, hipStream_t s, hipError_t& e)
+    const T* put(const T* src, size_t count, hipError_t& e)
     {
         const size_t bytes = sizeof(T) * count;
         if (off + bytes > cap) {
@@ -1477,10 +1481,18 @@ struct Arena {
         }
         std::memcpy(h + off, src, bytes);
         T* dst = reinterpret_cast<T*>(d + off);
-        e = hipMemcpyAsync(dst, h + off, bytes, hipMemcpyHostToDevice, s);
         off = (off + bytes + 255) & ~static_cast<size_t>(255);
+        e = hipSuccess;
         return dst;
     }
+    hipError_t flush(hipStream_t s)
+    {
+        hipError_t e = hipSuccess;
+        if (off > sent) e = hipMemcpyAsync(d + sent, h + sent, off - sent, hipMemcpyHostToDevice, s);
+        sent = off;
+        return e;
+    }
+    void reset() { off = sent = 0; }
 };
 
 }  // namespace
@@ -1575,19 +1587,20 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
     // Gram <a_i, b_j> of two column sets, read back to the host ([|a|][|b|])
     auto gram = [&](const double* ba, const Cols& ia, const double* bb, const Cols& ib,
                     std::vector<double>& out) -> hipError_t {
-        const int32_t* dia = ar.put(ia.data(), ia.size(), s, e);
+        const int32_t* dia = ar.put(ia.data(), ia.size(), e);
         if (e != hipSuccess) return e;
-        const int32_t* dib = ar.put(ib.data(), ib.size(), s, e);
+        const int32_t* dib = ar.put(ib.data(), ib.size(), e);
         if (e != hipSuccess) return e;
+        if ((e = ar.flush(s)) != hipSuccess) return e;
         e = timed(SLA_K_LOB_GRAM, s, [&] {
             return launch_blk_gram(ba, dia, static_cast<int>(ia.size()), bb, dib, static_cast<int>(ib.size()), n,
                                    d_gpart, d_g, s);
-        }, false);
+        }, false, 8.0 * static_cast<double>(n) * static_cast<double>(ia.size() + ib.size()));
         if (e != hipSuccess) return e;
         const size_t np = ia.size() * ib.size();
         if ((e = hipMemcpyAsync(h_g, d_g, sizeof(double) * np, hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
         if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-        ar.off = 0;
+        ar.reset();
         out.assign(h_g, h_g + np);
         return hipSuccess;
     };
@@ -1595,20 +1608,21 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
     auto comb = [&](const double* bin, const Cols& in, const std::vector<double>& Y, double* bout, const Cols& out,
                     std::vector<double>* norms) -> hipError_t {
         const int m = static_cast<int>(in.size()), q = static_cast<int>(out.size());
-        const int32_t* din = ar.put(in.data(), in.size(), s, e);
+        const int32_t* din = ar.put(in.data(), in.size(), e);
         if (e != hipSuccess) return e;
         for (int c0 = 0; c0 < q; c0 += 32) {
             const int qc = std::min(32, q - c0);
             std::vector<double> Yc(static_cast<size_t>(m) * qc);
             for (int j = 0; j < m; ++j)
                 for (int c = 0; c < qc; ++c) Yc[j * qc + c] = Y[static_cast<size_t>(j) * q + c0 + c];
-            const double* dY = ar.put(Yc.data(), Yc.size(), s, e);
+            const double* dY = ar.put(Yc.data(), Yc.size(), e);
             if (e != hipSuccess) return e;
-            const int32_t* dout = ar.put(out.data() + c0, qc, s, e);
+            const int32_t* dout = ar.put(out.data() + c0, qc, e);
             if (e != hipSuccess) return e;
+            if ((e = ar.flush(s)) != hipSuccess) return e;
             e = timed(SLA_K_LOB_COMB, s, [&] {
                 return launch_blk_comb(bin, din, m, dY, bout, dout, qc, n, norms ? d_cpart : nullptr, s);
-            });
+            }, true, 8.0 * static_cast<double>(n) * (m + qc));
             if (e != hipSuccess) return e;
             if (norms) {
                 e = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_reduce(d_cpart, Gc, qc, d_g, s); });
@@ -1616,21 +1630,26 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
                 if ((e = hipMemcpyAsync(h_g, d_g, sizeof(double) * qc, hipMemcpyDeviceToHost, s)) != hipSuccess)
                     return e;
                 if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-                ar.off = 0;
                 norms->insert(norms->end(), h_g, h_g + qc);
             }
         }
+        if (norms) ar.reset();   // synchronized after the last chunk; din stays valid until then
         return hipSuccess;
     };
     auto spmm = [&](const Cols& in, const Cols& out) -> hipError_t {
-        const int32_t* din = ar.put(in.data(), in.size(), s, e);
+        const int32_t* din = ar.put(in.data(), in.size(), e);
         if (e != hipSuccess) return e;
-        const int32_t* dout = ar.put(out.data(), out.size(), s, e);
+        const int32_t* dout = ar.put(out.data(), out.size(), e);
         if (e != hipSuccess) return e;
+        // values, columns and row pointers once, each input column once (the gathers are
+        // cache traffic), each output column written
+        const double bytes = 12.0 * static_cast<double>(A->nnz) + (A->krp_bits / 8.0) * static_cast<double>(n + 1) +
+                             16.0 * static_cast<double>(n) * static_cast<double>(in.size());
+        if ((e = ar.flush(s)) != hipSuccess) return e;
         return timed(SLA_K_LOB_SPMM, s, [&] {
             return launch_blk_spmm(A->krp, A->krp_bits, A->col, d_vals, pool, din, pool, dout,
                                    static_cast<int>(in.size()), n, s);
-        });
+        }, true, bytes);
     };
     // Z (and AZ) orthonormal: unit-scaled columns, then Cholesky QR twice; false when a
     // column is zero or a pivot fails.  On success Z, AZ name new columns (the inputs
@@ -1829,11 +1848,12 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
         Yo[r * k + r] = 1.0 / (sgn * nu);
     }
     if ((e = comb(pool, X, Yo, d_evecs, R0, nullptr)) != hipSuccess) return hip_fail("output");
-    const double* dth = ar.put(theta.data(), theta.size(), s, e);
+    const double* dth = ar.put(theta.data(), theta.size(), e);
     if (e != hipSuccess) return hip_fail("output");
+    HIP_TRY(ar.flush(s));
     HIP_TRY(hipMemcpyAsync(d_evals, dth, sizeof(double) * k, hipMemcpyDeviceToDevice, s));
     HIP_TRY(hipStreamSynchronize(s));
-    ar.off = 0;
+    ar.reset();
     info->iterations = it;
     info->state = state;
     info->restarts = 0;
@@ -2152,6 +2172,7 @@ sla_status sla_timing_reset(void)
     for (int i = 0; i < SLA_K_COUNT; ++i) {
         g_launches[i] = 0;
         g_ms[i] = 0.0;
+        g_bytes[i] = 0.0;
     }
     return SLA_OK;
 }
@@ -2169,6 +2190,15 @@ sla_status sla_timing_query(int32_t kernel, int64_t* launches, double* total_ms)
     std::lock_guard<std::mutex> lk(g_tmu);
     if (launches) *launches = g_launches[kernel];
     if (total_ms) *total_ms = g_ms[kernel];
+    return SLA_OK;
+}
+
+sla_status sla_timing_query_bytes(int32_t kernel, double* bytes)
+{
+    if (kernel < 0 || kernel >= SLA_K_COUNT) return fail(SLA_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+    if (!bytes) return fail(SLA_ERR_INVALID_ARG, "NULL argument");
+    std::lock_guard<std::mutex> lk(g_tmu);
+    *bytes = g_bytes[kernel];
     return SLA_OK;
 }
 

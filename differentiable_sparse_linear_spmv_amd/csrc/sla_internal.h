@@ -156,13 +156,13 @@ hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col,
 // Block kernels (LOBPCG).  A block is a set of n-vectors, column c at base + c n, named
 // by device index lists; coefficient matrices are device arrays.
 constexpr int kBlkMaxCols = 96;      // columns of a Gram operand (3 x SLA_EIG_MAX_K)
-constexpr int kBlkGramGroups = 512;  // workgroups of a Gram product (partials per pair)
+constexpr int kBlkGramGroups = 1024; // workgroups of a Gram product, at most (partials per pair)
 // out[idx_out[c]] = A in[idx_in[c]], c < q <= kBlkMaxCols.
 hipError_t launch_blk_spmm(const void* rp, int rp_bits, const int32_t* col, const double* vals, const double* in,
                            const int32_t* idx_in, double* out, const int32_t* idx_out, int q, int64_t n,
                            hipStream_t s);
 // out[a mv + b] = <A[ia[a]], B[ib[b]]> (a < mu, b < mv, both <= kBlkMaxCols), summed in
-// a fixed order; part: blk_gram_groups(n) * mu * mv doubles of scratch.
+// a fixed order; part: blk_gram_groups(n) * mu * mv doubles of scratch (at most).
 int blk_gram_groups(int64_t n);
 hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib, int mv,
                            int64_t n, double* part, double* out, hipStream_t s);

@@ -1990,54 +1990,83 @@ __global__ __launch_bounds__(kBlock) void k_blk_spmm(const RP* __restrict__ rp, 
 }
 
 // Partial Gram products part[g][a mv + b] = sum over this workgroup's row slices of
-// A_a[i] B_b[i] (a < mu, b < mv).  Slices of kGramRows rows, staged in LDS with a
-// padded stride (no bank conflicts); pair p = tid + s kBlock takes PP accumulators.
-constexpr int kGramRows = 32;
-constexpr int kGramPad = kGramRows + 1;
+// A_a[i] B_b[i] (a < mu, b < mv).  A slice of R rows of every operand column is staged
+// in LDS (R as large as 32 KiB allows, a multiple of 32, stride R + 1 against bank
+// conflicts), eight loads issued before their stores.  With tpp > 1 (mu mv tpp <=
+// kBlock) each pair is served by tpp threads over the rows r = sub, sub + tpp, ...,
+// their sums added in order of sub at the end; otherwise pair p = tid + u kBlock keeps
+// PP accumulators.
 template <int PP>
 __global__ __launch_bounds__(kBlock) void k_blk_gram(const double* __restrict__ A, const int32_t* __restrict__ ia,
                                                      int mu, const double* __restrict__ B,
-                                                     const int32_t* __restrict__ ib, int mv, int64_t n,
+                                                     const int32_t* __restrict__ ib, int mv, int64_t n, int R, int tpp,
                                                      double* __restrict__ part)
 {
-    __shared__ double s_a[kBlkMaxCols * kGramPad];
-    __shared__ double s_b[kBlkMaxCols * kGramPad];
+    extern __shared__ double s_g[];
+    __shared__ int32_t s_idx[2 * kBlkMaxCols];
     const int tid = threadIdx.x;
+    const int pad = R + 1;
+    const int ncol = mu + mv;
     const int np = mu * mv;
+    for (int t = tid; t < ncol; t += kBlock) s_idx[t] = t < mu ? ia[t] : ib[t - mu];
+    const int sub = tid % tpp;
+    const int lanes = kBlock / tpp;   // pairs served at once
     double acc[PP];
     int pa[PP], pb[PP];
 #pragma unroll
     for (int u = 0; u < PP; ++u) {
         acc[u] = 0.0;
-        const int p = min(tid + u * kBlock, np - 1);
+        const int p = min(tid / tpp + u * lanes, np - 1);
         pa[u] = p / mv;
         pb[u] = p - pa[u] * mv;
     }
-    const int64_t nslices = (n + kGramRows - 1) / kGramRows;
+    __syncthreads();
+    const int64_t nslices = (n + R - 1) / R;
+    const int total = ncol * R;
     for (int64_t sl = blockIdx.x; sl < nslices; sl += gridDim.x) {
-        const int64_t r0 = sl * kGramRows;
-        const int nr = static_cast<int>(min(static_cast<int64_t>(kGramRows), n - r0));
-        for (int t = tid; t < mu * kGramRows; t += kBlock) {
-            const int c = t / kGramRows, r = t - c * kGramRows;
-            s_a[c * kGramPad + r] = r < nr ? A[static_cast<int64_t>(ld_uniform_i(ia, c)) * n + r0 + r] : 0.0;
-        }
-        for (int t = tid; t < mv * kGramRows; t += kBlock) {
-            const int c = t / kGramRows, r = t - c * kGramRows;
-            s_b[c * kGramPad + r] = r < nr ? B[static_cast<int64_t>(ld_uniform_i(ib, c)) * n + r0 + r] : 0.0;
+        const int64_t r0 = sl * R;
+        const int nr = static_cast<int>(min(static_cast<int64_t>(R), n - r0));
+        for (int t0 = tid; t0 < total; t0 += 8 * kBlock) {
+            double v[8];
+            int dst[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u * kBlock;
+                const bool ok = t < total;
+                const int c = ok ? t / R : 0;
+                const int r = t - c * R;
+                const double* __restrict__ base = c < mu ? A : B;
+                v[u] = (ok && r < nr) ? base[static_cast<int64_t>(s_idx[c]) * n + r0 + r] : 0.0;
+                dst[u] = ok ? c * pad + r : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (dst[u] >= 0) s_g[dst[u]] = v[u];
         }
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < PP; ++u) {
-            const double* __restrict__ xa = s_a + pa[u] * kGramPad;
-            const double* __restrict__ xb = s_b + pb[u] * kGramPad;
+            const double* __restrict__ xa = s_g + pa[u] * pad;
+            const double* __restrict__ xb = s_g + (mu + pb[u]) * pad;
             double t = acc[u];
-            for (int r = 0; r < kGramRows; ++r) {
+            for (int r = sub; r < nr; r += tpp) {
                 const double p = xa[r] * xb[r];
                 t = t + p;
             }
             acc[u] = t;
         }
         __syncthreads();
+    }
+    if (tpp > 1) {   // PP == 1: the tpp partial sums of each pair, added in order of sub
+        s_g[tid] = acc[0];
+        __syncthreads();
+        const int p = tid / tpp;
+        if (sub == 0 && p < np) {
+            double t = 0.0;
+            for (int j = 0; j < tpp; ++j) t = t + s_g[tid + j];
+            part[static_cast<int64_t>(blockIdx.x) * np + p] = t;
+        }
+        return;
     }
 #pragma unroll
     for (int u = 0; u < PP; ++u) {
@@ -2046,15 +2075,17 @@ __global__ __launch_bounds__(kBlock) void k_blk_gram(const double* __restrict__ 
     }
 }
 
-// out[p] = sum over g < G of part[g][p] (g ascending), p < np.
+// out[p] = sum over g < G of part[g][p], p < np: one workgroup per p, a fixed order
+// (strided partial sums, then the workgroup tree).
 __global__ __launch_bounds__(kBlock) void k_blk_reduce(const double* __restrict__ part, int G, int np,
                                                        double* __restrict__ out)
 {
-    const int p = blockIdx.x * kBlock + threadIdx.x;
-    if (p >= np) return;
-    double s = 0.0;
-    for (int g = 0; g < G; ++g) s = s + part[static_cast<int64_t>(g) * np + p];
-    out[p] = s;
+    __shared__ double s_red[kBlock / 64];
+    const int p = blockIdx.x;
+    double v = 0.0;
+    for (int g = threadIdx.x; g < G; g += kBlock) v = v + part[static_cast<int64_t>(g) * np + p];
+    v = block_sum(v, s_red);
+    if (threadIdx.x == 0) out[p] = v;
 }
 
 // out[c] = sum_j Y[j][c] in[j] (j ascending) for c < q (q <= QQ), Y [m][q]; with part,
@@ -3178,7 +3209,7 @@ hipError_t launch_blk_spmm(const void* rp, int rp_bits, const int32_t* col, cons
 
 int blk_gram_groups(int64_t n)
 {
-    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kBlkGramGroups, (n + kGramRows - 1) / kGramRows)));
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kBlkGramGroups, (n + 31) / 32)));
 }
 
 hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib, int mv,
@@ -3186,27 +3217,35 @@ hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const dou
 {
     if (mu < 1 || mv < 1 || mu > kBlkMaxCols || mv > kBlkMaxCols || n < 1) return hipErrorInvalidValue;
     const int np = mu * mv;
-    const int G = blk_gram_groups(n);
+    // slice rows: (mu + mv) (R + 1) doubles within 32 KiB of LDS (five workgroups per
+    // CU keep loads in flight while others compute), R a multiple of 32
+    constexpr int kStage = 4000;
+    const int R = std::max(32, std::min(1024, (kStage / (mu + mv) - 1) / 32 * 32));
+    const int64_t nslices = (n + R - 1) / R;
+    const int G = static_cast<int>(std::min<int64_t>(blk_gram_groups(n), nslices));
+    // the LDS holds the staged slice and, at the end, kBlock partial sums
+    const size_t lds = sizeof(double) * std::max<size_t>(static_cast<size_t>(mu + mv) * (R + 1), kBlock);
     const dim3 grid(static_cast<unsigned>(G)), blk(kBlock);
+    int tpp = 1;   // threads per pair: a power of 2 with np tpp <= kBlock
+    while (np * tpp * 2 <= kBlock) tpp *= 2;
     const int pp = (np + kBlock - 1) / kBlock;
-    if (pp <= 1) SLA_LAUNCH(k_blk_gram<1>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
-    else if (pp <= 2) SLA_LAUNCH(k_blk_gram<2>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
-    else if (pp <= 4) SLA_LAUNCH(k_blk_gram<4>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
-    else if (pp <= 8) SLA_LAUNCH(k_blk_gram<8>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
-    else if (pp <= 16) SLA_LAUNCH(k_blk_gram<16>, grid, blk, 0, s, A, ia, mu, B, ib, mv, n, part);
-    else SLA_LAUNCH(k_blk_gram<(kBlkMaxCols * kBlkMaxCols + kBlock - 1) / kBlock>, grid, blk, 0, s, A, ia, mu, B, ib,
-                    mv, n, part);
+    if (pp <= 1) SLA_LAUNCH(k_blk_gram<1>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, tpp, part);
+    else if (pp <= 2) SLA_LAUNCH(k_blk_gram<2>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, 1, part);
+    else if (pp <= 4) SLA_LAUNCH(k_blk_gram<4>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, 1, part);
+    else if (pp <= 8) SLA_LAUNCH(k_blk_gram<8>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, 1, part);
+    else if (pp <= 16) SLA_LAUNCH(k_blk_gram<16>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, 1, part);
+    else SLA_LAUNCH(k_blk_gram<(kBlkMaxCols * kBlkMaxCols + kBlock - 1) / kBlock>, grid, blk, lds, s, A, ia, mu, B,
+                    ib, mv, n, R, 1, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>((np + kBlock - 1) / kBlock)), blk, 0, s, part, G, np, out);
+    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), blk, 0, s, part, G, np, out);
     return hipGetLastError();
 }
 
 hipError_t launch_blk_reduce(const double* part, int G, int np, double* out, hipStream_t s)
 {
     if (G < 1 || np < 1) return hipErrorInvalidValue;
-    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>((np + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, part, G, np,
-               out);
+    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), dim3(kBlock), 0, s, part, G, np, out);
     return hipGetLastError();
 }
 

@@ -367,9 +367,10 @@ class timing:
         lib = L.load()
         out = {}
         for k, name in enumerate(L.KERNEL_NAMES):
-            n, ms = C.c_int64(), C.c_double()
+            n, ms, by = C.c_int64(), C.c_double(), C.c_double()
             check(lib.sla_timing_query(k, C.byref(n), C.byref(ms)))
-            out[name] = dict(launches=n.value, total_ms=ms.value)
+            check(lib.sla_timing_query_bytes(k, C.byref(by)))
+            out[name] = dict(launches=n.value, total_ms=ms.value, bytes=by.value)
         return out
 
 

@@ -419,6 +419,10 @@ sla_status sla_timing_enable(int32_t enable);
 sla_status sla_timing_reset(void);
 sla_status sla_timing_collect(void);    /* synchronises pending timed launches */
 sla_status sla_timing_query(int32_t kernel, int64_t* launches, double* total_ms);
+/* Algorithmic bytes of the timed launches of a kernel id (each operand column read
+ * once, each output written once, the matrix once per product); counted by the LOBPCG
+ * block kernels, 0 elsewhere. */
+sla_status sla_timing_query_bytes(int32_t kernel, double* bytes);
 
 const char* sla_status_string(sla_status s);
 const char* sla_last_error(void);

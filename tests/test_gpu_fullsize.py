@@ -291,3 +291,41 @@ def test_fullsize_eigsh_varcoef1024(S):
         runs[name] = (ev, nA)
     (e0, nA), (e1, _) = runs["eigsh_varcoef1024"], runs["eigsh_tr_varcoef1024"]
     assert np.abs(e0 - e1).max() <= 1e-12 * nA
+
+
+def test_fullsize_lobpcg_varcoef1024(S):
+    """lobpcg_varcoef1024 (the 8 largest eigenpairs of the 1M-row varcoef matrix by
+    LOBPCG to tol 1e-8) as the benchmark runs it, by what holds at any size: true
+    residuals |A u - theta u| within tol |theta| and equal to the reported maximum,
+    Rayleigh quotients, orthonormal vectors with <u_r, X0[r]> >= 0, and the eigenvalues
+    within tol-derived bounds of the Lanczos run to tol 1e-10 (eigsh_varcoef1024): a
+    Ritz value with residual rho is within rho^2 / gap of an eigenvalue, and within rho
+    always."""
+    import scipy.sparse as sp
+    c = W.config("lobpcg_varcoef1024")
+    A = c["A"]
+    print("[lobpcg full size]", flush=True)
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=True)
+    ev, U, info = S.lobpcg(h, dev(A.vals), c["k"], dev(c["X0"]), which=c["which"], tol=c["tol"],
+                           max_iter=c["max_iter"])
+    ev, U = host(ev), host(U)
+    assert info["state"] == O.CONVERGED
+    M = sp.csr_matrix((A.vals, A.col, A.row_ptr.astype(np.int64)), shape=(A.n_rows, A.n_cols))
+    nA = float(np.add.reduceat(np.abs(A.vals), A.row_ptr[:-1].astype(np.int64)).max())
+    assert np.all(np.diff(ev) <= 0)
+    assert np.allclose(U @ U.T, np.eye(c["k"]), atol=1e-12)
+    res = []
+    for r in range(c["k"]):
+        assert U[r] @ c["X0"][r] >= 0.0
+        Au = M @ U[r]
+        res.append(np.linalg.norm(Au - ev[r] * U[r]))
+        assert res[-1] <= c["tol"] * abs(ev[r]) * (1 + 1e-6) + 1e-12 * nA, (r, res[-1])
+        assert abs(U[r] @ Au - ev[r]) <= 1e-12 * nA
+    assert abs(max(res) - info["max_res"]) <= 1e-6 * info["max_res"] + 1e-12 * nA
+    z = W.config("eigsh_varcoef1024")
+    hz = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=True)
+    evz, _, infoz = S.eigsh(hz, dev(A.vals), z["k"], dev(z["v0"]), which=z["which"], tol=z["tol"])
+    assert infoz["state"] == O.CONVERGED
+    evz = host(evz)
+    for r in range(c["k"]):
+        assert abs(ev[r] - evz[r]) <= res[r] + z["tol"] * abs(evz[r]) + 1e-12 * nA

@@ -350,6 +350,8 @@ def config(name: str, scale: int | None = None) -> dict:
                    (seed 3), and the Hellmann-Feynman gradient of sum(lambda).
     eigsh_tr_varcoef1024  the same with thick restart: a basis of 32 vectors (keep 20)
                    restarted until convergence.
+    lobpcg_varcoef1024  the 8 largest eigenpairs of the same matrix by LOBPCG to tol
+                   1e-8 from the start block X0[r] ~ N(0, 1) (seed 3 + r).
     poisson_list64 a SparseTensorList of 64 five-point Poisson grids of sides 64, 67, ...,
                    253 (distinct patterns, 1.7M rows in all), b_i ~ N(0, 1) seed i, CG to
                    1e-8 + adjoint of sum_i 0.5 |x_i|^2.
@@ -400,6 +402,11 @@ def config(name: str, scale: int | None = None) -> dict:
         if name == "eigsh_tr_varcoef1024":
             c.update(max_dim=32, max_iter=100000)
         return c
+    if name == "lobpcg_varcoef1024":
+        N = scale or 1024
+        A, _, _ = varcoef_poisson5(N, seed=0)
+        X0 = np.stack([rhs_normal(N * N, 3 + r) for r in range(8)])
+        return dict(name=name, A=A, X0=X0, k=8, which="largest", tol=1e-8, max_iter=5000, method="lobpcg")
     if name == "poisson13000":
         N = scale or 13000
         return dict(name=name, N=N, A=None, b=None, rtol=0.0, atol=0.0, max_iter=500,
