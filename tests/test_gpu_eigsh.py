@@ -234,3 +234,9 @@ def test_eigsh_autograd(S):
     r = orc_eigsh(A, 3, v0, which="smallest", tol=1e-12)
     ref = orc_eigsh_grad(A, r["evecs"], np.array([1.0, 2.0, -1.0]))
     assert np.linalg.norm(host(T.vals.grad) - ref) <= 1e-7 * np.linalg.norm(ref)
+
+
+def test_eigsh_k32(S):
+    # the most Ritz vectors a call returns (k_lz_ritz with 32 accumulators)
+    A, _, _ = W.varcoef_poisson5(30, seed=8)
+    compare(S, A, 32, "largest", 1e-10, seed=100, g=np.linspace(-1.0, 1.0, 32))

@@ -194,3 +194,17 @@ def test_lobpcg_autograd(S):
     r = orc_lobpcg(A, 3, X0, which="largest", tol=1e-12)
     ref = orc_eigsh_grad(A, r["evecs"], np.array([1.0, 2.0, -1.0]))
     assert np.linalg.norm(host(T.vals.grad) - ref) <= 1e-7 * np.linalg.norm(ref)
+
+
+def test_lobpcg_k32(S):
+    # the widest block: Rayleigh-Ritz on up to 96 columns (9216 Gram pairs, 36 per
+    # thread), combinations of 32 outputs, SpMM in four chunks of 8 columns
+    A, _, _ = W.varcoef_poisson5(30, seed=8)
+    compare(S, A, 32, "largest", 1e-8, X0=start_block(A.n_rows, 32, seed=100))
+
+
+def test_lobpcg_fem_mesh(S):
+    # an unstructured pattern (P1 FEM on a jittered, permuted mesh)
+    F, _ = W.fem_p1_batched(nv=30, B=1, seed=2)
+    A = W.CSR(F.n_rows, F.n_cols, F.row_ptr, F.col, F.vals[0].copy())
+    compare(S, A, 4, "largest", 1e-9, g=np.array([0.5, 1.0, -1.0, 2.0]))
