@@ -36,6 +36,11 @@ it fails when a column is zero or a pivot of the Cholesky factorization is not a
 carried through the same scaling, R^-1 and projections (A is linear), so every SpMV is
 applied to a W block only.
 
+With jacobi=True the residuals are preconditioned before they enter the basis,
+W = T R[:, active] with Knyazev's preconditioner T = D^-1 (D the stored diagonal of A,
+applied as a product with the reciprocals 1 / a_ii); every a_ii must be stored,
+finite and positive.
+
 The eigenvalues returned are the Ritz values from the wanted end; the vectors are
 unit Ritz vectors, signed so that <u_r, X0[r]> >= 0.  SpMV is the oracle's own
 (sla_oracle.c); Gram products, Cholesky, triangular solves and the small symmetric
@@ -102,7 +107,22 @@ def _wanted(H, k, which):
     return w[idx], V[:, idx]
 
 
-def lobpcg(A, k: int, X0, which: str = "largest", tol: float = 1e-8, max_iter: int = 1000, vals=None) -> dict:
+def jacobi_reciprocals(A, vals=None) -> np.ndarray:
+    """1 / a_ii for every row; ValueError unless each a_ii is stored, finite and > 0."""
+    v = A.vals if vals is None else _f64(vals)
+    rp = A.row_ptr.astype(np.int64)
+    d = np.full(A.n_rows, np.nan)
+    for i in range(A.n_rows):
+        for e in range(rp[i], rp[i + 1]):
+            if A.col[e] == i:
+                d[i] = v[e]
+    if not np.all(np.isfinite(d) & (d > 0.0)):
+        raise ValueError("Jacobi needs every diagonal entry stored, finite and positive")
+    return 1.0 / d
+
+
+def lobpcg(A, k: int, X0, which: str = "largest", tol: float = 1e-8, max_iter: int = 1000, vals=None,
+           jacobi: bool = False) -> dict:
     """Returns dict(evals [k], evecs [k, n], iterations, state, res [k] (true residual
     norms |A u - theta u| of the returned pairs, from the last check), blocks (per
     iteration: the widths of W and P used))."""
@@ -112,6 +132,7 @@ def lobpcg(A, k: int, X0, which: str = "largest", tol: float = 1e-8, max_iter: i
     X0 = np.atleast_2d(_f64(X0))
     if X0.shape != (k, n) or not 1 <= k or 3 * k > n:
         raise ValueError("need X0 of shape [k, n] with 3 k <= n")
+    tinv = jacobi_reciprocals(A, vals) if jacobi else None
     q = _orth(X0.T.copy())
     if q is None:
         raise ValueError("start block is rank deficient")
@@ -130,7 +151,8 @@ def lobpcg(A, k: int, X0, which: str = "largest", tol: float = 1e-8, max_iter: i
             state = CONVERGED if not active.any() else MAX_ITER
             break
         it += 1
-        W, _ = _project(R[:, active], None, X, AX)
+        W = R[:, active] * tinv[:, None] if jacobi else R[:, active]
+        W, _ = _project(W, None, X, AX)
         ow = _orth(W)
         W = ow[0] if ow is not None else None
         AW = _block_spmv(A, W, vals) if W is not None else None

@@ -152,3 +152,59 @@ def test_lobpcg_agrees_with_lanczos():
         z = eigsh(A, k, X0[0], which=which, tol=1e-12)
         assert r["state"] == z["state"] == O.CONVERGED
         assert np.abs(r["evals"] - z["evals"]).max() <= 1e-12 * np.abs(dense(A)).sum(axis=1).max()
+
+
+def knyazev_ritz(M, X0, k, which, iters, tinv=None):
+    """Ritz values after `iters` steps of Rayleigh-Ritz on span{X_i, T R_i, X_{i-1}}
+    (Knyazev's formulation; LOBPCG's basis [X, W, P] spans the same space), by numpy QR
+    and eigh on the dense matrix: independent of the oracle's blocks and factorizations."""
+    def rr(Q):
+        Q, _ = np.linalg.qr(Q)
+        w, V = np.linalg.eigh(Q.T @ M @ Q)
+        idx = np.arange(len(w) - 1, len(w) - 1 - k, -1) if which == "largest" else np.arange(k)
+        return w[idx], Q @ V[:, idx]
+    th, X = rr(X0.T)
+    Xprev = None
+    for _ in range(iters):
+        R = M @ X - X * th
+        W = R if tinv is None else R * tinv[:, None]
+        blocks = [X, W] + ([Xprev] if Xprev is not None else [])
+        Xprev = X
+        th, X = rr(np.hstack(blocks))
+    return th
+
+
+@pytest.mark.parametrize("jacobi", [False, True])
+@pytest.mark.parametrize("which", ["largest", "smallest"])
+def test_lobpcg_trial_space_is_knyazevs(which, jacobi):
+    A, _, _ = W.varcoef_poisson5(10, seed=2)
+    M = dense(A)
+    k = 3
+    X0 = start_block(A.n_rows, k, seed=6)
+    tinv = 1.0 / np.diag(M) if jacobi else None
+    for it in (1, 2, 3):
+        r = L.lobpcg(A, k, X0, which=which, tol=1e-300, max_iter=it, jacobi=jacobi)
+        ref = knyazev_ritz(M, X0, k, which, it, tinv)
+        assert np.abs(r["evals"] - ref).max() <= 1e-10 * np.abs(M).sum(axis=1).max(), (it, r["evals"], ref)
+
+
+def test_lobpcg_jacobi_vs_dense_eigh():
+    A, _, _ = W.varcoef_poisson5(14, seed=3)
+    M = dense(A)
+    w = np.linalg.eigvalsh(M)
+    k = 4
+    X0 = start_block(A.n_rows, k)
+    r = L.lobpcg(A, k, X0, which="smallest", tol=1e-10, max_iter=5000, jacobi=True)
+    p = L.lobpcg(A, k, X0, which="smallest", tol=1e-10, max_iter=5000)
+    assert r["state"] == O.CONVERGED and r["iterations"] < p["iterations"] / 2
+    assert np.abs(r["evals"] - w[:k]).max() <= 1e-12 * np.abs(w).max()
+    check_pairs(M, r, 1e-10, X0)
+
+
+def test_lobpcg_jacobi_needs_a_positive_diagonal():
+    A, _, _ = W.varcoef_poisson5(6, seed=1)
+    v = A.vals.copy()
+    rows = np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+    v[np.flatnonzero(rows == A.col)[3]] = -1.0
+    with pytest.raises(ValueError):
+        L.lobpcg(A, 2, start_block(A.n_rows, 2), jacobi=True, vals=v)

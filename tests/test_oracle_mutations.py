@@ -120,6 +120,10 @@ LOBPCG_MUTANTS = {
                                            "theta, Y = np.diag(S.T @ AS)[:k].copy(), np.eye(S.shape[1])[:, :k]"),
     "sign convention dropped": ("if U[r] @ X0[r] < 0.0:", "if False:"),
     "stop test on the absolute residual": ("active = res > tol * np.abs(theta)", "active = res > tol"),
+    "preconditioner ignored": ("W = R[:, active] * tinv[:, None] if jacobi else R[:, active]",
+                               "W = R[:, active]"),
+    "conjugate direction from the X part": ("P, AP = S[:, k:] @ Y[k:, :], AS[:, k:] @ Y[k:, :]",
+                                            "P, AP = S[:, :k] @ Y[:k, :], AS[:, :k] @ Y[:k, :]"),
 }
 
 
