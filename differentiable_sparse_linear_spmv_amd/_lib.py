@@ -23,6 +23,7 @@ SLA_JACOBI = 2
 SLA_BICGSTAB = 4
 SLA_EIG_LARGEST, SLA_EIG_SMALLEST = 0, 1
 SLA_EIG_MAX_K = 32
+SLA_EIG_JACOBI = 1
 (SLA_K_CG_INIT, SLA_K_CG_SPMV, SLA_K_CG_UPDATE, SLA_K_MATVEC, SLA_K_PATTERN_OUTER,
  SLA_K_GATHER_VALS, SLA_K_TRANSPOSE, SLA_K_CG_PUPD, SLA_K_GROUP_LAYOUT, SLA_K_BS_SPMV, SLA_K_BS_VEC,
  SLA_K_LZ_SPMV, SLA_K_LZ_ORTH, SLA_K_LZ_RITZ, SLA_K_LOB_SPMM, SLA_K_LOB_GRAM, SLA_K_LOB_COMB,
@@ -57,7 +58,7 @@ assert C.sizeof(SlaCgInfo) == 32
 class SlaEigOpts(C.Structure):
     _fields_ = [("tol", C.c_double), ("max_dim", C.c_int64), ("which", C.c_int32),
                 ("check_every", C.c_int32), ("max_iter", C.c_int64), ("keep", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("flags", C.c_int32)]
 
 
 class SlaEigInfo(C.Structure):

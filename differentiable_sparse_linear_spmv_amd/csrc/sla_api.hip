@@ -1136,6 +1136,7 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
         return fail(SLA_ERR_INVALID_ARG, "which must be SLA_EIG_LARGEST or SLA_EIG_SMALLEST");
     if (opts->check_every < 0) return fail(SLA_ERR_INVALID_ARG, "check_every must be >= 0");
     if (opts->max_iter < 0 || opts->keep < 0) return fail(SLA_ERR_INVALID_ARG, "max_iter and keep must be >= 0");
+    if (opts->flags != 0) return fail(SLA_ERR_INVALID_ARG, "flags: the Lanczos eigensolver takes none");
     // thick restart when the step budget exceeds the basis size
     const int64_t total = std::max<int64_t>(max_dim, opts->max_iter);
     const bool restart = total > max_dim;
@@ -1517,6 +1518,8 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
     if (opts->which != SLA_EIG_LARGEST && opts->which != SLA_EIG_SMALLEST)
         return fail(SLA_ERR_INVALID_ARG, "which must be SLA_EIG_LARGEST or SLA_EIG_SMALLEST");
     if (opts->max_iter < 0) return fail(SLA_ERR_INVALID_ARG, "max_iter must be >= 0");
+    if (opts->flags & ~SLA_EIG_JACOBI) return fail(SLA_ERR_INVALID_ARG, "unknown flags 0x%x", opts->flags);
+    const bool jacobi = (opts->flags & SLA_EIG_JACOBI) != 0;
     static_assert(3 * SLA_EIG_MAX_K <= kBlkMaxCols, "block width");
     const int64_t max_iter = opts->max_iter > 0 ? opts->max_iter : 1000;
     const bool largest = opts->which == SLA_EIG_LARGEST;
@@ -1524,8 +1527,9 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> guard(A->mu);
 
-    // workspace: NC block columns, Gram partials and results, combination norm partials
-    const int NC = 14 * k;
+    // workspace: NC block columns (the last holds the Jacobi reciprocals), Gram partials
+    // and results, combination norm partials
+    const int NC = 14 * k + 1;
     const int Gg = blk_gram_groups(n), Gc = blk_comb_groups(n);
     const size_t sz_pool = align256(sizeof(double) * static_cast<size_t>(NC) * n);
     const size_t sz_gp = align256(sizeof(double) * static_cast<size_t>(Gg) * 9 * k * k);
@@ -1565,7 +1569,8 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
 
     using Cols = std::vector<int32_t>;
     std::vector<int32_t> free_cols;
-    for (int c = NC - 1; c >= 0; --c) free_cols.push_back(c);
+    for (int c = NC - 2; c >= 0; --c) free_cols.push_back(c);
+    double* tinv = pool + static_cast<size_t>(NC - 1) * n;
     auto take = [&](int w, Cols& out) -> bool {
         if (static_cast<int>(free_cols.size()) < w) return false;
         out.resize(w);
@@ -1732,6 +1737,36 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
     };
     auto hip_fail = [&](const char* what) { return fail(SLA_ERR_HIP, "lobpcg %s: %s", what, hipGetErrorString(e)); };
 
+    if (jacobi) {   // T = diag(A)^-1, with a count of the rows that have no usable a_ii
+        e = timed(SLA_K_LOB_COMB, s, [&] {
+            return launch_blk_diag_inv(A->krp, A->krp_bits, A->col, d_vals, n, tinv, d_cpart, s);
+        });
+        if (e == hipSuccess) e = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_reduce(d_cpart, Gc, 1, d_g, s); });
+        if (e != hipSuccess) return hip_fail("jacobi");
+        HIP_TRY(hipMemcpyAsync(h_g, d_g, sizeof(double), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        if (h_g[0] != 0.0)
+            return fail(SLA_ERR_INVALID_ARG, "Jacobi needs every diagonal entry stored, finite and positive (%.0f rows "
+                        "have none)", h_g[0]);
+    }
+    // W = T R[:, active] (out of place; the inputs are released)
+    auto precondition = [&](Cols& Wc) -> hipError_t {
+        Cols W2;
+        if (!take(static_cast<int>(Wc.size()), W2)) return hipErrorOutOfMemory;
+        const int32_t* din = ar.put(Wc.data(), Wc.size(), e);
+        if (e != hipSuccess) return e;
+        const int32_t* dout = ar.put(W2.data(), W2.size(), e);
+        if (e != hipSuccess) return e;
+        if ((e = ar.flush(s)) != hipSuccess) return e;
+        e = timed(SLA_K_LOB_COMB, s, [&] {
+            return launch_blk_rowscale(pool, din, pool, dout, static_cast<int>(Wc.size()), n, tinv, s);
+        }, true, 8.0 * static_cast<double>(n) * (2 * Wc.size() + 1));
+        if (e != hipSuccess) return e;
+        give(Wc);
+        Wc = W2;
+        return hipSuccess;
+    };
+
     // start: X = orth(X0), AX = A X, Rayleigh-Ritz on X
     Cols X(k), AX, P, AP;
     for (int r = 0; r < k; ++r) X[r] = r;   // rows of the caller's X0
@@ -1792,6 +1827,7 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
         }
         P.clear();
         AP.clear();
+        if (jacobi && (e = precondition(W)) != hipSuccess) return hip_fail("preconditioner");
         if ((e = project(W, nullptr, X, nullptr)) != hipSuccess) return hip_fail("projection");
         bool wok = false;
         if ((e = orth(pool, W, nullptr, wok)) != hipSuccess) return hip_fail("orthonormalization");

@@ -171,6 +171,13 @@ hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const dou
 int blk_comb_groups(int64_t n);
 // out[p] = sum over g < G of part[g][p] (g ascending), p < np.
 hipError_t launch_blk_reduce(const double* part, int G, int np, double* out, hipStream_t s);
+// tinv[i] = 1 / a_ii; part[g] (blk_comb_groups(n) doubles): rows of group g whose a_ii
+// is missing, not finite or not positive (tinv 0 there).
+hipError_t launch_blk_diag_inv(const void* rp, int rp_bits, const int32_t* col, const double* vals, int64_t n,
+                               double* tinv, double* part, hipStream_t s);
+// out[idx_out[c]][i] = in[idx_in[c]][i] * t[i], c < q.
+hipError_t launch_blk_rowscale(const double* in, const int32_t* idx_in, double* out, const int32_t* idx_out, int q,
+                               int64_t n, const double* t, hipStream_t s);
 hipError_t launch_blk_comb(const double* in, const int32_t* idx_in, int m, const double* Y, double* out,
                            const int32_t* idx_out, int q, int64_t n, double* part, hipStream_t s);
 

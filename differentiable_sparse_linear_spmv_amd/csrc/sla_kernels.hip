@@ -2075,6 +2075,54 @@ __global__ __launch_bounds__(kBlock) void k_blk_gram(const double* __restrict__ 
     }
 }
 
+// tinv[i] = 1 / a_ii (binary search for column i in row i; the columns are sorted), and
+// per workgroup the number of rows whose a_ii is missing, not finite or not positive
+// (part[blockIdx.x], as a double).
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_blk_diag_inv(const RP* __restrict__ rp, const int32_t* __restrict__ col,
+                                                         const double* __restrict__ vals, int64_t n,
+                                                         double* __restrict__ tinv, double* __restrict__ part)
+{
+    __shared__ double s_red[kBlock / 64];
+    double bad = 0.0;
+    LZ_ROWS(i, n) {
+        int64_t lo = ld_rp(rp, i), hi = ld_rp(rp, i + 1);
+        double d = 0.0;
+        bool found = false;
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            const int32_t c = col[mid];
+            if (c == i) {
+                d = vals[mid];
+                found = true;
+                break;
+            }
+            if (c < i) lo = mid + 1;
+            else hi = mid;
+        }
+        const bool ok = found && d > 0.0 && d < HUGE_VAL;
+        tinv[i] = ok ? 1.0 / d : 0.0;
+        if (!ok) bad = bad + 1.0;
+    }
+    bad = block_sum(bad, s_red);
+    if (threadIdx.x == 0) part[blockIdx.x] = bad;
+}
+
+// out[c][i] = in[c][i] * t[i] for c < q (the preconditioned residuals T R).
+__global__ __launch_bounds__(kBlock) void k_blk_rowscale(const double* __restrict__ in,
+                                                         const int32_t* __restrict__ idx_in,
+                                                         double* __restrict__ out,
+                                                         const int32_t* __restrict__ idx_out, int q, int64_t n,
+                                                         const double* __restrict__ t)
+{
+    LZ_ROWS(i, n) {
+        const double ti = t[i];
+        for (int c = 0; c < q; ++c)
+            out[static_cast<int64_t>(ld_uniform_i(idx_out, c)) * n + i] =
+                in[static_cast<int64_t>(ld_uniform_i(idx_in, c)) * n + i] * ti;
+    }
+}
+
 // out[p] = sum over g < G of part[g][p], p < np: one workgroup per p, a fixed order
 // (strided partial sums, then the workgroup tree).
 __global__ __launch_bounds__(kBlock) void k_blk_reduce(const double* __restrict__ part, int G, int np,
@@ -3246,6 +3294,26 @@ hipError_t launch_blk_reduce(const double* part, int G, int np, double* out, hip
 {
     if (G < 1 || np < 1) return hipErrorInvalidValue;
     SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), dim3(kBlock), 0, s, part, G, np, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_blk_diag_inv(const void* rp, int rp_bits, const int32_t* col, const double* vals, int64_t n,
+                               double* tinv, double* part, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(blk_comb_groups(n))), blk(kBlock);
+    if (rp_bits == 64)
+        SLA_LAUNCH(k_blk_diag_inv<int64_t>, grid, blk, 0, s, static_cast<const int64_t*>(rp), col, vals, n, tinv, part);
+    else
+        SLA_LAUNCH(k_blk_diag_inv<int32_t>, grid, blk, 0, s, static_cast<const int32_t*>(rp), col, vals, n, tinv, part);
+    return hipGetLastError();
+}
+
+hipError_t launch_blk_rowscale(const double* in, const int32_t* idx_in, double* out, const int32_t* idx_out, int q,
+                               int64_t n, const double* t, hipStream_t s)
+{
+    if (q < 1 || n < 1) return hipErrorInvalidValue;
+    SLA_LAUNCH(k_blk_rowscale, dim3(static_cast<unsigned>(blk_comb_groups(n))), dim3(kBlock), 0, s, in, idx_in, out,
+               idx_out, q, n, t);
     return hipGetLastError();
 }
 

@@ -243,9 +243,9 @@ def eigsh(h: Handle, vals: torch.Tensor, k: int, v0: torch.Tensor, which: str = 
 
 
 def lobpcg(h: Handle, vals: torch.Tensor, k: int, X0: torch.Tensor, which: str = "largest", tol: float = 1e-8,
-           max_iter: int = 0):
-    """sla_lobpcg: k extreme eigenpairs by LOBPCG from the start block X0 [k, n].
-    Returns (evals [k], evecs [k, n], info)."""
+           max_iter: int = 0, jacobi: bool = False):
+    """sla_lobpcg: k extreme eigenpairs by LOBPCG from the start block X0 [k, n]
+    (jacobi: residuals preconditioned by diag(A)^-1).  Returns (evals [k], evecs [k, n], info)."""
     if which not in ("largest", "smallest"):
         raise ValueError(f"which must be 'largest' or 'smallest' (got {which!r})")
     _need(vals, "vals", torch.float64, h.nnz, h.device)
@@ -253,7 +253,7 @@ def lobpcg(h: Handle, vals: torch.Tensor, k: int, X0: torch.Tensor, which: str =
     evals = torch.empty(k, dtype=torch.float64, device=h.device)
     evecs = torch.empty((k, h.n_rows), dtype=torch.float64, device=h.device)
     opts = SlaEigOpts(float(tol), 0, L.SLA_EIG_LARGEST if which == "largest" else L.SLA_EIG_SMALLEST, 0,
-                      int(max_iter), 0, 0)
+                      int(max_iter), 0, L.SLA_EIG_JACOBI if jacobi else 0)
     info = SlaEigInfo()
     check(L.load().sla_lobpcg(h.ptr, _ptr(vals), int(k), _ptr(X0), _ptr(evals), _ptr(evecs), C.byref(opts),
                               C.byref(info), _stream(h.device)))
@@ -401,7 +401,7 @@ class _EigshFn(torch.autograd.Function):
     def forward(ctx, A, vals, v0, kw):
         if kw["method"] == "lobpcg":
             evals, evecs, info = lobpcg(A.handle, vals.detach(), kw["k"], v0.detach(), which=kw["which"],
-                                        tol=kw["tol"], max_iter=kw["max_iter"])
+                                        tol=kw["tol"], max_iter=kw["max_iter"], jacobi=kw["jacobi"])
         else:
             evals, evecs, info = eigsh(A.handle, vals.detach(), kw["k"], v0.detach(), which=kw["which"],
                                        tol=kw["tol"], max_dim=kw["max_dim"], max_iter=kw["max_iter"],
@@ -503,7 +503,8 @@ class SparseTensor:
         return x
 
     def eigsh(self, k: int = 6, which: str = "largest", tol: float = 1e-10, max_dim: int = 0,
-              v0: torch.Tensor | None = None, max_iter: int = 0, keep: int = 0, method: str = "lanczos"):
+              v0: torch.Tensor | None = None, max_iter: int = 0, keep: int = 0, method: str = "lanczos",
+              jacobi: bool = False):
         """k extreme eigenpairs; the eigenvalues are differentiable with respect to vals
         (Hellmann-Feynman), the eigenvectors carry no gradient.
         method "lanczos": v0 is the start vector [n] (by default N(0, 1) from a
@@ -511,14 +512,18 @@ class SparseTensor:
         restart of a basis of max_dim vectors, keeping `keep` Ritz vectors, up to
         max_iter steps in all.
         method "lobpcg": v0 is the start block [k, n] (by default N(0, 1) as above);
-        max_iter counts iterations (0: 1000).  Returns (evals [k], evecs [k, n])."""
+        max_iter counts iterations (0: 1000); jacobi preconditions the residuals with
+        diag(A)^-1 (for the smallest end).  Returns (evals [k], evecs [k, n])."""
         if method not in ("lanczos", "lobpcg"):
             raise ValueError(f"method must be 'lanczos' or 'lobpcg' (got {method!r})")
         if v0 is None:
             gen = torch.Generator(device=self.handle.device).manual_seed(0)
             shape = (k, self.handle.n_rows) if method == "lobpcg" else (self.handle.n_rows,)
             v0 = torch.randn(shape, dtype=torch.float64, device=self.handle.device, generator=gen)
-        kw = dict(k=k, which=which, tol=tol, max_dim=max_dim, max_iter=max_iter, keep=keep, method=method)
+        if jacobi and method != "lobpcg":
+            raise ValueError("jacobi applies to method='lobpcg'")
+        kw = dict(k=k, which=which, tol=tol, max_dim=max_dim, max_iter=max_iter, keep=keep, method=method,
+                  jacobi=jacobi)
         return _EigshFn.apply(self, self.vals, v0, kw)
 
     def info(self, backward: bool = False) -> list[dict]:

@@ -299,8 +299,9 @@ typedef struct {
     int64_t max_iter;            /* total Lanczos steps; > max_dim turns on thick restart (0: max_dim) */
     int32_t keep;                /* Ritz vectors kept at a restart, k <= keep < max_dim
                                     (0: min(max_dim - 1, max(k + 1, (max_dim + k) / 2))) */
-    int32_t reserved;            /* 0 */
+    int32_t flags;               /* sla_lobpcg: SLA_EIG_JACOBI or 0; sla_eigsh: 0 */
 } sla_eig_opts;
+#define SLA_EIG_JACOBI 1         /* LOBPCG preconditioned by T = diag(A)^-1 */
 
 typedef struct {
     int64_t iterations;          /* Lanczos steps taken (all bases: restarts included) */
@@ -364,11 +365,13 @@ sla_status sla_eigsh(const sla_csr* A, const double* d_vals, int32_t k, const do
  *                    SLA_ERR_INVALID_ARG)
  *   d_evals  [k]     output: the Ritz values, from the wanted end
  *   d_evecs  [k][n]  output: unit Ritz vectors, signed so that <u_r, X0[r]> >= 0
- *   opts     tol, which, max_iter (iterations; 0: 1000); max_dim, keep and check_every
- *            are not used
+ *   opts     tol, which, max_iter (iterations; 0: 1000), flags: SLA_EIG_JACOBI applies
+ *            Knyazev's preconditioner T = diag(A)^-1 to the residuals (W = T R; every
+ *            diagonal entry stored, finite and positive, else SLA_ERR_INVALID_ARG);
+ *            max_dim, keep and check_every are not used
  *   info     host output: iterations, max_res (largest |A u - theta u| at the last
  *            test), state (SLA_CONVERGED or SLA_MAX_ITER)
- * Memory: 14 k n doubles of block vectors, owned by the handle.  Synchronises the
+ * Memory: (14 k + 1) n doubles of block vectors, owned by the handle.  Synchronises the
  * calling thread with the stream several times per iteration (the small Gram
  * matrices are factored and solved on the host).
  */

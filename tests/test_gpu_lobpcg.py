@@ -59,13 +59,13 @@ def iters_close(a, b):
     return abs(a - b) <= max(1, math.floor(0.02 * b))
 
 
-def compare(S, A, k, which, tol, X0=None, g=None, max_iter=20000):
+def compare(S, A, k, which, tol, X0=None, g=None, max_iter=20000, jacobi=False):
     X0 = start_block(A.n_rows, k) if X0 is None else X0
     h = handle(S, A)
-    print(f"[lobpcg] n={A.n_rows} k={k} {which} tol={tol}", flush=True)
-    ev, U, info = S.lobpcg(h, dev(A.vals), k, dev(X0), which=which, tol=tol, max_iter=max_iter)
+    print(f"[lobpcg] n={A.n_rows} k={k} {which} tol={tol} jacobi={jacobi}", flush=True)
+    ev, U, info = S.lobpcg(h, dev(A.vals), k, dev(X0), which=which, tol=tol, max_iter=max_iter, jacobi=jacobi)
     ev, U = host(ev), host(U)
-    r = orc_lobpcg(A, k, X0, which=which, tol=tol, max_iter=max_iter)
+    r = orc_lobpcg(A, k, X0, which=which, tol=tol, max_iter=max_iter, jacobi=jacobi)
     assert info["state"] == r["state"], (info, r["state"])
     assert iters_close(info["iterations"], r["iterations"]), (info["iterations"], r["iterations"])
     nA = norm_inf(A)
@@ -208,3 +208,26 @@ def test_lobpcg_fem_mesh(S):
     F, _ = W.fem_p1_batched(nv=30, B=1, seed=2)
     A = W.CSR(F.n_rows, F.n_cols, F.row_ptr, F.col, F.vals[0].copy())
     compare(S, A, 4, "largest", 1e-9, g=np.array([0.5, 1.0, -1.0, 2.0]))
+
+
+@pytest.mark.parametrize("N,seed,k,tol", [(14, 3, 4, 1e-10), (40, 1, 3, 1e-8)])
+def test_lobpcg_jacobi_smallest(S, N, seed, k, tol):
+    # the preconditioned residuals T R, T = diag(A)^-1: the smallest end in 157 and 519
+    # iterations where the plain method needs 570 and 1684, and with a count that
+    # rounding does not move (the oracle's is the same under 1e-15 perturbations of X0)
+    A, _, _ = W.varcoef_poisson5(N, seed=seed)
+    ev, U, info, r = compare(S, A, k, "smallest", tol, jacobi=True, g=np.linspace(1.0, 2.0, k))
+    assert info["state"] == O.CONVERGED
+
+
+def test_lobpcg_jacobi_rejects_a_bad_diagonal(S):
+    A, _, _ = W.varcoef_poisson5(10, seed=1)
+    rows = np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+    v = A.vals.copy()
+    v[np.flatnonzero(rows == A.col)[7]] = 0.0
+    h = handle(S, A)
+    with pytest.raises(S.SlaError):
+        S.lobpcg(h, dev(v), 3, dev(start_block(A.n_rows, 3)), jacobi=True)
+    # the same values without the preconditioner are accepted (the flag is what checks)
+    ev, U, info = S.lobpcg(h, dev(A.vals), 3, dev(start_block(A.n_rows, 3)), jacobi=True, tol=1e-8)
+    assert info["state"] == O.CONVERGED
