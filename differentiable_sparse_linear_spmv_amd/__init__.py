@@ -13,8 +13,9 @@ _lib.load()
 
 from .sparse import (SparseTensor, SparseTensorList, cg_opts, csr_analysis, csr_create,  # noqa: E402
                      csr_destroy, csr_info, eigsh, eigsh_backward, list_create, list_solve,
-                     list_solve_backward, lobpcg, matvec, matvec_backward, read_info, solve, solve_backward, timing)
+                     list_solve_backward, lobpcg, matvec, matvec_backward, read_info, solve, solve_backward, timing,
+                     use_torch_allocator)
 
 __all__ = ["SparseTensor", "SparseTensorList", "SlaError", "cg_opts", "csr_analysis", "csr_create", "csr_destroy",
            "csr_info", "eigsh", "eigsh_backward", "list_create", "list_solve", "list_solve_backward", "lobpcg",
-           "matvec", "matvec_backward", "read_info", "solve", "solve_backward", "timing"]
+           "matvec", "matvec_backward", "read_info", "solve", "solve_backward", "timing", "use_torch_allocator"]

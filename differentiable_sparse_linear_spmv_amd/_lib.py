@@ -33,7 +33,7 @@ KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "g
                 "lz_ritz", "lob_spmm", "lob_gram", "lob_comb"]
 
 EXPORTS = [
-    "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
+    "sla_set_allocator", "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
     "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_solve",
     "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable",
     "sla_timing_reset", "sla_timing_collect", "sla_timing_query", "sla_timing_query_bytes", "sla_status_string",
@@ -53,6 +53,10 @@ class SlaCgInfo(C.Structure):
 
 
 assert C.sizeof(SlaCgInfo) == 32
+
+
+ALLOC_FN = C.CFUNCTYPE(C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p)
+FREE_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p, C.c_void_p)
 
 
 class SlaEigOpts(C.Structure):
@@ -126,6 +130,8 @@ def load():
     L.sla_lobpcg.restype = st
     L.sla_eigsh_backward.argtypes = [P, i32, P, P, P, P]
     L.sla_eigsh_backward.restype = st
+    L.sla_set_allocator.argtypes = [ALLOC_FN, FREE_FN, P]
+    L.sla_set_allocator.restype = st
     L.sla_timing_enable.argtypes = [i32]
     L.sla_timing_enable.restype = st
     L.sla_timing_reset.argtypes = []

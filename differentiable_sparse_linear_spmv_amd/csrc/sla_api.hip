@@ -22,6 +22,7 @@
 #include <memory>
 #include <mutex>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "sla.h"
@@ -222,10 +223,35 @@ sla_status check_device(const sla_csr* A)
     return SLA_OK;
 }
 
+// Device memory of the library: from the caller's allocator when one is registered
+// (sla_set_allocator), else hipMalloc.  Every block remembers the free function that
+// owns it, so a later change of allocator never frees through the wrong one.
+struct AllocHook {
+    sla_alloc_fn alloc = nullptr;
+    sla_free_fn free = nullptr;
+    void* ctx = nullptr;
+};
+std::mutex g_amu;
+AllocHook g_hook;
+std::unordered_map<void*, AllocHook> g_hooked;   // blocks from a registered allocator
+
 sla_status dev_alloc(void** p, size_t bytes)
 {
     *p = nullptr;
     if (bytes == 0) return SLA_OK;
+    AllocHook h;
+    {
+        std::lock_guard<std::mutex> lk(g_amu);
+        h = g_hook;
+    }
+    if (h.alloc) {
+        void* q = h.alloc(bytes, nullptr, h.ctx);
+        if (!q) return fail(SLA_ERR_OOM, "the registered allocator returned NULL for %zu bytes", bytes);
+        std::lock_guard<std::mutex> lk(g_amu);
+        g_hooked[q] = h;
+        *p = q;
+        return SLA_OK;
+    }
     hipError_t e = hipMalloc(p, bytes);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -233,6 +259,29 @@ sla_status dev_alloc(void** p, size_t bytes)
         return fail(SLA_ERR_OOM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
     }
     return SLA_OK;
+}
+
+// Frees a block of dev_alloc.  A block of a registered allocator goes back to it after
+// the device has finished with it (such allocators pool by stream, and the library may
+// have used the block on any stream).
+hipError_t dev_free(void* p)
+{
+    if (!p) return hipSuccess;
+    AllocHook h;
+    bool hooked = false;
+    {
+        std::lock_guard<std::mutex> lk(g_amu);
+        auto it = g_hooked.find(p);
+        if (it != g_hooked.end()) {
+            h = it->second;
+            hooked = true;
+            g_hooked.erase(it);
+        }
+    }
+    if (!hooked) return hipFree(p);
+    hipError_t e = hipDeviceSynchronize();
+    h.free(p, nullptr, h.ctx);
+    return e;
 }
 
 int choose_cap(int32_t tile_max)
@@ -293,7 +342,7 @@ sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int 
     if (need > A->ws_bytes) {
         if (A->ws) {
             HIP_TRY(hipDeviceSynchronize());
-            HIP_TRY(hipFree(A->ws));
+            HIP_TRY(dev_free(A->ws));
             A->ws = nullptr;
             A->ws_bytes = 0;
         }
@@ -355,7 +404,7 @@ sla_status ensure_transpose(sla_csr* A, hipStream_t s)
         },
         false);
     if (e != hipSuccess) {
-        (void)hipFree(scratch);
+        (void)dev_free(scratch);
         return fail(SLA_ERR_HIP, "transpose: %s", hipGetErrorString(e));
     }
     // analysis of the transposed pattern (also re-checks it)
@@ -366,12 +415,12 @@ sla_status ensure_transpose(sla_csr* A, hipStream_t s)
     HIP_TRY(hipStreamSynchronize(s));
     e = launch_validate(A->row_ptr_t, A->krp_bits, A->col_t, A->n_cols, A->n_rows, A->nnz, d_chk, s);
     if (e != hipSuccess) {
-        (void)hipFree(scratch);
+        (void)dev_free(scratch);
         return fail(SLA_ERR_HIP, "transpose analysis: %s", hipGetErrorString(e));
     }
     HIP_TRY(hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
-    (void)hipFree(scratch);
+    (void)dev_free(scratch);
     if (h[kChkErr] != 0)
         return fail(SLA_ERR_HIP, "internal error: transposed pattern failed validation (%d)", h[kChkErr]);
     A->cap_t = choose_cap(h[kChkTileMax]);
@@ -385,7 +434,7 @@ sla_status ensure_vals_t(sla_csr* A, int64_t batch, const double* vals, hipStrea
     if (need > A->vals_t_bytes) {
         if (A->vals_t) {
             HIP_TRY(hipDeviceSynchronize());
-            HIP_TRY(hipFree(A->vals_t));
+            HIP_TRY(dev_free(A->vals_t));
             A->vals_t = nullptr;
             A->vals_t_bytes = 0;
         }
@@ -464,7 +513,7 @@ sla_status ensure_reorder(sla_csr* A, hipStream_t s)
     }
     auto release = [&]() {
         for (int32_t** q : {&A->g_rp, &A->g_col, &A->g_eperm, &A->g_perm}) {
-            if (*q) (void)hipFree(*q);
+            if (*q) (void)dev_free(*q);
             *q = nullptr;
         }
     };
@@ -518,7 +567,7 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     if (need > A->gws_bytes) {
         if (A->gws) {
             HIP_TRY(hipDeviceSynchronize());
-            HIP_TRY(hipFree(A->gws));
+            HIP_TRY(dev_free(A->gws));
             A->gws = nullptr;
             A->gws_bytes = 0;
         }
@@ -894,7 +943,7 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
     if (e == hipSuccess) e = launch_validate(d_row_ptr, row_ptr_bits, d_col_idx, n_rows, n_cols, nnz, d_chk, s);
     if (e == hipSuccess) e = hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    (void)hipFree(d_chk);
+    (void)dev_free(d_chk);
     if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "CSR validation: %s", hipGetErrorString(e)));
     if (h[kChkErr] != 0) {
         const int c = h[kChkErr];
@@ -942,21 +991,21 @@ sla_status sla_csr_destroy(sla_csr* A)
     (void)hipGetDevice(&prev);
     if (prev != A->device) (void)hipSetDevice(A->device);
     (void)hipDeviceSynchronize();
-    if (A->ws) (void)hipFree(A->ws);
-    if (A->gws) (void)hipFree(A->gws);
-    if (A->vals_t) (void)hipFree(A->vals_t);
-    if (A->row_ptr_t) (void)hipFree(A->row_ptr_t);
-    if (A->col_t) (void)hipFree(A->col_t);
-    if (A->perm_t) (void)hipFree(A->perm_t);
-    if (A->rp_owned) (void)hipFree(A->rp_owned);
+    if (A->ws) (void)dev_free(A->ws);
+    if (A->gws) (void)dev_free(A->gws);
+    if (A->vals_t) (void)dev_free(A->vals_t);
+    if (A->row_ptr_t) (void)dev_free(A->row_ptr_t);
+    if (A->col_t) (void)dev_free(A->col_t);
+    if (A->perm_t) (void)dev_free(A->perm_t);
+    if (A->rp_owned) (void)dev_free(A->rp_owned);
     if (A->flag_host) (void)hipHostFree(A->flag_host);
-    if (A->eig_ws) (void)hipFree(A->eig_ws);
-    if (A->g_rp) (void)hipFree(A->g_rp);
-    if (A->g_col) (void)hipFree(A->g_col);
-    if (A->g_eperm) (void)hipFree(A->g_eperm);
-    if (A->g_perm) (void)hipFree(A->g_perm);
+    if (A->eig_ws) (void)dev_free(A->eig_ws);
+    if (A->g_rp) (void)dev_free(A->g_rp);
+    if (A->g_col) (void)dev_free(A->g_col);
+    if (A->g_eperm) (void)dev_free(A->g_eperm);
+    if (A->g_perm) (void)dev_free(A->g_perm);
     if (A->eig_host) (void)hipHostFree(A->eig_host);
-    if (A->lob_ws) (void)hipFree(A->lob_ws);
+    if (A->lob_ws) (void)dev_free(A->lob_ws);
     if (A->lob_host) (void)hipHostFree(A->lob_host);
     for (int i = 0; i < 2; ++i)
         if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);
@@ -1176,7 +1225,7 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     if (need > A->eig_ws_bytes) {
         if (A->eig_ws) {
             HIP_TRY(hipDeviceSynchronize());
-            HIP_TRY(hipFree(A->eig_ws));
+            HIP_TRY(dev_free(A->eig_ws));
             A->eig_ws = nullptr;
             A->eig_ws_bytes = 0;
         }
@@ -1540,7 +1589,7 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
     if (need > A->lob_ws_bytes) {
         if (A->lob_ws) {
             HIP_TRY(hipDeviceSynchronize());
-            HIP_TRY(hipFree(A->lob_ws));
+            HIP_TRY(dev_free(A->lob_ws));
             A->lob_ws = nullptr;
             A->lob_ws_bytes = 0;
         }
@@ -1925,12 +1974,12 @@ sla_status sla_list_destroy(sla_list* L)
     if (prev != L->device) (void)hipSetDevice(L->device);
     (void)hipDeviceSynchronize();
     if (L->packed) (void)sla_csr_destroy(L->packed);
-    if (L->rp) (void)hipFree(L->rp);
-    if (L->col) (void)hipFree(L->col);
-    if (L->d_wg) (void)hipFree(L->d_wg);
-    if (L->d_tiles) (void)hipFree(L->d_tiles);
-    if (L->d_rend) (void)hipFree(L->d_rend);
-    if (L->stage) (void)hipFree(L->stage);
+    if (L->rp) (void)dev_free(L->rp);
+    if (L->col) (void)dev_free(L->col);
+    if (L->d_wg) (void)dev_free(L->d_wg);
+    if (L->d_tiles) (void)dev_free(L->d_tiles);
+    if (L->d_rend) (void)dev_free(L->d_rend);
+    if (L->stage) (void)dev_free(L->stage);
     if (prev >= 0 && prev != L->device) (void)hipSetDevice(prev);
     delete L;
     return SLA_OK;
@@ -1993,7 +2042,7 @@ sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, cons
     if (e == hipSuccess)
         e = hipMemcpyAsync(h_chk.data(), d_chk, sizeof(int32_t) * h_chk.size(), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    (void)hipFree(d_chk);
+    (void)dev_free(d_chk);
     if (e != hipSuccess) return fail(SLA_ERR_HIP, "list validation: %s", hipGetErrorString(e));
     for (int32_t i = 0; i < items; ++i)
         if (h_chk[static_cast<size_t>(kChkCount) * i + kChkErr] != 0)
@@ -2065,7 +2114,7 @@ sla_status list_stage(sla_list* L, bool want_grad, double** vals, double** v0, d
     if (need > L->stage_bytes) {
         if (L->stage) {
             HIP_TRY(hipDeviceSynchronize());
-            HIP_TRY(hipFree(L->stage));
+            HIP_TRY(dev_free(L->stage));
             L->stage = nullptr;
             L->stage_bytes = 0;
         }
@@ -2199,6 +2248,15 @@ sla_status sla_timing_enable(int32_t enable)
 {
     std::lock_guard<std::mutex> lk(g_tmu);
     g_timing = enable != 0;
+    return SLA_OK;
+}
+
+sla_status sla_set_allocator(sla_alloc_fn alloc, sla_free_fn free_fn, void* ctx)
+{
+    if ((alloc == nullptr) != (free_fn == nullptr))
+        return fail(SLA_ERR_INVALID_ARG, "give both alloc and free, or neither");
+    std::lock_guard<std::mutex> lk(g_amu);
+    g_hook = AllocHook{alloc, free_fn, ctx};
     return SLA_OK;
 }
 

@@ -242,6 +242,34 @@ def eigsh(h: Handle, vals: torch.Tensor, k: int, v0: torch.Tensor, which: str = 
                               restarts=info.restarts, state_name=L.STATE_NAMES.get(info.state, str(info.state)))
 
 
+# Every callback pair ever registered stays alive: blocks they allocated are freed
+# through them even after the allocator has been switched (a handle may outlive it).
+_ALLOCATORS = []
+
+
+def use_torch_allocator(enable: bool = True) -> None:
+    """sla_set_allocator with torch's caching allocator (enable) or back to hipMalloc.
+    The library's workspaces then count in torch.cuda.memory_allocated() and come from
+    torch's pool on the current device and stream."""
+    lib = L.load()
+    if not enable:
+        check(lib.sla_set_allocator(L.ALLOC_FN(), L.FREE_FN(), None))
+        return
+
+    def _alloc(size, stream, ctx):
+        try:
+            return torch.cuda.caching_allocator_alloc(int(size))
+        except RuntimeError:   # out of memory: the library reports SLA_ERR_OOM
+            return None
+
+    def _free(ptr, stream, ctx):
+        torch.cuda.caching_allocator_delete(ptr)
+
+    cbs = (L.ALLOC_FN(_alloc), L.FREE_FN(_free))
+    _ALLOCATORS.append(cbs)
+    check(lib.sla_set_allocator(cbs[0], cbs[1], None))
+
+
 def lobpcg(h: Handle, vals: torch.Tensor, k: int, X0: torch.Tensor, which: str = "largest", tol: float = 1e-8,
            max_iter: int = 0, jacobi: bool = False):
     """sla_lobpcg: k extreme eigenpairs by LOBPCG from the start block X0 [k, n]

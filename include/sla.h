@@ -113,6 +113,25 @@ enum {
 
 typedef struct sla_csr sla_csr;   /* opaque handle: one sparsity pattern */
 
+/*
+ * Device memory of the library (handle workspaces, transposes, Lanczos and LOBPCG
+ * vectors, list staging) from a caller's allocator, e.g. a framework's caching
+ * allocator, instead of hipMalloc/hipFree.  Not a passage of the pages: the interface
+ * by which a host framework keeps the library's memory inside its own pool.
+ *   alloc(bytes, stream, ctx) returns device memory of at least `bytes` on the current
+ *     device, or NULL (the calling entry point then fails with SLA_ERR_OOM); stream is
+ *     passed as NULL: the library reuses its workspaces across calls and streams.
+ *   free(ptr, stream, ctx) takes back a block of alloc; the library synchronizes the
+ *     device first, so the block is idle on every stream.
+ * Both NULL restores hipMalloc/hipFree; one NULL is SLA_ERR_INVALID_ARG.  Applies to
+ * allocations made after the call; every block is freed through the allocator that
+ * made it.  Process-wide; the callbacks must be thread-safe if the library is used
+ * from several threads.
+ */
+typedef void* (*sla_alloc_fn)(size_t bytes, void* stream, void* ctx);
+typedef void (*sla_free_fn)(void* ptr, void* stream, void* ctx);
+sla_status sla_set_allocator(sla_alloc_fn alloc, sla_free_fn free, void* ctx);
+
 typedef struct {
     double rtol;                 /* relative tolerance on |r| / |rhs| (>= 0) */
     double atol;                 /* absolute tolerance on |r| (>= 0) */

@@ -90,3 +90,39 @@ def test_package_has_no_cpu_path():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "scipy" not in text and "numpy.linalg" not in text, f
+
+
+def test_struct_layouts_match_the_compiled_header(tmp_path):
+    # sizeof / offsetof from a C program built against include/sla.h, field by field
+    import shutil
+    import subprocess
+    from differentiable_sparse_linear_spmv_amd import _lib
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    structs = {"sla_cg_opts": _lib.SlaCgOpts, "sla_cg_info": _lib.SlaCgInfo, "sla_eig_opts": _lib.SlaEigOpts,
+               "sla_eig_info": _lib.SlaEigInfo}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "sla.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0; }"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_allocator_hook_arguments(lib):
+    from differentiable_sparse_linear_spmv_amd import _lib
+    assert lib.sla_set_allocator(_lib.ALLOC_FN(), _lib.FREE_FN(), None) == 0     # back to hipMalloc
+    only_alloc = _lib.ALLOC_FN(lambda n, s, c: None)
+    assert lib.sla_set_allocator(only_alloc, _lib.FREE_FN(), None) == 1         # SLA_ERR_INVALID_ARG
+    assert b"both" in lib.sla_last_error()
+    assert lib.sla_set_allocator(_lib.ALLOC_FN(), _lib.FREE_FN(), None) == 0

@@ -1,0 +1,112 @@
+"""The library's device memory through a caller's allocator (sla_set_allocator),
+through the C ABI: torch's caching allocator holds the workspaces while a handle
+lives, the results are those of the hipMalloc path bit for bit (the same kernels on
+the same data), and every block goes back through the allocator that made it, also
+after the allocator has been switched back.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import differentiable_sparse_linear_spmv_amd as S
+    yield S
+    S.use_torch_allocator(False)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def run(S, A, b, X0):
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=True)
+    vals = dev(A.vals)
+    x, _ = S.solve(h, vals, dev(b), S.cg_opts(rtol=1e-10))
+    gb, gv, _ = S.solve_backward(h, vals, x, x.clone(), S.cg_opts(rtol=1e-10))
+    ev, U, _ = S.eigsh(h, vals, 3, dev(b), tol=1e-10)
+    ew, V, _ = S.lobpcg(h, vals, 3, dev(X0), tol=1e-8)
+    torch.cuda.synchronize()
+    return h, [t.cpu().numpy() for t in (x, gb, gv, ev, U, ew, V)]
+
+
+def test_handle_outlives_the_switch(S):
+    # blocks from torch's allocator, the allocator switched back, then the handle
+    # destroyed: its blocks still go back to torch (the callbacks stay alive)
+    base = torch.cuda.memory_allocated()
+    S.use_torch_allocator(True)
+    A = W.poisson5(40)
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=True)
+    x, info = S.solve(h, dev(A.vals), dev(W.rhs_normal(A.n_rows, 3)), S.cg_opts(rtol=1e-8))
+    S.use_torch_allocator(False)
+    gc.collect()
+    del h, x, info
+    gc.collect()
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() <= base
+
+
+def test_torch_allocator_holds_the_workspaces(S):
+    A, b, _ = W.varcoef_poisson5(60, seed=2)
+    X0 = np.stack([W.rhs_normal(A.n_rows, 5 + r) for r in range(3)])
+    S.use_torch_allocator(False)
+    h, ref = run(S, A, b, X0)
+    del h
+    gc.collect()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    S.use_torch_allocator(True)
+    h, out = run(S, A, b, X0)
+    held = torch.cuda.memory_allocated() - base
+    # at least the CG workspace (4 vectors) and the LOBPCG block pool (43 vectors)
+    assert held >= 8 * A.n_rows * (4 + 43), held
+    for r, o in zip(ref, out):
+        assert np.array_equal(r, o)
+    del h
+    gc.collect()
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() - base <= 8 * A.n_rows * 4   # only the results remain
+    S.use_torch_allocator(False)
+
+
+def test_blocks_return_to_their_allocator(S):
+    from differentiable_sparse_linear_spmv_amd import _lib as L
+    calls = {"alloc": 0, "free": 0}
+
+    def _alloc(size, stream, ctx):
+        calls["alloc"] += 1
+        return torch.cuda.caching_allocator_alloc(int(size))
+
+    def _free(ptr, stream, ctx):
+        calls["free"] += 1
+        torch.cuda.caching_allocator_delete(ptr)
+
+    cbs = (L.ALLOC_FN(_alloc), L.FREE_FN(_free))
+    lib = L.load()
+    assert lib.sla_set_allocator(cbs[0], cbs[1], None) == 0
+    A = W.poisson5(50)
+    b = W.rhs_normal(A.n_rows, 1)
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=False)   # the adjoint builds a transpose
+    x, _ = S.solve(h, dev(A.vals), dev(b), S.cg_opts(rtol=1e-8))
+    S.solve_backward(h, dev(A.vals), x, x.clone(), S.cg_opts(rtol=1e-8))
+    torch.cuda.synchronize()
+    # blocks live in the handle (workspace, transpose, transposed values); create-time
+    # validation and transpose scratch have come and gone already
+    live = calls["alloc"] - calls["free"]
+    assert live >= 3, calls
+    # switch back to hipMalloc while the handle holds blocks of the callbacks: its
+    # destruction must still free them through the callbacks
+    assert lib.sla_set_allocator(L.ALLOC_FN(), L.FREE_FN(), None) == 0
+    del h
+    gc.collect()
+    torch.cuda.synchronize()
+    assert calls["free"] == calls["alloc"], calls
