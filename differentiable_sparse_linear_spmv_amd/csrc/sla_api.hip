@@ -653,7 +653,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     const bool jacobi = (o->flags & SLA_JACOBI) != 0;
     if (list) band = 0;
     if (!list && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 &&
-        A->krp_bits == 32 &&
+        A->krp_bits == 32 && A->nnz > 0 &&
         A->group_ok &&
         static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapLarge && row_ptr == A->krp)
         return run_cg_grouped(A, row_ptr, col, batch, vals, b, x, o, info, s);
@@ -852,7 +852,8 @@ int64_t band_stride_of(int64_t n_rows, int64_t n_cols, int64_t nnz, int32_t row_
         if (end != env && v > 0) min_stride = v;
     }
     const int64_t S = far_max;
-    if (n_rows != n_cols || n_rows >= (int64_t(1) << 29) || nnz >= (int64_t(1) << 31) || S <= 0) return 0;
+    // (an empty pattern never takes the banded kernel: its staging clamps to entry nnz - 1)
+    if (n_rows != n_cols || n_rows >= (int64_t(1) << 29) || nnz < 1 || nnz >= (int64_t(1) << 31) || S <= 0) return 0;
     if (far_min < S - kBandHalo) return 0;
     if (S < kTile + 2 * kBandHalo || S < min_stride) return 0;
     if (static_cast<int64_t>(kTile) * row_max > kCapLarge) return 0;
@@ -1100,6 +1101,30 @@ sla_status sla_matvec_backward(const sla_csr* Ac, int64_t batch, const double* d
     return SLA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// A 0 x 0 system: every one converges with 0 iterations (x and lambda are empty).
+sla_status empty_solve_info(int64_t batch, sla_cg_info* d_info, hipStream_t s)
+{
+    std::vector<sla_cg_info> h(static_cast<size_t>(batch));
+    for (auto& i : h) {
+        i.iterations = 0;
+        i.res_norm = 0.0;
+        i.rhs_norm = 0.0;
+        i.state = SLA_CONVERGED;
+        i.reserved = 0;
+    }
+    HIP_TRY(hipMemcpyAsync(d_info, h.data(), sizeof(sla_cg_info) * h.size(), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));   // h is pageable and local
+    return SLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, const double* d_b, double* d_x,
                      const sla_cg_opts* opts, sla_cg_info* d_info, void* stream)
 {
@@ -1107,7 +1132,9 @@ sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, con
     if (st != SLA_OK) return st;
     if (Ac->n_rows != Ac->n_cols) return fail(SLA_ERR_UNSUPPORTED, "solve needs a square matrix");
     if ((st = check_opts(opts)) != SLA_OK) return st;
-    if ((!d_vals && Ac->nnz > 0) || !d_b || !d_x || !d_info) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    if (!d_info) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    if (Ac->n_rows == 0) return empty_solve_info(batch, d_info, static_cast<hipStream_t>(stream));
+    if ((!d_vals && Ac->nnz > 0) || !d_b || !d_x) return fail(SLA_ERR_INVALID_ARG, "NULL array");
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lk(A->mu);
@@ -1131,7 +1158,9 @@ sla_status sla_solve_backward(const sla_csr* Ac, int64_t batch, const double* d_
     if (st != SLA_OK) return st;
     if (Ac->n_rows != Ac->n_cols) return fail(SLA_ERR_UNSUPPORTED, "solve_backward needs a square matrix");
     if ((st = check_opts(opts)) != SLA_OK) return st;
-    if ((!d_vals && Ac->nnz > 0) || !d_gx || !d_gb || !d_info || (d_gvals && !d_x))
+    if (!d_info) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    if (Ac->n_rows == 0) return empty_solve_info(batch, d_info, static_cast<hipStream_t>(stream));
+    if ((!d_vals && Ac->nnz > 0) || !d_gx || !d_gb || (d_gvals && !d_x))
         return fail(SLA_ERR_INVALID_ARG, "NULL array");
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -230,7 +230,9 @@ sla_status sla_matvec_backward(const sla_csr* A, int64_t batch, const double* d_
  * synchronisation happens inside an iteration: scalars and stop decisions live on
  * the device.  Requires n_rows == n_cols.  b = 0 gives x = 0 after 0 iterations.
  * With SLA_JACOBI in opts->flags the CG is Jacobi-preconditioned; with SLA_BICGSTAB
- * the method is BiCGStab (see the flags above).
+ * the method is BiCGStab (see the flags above).  A 0 x 0 matrix: every system
+ * converges with 0 iterations (d_b and d_x may be NULL; the info records are written,
+ * synchronously); a pattern with no entries is A = 0 (SLA_NOT_SPD unless b = 0).
  */
 sla_status sla_solve(const sla_csr* A, int64_t batch, const double* d_vals, const double* d_b,
                      double* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
