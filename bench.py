@@ -562,7 +562,7 @@ def main() -> int:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
         return 0
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         return 2
     rank = int(os.environ.get("RANK", "0"))
