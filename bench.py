@@ -106,6 +106,9 @@ def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
                 flops_iteration=(4 * nnz + 24 * n) * batch)
 
 
+LZ_FUSED_COLS = 32   # the library's fused update-and-dots threshold (bases of <= 32 vectors)
+
+
 def lanczos_positions(steps: int, max_dim: int, keep: int) -> list:
     """Basis position j of every Lanczos step: 0 .. max_dim - 1, then after each thick
     restart keep .. max_dim - 1 again (no restart: 0 .. steps - 1)."""
@@ -129,6 +132,8 @@ def eigsh_bytes(n: int, nnz: int, rp_bytes: int, steps: int, max_dim: int = 0, k
                w) 4 x 8 n; two Gram-Schmidt passes, each: dots read V_{0..j} and w,
                (j + 2) x 8 n, update read V_{0..j} and w, write w, (j + 3) x 8 n; next
                vector (read w, write v_{j+1}) 2 x 8 n               -> (4 j + 16) x 8 n
+               with j + 1 <= LZ_FUSED_COLS the first update and the second dots
+               share one read of V and w (and one write of w)       -> (3 j + 14) x 8 n
                plus, on the first step after a restart, the couplings: read V_{0..keep-1}
                and w, write w                                       -> (keep + 2) x 8 n
       restart  (per restart, timed with the Ritz kernels): read V_{0..m-1}, write
@@ -138,7 +143,8 @@ def eigsh_bytes(n: int, nnz: int, rp_bytes: int, steps: int, max_dim: int = 0, k
     mat = 8 * nnz + 4 * nnz + rp_bytes * (n + 1)
     spmv = mat + 2 * 8 * n
     pos = lanczos_positions(steps, max_dim, keep)
-    orth = sum((4 * j + 16) * 8 * n for j in pos) + restarts * (keep + 2) * 8 * n
+    orth = sum(((3 * j + 14) if j + 1 <= LZ_FUSED_COLS else (4 * j + 16)) * 8 * n for j in pos) \
+        + restarts * (keep + 2) * 8 * n
     rst = restarts * (max_dim + keep + 2) * 8 * n
     return dict(lz_spmv=spmv, lz_orth_total=orth, restart_total=rst, run=steps * spmv + orth + rst)
 

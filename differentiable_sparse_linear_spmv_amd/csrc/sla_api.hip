@@ -1349,11 +1349,20 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
         hipError_t e0 = timed(SLA_K_LZ_SPMV, s, [&] { return launch_bs(4, c, j, rp_bits, A->cap, s); });
         if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(2, a, j, 0.0, 0, s); });
         if (e0 == hipSuccess && couple) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(5, a, j, 0.0, 0, s); });
-        for (int pass = 0; pass < 2 && e0 == hipSuccess; ++pass) {
-            e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(3, a, j + 1, 0.0, 0, s); });
+        if (j + 1 <= kLzFusedCols) {
+            // dots, reduce, (update + second dots), reduce, update with |w|^2 partials
+            if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(3, a, j + 1, 0.0, 0, s); });
             if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(4, a, j + 1, 0.0, 0, s); });
-            if (e0 == hipSuccess)
-                e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(5, a, j + 1, 0.0, pass == 1, s); });
+            if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz_axpy_dots(a, j + 1, s); });
+            if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(4, a, j + 1, 0.0, 0, s); });
+            if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(5, a, j + 1, 0.0, 1, s); });
+        } else {
+            for (int pass = 0; pass < 2 && e0 == hipSuccess; ++pass) {
+                e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(3, a, j + 1, 0.0, 0, s); });
+                if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(4, a, j + 1, 0.0, 0, s); });
+                if (e0 == hipSuccess)
+                    e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(5, a, j + 1, 0.0, pass == 1, s); });
+            }
         }
         if (e0 == hipSuccess) e0 = timed(SLA_K_LZ_ORTH, s, [&] { return launch_lz(6, a, j, 0.0, 0, s); });
         return e0;

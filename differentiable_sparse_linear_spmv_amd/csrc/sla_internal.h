@@ -148,6 +148,10 @@ hipError_t launch_lz(int which, const LzArgs& a, int64_t j, double nrm, int last
 // Thick restart in place: V[r] = sum_{l<m} S[r][l] V[l] for r < lk (S [lk][m] on the
 // device), then V[lk] = V[m].  Needs 1 <= lk < m <= kLzStage.
 constexpr int64_t kLzStage = 8192;   // doubles of V staged in LDS per workgroup (64 KiB)
+// The first reorthogonalization pass's update fused with the second pass's dots (one
+// read of V instead of two) for bases of at most kLzFusedCols columns.
+constexpr int kLzFusedCols = 32;
+hipError_t launch_lz_axpy_dots(const LzArgs& a, int64_t ncols, hipStream_t s);
 hipError_t launch_lz_restart(const LzArgs& a, int64_t m, int64_t lk, hipStream_t s);
 // dL/dvals[e] = sum_r g[r] U[r][row(e)] U[r][col(e)] (Hellmann-Feynman), g and U on the device.
 hipError_t launch_eig_grad(const void* row_ptr, int rp_bits, const int32_t* col, const double* U, const double* g,

@@ -1840,6 +1840,58 @@ __global__ __launch_bounds__(kBlock) void k_lz_axpy(LzArgs a, int64_t ncols, int
     }
 }
 
+// The first pass's update and the second pass's dots in one read of V, for bases of at
+// most MAXC columns: each thread keeps its row's v_0 .. v_{ncols-1} in registers, forms
+// w_i -= sum_c h[c] v_c[i] (c ascending, as k_lz_axpy) and accumulates v_c[i] w_i over
+// its rows of this workgroup's kLzRows; the per-column sums (waves, then the four waves
+// in order) are the partials part_h[c][blockIdx.x] that k_lz_reduce sums, as after
+// k_lz_dots.
+template <int MAXC>
+__global__ __launch_bounds__(kBlock) void k_lz_axpy_dots(LzArgs a, int ncols)
+{
+    __shared__ double s_w[kBlock / 64][MAXC];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kLzRows;
+    double d[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) d[c] = 0.0;
+#pragma unroll 1
+    for (int t = 0; t < kLzRows / kBlock; ++t) {
+        const int64_t i = r0 + threadIdx.x + t * kBlock;
+        if (i < a.n) {
+            double v[MAXC];
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) v[c] = c < ncols ? a.V[static_cast<int64_t>(c) * a.n + i] : 0.0;
+            double acc = 0.0;
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+                if (c < ncols) {
+                    const double p = ld_uniform(a.h, c) * v[c];
+                    acc = acc + p;
+                }
+            }
+            const double wi = a.w[i] - acc;
+            a.w[i] = wi;
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+                const double p = v[c] * wi;
+                d[c] = d[c] + p;
+            }
+        }
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const double sum = wave_sum(d[c]);
+        if (lane == 0) s_w[wv][c] = sum;
+    }
+    __syncthreads();
+    if (threadIdx.x < ncols) {
+        const int c = threadIdx.x;
+        const double tsum = (s_w[0][c] + s_w[1][c]) + (s_w[2][c] + s_w[3][c]);
+        a.part_h[static_cast<int64_t>(c) * a.Gd + blockIdx.x] = tsum;
+    }
+}
+
 // beta_j = |w|, v_{j+1} = w / beta_j (0 when beta_j = 0: the Krylov space is invariant).
 __global__ __launch_bounds__(kBlock) void k_lz_next(LzArgs a, int64_t j)
 {
@@ -3349,6 +3401,15 @@ hipError_t launch_blk_comb(const double* in, const int32_t* idx_in, int m, const
     else if (q <= 8) SLA_LAUNCH(k_blk_comb<8>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
     else if (q <= 16) SLA_LAUNCH(k_blk_comb<16>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
     else SLA_LAUNCH(k_blk_comb<32>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+    return hipGetLastError();
+}
+
+hipError_t launch_lz_axpy_dots(const LzArgs& a, int64_t ncols, hipStream_t s)
+{
+    if (ncols < 1 || ncols > kLzFusedCols) return hipErrorInvalidValue;
+    static_assert(kBlock / 64 == 4 && kLzRows % kBlock == 0, "four waves, whole trips");
+    SLA_LAUNCH(k_lz_axpy_dots<kLzFusedCols>, dim3(static_cast<unsigned>(a.Gd)), dim3(kBlock), 0, s, a,
+               static_cast<int>(ncols));
     return hipGetLastError();
 }
 
