@@ -60,3 +60,25 @@ def test_side_stream_gives_the_same_bits(S):
     side.synchronize()
     for i, (u, v) in enumerate(zip(ref, got)):
         assert np.array_equal(u, v), i
+
+
+def test_polling_interval_changes_nothing(S):
+    # the host checks the stop word (CG) or the Ritz pairs (Lanczos) once per chunk of
+    # iterations; work enqueued past the stop is discarded, so the chunk size must not
+    # change a bit of the results or the counts
+    A, b, _ = W.varcoef_poisson5(70, seed=9)
+    h = S.csr_create(dev(A.row_ptr), dev(A.col), symmetric=True)
+    vals = dev(A.vals)
+    ref = None
+    for every in (1, 5, 32, 200):
+        o = S.cg_opts(rtol=1e-10, check_every=every)
+        x, info = S.solve(h, vals, dev(b), o)
+        ev, U, einfo = S.eigsh(h, vals, 3, dev(b), tol=1e-10, check_every=every)
+        out = (x.cpu().numpy(), ev.cpu().numpy(), U.cpu().numpy(), S.read_info(info)[0]["iterations"],
+               einfo["iterations"])
+        if ref is None:
+            ref = out
+            continue
+        for u, v in zip(ref[:3], out[:3]):
+            assert np.array_equal(u, v), every
+        assert ref[3:] == out[3:], (every, ref[3:], out[3:])
