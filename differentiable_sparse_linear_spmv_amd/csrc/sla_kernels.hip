@@ -2127,6 +2127,106 @@ __global__ __launch_bounds__(kBlock) void k_blk_gram(const double* __restrict__ 
     }
 }
 
+// The same Gram partials for many pairs (mu mv > kBlock), in 4 x 4 register tiles: tile
+// (ta, tb) holds the pairs a = 4 ta + da, b = 4 tb + db; per row a thread reads 8
+// staged values for 16 products (two reads per product without tiles, which made the
+// wide Rayleigh-Ritz Gram LDS-bound).  tpp threads share a tile over rows r = sub,
+// sub + tpp, ..., their sums added in order of sub at the end; with PT tiles per
+// thread.  Operand columns past mu (mv) read column mu - 1 (mv - 1) and are not written.
+template <int PT>
+__global__ __launch_bounds__(kBlock) void k_blk_gram_tiled(const double* __restrict__ A,
+                                                           const int32_t* __restrict__ ia, int mu,
+                                                           const double* __restrict__ B,
+                                                           const int32_t* __restrict__ ib, int mv, int64_t n, int R,
+                                                           int tpp, double* __restrict__ part)
+{
+    extern __shared__ double s_g[];
+    __shared__ int32_t s_idx[2 * kBlkMaxCols];
+    const int tid = threadIdx.x;
+    const int pad = R + 1;
+    const int ncol = mu + mv;
+    const int np = mu * mv;
+    const int tu = (mu + 3) / 4, tv = (mv + 3) / 4, ntile = tu * tv;
+    for (int t = tid; t < ncol; t += kBlock) s_idx[t] = t < mu ? ia[t] : ib[t - mu];
+    const int sub = tid % tpp;
+    const int lanes = kBlock / tpp;
+    double acc[PT][16];
+    int ra[PT][4], rb[PT][4];
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+        const int tile = min(tid / tpp + u * lanes, ntile - 1);
+        const int ta = tile / tv, tb = tile - ta * tv;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            ra[u][d] = min(4 * ta + d, mu - 1) * pad;
+            rb[u][d] = (mu + min(4 * tb + d, mv - 1)) * pad;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[u][e] = 0.0;
+    }
+    __syncthreads();
+    const int64_t nslices = (n + R - 1) / R;
+    const int total = ncol * R;
+    for (int64_t sl = blockIdx.x; sl < nslices; sl += gridDim.x) {
+        const int64_t r0 = sl * R;
+        const int nr = static_cast<int>(min(static_cast<int64_t>(R), n - r0));
+        for (int t0 = tid; t0 < total; t0 += 8 * kBlock) {
+            double v[8];
+            int dst[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u * kBlock;
+                const bool ok = t < total;
+                const int c = ok ? t / R : 0;
+                const int r = t - c * R;
+                const double* __restrict__ base = c < mu ? A : B;
+                v[u] = (ok && r < nr) ? base[static_cast<int64_t>(s_idx[c]) * n + r0 + r] : 0.0;
+                dst[u] = ok ? c * pad + r : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (dst[u] >= 0) s_g[dst[u]] = v[u];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            for (int r = sub; r < nr; r += tpp) {
+                double xa[4], xb[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    xa[d] = s_g[ra[u][d] + r];
+                    xb[d] = s_g[rb[u][d] + r];
+                }
+#pragma unroll
+                for (int da = 0; da < 4; ++da)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const double p = xa[da] * xb[db];
+                        acc[u][da * 4 + db] = acc[u][da * 4 + db] + p;
+                    }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+        const int tile = tid / tpp + u * lanes;
+        const int ta = tile / tv, tb = tile - ta * tv;
+        for (int e = 0; e < 16; ++e) {
+            // the tpp partial sums of this tile's entry e, added in order of sub
+            s_g[tid] = acc[u][e];
+            __syncthreads();
+            if (sub == 0 && tile < ntile) {
+                const int a = 4 * ta + e / 4, b = 4 * tb + e % 4;
+                double t = 0.0;
+                for (int j = 0; j < tpp; ++j) t = t + s_g[tid + j];
+                if (a < mu && b < mv) part[static_cast<int64_t>(blockIdx.x) * np + a * mv + b] = t;
+            }
+            __syncthreads();
+        }
+    }
+}
+
 // tinv[i] = 1 / a_ii (binary search for column i in row i; the columns are sorted), and
 // per workgroup the number of rows whose a_ii is missing, not finite or not positive
 // (part[blockIdx.x], as a double).
@@ -3342,6 +3442,19 @@ hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const dou
     // the LDS holds the staged slice and, at the end, kBlock partial sums
     const size_t lds = sizeof(double) * std::max<size_t>(static_cast<size_t>(mu + mv) * (R + 1), kBlock);
     const dim3 grid(static_cast<unsigned>(G)), blk(kBlock);
+    if (np > kBlock) {   // many pairs: 4 x 4 register tiles
+        const int ntile = ((mu + 3) / 4) * ((mv + 3) / 4);
+        int tpt = 1;   // threads per tile: a power of 2 with ntile tpt <= kBlock
+        while (ntile * tpt * 2 <= kBlock) tpt *= 2;
+        const int pt = (ntile + kBlock / tpt - 1) / (kBlock / tpt);
+        if (pt <= 1) SLA_LAUNCH(k_blk_gram_tiled<1>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, tpt, part);
+        else if (pt <= 2) SLA_LAUNCH(k_blk_gram_tiled<2>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, tpt, part);
+        else SLA_LAUNCH(k_blk_gram_tiled<3>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, tpt, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), blk, 0, s, part, G, np, out);
+        return hipGetLastError();
+    }
     int tpp = 1;   // threads per pair: a power of 2 with np tpp <= kBlock
     while (np * tpp * 2 <= kBlock) tpp *= 2;
     const int pp = (np + kBlock - 1) / kBlock;
