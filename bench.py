@@ -324,7 +324,8 @@ def make_workload(name: str, device):
         return dict(name=name, n=N * N, nnz=col.numel(), batch=1, rp=rp, col=col, vals=vals, b=b,
                     rtol=0.0, max_iter=c["max_iter"], fixed=True, loss="half_sq", host=None,
                     method="cg", symmetric=True,
-                    desc=f"5-point Poisson {N}x{N}, int64 row_ptr, b~N(0,1) seed 0, "
+                    desc=f"5-point Poisson {N}x{N}, int64 row_ptr handed in (the kernels read an int32 copy: "
+                         f"nnz < 2^31), b~N(0,1) seed 0, "
                          f"{c['max_iter']} fixed CG iterations + {c['max_iter']} adjoint")
     c = W.config(name)
     A = c["A"]
