@@ -58,14 +58,16 @@ def kernel_source_hash() -> str:
 
 
 # ------------------------------------------------------------------------------ bytes model
-def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False) -> dict:
+def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False, col_bytes: int = 4) -> dict:
     """Algorithmic HBM bytes of the kernels, per launch (all systems of the batch).
 
     rp_bytes is the width of the row pointers the kernels read: 4 whenever nnz < 2^31
-    (the library keeps a 32-bit copy of 64-bit row pointers that fit).
+    (the library keeps a 32-bit copy of 64-bit row pointers that fit).  col_bytes is
+    the width of the column indices the SpMV reads: 2 where the handle holds 16-bit
+    column offsets (sla_csr_col_bits), else 4.
 
     Fused schedule (plain or banded SpMV):
-      cg_spmv  : values 8 nnz B + columns 4 nnz + row pointers rp (n + 1)
+      cg_spmv  : values 8 nnz B + columns col_bytes nnz + row pointers rp (n + 1)
                  + vectors: read r, p_{k-1}, x; write p_k, q, x   -> 6 x 8 n B
       cg_update: read r, q; write r                              -> 3 x 8 n B
       one CG iteration = both (nine vector passes).
@@ -75,7 +77,7 @@ def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False
                  cache traffic), write q                          -> 2 x 8 n B
       cg_update: as above; one iteration = ten vector passes.
     """
-    mat = 8 * nnz * batch + 4 * nnz + rp_bytes * (n + 1)
+    mat = 8 * nnz * batch + col_bytes * nnz + rp_bytes * (n + 1)
     upd = 3 * 8 * n * batch
     if split:
         pupd = 5 * 8 * n * batch
@@ -87,7 +89,7 @@ def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False
                 flops_iteration=(2 * nnz + 10 * n) * batch)
 
 
-def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
+def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int, col_bytes: int = 4) -> dict:
     """Algorithmic HBM bytes of the BiCGStab kernels, per launch (all systems).
 
       v = A p  : values, columns, row pointers + read p (the gathers are cache traffic)
@@ -98,7 +100,7 @@ def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int) -> dict:
       update   : read x, p, s, t, rh; write x, r -> 7;  bs_vec: the mean of the three
       one iteration = both products + 14 vector passes.
     """
-    mat = 8 * nnz * batch + 4 * nnz + rp_bytes * (n + 1)
+    mat = 8 * nnz * batch + col_bytes * nnz + rp_bytes * (n + 1)
     v = 8 * n * batch
     spmv_v, spmv_t = mat + 3 * v, mat + 2 * v
     vec = 14 * v
@@ -123,7 +125,7 @@ def lanczos_positions(steps: int, max_dim: int, keep: int) -> list:
 
 
 def eigsh_bytes(n: int, nnz: int, rp_bytes: int, steps: int, max_dim: int = 0, keep: int = 0,
-                restarts: int = 0) -> dict:
+                restarts: int = 0, col_bytes: int = 4) -> dict:
     """Algorithmic HBM bytes of a Lanczos run of `steps` steps.
 
       lz_spmv  (per step): values, columns, row pointers + read v_j (the gathers are
@@ -140,7 +142,7 @@ def eigsh_bytes(n: int, nnz: int, rp_bytes: int, steps: int, max_dim: int = 0, k
                V_{0..keep-1}, copy v_m                               -> (m + keep + 2) x 8 n
       lz_ritz  u_r = V s_r: read V_{0..m-1} once, write k vectors (plus the start)
     """
-    mat = 8 * nnz + 4 * nnz + rp_bytes * (n + 1)
+    mat = 8 * nnz + col_bytes * nnz + rp_bytes * (n + 1)
     spmv = mat + 2 * 8 * n
     pos = lanczos_positions(steps, max_dim, keep)
     orth = sum(((3 * j + 14) if j + 1 <= LZ_FUSED_COLS else (4 * j + 16)) * 8 * n for j in pos) \
@@ -177,7 +179,8 @@ def run_eigsh(args, w, S, torch) -> dict:
     tq = S.timing.query()
     n, nnz = w["n"], w["nnz"]
     keep = w["keep"] or min(w["max_dim"] - 1, max(k + 1, (w["max_dim"] + k) // 2))
-    bm = eigsh_bytes(n, nnz, 4, steps_run, w["max_dim"], keep, infos[-1]["restarts"])
+    bm = eigsh_bytes(n, nnz, 4, steps_run, w["max_dim"], keep, infos[-1]["restarts"],
+                     col_bytes=S.csr_analysis(h)["col_bits"] // 8)
     orth_ms = tq["lz_orth"]["total_ms"]
     spmv_ms = tq["lz_spmv"]["total_ms"] / max(tq["lz_spmv"]["launches"], 1)
     achieved = bm["lz_orth_total"] / (orth_ms * 1e-3) / 1e9
@@ -265,9 +268,10 @@ def run_list(args, c, S, torch, dev) -> dict:
     S.timing.enable(False)
     tq = S.timing.query()
     # algorithmic bytes of every item-iteration of the fused CG SpMV, over its measured time
-    per_item = [bytes_model(A.n_rows, A.nnz, 1, 4)["cg_spmv"] for A in items]
+    cb = S.list_col_bits(h) // 8
+    per_item = [bytes_model(A.n_rows, A.nnz, 1, 4, col_bytes=cb)["cg_spmv"] for A in items]
     spmv_bytes = float(np.dot(np.array(fi) + np.array(bi), per_item))
-    it_bytes = float(np.dot(np.array(fi) + np.array(bi), [bytes_model(A.n_rows, A.nnz, 1, 4)["iteration"]
+    it_bytes = float(np.dot(np.array(fi) + np.array(bi), [bytes_model(A.n_rows, A.nnz, 1, 4, col_bytes=cb)["iteration"]
                                                           for A in items]))
     spmv_ms = tq["cg_spmv"]["total_ms"]
     iter_ms = spmv_ms + tq["cg_update"]["total_ms"] + tq["cg_pupd"]["total_ms"]
@@ -711,6 +715,9 @@ def main() -> int:
         spmv_kernel, schedule = "k_cg_spmv", "split (k_cg_pupd forms p_k, the SpMV gathers it)"
     else:
         spmv_kernel, schedule = "k_cg_spmv", "fused"
+    # the plain SpMV (CG and BiCGStab) reads the 16-bit column offsets where the handle
+    # has them; the banded and grouped kernels read the 32-bit columns
+    col_bytes = an["col_bits"] // 8 if spmv_kernel.startswith("k_cg_spmv ") or spmv_kernel == "k_cg_spmv" else 4
     if args.fixed_iters > 0:
         w["max_iter"], w["fixed"], w["rtol"] = args.fixed_iters, True, 0.0
     opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"], jacobi=args.jacobi,
@@ -766,12 +773,12 @@ def main() -> int:
         return tq[key]["total_ms"] / max(tq[key]["launches"], 1)
 
     if bicg:
-        bm = bytes_model_bicgstab(n, nnz, B, rp_bytes)
+        bm = bytes_model_bicgstab(n, nnz, B, rp_bytes, col_bytes)
         spmv_ms, spmv_bytes = avg_ms("bs_spmv"), bm["bs_spmv"]
         # per iteration: two products and three streaming kernels (init excluded)
         iter_ms = 2 * spmv_ms + 3 * avg_ms("bs_vec")
     else:
-        bm = bytes_model(n, nnz, B, rp_bytes, split=an["split"])
+        bm = bytes_model(n, nnz, B, rp_bytes, split=an["split"], col_bytes=col_bytes)
         spmv_ms, spmv_bytes = avg_ms("cg_spmv"), bm["cg_spmv"]
         iter_ms = spmv_ms + avg_ms("cg_update") + (avg_ms("cg_pupd") if an["split"] else 0.0)
     achieved = spmv_bytes / (spmv_ms * 1e-3) / 1e9

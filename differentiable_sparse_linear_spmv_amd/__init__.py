@@ -12,10 +12,10 @@ from ._lib import SlaError
 _lib.load()
 
 from .sparse import (SparseTensor, SparseTensorList, cg_opts, csr_analysis, csr_create,  # noqa: E402
-                     csr_destroy, csr_info, eigsh, eigsh_backward, list_create, list_solve,
+                     csr_destroy, csr_info, eigsh, eigsh_backward, list_col_bits, list_create, list_solve,
                      list_solve_backward, lobpcg, matvec, matvec_backward, read_info, solve, solve_backward, timing,
                      use_torch_allocator)
 
 __all__ = ["SparseTensor", "SparseTensorList", "SlaError", "cg_opts", "csr_analysis", "csr_create", "csr_destroy",
-           "csr_info", "eigsh", "eigsh_backward", "list_create", "list_solve", "list_solve_backward", "lobpcg",
+           "csr_info", "eigsh", "eigsh_backward", "list_col_bits", "list_create", "list_solve", "list_solve_backward", "lobpcg",
            "matvec", "matvec_backward", "read_info", "solve", "solve_backward", "timing", "use_torch_allocator"]

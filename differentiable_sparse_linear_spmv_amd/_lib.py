@@ -33,8 +33,8 @@ KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "g
                 "lz_ritz", "lob_spmm", "lob_gram", "lob_comb"]
 
 EXPORTS = [
-    "sla_set_allocator", "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_matvec", "sla_matvec_backward",
-    "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_solve",
+    "sla_set_allocator", "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_csr_col_bits", "sla_matvec", "sla_matvec_backward",
+    "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_col_bits", "sla_list_solve",
     "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable",
     "sla_timing_reset", "sla_timing_collect", "sla_timing_query", "sla_timing_query_bytes", "sla_status_string",
     "sla_last_error", "sla_version",
@@ -106,6 +106,8 @@ def load():
     L.sla_csr_analysis.argtypes = [P, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32), C.POINTER(i64),
                                    C.POINTER(i32)]
     L.sla_csr_analysis.restype = st
+    L.sla_csr_col_bits.argtypes = [P, C.POINTER(i32)]
+    L.sla_csr_col_bits.restype = st
     L.sla_matvec.argtypes = [P, i64, P, P, P, P]
     L.sla_matvec.restype = st
     L.sla_matvec_backward.argtypes = [P, i64, P, P, P, P, P, P]
@@ -120,6 +122,8 @@ def load():
     L.sla_list_destroy.restype = st
     L.sla_list_info.argtypes = [P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i32)]
     L.sla_list_info.restype = st
+    L.sla_list_col_bits.argtypes = [P, C.POINTER(i32)]
+    L.sla_list_col_bits.restype = st
     L.sla_list_solve.argtypes = [P, P, P, P, C.POINTER(SlaCgOpts), P, P]
     L.sla_list_solve.restype = st
     L.sla_list_solve_backward.argtypes = [P, P, P, P, P, P, C.POINTER(SlaCgOpts), P, P]

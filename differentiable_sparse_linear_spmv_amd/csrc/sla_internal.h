@@ -65,6 +65,7 @@ static_assert(sizeof(SysState) == 80, "SysState layout");
 struct CgArgs {
     const void* row_ptr;     // int32 or int64 [n + 1]
     const int32_t* col;      // [nnz]
+    const int16_t* col16;    // nullable, [nnz]: col minus the tile's first row (staged SpMV)
     const double* vals;      // [batch][nnz]
     const double* b;         // [batch][n]   right-hand side (r_0)
     double* x;               // [batch][n]
@@ -259,6 +260,12 @@ hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col,
 
 // out[i] = (int32) in[i] for i < n: 32-bit copy of 64-bit row pointers whose values fit.
 hipError_t launch_narrow_rp(const int64_t* in, int32_t* out, int64_t n, hipStream_t s);
+
+// 16-bit column offsets for the staged CG SpMV: out[e] = col[e] - (first row of the
+// 256-row tile holding entry e).  They fit when every stored entry has
+// |c - i| <= kCol16MaxSpan (then c - row0 lies in [-kCol16MaxSpan, 32767]).
+constexpr int32_t kCol16MaxSpan = 32767 - (kTile - 1);
+hipError_t launch_col16(const int32_t* rp, const int32_t* col, int16_t* out, int64_t n_rows, hipStream_t s);
 
 // Transposed pattern: row_ptr_t (same width as rp_bits) [n_cols + 1], col_t [nnz],
 // perm [nnz] (position in A of each entry of A^T).  scratch: see transpose_scratch_bytes.

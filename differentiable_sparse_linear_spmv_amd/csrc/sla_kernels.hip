@@ -561,9 +561,13 @@ struct TileStage {
 // Issue (without waiting) the loads of tile t.  k0 / k1 are the tile's first and
 // end entry positions (known two tiles ahead).  Indices are clamped so no load sits
 // behind a branch; the tile's entries are staged only if they fit the LDS cap.
-template <typename RP, int CAP, bool OFF32, bool SPLIT>
+// C16: the columns are read from the 16-bit offsets col16 (column minus the tile's
+// first row, sign-extended by the load itself); the tile's first row is added when
+// they are written to LDS.
+template <typename RP, int CAP, bool OFF32, bool SPLIT, bool C16>
 __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const RP* __restrict__ rp,
-                                           const int32_t* __restrict__ col, const double* __restrict__ vals,
+                                           const int32_t* __restrict__ col, const int16_t* __restrict__ col16,
+                                           const double* __restrict__ vals,
                                            const double* __restrict__ rin, const double* __restrict__ pprev,
                                            const double* __restrict__ x, int64_t t, int64_t n, int64_t k0,
                                            int64_t k1)
@@ -583,13 +587,23 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
     const int64_t cnt = k1 - k0;
     if (cnt <= CAP && cnt > 0) {
         const double* __restrict__ vb = vals + k0;
-        const int32_t* __restrict__ cb = col + k0;
         const int last = static_cast<int>(cnt) - 1;
+        if constexpr (C16) {
+            const int16_t* __restrict__ cb = col16 + k0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = min(tid + u * kBlock, last);
-            S.v[u] = vb[j];
-            S.c[u] = cb[j];
+            for (int u = 0; u < U; ++u) {
+                const int j = min(tid + u * kBlock, last);
+                S.v[u] = vb[j];
+                S.c[u] = cb[j];
+            }
+        } else {
+            const int32_t* __restrict__ cb = col + k0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = min(tid + u * kBlock, last);
+                S.v[u] = vb[j];
+                S.c[u] = cb[j];
+            }
         }
     }
 }
@@ -607,7 +621,10 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
 // computes q and the partial p^T q.  The row sums are the same to the last bit.
 // MODE kSpmvBsV / kSpmvBsT: the two products of a BiCGStab iteration, v = A p with
 // the partial <rh, v> (rh = b), and t = A s with the partials <t, s> and <t, t>.
-template <typename RP, int CAP, bool OFF32, int MODE>
+//
+// C16: the staged columns come from the 16-bit tile offsets a.col16 (2 bytes per entry
+// instead of 4); tiles past the LDS cap still read the 32-bit columns.
+template <typename RP, int CAP, bool OFF32, int MODE, bool C16>
 __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
 {
     constexpr bool SPLIT = MODE != kSpmvFused;
@@ -627,6 +644,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     const int64_t n = a.n;
     const RP* __restrict__ rp = static_cast<const RP*>(a.row_ptr);
     const int32_t* __restrict__ col = a.col;
+    const int16_t* __restrict__ col16 = a.col16;
     const double* __restrict__ vals = a.vals + val_off(a, sys);
     const int64_t ntiles = tr.len;   // positions of this workgroup: tr.first + j * step, below tr.len
     const int64_t Gs = tr.step;
@@ -652,7 +670,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     if (t < ntiles) {
         k0 = tile_k0(t);
         k1 = tile_k1(t);
-        stage_tile<RP, CAP, OFF32, SPLIT>(SA, rp, col, vals, SPLIT ? partner : rin, pprev, x, tile_of(t), n, k0,
+        stage_tile<RP, CAP, OFF32, SPLIT, C16>(SA, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tile_of(t), n, k0,
                                           k1);
     }
     if (t + Gs < ntiles) {
@@ -711,12 +729,13 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         double s = 0.0;
         const double ri = cur.ri, ppi = cur.ppi, xi = cur.xi;
         if (cnt <= CAP) {
+            const int32_t cbase = C16 ? static_cast<int32_t>(row0) : 0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = tid + u * kBlock;
                 if (j < cnt) {
                     s_val[j] = cur.v[u];
-                    s_col[j] = cur.c[u];
+                    s_col[j] = cbase + cur.c[u];
                 }
             }
             const int rs = static_cast<int>(static_cast<int64_t>(cur.a0) - k0);
@@ -733,7 +752,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
                 pv[u] = g(c);
             }
             if (tn < ntiles)
-                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
+                stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
                                                   k0n, k1n);
 #pragma unroll
             for (int u = 0; u < RC; ++u) {
@@ -763,7 +782,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         } else {
             s = tile_rowsum_long(rp, col, vals, row0, nr, g, s_val);
             if (tn < ntiles)
-                stage_tile<RP, CAP, OFF32, SPLIT>(nxt, rp, col, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
+                stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
                                                   k0n, k1n);
         }
         if (tid < nr) {
@@ -3176,6 +3195,20 @@ __global__ __launch_bounds__(kBlock) void k_narrow_i32(const int64_t* __restrict
         out[i] = static_cast<int32_t>(in[i]);
 }
 
+// out[e] = col[e] - (first row of e's 256-row tile): one workgroup per tile, whose
+// entries are contiguous.  The caller has checked that every offset fits 16 bits.
+__global__ __launch_bounds__(kBlock) void k_col16(const int32_t* __restrict__ rp, const int32_t* __restrict__ col,
+                                                  int16_t* __restrict__ out, int64_t n)
+{
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t row0 = t * kTile;
+        const int64_t k0 = rp[row0], k1 = rp[min(row0 + kTile, n)];
+        for (int64_t e = k0 + threadIdx.x; e < k1; e += kBlock)
+            out[e] = static_cast<int16_t>(col[e] - static_cast<int32_t>(row0));
+    }
+}
+
 inline unsigned grid_for(int64_t n, int64_t per_block, int64_t cap = 65536)
 {
     int64_t g = (n + per_block - 1) / per_block;
@@ -3204,26 +3237,28 @@ hipError_t scan_exclusive(int64_t* data, int64_t n, int64_t* scratch, hipStream_
 
 using CgKernel = void (*)(CgArgs, int64_t);
 
-template <typename RP, bool O, int MODE>
+template <typename RP, bool O, int MODE, bool C16 = false>
 CgKernel spmv_kernel_rp(int cap)
 {
-    if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O, MODE>;
-    if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O, MODE>;
-    return k_cg_spmv<RP, kCapLarge, O, MODE>;
+    if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O, MODE, C16>;
+    if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O, MODE, C16>;
+    return k_cg_spmv<RP, kCapLarge, O, MODE, C16>;
 }
 
+// c16: the 16-bit column offsets (built only with 32-bit row pointers and n < 2^29).
 template <int MODE>
-CgKernel spmv_kernel_mode(int rp_bits, int cap, bool off32)
+CgKernel spmv_kernel_mode(int rp_bits, int cap, bool off32, bool c16 = false)
 {
+    if (c16 && rp_bits == 32 && off32) return spmv_kernel_rp<int32_t, true, MODE, true>(cap);
     if (rp_bits == 64)
         return off32 ? spmv_kernel_rp<int64_t, true, MODE>(cap) : spmv_kernel_rp<int64_t, false, MODE>(cap);
     return off32 ? spmv_kernel_rp<int32_t, true, MODE>(cap) : spmv_kernel_rp<int32_t, false, MODE>(cap);
 }
 
-CgKernel spmv_kernel(int rp_bits, int cap, bool off32, bool split = false)
+CgKernel spmv_kernel(int rp_bits, int cap, bool off32, bool split = false, bool c16 = false)
 {
-    return split ? spmv_kernel_mode<kSpmvSplit>(rp_bits, cap, off32)
-                 : spmv_kernel_mode<kSpmvFused>(rp_bits, cap, off32);
+    return split ? spmv_kernel_mode<kSpmvSplit>(rp_bits, cap, off32, c16)
+                 : spmv_kernel_mode<kSpmvFused>(rp_bits, cap, off32, c16);
 }
 
 inline bool off32_ok(int64_t n) { return n < (int64_t(1) << 29); }
@@ -3325,8 +3360,8 @@ hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipS
     if (a.band_stride > 0)
         SLA_LAUNCH(band_kernel(cap), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
     else
-        SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n), a.split != 0), dim3(a.G, a.batch), dim3(kBlock), 0, s,
-                   a, k);
+        SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n), a.split != 0, a.col16 != nullptr), dim3(a.G, a.batch),
+                   dim3(kBlock), 0, s, a, k);
     return hipGetLastError();
 }
 
@@ -3385,9 +3420,9 @@ hipError_t launch_bs(int which, const CgArgs& a, int64_t k, int rp_bits, int cap
     switch (which) {
     case 0: SLA_LAUNCH(k_bs_init, gu, blk, 0, s, a); break;
     case 1: SLA_LAUNCH(k_bs_pupd, gu, blk, 0, s, a, k); break;
-    case 2: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsV>(rp_bits, cap, o), gs, blk, 0, s, a, k); break;
+    case 2: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsV>(rp_bits, cap, o, a.col16 != nullptr), gs, blk, 0, s, a, k); break;
     case 3: SLA_LAUNCH(k_bs_s, gu, blk, 0, s, a, k); break;
-    case 4: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsT>(rp_bits, cap, o), gs, blk, 0, s, a, k); break;
+    case 4: SLA_LAUNCH(spmv_kernel_mode<kSpmvBsT>(rp_bits, cap, o, a.col16 != nullptr), gs, blk, 0, s, a, k); break;
     default: SLA_LAUNCH(k_bs_update, gu, blk, 0, s, a, k); break;
     }
     return hipGetLastError();
@@ -3652,6 +3687,13 @@ hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col,
 hipError_t launch_narrow_rp(const int64_t* in, int32_t* out, int64_t n, hipStream_t s)
 {
     hipLaunchKernelGGL(k_narrow_i32, dim3(grid_for(n, kBlock, 8192)), dim3(kBlock), 0, s, in, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_col16(const int32_t* rp, const int32_t* col, int16_t* out, int64_t n_rows, hipStream_t s)
+{
+    const int64_t ntiles = (n_rows + kTile - 1) / kTile;
+    hipLaunchKernelGGL(k_col16, dim3(grid_for(ntiles, 1, 8192)), dim3(kBlock), 0, s, rp, col, out, n_rows);
     return hipGetLastError();
 }
 

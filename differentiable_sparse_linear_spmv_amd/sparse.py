@@ -111,8 +111,10 @@ def csr_analysis(h: Handle) -> dict:
     rm, tm, cap, band, split = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int64(), C.c_int32()
     check(lib.sla_csr_analysis(h.ptr, C.byref(rm), C.byref(tm), C.byref(cap), C.byref(band),
                                C.byref(split)))
+    cb = C.c_int32()
+    check(lib.sla_csr_col_bits(h.ptr, C.byref(cb)))
     return dict(row_max=rm.value, tile_max=tm.value, spmv_cap=cap.value, band_stride=band.value,
-                split=bool(split.value))
+                split=bool(split.value), col_bits=cb.value)
 
 
 def _batch_of(vals: torch.Tensor, nnz: int) -> int:
@@ -346,6 +348,13 @@ def list_create(row_ptrs: list[torch.Tensor], cols: list[torch.Tensor], symmetri
     h = ListHandle(out.value, n, nnz, symmetric, dev)
     h._keep = (row_ptrs, cols)
     return h
+
+
+def list_col_bits(h: ListHandle) -> int:
+    """sla_list_col_bits: 16 if the list's SpMV reads 16-bit column offsets, else 32."""
+    cb = C.c_int32()
+    check(L.load().sla_list_col_bits(h.ptr, C.byref(cb)))
+    return cb.value
 
 
 def list_solve(h: ListHandle, vals: list[torch.Tensor], b: list[torch.Tensor], opts: SlaCgOpts):

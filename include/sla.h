@@ -169,6 +169,16 @@ typedef struct {
  * SLA_BAND_MIN_STRIDE (read at each create).  The CG SpMV of a banded pattern walks
  * the rows line by line and reads the operand from LDS; results are the same to the
  * last bit per row as the plain SpMV's.
+ *
+ * Column offsets: a square pattern with n_rows < 2^29, 32-bit row pointers (or nnz <
+ * 2^31, when the library keeps a 32-bit copy) and every |c - i| <= 32512 also gets
+ * 16-bit column offsets (c minus the first row of the entry's 256-row tile, 2 nnz
+ * bytes of device memory), which the plain CG and BiCGStab SpMV read in place of
+ * d_col_idx: 2 bytes less per stored entry in every product, the same sums to the
+ * last bit.  The environment variable SLA_COL16=0 (read at each create) turns them
+ * off.  When the library builds such a copy (offsets, 32-bit row pointers) the call
+ * synchronises `stream` once more before it returns.  The pattern arrays must stay
+ * unchanged while the handle lives.
  */
 sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t nnz,
                           const void* d_row_ptr, int32_t row_ptr_bits, const int32_t* d_col_idx,
@@ -176,6 +186,10 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
 
 /* Destroy a handle and free everything the library allocated for it (synchronises the device). */
 sla_status sla_csr_destroy(sla_csr* A);
+
+/* Width in bits of the column indices the plain CG / BiCGStab SpMV reads: 16 when the
+ * handle holds 16-bit column offsets (see sla_csr_create), else 32. */
+sla_status sla_csr_col_bits(const sla_csr* A, int32_t* col_bits);
 
 /* Shape and workspace queries (host outputs; any pointer may be NULL). */
 sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int64_t* nnz,
@@ -276,7 +290,7 @@ typedef struct sla_list sla_list;   /* opaque */
  * Every item is validated on the device (SLA_ERR_INVALID_CSR names the first bad one).
  * The packed pattern and its per-item tables are owned by the list; the caller's
  * arrays are only read during this call.  flags: SLA_SYMMETRIC (every item symmetric)
- * and SLA_EAGER_TRANSPOSE as for sla_csr_create.  Synchronises the stream once.
+ * and SLA_EAGER_TRANSPOSE as for sla_csr_create.  Synchronises the stream.
  */
 sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, const int64_t* nnz,
                            const void* const* d_row_ptr, int32_t row_ptr_bits, const int32_t* const* d_col,
@@ -284,6 +298,9 @@ sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, cons
 sla_status sla_list_destroy(sla_list* L);   /* synchronises the device */
 /* Packed sizes (rows with padding, entries) and the number of workgroups of the grid. */
 sla_status sla_list_info(const sla_list* L, int64_t* n_total, int64_t* nnz_total, int32_t* workgroups);
+/* Width in bits of the column indices the list's SpMV reads (16 or 32), as
+ * sla_csr_col_bits for the packed pattern. */
+sla_status sla_list_col_bits(const sla_list* L, int32_t* col_bits);
 
 /*
  * Solve every item: x_i = A_i^{-1} b_i by CG (or Jacobi CG with SLA_JACOBI; SLA_BICGSTAB
