@@ -715,9 +715,9 @@ def main() -> int:
         spmv_kernel, schedule = "k_cg_spmv", "split (k_cg_pupd forms p_k, the SpMV gathers it)"
     else:
         spmv_kernel, schedule = "k_cg_spmv", "fused"
-    # the plain SpMV (CG and BiCGStab) reads the 16-bit column offsets where the handle
-    # has them; the banded and grouped kernels read the 32-bit columns
-    col_bytes = an["col_bits"] // 8 if spmv_kernel.startswith("k_cg_spmv ") or spmv_kernel == "k_cg_spmv" else 4
+    # the plain and banded SpMV (CG and BiCGStab) read 16-bit column offsets where the
+    # handle has them; the grouped kernels read the 32-bit columns
+    col_bytes = 4 if spmv_kernel == "k_gcg_spmv" else an["col_bits"] // 8
     if args.fixed_iters > 0:
         w["max_iter"], w["fixed"], w["rtol"] = args.fixed_iters, True, 0.0
     opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"], jacobi=args.jacobi,

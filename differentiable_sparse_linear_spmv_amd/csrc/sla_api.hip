@@ -47,6 +47,8 @@ struct sla_csr {
     // (SLA_COL16=0 turns them off); null otherwise.
     int16_t* col16 = nullptr;
     int16_t* col16_t = nullptr;   // the same for the transposed pattern
+    int16_t* colb16 = nullptr;    // banded pattern: offsets from the first row of the
+                                  // line-walking SpMV's window of each row
     int device = 0;
     int n_cu = 256;
     int cap = kCapSmall;        // LDS variant for A
@@ -715,6 +717,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     a.row_ptr = row_ptr;
     a.col = col;
     a.col16 = (col == A->col && row_ptr == A->krp) ? A->col16 : (col == A->col_t ? A->col16_t : nullptr);
+    if (band > 0) a.col16 = A->colb16;   // the banded SpMV's window-relative offsets, or none
     a.vals = vals;
     a.b = b;
     a.x = x;
@@ -1004,6 +1007,14 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
         e = launch_col16(static_cast<const int32_t*>(A->krp), d_col_idx, A->col16, n_rows, s);
         if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "column offsets: %s", hipGetErrorString(e)));
     }
+    if (c16 && A->band > 0 && A->band <= kCol16MaxSpan) {
+        if ((st = dev_alloc(reinterpret_cast<void**>(&A->colb16), sizeof(int16_t) * static_cast<size_t>(nnz))) !=
+            SLA_OK)
+            return bail(st);
+        e = launch_colb16(static_cast<const int32_t*>(A->krp), d_col_idx, A->colb16, n_rows,
+                          static_cast<int32_t>(A->band), s);
+        if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "band column offsets: %s", hipGetErrorString(e)));
+    }
     if (A->rp_owned || A->col16) {   // the handle may next be used on another stream
         e = hipStreamSynchronize(s);
         if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "create: %s", hipGetErrorString(e)));
@@ -1032,6 +1043,7 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->rp_owned) (void)dev_free(A->rp_owned);
     if (A->col16) (void)dev_free(A->col16);
     if (A->col16_t) (void)dev_free(A->col16_t);
+    if (A->colb16) (void)dev_free(A->colb16);
     if (A->flag_host) (void)hipHostFree(A->flag_host);
     if (A->eig_ws) (void)dev_free(A->eig_ws);
     if (A->g_rp) (void)dev_free(A->g_rp);
@@ -1083,6 +1095,7 @@ sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int6
         if (A->rp_owned) tb += 4 * (A->n_rows + 1);
         if (A->col16) tb += 2 * A->nnz;
         if (A->col16_t) tb += 2 * A->nnz;
+        if (A->colb16) tb += 2 * A->nnz;
         *workspace_bytes_out = static_cast<int64_t>(A->ws_bytes + A->vals_t_bytes) + tb;
     }
     return SLA_OK;

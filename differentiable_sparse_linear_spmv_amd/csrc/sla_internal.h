@@ -266,6 +266,10 @@ hipError_t launch_narrow_rp(const int64_t* in, int32_t* out, int64_t n, hipStrea
 // |c - i| <= kCol16MaxSpan (then c - row0 lies in [-kCol16MaxSpan, 32767]).
 constexpr int32_t kCol16MaxSpan = 32767 - (kTile - 1);
 hipError_t launch_col16(const int32_t* rp, const int32_t* col, int16_t* out, int64_t n_rows, hipStream_t s);
+// The same for the banded SpMV (line stride S <= kCol16MaxSpan): offsets from the
+// first row of the window (line i / S, strip (i % S) / kTile) that holds row i.
+hipError_t launch_colb16(const int32_t* rp, const int32_t* col, int16_t* out, int64_t n_rows, int32_t S,
+                         hipStream_t s);
 
 // Transposed pattern: row_ptr_t (same width as rp_bits) [n_cols + 1], col_t [nnz],
 // perm [nnz] (position in A of each entry of A^T).  scratch: see transpose_scratch_bytes.

@@ -936,6 +936,7 @@ struct BandStage {
 struct BandWalk {
     const int32_t* __restrict__ rp;
     const int32_t* __restrict__ col;
+    const int16_t* __restrict__ col16;   // C16: c minus the first row of the entry's window
     const double* __restrict__ vals;
     const double* __restrict__ rin;     // r_k
     const double* __restrict__ pprev;   // p_{k-1}
@@ -958,7 +959,9 @@ struct BandWalk {
 };
 
 // Issue the loads of window l (entries [k0, k1), row bounds, x) and of segment l + 1.
-template <int U>
+// C16: the columns come as 16-bit offsets from the window's first row (sign-extended
+// by the load itself), which is what band_operand needs.
+template <int U, bool C16>
 __device__ __forceinline__ void band_stage(const BandWalk& W, BandStage<U>& B, int32_t l, int32_t k0, int32_t k1)
 {
     const int tid = threadIdx.x;
@@ -972,13 +975,23 @@ __device__ __forceinline__ void band_stage(const BandWalk& W, BandStage<U>& B, i
     const int32_t cnt = k1 - k0;
     const int32_t kb = cnt > 0 ? k0 : min(k0, W.nnz - 1);
     const double* __restrict__ vb = W.vals + kb;
-    const int32_t* __restrict__ cb = W.col + kb;
     const int last = max(cnt - 1, 0);
+    if constexpr (C16) {
+        const int16_t* __restrict__ cb = W.col16 + kb;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int j = min(tid + u * kBlock, last);
-        B.v[u] = ld_stream(vb + j);
-        B.c[u] = ld_stream(cb + j);
+        for (int u = 0; u < U; ++u) {
+            const int j = min(tid + u * kBlock, last);
+            B.v[u] = ld_stream(vb + j);
+            B.c[u] = ld_stream(cb + j);
+        }
+    } else {
+        const int32_t* __restrict__ cb = W.col + kb;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(tid + u * kBlock, last);
+            B.v[u] = ld_stream(vb + j);
+            B.c[u] = ld_stream(cb + j);
+        }
     }
     seg_issue(B.seg, W.rin, W.pprev, W.base(l + 1) - kBandHalo, W.n);
 }
@@ -1038,7 +1051,7 @@ struct BandOut {
 
 // Row sum of this lane's row in window l (entries staged in LDS), and the row's
 // outputs: p_k, q = (A p_k)_i and the deferred update x_k = x_{k-1} + alpha_{k-1} p_{k-1}.
-template <int CAP>
+template <int CAP, bool C16>
 __device__ __forceinline__ BandOut band_window(const BandWalk& W, int32_t l, const double* s_val,
                                                const int32_t* s_col, const BandRows* s_rows, const double* s_p,
                                                const double* s_pp, int sp, int so, int sn, int po, double alpha_prev)
@@ -1055,7 +1068,7 @@ __device__ __forceinline__ BandOut band_window(const BandWalk& W, int32_t l, con
 #pragma unroll
         for (int u = 0; u < RC; ++u) {
             const int j = (j0 + u < re) ? j0 + u : j0;
-            pv[u] = band_operand(s_col[j], base, W.S, s_p, sp, so, sn);
+            pv[u] = band_operand(s_col[j], C16 ? 0 : base, W.S, s_p, sp, so, sn);
         }
 #pragma unroll
         for (int u = 0; u < RC; ++u) {
@@ -1103,7 +1116,7 @@ struct BandLds {
 // being read, so no load waits on another load's result.  Every load is unconditional
 // and every path that continues the loop passes a commit, so the compiler's wait counts
 // are exact and a commit leaves the newer window's loads in flight.
-template <int CAP>
+template <int CAP, bool C16>
 __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_t l1, BandLds<CAP>& L, double beta,
                                            double alpha_prev, double* __restrict__ pcur, double* __restrict__ q,
                                            double* __restrict__ x, double& sig)
@@ -1114,14 +1127,14 @@ __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_
     SegLoad Em, E0;   // segments of lines l0 - 1 and l0
     // entry ranges [k0, k1) of windows l, l + 1, l + 2
     int32_t k0a = W.k0(l0), k1a = W.k1(l0), k0b = 0, k1b = 0, k0c = 0, k1c = 0;
-    band_stage(W, SA, l0, k0a, k1a);
+    band_stage<U, C16>(W, SA, l0, k0a, k1a);
     seg_issue(Em, W.rin, W.pprev, W.base(l0 - 1) - kBandHalo, n);
     seg_issue(E0, W.rin, W.pprev, W.base(l0) - kBandHalo, n);
     if (l0 + 1 < l1) {
         k0b = W.k0(l0 + 1);
         k1b = W.k1(l0 + 1);
     }
-    band_stage(W, SB, l0 + 1, k0b, k1b);
+    band_stage<U, C16>(W, SB, l0 + 1, k0b, k1b);
     if (l0 + 2 < l1) {
         k0c = W.k0(l0 + 2);
         k1c = W.k1(l0 + 2);
@@ -1141,12 +1154,12 @@ __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_
 #define SLA_BAND_WINDOW(na, nb)                                                                            \
     {                                                                                                      \
         int32_t k0d = 0, k1d = 0;                                                                          \
-        band_stage(W, na, l + 2, k0c, k1c); /* past l1: harmless clamped loads, keeps counts exact */     \
+        band_stage<U, C16>(W, na, l + 2, k0c, k1c); /* past l1: harmless clamped loads, exact counts */ \
         if (l + 3 < l1) {                                                                                  \
             k0d = W.k0(l + 3);                                                                             \
             k1d = W.k1(l + 3);                                                                             \
         }                                                                                                  \
-        const BandOut o = band_window<CAP>(W, l, L.val, L.col, &L.rows, L.p, L.pp, sp, so, sn, po, alpha_prev); \
+        const BandOut o = band_window<CAP, C16>(W, l, L.val, L.col, &L.rows, L.p, L.pp, sp, so, sn, po, alpha_prev); \
         __syncthreads(); /* window l's LDS reads are done: rotate the rings */                            \
         const int t3 = sp;                                                                                 \
         sp = so;                                                                                           \
@@ -1181,7 +1194,7 @@ __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_
 // c * strips + j, and workgroup lb takes blocks lb, lb + G, ...: the workgroups in flight
 // cover consecutive blocks, so they stream one front of about G / strips * B lines
 // through memory together.
-template <int CAP>
+template <int CAP, bool C16>
 __global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
 {
     __shared__ BandLds<CAP> L;
@@ -1201,6 +1214,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
     BandWalk W;
     W.rp = static_cast<const int32_t*>(a.row_ptr);
     W.col = a.col;
+    W.col16 = a.col16;
     W.vals = a.vals + static_cast<int64_t>(sys) * a.nnz;
     W.rin = gathered_r(a, first) + off;             // r_k (r_0 = b), or z_k
     W.pprev = ((k & 1) ? a.p0 : a.p1) + off;       // p_{k-1}
@@ -1240,7 +1254,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
         const int32_t l0 = (b / strips) * B;
         W.pos0 = j * kTile;
         W.w = min(kTile, S - W.pos0);
-        band_block<CAP>(W, l0, min(l0 + B, lines), L, beta, alpha_prev, pcur, q, x, sig);
+        band_block<CAP, C16>(W, l0, min(l0 + B, lines), L, beta, alpha_prev, pcur, q, x, sig);
         __syncthreads();   // the next block refills the LDS
     }
     sig = block_sum(sig, s_red);
@@ -3209,6 +3223,20 @@ __global__ __launch_bounds__(kBlock) void k_col16(const int32_t* __restrict__ rp
     }
 }
 
+// out[e] = col[e] - (first row of the banded SpMV's window holding e's row i: line
+// i / S, strip (i % S) / kTile): one thread per row.  The caller has checked that S
+// fits (every offset lies in [-S, S + kTile - 1]).
+__global__ __launch_bounds__(kBlock) void k_colb16(const int32_t* __restrict__ rp, const int32_t* __restrict__ col,
+                                                   int16_t* __restrict__ out, int64_t n, int32_t S)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+        const int32_t ii = static_cast<int32_t>(i);
+        const int32_t wb = (ii / S) * S + ((ii % S) / kTile) * kTile;
+        for (int32_t e = rp[i]; e < rp[i + 1]; ++e) out[e] = static_cast<int16_t>(col[e] - wb);
+    }
+}
+
 inline unsigned grid_for(int64_t n, int64_t per_block, int64_t cap = 65536)
 {
     int64_t g = (n + per_block - 1) / per_block;
@@ -3263,11 +3291,17 @@ CgKernel spmv_kernel(int rp_bits, int cap, bool off32, bool split = false, bool 
 
 inline bool off32_ok(int64_t n) { return n < (int64_t(1) << 29); }
 
-CgKernel band_kernel(int cap)
+// c16: the window-relative 16-bit column offsets (a.col16 of a banded solve)
+CgKernel band_kernel(int cap, bool c16 = false)
 {
-    if (cap <= kCapSmall) return k_cg_spmv_band<kCapSmall>;
-    if (cap <= kCapMid) return k_cg_spmv_band<kCapMid>;
-    return k_cg_spmv_band<kCapLarge>;
+    if (c16) {
+        if (cap <= kCapSmall) return k_cg_spmv_band<kCapSmall, true>;
+        if (cap <= kCapMid) return k_cg_spmv_band<kCapMid, true>;
+        return k_cg_spmv_band<kCapLarge, true>;
+    }
+    if (cap <= kCapSmall) return k_cg_spmv_band<kCapSmall, false>;
+    if (cap <= kCapMid) return k_cg_spmv_band<kCapMid, false>;
+    return k_cg_spmv_band<kCapLarge, false>;
 }
 
 template <typename RP, bool O>
@@ -3358,7 +3392,7 @@ hipError_t launch_cg_init(const CgArgs& a, hipStream_t s)
 hipError_t launch_cg_spmv(const CgArgs& a, int64_t k, int rp_bits, int cap, hipStream_t s)
 {
     if (a.band_stride > 0)
-        SLA_LAUNCH(band_kernel(cap), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
+        SLA_LAUNCH(band_kernel(cap, a.col16 != nullptr), dim3(a.G, a.batch), dim3(kBlock), 0, s, a, k);
     else
         SLA_LAUNCH(spmv_kernel(rp_bits, cap, off32_ok(a.n), a.split != 0, a.col16 != nullptr), dim3(a.G, a.batch),
                    dim3(kBlock), 0, s, a, k);
@@ -3687,6 +3721,13 @@ hipError_t launch_validate(const void* row_ptr, int rp_bits, const int32_t* col,
 hipError_t launch_narrow_rp(const int64_t* in, int32_t* out, int64_t n, hipStream_t s)
 {
     hipLaunchKernelGGL(k_narrow_i32, dim3(grid_for(n, kBlock, 8192)), dim3(kBlock), 0, s, in, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_colb16(const int32_t* rp, const int32_t* col, int16_t* out, int64_t n_rows, int32_t S,
+                         hipStream_t s)
+{
+    hipLaunchKernelGGL(k_colb16, dim3(grid_for(n_rows, kBlock, 8192)), dim3(kBlock), 0, s, rp, col, out, n_rows, S);
     return hipGetLastError();
 }
 

@@ -175,7 +175,8 @@ typedef struct {
  * 16-bit column offsets (c minus the first row of the entry's 256-row tile, 2 nnz
  * bytes of device memory), which the plain CG and BiCGStab SpMV read in place of
  * d_col_idx: 2 bytes less per stored entry in every product, the same sums to the
- * last bit.  The environment variable SLA_COL16=0 (read at each create) turns them
+ * last bit.  A banded pattern also gets offsets from the first row of each row's
+ * window of the line-walking SpMV (another 2 nnz bytes).  The environment variable SLA_COL16=0 (read at each create) turns them
  * off.  When the library builds such a copy (offsets, 32-bit row pointers) the call
  * synchronises `stream` once more before it returns.  The pattern arrays must stay
  * unchanged while the handle lives.
@@ -187,8 +188,8 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
 /* Destroy a handle and free everything the library allocated for it (synchronises the device). */
 sla_status sla_csr_destroy(sla_csr* A);
 
-/* Width in bits of the column indices the plain CG / BiCGStab SpMV reads: 16 when the
- * handle holds 16-bit column offsets (see sla_csr_create), else 32. */
+/* Width in bits of the column indices the plain and banded CG / BiCGStab SpMV read: 16
+ * when the handle holds 16-bit column offsets (see sla_csr_create), else 32. */
 sla_status sla_csr_col_bits(const sla_csr* A, int32_t* col_bits);
 
 /* Shape and workspace queries (host outputs; any pointer may be NULL). */

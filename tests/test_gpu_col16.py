@@ -156,3 +156,31 @@ def test_lanczos_bit_identical(S, monkeypatch):
         res.append((host(ev), host(U), info))
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
     assert res[0][2] == res[1][2]
+
+
+def laplacian_rect(nx, ny):
+    """5-point Laplacian (4, -1) on an nx x ny grid in natural order (line stride nx)."""
+    Tx = sp.diags([-np.ones(nx - 1), 2 * np.ones(nx), -np.ones(nx - 1)], [-1, 0, 1])
+    Ty = sp.diags([-np.ones(ny - 1), 2 * np.ones(ny), -np.ones(ny - 1)], [-1, 0, 1])
+    return csr_of(sp.kron(sp.eye(ny), Tx) + sp.kron(Ty, sp.eye(nx)))
+
+
+@pytest.mark.parametrize("nx,ny,fixed", [(300, 300, False), (SPAN, 4, True)])
+def test_banded_bit_identical(S, monkeypatch, nx, ny, fixed):
+    # the line-walking SpMV reads offsets from each window's first row: strips of 256
+    # and 44 positions (stride 300), and the largest stride that takes offsets (the
+    # last row of a window reaching S + 255 = 32767)
+    monkeypatch.setenv("SLA_BAND_MIN_STRIDE", "272")
+    A = laplacian_rect(nx, ny)
+    b = W.rhs_normal(A.n_rows, 6)
+    opts = S.cg_opts(rtol=0.0, max_iter=40, fixed=True) if fixed else S.cg_opts(rtol=1e-10)
+    ha = handle(S, A, monkeypatch, True)
+    assert S.csr_analysis(ha)["band_stride"] == nx
+    (x, lam, gv), info, _ = same(S, A, b, monkeypatch, opts)
+    if fixed:
+        f = O.cg(A, b, rtol=0.0, max_iter=40, fixed=True)
+        assert info["iterations"] == 40 and rel(x, f["x"]) <= 1e-12
+    else:
+        f = O.cg(A, b, rtol=1e-10)
+        assert abs(info["iterations"] - f["iterations"]) <= math.floor(0.02 * f["iterations"])
+        assert rel(x, f["x"]) <= 1e-9
