@@ -662,6 +662,11 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
     const double* __restrict__ partner = MODE == kSpmvBsV ? a.b + off : opnd;     // rh = b, or the operand
     double* __restrict__ out = (MODE == kSpmvBsT ? a.z : a.q) + off;              // q or v, t (BiCGStab)
 
+    // SparseTensorList: an item that stopped in an earlier launch skips the prefetch of
+    // its first tile (late launches run while most items have stopped).  A stop word
+    // below k is final, so every thread reads the same decision.
+    if constexpr (MODE == kSpmvFused || MODE == kSpmvSplit)
+        if (a.list_wg && a.st[sys].stop_iter < k) return;
     int64_t t = tr.first;
     int64_t k0 = 0, k1 = 0, k0n = 0, k1n = 0;
     // Two stage buffers used alternately (the loop is unrolled by two), so the
@@ -1359,6 +1364,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
     const int64_t trip = kStreamUnroll * tr.step;
     double qa[kStreamUnroll], ra[kStreamUnroll], qb[kStreamUnroll], rb[kStreamUnroll];
     double da[JAC ? kStreamUnroll : 1], db[JAC ? kStreamUnroll : 1];
+    if (a.list_wg && st->stop_iter < k) return;   // an item stopped earlier: no prefetch
     if (tr.first < tr.len) load_trip<NT, JAC>(tr, tr.first, n, q, rin, dg, qa, ra, da);
 
     if (tid == 0) s_stop = st->stop_iter;
