@@ -808,7 +808,7 @@ def main() -> int:
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": w["desc"], "n": n, "nnz": nnz, "batch": B,
-                   "row_ptr": f"int{8 * rp_bytes}", "rtol": w["rtol"],
+                   "row_ptr": f"int{8 * rp_bytes}", "col_idx_read": f"int{8 * col_bytes}", "rtol": w["rtol"],
                    "fixed_iterations": w["fixed"], "parallelism": "none (1 GPU)",
                    "cg_schedule": schedule, "preconditioner": "jacobi" if args.jacobi else "none",
                    "method": method},
