@@ -89,6 +89,16 @@ def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False
                 flops_iteration=(2 * nnz + 10 * n) * batch)
 
 
+def bytes_model_v9(n: int, nnz: int, batch: int, rp_stated: int) -> int:
+    """Bytes of one CG iteration in the reported roofline model: values 8 nnz per
+    system, 4-byte column indices and row pointers of the width the workload states
+    (read once per iteration, shared by the batch), and nine passes over n-vectors
+    per system (read r, p_{k-1}, x and write p_k, q, x around the SpMV; read r, q and
+    write r in the update: the fewest a Hestenes-Stiefel iteration with a stored q
+    needs).  The fraction against it moves only with the iteration's time."""
+    return 8 * nnz * batch + 4 * nnz + rp_stated * (n + 1) + 72 * n * batch
+
+
 def bytes_model_bicgstab(n: int, nnz: int, batch: int, rp_bytes: int, col_bytes: int = 4) -> dict:
     """Algorithmic HBM bytes of the BiCGStab kernels, per launch (all systems).
 
@@ -373,35 +383,71 @@ def loss_grad(w, x):
 
 
 # ------------------------------------------------------------------------------ CPU baseline
-def cpu_baseline(w, iters: int) -> dict:
-    """The oracle as it stands (single-threaded C), on a bounded sample of the workload."""
-    import numpy as np
+def host_cpu() -> dict:
+    """The host the CPU baseline runs on: CPU model, cores this process may use, and
+    the OpenMP threads the timing mode takes (OMP_NUM_THREADS caps them when set)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(nproc, int(omp)) if omp.isdigit() and int(omp) > 0 else nproc
+    return dict(model=model, nproc=nproc, threads=threads)
+
+
+def cpu_baseline(w, iters: int, single_iters: int = 100) -> dict:
+    """The oracle timed on this host's cores, on a bounded sample of the workload.
+
+    Timing mode (the value): the oracle's CG steps with its SpMV rows, vector updates
+    and inner products split over OpenMP threads (orc_cg_timing), `iters` fixed
+    iterations forward and `iters` in the adjoint.  Parity mode beside it: the
+    single-threaded oracle itself (orc_cg + orc_solve_backward), `single_iters` + `single_iters`.
+    BiCGStab workloads have the parity mode only."""
     import oracle as O
     import workloads as W
 
+    host = host_cpu()
     if w["host"] is None:      # the 169M case: sample a 2048 x 2048 grid of the same stencil
         A = W.poisson5(2048)
         b = W.rhs_normal(A.n_rows, 0)
         vals = None
-        sample = (f"oracle CG on the same 5-point stencil at 2048x2048 (169M rows do not fit a "
-                  f"bounded CPU sample), {iters} fixed iterations + {iters} adjoint")
+        what = "the same 5-point stencil at 2048x2048 (169M rows do not fit a bounded CPU sample)"
     else:
         A = w["host"]["A"]
         b = w["host"]["b"].reshape(A.batch, A.n_rows)[0]
         vals = A.vals.reshape(A.batch, A.nnz)[0]
-        sample = (f"oracle CG on system 0 of this workload, {iters} fixed iterations + "
-                  f"{iters} adjoint iterations (single thread)")
+        what = "system 0 of this workload"
     method = w.get("method", "cg")
-    if method == "bicgstab":
-        sample = sample.replace("oracle CG", "oracle BiCGStab")
-    t0 = time.perf_counter()
-    f = O.cg(A, b, rtol=0.0, max_iter=iters, fixed=True, vals=vals, method=method)
-    O.solve_backward(A, f["x"], f["x"], symmetric=w.get("symmetric", True), rtol=0.0, max_iter=iters,
-                     fixed=True, vals=vals, method=method)
-    dt = time.perf_counter() - t0
     unit = "BiCGStab iters/s" if method == "bicgstab" else "CG iters/s"
-    return dict(value=round(2 * iters / dt, 3), unit=unit, cores=1, kind="oracle",
-                sample=sample, seconds=round(dt, 2))
+    name = "BiCGStab" if method == "bicgstab" else "CG"
+
+    si = single_iters if method == "cg" else iters
+    t0 = time.perf_counter()
+    f = O.cg(A, b, rtol=0.0, max_iter=si, fixed=True, vals=vals, method=method)
+    O.solve_backward(A, f["x"], f["x"], symmetric=w.get("symmetric", True), rtol=0.0, max_iter=si,
+                     fixed=True, vals=vals, method=method)
+    dt1 = time.perf_counter() - t0
+    single = dict(value=round(2 * si / dt1, 3), unit=unit, cores=1, kind="oracle",
+                  sample=f"parity mode (sequential oracle) on {what}, {si} fixed iterations + {si} adjoint",
+                  seconds=round(dt1, 2))
+    if method != "cg" or not w.get("symmetric", True):
+        single.update(nproc=host["nproc"], host_model=host["model"])
+        return single
+    t0 = time.perf_counter()
+    r = O.cg_timing(A, b, iters, host["threads"], adjoint=True, vals=vals)
+    dt = time.perf_counter() - t0
+    return dict(value=round(2 * iters / dt, 3), unit=unit, cores=r["threads"], kind="oracle",
+                mode="timing mode: the oracle's CG steps with OpenMP over rows (and over the inner "
+                     "products' slices)",
+                sample=f"oracle {name} on {what}, {iters} fixed iterations + {iters} adjoint iterations "
+                       f"on {r['threads']} threads", seconds=round(dt, 2),
+                nproc=host["nproc"], host_model=host["model"], single_thread=single)
 
 
 # ------------------------------------------------------------------------------ traffic
@@ -418,6 +464,12 @@ def read_traffic(workload: str, key: str = "bytes_per_launch"):
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
+    if key == "bytes_per_iteration" and key not in t:
+        parts = [t.get("bytes_per_launch"), t.get("update_bytes_per_launch")]
+        if None in parts:
+            return None, "no counter summary of every kernel of the iteration"
+        return sum(parts) + (t.get("pupd_bytes_per_launch") or 0.0), \
+            "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated (SpMV + update + p update launches)"
     return t.get(key), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
 
 
@@ -567,6 +619,13 @@ def main() -> int:
     ap.add_argument("--fixed-iters", type=int, default=0,
                     help="profiling runs: exactly this many CG iterations per solve")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--no-big", action="store_true",
+                    help="skip the 169M-DOF leg of the default poisson1024 line")
+    ap.add_argument("--big-steps", type=int, default=3,
+                    help="timed steps of the 169M-DOF leg (500 + 500 fixed iterations each)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-bandwidth ceiling")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="only run the streaming probes (every variant) and print the best of each mix")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -662,44 +721,43 @@ def main() -> int:
         if rank == 0:
             print(json.dumps(out), flush=True)
         return 0
-    w = make_workload(args.workload, dev)
-    n, nnz, B = w["n"], w["nnz"], w["batch"]
-    rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
-    method = w["method"]
-    if method == "eigsh":
-        r = run_eigsh(args, w, S, torch)
-        if args.calibrate_copy:
-            calibrate_copy(torch, dev)
-        traffic, traffic_src = read_traffic(args.workload, "bytes_per_run")
-        cpu = cpu_baseline_eigsh(w, 40) if (rank == 0 and not args.no_cpu_baseline) else None
-        out = {
-            "metric": METRIC_EIGSH, "value": round(r["value"], 2), "unit": "Lanczos steps/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * r["wall"] / args.steps, 4),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
-            "data": "synthetic",
-            "config": {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "k": w["k"], "which": w["which"],
-                       "tol": w["tol"], "max_dim": w["max_dim"], "max_iter": w["max_iter"],
-                       "parallelism": "none (1 GPU)", "method": "eigsh"},
-            "lanczos_steps": r["info"]["iterations"], "restarts": r["info"]["restarts"],
-            "state": r["info"]["state_name"],
-            "kernels": {kk: {"launches": v["launches"],
-                             "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
-                        for kk, v in r["tq"].items() if v["launches"]},
-            "bytes_model": r["bm"],
-            "lz_spmv_gbps": round(r["spmv_gbps"], 1),
-            "roofline": {"bound": "hbm",
-                         "kernel": "Lanczos reorthogonalization (k_lz_three, k_lz_dots, k_lz_reduce, k_lz_axpy, "
-                                   "k_lz_next), all launches of one run",
-                         "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                         "traffic_source": traffic_src, "traffic_unit": "bytes per run (all launches)",
-                         "bytes_per_launch": None, "bytes_per_run": r["bm"]["lz_orth_total"],
-                         "run_ms": round(r["orth_ms"], 3)},
-            "cpu_baseline": cpu,
-        }
-        if rank == 0:
-            print(json.dumps(out), flush=True)
+    if args.ceiling_sweep:
+        print(json.dumps({"ceiling_sweep": measure_ceiling(S, torch, dev, sweep=True)}), flush=True)
         return 0
+    w = make_workload(args.workload, dev)
+    r = measure_cg(args, w, S, torch, args.steps, args.warmup)
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev)
+    ceiling = measure_ceiling(S, torch, dev) if not args.no_ceiling else None
+    big = None
+    if args.workload == "poisson1024" and not args.no_big and args.fixed_iters == 0 and not args.jacobi:
+        # the metric's second configuration, 169M DOF (500 + 500 fixed iterations), timed
+        # beside the 1M headline in the same run
+        del w
+        torch.cuda.empty_cache()
+        wb = make_workload("poisson13000", dev)
+        rb = measure_cg(args, wb, S, torch, args.big_steps, 1)
+        big = cg_summary(rb, ceiling, args)
+        del wb, rb
+        torch.cuda.empty_cache()
+    cpu = None
+    if rank == 0 and not args.no_cpu_baseline:
+        # a BiCGStab iteration is two products: half as many keep the sample's CPU time
+        cpu = cpu_baseline(r["w"], max(1, args.cpu_iters // 2) if r["bicg"] else args.cpu_iters)
+    out = cg_line(r, args, ceiling, cpu)
+    if big is not None:
+        out["poisson13000"] = big
+    if rank == 0:
+        print(json.dumps(out), flush=True)
+    return 0
+
+
+# ------------------------------------------------------------------------------ CG measurement
+def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
+    """Time `steps` solve + adjoint steps of workload w (after `warmup` untimed ones),
+    then time every kernel of one more step with HIP events on the library's stream."""
+    n, nnz, B = w["n"], w["nnz"], w["batch"]
+    method = w["method"]
     bicg = method == "bicgstab"
     h = S.csr_create(w["rp"], w["col"], symmetric=w["symmetric"])
     an = S.csr_analysis(h)
@@ -718,6 +776,8 @@ def main() -> int:
     # the plain and banded SpMV (CG and BiCGStab) read 16-bit column offsets where the
     # handle has them; the grouped kernels read the 32-bit columns
     col_bytes = 4 if spmv_kernel == "k_gcg_spmv" else an["col_bits"] // 8
+    rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
+    rp_stated = w["rp"].element_size()        # the row-pointer width the workload hands in
     if args.fixed_iters > 0:
         w["max_iter"], w["fixed"], w["rtol"] = args.fixed_iters, True, 0.0
     opts = S.cg_opts(rtol=w["rtol"], max_iter=w["max_iter"], fixed=w["fixed"], jacobi=args.jacobi,
@@ -730,7 +790,7 @@ def main() -> int:
         gb, gv, binfo = S.solve_backward(h, vals, x, g, opts)
         return x, gb, gv, info, binfo
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -739,25 +799,21 @@ def main() -> int:
     t0 = time.perf_counter()
     e0.record(stream)
     infos = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         _, _, _, info, binfo = step()
         infos.append((info, binfo))
     e1.record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
+    wall = time.perf_counter() - t0
     fwd_it = [sum(s["iterations"] for s in S.read_info(i)) for i, _ in infos]
     bwd_it = [sum(s["iterations"] for s in S.read_info(bi)) for _, bi in infos]
     max_fwd = max(s["iterations"] for s in S.read_info(infos[-1][0]))
     max_bwd = max(s["iterations"] for s in S.read_info(infos[-1][1]))
     total_it = sum(fwd_it) + sum(bwd_it)
-    # iterations of the batch advance together: count per-system iterations for batch > 1
-    value = total_it / wall
-    ms_step = 1e3 * wall / args.steps
 
-    # Dominant-kernel timing: the same solve + backward once more with per-launch HIP
-    # events on the library's stream, fixed at the measured iteration counts so every
-    # timed launch is a working one.
+    # Kernel timing: the same solve + backward once more with per-launch HIP events on
+    # the library's stream, fixed at the measured iteration counts so every timed
+    # launch is a working one.
     S.timing.reset()
     S.timing.enable(True)
     fo = S.cg_opts(rtol=0.0, max_iter=max_fwd, fixed=True, jacobi=args.jacobi, method=method)
@@ -768,69 +824,174 @@ def main() -> int:
     S.timing.enable(False)
     tq = S.timing.query()
     torch.cuda.synchronize()
+    del x, h
+    return dict(w=w, an=an, bicg=bicg, spmv_kernel=spmv_kernel, schedule=schedule, col_bytes=col_bytes,
+                rp_bytes=rp_bytes, rp_stated=rp_stated, steps=steps, warmup=warmup, wall=wall,
+                event_ms=e0.elapsed_time(e1) / steps, fwd_it=fwd_it, bwd_it=bwd_it, total_it=total_it, tq=tq)
+
+
+def iteration_roofline(r) -> dict:
+    """Roofline of one CG iteration (every kernel of it: SpMV, update, and the p update
+    of the split schedule), HIP-event timed.
+
+    frac: the bytes of the iteration model with V = 9 vector passes, 4-byte column
+    indices and the workload's stated row-pointer width (B 8 nnz + 4 nnz + rp (n + 1)
+    + 72 n B), over the iteration's time, over 8 TB/s.  frac_bytes_moved: the bytes the
+    kernels actually read and write (16-bit column offsets where the handle has them,
+    the 32-bit row-pointer copy, the split schedule's extra pass), same time.
+    frac_spmv_only: the SpMV's own bytes over its own time."""
+    w, tq = r["w"], r["tq"]
+    n, nnz, B = w["n"], w["nnz"], w["batch"]
 
     def avg_ms(key):
         return tq[key]["total_ms"] / max(tq[key]["launches"], 1)
 
-    if bicg:
-        bm = bytes_model_bicgstab(n, nnz, B, rp_bytes, col_bytes)
+    if r["bicg"]:
+        bm = bytes_model_bicgstab(n, nnz, B, r["rp_bytes"], r["col_bytes"])
         spmv_ms, spmv_bytes = avg_ms("bs_spmv"), bm["bs_spmv"]
-        # per iteration: two products and three streaming kernels (init excluded)
         iter_ms = 2 * spmv_ms + 3 * avg_ms("bs_vec")
+        v9 = bm["iteration"]   # BiCGStab: its own model (two products, 14 vector passes)
     else:
-        bm = bytes_model(n, nnz, B, rp_bytes, split=an["split"], col_bytes=col_bytes)
+        bm = bytes_model(n, nnz, B, r["rp_bytes"], split=r["an"]["split"], col_bytes=r["col_bytes"])
         spmv_ms, spmv_bytes = avg_ms("cg_spmv"), bm["cg_spmv"]
-        iter_ms = spmv_ms + avg_ms("cg_update") + (avg_ms("cg_pupd") if an["split"] else 0.0)
-    achieved = spmv_bytes / (spmv_ms * 1e-3) / 1e9
-    traffic, traffic_src = read_traffic(args.workload)
-    iter_gbps = bm["iteration"] / (iter_ms * 1e-3) / 1e9
-    wall_gbps = bm["iteration"] * (total_it / B) / wall / 1e9
+        iter_ms = spmv_ms + avg_ms("cg_update") + (avg_ms("cg_pupd") if r["an"]["split"] else 0.0)
+        v9 = bytes_model_v9(n, nnz, B, r["rp_stated"])
+    gbps = lambda by, ms: by / (ms * 1e-3) / 1e9
+    achieved = gbps(v9, iter_ms)
+    return dict(bm=bm, v9=v9, iter_ms=iter_ms, spmv_ms=spmv_ms, spmv_bytes=spmv_bytes, achieved=achieved,
+                moved_gbps=gbps(bm["iteration"], iter_ms), spmv_gbps=gbps(spmv_bytes, spmv_ms))
 
-    if args.calibrate_copy:
-        calibrate_copy(torch, dev)
 
-    cpu = None
-    if rank == 0 and not args.no_cpu_baseline:
-        # a BiCGStab iteration is two products: half as many keep the sample's CPU time
-        cpu = cpu_baseline(w, max(1, args.cpu_iters // 2) if bicg else args.cpu_iters)
+def cg_summary(r, ceiling, args) -> dict:
+    """The measured numbers of one CG workload (headline fields and its roofline)."""
+    w = r["w"]
+    B = w["batch"]
+    rf = iteration_roofline(r)
+    traffic, traffic_src = read_traffic(w["name"], "bytes_per_iteration")
+    ms_step = 1e3 * r["wall"] / r["steps"]
+    resident = (12 * w["nnz"] + 52 * w["n"]) * B < 200e6   # fits the 256 MB Infinity Cache
+    roof = {"bound": "hbm",
+            "kernel": ("one BiCGStab iteration (two products, three streaming kernels)" if r["bicg"] else
+                       "one CG iteration: " + r["spmv_kernel"] + " + k_cg_update"
+                       + (" + k_cg_pupd" if r["an"]["split"] else "")),
+            "achieved": round(rf["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(rf["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "traffic_source": traffic_src, "traffic_unit": "HBM bytes per iteration (all kernels of it)",
+            "bytes_model": ("BiCGStab: two products + 14 vector passes" if r["bicg"] else
+                            "V=9: 8 nnz B + 4 nnz + rp (n+1) + 72 n B, 4-byte columns, "
+                            f"rp = {r['rp_stated']} B as stated"),
+            "bytes_per_iteration": rf["v9"], "iteration_us": round(1e3 * rf["iter_ms"], 3),
+            "frac_bytes_moved": round(rf["moved_gbps"] / HBM_PEAK_GBPS, 4),
+            "bytes_moved_per_iteration": rf["bm"]["iteration"],
+            "frac_spmv_only": round(rf["spmv_gbps"] / HBM_PEAK_GBPS, 4),
+            "spmv_us": round(1e3 * rf["spmv_ms"], 3), "spmv_bytes": rf["spmv_bytes"],
+            "cache_resident": bool(resident)}
+    if ceiling:
+        roof["ceiling_gbps"] = {"spmv_mix": ceiling["spmv_mix"]["gbps"], "triad": ceiling["triad"]["gbps"]}
+        # the iteration's bytes moved against the same-run streaming rate of its own mix:
+        # the SpMV's bytes at the SpMV-mix ceiling plus the update's at the triad ceiling
+        if not r["bicg"] and not r["an"]["split"]:
+            t_ceil = (rf["bm"]["cg_spmv"] / ceiling["spmv_mix"]["gbps"] +
+                      rf["bm"]["cg_update"] / ceiling["triad"]["gbps"]) / 1e9
+            roof["frac_of_ceiling"] = round(t_ceil / (rf["iter_ms"] * 1e-3), 4)
+    return {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "batch": B,
+            "row_ptr": f"int{8 * r['rp_stated']} (kernels read int{8 * r['rp_bytes']})",
+            "col_idx_read": f"int{8 * r['col_bytes']}", "rtol": w["rtol"], "fixed_iterations": w["fixed"],
+            "cg_schedule": r["schedule"], "steps": r["steps"], "warmup": r["warmup"],
+            "ms_per_step": round(ms_step, 4), "solve_adjoint_ms": round(ms_step, 4),
+            "iterations_per_step": {"forward": r["fwd_it"][-1], "adjoint": r["bwd_it"][-1]},
+            "iters_per_s": round(r["total_it"] / r["wall"], 2),
+            "hbm_gbps_per_iteration": round(rf["achieved"], 1),
+            "hbm_gbps_moved_per_iteration": round(rf["moved_gbps"], 1),
+            "event_ms_per_step": round(r["event_ms"], 4),
+            "kernels": {k: {"launches": v["launches"],
+                            "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
+                        for k, v in r["tq"].items() if v["launches"]},
+            "bytes_model": rf["bm"], "roofline": roof}
 
+
+def cg_line(r, args, ceiling, cpu) -> dict:
+    w = r["w"]
+    sm = cg_summary(r, ceiling, args)
     out = {
-        "metric": METRIC_BICGSTAB if bicg else METRIC,
-        "value": round(value, 2),
-        "unit": "BiCGStab iters/s" if bicg else "CG iters/s",
+        "metric": METRIC_BICGSTAB if r["bicg"] else METRIC,
+        "value": sm["iters_per_s"],
+        "unit": "BiCGStab iters/s" if r["bicg"] else "CG iters/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "steps": r["steps"],
+        "warmup": r["warmup"],
+        "ms_per_step": sm["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": w["desc"], "n": n, "nnz": nnz, "batch": B,
-                   "row_ptr": f"int{8 * rp_bytes}", "col_idx_read": f"int{8 * col_bytes}", "rtol": w["rtol"],
+        "config": {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "batch": w["batch"],
+                   "row_ptr": sm["row_ptr"], "col_idx_read": sm["col_idx_read"], "rtol": w["rtol"],
                    "fixed_iterations": w["fixed"], "parallelism": "none (1 GPU)",
-                   "cg_schedule": schedule, "preconditioner": "jacobi" if args.jacobi else "none",
-                   "method": method},
-        "iterations_per_step": {"forward": fwd_it[-1], "adjoint": bwd_it[-1]},
-        "solve_adjoint_ms": round(ms_step, 4),
-        "hbm_gbps_per_iteration": round(iter_gbps, 1),
-        "hbm_gbps_wall": round(wall_gbps, 1),
-        "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),
-        "kernels": {k: {"launches": v["launches"],
-                        "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
-                    for k, v in tq.items() if v["launches"]},
-        "bytes_model": bm,
-        "roofline": {"bound": "hbm", "kernel": spmv_kernel, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "traffic_source": traffic_src,
-                     "bytes_per_launch": spmv_bytes, "avg_launch_us": round(1e3 * spmv_ms, 3)},
-        "cpu_baseline": cpu,
+                   "cg_schedule": r["schedule"], "preconditioner": "jacobi" if args.jacobi else "none",
+                   "method": w["method"]},
     }
-    if rank == 0:
-        print(json.dumps(out), flush=True)
-    return 0
+    for k in ("iterations_per_step", "solve_adjoint_ms", "hbm_gbps_per_iteration", "hbm_gbps_moved_per_iteration",
+              "event_ms_per_step", "kernels", "bytes_model", "roofline"):
+        out[k] = sm[k]
+    if ceiling:
+        out["ceiling"] = ceiling
+    out["cpu_baseline"] = cpu
+    return out
 
+
+# ------------------------------------------------------------------------------ ceiling
+# Streaming probes (sla_probe_stream): (reads, writes) per element of each mix, and the
+# variants (16-byte accesses in flight per thread and array, non-temporal hint,
+# workgroups per CU) whose best rate is reported.
+# Every variant is timed (about 0.2 s for all mixes): the reported rate of a mix is its
+# best over all 24.
+CEILING_MIXES = {"read": (1, 0), "write": (0, 1), "copy": (1, 1), "triad": (2, 1), "spmv_mix": (10, 3)}
+CEILING_SWEEP = [(u, nt, bpc) for u in (1, 2, 4) for nt in (1, 0) for bpc in (1, 2, 4, 8)]
+
+
+def measure_ceiling(S, torch, dev, sweep: bool = True, elems: int = 1 << 26) -> dict:
+    """Bandwidth of plain coalesced streams on this GPU, in this run: for each mix the
+    best rate (bytes read + written / event-timed launch) over the variants.  Arrays of
+    `elems` doubles (512 MiB each by default: every mix streams far past the 256 MB
+    Infinity Cache); the SpMV mix uses arrays a quarter as long (13 of them)."""
+    import ctypes as C
+    from differentiable_sparse_linear_spmv_amd import _lib as L
+    lib = L.load()
+    bufs = [torch.empty(elems, dtype=torch.float64, device=dev) for _ in range(13)]
+    for bb in bufs:
+        bb.fill_(1.0)
+    part = torch.zeros(8 * 1024, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, (nr, nw) in CEILING_MIXES.items():
+        n = elems // 4 if nr + nw > 4 else elems
+        ins = (C.c_void_p * max(nr, 1))(*[bufs[i].data_ptr() for i in range(nr)])
+        outs = (C.c_void_p * max(nw, 1))(*[bufs[nr + i].data_ptr() for i in range(nw)])
+        best = None
+        for (u, nt, bpc) in (CEILING_SWEEP if sweep else CEILING_SWEEP[:1]):
+            def launch():
+                L.check(lib.sla_probe_stream(nr, nw, ins, outs, n, u, nt, bpc, part.data_ptr(),
+                                             stream.cuda_stream))
+            launch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record(stream)
+            for _ in range(reps):
+                launch()
+            e1.record(stream)
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            gbps = 8.0 * n * (nr + nw) / (ms * 1e-3) / 1e9
+            if best is None or gbps > best["gbps"]:
+                best = {"gbps": round(gbps, 1), "unroll": u, "nontemporal": nt, "blocks_per_cu": bpc,
+                        "us": round(1e3 * ms, 2), "bytes": 8 * n * (nr + nw)}
+        out[name] = best
+    del bufs, part
+    torch.cuda.empty_cache()
+    out["frac_of_peak"] = {k: round(v["gbps"] / HBM_PEAK_GBPS, 4) for k, v in out.items()}
+    return out
 
 if __name__ == "__main__":
     sys.exit(main())

@@ -37,7 +37,7 @@ EXPORTS = [
     "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_col_bits", "sla_list_solve",
     "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable",
     "sla_timing_reset", "sla_timing_collect", "sla_timing_query", "sla_timing_query_bytes", "sla_status_string",
-    "sla_last_error", "sla_version",
+    "sla_last_error", "sla_version", "sla_probe_stream",
 ]
 
 
@@ -146,6 +146,8 @@ def load():
     L.sla_timing_query.restype = st
     L.sla_timing_query_bytes.argtypes = [i32, C.POINTER(C.c_double)]
     L.sla_timing_query_bytes.restype = st
+    L.sla_probe_stream.argtypes = [i32, i32, P, P, i64, i32, i32, i32, P, P]
+    L.sla_probe_stream.restype = st
     L.sla_status_string.argtypes = [st]
     L.sla_status_string.restype = C.c_char_p
     L.sla_last_error.argtypes = []

@@ -45,7 +45,9 @@ struct sla_csr {
     // staged CG / BiCGStab SpMV reads instead of the 32-bit columns: 2 bytes per entry
     // less in every product.  Built at create when every |c - i| <= kCol16MaxSpan
     // (SLA_COL16=0 turns them off); null otherwise.
+    // A banded handle builds them on first use only (its CG SpMV reads colb16 instead).
     int16_t* col16 = nullptr;
+    bool c16_ok = false;          // every |c - i| <= kCol16MaxSpan: col16 may be built
     int16_t* col16_t = nullptr;   // the same for the transposed pattern
     int16_t* colb16 = nullptr;    // banded pattern: offsets from the first row of the
                                   // line-walking SpMV's window of each row
@@ -394,54 +396,87 @@ sla_status check_opts(const sla_cg_opts* o)
     return SLA_OK;
 }
 
+// The transposed pattern, built once per handle.  Everything is built into local
+// blocks first and handed to the handle only when all of it succeeded: a failed
+// allocation or launch frees what this call allocated, so a later call starts clean.
 sla_status ensure_transpose(sla_csr* A, hipStream_t s)
 {
     if (A->has_t) return SLA_OK;
+    void* rpt = nullptr;
+    int32_t* colt = nullptr;
+    int64_t* permt = nullptr;
+    int16_t* c16t = nullptr;
     void* scratch = nullptr;
+    auto release = [&](sla_status st) {
+        (void)hipStreamSynchronize(s);   // no launch of this call may still use the blocks
+        for (void* q : {rpt, static_cast<void*>(colt), static_cast<void*>(permt), static_cast<void*>(c16t), scratch})
+            if (q) (void)dev_free(q);
+        return st;
+    };
     sla_status st;
     const size_t rpt_bytes = static_cast<size_t>(A->n_cols + 1) * (A->krp_bits == 64 ? 8 : 4);
-    if ((st = dev_alloc(&A->row_ptr_t, std::max<size_t>(rpt_bytes, 8))) != SLA_OK) return st;
-    if ((st = dev_alloc(reinterpret_cast<void**>(&A->col_t), std::max<size_t>(4 * A->nnz, 4))) != SLA_OK) return st;
-    if ((st = dev_alloc(reinterpret_cast<void**>(&A->perm_t), std::max<size_t>(8 * A->nnz, 8))) != SLA_OK) return st;
-    if ((st = dev_alloc(&scratch, transpose_scratch_bytes(A->n_rows, A->n_cols, A->nnz))) != SLA_OK) return st;
+    if ((st = dev_alloc(&rpt, std::max<size_t>(rpt_bytes, 8))) != SLA_OK) return release(st);
+    if ((st = dev_alloc(reinterpret_cast<void**>(&colt), std::max<size_t>(4 * A->nnz, 4))) != SLA_OK)
+        return release(st);
+    if ((st = dev_alloc(reinterpret_cast<void**>(&permt), std::max<size_t>(8 * A->nnz, 8))) != SLA_OK)
+        return release(st);
+    if ((st = dev_alloc(&scratch, transpose_scratch_bytes(A->n_rows, A->n_cols, A->nnz))) != SLA_OK)
+        return release(st);
     hipError_t e = timed(
         SLA_K_TRANSPOSE, s,
         [&] {
-            return launch_transpose(A->krp, A->krp_bits, A->col, A->n_rows, A->n_cols, A->nnz, A->row_ptr_t,
-                                    A->col_t, A->perm_t, scratch, s);
+            return launch_transpose(A->krp, A->krp_bits, A->col, A->n_rows, A->n_cols, A->nnz, rpt, colt, permt,
+                                    scratch, s);
         },
         false);
-    if (e != hipSuccess) {
-        (void)dev_free(scratch);
-        return fail(SLA_ERR_HIP, "transpose: %s", hipGetErrorString(e));
-    }
+    if (e != hipSuccess) return release(fail(SLA_ERR_HIP, "transpose: %s", hipGetErrorString(e)));
     // analysis of the transposed pattern (also re-checks it)
     int32_t* d_chk = static_cast<int32_t*>(scratch);   // reuse: the scan data is no longer needed
-    HIP_TRY(hipStreamSynchronize(s));
     int32_t h[kChkCount] = {0, 0, 0, INT32_MAX, 0};
-    HIP_TRY(hipMemcpyAsync(d_chk, h, sizeof(h), hipMemcpyHostToDevice, s));
-    HIP_TRY(hipStreamSynchronize(s));
-    e = launch_validate(A->row_ptr_t, A->krp_bits, A->col_t, A->n_cols, A->n_rows, A->nnz, d_chk, s);
-    if (e != hipSuccess) {
-        (void)dev_free(scratch);
-        return fail(SLA_ERR_HIP, "transpose analysis: %s", hipGetErrorString(e));
-    }
-    HIP_TRY(hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
-    (void)dev_free(scratch);
+    e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d_chk, h, sizeof(h), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = launch_validate(rpt, A->krp_bits, colt, A->n_cols, A->n_rows, A->nnz, d_chk, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h, d_chk, sizeof(h), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return release(fail(SLA_ERR_HIP, "transpose analysis: %s", hipGetErrorString(e)));
     if (h[kChkErr] != 0)
-        return fail(SLA_ERR_HIP, "internal error: transposed pattern failed validation (%d)", h[kChkErr]);
-    A->cap_t = choose_cap(h[kChkTileMax]);
-    // the transpose has the same spans |c - i|, so it gets offsets when A has them
-    if (A->col16 && A->krp_bits == 32) {
-        if ((st = dev_alloc(reinterpret_cast<void**>(&A->col16_t), sizeof(int16_t) * static_cast<size_t>(A->nnz))) !=
+        return release(fail(SLA_ERR_HIP, "internal error: transposed pattern failed validation (%d)", h[kChkErr]));
+    // the transpose has the same spans |c - i|, so it gets offsets when A may have them
+    if (A->c16_ok && A->krp_bits == 32) {
+        if ((st = dev_alloc(reinterpret_cast<void**>(&c16t), sizeof(int16_t) * static_cast<size_t>(A->nnz))) !=
             SLA_OK)
-            return st;
-        e = launch_col16(static_cast<const int32_t*>(A->row_ptr_t), A->col_t, A->col16_t, A->n_cols, s);
-        if (e != hipSuccess) return fail(SLA_ERR_HIP, "transposed column offsets: %s", hipGetErrorString(e));
-        HIP_TRY(hipStreamSynchronize(s));
+            return release(st);
+        e = launch_col16(static_cast<const int32_t*>(rpt), colt, c16t, A->n_cols, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return release(fail(SLA_ERR_HIP, "transposed column offsets: %s", hipGetErrorString(e)));
     }
+    (void)dev_free(scratch);
+    A->row_ptr_t = rpt;
+    A->col_t = colt;
+    A->perm_t = permt;
+    A->col16_t = c16t;
+    A->cap_t = choose_cap(h[kChkTileMax]);
     A->has_t = true;
+    return SLA_OK;
+}
+
+// The 16-bit tile offsets of A's own pattern, built on first use when the handle did
+// not build them at create (a banded handle, whose CG SpMV reads colb16).
+sla_status ensure_col16(sla_csr* A, hipStream_t s)
+{
+    if (!A->c16_ok || A->col16) return SLA_OK;
+    int16_t* c16 = nullptr;
+    sla_status st = dev_alloc(reinterpret_cast<void**>(&c16), sizeof(int16_t) * static_cast<size_t>(A->nnz));
+    if (st != SLA_OK) return st;
+    hipError_t e = launch_col16(static_cast<const int32_t*>(A->krp), A->col, c16, A->n_rows, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        (void)hipStreamSynchronize(s);
+        (void)dev_free(c16);
+        return fail(SLA_ERR_HIP, "column offsets: %s", hipGetErrorString(e));
+    }
+    A->col16 = c16;
     return SLA_OK;
 }
 
@@ -713,6 +748,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi ? kMethodJacobi : kMethodCG,
                                      list ? list->items : -1);
     if (st != SLA_OK) return st;
+    if (band == 0 && col == A->col && (st = ensure_col16(A, s)) != SLA_OK) return st;
 
     CgArgs a{};
     a.row_ptr = row_ptr;
@@ -806,6 +842,7 @@ sla_status run_bicgstab(sla_csr* A, const void* row_ptr, const int32_t* col, int
     Workspace w;
     sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, kMethodBiCGStab);
     if (st != SLA_OK) return st;
+    if (col == A->col && (st = ensure_col16(A, s)) != SLA_OK) return st;
 
     CgArgs a{};
     a.row_ptr = row_ptr;
@@ -1002,14 +1039,16 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
     bool c16 = A->krp_bits == 32 && n_rows == n_cols && n_rows < (int64_t(1) << 29) && nnz > 0 &&
                std::max<int32_t>(h[kChkFarMax], kBandHalo) <= kCol16MaxSpan;
     if (const char* env = std::getenv("SLA_COL16")) c16 = c16 && std::strcmp(env, "0") != 0;
-    if (c16) {
+    A->c16_ok = c16;
+    const bool cb16 = c16 && A->band > 0 && A->band <= kCol16MaxSpan;
+    if (c16 && !cb16) {   // a banded handle builds the tile offsets on first use only
         if ((st = dev_alloc(reinterpret_cast<void**>(&A->col16), sizeof(int16_t) * static_cast<size_t>(nnz))) !=
             SLA_OK)
             return bail(st);
         e = launch_col16(static_cast<const int32_t*>(A->krp), d_col_idx, A->col16, n_rows, s);
         if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "column offsets: %s", hipGetErrorString(e)));
     }
-    if (c16 && A->band > 0 && A->band <= kCol16MaxSpan) {
+    if (cb16) {
         if ((st = dev_alloc(reinterpret_cast<void**>(&A->colb16), sizeof(int16_t) * static_cast<size_t>(nnz))) !=
             SLA_OK)
             return bail(st);
@@ -1017,7 +1056,7 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
                           static_cast<int32_t>(A->band), s);
         if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "band column offsets: %s", hipGetErrorString(e)));
     }
-    if (A->rp_owned || A->col16) {   // the handle may next be used on another stream
+    if (A->rp_owned || A->col16 || A->colb16) {   // the handle may next be used on another stream
         e = hipStreamSynchronize(s);
         if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "create: %s", hipGetErrorString(e)));
     }
@@ -1077,7 +1116,7 @@ sla_status sla_csr_analysis(const sla_csr* A, int32_t* row_max, int32_t* tile_ma
 sla_status sla_csr_col_bits(const sla_csr* A, int32_t* col_bits)
 {
     if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
-    if (col_bits) *col_bits = A->col16 ? 16 : 32;
+    if (col_bits) *col_bits = A->c16_ok ? 16 : 32;
     return SLA_OK;
 }
 
@@ -1289,6 +1328,7 @@ sla_status sla_eigsh(const sla_csr* Ac, const double* d_vals, int32_t k, const d
     sla_csr* A = const_cast<sla_csr*>(Ac);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> guard(A->mu);
+    if ((st = ensure_col16(A, s)) != SLA_OK) return st;
     const bool largest = opts->which == SLA_EIG_LARGEST;
     const int rp_bits = A->krp_bits;
     const int64_t ntiles = (n + kTile - 1) / kTile;

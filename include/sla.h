@@ -252,6 +252,7 @@ sla_status sla_matvec_backward(const sla_csr* A, int64_t batch, const double* d_
 sla_status sla_solve(const sla_csr* A, int64_t batch, const double* d_vals, const double* d_b,
                      double* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
 
+
 /*
  * Adjoint backward pass of x = A^{-1} b (gist.science summaries, Methodology item 2;
  * paperpeel section 3.2.3): solve A^T lambda = dL/dx with the same method (CG,
@@ -465,6 +466,23 @@ sla_status sla_timing_query(int32_t kernel, int64_t* launches, double* total_ms)
  * once, each output written once, the matrix once per product); counted by the LOBPCG
  * block kernels, 0 elsewhere. */
 sla_status sla_timing_query_bytes(int32_t kernel, double* bytes);
+
+/* Measurement hook, not part of the solver: one launch of a streaming probe that reads
+ * n_read arrays and writes n_write arrays of n doubles (n even, every array 16-byte
+ * aligned and holding n doubles), with coalesced 16-byte accesses and nothing else.
+ * It measures the bandwidth plain streams of that read/write mix reach, the ceiling
+ * beside which the CG kernels' bandwidth is reported.  Supported mixes (n_read,
+ * n_write): (1,0) read, (0,1) write, (1,1) copy, (2,1) triad (the CG update's mix),
+ * (10,3) about the banded CG SpMV's 78 bytes read per 24 written.  in / out: host
+ * arrays of device pointers.  unroll 1, 2 or 4 (16-byte accesses in flight per thread
+ * and array), nontemporal 0/1 (the streaming hint on every access), blocks_per_cu in
+ * [1, 8] (grid = CUs x blocks_per_cu).  part: device array of at least 8 x CUs doubles,
+ * written by read-only probes (n_write == 0) with per-workgroup sums; may be NULL
+ * otherwise.  Enqueued on `stream`; returns SLA_ERR_INVALID_ARG or SLA_ERR_UNSUPPORTED
+ * (another mix or unroll) before any launch. */
+sla_status sla_probe_stream(int32_t n_read, int32_t n_write, const double* const* in, double* const* out,
+                            int64_t n, int32_t unroll, int32_t nontemporal, int32_t blocks_per_cu,
+                            double* part, void* stream);
 
 const char* sla_status_string(sla_status s);
 const char* sla_last_error(void);

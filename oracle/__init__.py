@@ -71,6 +71,8 @@ def lib():
         L.orc_solve_backward.argtypes = [i64, P, P, P, i32, P, P, f64, f64, i64, i32, i32, P, P, P,
                                          P, P, P]
         L.orc_solve_backward.restype = i32
+        L.orc_cg_timing.argtypes = [i64, P, P, P, P, P, i64, i32, P, P, P, i32]
+        L.orc_cg_timing.restype = i32
         _lib = L
     return _lib
 
@@ -195,3 +197,20 @@ def solve_batched(A, b, **kw):
 
 def solve_backward_batched(A, x, g, **kw):
     return [solve_backward(A, x[s], g[s], vals=A.vals[s], **kw) for s in range(A.vals.shape[0])]
+
+
+def cg_timing(A, b, iters, threads, adjoint=True, vals=None):
+    """The CPU baseline's timing mode (orc_cg_timing): `iters` fixed CG iterations on
+    `threads` OpenMP threads, then (adjoint) the backward pass of L = 0.5 |x|^2 on a
+    symmetric A with the same budget.  Returns dict(x, lam, gvals, threads)."""
+    rp, col = _pattern(A)
+    v = _f64(A.vals if vals is None else vals)
+    b = _f64(b)
+    n = A.n_rows
+    x = np.empty(n, np.float64)
+    lam = np.empty(n, np.float64)
+    gv = np.empty(max(A.nnz, 1), np.float64)
+    work = np.empty(4 * max(n, 1), np.float64)
+    nt = lib().orc_cg_timing(n, _p(rp), _p(col), _p(v), _p(b), _p(x), int(iters), 1 if adjoint else 0,
+                             _p(lam), _p(gv), _p(work), int(threads))
+    return dict(x=x, lam=lam, gvals=gv[:A.nnz], threads=int(nt))

@@ -444,3 +444,98 @@ int orc_solve_backward(int64_t n, const int64_t* row_ptr, const int32_t* col, co
     if (gvals) orc_pattern_outer(n, row_ptr, col, -1.0, lam, x, gvals);
     return state;
 }
+
+/*
+ * Timing mode of the CPU baseline (not a parity reference; the parity functions
+ * above stay sequential).  The same steps as orc_cg run for exactly `iters`
+ * iterations (the fixed-budget mode), with the SpMV rows, the vector updates and the
+ * inner products split into contiguous slices over OpenMP threads: each thread sums
+ * its slice as orc_dot does and the slices' sums are added in thread order, so the
+ * iterates differ from orc_cg's only by that order.  Then, when adjoint != 0, the
+ * backward pass of a symmetric A for g = x: the same CG on g (lam), and
+ * gvals[k] = -lam[row(k)] * x[col(k)].  work: 4 n doubles (r, p, q, the adjoint's
+ * right-hand side).  Returns the number of threads used.
+ */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double dot_threads(int64_t n, const double* a, const double* b, double* part, int nt)
+{
+#pragma omp parallel num_threads(nt)
+    {
+        int t = 0, m = 1;
+#ifdef _OPENMP
+        t = omp_get_thread_num();
+        m = omp_get_num_threads();
+#endif
+        int64_t lo = n * t / m, hi = n * (t + 1) / m;
+        part[t] = orc_dot(hi - lo, a + lo, b + lo);
+        if (t == 0)
+            for (int u = m; u < nt; ++u) part[u] = 0.0;
+    }
+    double s = 0.0;
+    for (int t = 0; t < nt; ++t) s = s + part[t];
+    return s;
+}
+
+static void cg_fixed_threads(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
+                             const double* b, double* x, int64_t iters, double* work, double* part, int nt)
+{
+    double* r = work;
+    double* p = work + n;
+    double* q = work + 2 * n;
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; p[i] = b[i]; }
+    double rho = dot_threads(n, r, r, part, nt);
+    for (int64_t k = 0; k < iters; ++k) {
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                double t = val[e] * p[col[e]];
+                s = s + t;
+            }
+            q[i] = s;
+        }
+        double sigma = dot_threads(n, p, q, part, nt);
+        if (!(sigma > 0.0)) return;
+        double alpha = rho / sigma;
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            double t = alpha * p[i];
+            x[i] = x[i] + t;
+            double u = alpha * q[i];
+            r[i] = r[i] - u;
+        }
+        double rho1 = dot_threads(n, r, r, part, nt);
+        double beta = rho1 / rho;
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            double t = beta * p[i];
+            p[i] = r[i] + t;
+        }
+        rho = rho1;
+    }
+}
+
+int orc_cg_timing(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val, const double* b,
+                  double* x, int64_t iters, int adjoint, double* lam, double* gvals, double* work, int threads)
+{
+    int nt = threads > 0 ? threads : 1;
+    if (nt > 1024) nt = 1024;
+    double part[1024];
+    cg_fixed_threads(n, row_ptr, col, val, b, x, iters, work, part, nt);
+    if (adjoint) {
+        double* g = work + 3 * n;
+        memcpy(g, x, sizeof(double) * (size_t)n);
+        cg_fixed_threads(n, row_ptr, col, val, g, lam, iters, work, part, nt);
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                double t = lam[i] * x[col[e]];
+                gvals[e] = -1.0 * t;
+            }
+    }
+    return nt;
+}

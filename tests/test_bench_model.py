@@ -61,3 +61,38 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
+
+
+def test_v9_iteration_model():
+    # the reported roofline's bytes: 4-byte columns and the stated row-pointer width,
+    # whatever the kernels read; nine vector passes per system
+    assert bench.bytes_model_v9(N, NNZ, 1, 4) == 12 * NNZ + 4 * (N + 1) + 72 * N
+    n, nnz = 169_000_000, 844_948_000
+    assert bench.bytes_model_v9(n, nnz, 1, 8) == 12 * nnz + 8 * (n + 1) + 72 * n
+    # a batch multiplies the values and vectors, not the pattern
+    assert bench.bytes_model_v9(N, NNZ, 4, 4) == 32 * NNZ + 4 * NNZ + 4 * (N + 1) + 288 * N
+    # the kernels' own fused model counts the same nine passes
+    m = bench.bytes_model(N, NNZ, 1, 4, col_bytes=4)
+    assert m["iteration"] == bench.bytes_model_v9(N, NNZ, 1, 4)
+
+
+def test_host_cpu_report():
+    h = bench.host_cpu()
+    assert h["nproc"] >= 1 and 1 <= h["threads"] <= h["nproc"]
+
+
+def test_oracle_timing_mode_follows_the_parity_oracle():
+    # the CPU baseline's OpenMP timing mode runs the parity oracle's CG steps: on a
+    # small grid its iterates agree with the sequential oracle to rounding
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    A = W.poisson5(40)
+    b = W.rhs_normal(A.n_rows, 0)
+    r = O.cg_timing(A, b, 30, 3)
+    f = O.cg(A, b, rtol=0.0, max_iter=30, fixed=True)
+    bw = O.solve_backward(A, f["x"], f["x"], rtol=0.0, max_iter=30, fixed=True)
+    rel = lambda a, c: np.linalg.norm(a - c) / np.linalg.norm(c)
+    assert r["threads"] == 3
+    assert rel(r["x"], f["x"]) < 1e-13 and rel(r["lam"], bw["lam"]) < 1e-13
+    assert rel(r["gvals"], bw["gvals"]) < 1e-13

@@ -110,3 +110,74 @@ def test_blocks_return_to_their_allocator(S):
     gc.collect()
     torch.cuda.synchronize()
     assert calls["free"] == calls["alloc"], calls
+
+
+def test_failing_allocator_reports_oom_and_leaks_nothing(S):
+    # An allocator that returns NULL at its N-th call, for every N that a create +
+    # solve + adjoint on a non-symmetric handle reaches (validation scratch, workspace,
+    # the transpose, its scratch and offsets, the transposed values).  Each failing call
+    # reports SLA_ERR_OOM; the handle it leaves (if create succeeded) then finishes the
+    # same run bit for bit once allocation works again, so a half-built transpose left
+    # nothing behind; and after the handle is gone every block has come back.
+    from differentiable_sparse_linear_spmv_amd import _lib as L
+    lib = L.load()
+    A = W.poisson5(30)     # declared non-symmetric: the adjoint runs on the device transpose
+    b = W.rhs_normal(A.n_rows, 2)
+    state = {"calls": 0, "fail_at": 0, "live": {}, "bad_free": 0}
+
+    def _alloc(size, stream, ctx):
+        state["calls"] += 1
+        if state["calls"] == state["fail_at"]:
+            return None
+        p = torch.cuda.caching_allocator_alloc(int(size))
+        state["live"][p] = int(size)
+        return p
+
+    def _free(ptr, stream, ctx):
+        if state["live"].pop(ptr, None) is None:
+            state["bad_free"] += 1
+            return
+        torch.cuda.caching_allocator_delete(ptr)
+
+    cbs = (L.ALLOC_FN(_alloc), L.FREE_FN(_free))
+    assert lib.sla_set_allocator(cbs[0], cbs[1], None) == 0
+    opts = S.cg_opts(rtol=1e-10)
+    rp, col, vals, bd = dev(A.row_ptr), dev(A.col), dev(A.vals), dev(b)
+
+    def full_run(h):
+        x, _ = S.solve(h, vals, bd, opts)
+        gb, gv, _ = S.solve_backward(h, vals, x, x.clone(), opts)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in (x, gb, gv)]
+
+    try:
+        h = S.csr_create(rp, col, symmetric=False)
+        ref = full_run(h)
+        total = state["calls"]
+        del h
+        gc.collect()
+        torch.cuda.synchronize()
+        assert not state["live"] and total >= 5, (state, total)
+        failed = 0
+        for n_fail in range(1, total + 1):
+            state.update(calls=0, fail_at=n_fail)
+            h = None
+            try:
+                h = S.csr_create(rp, col, symmetric=False)
+                full_run(h)
+            except L.SlaError as e:
+                assert e.status == L.SLA_ERR_OOM, (n_fail, str(e))
+                failed += 1
+            state["fail_at"] = 0
+            if h is not None:   # the handle survives a failed call and completes the run
+                out = full_run(h)
+                for r, o in zip(ref, out):
+                    assert np.array_equal(r, o), n_fail
+            del h
+            gc.collect()
+            torch.cuda.synchronize()
+            assert not state["live"], (n_fail, state["live"])
+        assert failed == total, (failed, total)
+        assert state["bad_free"] == 0
+    finally:
+        assert lib.sla_set_allocator(L.ALLOC_FN(), L.FREE_FN(), None) == 0
