@@ -37,7 +37,7 @@ EXPORTS = [
     "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_col_bits", "sla_list_solve",
     "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable",
     "sla_timing_reset", "sla_timing_collect", "sla_timing_query", "sla_timing_query_bytes", "sla_status_string",
-    "sla_last_error", "sla_version", "sla_probe_stream",
+    "sla_last_error", "sla_version", "sla_probe_stream", "sla_solve_noalloc",
 ]
 
 
@@ -114,6 +114,8 @@ def load():
     L.sla_matvec_backward.restype = st
     L.sla_solve.argtypes = [P, i64, P, P, P, C.POINTER(SlaCgOpts), P, P]
     L.sla_solve.restype = st
+    L.sla_solve_noalloc.argtypes = [P, i64, P, P, P, C.POINTER(SlaCgOpts), P, P]
+    L.sla_solve_noalloc.restype = st
     L.sla_solve_backward.argtypes = [P, i64, P, P, P, P, P, C.POINTER(SlaCgOpts), P, P]
     L.sla_solve_backward.restype = st
     L.sla_list_create.argtypes = [C.POINTER(P), i32, P, P, P, i32, P, u32, P]

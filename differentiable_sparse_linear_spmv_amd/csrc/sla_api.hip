@@ -341,26 +341,12 @@ size_t workspace_bytes(int64_t n, int64_t batch, int G, int method, int64_t nsta
     return kWsVectors[method] * vec + kWsPartials[method] * part + align256(sizeof(SysState) * nstate) + 256;
 }
 
-// G: the larger of the two grids (every partial array gets room for it).  nstate: the
-// number of systems (batch, or the items of a SparseTensorList; < 0: batch).
-sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int method = kMethodCG,
-                            int64_t nstate = -1)
+// The workspace's arrays carved from one block at p (workspace_bytes of the same
+// arguments).  nstate: the number of systems (batch, or the items of a
+// SparseTensorList; < 0: batch).
+void carve_workspace(char* p, int64_t n, int64_t batch, int G, Workspace* w, int method, int64_t nstate)
 {
-    const int64_t n = A->n_rows;
     if (nstate < 0) nstate = batch;
-    const size_t need = workspace_bytes(n, batch, G, method, nstate);
-    if (need > A->ws_bytes) {
-        if (A->ws) {
-            HIP_TRY(hipDeviceSynchronize());
-            HIP_TRY(dev_free(A->ws));
-            A->ws = nullptr;
-            A->ws_bytes = 0;
-        }
-        sla_status s = dev_alloc(&A->ws, need);
-        if (s != SLA_OK) return s;
-        A->ws_bytes = need;
-    }
-    char* p = static_cast<char*>(A->ws);
     const size_t vec = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t part = align256(sizeof(double) * static_cast<size_t>(G) * batch);
     const int nv = kWsVectors[method], np = kWsPartials[method];
@@ -379,6 +365,44 @@ sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int 
     w->part_tt = part_at(4);
     w->st = reinterpret_cast<SysState*>(p + nv * vec + np * part);
     w->n_active = reinterpret_cast<int32_t*>(p + nv * vec + np * part + align256(sizeof(SysState) * nstate));
+}
+
+// A caller-fixed workspace block (the allocation-free entry point): the solve drivers
+// carve their workspace from it instead of the handle's, and allocate nothing.
+struct FixedWs {
+    char* base;
+    size_t bytes;
+};
+
+// G: the larger of the two grids (every partial array gets room for it).  nstate: the
+// number of systems (batch, or the items of a SparseTensorList; < 0: batch).  With fx,
+// the workspace is carved from fx's block (SLA_ERR_INVALID_ARG if it does not fit).
+sla_status ensure_workspace(sla_csr* A, int64_t batch, int G, Workspace* w, int method = kMethodCG,
+                            int64_t nstate = -1, const FixedWs* fx = nullptr)
+{
+    const int64_t n = A->n_rows;
+    if (nstate < 0) nstate = batch;
+    const size_t need = workspace_bytes(n, batch, G, method, nstate);
+    if (fx) {
+        if (need > fx->bytes)
+            return fail(SLA_ERR_INVALID_ARG,
+                        "the allocation-free solve needs %zu bytes of scratch here, more than its %zu",
+                        need, fx->bytes);
+        carve_workspace(fx->base, n, batch, G, w, method, nstate);
+        return SLA_OK;
+    }
+    if (need > A->ws_bytes) {
+        if (A->ws) {
+            HIP_TRY(hipDeviceSynchronize());
+            HIP_TRY(dev_free(A->ws));
+            A->ws = nullptr;
+            A->ws_bytes = 0;
+        }
+        sla_status s = dev_alloc(&A->ws, need);
+        if (s != SLA_OK) return s;
+        A->ws_bytes = need;
+    }
+    carve_workspace(static_cast<char*>(A->ws), n, batch, G, w, method, nstate);
     return SLA_OK;
 }
 
@@ -698,13 +722,15 @@ struct ListPlan {
 // band > 0: the pattern is banded with line stride `band` and takes the line-walking
 // SpMV (LDS variant band_cap) on a persistent grid over blocks of lines of one strip.
 // list: a SparseTensorList solve on the packed pattern (batch 1, plain or split SpMV).
+// fx: the allocation-free entry point's scratch (nothing is allocated: no grouped
+// layout, column offsets only where the handle already holds them).
 sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t band, int band_cap,
                   bool split, int64_t batch, const double* vals, const double* b, double* x, const sla_cg_opts* o,
-                  sla_cg_info* info, hipStream_t s, const ListPlan* list = nullptr)
+                  sla_cg_info* info, hipStream_t s, const ListPlan* list = nullptr, const FixedWs* fx = nullptr)
 {
     const bool jacobi = (o->flags & SLA_JACOBI) != 0;
     if (list) band = 0;
-    if (!list && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 &&
+    if (!list && !fx && split && band == 0 && batch >= kGroupMinBatch && batch % kGroup == 0 &&
         A->krp_bits == 32 && A->nnz > 0 &&
         A->group_ok &&
         static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapLarge && row_ptr == A->krp)
@@ -746,9 +772,9 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     if (list) G = Gu = list->total_wg;   // one grid and one partial slot per workgroup
     Workspace w;
     sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi ? kMethodJacobi : kMethodCG,
-                                     list ? list->items : -1);
+                                     list ? list->items : -1, fx);
     if (st != SLA_OK) return st;
-    if (band == 0 && col == A->col && (st = ensure_col16(A, s)) != SLA_OK) return st;
+    if (!fx && band == 0 && col == A->col && (st = ensure_col16(A, s)) != SLA_OK) return st;
 
     CgArgs a{};
     a.row_ptr = row_ptr;
@@ -827,7 +853,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
 // polling is run_cg's.
 sla_status run_bicgstab(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, int64_t batch,
                         const double* vals, const double* b, double* x, const sla_cg_opts* o, sla_cg_info* info,
-                        hipStream_t s)
+                        hipStream_t s, const FixedWs* fx = nullptr)
 {
     const int64_t n = A->n_rows;
     const int64_t ntiles = (n + kTile - 1) / kTile;
@@ -840,9 +866,9 @@ sla_status run_bicgstab(sla_csr* A, const void* row_ptr, const int32_t* col, int
         if (Gu > ntiles) Gu = G;
     }
     Workspace w;
-    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, kMethodBiCGStab);
+    sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, kMethodBiCGStab, -1, fx);
     if (st != SLA_OK) return st;
-    if (col == A->col && (st = ensure_col16(A, s)) != SLA_OK) return st;
+    if (!fx && col == A->col && (st = ensure_col16(A, s)) != SLA_OK) return st;
 
     CgArgs a{};
     a.row_ptr = row_ptr;
@@ -1239,6 +1265,71 @@ sla_status sla_solve(const sla_csr* Ac, int64_t batch, const double* d_vals, con
     else
         st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_b, d_x, opts,
                     d_info, s);
+    if (st == SLA_OK && !(opts->flags & SLA_FIXED_ITERS)) {
+        hipError_t e = timing_collect();
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));
+    }
+    return st;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free solve (sla_solve_noalloc): one call's CG / Jacobi /
+// BiCGStab workspace, in a static device array instead of memory from an allocator.
+// Every GPU the library runs on holds its own copy until the process ends.  In host
+// code the array's name is not a device address: each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(SLA_NOALLOC_SCRATCH_MIB) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+sla_status scratch_of_device(int dev, char** out)
+{
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(SLA_ERR_UNSUPPORTED, "the allocation-free solve supports device ordinals below %d",
+                    kScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<char*>(g_scratch_ptr[dev]);
+    return SLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sla_status sla_solve_noalloc(const sla_csr* Ac, int64_t batch, const double* d_vals, const double* d_b, double* d_x,
+                             const sla_cg_opts* opts, sla_cg_info* d_info, void* stream)
+{
+    sla_status st = check_common(Ac, batch);
+    if (st != SLA_OK) return st;
+    if (Ac->n_rows != Ac->n_cols) return fail(SLA_ERR_UNSUPPORTED, "solve needs a square matrix");
+    if ((st = check_opts(opts)) != SLA_OK) return st;
+    if (!d_info) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    if (Ac->n_rows == 0) return empty_solve_info(batch, d_info, static_cast<hipStream_t>(stream));
+    if ((!d_vals && Ac->nnz > 0) || !d_b || !d_x) return fail(SLA_ERR_INVALID_ARG, "NULL array");
+    char* base = nullptr;
+    if ((st = scratch_of_device(Ac->device, &base)) != SLA_OK) return st;
+    const FixedWs fx{base, kScratchBytes};
+    sla_csr* A = const_cast<sla_csr*>(Ac);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(A->mu);
+    if (opts->flags & SLA_BICGSTAB)
+        st = run_bicgstab(A, A->krp, A->col, A->cap, batch, d_vals, d_b, d_x, opts, d_info, s, &fx);
+    else
+        st = run_cg(A, A->krp, A->col, A->cap, A->band, A->band_cap, A->split, batch, d_vals, d_b, d_x, opts,
+                    d_info, s, nullptr, &fx);
     if (st == SLA_OK && !(opts->flags & SLA_FIXED_ITERS)) {
         hipError_t e = timing_collect();
         if (e != hipSuccess) return fail(SLA_ERR_HIP, "timing collect: %s", hipGetErrorString(e));

@@ -24,6 +24,7 @@ from ._lib import SlaCgInfo, SlaCgOpts, SlaEigInfo, SlaEigOpts, check
 
 __all__ = [
     "csr_create", "csr_destroy", "csr_info", "csr_analysis", "matvec", "matvec_backward", "solve",
+    "solve_noalloc", "info_buffer",
     "solve_backward", "cg_opts", "read_info", "eigsh", "eigsh_backward", "list_create", "list_solve",
     "list_solve_backward", "SparseTensor", "SparseTensorList", "timing",
 ]
@@ -183,6 +184,26 @@ def read_info(info: torch.Tensor) -> list[dict]:
         out.append(dict(iterations=s.iterations, res_norm=s.res_norm, rhs_norm=s.rhs_norm,
                         state=s.state, state_name=L.STATE_NAMES.get(s.state, str(s.state))))
     return out
+
+
+def solve_noalloc(h: Handle, vals: torch.Tensor, b: torch.Tensor, opts: SlaCgOpts,
+                  x: torch.Tensor, info: torch.Tensor):
+    """sla_solve_noalloc: sla_solve with its workspace in the library's static device
+    scratch (nothing allocated by the call).  The caller passes x and info (from
+    info_buffer); calls that overlap on one GPU race."""
+    B = _batch_of(vals, h.nnz)
+    _need(vals, "vals", torch.float64, B * h.nnz, h.device)
+    _need(b, "b", torch.float64, B * h.n_rows, h.device)
+    _need(x, "x", torch.float64, B * h.n_rows, h.device)
+    _need(info, "info", torch.uint8, B * C.sizeof(SlaCgInfo), h.device)
+    check(L.load().sla_solve_noalloc(h.ptr, B, _ptr(vals), _ptr(b), _ptr(x), C.byref(opts), _ptr(info),
+                                     _stream(h.device)))
+    return x, info
+
+
+def info_buffer(batch: int, device) -> torch.Tensor:
+    """A device buffer for `batch` sla_cg_info records."""
+    return _info_buffer(batch, device)
 
 
 def solve(h: Handle, vals: torch.Tensor, b: torch.Tensor, opts: SlaCgOpts,

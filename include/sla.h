@@ -252,6 +252,31 @@ sla_status sla_matvec_backward(const sla_csr* A, int64_t batch, const double* d_
 sla_status sla_solve(const sla_csr* A, int64_t batch, const double* d_vals, const double* d_b,
                      double* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
 
+/*
+ * sla_solve without any allocation, for callers that cannot allocate device memory
+ * during the call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, methods, kernels and results as sla_solve; the
+ * solver's workspace (r, p, p', q, and z, d for Jacobi or z for BiCGStab, the
+ * reduction partials and the per-system state) lives in a static device array of
+ * SLA_NOALLOC_SCRATCH_MIB MiB, which every GPU the library runs on holds until the
+ * process ends, instead of memory the handle allocates.  Nothing is allocated by the
+ * call: no hipMalloc or hipFree, no registered allocator.  The limit: the workspace must
+ * fit the scratch, about 8 x (4 + 2 Jacobi, + 1 BiCGStab) bytes per row and system plus
+ * 8 bytes per workgroup and system for the partials: CG up to about 1.5M rows x
+ * systems, Jacobi CG and BiCGStab up to about 1M.  A larger problem returns
+ * SLA_ERR_INVALID_ARG (the message gives the bytes needed) before any launch.  Other
+ * differences from sla_solve, all so that nothing is allocated: batches run the
+ * per-system kernels (never the grouped layout), and the plain SpMV reads the 16-bit
+ * column offsets only where the handle already holds them (a banded handle builds them
+ * on its first plain product; without them the 32-bit columns are read, same row sums).
+ * The handle itself (sla_csr_create, and the transpose of a non-symmetric handle)
+ * allocates as documented there.  Every call on a GPU shares that GPU's scratch, which
+ * keeps the last call's contents (each call initialises what it reads): calls that
+ * overlap in time on one GPU, on any streams or threads, race and must not be issued.
+ */
+#define SLA_NOALLOC_SCRATCH_MIB 50
+sla_status sla_solve_noalloc(const sla_csr* A, int64_t batch, const double* d_vals, const double* d_b,
+                             double* d_x, const sla_cg_opts* opts, sla_cg_info* d_info, void* stream);
 
 /*
  * Adjoint backward pass of x = A^{-1} b (gist.science summaries, Methodology item 2;
