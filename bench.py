@@ -58,13 +58,17 @@ def kernel_source_hash() -> str:
 
 
 # ------------------------------------------------------------------------------ bytes model
-def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False, col_bytes: int = 4) -> dict:
+def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False, col_bytes: int = 4,
+                dia_nd: int = 0) -> dict:
     """Algorithmic HBM bytes of the kernels, per launch (all systems of the batch).
 
     rp_bytes is the width of the row pointers the kernels read: 4 whenever nnz < 2^31
     (the library keeps a 32-bit copy of 64-bit row pointers that fit).  col_bytes is
     the width of the column indices the SpMV reads: 2 where the handle holds 16-bit
-    column offsets (sla_csr_col_bits), else 4.
+    column offsets (sla_csr_col_bits), else 4.  dia_nd > 0: the banded SpMV reads the
+    diagonal layout instead of the CSR arrays: dia_nd values per row and system (absent
+    entries' slots included) and a mask of 1 byte per row (2 above 8 diagonals), no
+    column indices and no row pointers.
 
     Fused schedule (plain or banded SpMV):
       cg_spmv  : values 8 nnz B + columns col_bytes nnz + row pointers rp (n + 1)
@@ -77,7 +81,10 @@ def bytes_model(n: int, nnz: int, batch: int, rp_bytes: int, split: bool = False
                  cache traffic), write q                          -> 2 x 8 n B
       cg_update: as above; one iteration = ten vector passes.
     """
-    mat = 8 * nnz * batch + col_bytes * nnz + rp_bytes * (n + 1)
+    if dia_nd > 0:
+        mat = 8 * dia_nd * n * batch + (1 if dia_nd <= 8 else 2) * n
+    else:
+        mat = 8 * nnz * batch + col_bytes * nnz + rp_bytes * (n + 1)
     upd = 3 * 8 * n * batch
     if split:
         pupd = 5 * 8 * n * batch
@@ -764,6 +771,10 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     if bicg:
         spmv_kernel = "k_cg_spmv (BiCGStab modes: v = A p, t = A s)"
         schedule = "BiCGStab: p update, v = A p, s, t = A s, update (adjoint on the device transpose)"
+    elif an["band_stride"] > 0 and an["diagonals"] > 0:
+        spmv_kernel = "k_cg_spmv_dia"
+        schedule = (f"fused, banded SpMV on the diagonal layout (line stride {an['band_stride']}, "
+                    f"{an['diagonals']} diagonals)")
     elif an["band_stride"] > 0:
         spmv_kernel, schedule = "k_cg_spmv_band", f"fused, banded SpMV (line stride {an['band_stride']})"
     elif an["split"] and B >= 8 and B % 4 == 0 and nnz < 2 ** 31:
@@ -776,6 +787,7 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     # the plain and banded SpMV (CG and BiCGStab) read 16-bit column offsets where the
     # handle has them; the grouped kernels read the 32-bit columns
     col_bytes = 4 if spmv_kernel == "k_gcg_spmv" else an["col_bits"] // 8
+    dia_nd = an["diagonals"] if spmv_kernel == "k_cg_spmv_dia" else 0
     rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
     rp_stated = w["rp"].element_size()        # the row-pointer width the workload hands in
     if args.fixed_iters > 0:
@@ -825,7 +837,7 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     tq = S.timing.query()
     torch.cuda.synchronize()
     del x, h
-    return dict(w=w, an=an, bicg=bicg, spmv_kernel=spmv_kernel, schedule=schedule, col_bytes=col_bytes,
+    return dict(w=w, an=an, bicg=bicg, spmv_kernel=spmv_kernel, schedule=schedule, col_bytes=col_bytes, dia_nd=dia_nd,
                 rp_bytes=rp_bytes, rp_stated=rp_stated, steps=steps, warmup=warmup, wall=wall,
                 event_ms=e0.elapsed_time(e1) / steps, fwd_it=fwd_it, bwd_it=bwd_it, total_it=total_it, tq=tq)
 
@@ -852,7 +864,8 @@ def iteration_roofline(r) -> dict:
         iter_ms = 2 * spmv_ms + 3 * avg_ms("bs_vec")
         v9 = bm["iteration"]   # BiCGStab: its own model (two products, 14 vector passes)
     else:
-        bm = bytes_model(n, nnz, B, r["rp_bytes"], split=r["an"]["split"], col_bytes=r["col_bytes"])
+        bm = bytes_model(n, nnz, B, r["rp_bytes"], split=r["an"]["split"], col_bytes=r["col_bytes"],
+                         dia_nd=r["dia_nd"])
         spmv_ms, spmv_bytes = avg_ms("cg_spmv"), bm["cg_spmv"]
         iter_ms = spmv_ms + avg_ms("cg_update") + (avg_ms("cg_pupd") if r["an"]["split"] else 0.0)
         v9 = bytes_model_v9(n, nnz, B, r["rp_stated"])
@@ -896,7 +909,8 @@ def cg_summary(r, ceiling, args) -> dict:
             roof["frac_of_ceiling"] = round(t_ceil / (rf["iter_ms"] * 1e-3), 4)
     return {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "batch": B,
             "row_ptr": f"int{8 * r['rp_stated']} (kernels read int{8 * r['rp_bytes']})",
-            "col_idx_read": f"int{8 * r['col_bytes']}", "rtol": w["rtol"], "fixed_iterations": w["fixed"],
+            "col_idx_read": ("none (diagonal layout)" if r["dia_nd"] else f"int{8 * r['col_bytes']}"),
+            "rtol": w["rtol"], "fixed_iterations": w["fixed"],
             "cg_schedule": r["schedule"], "steps": r["steps"], "warmup": r["warmup"],
             "ms_per_step": round(ms_step, 4), "solve_adjoint_ms": round(ms_step, 4),
             "iterations_per_step": {"forward": r["fwd_it"][-1], "adjoint": r["bwd_it"][-1]},

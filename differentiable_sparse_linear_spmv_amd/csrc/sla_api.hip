@@ -59,6 +59,17 @@ struct sla_csr {
     // Banded pattern (line-walking SpMV): line stride S, 0 if the plain SpMV is used.
     int64_t band = 0;
     int band_cap = kCapSmall;
+    // Diagonal layout of a banded pattern with at most kDiaMax distinct offsets (the CG
+    // SpMV k_cg_spmv_dia): dia_nd diagonals (0: none), their codes' map, per-row masks
+    // (uint8, or uint16 above 8 diagonals), and the values in that layout [batch][nd][n],
+    // rewritten by each solve (SLA_DIA=0 at create turns the layout off).
+    int dia_nd = 0;
+    DiaMap dia_map{};
+    int8_t dia_b[kDiaMax] = {};
+    int8_t dia_e[kDiaMax] = {};
+    void* dia_mask = nullptr;
+    double* dia_vals = nullptr;
+    size_t dia_vals_bytes = 0;
     // Split CG schedule (unstructured patterns); the transposed pattern has the same span.
     bool split = false;
     // Grouped kernels for batches of split-schedule patterns (SLA_CG_GROUPED=0 turns them off).
@@ -526,6 +537,52 @@ sla_status ensure_vals_t(sla_csr* A, int64_t batch, const double* vals, hipStrea
     return SLA_OK;
 }
 
+// The diagonal layout of a banded handle (line stride A->band, 32-bit row pointers):
+// the distinct offsets of its entries, ascending; with at most kDiaMax of them, their map
+// and the per-row masks.  A pattern with more keeps the staged banded SpMV (dia_nd = 0).
+sla_status build_dia(sla_csr* A, hipStream_t s)
+{
+    const int32_t S = static_cast<int32_t>(A->band);
+    const int32_t* rp = static_cast<const int32_t*>(A->krp);
+    uint32_t* d_codes = nullptr;
+    sla_status st = dev_alloc(reinterpret_cast<void**>(&d_codes), 3 * sizeof(uint32_t));
+    if (st != SLA_OK) return st;
+    uint32_t h[3] = {0, 0, 0};
+    hipError_t e = hipMemcpyAsync(d_codes, h, sizeof(h), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = launch_dia_codes(rp, A->col, A->n_rows, S, d_codes, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h, d_codes, sizeof(h), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    (void)dev_free(d_codes);
+    if (e != hipSuccess) return fail(SLA_ERR_HIP, "diagonal analysis: %s", hipGetErrorString(e));
+    if (h[2] != 0) return SLA_OK;   // an entry off the band's diagonals (cannot happen for a banded handle)
+    DiaMap m{};
+    for (int c = 0; c <= kDiaCodes; ++c) m.d_of_code[c] = -1;
+    int nd = 0;
+    for (int c = 0; c < kDiaCodes; ++c) {
+        const bool on = c < 32 ? ((h[0] >> c) & 1u) : ((h[1] >> (c - 32)) & 1u);
+        if (!on) continue;
+        if (nd == kDiaMax) return SLA_OK;   // too many diagonals: the staged banded SpMV
+        m.d_of_code[c] = static_cast<int8_t>(nd);
+        A->dia_b[nd] = static_cast<int8_t>(c / kDiaCodesPerBand - 1);
+        A->dia_e[nd] = static_cast<int8_t>(c % kDiaCodesPerBand - kBandHalo);
+        ++nd;
+    }
+    if (nd == 0) return SLA_OK;
+    const bool m16 = nd > 8;
+    void* mask = nullptr;
+    if ((st = dev_alloc(&mask, (m16 ? 2 : 1) * static_cast<size_t>(A->n_rows))) != SLA_OK) return st;
+    e = launch_dia_mask(rp, A->col, A->n_rows, S, m, mask, m16, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        (void)dev_free(mask);
+        return fail(SLA_ERR_HIP, "diagonal masks: %s", hipGetErrorString(e));
+    }
+    A->dia_map = m;
+    A->dia_mask = mask;
+    A->dia_nd = nd;
+    return SLA_OK;
+}
+
 // One CG solve (batch systems) on the pattern (row_ptr, col, cap) with values vals.
 // Enqueue the iterations k = 0 .. max_iter (step(k) launches one iteration's kernels).
 // Fixed-iteration mode enqueues them all.  Otherwise chunks of check_every (default
@@ -742,15 +799,19 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     const int Gp = blocks_per_system(A, ntiles, batch, cg_blocks_per_cu(A->krp_bits, cap, n, split));
     int G = Gp, band_block = 0;
     int64_t band_lines = 0;
+    // The diagonal layout (k_cg_spmv_dia) serves a banded handle's own pattern whenever
+    // it exists; the allocation-free entry point keeps the staged banded SpMV (the layout's
+    // values need a buffer).
+    const bool dia = band > 0 && !list && !fx && A->dia_nd > 0 && row_ptr == A->krp && col == A->col;
     if (band > 0) {
-        // Persistent grid over blocks of band_block lines of one strip (k_cg_spmv_band):
-        // blocks of up to kBandBlockLines lines, shorter when needed to give every
-        // workgroup of the grid a block.
+        // Persistent grid over blocks of band_block lines of one strip (k_cg_spmv_band,
+        // k_cg_spmv_dia): blocks of up to kBandBlockLines lines, shorter when needed to
+        // give every workgroup of the grid a block.
         const int64_t strips = (band + kTile - 1) / kTile;
         band_lines = (n + band - 1) / band;
         const int64_t spmv_bytes = (12 * A->nnz + 52 * n) * batch;   // values, columns, rows, six vectors
-        int per_cu = cg_band_blocks_per_cu(band_cap);
-        if (spmv_bytes > kBandStreamBytes) per_cu = std::min(per_cu, kBandBlocksPerCu);
+        int per_cu = dia ? cg_dia_blocks_per_cu(A->dia_nd) : cg_band_blocks_per_cu(band_cap);
+        if (spmv_bytes > kBandStreamBytes) per_cu = std::min(per_cu, dia ? kDiaBlocksPerCu : kBandBlocksPerCu);
         const int64_t target = std::max<int64_t>(1, (static_cast<int64_t>(A->n_cu) * per_cu) / batch);
         const int64_t bl = std::max<int64_t>(4, std::min<int64_t>(kBandBlockLines, strips * band_lines / target));
         band_block = static_cast<int>(std::min<int64_t>(band_lines, bl));
@@ -769,12 +830,41 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         Gu = static_cast<int>(std::max<int64_t>(8, std::min<int64_t>(Gp, g)));
         if (Gu > ntiles) Gu = Gp;
     }
+    // The 16-byte update kernel (k_cg_update_wide) serves every per-system solve whose
+    // vectors are 16-byte aligned: one system, or an even n (the caller's b, read as r_0,
+    // must be aligned too).  Systems that stream from HBM give it 3 workgroups per CU:
+    // at 169M rows 684 us per launch against 782 us for the 8-tile kernel on one box
+    // (1024 workgroups: 701 us; 2048: 810 us); at 1M rows the 8-tile grid stays best for
+    // it too (6.6 us against 7.2 us for the 8-tile kernel).
+    const bool wide = !list && !(batch >= 8 && batch % 8 == 0) && (batch == 1 || n % 2 == 0) &&
+                      (reinterpret_cast<uintptr_t>(b) & 15) == 0;
+    const bool streaming = (12 * A->nnz + 52 * n) * batch > kBandStreamBytes;
+    if (wide && streaming && batch == 1) Gu = std::max(Gu, 3 * A->n_cu);
     if (list) G = Gu = list->total_wg;   // one grid and one partial slot per workgroup
     Workspace w;
     sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi ? kMethodJacobi : kMethodCG,
                                      list ? list->items : -1, fx);
     if (st != SLA_OK) return st;
     if (!fx && band == 0 && col == A->col && (st = ensure_col16(A, s)) != SLA_OK) return st;
+    if (dia) {
+        const size_t need = sizeof(double) * static_cast<size_t>(A->dia_nd) * n * batch;
+        if (need > A->dia_vals_bytes) {
+            if (A->dia_vals) {
+                HIP_TRY(hipDeviceSynchronize());
+                HIP_TRY(dev_free(A->dia_vals));
+                A->dia_vals = nullptr;
+                A->dia_vals_bytes = 0;
+            }
+            if ((st = dev_alloc(reinterpret_cast<void**>(&A->dia_vals), need)) != SLA_OK) return st;
+            A->dia_vals_bytes = need;
+        }
+        hipError_t e = timed(SLA_K_GROUP_LAYOUT, s, [&] {
+            return launch_dia_vals(static_cast<const int32_t*>(A->krp), A->col, vals, n, A->nnz,
+                                   static_cast<int32_t>(band), A->dia_map, A->dia_nd, static_cast<int>(batch),
+                                   A->dia_vals, s);
+        });
+        if (e != hipSuccess) return fail(SLA_ERR_HIP, "diagonal layout of the values: %s", hipGetErrorString(e));
+    }
 
     CgArgs a{};
     a.row_ptr = row_ptr;
@@ -815,10 +905,21 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     // systems far beyond the caches: the update pass streams with the non-temporal
     // hint (measured 5 % faster at 169M rows; slower where the 256 MB cache holds the
     // working set across iterations)
-    a.stream_nt = (12 * A->nnz + 52 * n) * batch > kBandStreamBytes ? 1 : 0;
+    a.stream_nt = streaming ? 1 : 0;
+    a.wide_update = wide ? 1 : 0;
     a.band_block = band_block;
     a.band_stride = band;
     a.band_lines = band_lines;
+    if (dia) {
+        a.dia_vals = A->dia_vals;
+        a.dia_mask = A->dia_mask;
+        a.dia_nd = A->dia_nd;
+        for (int d = 0; d < kDiaMax; ++d) {
+            a.dia_b[d] = d < A->dia_nd ? A->dia_b[d] : 0;
+            a.dia_e[d] = d < A->dia_nd ? A->dia_e[d] : 0;
+            a.dia_v[d] = A->dia_vals + static_cast<size_t>(std::min(d, A->dia_nd - 1)) * n;
+        }
+    }
     if (list) {
         a.list_wg = list->wg;
         a.list_tiles = list->tiles;
@@ -1082,7 +1183,12 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
                           static_cast<int32_t>(A->band), s);
         if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "band column offsets: %s", hipGetErrorString(e)));
     }
-    if (A->rp_owned || A->col16 || A->colb16) {   // the handle may next be used on another stream
+    if (A->band > 0 && A->krp_bits == 32) {
+        bool dia = true;
+        if (const char* env = std::getenv("SLA_DIA")) dia = std::strcmp(env, "0") != 0;
+        if (dia && (st = build_dia(A, s)) != SLA_OK) return bail(st);
+    }
+    if (A->rp_owned || A->col16 || A->colb16 || A->dia_mask) {   // the handle may next be used on another stream
         e = hipStreamSynchronize(s);
         if (e != hipSuccess) return bail(fail(SLA_ERR_HIP, "create: %s", hipGetErrorString(e)));
     }
@@ -1111,6 +1217,8 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->col16) (void)dev_free(A->col16);
     if (A->col16_t) (void)dev_free(A->col16_t);
     if (A->colb16) (void)dev_free(A->colb16);
+    if (A->dia_mask) (void)dev_free(A->dia_mask);
+    if (A->dia_vals) (void)dev_free(A->dia_vals);
     if (A->flag_host) (void)hipHostFree(A->flag_host);
     if (A->eig_ws) (void)dev_free(A->eig_ws);
     if (A->g_rp) (void)dev_free(A->g_rp);
@@ -1146,6 +1254,13 @@ sla_status sla_csr_col_bits(const sla_csr* A, int32_t* col_bits)
     return SLA_OK;
 }
 
+sla_status sla_csr_diagonals(const sla_csr* A, int32_t* n_diagonals)
+{
+    if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
+    if (n_diagonals) *n_diagonals = A->dia_nd;
+    return SLA_OK;
+}
+
 sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int64_t* nnz, int32_t* row_ptr_bits,
                         uint32_t* flags, int64_t* workspace_bytes_out)
 {
@@ -1163,7 +1278,8 @@ sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int6
         if (A->col16) tb += 2 * A->nnz;
         if (A->col16_t) tb += 2 * A->nnz;
         if (A->colb16) tb += 2 * A->nnz;
-        *workspace_bytes_out = static_cast<int64_t>(A->ws_bytes + A->vals_t_bytes) + tb;
+        if (A->dia_mask) tb += (A->dia_nd > 8 ? 2 : 1) * A->n_rows;
+        *workspace_bytes_out = static_cast<int64_t>(A->ws_bytes + A->vals_t_bytes + A->dia_vals_bytes) + tb;
     }
     return SLA_OK;
 }

@@ -30,6 +30,9 @@ constexpr int kBandBlockLines = 32;
 // sequential runs (measured on 169M rows: 2 per CU beat 1 and 4).  Smaller systems,
 // served largely from the 256 MB Infinity Cache, run at full occupancy.
 constexpr int kBandBlocksPerCu = 2;
+// The same for the diagonal-layout SpMV (k_cg_spmv_dia): one workgroup per CU (169M
+// rows: 2879 us per launch, against 2997 us with 2, 3050 with 3 and 3058 with 4).
+constexpr int kDiaBlocksPerCu = 1;
 constexpr int64_t kBandStreamBytes = int64_t(1) << 30;
 
 // Patterns that are not banded but reach columns at least this far from the diagonal
@@ -114,7 +117,40 @@ struct CgArgs {
     int32_t band_block;      // banded SpMV: lines per block of work
     int64_t band_stride;     // banded SpMV: line length S (0: plain SpMV)
     int64_t band_lines;      // banded SpMV: ceil(n / S)
+    int32_t wide_update;     // 1: k_cg_update_wide (16-byte accesses, grid-stride row pairs)
+    // Diagonal layout of a banded pattern (k_cg_spmv_dia; dia_nd = 0: not used).  The
+    // pattern's distinct offsets c - i, ascending, are b S + e with b in {-1, 0, 1} and
+    // |e| <= kBandHalo; diagonal d lives in LDS ring segment dia_b[d] + 1 (line l - 1, l,
+    // l + 1) at position dia_e[d] + kBandHalo + (the row's position in the strip).
+    const double* dia_vals;  // [batch][dia_nd][n]: value of row i on diagonal d at [d][i]
+    const double* dia_v[16]; // system 0's diagonal d at dia_v[d] (d < dia_nd; the last one repeated after)
+    const void* dia_mask;    // [n] uint8 (dia_nd <= 8) or uint16: bit d set if row i stores diagonal d
+    int32_t dia_nd;
+    int8_t dia_b[16];
+    int8_t dia_e[16];
 };
+
+// Diagonal layout of banded patterns: offsets c - i = b S + e (b in {-1, 0, 1}, |e| <=
+// kBandHalo) numbered by code (b + 1) kDiaCodesPerBand + e + kBandHalo, ascending in c - i.
+constexpr int kDiaMax = 16;                       // diagonals of the layout, at most
+constexpr int kDiaCodesPerBand = 2 * kBandHalo + 1;   // e in [-kBandHalo, kBandHalo]
+constexpr int kDiaCodes = 3 * kDiaCodesPerBand;   // 51
+struct DiaMap {
+    int8_t d_of_code[kDiaCodes + 1];   // diagonal index of each code, -1 if the pattern has none
+};
+// Codes present in a banded pattern of line stride S (rows with 32-bit row pointers):
+// out[0] |= bits of codes 0..31, out[1] |= bits of codes 32..50; out[2] != 0 if some
+// entry has no code (not banded with stride S).  out zeroed by the caller.
+hipError_t launch_dia_codes(const int32_t* rp, const int32_t* col, int64_t n, int32_t S, uint32_t* out,
+                            hipStream_t s);
+// mask[i] (uint8 when m16 is false, else uint16): bit d set if row i stores diagonal d.
+hipError_t launch_dia_mask(const int32_t* rp, const int32_t* col, int64_t n, int32_t S, const DiaMap& m, void* mask,
+                           bool m16, hipStream_t s);
+// out[b][d][i] = vals[b][k] for every stored entry k = (i, c) of diagonal d (entries a row
+// does not store are left as they are: the mask excludes them).
+hipError_t launch_dia_vals(const int32_t* rp, const int32_t* col, const double* vals, int64_t n, int64_t nnz, int32_t S,
+                           const DiaMap& m, int nd, int batch, double* out, hipStream_t s);
+int cg_dia_blocks_per_cu(int nd);   // the diagonal-layout SpMV
 
 // Lanczos eigensolver (sla_eigsh).  V [max_dim + 1][n]: row j is the Lanczos vector
 // v_j; w [n] the vector being orthogonalized.  Grids: Gu workgroups for the streaming

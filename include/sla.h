@@ -191,6 +191,14 @@ sla_status sla_csr_destroy(sla_csr* A);
 /* Width in bits of the column indices the plain and banded CG / BiCGStab SpMV read: 16
  * when the handle holds 16-bit column offsets (see sla_csr_create), else 32. */
 sla_status sla_csr_col_bits(const sla_csr* A, int32_t* col_bits);
+/* Diagonals of the banded CG SpMV's diagonal layout (set at sla_csr_create): for a
+ * banded pattern (sla_csr_analysis band_stride > 0) whose stored offsets c - i take at
+ * most 16 distinct values, that number (5 for a 5-point grid stencil), and the CG
+ * solves on the handle's own pattern read the values in that layout: one value per
+ * diagonal and row, copied from the CSR values once per solve, and a per-row mask of the
+ * diagonals the row stores.  0: the staged CSR banded SpMV (more diagonals, not banded,
+ * or SLA_DIA=0 in the environment at create).  Row sums are the same either way. */
+sla_status sla_csr_diagonals(const sla_csr* A, int32_t* n_diagonals);
 
 /* Shape and workspace queries (host outputs; any pointer may be NULL). */
 sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int64_t* nnz,
@@ -472,7 +480,7 @@ enum {
     SLA_K_GATHER_VALS = 5,  /* transposed values */
     SLA_K_TRANSPOSE = 6,    /* pattern transpose (all its kernels) */
     SLA_K_CG_PUPD = 7,      /* split schedule: step decisions, p = r + beta p, x update */
-    SLA_K_GROUP_LAYOUT = 8, /* grouped batches: values and x between layouts */
+    SLA_K_GROUP_LAYOUT = 8, /* value layouts: grouped batches (values, x), banded diagonal layout (values) */
     SLA_K_BS_SPMV = 9,      /* BiCGStab: v = A p with <rh, v>, and t = A s with <t, s>, <t, t> */
     SLA_K_BS_VEC = 10,      /* BiCGStab: init, p update, s = r - alpha v, x and r update */
     SLA_K_LZ_SPMV = 11,     /* Lanczos: w = A v_j with <v_j, w> */

@@ -96,3 +96,14 @@ def test_oracle_timing_mode_follows_the_parity_oracle():
     assert r["threads"] == 3
     assert rel(r["x"], f["x"]) < 1e-13 and rel(r["lam"], bw["lam"]) < 1e-13
     assert rel(r["gvals"], bw["gvals"]) < 1e-13
+
+
+def test_diagonal_layout_model():
+    # the banded SpMV on the diagonal layout reads nd values per row and a mask, no
+    # column indices or row pointers; the vectors and the update are unchanged
+    n, nnz = 169_000_000, 844_948_000
+    m = bench.bytes_model(n, nnz, 1, 4, col_bytes=2, dia_nd=5)
+    assert m["cg_spmv"] == 40 * n + n + 48 * n
+    assert m["cg_update"] == 24 * n
+    m9 = bench.bytes_model(1000, 8000, 2, 4, dia_nd=9)
+    assert m9["cg_spmv"] == 8 * 9 * 1000 * 2 + 2 * 1000 + 48 * 1000 * 2
