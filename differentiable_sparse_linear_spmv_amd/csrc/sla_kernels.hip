@@ -885,6 +885,31 @@ __device__ __forceinline__ void st32_stream(double* __restrict__ base, int32_t e
 #endif
 }
 
+// 16-byte loads and stores (a pair of doubles), with the non-temporal hint when NT.
+template <bool NT>
+__device__ __forceinline__ double2 ld2v(const double2* p)
+{
+    if constexpr (NT) {
+        double2 v;
+        v.x = __builtin_nontemporal_load(&p->x);
+        v.y = __builtin_nontemporal_load(&p->y);
+        return v;
+    } else {
+        return *p;
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st2v(double2* p, double2 v)
+{
+    if constexpr (NT) {
+        __builtin_nontemporal_store(v.x, &p->x);
+        __builtin_nontemporal_store(v.y, &p->y);
+    } else {
+        *p = v;
+    }
+}
+
 // Raw loads of one segment (positions tid, and tid + kTile for tid < 2 kBandHalo).
 struct SegLoad {
     double r0, pp0, r1, pp1;
@@ -1197,21 +1222,24 @@ __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_
 
 // Deferred x update x_k = x_{k-1} + alpha_{k-1} p_{k-1} of the rows of every block a
 // workgroup of the line-walking SpMV owns (a system that stops at iteration k).
+// sw: positions per strip (kTile, or 2 kTile for the two-rows-per-lane kernel).
 __device__ __forceinline__ void band_stop_x(int32_t lb, int32_t G, int32_t nblk, int32_t strips, int32_t B,
                                             int32_t lines, int32_t S, int32_t n, double alpha_prev,
-                                            const double* __restrict__ pprev, double* __restrict__ x)
+                                            const double* __restrict__ pprev, double* __restrict__ x,
+                                            int32_t sw = kTile)
 {
-    const int tid = threadIdx.x;
     for (int32_t b = lb; b < nblk; b += G) {
         const int32_t j = b % strips;
         const int32_t l0 = (b / strips) * B;
         const int32_t l1 = min(l0 + B, lines);
-        const int32_t w = min(kTile, S - j * kTile);
+        const int32_t w = min(sw, S - j * sw);
         for (int32_t m = l0; m < l1; ++m) {
-            const int32_t i = m * S + j * kTile + tid;
-            if (tid < w && i < n) {
-                const double tx = alpha_prev * ld32(pprev, i);
-                st32(x, i, ld32(x, i) + tx);
+            for (int32_t t = threadIdx.x; t < w; t += kBlock) {
+                const int32_t i = m * S + j * sw + t;
+                if (i < n) {
+                    const double tx = alpha_prev * ld32(pprev, i);
+                    st32(x, i, ld32(x, i) + tx);
+                }
             }
         }
     }
@@ -1734,30 +1762,6 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(CgArgs a, int64_t k)
 // 169M rows it streams 4.06 GB in 667 us against 753 us for the 8-byte, tile-strided
 // kernel.  Requires 16-byte aligned vectors (n even, or one system) and no list; an odd
 // n leaves its last row to thread 0 of workgroup 0.
-template <bool NT>
-__device__ __forceinline__ double2 ld2v(const double2* p)
-{
-    if constexpr (NT) {
-        double2 v;
-        v.x = __builtin_nontemporal_load(&p->x);
-        v.y = __builtin_nontemporal_load(&p->y);
-        return v;
-    } else {
-        return *p;
-    }
-}
-
-template <bool NT>
-__device__ __forceinline__ void st2v(double2* p, double2 v)
-{
-    if constexpr (NT) {
-        __builtin_nontemporal_store(v.x, &p->x);
-        __builtin_nontemporal_store(v.y, &p->y);
-    } else {
-        *p = v;
-    }
-}
-
 template <bool NT, bool JAC>
 __global__ __launch_bounds__(kBlock) void k_cg_update_wide(CgArgs a, int64_t k)
 {

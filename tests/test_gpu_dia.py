@@ -3,9 +3,9 @@
 A banded pattern whose stored offsets c - i take at most 16 distinct values gets a
 diagonal layout at create: one value per diagonal and row (copied from the CSR values
 once per solve) and a per-row mask of the diagonals the row stores.  Each row sum is
-the CSR row sum in the same (ascending column) order, so every result must equal the
-staged banded kernel's -- the same handle built with SLA_DIA=0 -- to the bit, and the
-oracle's to the usual bars.  Cases: the 5-point grid (5 diagonals, 8-bit masks, the
+the CSR row sum in the same (ascending column) order, and the inner products are
+summed over the same lanes, so every result must equal the staged banded kernel's --
+the same handle built with SLA_DIA=0 -- to the bit, and the oracle's to the usual bars.  Cases: the 5-point grid (5 diagonals, 8-bit masks, the
 5-slot kernel), a 7-diagonal pattern (8-slot kernel), the 9-point grid (16-slot kernel,
 16-bit masks), a grid with symmetric pairs of entries removed (rows that skip
 diagonals), a last line cut short, a batch, Jacobi PCG, fixed iterations with the
@@ -140,7 +140,8 @@ def check_oracle(A, b, res, rtol, vals=None):
     assert rel(x, f["x"]) <= 1e-9 and rel(lam, bw["lam"]) <= 1e-8 and rel(gv, bw["gvals"]) <= 1e-8
 
 
-@pytest.mark.parametrize("case", ["poisson520", "seven", "nine", "dropped", "cut"])
+@pytest.mark.parametrize("case", ["poisson520", "seven", "nine", "dropped", "cut",
+                                  "poisson600", "seven600", "nine599", "dropped599", "cut600"])
 def test_dia_equals_staged_band_and_oracle(S, band_env, case):
     if case == "poisson520":
         A, nd = W.poisson5(520), 5
@@ -150,8 +151,18 @@ def test_dia_equals_staged_band_and_oracle(S, band_env, case):
         A, nd = nine_point(300, 12), 9
     elif case == "dropped":
         A, nd = drop_pairs(nine_point(300, 10), 0.3, seed=3), 9
-    else:
+    elif case == "cut":
         A, nd = leading(W.poisson5(300), 300 * 9 - 37), 5
+    elif case == "poisson600":
+        A, nd = W.poisson5(600), 5
+    elif case == "seven600":
+        A, nd = offsets_matrix(600 * 30, [-600, -2, -1, 0, 1, 2, 600], 6.5), 7
+    elif case == "nine599":      # stride 600
+        A, nd = nine_point(599, 12), 9
+    elif case == "dropped599":
+        A, nd = drop_pairs(nine_point(599, 10), 0.3, seed=4), 9
+    else:                        # a last line cut short, n even
+        A, nd = leading(W.poisson5(600), 600 * 9 - 38), 5
     b = W.rhs_normal(A.n_rows, 11)
     ad, rd, rs = both(S, A, b, S.cg_opts(rtol=1e-10), band_env)
     assert ad["diagonals"] == nd
@@ -222,7 +233,7 @@ def test_dia_too_many_diagonals_keeps_the_staged_kernel(S, band_env):
 
 def test_dia_several_blocks_per_workgroup(S, monkeypatch):
     # 3000 x 3000 at the default minimum stride: the diagonal layout, bit for bit the
-    # staged kernel over 12 fixed iterations, and the oracle's history
+    # staged kernel over 12 fixed iterations, and the oracle's
     A = W.poisson5(3000)
     b = W.rhs_normal(A.n_rows, 8)
     K = 12
