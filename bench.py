@@ -374,6 +374,8 @@ def make_workload(name: str, device):
                        "CG to 1e-8 + adjoint of 0.5|x|^2",
         "varcoef2048": "variable-coefficient Poisson 2048x2048, kappa=exp(GRF), CG to 1e-8 + adjoint",
         "fem256x256": "256 P1 FEM systems on a jittered 256x256-vertex mesh, CG to 1e-8 + adjoint",
+        "graph1m": "graph Laplacian + I of a power-law graph (2^20 nodes, average degree 8, exponent 2.5, "
+                   "random node order, seed 0): skewed row lengths, CG to 1e-8 + adjoint of 0.5|x|^2",
         "convdiff1024": "nonsymmetric convection-diffusion 1024x1024 (upwind, recirculating wind W=100), "
                         "b~N(0,1) seed 0, BiCGStab to 1e-8 + BiCGStab adjoint on A^T",
     }
@@ -615,7 +617,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="poisson1024",
-                    choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000",
+                    choices=["poisson64", "poisson1024", "varcoef2048", "fem256x256", "poisson13000", "graph1m",
                              "convdiff1024", "eigsh_varcoef1024", "eigsh_tr_varcoef1024", "lobpcg_varcoef1024",
                              "poisson_list64"])
     ap.add_argument("--cpu-iters", type=int, default=300)

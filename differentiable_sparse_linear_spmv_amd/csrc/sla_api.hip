@@ -305,8 +305,9 @@ hipError_t dev_free(void* p)
     return e;
 }
 
-int choose_cap(int32_t tile_max)
+int choose_cap(int32_t tile_max, int32_t row_max)
 {
+    if (row_max > kBinLaneMax) return kCapSkew;
     if (tile_max <= kCapSmall) return kCapSmall;
     if (tile_max <= kCapMid) return kCapMid;
     return kCapLarge;
@@ -491,7 +492,7 @@ sla_status ensure_transpose(sla_csr* A, hipStream_t s)
     A->col_t = colt;
     A->perm_t = permt;
     A->col16_t = c16t;
-    A->cap_t = choose_cap(h[kChkTileMax]);
+    A->cap_t = choose_cap(h[kChkTileMax], h[kChkRowMax]);
     A->has_t = true;
     return SLA_OK;
 }
@@ -1142,9 +1143,9 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
     }
     A->tile_max = h[kChkTileMax];
     A->row_max = h[kChkRowMax];
-    A->cap = choose_cap(h[kChkTileMax]);
+    A->cap = choose_cap(h[kChkTileMax], h[kChkRowMax]);
     A->band = band_stride_of(n_rows, n_cols, nnz, h[kChkRowMax], h[kChkFarMin], h[kChkFarMax]);
-    A->band_cap = choose_cap(kTile * std::max<int32_t>(h[kChkRowMax], 1));
+    A->band_cap = choose_cap(kTile * std::max<int32_t>(h[kChkRowMax], 1), 0);
     A->split = A->band == 0 && h[kChkFarMax] >= kSplitMinSpan;
     if (const char* env = std::getenv("SLA_CG_SCHEDULE")) {   // "fused" or "split" overrides the choice
         if (std::strcmp(env, "fused") == 0) A->split = false;
@@ -1241,7 +1242,7 @@ sla_status sla_csr_analysis(const sla_csr* A, int32_t* row_max, int32_t* tile_ma
     if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
     if (row_max) *row_max = A->row_max;
     if (tile_max) *tile_max = A->tile_max;
-    if (spmv_cap) *spmv_cap = A->band > 0 ? A->band_cap : A->cap;
+    if (spmv_cap) *spmv_cap = std::min(A->band > 0 ? A->band_cap : A->cap, kCapLarge);
     if (band_stride) *band_stride = A->band;
     if (cg_split) *cg_split = A->split ? 1 : 0;
     return SLA_OK;

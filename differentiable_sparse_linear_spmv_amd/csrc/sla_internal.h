@@ -18,6 +18,11 @@ constexpr int kTile = 256;    // CSR rows per tile: one row per lane
 constexpr int kCapSmall = 1280;   // 5 entries per row
 constexpr int kCapMid = 2048;     // 8 per row
 constexpr int kCapLarge = 4096;   // 16 per row
+// Patterns with a row of more than kBinLaneMax entries take the products-first variant
+// of the staged kernels (LDS of kCapLarge entries): every entry's product is formed in
+// parallel over the workgroup into LDS, then each lane sums its row's products in order.
+constexpr int kBinLaneMax = 32;
+constexpr int kCapSkew = kCapLarge + 1;
 
 // Banded patterns (every entry within kBandHalo of the diagonal or of distance S from
 // it) take the line-walking SpMV; its segments extend kBandHalo past each strip end.

@@ -226,6 +226,203 @@ struct GatherX {
     __device__ __forceinline__ double operator()(int64_t c) const { return ldv<OFF32>(x, c); }
 };
 
+// Row-length bins of a tile whose entries exceed the LDS cap.
+constexpr int kBinLaneMax = 32;     // rows of at most this many entries: one lane per row
+constexpr int kBinGroupMax = 512;   // then one 16-lane group per row; longer rows: the workgroup
+constexpr int kBinGroup = 16;
+constexpr int kBinUnroll = 8;       // gathers in flight per lane in the group and workgroup bins
+
+// Sum over a 16-lane group (lanes of one group only), fixed xor tree.
+__device__ __forceinline__ double group16_sum(double v)
+{
+#pragma unroll
+    for (int off = kBinGroup / 2; off > 0; off >>= 1) v = v + __shfl_xor(v, off, kBinGroup);
+    return v;
+}
+
+// This lane's share of a row: entries ra + lane0, ra + lane0 + stride, ... < re, summed
+// in that order, kBinUnroll gathers in flight (clamped addresses, masked sums).
+template <typename RP, typename G>
+__device__ __forceinline__ double strided_rowpart(const int32_t* __restrict__ col, const double* __restrict__ vals,
+                                                  int64_t ra, int64_t re, int lane0, int stride, const G& g)
+{
+    double acc = 0.0;
+    for (int64_t k0 = ra + lane0; k0 < re; k0 += static_cast<int64_t>(stride) * kBinUnroll) {
+        double v[kBinUnroll], p[kBinUnroll];
+#pragma unroll
+        for (int u = 0; u < kBinUnroll; ++u) {
+            const int64_t k = k0 + static_cast<int64_t>(u) * stride;
+            const int64_t j = k < re ? k : k0;
+            v[u] = vals[j];
+            p[u] = g(col[j]);
+        }
+#pragma unroll
+        for (int u = 0; u < kBinUnroll; ++u) {
+            const bool ok = k0 + static_cast<int64_t>(u) * stride < re;
+            const double t = v[u] * p[u];
+            const double an = acc + t;
+            acc = ok ? an : acc;
+        }
+    }
+    return acc;
+}
+
+// Row sums of a tile whose entries exceed the LDS cap, binned by row length (the rows
+// are read from global memory, not staged):
+//   * at most kBinLaneMax entries: the row's own lane sums it sequentially in ascending
+//     entry order, RC gathers in flight -- the oracle's order, so these rows are exact;
+//   * up to kBinGroupMax: a 16-lane group per row (four rows per wave at a time), each
+//     lane summing the entries j = lane, lane + 16, ... of the row in order, then a
+//     fixed xor tree over the group;
+//   * longer rows: the whole workgroup per row, one after the other, each thread summing
+//     the entries j = tid, tid + 256, ... in order, then the fixed workgroup tree.
+// Group and workgroup rows are listed in LDS (s_col) by an atomic append: which group
+// takes a row varies, but each row's sum does not.  Every thread of the workgroup must
+// call it (workgroup barriers); s_val holds kTile doubles, s_col kTile + 2 ints.
+template <typename RP, int RC, typename G>
+__device__ __forceinline__ double tile_rowsum_long(const RP* __restrict__ rp, const int32_t* __restrict__ col,
+                                                const double* __restrict__ vals, int64_t row0, int nr,
+                                                const G& g, double* s_val, int32_t* s_col)
+{
+    __shared__ double s_red[kBlock / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    int32_t* s_list = s_col;              // [0, n_grp): group rows; from the top down: workgroup rows
+    int32_t* s_cnt = s_col + kTile;       // [0] group rows, [1] workgroup rows
+    double* s_q = s_val;
+    if (tid < 2) s_cnt[tid] = 0;
+    __syncthreads();
+    const int tl = min(tid, nr - 1);
+    const int64_t a = ld_rp(rp, row0 + tl);
+    const int64_t e = (tid < nr) ? ld_rp(rp, row0 + tl + 1) : a;
+    const int64_t len = e - a;
+    double s = 0.0;
+    if (len > kBinLaneMax) {
+        if (len > kBinGroupMax) s_list[kTile - 1 - atomicAdd(&s_cnt[1], 1)] = tid;
+        else s_list[atomicAdd(&s_cnt[0], 1)] = tid;
+    } else {
+        for (int64_t j0 = a; j0 < e; j0 += RC) {
+            double pv[RC], vv[RC];
+#pragma unroll
+            for (int u = 0; u < RC; ++u) {
+                const int64_t j = (j0 + u < e) ? j0 + u : j0;
+                vv[u] = vals[j];
+                pv[u] = g(col[j]);
+            }
+#pragma unroll
+            for (int u = 0; u < RC; ++u) {
+                const bool ok = j0 + u < e;
+                const double t = vv[u] * pv[u];
+                const double sn = s + t;
+                s = ok ? sn : s;
+            }
+        }
+    }
+    __syncthreads();
+    const int n_grp = s_cnt[0], n_wg = s_cnt[1];
+    // 16-lane groups: group gi of the workgroup takes rows gi, gi + 16, ... of the list
+    const int sub = lane & (kBinGroup - 1);
+    const int gi = tid / kBinGroup;
+    constexpr int kGroups = kBlock / kBinGroup;
+    for (int base = 0; base < n_grp; base += kGroups) {   // uniform trip count
+        const int li = base + gi;
+        const int rr = li < n_grp ? s_list[li] : -1;
+        double acc = 0.0;
+        if (rr >= 0) acc = strided_rowpart<RP>(col, vals, ld_rp(rp, row0 + rr), ld_rp(rp, row0 + rr + 1), sub,
+                                               kBinGroup, g);
+        acc = group16_sum(acc);
+        if (rr >= 0 && sub == 0) s_q[rr] = acc;
+    }
+    // the longest rows: the whole workgroup on each
+    for (int wi = 0; wi < n_wg; ++wi) {
+        const int rr = s_list[kTile - 1 - wi];
+        double acc = strided_rowpart<RP>(col, vals, ld_rp(rp, row0 + rr), ld_rp(rp, row0 + rr + 1), tid, kBlock, g);
+        acc = block_sum(acc, s_red);
+        if (tid == 0) s_q[rr] = acc;
+    }
+    __syncthreads();
+    if (len > kBinLaneMax) s = s_q[tid];
+    __syncthreads();
+    return (tid < nr) ? s : 0.0;
+}
+
+// Rows of more than this many entries are summed by the workgroup in the
+// products-first kernels (a fixed tree); shorter ones by their own lane, in order.
+constexpr int kBinSeqMax = 1024;
+
+// Row sums of one tile, products first (patterns with a row of more than kBinLaneMax
+// entries).  The tile's entries go through LDS in chunks of kCapLarge: per chunk every
+// thread forms the products of entries j = tid, tid + kBlock, ... (values and columns
+// loaded coalesced, all gathers in flight at once, spread evenly whatever the row
+// lengths) and stores them; then each lane adds its row's products of the chunk in
+// ascending order, carrying its sum across chunks.  The products are the rounded
+// val * x[col] and the order ascending, so rows of up to kBinSeqMax entries get the
+// oracle's sums to the bit; longer rows are summed by the whole workgroup (each
+// thread's strided share in order, then the fixed tree).  Every thread of the
+// workgroup must call it (workgroup barriers); s_val holds kCapLarge doubles, s_col
+// kTile + 2 ints.
+template <typename RP, typename G>
+__device__ __forceinline__ double tile_rowsum_pf(const RP* __restrict__ rp, const int32_t* __restrict__ col,
+                                              const double* __restrict__ vals, int64_t row0, int nr, const G& g,
+                                              double* s_val, int32_t* s_col)
+{
+    __shared__ double s_red[kBlock / 64];
+    constexpr int C = kCapLarge;
+    constexpr int U = C / kBlock;
+    const int tid = threadIdx.x;
+    const int64_t k0 = ld_rp(rp, row0);
+    const int64_t cnt = ld_rp(rp, row0 + nr) - k0;
+    const int tl = min(tid, nr - 1);
+    const int64_t rs = ld_rp(rp, row0 + tl) - k0;
+    const int64_t re = (tid < nr) ? ld_rp(rp, row0 + tl + 1) - k0 : rs;
+    const bool lng = re - rs > kBinSeqMax;
+    double s = 0.0;
+    for (int64_t c0 = 0; c0 < cnt; c0 += C) {   // uniform trip count
+        const int clen = static_cast<int>(min(static_cast<int64_t>(C), cnt - c0));
+        const double* __restrict__ vb = vals + k0 + c0;
+        const int32_t* __restrict__ cb = col + k0 + c0;
+        double v[U], pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(tid + u * kBlock, clen - 1);
+            v[u] = vb[j];
+            pv[u] = g(cb[j]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = tid + u * kBlock;
+            if (j < clen) s_val[j] = v[u] * pv[u];
+        }
+        __syncthreads();
+        if (!lng) {
+            const int a0 = static_cast<int>(max(rs - c0, int64_t(0)));
+            const int a1 = static_cast<int>(min(re - c0, static_cast<int64_t>(clen)));
+#pragma unroll 4
+            for (int j = a0; j < a1; ++j) s = s + s_val[j];
+        }
+        __syncthreads();
+    }
+    if (__syncthreads_or(lng)) {
+        int32_t* s_list = s_col;
+        int32_t* s_cnt = s_col + kTile;
+        if (tid == 0) s_cnt[0] = 0;
+        __syncthreads();
+        if (lng) s_list[atomicAdd(&s_cnt[0], 1)] = tid;
+        __syncthreads();
+        const int n_long = s_cnt[0];
+        for (int wi = 0; wi < n_long; ++wi) {
+            const int rr = s_list[wi];
+            double acc = strided_rowpart<RP>(col, vals, ld_rp(rp, row0 + rr), ld_rp(rp, row0 + rr + 1), tid, kBlock, g);
+            acc = block_sum(acc, s_red);
+            if (tid == 0) s_val[rr] = acc;
+        }
+        __syncthreads();
+        if (lng) s = s_val[tid];
+        __syncthreads();
+    }
+    return (tid < nr) ? s : 0.0;
+}
+
 // Row sums of one tile [row0, row0 + nr) for lane tid (0 for tid >= nr).  Contains
 // the workgroup barriers of the LDS staging; every thread of the workgroup must call it.
 // Loads are never behind a divergent branch: out-of-range slots re-read a valid
@@ -236,6 +433,7 @@ __device__ __forceinline__ double tile_rowsum(const RP* __restrict__ rp, const i
                                               const double* __restrict__ vals, int64_t row0, int nr,
                                               const G& g, double* s_val, int32_t* s_col)
 {
+    if constexpr (CAP == kCapSkew) return tile_rowsum_pf<RP>(rp, col, vals, row0, nr, g, s_val, s_col);
     const int tid = threadIdx.x;
     const int64_t k0 = ld_rp(rp, row0);
     const int64_t k1 = ld_rp(rp, row0 + nr);
@@ -286,52 +484,8 @@ __device__ __forceinline__ double tile_rowsum(const RP* __restrict__ rp, const i
         }
         __syncthreads();
     } else {
-        // Wave per row: lanes stride over the row's entries, fixed-order shuffle sum.
-        const int lane = tid & 63;
-        const int w = tid >> 6;
-        double* s_q = s_val;   // nr <= kTile doubles, CAP >= kTile
-        for (int rr = w; rr < nr; rr += kBlock / 64) {
-            const int64_t a = ld_rp(rp, row0 + rr);
-            const int64_t e = ld_rp(rp, row0 + rr + 1);
-            double acc = 0.0;
-            for (int64_t kk = a + lane; kk < e; kk += 64) {
-                const double t = vals[kk] * g(col[kk]);
-                acc = acc + t;
-            }
-            acc = wave_sum(acc);
-            if (lane == 0) s_q[rr] = acc;
-        }
-        __syncthreads();
-        if (tid < nr) s = s_q[tid];
-        __syncthreads();
+        s = tile_rowsum_long<RP, RC>(rp, col, vals, row0, nr, g, s_val, s_col);
     }
-    return s;
-}
-
-// Row sums of a tile whose entries exceed the LDS cap: wave per row, lanes stride
-// over the row's entries, fixed-order shuffle sum.  Contains workgroup barriers.
-template <typename RP, typename G>
-__device__ __forceinline__ double tile_rowsum_long(const RP* __restrict__ rp, const int32_t* __restrict__ col,
-                                                const double* __restrict__ vals, int64_t row0, int nr,
-                                                const G& g, double* s_q)
-{
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
-    for (int rr = w; rr < nr; rr += kBlock / 64) {
-        const int64_t a = ld_rp(rp, row0 + rr);
-        const int64_t e = ld_rp(rp, row0 + rr + 1);
-        double acc = 0.0;
-        for (int64_t kk = a + lane; kk < e; kk += 64) {
-            const double t = vals[kk] * g(col[kk]);
-            acc = acc + t;
-        }
-        acc = wave_sum(acc);
-        if (lane == 0) s_q[rr] = acc;
-    }
-    __syncthreads();
-    const double s = (tid < nr) ? s_q[tid] : 0.0;
-    __syncthreads();
     return s;
 }
 
@@ -585,7 +739,8 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
         S.xi = x[i];
     }
     const int64_t cnt = k1 - k0;
-    if (cnt <= CAP && cnt > 0) {
+    // (the products-first variant reads its entries itself, chunk by chunk)
+    if (CAP != kCapSkew && cnt <= CAP && cnt > 0) {
         const double* __restrict__ vb = vals + k0;
         const int last = static_cast<int>(cnt) - 1;
         if constexpr (C16) {
@@ -733,7 +888,12 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
         }
         double s = 0.0;
         const double ri = cur.ri, ppi = cur.ppi, xi = cur.xi;
-        if (cnt <= CAP) {
+        if constexpr (CAP == kCapSkew) {
+            s = tile_rowsum_pf<RP>(rp, col, vals, row0, nr, g, s_val, s_col);
+            if (tn < ntiles)
+                stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x,
+                                                       tile_of(tn), n, k0n, k1n);
+        } else if (cnt <= CAP) {
             const int32_t cbase = C16 ? static_cast<int32_t>(row0) : 0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -785,7 +945,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
             }
             __syncthreads();
         } else {
-            s = tile_rowsum_long(rp, col, vals, row0, nr, g, s_val);
+            s = tile_rowsum_long<RP, RC>(rp, col, vals, row0, nr, g, s_val, s_col);
             if (tn < ntiles)
                 stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
                                                   k0n, k1n);
@@ -3713,6 +3873,7 @@ CgKernel spmv_kernel_rp(int cap)
 {
     if (cap <= kCapSmall) return k_cg_spmv<RP, kCapSmall, O, MODE, C16>;
     if (cap <= kCapMid) return k_cg_spmv<RP, kCapMid, O, MODE, C16>;
+    if (cap == kCapSkew) return k_cg_spmv<RP, kCapSkew, O, MODE, C16>;
     return k_cg_spmv<RP, kCapLarge, O, MODE, C16>;
 }
 
@@ -3757,6 +3918,8 @@ hipError_t launch_matvec_rp(const RP* rp, const int32_t* col, const double* vals
         SLA_LAUNCH((k_matvec<RP, kCapSmall, O>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
     else if (cap <= kCapMid)
         SLA_LAUNCH((k_matvec<RP, kCapMid, O>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
+    else if (cap == kCapSkew)
+        SLA_LAUNCH((k_matvec<RP, kCapSkew, O>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
     else
         SLA_LAUNCH((k_matvec<RP, kCapLarge, O>), grid, block, 0, s, rp, col, vals, x, y, n_rows, nnz, n_cols);
     return hipGetLastError();
@@ -3778,9 +3941,9 @@ hipError_t launch_matvec_any(const RP* rp, const int32_t* col, const double* val
 // ----------------------------------------------------------------------------------
 int cg_blocks_per_cu(int rp_bits, int cap, int64_t n, bool split)
 {
-    static int cache[2][3][2][2] = {};   // occupancy is fixed per variant: query once
+    static int cache[2][4][2][2] = {};   // occupancy is fixed per variant: query once
     const int ri = rp_bits == 64 ? 1 : 0;
-    const int ci = cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : 2);
+    const int ci = cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : (cap == kCapSkew ? 3 : 2));
     const bool o = off32_ok(n);
     int& c = cache[ri][ci][o ? 1 : 0][split ? 1 : 0];
     if (c > 0) return c;
@@ -3923,9 +4086,9 @@ hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s)
 
 int bs_blocks_per_cu(int rp_bits, int cap, int64_t n)
 {
-    static int cache[2][3][2] = {};
+    static int cache[2][4][2] = {};
     const int ri = rp_bits == 64 ? 1 : 0;
-    const int ci = cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : 2);
+    const int ci = cap <= kCapSmall ? 0 : (cap <= kCapMid ? 1 : (cap == kCapSkew ? 3 : 2));
     const bool o = off32_ok(n);
     int& c = cache[ri][ci][o ? 1 : 0];
     if (c > 0) return c;

@@ -579,3 +579,41 @@ def test_grf_marginal_variance():
     g = np.stack([W.gaussian_random_field(66, 1 / 65, 0.1, 1.0, rng) for _ in range(40)])
     var = float(np.mean(g ** 2))
     assert 0.8 < var < 1.2
+
+
+def test_graph_laplacian_generator_invariants():
+    # L + I of a weighted power-law graph: symmetric, every row sums to 1, columns
+    # strictly ascending, positive definite (smallest eigenvalue 1: L 1 = 0), and the
+    # row lengths skewed (hubs far above the median)
+    A = W.graph_laplacian(3000, avg_deg=10.0, gamma=2.1, seed=5)
+    M = sp.csr_matrix((A.vals, A.col, A.row_ptr), shape=(A.n_rows,) * 2)
+    assert abs(M - M.T).max() == 0.0
+    assert np.max(np.abs(M @ np.ones(A.n_rows) - 1.0)) <= 1e-12 * np.max(np.abs(A.vals))
+    rows = np.repeat(np.arange(A.n_rows), np.diff(A.row_ptr.astype(np.int64)))
+    same_row = rows[1:] == rows[:-1]
+    assert np.all(A.col[1:][same_row] > A.col[:-1][same_row])
+    lens = np.diff(A.row_ptr.astype(np.int64))
+    assert lens.max() >= 30 * np.median(lens)
+    off = A.vals[A.col != rows]
+    assert np.all((off <= -0.5) & (off >= -1.5))
+    small = W.graph_laplacian(300, avg_deg=6.0, gamma=2.1, seed=2)
+    D = sp.csr_matrix((small.vals, small.col, small.row_ptr), shape=(300, 300)).toarray()
+    ev = np.linalg.eigvalsh(D)
+    assert abs(ev[0] - 1.0) <= 1e-12 * ev[-1] and ev[-1] <= 2.0 * np.max(np.diag(D)) + 1.0
+
+
+def test_cg_and_adjoint_vs_dense_lu_on_a_graph_laplacian():
+    # the skewed pattern through the oracle: CG and the adjoint against dense solves
+    A = W.graph_laplacian(400, avg_deg=8.0, gamma=2.1, seed=3)
+    D = sp.csr_matrix((A.vals, A.col, A.row_ptr), shape=(400, 400)).toarray()
+    b = W.rhs_normal(400, 1)
+    f = O.cg(A, b, rtol=1e-12)
+    x = np.linalg.solve(D, b)
+    assert f["state"] == O.CONVERGED
+    kappa = np.linalg.cond(D)
+    assert np.linalg.norm(f["x"] - x) <= kappa * 1e-12 * np.linalg.norm(x)
+    bw = O.solve_backward(A, f["x"], f["x"], symmetric=True, rtol=1e-12)
+    lam = np.linalg.solve(D.T, f["x"])
+    assert np.linalg.norm(bw["lam"] - lam) <= kappa * 1e-12 * np.linalg.norm(lam)
+    rows = np.repeat(np.arange(400), np.diff(A.row_ptr.astype(np.int64)))
+    assert np.allclose(bw["gvals"], -lam[rows] * f["x"][A.col], rtol=1e-9, atol=1e-12 * np.abs(lam).max())

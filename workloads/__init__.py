@@ -22,7 +22,7 @@ import numpy as np
 
 __all__ = [
     "CSR", "poisson5", "poisson5_torch", "varcoef_poisson5", "gaussian_random_field",
-    "fem_p1_batched", "convdiff5", "rhs_uniform", "rhs_normal", "config",
+    "fem_p1_batched", "convdiff5", "graph_laplacian", "rhs_uniform", "rhs_normal", "config",
 ]
 
 
@@ -326,6 +326,46 @@ def rhs_normal(n: int, seed: int = 0) -> np.ndarray:
     return np.random.default_rng(seed).standard_normal(n)
 
 
+def graph_laplacian(n: int, avg_deg: float = 8.0, gamma: float = 2.5, seed: int = 0) -> CSR:
+    """Weighted graph Laplacian + identity of a random power-law graph: an SPD system
+    with a skewed row-length distribution (a few rows with thousands of entries, most
+    with a handful).  The pages name graph Laplacians as the next validation target
+    (paperpeel page, section 5 "Limitations and future work"); this is the stand-in.
+
+    Graph (Chung-Lu): node i has weight w_i = (i + 1)^(-1 / (gamma - 1)); n avg_deg / 2
+    edges draw both endpoints independently with probability proportional to w; self
+    loops and repeated pairs are dropped, so degrees follow a power law with exponent
+    gamma.  Each edge gets a weight c_e ~ U[0.5, 1.5].  The node ids are a random
+    permutation (the hubs are scattered over the rows).  Matrix: A_ij = -c_e for every
+    edge e = {i, j}, A_ii = 1 + sum of the weights at i, so A = L + I (L the weighted
+    Laplacian, positive semidefinite) and every row of A sums to 1.  One seeded stream
+    draws the endpoints, the weights and the permutation, in that order.  Columns ascend
+    within a row; int32 indices.
+    """
+    rng = np.random.default_rng(seed)
+    w = (np.arange(n, dtype=np.float64) + 1.0) ** (-1.0 / (gamma - 1.0))
+    p = w / w.sum()
+    m = int(n * avg_deg / 2)
+    u = rng.choice(n, size=m, p=p)
+    v = rng.choice(n, size=m, p=p)
+    keep = u != v
+    lo, hi = np.minimum(u[keep], v[keep]), np.maximum(u[keep], v[keep])
+    key = np.unique(lo.astype(np.int64) * n + hi)
+    lo, hi = key // n, key % n
+    c = rng.uniform(0.5, 1.5, key.shape[0])
+    perm = rng.permutation(n)
+    lo, hi = perm[lo], perm[hi]
+    rows = np.concatenate([lo, hi, np.arange(n)])
+    cols = np.concatenate([hi, lo, np.arange(n)])
+    deg = np.bincount(lo, weights=c, minlength=n) + np.bincount(hi, weights=c, minlength=n)
+    vals = np.concatenate([-c, -c, 1.0 + deg])
+    order = np.lexsort((cols, rows))
+    rows, cols, vals = rows[order], cols[order], vals[order]
+    rp = np.zeros(n + 1, np.int64)
+    np.cumsum(np.bincount(rows, minlength=n), out=rp[1:])
+    return CSR(n, n, rp.astype(np.int32), cols.astype(np.int32), vals)
+
+
 # --------------------------------------------------------------------------------------
 # The five benchmark workloads, by name.  Each returns a dict with the CSR, the
 # right-hand side(s), the loss gradient rule and the solver settings.
@@ -355,6 +395,9 @@ def config(name: str, scale: int | None = None) -> dict:
     poisson_list64 a SparseTensorList of 64 five-point Poisson grids of sides 64, 67, ...,
                    253 (distinct patterns, 1.7M rows in all), b_i ~ N(0, 1) seed i, CG to
                    1e-8 + adjoint of sum_i 0.5 |x_i|^2.
+    graph1m        graph Laplacian + I of a power-law graph (:func:`graph_laplacian`,
+                   2^20 nodes, average degree 8, exponent 2.5, seed 0): skewed row
+                   lengths; b ~ N(0, 1) (seed 0), CG to 1e-8 + adjoint of 0.5 |x|^2.
     convdiff1024   nonsymmetric convection-diffusion (:func:`convdiff5`, W = 100) on
                    1024 x 1024, b ~ N(0, 1) (seed 0), BiCGStab to rtol 1e-8 forward and
                    on A^T in the adjoint, loss 0.5 |x|^2.
@@ -407,6 +450,11 @@ def config(name: str, scale: int | None = None) -> dict:
         A, _, _ = varcoef_poisson5(N, seed=0)
         X0 = np.stack([rhs_normal(N * N, 3 + r) for r in range(8)])
         return dict(name=name, A=A, X0=X0, k=8, which="largest", tol=1e-8, max_iter=5000, method="lobpcg")
+    if name == "graph1m":
+        n = scale or (1 << 20)
+        A = graph_laplacian(n, avg_deg=8.0, gamma=2.5, seed=0)
+        return dict(name=name, A=A, b=rhs_normal(n, 0), rtol=1e-8, atol=0.0, max_iter=100000,
+                    fixed=False, loss="half_sq")
     if name == "poisson13000":
         N = scale or 13000
         return dict(name=name, N=N, A=None, b=None, rtol=0.0, atol=0.0, max_iter=500,
