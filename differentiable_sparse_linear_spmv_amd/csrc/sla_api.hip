@@ -815,7 +815,17 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         if (spmv_bytes > kBandStreamBytes) per_cu = std::min(per_cu, dia ? kDiaBlocksPerCu : kBandBlocksPerCu);
         const int64_t target = std::max<int64_t>(1, (static_cast<int64_t>(A->n_cu) * per_cu) / batch);
         const int64_t bl = std::max<int64_t>(4, std::min<int64_t>(kBandBlockLines, strips * band_lines / target));
-        band_block = static_cast<int>(std::min<int64_t>(band_lines, bl));
+        // Within [bl / 2, bl], the block length whose busiest workgroup walks the fewest
+        // lines (ties to the longer blocks, which restart the pipeline less often): blocks
+        // that do not divide evenly over the grid leave most workgroups idle at the end.
+        int64_t best_b = 0, best_cost = 0;
+        for (int64_t bb = bl; bb >= std::max<int64_t>(4, bl / 2); --bb) {
+            const int64_t nb = strips * ((band_lines + bb - 1) / bb);
+            const int64_t g = std::min<int64_t>(nb, target);
+            const int64_t cost = ((nb + g - 1) / g) * bb;
+            if (best_b == 0 || cost < best_cost) best_b = bb, best_cost = cost;
+        }
+        band_block = static_cast<int>(std::min<int64_t>(band_lines, best_b));
         const int64_t nblk = strips * ((band_lines + band_block - 1) / band_block);
         G = static_cast<int>(std::min<int64_t>(nblk, target));
         cap = band_cap;

@@ -1076,11 +1076,14 @@ struct SegLoad {
 };
 
 // Every lane issues the same number of loads (the lanes past the segment's end re-read
-// its last position), so the compiler's counts of loads in flight are exact.
+// its last position), so the compiler's counts of loads in flight are exact.  A segment
+// that is not `live` (issued only to keep those counts) has every lane read one
+// position: a few cache lines instead of the segment.
 __device__ __forceinline__ void seg_issue(SegLoad& L, const double* __restrict__ rin,
-                                          const double* __restrict__ pprev, int32_t e0, int32_t n)
+                                          const double* __restrict__ pprev, int32_t e0, int32_t n, bool live = true)
 {
-    const int tid = threadIdx.x;
+    const int32_t keep = -static_cast<int32_t>(live);   // all ones or zero: a mask, not a branch
+    const int tid = threadIdx.x & keep;
     const int32_t e = min(max(e0 + tid, 0), n - 1);
     L.r0 = ld32(rin, e);
     L.pp0 = ld32(pprev, e);
@@ -1092,22 +1095,27 @@ __device__ __forceinline__ void seg_issue(SegLoad& L, const double* __restrict__
 // Form p_k on the segment and store it (positions outside [0, n) hold 0; no column
 // points there).  The segment's own positions [kBandHalo, kBandHalo + kTile) also keep
 // p_{k-1} in s_pp (when given), for the deferred x update of that line's rows.
+//
+// Every lane forms its halo value too, and stores it without a branch: a lane past the
+// halo stores it to its own main position, which its next store overwrites (one lane's
+// LDS stores land in program order).  A halo store behind a branch lets the compiler
+// sink the two halo loads into that branch, where their wait also drains every load
+// issued after them (the next windows' loads, in the pipelined kernels' prologues).
 __device__ __forceinline__ void seg_commit(const SegLoad& L, double* s_seg, double* s_pp, double beta, int32_t e0,
                                            int32_t n)
 {
     const int tid = threadIdx.x;
+    const bool halo = tid < 2 * kBandHalo;
     const int32_t e = e0 + tid;
+    const int32_t e1 = e + kTile;
+    const double t1 = beta * L.pp1;
+    const double v1 = L.r1 + t1;
+    s_seg[halo ? tid + kTile : tid] = (e1 >= 0 && e1 < n) ? v1 : 0.0;
     const double t0 = beta * L.pp0;
     const double v0 = L.r0 + t0;
     s_seg[tid] = (e >= 0 && e < n) ? v0 : 0.0;
     if (s_pp && tid >= kBandHalo) s_pp[tid - kBandHalo] = L.pp0;
-    if (tid < 2 * kBandHalo) {
-        const int32_t e1 = e + kTile;
-        const double t1 = beta * L.pp1;
-        const double v1 = L.r1 + t1;
-        s_seg[tid + kTile] = (e1 >= 0 && e1 < n) ? v1 : 0.0;
-        if (s_pp && tid < kBandHalo) s_pp[tid + kTile - kBandHalo] = L.pp1;
-    }
+    if (s_pp && tid < kBandHalo) s_pp[tid + kTile - kBandHalo] = L.pp1;
 }
 
 // Registers of one staged window: its entries, this lane's row bounds and x, and the
@@ -1150,11 +1158,18 @@ struct BandWalk {
 
 // Issue the loads of window l (entries [k0, k1), row bounds, x) and of segment l + 1.
 // C16: the columns come as 16-bit offsets from the window's first row (sign-extended
-// by the load itself), which is what band_operand needs.
+// by the load itself), which is what band_operand needs.  A window past the block's
+// last line l1 is issued only to keep the load counts exact: its entry range is empty
+// (one entry read) and its segment reads one position of the block's last segment.
+// Its row bounds and x are still the window's (clamping those rows as well made the
+// compiler reuse registers of loads in flight at the next block's start, and wait for
+// all of them there).
 template <int U, bool C16>
-__device__ __forceinline__ void band_stage(const BandWalk& W, BandStage<U>& B, int32_t l, int32_t k0, int32_t k1)
+__device__ __forceinline__ void band_stage(const BandWalk& W, BandStage<U>& B, int32_t l, int32_t l1, int32_t k0,
+                                           int32_t k1)
 {
     const int tid = threadIdx.x;
+    const bool live = l < l1;
     const int nr = W.rows(l);
     const int32_t i = min(W.base(l) + min(tid, max(nr - 1, 0)), W.n - 1);
     const int32_t* __restrict__ rpi = W.rp + i;
@@ -1183,7 +1198,7 @@ __device__ __forceinline__ void band_stage(const BandWalk& W, BandStage<U>& B, i
             B.c[u] = ld_stream(cb + j);
         }
     }
-    seg_issue(B.seg, W.rin, W.pprev, W.base(l + 1) - kBandHalo, W.n);
+    seg_issue(B.seg, W.rin, W.pprev, W.base(min(l, l1 - 1) + 1) - kBandHalo, W.n, live);
 }
 
 // LDS of one staged window besides its entries: this lane's row bounds (relative to
@@ -1317,14 +1332,14 @@ __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_
     SegLoad Em, E0;   // segments of lines l0 - 1 and l0
     // entry ranges [k0, k1) of windows l, l + 1, l + 2
     int32_t k0a = W.k0(l0), k1a = W.k1(l0), k0b = 0, k1b = 0, k0c = 0, k1c = 0;
-    band_stage<U, C16>(W, SA, l0, k0a, k1a);
+    band_stage<U, C16>(W, SA, l0, l1, k0a, k1a);
     seg_issue(Em, W.rin, W.pprev, W.base(l0 - 1) - kBandHalo, n);
     seg_issue(E0, W.rin, W.pprev, W.base(l0) - kBandHalo, n);
     if (l0 + 1 < l1) {
         k0b = W.k0(l0 + 1);
         k1b = W.k1(l0 + 1);
     }
-    band_stage<U, C16>(W, SB, l0 + 1, k0b, k1b);
+    band_stage<U, C16>(W, SB, l0 + 1, l1, k0b, k1b);
     if (l0 + 2 < l1) {
         k0c = W.k0(l0 + 2);
         k1c = W.k1(l0 + 2);
@@ -1344,7 +1359,7 @@ __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_
 #define SLA_BAND_WINDOW(na, nb)                                                                            \
     {                                                                                                      \
         int32_t k0d = 0, k1d = 0;                                                                          \
-        band_stage<U, C16>(W, na, l + 2, k0c, k1c); /* past l1: harmless clamped loads, exact counts */ \
+        band_stage<U, C16>(W, na, l + 2, l1, k0c, k1c); /* past l1: one row, exact counts */          \
         if (l + 3 < l1) {                                                                                  \
             k0d = W.k0(l + 3);                                                                             \
             k1d = W.k1(l + 3);                                                                             \
@@ -1383,12 +1398,23 @@ __device__ __forceinline__ void band_block(const BandWalk& W, int32_t l0, int32_
 // Deferred x update x_k = x_{k-1} + alpha_{k-1} p_{k-1} of the rows of every block a
 // workgroup of the line-walking SpMV owns (a system that stops at iteration k).
 // sw: positions per strip (kTile, or 2 kTile for the two-rows-per-lane kernel).
+// First block of workgroup lb in the persistent band grid (it then takes every G-th
+// block).  Workgroup lb runs on XCD lb mod 8; with G a multiple of 8, the G / 8
+// workgroups of one XCD take consecutive blocks of each round of G blocks, i.e.
+// neighbouring strips of a line block.  Where a grid line does not start on a 128-byte
+// boundary, neighbouring strips share a cache line at their edge, and this way both
+// halves meet in one XCD's L2 (one fetch, one full-line write-back) instead of two.
+__device__ __forceinline__ int32_t band_first_block(int32_t lb, int32_t G)
+{
+    return (G & 7) ? lb : (lb & 7) * (G >> 3) + (lb >> 3);
+}
+
 __device__ __forceinline__ void band_stop_x(int32_t lb, int32_t G, int32_t nblk, int32_t strips, int32_t B,
                                             int32_t lines, int32_t S, int32_t n, double alpha_prev,
                                             const double* __restrict__ pprev, double* __restrict__ x,
                                             int32_t sw = kTile)
 {
-    for (int32_t b = lb; b < nblk; b += G) {
+    for (int32_t b = band_first_block(lb, G); b < nblk; b += G) {
         const int32_t j = b % strips;
         const int32_t l0 = (b / strips) * B;
         const int32_t l1 = min(l0 + B, lines);
@@ -1406,9 +1432,9 @@ __device__ __forceinline__ void band_stop_x(int32_t lb, int32_t G, int32_t nblk,
 }
 
 // Grid: (G, batch).  The blocks (strip j, lines [c B, c B + B)) are numbered
-// c * strips + j, and workgroup lb takes blocks lb, lb + G, ...: the workgroups in flight
-// cover consecutive blocks, so they stream one front of about G / strips * B lines
-// through memory together.
+// c * strips + j, and workgroup lb takes every G-th block from band_first_block(lb, G):
+// the workgroups in flight cover consecutive blocks, so they stream one front of about
+// G / strips * B lines through memory together.
 template <int CAP, bool C16>
 __global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
 {
@@ -1450,7 +1476,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_band(CgArgs a, int64_t k)
     double* __restrict__ q = a.q + off;
     double sig = 0.0;
 #pragma unroll 1
-    for (int32_t b = lb; b < nblk; b += a.G) {
+    for (int32_t b = band_first_block(lb, a.G); b < nblk; b += a.G) {
         const int32_t j = b % strips;
         const int32_t l0 = (b / strips) * B;
         W.pos0 = j * kTile;
@@ -1582,22 +1608,27 @@ __device__ __forceinline__ T ld32_stream(const T* __restrict__ base, int32_t e)
 }
 
 // Issue the loads of window l (every load unconditional: slots past nd re-read the
-// last diagonal, rows past the window re-read its last row; both are masked).
+// last diagonal, rows past the window re-read its last row; both are masked).  Windows
+// past the block's last line l1 are issued only to keep the pipeline's load counts
+// exact: every lane reads the first row of the block's last window (and one position of
+// the segment below it), which the last real stage has just brought into the cache.
 // The diagonals' bases are separate uniform pointers (one scalar base per load, the
 // row as a 32-bit offset), which keeps 64-bit address arithmetic out of the vector
 // registers the loads in flight are writing.
 template <int ND, bool M16>
-__device__ __forceinline__ void dia_stage(const DiaWalk<ND>& W, DiaStage<ND>& B, int32_t l)
+__device__ __forceinline__ void dia_stage(const DiaWalk<ND>& W, DiaStage<ND>& B, int32_t l, int32_t l1)
 {
     const int tid = threadIdx.x;
-    const int nr = W.rows(l);
-    const int32_t i = min(W.base(l) + min(tid, max(nr - 1, 0)), W.n - 1);
+    const bool live = l < l1;
+    const int32_t ll = min(l, l1 - 1);
+    const int nr = W.rows(ll) & -static_cast<int>(live);   // a mask, not a branch
+    const int32_t i = min(W.base(ll) + min(tid, max(nr - 1, 0)), W.n - 1);
 #pragma unroll
     for (int d = 0; d < ND; ++d) B.v[d] = ld32_stream(W.vd[d], i);
     if constexpr (M16) B.m = ld32_stream(static_cast<const uint16_t*>(W.mask), i);
     else B.m = ld32_stream(static_cast<const uint8_t*>(W.mask), i);
     B.xi = ld32(W.x, i);
-    seg_issue(B.seg, W.rin, W.pprev, W.base(l + 1) - kBandHalo, W.n);
+    seg_issue(B.seg, W.rin, W.pprev, W.base(ll + 1) - kBandHalo, W.n, live);
 }
 
 // LDS of one committed window of the diagonal-layout SpMV: its rows' values by
@@ -1626,7 +1657,8 @@ __device__ __forceinline__ void dia_commit(const DiaWalk<ND>& W, const DiaStage<
 // One block: lines [l0, l1) of the strip W describes, pipelined as band_block: while
 // window l is summed from LDS, the loads of windows l + 1 and l + 2 (values, masks, x,
 // segments l + 2 and l + 3) are in flight in the two stage buffers, which alternate in
-// place (the loop is unrolled by two).
+// place (the loop is unrolled by two).  A third buffer (three windows in flight) and
+// two workgroups per CU both measured slower at 169M rows.
 template <int ND, bool M16>
 __device__ __forceinline__ void dia_block(const DiaWalk<ND>& W, const CgArgs& a, int32_t l0, int32_t l1, double* s_p,
                                           double* s_pp, DiaRows<ND>* R, double beta, double alpha_prev,
@@ -1637,10 +1669,10 @@ __device__ __forceinline__ void dia_block(const DiaWalk<ND>& W, const CgArgs& a,
     const int32_t n = W.n;
     DiaStage<ND> SA, SB;
     SegLoad Em, E0;
-    dia_stage<ND, M16>(W, SA, l0);
+    dia_stage<ND, M16>(W, SA, l0, l1);
     seg_issue(Em, W.rin, W.pprev, W.base(l0 - 1) - kBandHalo, n);
     seg_issue(E0, W.rin, W.pprev, W.base(l0) - kBandHalo, n);
-    dia_stage<ND, M16>(W, SB, l0 + 1);
+    dia_stage<ND, M16>(W, SB, l0 + 1, l1);
     int sp = 0, so = 1, sn = 2, po = 0;
     seg_commit(Em, s_p + sp * kSeg, nullptr, beta, W.base(l0 - 1) - kBandHalo, n);
     seg_commit(E0, s_p + so * kSeg, s_pp + po * kTile, beta, W.base(l0) - kBandHalo, n);
@@ -1653,7 +1685,7 @@ __device__ __forceinline__ void dia_block(const DiaWalk<ND>& W, const CgArgs& a,
     // includes them).
 #define SLA_DIA_WINDOW(na, nb)                                                                            \
     {                                                                                                     \
-        dia_stage<ND, M16>(W, na, l + 2); /* past l1: harmless clamped loads, exact counts */            \
+        dia_stage<ND, M16>(W, na, l + 2, l1); /* past l1: one row, exact counts */                        \
         double s = 0.0;                                                                                   \
         const uint32_t msk = R->m[tid];                                                                   \
         _Pragma("unroll") for (int d = 0; d < ND; ++d)                                                    \
@@ -1739,7 +1771,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_dia(CgArgs a, int64_t k)
     double* __restrict__ q = a.q + off;
     double sig = 0.0;
 #pragma unroll 1
-    for (int32_t b = lb; b < nblk; b += a.G) {
+    for (int32_t b = band_first_block(lb, a.G); b < nblk; b += a.G) {
         const int32_t j = b % strips;
         const int32_t l0 = (b / strips) * B;
         W.pos0 = j * kTile;
