@@ -33,7 +33,7 @@ KERNEL_NAMES = ["cg_init", "cg_spmv", "cg_update", "matvec", "pattern_outer", "g
                 "lz_ritz", "lob_spmm", "lob_gram", "lob_comb"]
 
 EXPORTS = [
-    "sla_set_allocator", "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_csr_col_bits", "sla_csr_diagonals", "sla_matvec", "sla_matvec_backward",
+    "sla_set_allocator", "sla_csr_create", "sla_csr_destroy", "sla_csr_info", "sla_csr_analysis", "sla_csr_col_bits", "sla_csr_diagonals", "sla_csr_group_window", "sla_matvec", "sla_matvec_backward",
     "sla_solve", "sla_solve_backward", "sla_list_create", "sla_list_destroy", "sla_list_info", "sla_list_col_bits", "sla_list_solve",
     "sla_list_solve_backward", "sla_eigsh", "sla_lobpcg", "sla_eigsh_backward", "sla_timing_enable",
     "sla_timing_reset", "sla_timing_collect", "sla_timing_query", "sla_timing_query_bytes", "sla_status_string",
@@ -110,6 +110,8 @@ def load():
     L.sla_csr_col_bits.restype = st
     L.sla_csr_diagonals.argtypes = [P, C.POINTER(i32)]
     L.sla_csr_diagonals.restype = st
+    L.sla_csr_group_window.argtypes = [P, C.POINTER(i32)]
+    L.sla_csr_group_window.restype = st
     L.sla_matvec.argtypes = [P, i64, P, P, P, P]
     L.sla_matvec.restype = st
     L.sla_matvec_backward.argtypes = [P, i64, P, P, P, P, P, P]

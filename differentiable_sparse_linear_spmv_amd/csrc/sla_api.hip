@@ -78,8 +78,10 @@ struct sla_csr {
     // the first grouped solve (SLA_CG_REORDER=0 turns it off): row pointers, columns, the
     // entry permutation and the row permutation (new -> caller's), all int32.
     bool reorder_ok = true;
+    bool g_win_ok = true;   // the grouped SpMV may keep its operand in an LDS window (SLA_GCG_WINDOW=0: never)
     bool g_reordered = false;
     int32_t *g_rp = nullptr, *g_col = nullptr, *g_eperm = nullptr, *g_perm = nullptr;
+    int32_t g_halo = 0;   // operand window of the grouped SpMV on the reordered pattern (0: none)
     // transposed pattern (lazily built unless SLA_SYMMETRIC)
     bool has_t = false;
     void* row_ptr_t = nullptr;
@@ -645,6 +647,13 @@ sla_status ensure_reorder(sla_csr* A, hipStream_t s)
         }
         rp2[i + 1] = rp2[i] + static_cast<int32_t>(row.size());
     }
+    // bandwidth of the reordered pattern: the grouped SpMV's operand window needs every
+    // column within g_halo rows of its row's tile
+    int64_t bw = 0;
+    for (int64_t i = 0; i < n; ++i)
+        for (int32_t k = rp2[i]; k < rp2[i + 1]; ++k) bw = std::max<int64_t>(bw, std::abs(col2[k] - i));
+    const int64_t halo = (bw + 63) / 64 * 64;
+    A->g_halo = halo <= kGWinMaxHalo ? static_cast<int32_t>(halo) : 0;
     auto release = [&]() {
         for (int32_t** q : {&A->g_rp, &A->g_col, &A->g_eperm, &A->g_perm}) {
             if (*q) (void)dev_free(*q);
@@ -683,7 +692,14 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     // SpMV grid per group: with groups pinned to XCDs (groups % 8 == 0), the resident
     // workgroups of one XCD; otherwise an equal share of the GPU.
     const int gcap = static_cast<int64_t>(kBlock / kGroup) * A->row_max <= kGCapSmall ? kGCapSmall : kGCapLarge;
-    const int occ = cg_group_blocks_per_cu(gcap);
+    const bool reorder = A->reorder_ok;
+    if (reorder) {
+        const sla_status st0 = ensure_reorder(A, s);
+        if (st0 != SLA_OK) return st0;
+    }
+    // the operand window (k_gcg_spmv<..., true>) on a reordered pattern of small bandwidth
+    const int32_t win = reorder && A->g_win_ok ? A->g_halo : 0;
+    const int occ = cg_group_blocks_per_cu(gcap, win > 0);
     const bool pinned = groups >= 8 && groups % 8 == 0;
     int64_t P = pinned ? static_cast<int64_t>(A->n_cu / 8) * occ : (static_cast<int64_t>(A->n_cu) * occ) / groups;
     P = std::max<int64_t>(1, std::min<int64_t>(P, gtiles));
@@ -694,8 +710,6 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     sla_status st = ensure_workspace(A, batch, static_cast<int>(std::max(P, Pu)), &w,
                                      jacobi ? kMethodJacobi : kMethodCG);
     if (st != SLA_OK) return st;
-    const bool reorder = A->reorder_ok;
-    if (reorder && (st = ensure_reorder(A, s)) != SLA_OK) return st;
     const size_t xb = align256(sizeof(double) * static_cast<size_t>(n) * batch);
     const size_t need = xb + sizeof(double) * static_cast<size_t>(A->nnz) * batch;
     if (need > A->gws_bytes) {
@@ -747,6 +761,7 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     a.groups = groups;
     a.cap = gcap;
     a.xg = xg;
+    a.g_halo = win;
 
     hipError_t e = timed(SLA_K_GROUP_LAYOUT, s, [&] {
         return launch_group_vals(vals, vg, A->nnz, groups, reorder ? A->g_eperm : nullptr, s);
@@ -1163,6 +1178,7 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
     }
     if (const char* env = std::getenv("SLA_CG_GROUPED")) A->group_ok = std::strcmp(env, "0") != 0;
     if (const char* env = std::getenv("SLA_CG_REORDER")) A->reorder_ok = std::strcmp(env, "0") != 0;
+    if (const char* env = std::getenv("SLA_GCG_WINDOW")) A->g_win_ok = std::strcmp(env, "0") != 0;
     A->krp = d_row_ptr;
     A->krp_bits = row_ptr_bits;
     if (row_ptr_bits == 64 && nnz < (int64_t(1) << 31)) {
@@ -1269,6 +1285,13 @@ sla_status sla_csr_diagonals(const sla_csr* A, int32_t* n_diagonals)
 {
     if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
     if (n_diagonals) *n_diagonals = A->dia_nd;
+    return SLA_OK;
+}
+
+sla_status sla_csr_group_window(const sla_csr* A, int32_t* halo_rows)
+{
+    if (!A) return fail(SLA_ERR_INVALID_ARG, "handle is NULL");
+    if (halo_rows) *halo_rows = (A->g_reordered && A->reorder_ok && A->g_win_ok) ? A->g_halo : 0;
     return SLA_OK;
 }
 

@@ -53,6 +53,9 @@ constexpr int kGroupMinBatch = 8;
 // Entries per 64-row tile staged by the grouped SpMV: rows of at most 8 or 16 entries.
 constexpr int kGCapSmall = 512;
 constexpr int kGCapLarge = 1024;
+// The grouped SpMV keeps the operand in an LDS window when the (reordered) pattern's
+// bandwidth is at most this many rows (7 chunks of 64 rows on each side of a tile).
+constexpr int kGWinMaxHalo = 448;
 
 // Per-system solver state in device memory (80 bytes).  Double-buffered by the
 // parity of the iteration index so that a kernel reads the previous value while
@@ -110,6 +113,7 @@ struct CgArgs {
     int32_t groups;          // grouped batch: number of groups (r, p0, p1, q, vals, xg grouped)
     int32_t cap;             // grouped batch: entries per tile staged (kGCapSmall or kGCapLarge)
     double* xg;              // grouped batch: x in the grouped layout
+    int32_t g_halo;          // grouped batch: operand window halo (rows, a multiple of 64), 0 = no window
     const int32_t* gperm;    // grouped batch on a reordered pattern: row i is the caller's row gperm[i]
     // SparseTensorList (distinct patterns, packed block-diagonally; null otherwise):
     // system s owns tiles [list_tiles[s], list_tiles[s + 1]) and workgroups
@@ -251,7 +255,7 @@ LaunchEvents& launch_events();
 // sized to fill the GPU exactly once).
 int cg_blocks_per_cu(int rp_bits, int cap, int64_t n, bool split);
 int cg_band_blocks_per_cu(int cap);   // the banded SpMV (32-bit row pointers only)
-int cg_group_blocks_per_cu(int cap);   // the grouped SpMV
+int cg_group_blocks_per_cu(int cap, bool win);   // the grouped SpMV (win: the windowed variant)
 
 // Host-side launchers (defined in sla_kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_cg_init(const CgArgs& a, hipStream_t s);

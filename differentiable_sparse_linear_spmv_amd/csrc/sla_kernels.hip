@@ -82,11 +82,21 @@ __device__ __forceinline__ double block_sum(double v, double* s_red)
     return t;
 }
 
-// Deterministic sum of G partials written by the previous kernel.
+// Deterministic sum of G partials written by the previous kernel: thread t adds
+// part[t], part[t + kBlock], ... in that order, then the fixed workgroup tree.  The
+// loads of a trip of 8 (G <= 2048 in one trip) are all issued before the first is
+// added, so the reduction costs one memory round trip rather than one per partial.
 __device__ __forceinline__ double reduce_partials(const double* part, int G, double* s_red)
 {
+    constexpr int U = 8;
     double v = 0.0;
-    for (int i = threadIdx.x; i < G; i += kBlock) v = v + part[i];
+    for (int i0 = threadIdx.x; i0 < G; i0 += U * kBlock) {
+        double t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) t[u] = part[min(i0 + u * kBlock, G - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v = (i0 + u * kBlock < G) ? v + t[u] : v;
+    }
     return block_sum(v, s_red);
 }
 
@@ -3319,17 +3329,36 @@ __global__ __launch_bounds__(kBlock) void k_gcg_pupd(CgArgs a, int64_t k)
 // q = A p_k for the group's systems (p_k formed by k_gcg_pupd), partial p_k^T q.
 // Tiles of kGRows rows: the tile's entries (values of all kGroup systems, columns) are
 // one contiguous range, loaded coalesced and staged through LDS (the lanes of one row
-// read its entries there); only the operand is gathered from memory.  Pipelined like
-// the banded kernel: while tile t is summed, tile t + P's loads are in flight, every
-// load unconditional (clamped), and the outputs are stored after the next commit.
+// read its entries there).  Pipelined like the banded kernel: while tile t is summed,
+// the next tile's loads are in flight, every load unconditional (clamped), and the
+// outputs are stored after the next commit.
+//
+// The operand, two ways:
+//   * WIN = false: workgroup lb takes tiles lb, lb + P, ... and gathers p_k[col] of
+//     every entry from memory (through the XCD's L2, which holds the group's operand);
+//   * WIN = true (a pattern whose bandwidth, after the reordering, is at most
+//     kGWinMaxHalo rows): workgroup lb takes one contiguous run of tiles and keeps an
+//     LDS ring of the operand rows [row0 - H, row0 + kGRows + H) of its current tile, H =
+//     a.g_halo (a multiple of kGRows).  Every column of the tile's rows lies in that
+//     range, so the gathers are LDS reads; moving to the next tile loads one coalesced
+//     chunk of kGRows rows (all kGroup systems) into the ring, the chunk H rows past the
+//     next tile.  The first tile of a run fills the ring with 2 H / kGRows + 1 chunks.
+// Both give the same row sums (same products, same order); they differ in which
+// workgroup sums which rows, so the partials of p^T q are grouped differently.
 template <int CAPG>   // entries per tile (kGRows rows of at most CAPG / kGRows entries)
 struct GStage {
     double v[CAPG * kGroup / kBlock];
     int32_t c[CAPG / kBlock];
     int32_t a0, a1;
+    double w;   // WIN: this lane's element of the operand chunk the next tile brings in
 };
 
-template <int CAPG>
+constexpr int kGWinRows = 1024;   // operand ring (rows; a power of two, a multiple of kGRows)
+// Largest halo in chunks: a tile's 2 hc + 1 chunks must occupy distinct ring slots.
+constexpr int kGWinHaloChunks = (kGWinRows / kGRows - 1) / 2;
+static_assert(kGWinHaloChunks * kGRows == kGWinMaxHalo, "the host's window limit is the ring's");
+
+template <int CAPG, bool WIN>
 __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
 {
     constexpr int UV = CAPG * kGroup / kBlock;
@@ -3340,6 +3369,7 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
     __shared__ int32_t s_rs[kBlock], s_re[kBlock];
     __shared__ double s_red[4 * kGroup];
     __shared__ int64_t s_stop[kGroup];
+    __shared__ double s_win[WIN ? kGWinRows * kGroup : 1];
     const GroupCoord gc = group_coord(a, a.G);
     const int tid = threadIdx.x;
     const int sy = tid % kGroup;
@@ -3358,8 +3388,22 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
     const int32_t gtiles = (n + kGRows - 1) / kGRows;
     const int32_t P = a.G;
     const int32_t nnz = static_cast<int32_t>(a.nnz);
+    // tiles of this workgroup: t = tb, tb + ts, ... while t < te
+    const int32_t tb = WIN ? static_cast<int32_t>((static_cast<int64_t>(gc.lb) * gtiles) / P) : gc.lb;
+    const int32_t te = WIN ? static_cast<int32_t>((static_cast<int64_t>(gc.lb + 1) * gtiles) / P) : gtiles;
+    const int32_t ts = WIN ? 1 : P;
+    const int32_t hc = WIN ? a.g_halo / kGRows : 0;   // halo chunks on each side
     auto tk0 = [&](int32_t t) { return static_cast<int32_t>(ld_rp_uniform(rp, min(t * kGRows, n))); };
     auto tk1 = [&](int32_t t) { return static_cast<int32_t>(ld_rp_uniform(rp, min((t + 1) * kGRows, n))); };
+    // WIN: this lane's element of operand chunk c (rows c kGRows ...), clamped into range
+    auto chunk_ld = [&](int32_t c) __attribute__((always_inline)) {
+        const int32_t i = min(max(c * kGRows + tid / kGroup, 0), n - 1);
+        return pg[static_cast<int64_t>(i) * kGroup + sy];
+    };
+    auto chunk_st = [&](int32_t c, double v) __attribute__((always_inline)) {
+        const int32_t i = c * kGRows + tid / kGroup;   // may lie outside [0, n): never read then
+        s_win[(i & (kGWinRows - 1)) * kGroup + sy] = v;
+    };
     // issue the loads of tile t (entries [k0, k1)); clamped, so every lane issues them all
     auto stage = [&](GStage<CAPG>& S, int32_t t, int32_t k0, int32_t k1) __attribute__((always_inline)) {
         const int32_t i = min(t * kGRows + tid / kGroup, n - 1);
@@ -3371,11 +3415,12 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         const int32_t* __restrict__ cb = col + kb;
         const int lastv = max(cnt * kGroup - 1, 0), lastc = max(cnt - 1, 0);
         // the values (every system's, read once per SpMV) stream with the non-temporal
-        // hint, leaving the caches to the gathered operand
+        // hint, leaving the caches to the operand
 #pragma unroll
         for (int u = 0; u < UV; ++u) S.v[u] = __builtin_nontemporal_load(vb + min(tid + u * kBlock, lastv));
 #pragma unroll
         for (int u = 0; u < UC; ++u) S.c[u] = cb[min(tid + u * kBlock, lastc)];
+        if constexpr (WIN) S.w = chunk_ld(t + hc);   // the chunk this tile adds to the ring
     };
     auto commit = [&](const GStage<CAPG>& S, int32_t t, int32_t k0, int32_t k1) __attribute__((always_inline)) {
         const int32_t cnt = k1 - k0;
@@ -3392,11 +3437,16 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         const bool has = t * kGRows + tid / kGroup < n;
         s_rs[tid] = S.a0 - k0;
         s_re[tid] = has ? S.a1 - k0 : S.a0 - k0;
+        if constexpr (WIN) chunk_st(t + hc, S.w);
+    };
+    auto operand = [&](int32_t c) __attribute__((always_inline)) {
+        if constexpr (WIN) return s_win[(c & (kGWinRows - 1)) * kGroup + sy];
+        else return pg[static_cast<int64_t>(c) * kGroup + sy];
     };
 
     double sig = 0.0;
-    int32_t t = gc.lb;
-    if (t >= gtiles) {
+    int32_t t = tb;
+    if (t >= te) {
         sig = group_block_sum(sig, s_red);
         if (tid < kGroup) a.part_sigma[static_cast<int64_t>(sys0 + tid) * a.G + gc.lb] = sig;
         return;
@@ -3404,19 +3454,30 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
     GStage<CAPG> SA, SB;
     int32_t k0a = tk0(t), k1a = tk1(t), k0b = 0, k1b = 0;
     stage(SA, t, k0a, k1a);
-    if (t + P < gtiles) {
-        k0b = tk0(t + P);
-        k1b = tk1(t + P);
+    if constexpr (WIN) {
+        // the ring's first fill: chunks t - hc ... t + hc - 1 (stage brought t + hc),
+        // every load issued before the first store (unconditional: past 2 hc they
+        // repeat the last chunk)
+        double fill[2 * kGWinHaloChunks];
+#pragma unroll
+        for (int u = 0; u < 2 * kGWinHaloChunks; ++u) fill[u] = chunk_ld(t - hc + min(u, max(2 * hc - 1, 0)));
+#pragma unroll
+        for (int u = 0; u < 2 * kGWinHaloChunks; ++u)
+            if (u < 2 * hc) chunk_st(t - hc + u, fill[u]);
+    }
+    if (t + ts < te) {
+        k0b = tk0(t + ts);
+        k1b = tk1(t + ts);
     }
     commit(SA, t, k0a, k1a);
     __syncthreads();
 #define SLA_GCG_TILE(nxt)                                                                                  \
     {                                                                                                      \
-        stage(nxt, t + P, k0b, k1b); /* past the end: clamped loads, keeps the wait counts exact */       \
+        stage(nxt, t + ts, k0b, k1b); /* past the end: clamped loads, keeps the wait counts exact */      \
         int32_t k0c = 0, k1c = 0;                                                                          \
-        if (t + 2 * P < gtiles) {                                                                          \
-            k0c = tk0(t + 2 * P);                                                                          \
-            k1c = tk1(t + 2 * P);                                                                          \
+        if (t + 2 * ts < te) {                                                                             \
+            k0c = tk0(t + 2 * ts);                                                                         \
+            k1c = tk1(t + 2 * ts);                                                                         \
         }                                                                                                  \
         const int rs = s_rs[tid], re = s_re[tid];                                                          \
         double sum = 0.0;                                                                                  \
@@ -3424,7 +3485,7 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
             double pv[RC];                                                                                 \
             _Pragma("unroll") for (int u = 0; u < RC; ++u) {                                               \
                 const int j = (j0 + u < re) ? j0 + u : j0;                                                 \
-                pv[u] = pg[static_cast<int64_t>(s_col[j]) * kGroup + sy];                                  \
+                pv[u] = operand(s_col[j]);                                                                 \
             }                                                                                              \
             _Pragma("unroll") for (int u = 0; u < RC; ++u) {                                               \
                 const bool ok = j0 + u < re;                                                               \
@@ -3435,19 +3496,20 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
             }                                                                                              \
         }                                                                                                  \
         const int32_t i = t * kGRows + tid / kGroup;                                                       \
+        const double pown = WIN ? operand(min(i, n - 1)) : 0.0;                                            \
         __syncthreads(); /* tile t's LDS reads are done */                                                 \
-        t += P;                                                                                            \
+        t += ts;                                                                                           \
         const int32_t k0n = k0b, k1n = k1b;                                                                \
         k0b = k0c;                                                                                         \
         k1b = k1c;                                                                                         \
-        if (t < gtiles) commit(nxt, t, k0n, k1n);                                                          \
+        if (t < te) commit(nxt, t, k0n, k1n);                                                              \
         if (run && i < n) {                                                                                \
             const int64_t e = static_cast<int64_t>(i) * kGroup + sy;                                      \
             qg[e] = sum;                                                                                   \
-            const double w = pg[e] * sum;                                                                  \
+            const double w = (WIN ? pown : pg[e]) * sum;                                                   \
             sig = sig + w;                                                                                 \
         }                                                                                                  \
-        if (t >= gtiles) break;                                                                            \
+        if (t >= te) break;                                                                                \
         __syncthreads();                                                                                   \
     }
 #pragma unroll 1
@@ -3999,17 +4061,15 @@ int cg_band_blocks_per_cu(int cap)
     return c;
 }
 
-int cg_group_blocks_per_cu(int cap)
+int cg_group_blocks_per_cu(int cap, bool win)
 {
-    static int cache[2] = {};
-    int& c = cache[cap <= kGCapSmall ? 0 : 1];
+    static int cache[2][2] = {};
+    int& c = cache[cap <= kGCapSmall ? 0 : 1][win ? 1 : 0];
     if (c > 0) return c;
+    CgKernel f = cap <= kGCapSmall ? (win ? k_gcg_spmv<kGCapSmall, true> : k_gcg_spmv<kGCapSmall, false>)
+                                   : (win ? k_gcg_spmv<kGCapLarge, true> : k_gcg_spmv<kGCapLarge, false>);
     int a = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, cap <= kGCapSmall ? k_gcg_spmv<kGCapSmall>
-                                                                            : k_gcg_spmv<kGCapLarge>,
-                                                    kBlock, 0) != hipSuccess ||
-        a < 1)
-        a = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, f, kBlock, 0) != hipSuccess || a < 1) a = 1;
     c = a;
     return c;
 }
@@ -4106,8 +4166,13 @@ hipError_t launch_gcg(int which, const CgArgs& a, int64_t k, hipStream_t s)
     case 0: SLA_LAUNCH(k_gcg_init, gu, blk, 0, s, a); break;
     case 1: SLA_LAUNCH(k_gcg_pupd, gu, blk, 0, s, a, k); break;
     case 2:
-        if (a.cap <= kGCapSmall) SLA_LAUNCH(k_gcg_spmv<kGCapSmall>, gs, blk, 0, s, a, k);
-        else SLA_LAUNCH(k_gcg_spmv<kGCapLarge>, gs, blk, 0, s, a, k);
+        if (a.g_halo > 0) {
+            if (a.cap <= kGCapSmall) SLA_LAUNCH((k_gcg_spmv<kGCapSmall, true>), gs, blk, 0, s, a, k);
+            else SLA_LAUNCH((k_gcg_spmv<kGCapLarge, true>), gs, blk, 0, s, a, k);
+        } else {
+            if (a.cap <= kGCapSmall) SLA_LAUNCH((k_gcg_spmv<kGCapSmall, false>), gs, blk, 0, s, a, k);
+            else SLA_LAUNCH((k_gcg_spmv<kGCapLarge, false>), gs, blk, 0, s, a, k);
+        }
         break;
     case 3: SLA_LAUNCH(k_gcg_update, gu, blk, 0, s, a, k); break;
     case 5: SLA_LAUNCH(k_gcg_diag, gu, blk, 0, s, a); break;

@@ -112,11 +112,12 @@ def csr_analysis(h: Handle) -> dict:
     rm, tm, cap, band, split = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int64(), C.c_int32()
     check(lib.sla_csr_analysis(h.ptr, C.byref(rm), C.byref(tm), C.byref(cap), C.byref(band),
                                C.byref(split)))
-    cb, nd = C.c_int32(), C.c_int32()
+    cb, nd, gw = C.c_int32(), C.c_int32(), C.c_int32()
     check(lib.sla_csr_col_bits(h.ptr, C.byref(cb)))
     check(lib.sla_csr_diagonals(h.ptr, C.byref(nd)))
+    check(lib.sla_csr_group_window(h.ptr, C.byref(gw)))
     return dict(row_max=rm.value, tile_max=tm.value, spmv_cap=cap.value, band_stride=band.value,
-                split=bool(split.value), col_bits=cb.value, diagonals=nd.value)
+                split=bool(split.value), col_bits=cb.value, diagonals=nd.value, group_window=gw.value)
 
 
 def _batch_of(vals: torch.Tensor, nnz: int) -> int:

@@ -199,6 +199,16 @@ sla_status sla_csr_col_bits(const sla_csr* A, int32_t* col_bits);
  * diagonals the row stores.  0: the staged CSR banded SpMV (more diagonals, not banded,
  * or SLA_DIA=0 in the environment at create).  Row sums are the same either way. */
 sla_status sla_csr_diagonals(const sla_csr* A, int32_t* n_diagonals);
+/* Operand window of the grouped batch SpMV (batches of at least 8 systems, a multiple
+ * of 4, on split-schedule patterns; paperpeel section 3.1: batched SparseTensor).  Those
+ * solves run on a reverse Cuthill-McKee order of the pattern, computed at the handle's
+ * first grouped solve.  When every entry of that order lies within 448 rows of its
+ * row, each workgroup of the SpMV keeps the operand rows around its tile in LDS and
+ * reads the gathers there; *halo_rows is then that halo (rows on each side, a multiple
+ * of 64).  0: the SpMV gathers from memory (bandwidth above 448, the reordering off, or
+ * SLA_GCG_WINDOW=0 in the environment at create), or no grouped solve has run yet.
+ * Row sums are the same either way. */
+sla_status sla_csr_group_window(const sla_csr* A, int32_t* halo_rows);
 
 /* Shape and workspace queries (host outputs; any pointer may be NULL). */
 sla_status sla_csr_info(const sla_csr* A, int64_t* n_rows, int64_t* n_cols, int64_t* nnz,

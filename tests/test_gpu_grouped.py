@@ -8,7 +8,9 @@ those of the single-system path against the oracle: iterations within 2 %, x wit
 1e-9, lambda and dL/dvals within 1e-8, and 1e-12 over fixed iterations.  Cases: 32
 systems (8 groups: every group pinned to one XCD), 12 systems (3 groups, not pinned),
 a batch of 8 whose systems start from b = 0, are not SPD, hold a NaN or run out of
-budget, and the residual histories of a fixed run.
+budget, and the residual histories of a fixed run.  The SpMV keeps the operand in an LDS
+window where the reordered bandwidth allows (at most 448 rows): against the gathering
+kernel, on long runs of tiles per workgroup, and a mesh whose bandwidth is too wide.
 
 The fixed-iteration comparisons stop at 6 iterations.  On these FEM systems the early
 CG iterates amplify rounding differences about tenfold per iteration: on the CPU, the
@@ -175,3 +177,47 @@ def test_grouped_reordering_matches_the_original_order(S, mesh, monkeypatch):
         assert rel(a_, b_) <= 1e-12
     out = solve_pair(S, A, A.vals[:8], b[:8], rtol=1e-8)
     check_against_oracle(A, A.vals[:8], b[:8], out, rtol=1e-8, systems=[0, 7])
+
+
+def window_of(S, A, vals, b):
+    """Operand window the grouped SpMV used for this pattern (known after a solve)."""
+    h = handle(S, A)
+    S.solve(h, dev(vals), dev(b), S.cg_opts(rtol=0.0, max_iter=1, fixed=True))
+    torch.cuda.synchronize()
+    return S.csr_analysis(h)["group_window"]
+
+
+def test_grouped_window_matches_gathers(S, mesh, monkeypatch):
+    # On the reordered 100 x 100 mesh (bandwidth about 100 rows) the grouped SpMV keeps
+    # its operand in an LDS window; with SLA_GCG_WINDOW=0 it gathers every entry from
+    # memory.  The row sums are the same; only which workgroup sums which rows differs
+    # (the grouping of the p^T q partials), so the iterates agree to rounding.
+    A, b = mesh
+    assert 0 < window_of(S, A, A.vals[:8], b[:8]) <= 448
+    out_w = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
+    monkeypatch.setenv("SLA_GCG_WINDOW", "0")
+    assert window_of(S, A, A.vals[:8], b[:8]) == 0
+    out_g = solve_pair(S, A, A.vals[:8], b[:8], rtol=0.0, max_iter=6, fixed=True)
+    for a_, b_ in zip(out_w[:3], out_g[:3]):
+        assert rel(a_, b_) <= 1e-12
+
+
+def test_grouped_window_long_runs(S):
+    # 32 systems (8 groups, pinned) on a 200 x 200 mesh: every workgroup walks a run of
+    # several tiles, so the ring wraps and slides; halo of a few hundred rows
+    A, b = W.fem_p1_batched(nv=200, B=32, seed=9)
+    halo = window_of(S, A, A.vals, b)
+    assert 128 <= halo <= 448, halo
+    out = solve_pair(S, A, A.vals, b, rtol=0.0, max_iter=6, fixed=True)
+    check_against_oracle(A, A.vals, b, out, rtol=0.0, max_iter=6, fixed=True, systems=[0, 9, 31])
+    out = solve_pair(S, A, A.vals, b, rtol=1e-8)
+    check_against_oracle(A, A.vals, b, out, rtol=1e-8, systems=[3, 20])
+
+
+def test_grouped_bandwidth_above_the_window(S):
+    # a 500 x 500 mesh: the reordered bandwidth exceeds the 448-row window, so the
+    # grouped SpMV gathers from memory; same bars
+    A, b = W.fem_p1_batched(nv=500, B=8, seed=2)
+    assert window_of(S, A, A.vals, b) == 0
+    out = solve_pair(S, A, A.vals, b, rtol=0.0, max_iter=6, fixed=True)
+    check_against_oracle(A, A.vals, b, out, rtol=0.0, max_iter=6, fixed=True, systems=[0, 7])
