@@ -2442,18 +2442,40 @@ sla_status sla_list_create(sla_list** out, int32_t items, const int64_t* n, cons
         return st;
     L->packed->band = 0;          // the list solve runs the plain or split SpMV
     L->packed->group_ok = false;
-    // workgroups per item, in proportion to its tiles (at least one each), for a grid
-    // that fills the GPU about once
+    // Workgroups per item.  Every launch of the solve lasts as long as its busiest
+    // workgroup, so the split minimises the most tiles any workgroup walks, m, over
+    // grids that fit the GPU once (n_cu x the SpMV's occupancy): each item gets the
+    // fewest workgroups with at most m tiles each, a multiple of 8 from 8 up where the
+    // item has the tiles (its workgroups on one XCD then sweep a contiguous eighth of
+    // its tiles, block_coord; an eighth holds at most ceil(ti / 8) tiles).
     const int per_cu = cg_blocks_per_cu(L->packed->krp_bits, L->packed->cap, L->n_total, L->packed->split);
-    const double target = static_cast<double>(L->packed->n_cu) * per_cu;
+    const int64_t capacity = std::max<int64_t>(items, static_cast<int64_t>(L->packed->n_cu) * per_cu);
+    auto count_for = [](int64_t ti, int64_t m) {
+        int64_t gi = std::max<int64_t>(1, (ti + m - 1) / m);
+        if (gi >= 8) {
+            int64_t g8 = (gi + 7) & ~int64_t(7);
+            while (g8 <= ti && ((ti + 7) / 8 + g8 / 8 - 1) / (g8 / 8) > m) g8 += 8;
+            if (g8 <= ti) gi = g8;
+        }
+        return std::min<int64_t>(gi, ti);
+    };
+    auto total_for = [&](int64_t m) {
+        int64_t acc = 0;
+        for (int32_t i = 0; i < items; ++i) acc += count_for(tile0[i + 1] - tile0[i], m);
+        return acc;
+    };
+    int64_t mlo = 1, mhi = 1;
+    for (int32_t i = 0; i < items; ++i) mhi = std::max<int64_t>(mhi, tile0[i + 1] - tile0[i]);
+    while (mlo < mhi) {   // smallest m whose grid fits (m = the largest item's tiles: one each)
+        const int64_t mid = (mlo + mhi) / 2;
+        if (total_for(mid) <= capacity) mhi = mid;
+        else mlo = mid + 1;
+    }
     std::vector<int32_t> wg(items + 1);
     int64_t acc = 0;
     for (int32_t i = 0; i < items; ++i) {
         wg[i] = static_cast<int32_t>(acc);
-        const int64_t ti = tile0[i + 1] - tile0[i];
-        const int64_t gi = std::max<int64_t>(
-            1, std::min<int64_t>(ti, static_cast<int64_t>(std::llround(target * ti / static_cast<double>(tiles)))));
-        acc += gi;
+        acc += count_for(tile0[i + 1] - tile0[i], mlo);
     }
     if (acc >= (int64_t(1) << 31)) return fail(SLA_ERR_UNSUPPORTED, "too many workgroups");
     wg[items] = static_cast<int32_t>(acc);

@@ -144,8 +144,17 @@ __device__ __forceinline__ BlockCoord block_coord(const CgArgs& a, int G)
             else hi = mid;
         }
         const int32_t g0 = a.list_wg[lo], gi = a.list_wg[lo + 1] - g0;
-        const int64_t t0 = a.list_tiles[lo];
-        return BlockCoord{lo, static_cast<int>(L - g0), TileRange{t0, a.list_tiles[lo + 1] - t0, L - g0, gi}};
+        const int64_t t0 = a.list_tiles[lo], len = a.list_tiles[lo + 1] - t0;
+        const int j = static_cast<int>(L - g0);
+        if ((gi & 7) == 0) {
+            // the item's workgroups j, j + 8, ... run on one XCD (workgroup L on XCD L % 8):
+            // they sweep one contiguous eighth of the item's tiles, so the neighbouring
+            // tiles a tile's rows reach into are read through that XCD's L2
+            const int x = j & 7;
+            const int64_t tlo = (len * x) >> 3, thi = (len * (x + 1)) >> 3;
+            return BlockCoord{lo, j, TileRange{t0 + tlo, thi - tlo, j >> 3, gi >> 3}};
+        }
+        return BlockCoord{lo, j, TileRange{t0, len, j, gi}};
     }
     if (a.sys_per_xcd) {
         const int64_t L = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
