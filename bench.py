@@ -787,7 +787,8 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     else:
         spmv_kernel, schedule = "k_cg_spmv", "fused"
     # the plain and banded SpMV (CG and BiCGStab) read 16-bit column offsets where the
-    # handle has them; the grouped kernels read the 32-bit columns
+    # handle has them; the grouped kernels read the 32-bit columns unless their operand
+    # window is on (below)
     col_bytes = 4 if spmv_kernel == "k_gcg_spmv" else an["col_bits"] // 8
     dia_nd = an["diagonals"] if spmv_kernel == "k_cg_spmv_dia" else 0
     rp_bytes = 4 if nnz < 2 ** 31 else 8      # the row pointers the kernels read
@@ -838,6 +839,11 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     S.timing.enable(False)
     tq = S.timing.query()
     torch.cuda.synchronize()
+    if spmv_kernel == "k_gcg_spmv" and S.csr_analysis(h)["group_window"] > 0:
+        # the windowed grouped SpMV (known after the first grouped solve) reads 16-bit
+        # column offsets
+        col_bytes = 2
+        schedule += "; operand in an LDS window, 16-bit column offsets"
     del x, h
     return dict(w=w, an=an, bicg=bicg, spmv_kernel=spmv_kernel, schedule=schedule, col_bytes=col_bytes, dia_nd=dia_nd,
                 rp_bytes=rp_bytes, rp_stated=rp_stated, steps=steps, warmup=warmup, wall=wall,

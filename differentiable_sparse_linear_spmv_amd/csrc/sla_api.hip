@@ -81,6 +81,7 @@ struct sla_csr {
     bool g_win_ok = true;   // the grouped SpMV may keep its operand in an LDS window (SLA_GCG_WINDOW=0: never)
     bool g_reordered = false;
     int32_t *g_rp = nullptr, *g_col = nullptr, *g_eperm = nullptr, *g_perm = nullptr;
+    int16_t* g_col16 = nullptr;   // reordered columns minus the first row of their 64-row tile (g_halo > 0)
     int32_t g_halo = 0;   // operand window of the grouped SpMV on the reordered pattern (0: none)
     // transposed pattern (lazily built unless SLA_SYMMETRIC)
     bool has_t = false;
@@ -654,18 +655,30 @@ sla_status ensure_reorder(sla_csr* A, hipStream_t s)
         for (int32_t k = rp2[i]; k < rp2[i + 1]; ++k) bw = std::max<int64_t>(bw, std::abs(col2[k] - i));
     const int64_t halo = (bw + 63) / 64 * 64;
     A->g_halo = halo <= kGWinMaxHalo ? static_cast<int32_t>(halo) : 0;
+    // with a window every column lies within halo + 63 rows of its tile's first row, so
+    // the windowed SpMV reads these 16-bit offsets instead of the columns
+    std::vector<int16_t> c16;
+    if (A->g_halo > 0) {
+        c16.resize(std::max<int64_t>(nnz, 1));
+        for (int64_t i = 0; i < n; ++i)
+            for (int32_t k = rp2[i]; k < rp2[i + 1]; ++k) c16[k] = static_cast<int16_t>(col2[k] - (i / 64) * 64);
+    }
     auto release = [&]() {
         for (int32_t** q : {&A->g_rp, &A->g_col, &A->g_eperm, &A->g_perm}) {
             if (*q) (void)dev_free(*q);
             *q = nullptr;
         }
+        if (A->g_col16) (void)dev_free(A->g_col16);
+        A->g_col16 = nullptr;
     };
     release();   // nothing is left from an earlier attempt that failed
     sla_status st;
     if ((st = dev_alloc(reinterpret_cast<void**>(&A->g_rp), sizeof(int32_t) * (n + 1))) != SLA_OK ||
         (st = dev_alloc(reinterpret_cast<void**>(&A->g_col), sizeof(int32_t) * col2.size())) != SLA_OK ||
         (st = dev_alloc(reinterpret_cast<void**>(&A->g_eperm), sizeof(int32_t) * ep.size())) != SLA_OK ||
-        (st = dev_alloc(reinterpret_cast<void**>(&A->g_perm), sizeof(int32_t) * n)) != SLA_OK) {
+        (st = dev_alloc(reinterpret_cast<void**>(&A->g_perm), sizeof(int32_t) * n)) != SLA_OK ||
+        (!c16.empty() &&
+         (st = dev_alloc(reinterpret_cast<void**>(&A->g_col16), sizeof(int16_t) * c16.size())) != SLA_OK)) {
         release();
         return st;
     }
@@ -673,6 +686,8 @@ sla_status ensure_reorder(sla_csr* A, hipStream_t s)
     HIP_TRY(hipMemcpyAsync(A->g_col, col2.data(), sizeof(int32_t) * col2.size(), hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(A->g_eperm, ep.data(), sizeof(int32_t) * ep.size(), hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(A->g_perm, perm.data(), sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
+    if (!c16.empty())
+        HIP_TRY(hipMemcpyAsync(A->g_col16, c16.data(), sizeof(int16_t) * c16.size(), hipMemcpyHostToDevice, s));
     HIP_TRY(hipStreamSynchronize(s));
     A->g_reordered = true;
     return SLA_OK;
@@ -762,6 +777,7 @@ sla_status run_cg_grouped(sla_csr* A, const void* row_ptr, const int32_t* col, i
     a.cap = gcap;
     a.xg = xg;
     a.g_halo = win;
+    a.g_col16 = win > 0 ? A->g_col16 : nullptr;
 
     hipError_t e = timed(SLA_K_GROUP_LAYOUT, s, [&] {
         return launch_group_vals(vals, vg, A->nnz, groups, reorder ? A->g_eperm : nullptr, s);
@@ -1252,6 +1268,7 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->g_col) (void)dev_free(A->g_col);
     if (A->g_eperm) (void)dev_free(A->g_eperm);
     if (A->g_perm) (void)dev_free(A->g_perm);
+    if (A->g_col16) (void)dev_free(A->g_col16);
     if (A->eig_host) (void)hipHostFree(A->eig_host);
     if (A->lob_ws) (void)dev_free(A->lob_ws);
     if (A->lob_host) (void)hipHostFree(A->lob_host);

@@ -114,6 +114,7 @@ struct CgArgs {
     int32_t cap;             // grouped batch: entries per tile staged (kGCapSmall or kGCapLarge)
     double* xg;              // grouped batch: x in the grouped layout
     int32_t g_halo;          // grouped batch: operand window halo (rows, a multiple of 64), 0 = no window
+    const int16_t* g_col16;  // grouped batch with a window: columns minus the first row of their 64-row tile
     const int32_t* gperm;    // grouped batch on a reordered pattern: row i is the caller's row gperm[i]
     // SparseTensorList (distinct patterns, packed block-diagonally; null otherwise):
     // system s owns tiles [list_tiles[s], list_tiles[s + 1]) and workgroups

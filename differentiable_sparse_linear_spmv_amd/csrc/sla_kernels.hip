@@ -3352,6 +3352,8 @@ __global__ __launch_bounds__(kBlock) void k_gcg_pupd(CgArgs a, int64_t k)
 //     range, so the gathers are LDS reads; moving to the next tile loads one coalesced
 //     chunk of kGRows rows (all kGroup systems) into the ring, the chunk H rows past the
 //     next tile.  The first tile of a run fills the ring with 2 H / kGRows + 1 chunks.
+//     The columns come as 16-bit offsets from the tile's first row (every column lies
+//     within H + kGRows - 1 of it).
 // Both give the same row sums (same products, same order); they differ in which
 // workgroup sums which rows, so the partials of p^T q are grouped differently.
 template <int CAPG>   // entries per tile (kGRows rows of at most CAPG / kGRows entries)
@@ -3421,15 +3423,23 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         const int32_t cnt = k1 - k0;
         const int32_t kb = cnt > 0 ? k0 : min(k0, nnz - 1);
         const double* __restrict__ vb = vg + static_cast<int64_t>(kb) * kGroup;
-        const int32_t* __restrict__ cb = col + kb;
         const int lastv = max(cnt * kGroup - 1, 0), lastc = max(cnt - 1, 0);
         // the values (every system's, read once per SpMV) stream with the non-temporal
         // hint, leaving the caches to the operand
 #pragma unroll
         for (int u = 0; u < UV; ++u) S.v[u] = __builtin_nontemporal_load(vb + min(tid + u * kBlock, lastv));
+        if constexpr (WIN) {
+            // 16-bit offsets from the tile's first row (sign-extended by the load); the
+            // commit adds the row back
+            const int16_t* __restrict__ cb = a.g_col16 + kb;
 #pragma unroll
-        for (int u = 0; u < UC; ++u) S.c[u] = cb[min(tid + u * kBlock, lastc)];
-        if constexpr (WIN) S.w = chunk_ld(t + hc);   // the chunk this tile adds to the ring
+            for (int u = 0; u < UC; ++u) S.c[u] = cb[min(tid + u * kBlock, lastc)];
+            S.w = chunk_ld(t + hc);   // the chunk this tile adds to the ring
+        } else {
+            const int32_t* __restrict__ cb = col + kb;
+#pragma unroll
+            for (int u = 0; u < UC; ++u) S.c[u] = cb[min(tid + u * kBlock, lastc)];
+        }
     };
     auto commit = [&](const GStage<CAPG>& S, int32_t t, int32_t k0, int32_t k1) __attribute__((always_inline)) {
         const int32_t cnt = k1 - k0;
@@ -3438,10 +3448,11 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
             const int e = tid + u * kBlock;
             if (e < cnt * kGroup) s_val[e] = S.v[u];
         }
+        const int32_t cbase = WIN ? t * kGRows : 0;
 #pragma unroll
         for (int u = 0; u < UC; ++u) {
             const int e = tid + u * kBlock;
-            if (e < cnt) s_col[e] = S.c[u];
+            if (e < cnt) s_col[e] = S.c[u] + cbase;
         }
         const bool has = t * kGRows + tid / kGroup < n;
         s_rs[tid] = S.a0 - k0;
