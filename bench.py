@@ -734,6 +734,41 @@ def main() -> int:
         print(json.dumps({"ceiling_sweep": measure_ceiling(S, torch, dev, sweep=True)}), flush=True)
         return 0
     w = make_workload(args.workload, dev)
+    method = w["method"]
+    if method == "eigsh":
+        r = run_eigsh(args, w, S, torch)
+        if args.calibrate_copy:
+            calibrate_copy(torch, dev)
+        traffic, traffic_src = read_traffic(args.workload, "bytes_per_run")
+        cpu = cpu_baseline_eigsh(w, 40) if (rank == 0 and not args.no_cpu_baseline) else None
+        out = {
+            "metric": METRIC_EIGSH, "value": round(r["value"], 2), "unit": "Lanczos steps/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * r["wall"] / args.steps, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+            "data": "synthetic",
+            "config": {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "k": w["k"], "which": w["which"],
+                       "tol": w["tol"], "max_dim": w["max_dim"], "max_iter": w["max_iter"],
+                       "parallelism": "none (1 GPU)", "method": "eigsh"},
+            "lanczos_steps": r["info"]["iterations"], "restarts": r["info"]["restarts"],
+            "state": r["info"]["state_name"],
+            "kernels": {kk: {"launches": v["launches"],
+                             "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3) if v["launches"] else None}
+                        for kk, v in r["tq"].items() if v["launches"]},
+            "bytes_model": r["bm"],
+            "lz_spmv_gbps": round(r["spmv_gbps"], 1),
+            "roofline": {"bound": "hbm",
+                         "kernel": "Lanczos reorthogonalization (k_lz_three, k_lz_dots, k_lz_reduce, k_lz_axpy, "
+                                   "k_lz_next), all launches of one run",
+                         "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(r["achieved"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                         "traffic_source": traffic_src, "traffic_unit": "bytes per run (all launches)",
+                         "bytes_per_launch": None, "bytes_per_run": r["bm"]["lz_orth_total"],
+                         "run_ms": round(r["orth_ms"], 3)},
+            "cpu_baseline": cpu,
+        }
+        if rank == 0:
+            print(json.dumps(out), flush=True)
+        return 0
     r = measure_cg(args, w, S, torch, args.steps, args.warmup)
     if args.calibrate_copy:
         calibrate_copy(torch, dev)

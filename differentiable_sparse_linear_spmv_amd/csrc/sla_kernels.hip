@@ -249,7 +249,12 @@ struct GatherX {
 constexpr int kBinLaneMax = 32;     // rows of at most this many entries: one lane per row
 constexpr int kBinGroupMax = 512;   // then one 16-lane group per row; longer rows: the workgroup
 constexpr int kBinGroup = 16;
-constexpr int kBinUnroll = 8;       // gathers in flight per lane in the group and workgroup bins
+// Gathers in flight per lane in the group and workgroup bins.  Those bins sit in every
+// capped SpMV, and a kernel's registers are those of its widest path: at 8 they took
+// the BiCGStab products from 110 to 131 VGPRs (4 to 3 waves per SIMD, 15.9 to 18.3 us
+// at 1M rows).  A row of more than kBinLaneMax entries sends its pattern to the
+// products-first kernels, so in the capped kernels these bins only guard.
+constexpr int kBinUnroll = 4;
 
 // Sum over a 16-lane group (lanes of one group only), fixed xor tree.
 __device__ __forceinline__ double group16_sum(double v)
