@@ -64,6 +64,7 @@ struct sla_csr {
     // (uint8, or uint16 above 8 diagonals), and the values in that layout [batch][nd][n],
     // rewritten by each solve (SLA_DIA=0 at create turns the layout off).
     int dia_nd = 0;
+    bool dia_align = true;   // line stride = 8 (mod 16): windows shifted onto 128-byte boundaries (SLA_DIA_ALIGN=0: not)
     DiaMap dia_map{};
     int8_t dia_b[kDiaMax] = {};
     int8_t dia_e[kDiaMax] = {};
@@ -956,6 +957,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
         a.dia_vals = A->dia_vals;
         a.dia_mask = A->dia_mask;
         a.dia_nd = A->dia_nd;
+        a.dia_shift = (A->dia_align && band % 16 == 8) ? 8 : 0;
         for (int d = 0; d < kDiaMax; ++d) {
             a.dia_b[d] = d < A->dia_nd ? A->dia_b[d] : 0;
             a.dia_e[d] = d < A->dia_nd ? A->dia_e[d] : 0;
@@ -1229,6 +1231,7 @@ sla_status sla_csr_create(sla_csr** out, int64_t n_rows, int64_t n_cols, int64_t
     if (A->band > 0 && A->krp_bits == 32) {
         bool dia = true;
         if (const char* env = std::getenv("SLA_DIA")) dia = std::strcmp(env, "0") != 0;
+        if (const char* env = std::getenv("SLA_DIA_ALIGN")) A->dia_align = std::strcmp(env, "0") != 0;
         if (dia && (st = build_dia(A, s)) != SLA_OK) return bail(st);
     }
     if (A->rp_owned || A->col16 || A->colb16 || A->dia_mask) {   // the handle may next be used on another stream

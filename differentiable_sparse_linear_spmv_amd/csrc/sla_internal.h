@@ -136,6 +136,7 @@ struct CgArgs {
     const double* dia_v[16]; // system 0's diagonal d at dia_v[d] (d < dia_nd; the last one repeated after)
     const void* dia_mask;    // [n] uint8 (dia_nd <= 8) or uint16: bit d set if row i stores diagonal d
     int32_t dia_nd;
+    int32_t dia_shift;       // diagonal layout: 8 when windows of odd lines are shifted onto 128-byte boundaries
     int8_t dia_b[16];
     int8_t dia_e[16];
 };

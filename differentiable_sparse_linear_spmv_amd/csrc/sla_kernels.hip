@@ -1602,6 +1602,12 @@ struct DiaStage {
     SegLoad seg;
 };
 
+// Segments of the diagonal-layout SpMV: kDiaSeg positions from seg0(m), kDiaMargin
+// before the strip's origin (less the line's shift), so that each holds what the
+// windows of lines m - 1, m and m + 1 read from line m, shifted or not.
+constexpr int kDiaMargin = 16;
+constexpr int kDiaSeg = kTile + 2 * kDiaMargin;
+
 template <int ND>
 struct DiaWalk {
     const double* vd[ND];               // diagonal d of this system (slots past nd repeat the last)
@@ -1612,15 +1618,63 @@ struct DiaWalk {
     int32_t n;
     int32_t S;
     int32_t nd;
-    int32_t pos0;
-    int32_t w;
-    __device__ __forceinline__ int32_t base(int32_t l) const { return l * S + pos0; }
-    __device__ __forceinline__ int rows(int32_t l) const
+    int32_t pos0;   // first position of the strip within a line (j kTile)
+    int32_t j;      // the strip
+    int32_t last;   // the last strip of a line
+    int32_t sh;     // 8 when the windows are aligned (S = 8 mod 16), else 0
+    // Line l's shift: with S = 8 (mod 16) every odd line starts 64 bytes past a 128-byte
+    // boundary; its windows after the first start delta(l) rows before the strip's
+    // origin, which puts them (and their values, masks, x and outputs) on one.
+    __device__ __forceinline__ int32_t delta(int32_t l) const { return sh & -(l & 1); }
+    __device__ __forceinline__ int32_t base(int32_t l) const { return l * S + pos0 - (j > 0 ? delta(l) : 0); }
+    __device__ __forceinline__ int32_t end(int32_t l) const
     {
-        const int32_t m = n - base(l);
-        return m <= 0 ? 0 : (m < w ? m : w);
+        return j == last ? (l + 1) * S : l * S + pos0 + kTile - delta(l);
     }
+    __device__ __forceinline__ int rows(int32_t l) const   // rows of window l that exist (<= kTile)
+    {
+        const int32_t m = min(end(l), n) - base(l);
+        return m <= 0 ? 0 : m;
+    }
+    __device__ __forceinline__ int32_t seg0(int32_t m) const { return m * S + pos0 - delta(m) - kDiaMargin; }
+    // position of window m's first row in line m's segment (its p_{k-1} for the x update)
+    __device__ __forceinline__ int32_t own0(int32_t m) const { return kDiaMargin + (j > 0 ? 0 : delta(m)); }
 };
+
+// Segment loads of the diagonal-layout SpMV: kTile positions from e0 and kDiaSeg - kTile
+// more (every lane issues both; `live` as in seg_issue).
+__device__ __forceinline__ void dia_seg_issue(SegLoad& L, const double* __restrict__ rin,
+                                              const double* __restrict__ pprev, int32_t e0, int32_t n, bool live)
+{
+    const int32_t keep = -static_cast<int32_t>(live);   // all ones or zero: a mask, not a branch
+    const int tid = threadIdx.x & keep;
+    const int32_t e = min(max(e0 + tid, 0), n - 1);
+    L.r0 = ld32(rin, e);
+    L.pp0 = ld32(pprev, e);
+    const int32_t e1 = min(max(e0 + kTile + min(tid, kDiaSeg - kTile - 1), 0), n - 1);
+    L.r1 = ld32(rin, e1);
+    L.pp1 = ld32(pprev, e1);
+}
+
+// p_k on the segment (positions outside [0, n) hold 0), and, when s_pp is given, the
+// window's own p_{k-1} (positions own0 ... own0 + kTile - 1) into s_pp.  Stores without
+// a branch on the halo, as seg_commit.
+__device__ __forceinline__ void dia_seg_commit(const SegLoad& L, double* s_seg, double* s_pp, double beta,
+                                               int32_t e0, int32_t n, int32_t own0)
+{
+    const int tid = threadIdx.x;
+    const bool halo = tid < kDiaSeg - kTile;
+    const int32_t e = e0 + tid;
+    const int32_t e1 = e + kTile;
+    const double t1 = beta * L.pp1;
+    const double v1 = L.r1 + t1;
+    s_seg[halo ? tid + kTile : tid] = (e1 >= 0 && e1 < n) ? v1 : 0.0;
+    const double t0 = beta * L.pp0;
+    const double v0 = L.r0 + t0;
+    s_seg[tid] = (e >= 0 && e < n) ? v0 : 0.0;
+    if (s_pp && tid >= own0) s_pp[tid - own0] = L.pp0;
+    if (s_pp && tid < own0) s_pp[tid + kTile - own0] = L.pp1;
+}
 
 // Element e (0 <= e < 2^29) of a streamed array: uniform base plus a 32-bit byte
 // offset, with the non-temporal hint.
@@ -1652,7 +1706,7 @@ __device__ __forceinline__ void dia_stage(const DiaWalk<ND>& W, DiaStage<ND>& B,
     if constexpr (M16) B.m = ld32_stream(static_cast<const uint16_t*>(W.mask), i);
     else B.m = ld32_stream(static_cast<const uint8_t*>(W.mask), i);
     B.xi = ld32(W.x, i);
-    seg_issue(B.seg, W.rin, W.pprev, W.base(ll + 1) - kBandHalo, W.n, live);
+    dia_seg_issue(B.seg, W.rin, W.pprev, W.seg0(ll + 1), W.n, live);
 }
 
 // LDS of one committed window of the diagonal-layout SpMV: its rows' values by
@@ -1675,7 +1729,7 @@ __device__ __forceinline__ void dia_commit(const DiaWalk<ND>& W, const DiaStage<
     for (int d = 0; d < ND; ++d) R->v[d][tid] = B.v[d];
     R->xi[tid] = B.xi;
     R->m[tid] = B.m;
-    seg_commit(B.seg, s_seg, s_pp, beta, W.base(l + 1) - kBandHalo, W.n);
+    dia_seg_commit(B.seg, s_seg, s_pp, beta, W.seg0(l + 1), W.n, W.own0(l + 1));
 }
 
 // One block: lines [l0, l1) of the strip W describes, pipelined as band_block: while
@@ -1694,13 +1748,13 @@ __device__ __forceinline__ void dia_block(const DiaWalk<ND>& W, const CgArgs& a,
     DiaStage<ND> SA, SB;
     SegLoad Em, E0;
     dia_stage<ND, M16>(W, SA, l0, l1);
-    seg_issue(Em, W.rin, W.pprev, W.base(l0 - 1) - kBandHalo, n);
-    seg_issue(E0, W.rin, W.pprev, W.base(l0) - kBandHalo, n);
+    dia_seg_issue(Em, W.rin, W.pprev, W.seg0(l0 - 1), n, true);
+    dia_seg_issue(E0, W.rin, W.pprev, W.seg0(l0), n, true);
     dia_stage<ND, M16>(W, SB, l0 + 1, l1);
     int sp = 0, so = 1, sn = 2, po = 0;
-    seg_commit(Em, s_p + sp * kSeg, nullptr, beta, W.base(l0 - 1) - kBandHalo, n);
-    seg_commit(E0, s_p + so * kSeg, s_pp + po * kTile, beta, W.base(l0) - kBandHalo, n);
-    dia_commit<ND>(W, SA, l0, R, s_p + sn * kSeg, s_pp + (po ^ 1) * kTile, beta);
+    dia_seg_commit(Em, s_p + sp * kDiaSeg, nullptr, beta, W.seg0(l0 - 1), n, 0);
+    dia_seg_commit(E0, s_p + so * kDiaSeg, s_pp + po * kTile, beta, W.seg0(l0), n, W.own0(l0));
+    dia_commit<ND>(W, SA, l0, R, s_p + sn * kDiaSeg, s_pp + (po ^ 1) * kTile, beta);
     __syncthreads();
     int32_t l = l0;
     // Window l, window l + 1's loads in flight in `nb`: issue window l + 2's loads into
@@ -1712,18 +1766,24 @@ __device__ __forceinline__ void dia_block(const DiaWalk<ND>& W, const CgArgs& a,
         dia_stage<ND, M16>(W, na, l + 2, l1); /* past l1: one row, exact counts */                        \
         double s = 0.0;                                                                                   \
         const uint32_t msk = R->m[tid];                                                                   \
+        /* where row base(l) + tid's position sits in the segments of lines l - 1, l, l + 1 */            \
+        const int32_t dl = W.j > 0 ? W.delta(l) : 0;                                                      \
+        const int32_t offm = kDiaMargin + W.delta(l - 1) - dl;                                            \
+        const int32_t off0 = kDiaMargin + W.delta(l) - dl;                                                \
+        const int32_t offp = kDiaMargin + W.delta(l + 1) - dl;                                            \
         _Pragma("unroll") for (int d = 0; d < ND; ++d)                                                    \
         {                                                                                                 \
             const int sb = a.dia_b[d];                                                                    \
             const int seg = sb < 0 ? sp : (sb > 0 ? sn : so);                                             \
-            const double pv = s_p[seg * kSeg + a.dia_e[d] + kBandHalo + tid];                             \
+            const int32_t ob = sb < 0 ? offm : (sb > 0 ? offp : off0);                                    \
+            const double pv = s_p[seg * kDiaSeg + a.dia_e[d] + ob + tid];                                 \
             const double t = R->v[d][tid] * pv;                                                           \
             const double s2 = s + t;                                                                      \
             s = ((msk >> d) & 1u) ? s2 : s;                                                               \
         }                                                                                                 \
         const bool own = tid < W.rows(l);                                                                 \
         const int32_t i = W.base(l) + tid;                                                                \
-        const double pk = s_p[so * kSeg + kBandHalo + tid];                                               \
+        const double pk = s_p[so * kDiaSeg + off0 + tid];                                                 \
         const double tx = alpha_prev * s_pp[po * kTile + tid]; /* alpha_{-1} = 0 for k = 0 */             \
         const double xo = R->xi[tid] + tx;                                                                \
         __syncthreads(); /* window l's LDS reads are done: rotate the rings */                            \
@@ -1733,7 +1793,7 @@ __device__ __forceinline__ void dia_block(const DiaWalk<ND>& W, const CgArgs& a,
         sn = t3;                                                                                          \
         po ^= 1;                                                                                          \
         ++l;                                                                                              \
-        if (l < l1) dia_commit<ND>(W, nb, l, R, s_p + sn * kSeg, s_pp + (po ^ 1) * kTile, beta);          \
+        if (l < l1) dia_commit<ND>(W, nb, l, R, s_p + sn * kDiaSeg, s_pp + (po ^ 1) * kTile, beta);       \
         if (own) {                                                                                        \
             st32_stream(pcur, i, pk);                                                                     \
             st32_stream(q, i, s);                                                                         \
@@ -1756,7 +1816,7 @@ __device__ __forceinline__ void dia_block(const DiaWalk<ND>& W, const CgArgs& a,
 template <int ND, bool M16>
 __global__ __launch_bounds__(kBlock) void k_cg_spmv_dia(CgArgs a, int64_t k)
 {
-    __shared__ double s_p[3 * kSeg];
+    __shared__ double s_p[3 * kDiaSeg];
     __shared__ double s_pp[2 * kTile];
     __shared__ DiaRows<ND> s_rows;
     __shared__ double s_red[kBlock / 64];
@@ -1784,6 +1844,8 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_dia(CgArgs a, int64_t k)
     W.n = n;
     W.S = S;
     W.nd = a.dia_nd;
+    W.last = strips - 1;
+    W.sh = a.dia_shift;
 
     double beta, alpha_prev;
     const int run = cg_step_begin(a, sys, lb, k, s_red, &s_stop, beta, alpha_prev);
@@ -1799,7 +1861,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv_dia(CgArgs a, int64_t k)
         const int32_t j = b % strips;
         const int32_t l0 = (b / strips) * B;
         W.pos0 = j * kTile;
-        W.w = min(kTile, S - W.pos0);
+        W.j = j;
         dia_block<ND, M16>(W, a, l0, min(l0 + B, lines), s_p, s_pp, &s_rows, beta, alpha_prev, pcur, q, x, sig);
         __syncthreads();   // the next block refills the ring
     }

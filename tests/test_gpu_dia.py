@@ -10,7 +10,10 @@ the same handle built with SLA_DIA=0 -- to the bit, and the oracle's to the usua
 16-bit masks), a grid with symmetric pairs of entries removed (rows that skip
 diagonals), a last line cut short, a batch, Jacobi PCG, fixed iterations with the
 residual history, a 19-diagonal pattern (no layout: the staged kernel), and a grid at
-the default minimum stride with several blocks per workgroup.
+the default minimum stride with several blocks per workgroup.  Line strides of 8
+(mod 16) take windows shifted onto 128-byte boundaries by default: those are held to the
+oracle, and to the unshifted layout over fixed iterations; strides 504 and 280 put the
+shifted last window at its widest and near its narrowest.
 """
 import math
 
@@ -111,18 +114,27 @@ def run(S, h, vals, b, opts, jac=False):
 
 
 def both(S, A, b, opts, monkeypatch, vals=None):
-    """The same solve + adjoint with the diagonal layout and with the staged banded
-    kernel (SLA_DIA=0 at create); both handles must have the same band."""
+    """The same solve + adjoint with the diagonal layout's windows unshifted
+    (SLA_DIA_ALIGN=0), with the staged banded kernel (SLA_DIA=0) and with the default
+    layout, whose windows on every other line start 8 rows early when the line stride is
+    8 (mod 16) so that they sit on 128-byte boundaries.  All handles have the same band.
+    The unshifted layout sums every row in the staged kernel's order and in the same
+    workgroup, so it must match it to the bit; the shifted one sums the same rows in the
+    same order, but some in another workgroup (the grouping of p^T q's partials)."""
     vals = A.vals if vals is None else vals
     rp, col = dev(A.row_ptr.astype(np.int32)), dev(A.col.astype(np.int32))
+    ha = S.csr_create(rp, col, symmetric=True)
+    monkeypatch.setenv("SLA_DIA_ALIGN", "0")
     hd = S.csr_create(rp, col, symmetric=True)
+    monkeypatch.delenv("SLA_DIA_ALIGN")
     monkeypatch.setenv("SLA_DIA", "0")
     hs = S.csr_create(rp, col, symmetric=True)
     monkeypatch.delenv("SLA_DIA")
     ad, as_ = S.csr_analysis(hd), S.csr_analysis(hs)
     assert ad["band_stride"] == as_["band_stride"] > 0 and as_["diagonals"] == 0
+    assert S.csr_analysis(ha)["diagonals"] == ad["diagonals"]
     dv, db = dev(vals), dev(b)
-    return ad, run(S, hd, dv, db, opts), run(S, hs, dv, db, opts)
+    return ad, run(S, hd, dv, db, opts), run(S, hs, dv, db, opts), run(S, ha, dv, db, opts)
 
 
 def assert_bit_identical(r_dia, r_staged):
@@ -141,7 +153,8 @@ def check_oracle(A, b, res, rtol, vals=None):
 
 
 @pytest.mark.parametrize("case", ["poisson520", "seven", "nine", "dropped", "cut",
-                                  "poisson600", "seven600", "nine599", "dropped599", "cut600"])
+                                  "poisson600", "seven600", "nine599", "dropped599", "cut600",
+                                  "poisson504", "poisson280"])
 def test_dia_equals_staged_band_and_oracle(S, band_env, case):
     if case == "poisson520":
         A, nd = W.poisson5(520), 5
@@ -161,13 +174,18 @@ def test_dia_equals_staged_band_and_oracle(S, band_env, case):
         A, nd = nine_point(599, 12), 9
     elif case == "dropped599":
         A, nd = drop_pairs(nine_point(599, 10), 0.3, seed=4), 9
-    else:                        # a last line cut short, n even
+    elif case == "cut600":       # a last line cut short, n even
         A, nd = leading(W.poisson5(600), 600 * 9 - 38), 5
+    elif case == "poisson504":   # 504 = 248 (mod 256): shifted last windows are exactly 256 rows
+        A, nd = leading(W.poisson5(504), 504 * 40), 5
+    else:                        # 280 = 24 (mod 256): last windows of 24 and 32 rows
+        A, nd = leading(W.poisson5(280), 280 * 40), 5
     b = W.rhs_normal(A.n_rows, 11)
-    ad, rd, rs = both(S, A, b, S.cg_opts(rtol=1e-10), band_env)
+    ad, rd, rs, ra = both(S, A, b, S.cg_opts(rtol=1e-10), band_env)
     assert ad["diagonals"] == nd
     assert_bit_identical(rd, rs)
     check_oracle(A, b, rd, 1e-10)
+    check_oracle(A, b, ra, 1e-10)
 
 
 def test_dia_fixed_iterations_history(S, band_env):
@@ -189,20 +207,21 @@ def test_dia_batch_and_jacobi(S, band_env):
     B = 3
     vals = np.stack([A.vals * (1.0 + 0.5 * s) for s in range(B)])
     b = np.stack([W.rhs_normal(A.n_rows, 20 + s) for s in range(B)])
-    ad, rd, rs = both(S, A, b, S.cg_opts(rtol=1e-10), band_env, vals=vals)
+    ad, rd, rs, ra = both(S, A, b, S.cg_opts(rtol=1e-10), band_env, vals=vals)
     assert ad["diagonals"] == 5
     assert_bit_identical(rd, rs)
     for s in range(B):
         f = O.cg(A, b[s], rtol=1e-10, vals=vals[s])
-        assert rel(rd[0][0][s], f["x"]) <= 1e-9
+        assert rel(rd[0][0][s], f["x"]) <= 1e-9 and rel(ra[0][0][s], f["x"]) <= 1e-9
     # Jacobi on a variable-coefficient grid (its diagonal is not constant)
     V, bv, _ = W.varcoef_poisson5(300, seed=5)
-    ad, rd, rs = both(S, V, bv, S.cg_opts(rtol=1e-10, jacobi=True), band_env)
+    ad, rd, rs, ra = both(S, V, bv, S.cg_opts(rtol=1e-10, jacobi=True), band_env)
     assert ad["diagonals"] == 5
     assert_bit_identical(rd, rs)
     f = O.cg(V, bv, rtol=1e-10, jacobi=True)
-    assert abs(rd[1][0]["iterations"] - f["iterations"]) <= math.floor(0.02 * f["iterations"])
-    assert rel(rd[0][0], f["x"]) <= 1e-9
+    for r in (rd, ra):
+        assert abs(r[1][0]["iterations"] - f["iterations"]) <= math.floor(0.02 * f["iterations"])
+        assert rel(r[0][0], f["x"]) <= 1e-9
 
 
 def test_dia_too_many_diagonals_keeps_the_staged_kernel(S, band_env):
@@ -237,8 +256,12 @@ def test_dia_several_blocks_per_workgroup(S, monkeypatch):
     A = W.poisson5(3000)
     b = W.rhs_normal(A.n_rows, 8)
     K = 12
-    ad, rd, rs = both(S, A, b, S.cg_opts(rtol=0.0, max_iter=K, fixed=True), monkeypatch)
+    ad, rd, rs, ra = both(S, A, b, S.cg_opts(rtol=0.0, max_iter=K, fixed=True), monkeypatch)
     assert ad["diagonals"] == 5 and ad["band_stride"] == 3000
     assert_bit_identical(rd, rs)
     f = O.cg(A, b, rtol=0.0, max_iter=K, fixed=True)
     assert rel(rd[0][0], f["x"]) <= 1e-12
+    # the shifted windows (3000 = 8 mod 16): the same iterates to rounding
+    for a_, c_ in zip(ra[0], rd[0]):
+        assert rel(a_, c_) <= 1e-12
+    assert rel(ra[0][0], f["x"]) <= 1e-12
