@@ -2072,7 +2072,10 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
             if (e != hipSuccess) return e;
             if ((e = ar.flush(s)) != hipSuccess) return e;
             e = timed(SLA_K_LOB_COMB, s, [&] {
-                return launch_blk_comb(bin, din, m, dY, bout, dout, qc, n, norms ? d_cpart : nullptr, s);
+                // pairs of rows with 16-byte accesses where every column base allows it
+                const bool pairs = (n % 2 == 0) && (reinterpret_cast<uintptr_t>(bin) & 15) == 0 &&
+                                   (reinterpret_cast<uintptr_t>(bout) & 15) == 0;
+                return launch_blk_comb(bin, din, m, dY, bout, dout, qc, n, norms ? d_cpart : nullptr, s, pairs);
             }, true, 8.0 * static_cast<double>(n) * (m + qc));
             if (e != hipSuccess) return e;
             if (norms) {

@@ -231,7 +231,8 @@ hipError_t launch_blk_diag_inv(const void* rp, int rp_bits, const int32_t* col, 
 hipError_t launch_blk_rowscale(const double* in, const int32_t* idx_in, double* out, const int32_t* idx_out, int q,
                                int64_t n, const double* t, hipStream_t s);
 hipError_t launch_blk_comb(const double* in, const int32_t* idx_in, int m, const double* Y, double* out,
-                           const int32_t* idx_out, int q, int64_t n, double* part, hipStream_t s);
+                           const int32_t* idx_out, int q, int64_t n, double* part, hipStream_t s,
+                           bool pairs = false);
 
 // Bandwidth-reducing order of a square pattern (reverse Cuthill-McKee, host code,
 // sla_reorder.hip): perm[new] = old.  rp / col are host copies of the pattern.

@@ -3098,6 +3098,76 @@ __global__ __launch_bounds__(kBlock) void k_blk_comb(const double* __restrict__ 
     }
 }
 
+// k_blk_comb on pairs of rows: the same sums, row by row in ascending j, with 16-byte
+// loads and stores (every column base 16-byte aligned, n even), so each load moves two
+// rows and a thread's four-input groups wait half as often per row.  The squared norms
+// add the pair's two rows in order (a different grouping of the same terms than
+// k_blk_comb's).
+template <int QQ>
+__global__ __launch_bounds__(kBlock) void k_blk_comb2(const double* __restrict__ in, const int32_t* __restrict__ idx_in,
+                                                      int m, const double* __restrict__ Y, double* __restrict__ out,
+                                                      const int32_t* __restrict__ idx_out, int q, int64_t n,
+                                                      double* __restrict__ part)
+{
+    __shared__ double s_red[kBlock / 64];
+    double nrm[QQ];
+#pragma unroll
+    for (int u = 0; u < QQ; ++u) nrm[u] = 0.0;
+    const int64_t n2 = n >> 1;
+    for (int64_t i2 = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i2 < n2;
+         i2 += static_cast<int64_t>(gridDim.x) * kBlock) {
+        double ax[QQ], ay[QQ];
+#pragma unroll
+        for (int u = 0; u < QQ; ++u) ax[u] = ay[u] = 0.0;
+        int j = 0;
+        for (; j + 4 <= m; j += 4) {
+            double2 v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                v[t] = reinterpret_cast<const double2*>(in + static_cast<int64_t>(ld_uniform_i(idx_in, j + t)) * n)[i2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int u = 0; u < QQ; ++u) {
+                    const double y = ld_uniform(Y, static_cast<int64_t>(j + t) * q + (u < q ? u : 0));
+                    const double px = y * v[t].x;
+                    const double py = y * v[t].y;
+                    ax[u] = ax[u] + px;
+                    ay[u] = ay[u] + py;
+                }
+            }
+        }
+        for (; j < m; ++j) {
+            const double2 v = reinterpret_cast<const double2*>(in + static_cast<int64_t>(ld_uniform_i(idx_in, j)) * n)[i2];
+#pragma unroll
+            for (int u = 0; u < QQ; ++u) {
+                const double y = ld_uniform(Y, static_cast<int64_t>(j) * q + (u < q ? u : 0));
+                const double px = y * v.x;
+                const double py = y * v.y;
+                ax[u] = ax[u] + px;
+                ay[u] = ay[u] + py;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < QQ; ++u) {
+            if (u < q)
+                reinterpret_cast<double2*>(out + static_cast<int64_t>(ld_uniform_i(idx_out, u)) * n)[i2] =
+                    double2{ax[u], ay[u]};
+            const double tx = ax[u] * ax[u];
+            const double ty = ay[u] * ay[u];
+            nrm[u] = nrm[u] + tx;
+            nrm[u] = nrm[u] + ty;
+        }
+    }
+    if (part) {
+#pragma unroll
+        for (int u = 0; u < QQ; ++u) {
+            const double sv = block_sum(nrm[u], s_red);
+            if (threadIdx.x == 0 && u < q) part[static_cast<int64_t>(blockIdx.x) * q + u] = sv;
+        }
+    }
+}
+
 #undef LZ_ROWS
 
 // Hellmann-Feynman gradient on the stored entries: gvals[e] = sum_r g[r] U[r][i] U[r][c]
@@ -4411,10 +4481,21 @@ int blk_comb_groups(int64_t n)
 }
 
 hipError_t launch_blk_comb(const double* in, const int32_t* idx_in, int m, const double* Y, double* out,
-                           const int32_t* idx_out, int q, int64_t n, double* part, hipStream_t s)
+                           const int32_t* idx_out, int q, int64_t n, double* part, hipStream_t s, bool pairs)
 {
     if (m < 1 || q < 1 || q > 32 || n < 1) return hipErrorInvalidValue;
+    if (pairs && ((n & 1) || (reinterpret_cast<uintptr_t>(in) & 15) || (reinterpret_cast<uintptr_t>(out) & 15)))
+        return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blk_comb_groups(n))), blk(kBlock);
+    if (pairs) {
+        if (q <= 1) SLA_LAUNCH(k_blk_comb2<1>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+        else if (q <= 2) SLA_LAUNCH(k_blk_comb2<2>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+        else if (q <= 4) SLA_LAUNCH(k_blk_comb2<4>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+        else if (q <= 8) SLA_LAUNCH(k_blk_comb2<8>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+        else if (q <= 16) SLA_LAUNCH(k_blk_comb2<16>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+        else SLA_LAUNCH(k_blk_comb2<32>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
+        return hipGetLastError();
+    }
     if (q <= 1) SLA_LAUNCH(k_blk_comb<1>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
     else if (q <= 2) SLA_LAUNCH(k_blk_comb<2>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
     else if (q <= 4) SLA_LAUNCH(k_blk_comb<4>, grid, blk, 0, s, in, idx_in, m, Y, out, idx_out, q, n, part);
