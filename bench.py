@@ -994,8 +994,17 @@ def cg_line(r, args, ceiling, cpu) -> dict:
         out[k] = sm[k]
     if ceiling:
         out["ceiling"] = ceiling
+    out["device"] = device_info()
     out["cpu_baseline"] = cpu
     return out
+
+
+def device_info() -> dict:
+    """The GPU the line was measured on (figures vary from box to box)."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1)}
 
 
 # ------------------------------------------------------------------------------ ceiling

@@ -265,3 +265,21 @@ def test_dia_several_blocks_per_workgroup(S, monkeypatch):
     for a_, c_ in zip(ra[0], rd[0]):
         assert rel(a_, c_) <= 1e-12
     assert rel(ra[0][0], f["x"]) <= 1e-12
+
+
+def test_dia_aligned_windows_batch(S, band_env):
+    # a batch of three systems at stride 520 (8 mod 16: shifted windows) against the
+    # oracle, and the unshifted layout bit for bit against the staged kernel
+    A = leading(W.poisson5(520), 520 * 60)
+    B = 3
+    vals = np.stack([A.vals * (1.0 + 0.25 * s) for s in range(B)])
+    b = np.stack([W.rhs_normal(A.n_rows, 40 + s) for s in range(B)])
+    ad, rd, rs, ra = both(S, A, b, S.cg_opts(rtol=1e-10), band_env, vals=vals)
+    assert ad["diagonals"] == 5 and ad["band_stride"] == 520
+    assert_bit_identical(rd, rs)
+    for s in range(B):
+        f = O.cg(A, b[s], rtol=1e-10, vals=vals[s])
+        bw = O.solve_backward(A, ra[0][0][s], ra[0][0][s], symmetric=True, rtol=1e-10, vals=vals[s])
+        assert abs(ra[1][s]["iterations"] - f["iterations"]) <= math.floor(0.02 * f["iterations"])
+        assert rel(ra[0][0][s], f["x"]) <= 1e-9
+        assert rel(ra[0][1][s], bw["lam"]) <= 1e-8 and rel(ra[0][2][s], bw["gvals"]) <= 1e-8
