@@ -22,6 +22,7 @@
 #include <memory>
 #include <mutex>
 #include <new>
+#include <map>
 #include <unordered_map>
 #include <vector>
 
@@ -109,6 +110,8 @@ struct sla_csr {
     size_t lob_ws_bytes = 0;
     char* lob_host = nullptr;
     size_t lob_host_bytes = 0;
+    double* lob_res = nullptr;   // coherent pinned memory the kernels write results into
+    size_t lob_res_bytes = 0;
     hipEvent_t poll_ev[2] = {nullptr, nullptr};
     std::mutex mu;
 };
@@ -1275,6 +1278,7 @@ sla_status sla_csr_destroy(sla_csr* A)
     if (A->eig_host) (void)hipHostFree(A->eig_host);
     if (A->lob_ws) (void)dev_free(A->lob_ws);
     if (A->lob_host) (void)hipHostFree(A->lob_host);
+    if (A->lob_res) (void)hipHostFree(A->lob_res);
     for (int i = 0; i < 2; ++i)
         if (A->poll_ev[i]) (void)hipEventDestroy(A->poll_ev[i]);
     if (prev >= 0 && prev != A->device) (void)hipSetDevice(prev);
@@ -1973,16 +1977,21 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> guard(A->mu);
 
-    // workspace: NC block columns (the last holds the Jacobi reciprocals), Gram partials
-    // and results, combination norm partials
-    const int NC = 14 * k + 1;
+    // The block columns sit in fixed slots of k columns; the Ritz step's outputs (X, AX,
+    // P, AP) alternate between two slots, so an iteration's index lists change only with
+    // its active set.  The last column holds the Jacobi reciprocals.
+    enum { kSX = 0, kSAX = 2, kSP = 4, kSAP = 6, kSR = 8, kSWa, kSWb, kSWc, kSAW, kSPa, kSPb, kSAPa, kSAPb, kSlots };
+    const int NC = kSlots * k + 1;
     const int Gg = blk_gram_groups(n), Gc = blk_comb_groups(n);
+    const size_t kk9 = 9 * static_cast<size_t>(k) * k;
+    constexpr size_t kListCap = 1 << 16;   // int32 entries of the device list table
     const size_t sz_pool = align256(sizeof(double) * static_cast<size_t>(NC) * n);
-    const size_t sz_gp = align256(sizeof(double) * static_cast<size_t>(Gg) * 9 * k * k);
-    const size_t sz_g = align256(sizeof(double) * 9 * k * k);
+    const size_t sz_gp = align256(sizeof(double) * static_cast<size_t>(Gg) * kk9);
+    const size_t sz_sm = align256(sizeof(double) * kk9);
     const size_t sz_cp = align256(sizeof(double) * static_cast<size_t>(Gc) * k);
+    const size_t sz_lists = align256(sizeof(int32_t) * kListCap);
     const size_t sz_arena = 1 << 20;
-    const size_t need = sz_pool + sz_gp + sz_g + sz_cp + sz_arena;
+    const size_t need = sz_pool + sz_gp + 2 * sz_sm + sz_cp + sz_lists + sz_arena;
     if (need > A->lob_ws_bytes) {
         if (A->lob_ws) {
             HIP_TRY(hipDeviceSynchronize());
@@ -1993,7 +2002,7 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
         if ((st = dev_alloc(&A->lob_ws, need)) != SLA_OK) return st;
         A->lob_ws_bytes = need;
     }
-    const size_t hneed = sz_arena + sz_g;
+    const size_t hneed = sz_arena + sz_lists;
     if (hneed > A->lob_host_bytes) {
         HIP_TRY(hipStreamSynchronize(s));
         if (A->lob_host) HIP_TRY(hipHostFree(A->lob_host));
@@ -2002,343 +2011,365 @@ sla_status sla_lobpcg(const sla_csr* Ac, const double* d_vals, int32_t k, const 
         HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&A->lob_host), hneed, hipHostMallocDefault));
         A->lob_host_bytes = hneed;
     }
+    // results the kernels write straight into host memory (coherent, so a stream
+    // synchronization is all the host waits for): a Gram matrix, the squared residual
+    // norms, the W and P block flags
+    const size_t rneed = sizeof(double) * (kk9 + k + 2);
+    if (rneed > A->lob_res_bytes) {
+        HIP_TRY(hipStreamSynchronize(s));
+        if (A->lob_res) HIP_TRY(hipHostFree(A->lob_res));
+        A->lob_res = nullptr;
+        A->lob_res_bytes = 0;
+        HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&A->lob_res), rneed, hipHostMallocCoherent));
+        A->lob_res_bytes = rneed;
+    }
+    double* hH = A->lob_res;
+    double* hN = hH + kk9;
+    double* hF = hN + k;
+    double* dH = nullptr;
+    HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void**>(&dH), A->lob_res, 0));
+    double* dN = dH + kk9;
+    double* dF = dN + k;
+
     char* p = static_cast<char*>(A->lob_ws);
     double* pool = reinterpret_cast<double*>(p);
-    double* d_gpart = reinterpret_cast<double*>(p + sz_pool);
-    double* d_g = reinterpret_cast<double*>(p + sz_pool + sz_gp);
-    double* d_cpart = reinterpret_cast<double*>(p + sz_pool + sz_gp + sz_g);
-    Arena ar;
-    ar.d = p + sz_pool + sz_gp + sz_g + sz_cp;
+    p += sz_pool;
+    double* d_gpart = reinterpret_cast<double*>(p);
+    p += sz_gp;
+    double* d_cg = reinterpret_cast<double*>(p);   // Gram matrices the device factors
+    p += sz_sm;
+    double* d_cy = reinterpret_cast<double*>(p);   // coefficient matrices formed on the device
+    p += sz_sm;
+    double* d_cpart = reinterpret_cast<double*>(p);
+    p += sz_cp;
+    int32_t* d_lists = reinterpret_cast<int32_t*>(p);
+    p += sz_lists;
+    Arena ar;   // per-step uploads: the Ritz and residual coefficients
+    ar.d = p;
     ar.h = A->lob_host;
     ar.cap = sz_arena;
-    double* h_g = reinterpret_cast<double*>(A->lob_host + sz_arena);
+    double* tinv = pool + static_cast<size_t>(NC - 1) * n;
+
+    // Index lists, uploaded once and kept on the device while the active set lasts.
+    // get() stages a new list on the host; flush() sends what is staged in one copy.
+    // Tables fill only after a synchronization, so a reset never pulls a list from
+    // under a kernel in flight.
+    struct Lists {
+        int32_t* h = nullptr;
+        int32_t* d = nullptr;
+        size_t off = 0, sent = 0;
+        std::map<std::vector<int32_t>, size_t> at;
+        const int32_t* get(const std::vector<int32_t>& v)
+        {
+            auto it = at.find(v);
+            if (it != at.end()) return d + it->second;
+            std::memcpy(h + off, v.data(), sizeof(int32_t) * v.size());
+            at.emplace(v, off);
+            const int32_t* q = d + off;
+            off += v.size();
+            return q;
+        }
+        void room(size_t need)
+        {
+            if (off + need > kListCap) {
+                at.clear();
+                off = sent = 0;
+            }
+        }
+        hipError_t flush(hipStream_t st)
+        {
+            hipError_t e = hipSuccess;
+            if (off > sent)
+                e = hipMemcpyAsync(d + sent, h + sent, sizeof(int32_t) * (off - sent), hipMemcpyHostToDevice, st);
+            sent = off;
+            return e;
+        }
+    } lists;
+    lists.h = reinterpret_cast<int32_t*>(A->lob_host + sz_arena);
+    lists.d = d_lists;
+    const size_t kPhaseLists = 64 * static_cast<size_t>(kBlkMaxCols);   // more than one step's lists
 
     using Cols = std::vector<int32_t>;
-    std::vector<int32_t> free_cols;
-    for (int c = NC - 2; c >= 0; --c) free_cols.push_back(c);
-    double* tinv = pool + static_cast<size_t>(NC - 1) * n;
-    auto take = [&](int w, Cols& out) -> bool {
-        if (static_cast<int>(free_cols.size()) < w) return false;
-        out.resize(w);
-        for (int i = 0; i < w; ++i) {
-            out[i] = free_cols.back();
-            free_cols.pop_back();
-        }
-        return true;
-    };
-    auto give = [&](const Cols& c) {
-        for (int32_t v : c) free_cols.push_back(v);
+    auto slot = [&](int sl, const std::vector<int>& idx) {
+        Cols c(idx.size());
+        for (size_t i = 0; i < idx.size(); ++i) c[i] = sl * k + idx[i];
+        return c;
     };
     auto cat = [](std::initializer_list<const Cols*> parts) {
         Cols o;
         for (const Cols* q : parts) o.insert(o.end(), q->begin(), q->end());
         return o;
     };
+    std::vector<int> allk(k);
+    for (int r = 0; r < k; ++r) allk[r] = r;
     hipError_t e = hipSuccess;
-    // Gram <a_i, b_j> of two column sets, read back to the host ([|a|][|b|])
-    auto gram = [&](const double* ba, const Cols& ia, const double* bb, const Cols& ib,
-                    std::vector<double>& out) -> hipError_t {
-        const int32_t* dia = ar.put(ia.data(), ia.size(), e);
-        if (e != hipSuccess) return e;
-        const int32_t* dib = ar.put(ib.data(), ib.size(), e);
-        if (e != hipSuccess) return e;
-        if ((e = ar.flush(s)) != hipSuccess) return e;
-        e = timed(SLA_K_LOB_GRAM, s, [&] {
-            return launch_blk_gram(ba, dia, static_cast<int>(ia.size()), bb, dib, static_cast<int>(ib.size()), n,
-                                   d_gpart, d_g, s);
-        }, false, 8.0 * static_cast<double>(n) * static_cast<double>(ia.size() + ib.size()));
-        if (e != hipSuccess) return e;
-        const size_t np = ia.size() * ib.size();
-        if ((e = hipMemcpyAsync(h_g, d_g, sizeof(double) * np, hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
-        if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-        ar.reset();
-        out.assign(h_g, h_g + np);
-        return hipSuccess;
+    auto hip_fail = [&](const char* what) { return fail(SLA_ERR_HIP, "lobpcg %s: %s", what, hipGetErrorString(e)); };
+    const bool even = (n % 2) == 0;
+    auto aligned = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+
+    // launches on column lists already on the device
+    auto gram = [&](const double* ba, const int32_t* la, int mu, const double* bb, const int32_t* lb, int mv,
+                    bool same, double* out, double* yproj = nullptr) -> hipError_t {
+        return timed(SLA_K_LOB_GRAM, s, [&] {
+            return launch_blk_gram(ba, la, mu, bb, lb, mv, n, d_gpart, out, s, same, yproj);
+        }, false, 8.0 * static_cast<double>(n) * (same ? mu : mu + mv));
     };
-    // out = in Y (Y [|in|][|out|] on the host), optionally the squared column norms
-    auto comb = [&](const double* bin, const Cols& in, const std::vector<double>& Y, double* bout, const Cols& out,
-                    std::vector<double>* norms) -> hipError_t {
-        const int m = static_cast<int>(in.size()), q = static_cast<int>(out.size());
-        const int32_t* din = ar.put(in.data(), in.size(), e);
-        if (e != hipSuccess) return e;
-        for (int c0 = 0; c0 < q; c0 += 32) {
-            const int qc = std::min(32, q - c0);
-            std::vector<double> Yc(static_cast<size_t>(m) * qc);
-            for (int j = 0; j < m; ++j)
-                for (int c = 0; c < qc; ++c) Yc[j * qc + c] = Y[static_cast<size_t>(j) * q + c0 + c];
-            const double* dY = ar.put(Yc.data(), Yc.size(), e);
-            if (e != hipSuccess) return e;
-            const int32_t* dout = ar.put(out.data() + c0, qc, e);
-            if (e != hipSuccess) return e;
-            if ((e = ar.flush(s)) != hipSuccess) return e;
-            e = timed(SLA_K_LOB_COMB, s, [&] {
-                // pairs of rows with 16-byte accesses where every column base allows it
-                const bool pairs = (n % 2 == 0) && (reinterpret_cast<uintptr_t>(bin) & 15) == 0 &&
-                                   (reinterpret_cast<uintptr_t>(bout) & 15) == 0;
-                return launch_blk_comb(bin, din, m, dY, bout, dout, qc, n, norms ? d_cpart : nullptr, s, pairs);
-            }, true, 8.0 * static_cast<double>(n) * (m + qc));
-            if (e != hipSuccess) return e;
-            if (norms) {
-                e = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_reduce(d_cpart, Gc, qc, d_g, s); });
-                if (e != hipSuccess) return e;
-                if ((e = hipMemcpyAsync(h_g, d_g, sizeof(double) * qc, hipMemcpyDeviceToHost, s)) != hipSuccess)
-                    return e;
-                if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-                norms->insert(norms->end(), h_g, h_g + qc);
-            }
-        }
-        if (norms) ar.reset();   // synchronized after the last chunk; din stays valid until then
-        return hipSuccess;
+    auto comb = [&](const double* bin, const int32_t* lin, int m, const double* dY, double* bout,
+                    const int32_t* lout, int q, double* norms) -> hipError_t {
+        hipError_t r = timed(SLA_K_LOB_COMB, s, [&] {
+            // pairs of rows with 16-byte accesses where every column base allows it
+            const bool pairs = even && aligned(bin) && aligned(bout);
+            return launch_blk_comb(bin, lin, m, dY, bout, lout, q, n, norms ? d_cpart : nullptr, s, pairs);
+        }, true, 8.0 * static_cast<double>(n) * (m + q));
+        if (r == hipSuccess && norms)
+            r = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_reduce(d_cpart, Gc, q, norms, s); });
+        return r;
     };
-    auto spmm = [&](const Cols& in, const Cols& out) -> hipError_t {
-        const int32_t* din = ar.put(in.data(), in.size(), e);
-        if (e != hipSuccess) return e;
-        const int32_t* dout = ar.put(out.data(), out.size(), e);
-        if (e != hipSuccess) return e;
+    auto spmm = [&](const int32_t* lin, const int32_t* lout, int q) -> hipError_t {
         // values, columns and row pointers once, each input column once (the gathers are
         // cache traffic), each output column written
         const double bytes = 12.0 * static_cast<double>(A->nnz) + (A->krp_bits / 8.0) * static_cast<double>(n + 1) +
-                             16.0 * static_cast<double>(n) * static_cast<double>(in.size());
-        if ((e = ar.flush(s)) != hipSuccess) return e;
+                             16.0 * static_cast<double>(n) * static_cast<double>(q);
         return timed(SLA_K_LOB_SPMM, s, [&] {
-            return launch_blk_spmm(A->krp, A->krp_bits, A->col, d_vals, pool, din, pool, dout,
-                                   static_cast<int>(in.size()), n, s);
+            return launch_blk_spmm(A->krp, A->krp_bits, A->col, d_vals, pool, lin, pool, lout, q, n, s);
         }, true, bytes);
     };
-    // Z (and AZ) orthonormal: unit-scaled columns, then Cholesky QR twice; false when a
-    // column is zero or a pivot fails.  On success Z, AZ name new columns (the inputs
-    // are released unless they live outside the pool).
-    auto orth = [&](const double* bz, Cols& Z, Cols* AZ, bool& ok) -> hipError_t {
-        const int w = static_cast<int>(Z.size());
-        std::vector<double> G, Rinv, T;
-        ok = false;
-        for (int pass = 0; pass < 2; ++pass) {
-            const double* base = pass == 0 ? bz : pool;
-            if ((e = gram(base, Z, base, Z, G)) != hipSuccess) return e;
-            std::vector<double> nrm(w, 1.0);
-            if (pass == 0) {
-                for (int c = 0; c < w; ++c) {
-                    nrm[c] = std::sqrt(G[c * w + c]);
-                    if (!(nrm[c] > 0.0)) return hipSuccess;
-                }
-                for (int a = 0; a < w; ++a)
-                    for (int b = 0; b < w; ++b) G[a * w + b] = G[a * w + b] / (nrm[a] * nrm[b]);
-            }
-            if (!chol_rinv(G, w, Rinv)) return hipSuccess;
-            T.assign(static_cast<size_t>(w) * w, 0.0);
-            for (int a = 0; a < w; ++a)
-                for (int b = 0; b < w; ++b) T[a * w + b] = Rinv[a * w + b] / nrm[a];
-            Cols Z2, AZ2;
-            if (!take(w, Z2)) return hipErrorOutOfMemory;
-            if ((e = comb(base, Z, T, pool, Z2, nullptr)) != hipSuccess) return e;
-            if (base == pool) give(Z);
-            Z = Z2;
-            if (AZ) {
-                if (!take(w, AZ2)) return hipErrorOutOfMemory;
-                if ((e = comb(pool, *AZ, T, pool, AZ2, nullptr)) != hipSuccess) return e;
-                give(*AZ);
-                *AZ = AZ2;
-            }
-        }
-        ok = true;
+    // the Cholesky QR coefficients of a block (its Gram and factorization) into d_cy
+    auto orth_coef = [&](const double* bz, const int32_t* lz, int w, bool scale, double* flag) -> hipError_t {
+        return timed(SLA_K_LOB_GRAM, s, [&] {
+            return launch_blk_gram_orth(bz, lz, w, n, d_gpart, d_cg, scale, kOrthPivot, flag, d_cy, s);
+        }, false, 8.0 * static_cast<double>(n) * w);
+    };
+    // Z (w columns; AZ alike when given) out of place through two Cholesky QR passes,
+    // unit-scaled first, ending in slots z2 (and az2); flag: the block's flag
+    auto orth = [&](const double* bz, const int32_t* lz, const int32_t* lz1, const int32_t* lz2,
+                    const int32_t* laz, const int32_t* laz1, const int32_t* laz2, int w, double* flag) -> hipError_t {
+        // pass 0: Z -> Z1 (AZ -> AZ1), pass 1: Z1 -> Z2 (AZ1 -> AZ2)
+        if ((e = orth_coef(bz, lz, w, true, flag)) != hipSuccess) return e;
+        if ((e = comb(bz, lz, w, d_cy, pool, lz1, w, nullptr)) != hipSuccess) return e;
+        if (laz && (e = comb(pool, laz, w, d_cy, pool, laz1, w, nullptr)) != hipSuccess) return e;
+        if ((e = orth_coef(pool, lz1, w, false, flag)) != hipSuccess) return e;
+        if ((e = comb(pool, lz1, w, d_cy, pool, lz2, w, nullptr)) != hipSuccess) return e;
+        if (laz && (e = comb(pool, laz1, w, d_cy, pool, laz2, w, nullptr)) != hipSuccess) return e;
         return hipSuccess;
     };
-    // twice Z = Z - B (B^T Z) (AZ = AZ - AB (B^T Z)) against the orthonormal block B
-    auto project = [&](Cols& Z, Cols* AZ, const Cols& B, const Cols* AB) -> hipError_t {
-        const int w = static_cast<int>(Z.size()), b = static_cast<int>(B.size());
-        std::vector<double> C;
-        for (int pass = 0; pass < 2; ++pass) {
-            if ((e = gram(pool, B, pool, Z, C)) != hipSuccess) return e;   // [b][w]
-            std::vector<double> Y(static_cast<size_t>(w + b) * w, 0.0);
-            for (int c = 0; c < w; ++c) Y[c * w + c] = 1.0;
-            for (int j = 0; j < b; ++j)
-                for (int c = 0; c < w; ++c) Y[(w + j) * w + c] = -C[j * w + c];
-            Cols Z2;
-            if (!take(w, Z2)) return hipErrorOutOfMemory;
-            if ((e = comb(pool, cat({&Z, &B}), Y, pool, Z2, nullptr)) != hipSuccess) return e;
-            give(Z);
-            Z = Z2;
-            if (AZ) {
-                Cols AZ2;
-                if (!take(w, AZ2)) return hipErrorOutOfMemory;
-                if ((e = comb(pool, cat({AZ, AB}), Y, pool, AZ2, nullptr)) != hipSuccess) return e;
-                give(*AZ);
-                *AZ = AZ2;
-            }
-        }
+    // one projection pass Z - B (B^T Z) (AZ - AB (B^T Z)) into slots z1 (az1); lzb lists
+    // [Z, B], lazb [AZ, AB]
+    auto project = [&](const int32_t* lb, int b, const int32_t* lz, const int32_t* lzb, const int32_t* lz1,
+                       const int32_t* lazb, const int32_t* laz1, int w) -> hipError_t {
+        // C = B^T Z [b][w], written as the coefficients [I; -C] over [Z, B]
+        if ((e = gram(pool, lb, b, pool, lz, w, false, nullptr, d_cy)) != hipSuccess) return e;
+        if ((e = comb(pool, lzb, w + b, d_cy, pool, lz1, w, nullptr)) != hipSuccess) return e;
+        if (lazb && (e = comb(pool, lazb, w + b, d_cy, pool, laz1, w, nullptr)) != hipSuccess) return e;
         return hipSuccess;
     };
-    // Rayleigh-Ritz on the orthonormal S: theta (k), Y [|S|][k]
-    std::vector<double> theta(k), Ys, Y;
-    auto rayleigh_ritz = [&](const Cols& S, const Cols& AS) -> hipError_t {
-        const int m = static_cast<int>(S.size());
-        std::vector<double> H;
-        if ((e = gram(pool, S, pool, AS, H)) != hipSuccess) return e;
-        std::vector<double> Hs(static_cast<size_t>(m) * m);
-        for (int a = 0; a < m; ++a)
-            for (int b = 0; b < m; ++b) Hs[a * m + b] = 0.5 * (H[a * m + b] + H[b * m + a]);
-        Ys.assign(static_cast<size_t>(k) * m, 0.0);
-        sym_eigpairs(Hs.data(), m, k, largest, theta.data(), Ys.data());
+    // Rayleigh-Ritz on the orthonormal S of m columns (H = S^T AS in hH), keeping the
+    // columns listed: theta (k), Y [m][k] with zero rows for the columns left out, and
+    // the residual coefficients Yr [2k][k] = [I; -diag(theta)]; both uploaded
+    std::vector<double> theta(k), Y, Yr;
+    const double *dY = nullptr, *dYr = nullptr;
+    auto rayleigh_ritz = [&](int m, const std::vector<int>& keep) -> hipError_t {
+        const int me = static_cast<int>(keep.size());
+        std::vector<double> Hs(static_cast<size_t>(me) * me), Ys(static_cast<size_t>(k) * me);
+        for (int a = 0; a < me; ++a)
+            for (int b = 0; b < me; ++b)
+                Hs[a * me + b] = 0.5 * (hH[keep[a] * m + keep[b]] + hH[keep[b] * m + keep[a]]);
+        sym_eigpairs(Hs.data(), me, k, largest, theta.data(), Ys.data());
         Y.assign(static_cast<size_t>(m) * k, 0.0);
         for (int r = 0; r < k; ++r)
-            for (int j = 0; j < m; ++j) Y[j * k + r] = Ys[static_cast<size_t>(r) * m + j];
-        return hipSuccess;
+            for (int j = 0; j < me; ++j) Y[static_cast<size_t>(keep[j]) * k + r] = Ys[static_cast<size_t>(r) * me + j];
+        Yr.assign(static_cast<size_t>(2 * k) * k, 0.0);
+        for (int r = 0; r < k; ++r) {
+            Yr[r * k + r] = 1.0;
+            Yr[(k + r) * k + r] = -theta[r];
+        }
+        ar.reset();
+        dY = ar.put(Y.data(), Y.size(), e);
+        if (e != hipSuccess) return e;
+        dYr = ar.put(Yr.data(), Yr.size(), e);
+        if (e != hipSuccess) return e;
+        return ar.flush(s);
     };
-    auto hip_fail = [&](const char* what) { return fail(SLA_ERR_HIP, "lobpcg %s: %s", what, hipGetErrorString(e)); };
 
     if (jacobi) {   // T = diag(A)^-1, with a count of the rows that have no usable a_ii
         e = timed(SLA_K_LOB_COMB, s, [&] {
             return launch_blk_diag_inv(A->krp, A->krp_bits, A->col, d_vals, n, tinv, d_cpart, s);
         });
-        if (e == hipSuccess) e = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_reduce(d_cpart, Gc, 1, d_g, s); });
+        if (e == hipSuccess) e = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_reduce(d_cpart, Gc, 1, dN, s); });
         if (e != hipSuccess) return hip_fail("jacobi");
-        HIP_TRY(hipMemcpyAsync(h_g, d_g, sizeof(double), hipMemcpyDeviceToHost, s));
         HIP_TRY(hipStreamSynchronize(s));
-        if (h_g[0] != 0.0)
+        if (hN[0] != 0.0)
             return fail(SLA_ERR_INVALID_ARG, "Jacobi needs every diagonal entry stored, finite and positive (%.0f rows "
-                        "have none)", h_g[0]);
+                        "have none)", hN[0]);
     }
-    // W = T R[:, active] (out of place; the inputs are released)
-    auto precondition = [&](Cols& Wc) -> hipError_t {
-        Cols W2;
-        if (!take(static_cast<int>(Wc.size()), W2)) return hipErrorOutOfMemory;
-        const int32_t* din = ar.put(Wc.data(), Wc.size(), e);
-        if (e != hipSuccess) return e;
-        const int32_t* dout = ar.put(W2.data(), W2.size(), e);
-        if (e != hipSuccess) return e;
-        if ((e = ar.flush(s)) != hipSuccess) return e;
-        e = timed(SLA_K_LOB_COMB, s, [&] {
-            return launch_blk_rowscale(pool, din, pool, dout, static_cast<int>(Wc.size()), n, tinv, s);
-        }, true, 8.0 * static_cast<double>(n) * (2 * Wc.size() + 1));
-        if (e != hipSuccess) return e;
-        give(Wc);
-        Wc = W2;
-        return hipSuccess;
-    };
 
-    // start: X = orth(X0), AX = A X, Rayleigh-Ritz on X
-    Cols X(k), AX, P, AP;
-    for (int r = 0; r < k; ++r) X[r] = r;   // rows of the caller's X0
-    bool ok = false;
-    if ((e = orth(d_X0, X, nullptr, ok)) != hipSuccess) return hip_fail("start");
-    if (!ok) return fail(SLA_ERR_INVALID_ARG, "start block X0 is rank deficient (or has a zero row)");
-    if (!take(k, AX)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
-    if ((e = spmm(X, AX)) != hipSuccess) return hip_fail("start");
-    if ((e = rayleigh_ritz(X, AX)) != hipSuccess) return hip_fail("start");
+    // start: X = orth(X0) into slot X[0], AX = A X, Rayleigh-Ritz on X, X = X Y into X[1]
+    const Cols c_x0(allk.begin(), allk.end());   // the caller's rows of X0
+    const Cols c_x[2] = {slot(kSX, allk), slot(kSX + 1, allk)}, c_ax[2] = {slot(kSAX, allk), slot(kSAX + 1, allk)};
+    const Cols c_p[2] = {slot(kSP, allk), slot(kSP + 1, allk)}, c_ap[2] = {slot(kSAP, allk), slot(kSAP + 1, allk)};
+    const Cols c_r = slot(kSR, allk), c_wa = slot(kSWa, allk);
     {
-        Cols X2, AX2;
-        if (!take(k, X2) || !take(k, AX2)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
-        if ((e = comb(pool, X, Y, pool, X2, nullptr)) != hipSuccess) return hip_fail("start");
-        if ((e = comb(pool, AX, Y, pool, AX2, nullptr)) != hipSuccess) return hip_fail("start");
-        give(X);
-        give(AX);
-        X = X2;
-        AX = AX2;
+        lists.room(kPhaseLists);
+        const int32_t* l_x0 = lists.get(c_x0);
+        const int32_t* l_wa = lists.get(c_wa);
+        const int32_t* l_x = lists.get(c_x[0]);
+        const int32_t* l_ax = lists.get(c_ax[0]);
+        const int32_t* l_x1 = lists.get(c_x[1]);
+        const int32_t* l_ax1 = lists.get(c_ax[1]);
+        if ((e = lists.flush(s)) != hipSuccess) return hip_fail("start");
+        if ((e = orth(d_X0, l_x0, l_wa, l_x, nullptr, nullptr, nullptr, k, dF)) != hipSuccess) return hip_fail("start");
+        HIP_TRY(hipStreamSynchronize(s));
+        if (hF[0] == 0.0) return fail(SLA_ERR_INVALID_ARG, "start block X0 is rank deficient (or has a zero row)");
+        if ((e = spmm(l_x, l_ax, k)) != hipSuccess) return hip_fail("start");
+        if ((e = gram(pool, l_x, k, pool, l_ax, k, false, dH)) != hipSuccess) return hip_fail("start");
+        HIP_TRY(hipStreamSynchronize(s));
+        if ((e = rayleigh_ritz(k, allk)) != hipSuccess) return hip_fail("start");
+        if ((e = comb(pool, l_x, k, dY, pool, l_x1, k, nullptr)) != hipSuccess) return hip_fail("start");
+        if ((e = comb(pool, l_ax, k, dY, pool, l_ax1, k, nullptr)) != hipSuccess) return hip_fail("start");
     }
+    int par = 1;         // X, AX (and P, AP) live in slot kSX + par ...
+    bool has_p = false;  // no P before the first iteration
     int64_t it = 0;
     int state = SLA_MAX_ITER;
     std::vector<double> res(k);
     while (true) {
-        // residuals R = A X - X diag(theta) and their norms
-        Cols R;
-        if (!take(k, R)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
-        std::vector<double> Yr(static_cast<size_t>(2 * k) * k, 0.0), nr;
-        for (int r = 0; r < k; ++r) {
-            Yr[r * k + r] = 1.0;
-            Yr[(k + r) * k + r] = -theta[r];
+        // residuals R = A X - X diag(theta), their squared norms straight to host memory
+        {
+            const Cols in = cat({&c_ax[par], &c_x[par]});
+            lists.room(kPhaseLists);
+            const int32_t* l_in = lists.get(in);
+            const int32_t* l_r = lists.get(c_r);
+            if ((e = lists.flush(s)) != hipSuccess) return hip_fail("residual");
+            if ((e = comb(pool, l_in, 2 * k, dYr, pool, l_r, k, dN)) != hipSuccess) return hip_fail("residual");
+            HIP_TRY(hipStreamSynchronize(s));
         }
-        if ((e = comb(pool, cat({&AX, &X}), Yr, pool, R, &nr)) != hipSuccess) return hip_fail("residual");
         std::vector<int> active;
         for (int r = 0; r < k; ++r) {
-            res[r] = std::sqrt(nr[r]);
+            res[r] = std::sqrt(hN[r]);
             if (res[r] > opts->tol * std::fabs(theta[r])) active.push_back(r);
         }
         if (active.empty() || it == max_iter) {
             state = active.empty() ? SLA_CONVERGED : SLA_MAX_ITER;
-            give(R);
             break;
         }
         ++it;
-        Cols W, AW, Pa, APa;
-        for (int r = 0; r < k; ++r) {
-            const bool act = std::find(active.begin(), active.end(), r) != active.end();
-            if (act) W.push_back(R[r]);
-            else free_cols.push_back(R[r]);
-            if (!P.empty()) {
-                if (act) {
-                    Pa.push_back(P[r]);
-                    APa.push_back(AP[r]);
-                } else {
-                    free_cols.push_back(P[r]);
-                    free_cols.push_back(AP[r]);
-                }
-            }
-        }
-        P.clear();
-        AP.clear();
-        if (jacobi && (e = precondition(W)) != hipSuccess) return hip_fail("preconditioner");
-        if ((e = project(W, nullptr, X, nullptr)) != hipSuccess) return hip_fail("projection");
-        bool wok = false;
-        if ((e = orth(pool, W, nullptr, wok)) != hipSuccess) return hip_fail("orthonormalization");
-        if (!wok) {
-            give(W);
-            W.clear();
-        } else {
-            if (!take(static_cast<int>(W.size()), AW)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
-            if ((e = spmm(W, AW)) != hipSuccess) return hip_fail("spmm");
-        }
-        if (!Pa.empty()) {
-            const Cols B = cat({&X, &W}), AB = cat({&AX, &AW});
-            if ((e = project(Pa, &APa, B, &AB)) != hipSuccess) return hip_fail("projection");
-            bool pok = false;
-            if ((e = orth(pool, Pa, &APa, pok)) != hipSuccess) return hip_fail("orthonormalization");
-            if (!pok) {
-                give(Pa);
-                give(APa);
-                Pa.clear();
-                APa.clear();
-            }
-        }
-        const Cols S = cat({&X, &W, &Pa}), AS = cat({&AX, &AW, &APa});
+        const int a = static_cast<int>(active.size());
+        std::vector<int> ia(a);
+        for (int j = 0; j < a; ++j) ia[j] = j;
+        const Cols &X = c_x[par], &AX = c_ax[par];
+        const Cols RA = slot(kSR, active), PA = slot(kSP + par, active), APA = slot(kSAP + par, active);
+        const Cols Wa = slot(kSWa, ia), Wb = slot(kSWb, ia), Wc = slot(kSWc, ia), AW = slot(kSAW, ia);
+        const Cols Pa = slot(kSPa, ia), Pb = slot(kSPb, ia), APa = slot(kSAPa, ia), APb = slot(kSAPb, ia);
+        const Cols& Z0 = jacobi ? Wc : RA;
+        const Cols Z0X = cat({&Z0, &X}), WaX = cat({&Wa, &X});
+        const Cols B = cat({&X, &Wb}), AB = cat({&AX, &AW});
+        const Cols PAB = cat({&PA, &B}), APAAB = cat({&APA, &AB}), PaB = cat({&Pa, &B}), APaAB = cat({&APa, &AB});
+        const Cols S = has_p ? cat({&X, &Wb, &Pb}) : cat({&X, &Wb});
+        const Cols AS = has_p ? cat({&AX, &AW, &APb}) : cat({&AX, &AW});
+        const Cols Sk(S.begin() + k, S.end()), ASk(AS.begin() + k, AS.end());
         const int m = static_cast<int>(S.size());
-        if ((e = rayleigh_ritz(S, AS)) != hipSuccess) return hip_fail("rayleigh-ritz");
-        Cols X2, AX2, P2, AP2;
-        if (!take(k, X2) || !take(k, AX2)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
-        if ((e = comb(pool, S, Y, pool, X2, nullptr)) != hipSuccess) return hip_fail("ritz vectors");
-        if ((e = comb(pool, AS, Y, pool, AX2, nullptr)) != hipSuccess) return hip_fail("ritz vectors");
-        if (m > k) {   // P = S[k:] Y[k:], AP = AS[k:] Y[k:]
-            const Cols Sk(S.begin() + k, S.end()), ASk(AS.begin() + k, AS.end());
-            std::vector<double> Yk(Y.begin() + static_cast<size_t>(k) * k, Y.end());
-            if (!take(k, P2) || !take(k, AP2)) return fail(SLA_ERR_HIP, "lobpcg: block pool exhausted");
-            if ((e = comb(pool, Sk, Yk, pool, P2, nullptr)) != hipSuccess) return hip_fail("directions");
-            if ((e = comb(pool, ASk, Yk, pool, AP2, nullptr)) != hipSuccess) return hip_fail("directions");
+        const int nx = 1 - par;
+        lists.room(kPhaseLists);
+        const int32_t *l_x = lists.get(X), *l_ra = lists.get(RA), *l_wc = lists.get(Wc), *l_z0 = lists.get(Z0);
+        const int32_t *l_z0x = lists.get(Z0X), *l_wa = lists.get(Wa), *l_wax = lists.get(WaX), *l_wb = lists.get(Wb);
+        const int32_t *l_aw = lists.get(AW), *l_s = lists.get(S), *l_as = lists.get(AS);
+        const int32_t *l_sk = lists.get(Sk), *l_ask = lists.get(ASk);
+        const int32_t *l_xn = lists.get(c_x[nx]), *l_axn = lists.get(c_ax[nx]);
+        const int32_t *l_pn = lists.get(c_p[nx]), *l_apn = lists.get(c_ap[nx]);
+        const int32_t *l_b = nullptr, *l_pa0 = nullptr, *l_pab = nullptr, *l_apab = nullptr, *l_pa = nullptr;
+        const int32_t *l_apa = nullptr, *l_pa_b = nullptr, *l_apa_ab = nullptr, *l_pb = nullptr, *l_apb = nullptr;
+        if (has_p) {
+            l_b = lists.get(B);
+            l_pa0 = lists.get(PA);
+            l_pab = lists.get(PAB);
+            l_apab = lists.get(APAAB);
+            l_pa = lists.get(Pa);
+            l_apa = lists.get(APa);
+            l_pa_b = lists.get(PaB);
+            l_apa_ab = lists.get(APaAB);
+            l_pb = lists.get(Pb);
+            l_apb = lists.get(APb);
         }
-        give(S);
-        give(AS);
-        X = X2;
-        AX = AX2;
-        P = P2;
-        AP = AP2;
+        if ((e = lists.flush(s)) != hipSuccess) return hip_fail("lists");
+        // W = T R[:, active] with Jacobi, then made orthonormal against X and orthonormal
+        if (jacobi) {
+            e = timed(SLA_K_LOB_COMB, s, [&] { return launch_blk_rowscale(pool, l_ra, pool, l_wc, a, n, tinv, s); },
+                      true, 8.0 * static_cast<double>(n) * (2 * a + 1));
+            if (e != hipSuccess) return hip_fail("preconditioner");
+        }
+        if ((e = project(l_x, k, l_z0, l_z0x, l_wa, nullptr, nullptr, a)) != hipSuccess) return hip_fail("projection");
+        if ((e = project(l_x, k, l_wa, l_wax, l_wb, nullptr, nullptr, a)) != hipSuccess) return hip_fail("projection");
+        if ((e = orth(pool, l_wb, l_wa, l_wb, nullptr, nullptr, nullptr, a, dF)) != hipSuccess)
+            return hip_fail("orthonormalization");
+        if ((e = spmm(l_wb, l_aw, a)) != hipSuccess) return hip_fail("spmm");
+        // P = P[:, active] (AP alike) made orthonormal against [X, W] and orthonormal; a
+        // block that fails is zero from there on and left out of the Rayleigh-Ritz step
+        if (has_p) {
+            if ((e = project(l_b, k + a, l_pa0, l_pab, l_pa, l_apab, l_apa, a)) != hipSuccess)
+                return hip_fail("projection");
+            if ((e = project(l_b, k + a, l_pa, l_pa_b, l_pb, l_apa_ab, l_apb, a)) != hipSuccess)
+                return hip_fail("projection");
+            if ((e = orth(pool, l_pb, l_pa, l_pb, l_apb, l_apa, l_apb, a, dF + 1)) != hipSuccess)
+                return hip_fail("orthonormalization");
+        }
+        if ((e = gram(pool, l_s, m, pool, l_as, m, false, dH)) != hipSuccess) return hip_fail("rayleigh-ritz");
+        HIP_TRY(hipStreamSynchronize(s));
+        std::vector<int> keep(allk);
+        if (hF[0] != 0.0)
+            for (int j = 0; j < a; ++j) keep.push_back(k + j);
+        if (has_p && hF[1] != 0.0)
+            for (int j = 0; j < a; ++j) keep.push_back(k + a + j);
+        if ((e = rayleigh_ritz(m, keep)) != hipSuccess) return hip_fail("rayleigh-ritz");
+        // X = S Y, AX = AS Y; P = S[k:] Y[k:], AP = AS[k:] Y[k:] (Knyazev's direction),
+        // X and P in one pass over S (AX and AP over AS) where rows pair up
+        if (even) {
+            const double bytes = 8.0 * static_cast<double>(n) * (m + 2 * k);
+            e = timed(SLA_K_LOB_COMB, s, [&] {
+                return launch_blk_comb_dual(pool, l_s, m, k, dY, pool, l_xn, l_pn, k, n, s);
+            }, true, bytes);
+            if (e == hipSuccess)
+                e = timed(SLA_K_LOB_COMB, s, [&] {
+                    return launch_blk_comb_dual(pool, l_as, m, k, dY, pool, l_axn, l_apn, k, n, s);
+                }, true, bytes);
+            if (e != hipSuccess) return hip_fail("ritz vectors");
+        } else {
+            if ((e = comb(pool, l_s, m, dY, pool, l_xn, k, nullptr)) != hipSuccess) return hip_fail("ritz vectors");
+            if ((e = comb(pool, l_as, m, dY, pool, l_axn, k, nullptr)) != hipSuccess) return hip_fail("ritz vectors");
+            const double* dYk = dY + static_cast<size_t>(k) * k;
+            if ((e = comb(pool, l_sk, m - k, dYk, pool, l_pn, k, nullptr)) != hipSuccess) return hip_fail("directions");
+            if ((e = comb(pool, l_ask, m - k, dYk, pool, l_apn, k, nullptr)) != hipSuccess)
+                return hip_fail("directions");
+        }
+        par = nx;
+        has_p = true;
     }
     // unit Ritz vectors signed by <u_r, X0[r]>, written to d_evecs
-    std::vector<double> Gxx, Gx0;
-    Cols R0(k);
-    for (int r = 0; r < k; ++r) R0[r] = r;
-    if ((e = gram(pool, X, pool, X, Gxx)) != hipSuccess) return hip_fail("output");
-    if ((e = gram(pool, X, d_X0, R0, Gx0)) != hipSuccess) return hip_fail("output");
-    std::vector<double> Yo(static_cast<size_t>(k) * k, 0.0);
-    for (int r = 0; r < k; ++r) {
-        const double nu = std::sqrt(Gxx[r * k + r]);
-        const double sgn = Gx0[r * k + r] < 0.0 ? -1.0 : 1.0;
-        Yo[r * k + r] = 1.0 / (sgn * nu);
+    {
+        lists.room(kPhaseLists);
+        const int32_t* l_x = lists.get(c_x[par]);
+        const int32_t* l_x0 = lists.get(c_x0);
+        if ((e = lists.flush(s)) != hipSuccess) return hip_fail("output");
+        if ((e = gram(pool, l_x, k, pool, l_x, k, true, dH)) != hipSuccess) return hip_fail("output");
+        if ((e = gram(pool, l_x, k, d_X0, l_x0, k, false, dH + static_cast<size_t>(k) * k)) != hipSuccess)
+            return hip_fail("output");
+        HIP_TRY(hipStreamSynchronize(s));
+        std::vector<double> Yo(static_cast<size_t>(k) * k, 0.0);
+        for (int r = 0; r < k; ++r) {
+            const double nu = std::sqrt(hH[r * k + r]);
+            const double sgn = hH[static_cast<size_t>(k) * k + r * k + r] < 0.0 ? -1.0 : 1.0;
+            Yo[r * k + r] = 1.0 / (sgn * nu);
+        }
+        ar.reset();
+        const double* dYo = ar.put(Yo.data(), Yo.size(), e);
+        if (e != hipSuccess) return hip_fail("output");
+        const double* dth = ar.put(theta.data(), theta.size(), e);
+        if (e != hipSuccess) return hip_fail("output");
+        HIP_TRY(ar.flush(s));
+        if ((e = comb(pool, l_x, k, dYo, d_evecs, l_x0, k, nullptr)) != hipSuccess) return hip_fail("output");
+        HIP_TRY(hipMemcpyAsync(d_evals, dth, sizeof(double) * k, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        ar.reset();
     }
-    if ((e = comb(pool, X, Yo, d_evecs, R0, nullptr)) != hipSuccess) return hip_fail("output");
-    const double* dth = ar.put(theta.data(), theta.size(), e);
-    if (e != hipSuccess) return hip_fail("output");
-    HIP_TRY(ar.flush(s));
-    HIP_TRY(hipMemcpyAsync(d_evals, dth, sizeof(double) * k, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(hipStreamSynchronize(s));
-    ar.reset();
     info->iterations = it;
     info->state = state;
     info->restarts = 0;

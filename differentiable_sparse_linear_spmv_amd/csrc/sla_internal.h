@@ -214,10 +214,14 @@ hipError_t launch_blk_spmm(const void* rp, int rp_bits, const int32_t* col, cons
                            const int32_t* idx_in, double* out, const int32_t* idx_out, int q, int64_t n,
                            hipStream_t s);
 // out[a mv + b] = <A[ia[a]], B[ib[b]]> (a < mu, b < mv, both <= kBlkMaxCols), summed in
-// a fixed order; part: blk_gram_groups(n) * mu * mv doubles of scratch (at most).
+// a fixed order; part: blk_gram_groups(n) * mu * mv doubles of scratch (at most).  same:
+// B's columns are A's (mu == mv; B and ib are not read), which are then loaded once.
+// yproj (mu >= mv): instead of out, the coefficients [I; -out] [(mv + mu)][mv] of the
+// projection Z - B (B^T Z) over [Z, B] (A = B, the orthonormal block; B = Z).
 int blk_gram_groups(int64_t n);
 hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib, int mv,
-                           int64_t n, double* part, double* out, hipStream_t s);
+                           int64_t n, double* part, double* out, hipStream_t s, bool same = false,
+                           double* yproj = nullptr);
 // out[idx_out[c]] = sum_j Y[j][c] in[idx_in[j]] (c < q <= 32, Y [m][q]); part (nullable):
 // blk_comb_groups(n) * q partials of |out[c]|^2, [group][c].  out must not alias in.
 int blk_comb_groups(int64_t n);
@@ -227,6 +231,17 @@ hipError_t launch_blk_reduce(const double* part, int G, int np, double* out, hip
 // is missing, not finite or not positive (tinv 0 there).
 hipError_t launch_blk_diag_inv(const void* rp, int rp_bits, const int32_t* col, const double* vals, int64_t n,
                                double* tinv, double* part, hipStream_t s);
+// T [w][w] (w <= SLA_EIG_MAX_K): the Cholesky QR coefficients of the block Z = A[ia[c]]
+// (c < w) from its Gram matrix (left in gram, w w doubles), Z T orthonormal; scale: unit
+// columns first.  part: scratch as for launch_blk_gram.  flag (device-visible): set with
+// scale, read otherwise; a failed block gets T = 0 and flag 0.
+hipError_t launch_blk_gram_orth(const double* A, const int32_t* ia, int w, int64_t n, double* part, double* gram,
+                                bool scale, double pivot, double* flag, double* T, hipStream_t s);
+// out[idx_out[c]] = sum_{j < m} Y[j][c] in[idx_in[j]] and out[idx_out2[c]] = the same sum
+// from j = j0, in one pass (c < q <= 32, Y [m][q]); n even, in and out 16-byte aligned.
+hipError_t launch_blk_comb_dual(const double* in, const int32_t* idx_in, int m, int j0, const double* Y,
+                                double* out, const int32_t* idx_out, const int32_t* idx_out2, int q, int64_t n,
+                                hipStream_t s);
 // out[idx_out[c]][i] = in[idx_in[c]][i] * t[i], c < q.
 hipError_t launch_blk_rowscale(const double* in, const int32_t* idx_in, double* out, const int32_t* idx_out, int q,
                                int64_t n, const double* t, hipStream_t s);

@@ -2981,6 +2981,287 @@ __global__ __launch_bounds__(kBlock) void k_blk_gram_tiled(const double* __restr
     }
 }
 
+// Gram partials with the slice loads pipelined (n even, every column base 16-byte
+// aligned).  Slice sl holds rows [sl R, sl R + R) of the ncol operand columns (ncol = mu,
+// or mu + mv when B's columns are not A's), staged in LDS at stride R + 2; R is a power
+// of two with ncol R <= 4096.  Thread t owns the 16-byte pieces e = t + u kBlock (column
+// e / (R / 2), row pair e % (R / 2)): it issues the loads of its workgroup's next slice
+// before the products of the current one, and stores them after.  The products run in
+// TA x TB register tiles over (a, b); tpt threads (a power of two) share a tile over rows
+// r = sub, sub + tpt, ..., their sums combined at the end by a butterfly within the wave
+// and then in wave order.  Every pair's sum runs over its rows in a fixed order.
+template <int TA, int TB, int PT, int U>
+__global__ __launch_bounds__(kBlock) void k_blk_gram_pipe(const double* __restrict__ A,
+                                                          const int32_t* __restrict__ ia, int mu,
+                                                          const double* __restrict__ B,
+                                                          const int32_t* __restrict__ ib, int mv, int same, int64_t n,
+                                                          int lgh, int tpt, double* __restrict__ part)
+{
+    extern __shared__ double s_g[];
+    const int tid = threadIdx.x;
+    const int R2 = 1 << lgh, R = 2 * R2, pad = R + 2;
+    const int ncol = same ? mu : mu + mv;
+    const int E = ncol * R2;
+    const int np = mu * mv;
+    const int boff = same ? 0 : mu;
+    const int tu = (mu + TA - 1) / TA, tv = (mv + TB - 1) / TB, ntile = tu * tv;
+    const int sub = tid % tpt;
+    const int lanes = kBlock / tpt;
+    // this thread's pieces: source column start (row 0) and LDS offset
+    const double* src[U];
+    int dst[U], off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = min(tid + u * kBlock, E - 1);   // pieces past E repeat the last one
+        const int c = e >> lgh;
+        const int r2 = e & (R2 - 1);
+        const double* base = c < mu ? A : B;
+        const int32_t ci = c < mu ? ia[c] : ib[c - mu];
+        src[u] = base + static_cast<int64_t>(ci) * n;
+        off[u] = 2 * r2;
+        dst[u] = tid + u * kBlock < E ? c * pad + 2 * r2 : -1;
+    }
+    double acc[PT][TA * TB];
+    int ra[PT][TA], rb[PT][TB];
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+        const int tile = min(tid / tpt + p * lanes, ntile - 1);
+        const int ta = tile / tv, tb = tile - ta * tv;
+#pragma unroll
+        for (int d = 0; d < TA; ++d) ra[p][d] = min(TA * ta + d, mu - 1) * pad;
+#pragma unroll
+        for (int d = 0; d < TB; ++d) rb[p][d] = (boff + min(TB * tb + d, mv - 1)) * pad;
+#pragma unroll
+        for (int e = 0; e < TA * TB; ++e) acc[p][e] = 0.0;
+    }
+    const int64_t nslices = (n + R - 1) / R;
+    const int64_t G = gridDim.x;
+    double2 v[U];
+    // the loads of slice sl (rows past n read the last pair; the store zeroes them, so
+    // nothing waits on a load before the products of the slice in LDS)
+    auto load = [&](int64_t sl) __attribute__((always_inline)) {
+        const int64_t r0 = sl * R;
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const double2*>(src[u] + min(r0 + off[u], n - 2));
+    };
+    auto store = [&](int64_t sl) __attribute__((always_inline)) {
+        const int64_t r0 = sl * R;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (dst[u] >= 0)
+                *reinterpret_cast<double2*>(s_g + dst[u]) = r0 + off[u] < n ? v[u] : double2{0.0, 0.0};
+    };
+    int64_t sl = blockIdx.x;
+    if (sl < nslices) {
+        load(sl);
+        store(sl);
+    }
+    __syncthreads();
+    for (; sl < nslices; sl += G) {
+        const int nr = static_cast<int>(min(static_cast<int64_t>(R), n - sl * R));
+        // the next slice's loads (the last slice reloads itself: cache hits, never stored)
+        const bool more = sl + G < nslices;
+        load(more ? sl + G : sl);
+#pragma unroll
+        for (int p = 0; p < PT; ++p) {
+            for (int r = sub; r < nr; r += tpt) {
+                double xa[TA], xb[TB];
+#pragma unroll
+                for (int d = 0; d < TA; ++d) xa[d] = s_g[ra[p][d] + r];
+#pragma unroll
+                for (int d = 0; d < TB; ++d) xb[d] = s_g[rb[p][d] + r];
+#pragma unroll
+                for (int da = 0; da < TA; ++da)
+#pragma unroll
+                    for (int db = 0; db < TB; ++db) {
+                        const double q = xa[da] * xb[db];
+                        acc[p][da * TB + db] = acc[p][da * TB + db] + q;
+                    }
+            }
+        }
+        __syncthreads();
+        if (more) store(sl + G);
+        __syncthreads();
+    }
+    // the tpt partial sums of each tile entry: a butterfly over the tile's lanes of one
+    // wave (every lane ends with the same sum), then, for tiles wider than a wave, the
+    // waves' sums added in wave order
+    const int wl = min(tpt, 64);
+#pragma unroll
+    for (int p = 0; p < PT; ++p)
+#pragma unroll
+        for (int e = 0; e < TA * TB; ++e)
+            for (int off = 1; off < wl; off <<= 1) acc[p][e] = acc[p][e] + __shfl_xor(acc[p][e], off, 64);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (tpt > 64) {   // PT == 1 here (ntile <= 2)
+        if (lane == 0)
+#pragma unroll
+            for (int e = 0; e < TA * TB; ++e) s_g[wave * TA * TB + e] = acc[0][e];
+        __syncthreads();
+        const int tile = tid / tpt;
+        const int ta = tile / tv, tb = tile - ta * tv;
+        if (sub == 0 && tile < ntile)
+#pragma unroll
+            for (int e = 0; e < TA * TB; ++e) {
+                double t = 0.0;
+                for (int w = 0; w < tpt / 64; ++w) t = t + s_g[(wave + w) * TA * TB + e];
+                const int a = TA * ta + e / TB, b = TB * tb + e % TB;
+                if (a < mu && b < mv) part[static_cast<int64_t>(blockIdx.x) * np + a * mv + b] = t;
+            }
+        return;
+    }
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+        const int tile = tid / tpt + p * lanes;
+        const int ta = tile / tv, tb = tile - ta * tv;
+        if (sub == 0 && tile < ntile)
+#pragma unroll
+            for (int e = 0; e < TA * TB; ++e) {
+                const int a = TA * ta + e / TB, b = TB * tb + e % TB;
+                if (a < mu && b < mv) part[static_cast<int64_t>(blockIdx.x) * np + a * mv + b] = acc[p][e];
+            }
+    }
+    (void)lane;
+}
+
+// Gram partials streamed like the combinations, with no staging (n even, column bases
+// 16-byte aligned): NTP lanes share each pair of rows, lane t of them holding tile t, a
+// TA x TB register tile of the products (columns past mu or mv repeat the last one and
+// are not written).  A wave covers 64 / NTP row pairs, the grid strides over them, and
+// each pair's sum runs over rows in a fixed order: a lane's rows in order, then a
+// butterfly over the wave's lanes of the same tile, then the four waves in order.
+template <int TA, int TB, int NTP>
+__global__ __launch_bounds__(kBlock) void k_blk_gram_rt(const double* __restrict__ A, const int32_t* __restrict__ ia,
+                                                        int mu, const double* __restrict__ B,
+                                                        const int32_t* __restrict__ ib, int mv, int64_t n,
+                                                        double* __restrict__ part)
+{
+    constexpr int RPW = 64 / NTP;   // row pairs of a wave
+    __shared__ double s_w[kBlock / 64][NTP][TA * TB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = lane / RPW, rp = lane - t * RPW;
+    const int tu = (mu + TA - 1) / TA, tv = (mv + TB - 1) / TB, ntile = tu * tv;
+    const int tt = min(t, ntile - 1);
+    const int ta = tt / tv, tb = tt - ta * tv;
+    const double2* pa[TA];
+    const double2* pb[TB];
+#pragma unroll
+    for (int d = 0; d < TA; ++d)
+        pa[d] = reinterpret_cast<const double2*>(A + static_cast<int64_t>(ia[min(TA * ta + d, mu - 1)]) * n);
+#pragma unroll
+    for (int d = 0; d < TB; ++d)
+        pb[d] = reinterpret_cast<const double2*>(B + static_cast<int64_t>(ib[min(TB * tb + d, mv - 1)]) * n);
+    double acc[TA * TB];
+#pragma unroll
+    for (int e = 0; e < TA * TB; ++e) acc[e] = 0.0;
+    const int64_t n2 = n >> 1;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kBlock / 64) * RPW;
+    for (int64_t i2 = (static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + wave) * RPW + rp; i2 < n2; i2 += step) {
+        double2 xa[TA], xb[TB];
+#pragma unroll
+        for (int d = 0; d < TA; ++d) xa[d] = pa[d][i2];
+#pragma unroll
+        for (int d = 0; d < TB; ++d) xb[d] = pb[d][i2];
+#pragma unroll
+        for (int da = 0; da < TA; ++da)
+#pragma unroll
+            for (int db = 0; db < TB; ++db) {
+                const double px = xa[da].x * xb[db].x;
+                const double py = xa[da].y * xb[db].y;
+                acc[da * TB + db] = acc[da * TB + db] + px;
+                acc[da * TB + db] = acc[da * TB + db] + py;
+            }
+    }
+#pragma unroll
+    for (int e = 0; e < TA * TB; ++e)
+        for (int off = 1; off < RPW; off <<= 1) acc[e] = acc[e] + __shfl_xor(acc[e], off, 64);
+    if (rp == 0)
+#pragma unroll
+        for (int e = 0; e < TA * TB; ++e) s_w[wave][t][e] = acc[e];
+    __syncthreads();
+    const int np = mu * mv;
+    for (int q = tid; q < NTP * TA * TB; q += kBlock) {
+        const int tq = q / (TA * TB), e = q - tq * (TA * TB);
+        if (tq >= ntile) continue;
+        double v = 0.0;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) v = v + s_w[w][tq][e];
+        const int qa = tq / tv, qb = tq - qa * tv;
+        const int a = TA * qa + e / TB, b = TB * qb + e % TB;
+        if (a < mu && b < mv) part[static_cast<int64_t>(blockIdx.x) * np + a * mv + b] = v;
+    }
+}
+
+// Small dense steps of LOBPCG, on the device so the host never waits for them.
+constexpr int kCoefMax = SLA_EIG_MAX_K;   // widest block factored here
+
+// Cholesky QR coefficients of a block of w <= kCoefMax columns from its Gram matrix G0
+// [w][w], one wave.  scale: the columns are first taken to unit norm (G_ab / (|z_a| |z_b|)
+// with |z_c| = sqrt(G_cc); a zero column fails).  G is then symmetrized and factored as
+// R^T R column by column, each pivot tested against pivot times the largest diagonal
+// entry; T = R^-1, times diag(1 / |z|) with scale, so that Z T has orthonormal columns.
+// The sums run in the order of the textbook algorithm (ascending inner index).  flag:
+// written with scale, read otherwise; a block that fails, or failed in the pass before,
+// gets T = 0 (its columns become zero) and flag 0.
+__global__ __launch_bounds__(64) void k_blk_orth_coef(const double* __restrict__ G0, int w, int scale, double pivot,
+                                                      double* flag, double* __restrict__ T)
+{
+    __shared__ double s_g[kCoefMax * kCoefMax], s_l[kCoefMax * kCoefMax], s_nrm[kCoefMax];
+    __shared__ double s_gmax;
+    __shared__ int s_ok;
+    const int t = threadIdx.x;
+    const int np = w * w;
+    if (t == 0) s_ok = scale ? 1 : (*flag != 0.0 ? 1 : 0);
+    if (t < w) s_nrm[t] = scale ? sqrt(G0[t * w + t]) : 1.0;
+    __syncthreads();
+    if (t == 0)
+        for (int c = 0; c < w; ++c)
+            if (!(s_nrm[c] > 0.0)) s_ok = 0;
+    for (int e = t; e < np; e += 64) {
+        const int a = e / w, b = e - a * w;
+        const double gab = scale ? G0[e] / (s_nrm[a] * s_nrm[b]) : G0[e];
+        const double gba = scale ? G0[b * w + a] / (s_nrm[b] * s_nrm[a]) : G0[b * w + a];
+        s_g[e] = 0.5 * (gab + gba);
+        s_l[e] = 0.0;
+    }
+    __syncthreads();
+    if (t == 0) {
+        double gmax = 0.0;
+        for (int a = 0; a < w; ++a) gmax = fmax(gmax, s_g[a * w + a]);
+        s_gmax = gmax;
+    }
+    __syncthreads();
+    for (int j = 0; j < w && s_ok; ++j) {   // s_ok is uniform at every test
+        if (t == 0) {
+            double d = s_g[j * w + j];
+            for (int p = 0; p < j; ++p) d -= s_l[j * w + p] * s_l[j * w + p];
+            if (d > pivot * s_gmax) s_l[j * w + j] = sqrt(d);
+            else s_ok = 0;
+        }
+        __syncthreads();
+        if (s_ok && t > j && t < w) {
+            double v = s_g[t * w + j];
+            for (int p = 0; p < j; ++p) v -= s_l[t * w + p] * s_l[j * w + p];
+            s_l[t * w + j] = v / s_l[j * w + j];
+        }
+        __syncthreads();
+    }
+    // column c of R^-1 (R = L^T), rows c down to 0, into s_g (each lane its own column)
+    if (s_ok && t < w) {
+        const int c = t;
+        for (int i = w - 1; i > c; --i) s_g[i * w + c] = 0.0;
+        for (int i = c; i >= 0; --i) {
+            double v = (i == c) ? 1.0 : 0.0;
+            for (int p = i + 1; p <= c; ++p) v -= s_l[p * w + i] * s_g[p * w + c];
+            s_g[i * w + c] = v / s_l[i * w + i];
+        }
+    }
+    __syncthreads();
+    const bool ok = s_ok != 0;
+    for (int e = t; e < np; e += 64) T[e] = ok ? s_g[e] / s_nrm[e / w] : 0.0;
+    if (t == 0) *flag = ok ? 1.0 : 0.0;
+}
+
 // tinv[i] = 1 / a_ii (binary search for column i in row i; the columns are sorted), and
 // per workgroup the number of rows whose a_ii is missing, not finite or not positive
 // (part[blockIdx.x], as a double).
@@ -3030,16 +3311,24 @@ __global__ __launch_bounds__(kBlock) void k_blk_rowscale(const double* __restric
 }
 
 // out[p] = sum over g < G of part[g][p], p < np: one workgroup per p, a fixed order
-// (strided partial sums, then the workgroup tree).
+// (strided partial sums, then the workgroup tree).  yproj (for a Gram C = B^T Z [b][w],
+// b >= w): the projection coefficients Y [(w + b)][w] = [I; -C] instead.
 __global__ __launch_bounds__(kBlock) void k_blk_reduce(const double* __restrict__ part, int G, int np,
-                                                       double* __restrict__ out)
+                                                       double* __restrict__ out, double* __restrict__ yproj, int w)
 {
     __shared__ double s_red[kBlock / 64];
     const int p = blockIdx.x;
     double v = 0.0;
     for (int g = threadIdx.x; g < G; g += kBlock) v = v + part[static_cast<int64_t>(g) * np + p];
     v = block_sum(v, s_red);
-    if (threadIdx.x == 0) out[p] = v;
+    if (threadIdx.x == 0) {
+        if (yproj) {
+            yproj[w * w + p] = -v;
+            if (p < w * w) yproj[p] = (p / w == p % w) ? 1.0 : 0.0;
+        } else {
+            out[p] = v;
+        }
+    }
 }
 
 // out[c] = sum_j Y[j][c] in[j] (j ascending) for c < q (q <= QQ), Y [m][q]; with part,
@@ -3165,6 +3454,64 @@ __global__ __launch_bounds__(kBlock) void k_blk_comb2(const double* __restrict__
             const double sv = block_sum(nrm[u], s_red);
             if (threadIdx.x == 0 && u < q) part[static_cast<int64_t>(blockIdx.x) * q + u] = sv;
         }
+    }
+}
+
+// Two combinations in one pass over the inputs, on pairs of rows as in k_blk_comb2:
+// out[c] = sum_{j < m} Y[j][c] in[j] and out2[c] = sum_{j0 <= j < m} Y[j][c] in[j]
+// (c < q), each sum in ascending j from its own first term, so each equals what a pass
+// of its own gives.  The Ritz step's X = S Y with P = S[j0:] Y[j0:].
+template <int QQ>
+__global__ __launch_bounds__(kBlock) void k_blk_comb2d(const double* __restrict__ in,
+                                                       const int32_t* __restrict__ idx_in, int m, int j0,
+                                                       const double* __restrict__ Y, double* __restrict__ out,
+                                                       const int32_t* __restrict__ idx_out,
+                                                       const int32_t* __restrict__ idx_out2, int q, int64_t n)
+{
+    const int64_t n2 = n >> 1;
+    for (int64_t i2 = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i2 < n2;
+         i2 += static_cast<int64_t>(gridDim.x) * kBlock) {
+        double ax[QQ], ay[QQ], bx[QQ], by[QQ];
+#pragma unroll
+        for (int u = 0; u < QQ; ++u) ax[u] = ay[u] = bx[u] = by[u] = 0.0;
+        // terms of inputs j .. j + G - 1 (G = 4 or 1); BOTH: they enter the second sum too
+        auto terms = [&](int j, auto group, auto both) __attribute__((always_inline)) {
+            constexpr int G = decltype(group)::value;
+            double2 v[G];
+#pragma unroll
+            for (int t = 0; t < G; ++t)
+                v[t] = reinterpret_cast<const double2*>(in + static_cast<int64_t>(ld_uniform_i(idx_in, j + t)) * n)[i2];
+#pragma unroll
+            for (int t = 0; t < G; ++t) {
+#pragma unroll
+                for (int u = 0; u < QQ; ++u) {
+                    const double y = ld_uniform(Y, static_cast<int64_t>(j + t) * q + (u < q ? u : 0));
+                    const double px = y * v[t].x;
+                    const double py = y * v[t].y;
+                    ax[u] = ax[u] + px;
+                    ay[u] = ay[u] + py;
+                    if constexpr (decltype(both)::value) {
+                        bx[u] = bx[u] + px;
+                        by[u] = by[u] + py;
+                    }
+                }
+            }
+        };
+        using Four = std::integral_constant<int, 4>;
+        using One = std::integral_constant<int, 1>;
+        int j = 0;
+        for (; j + 4 <= j0; j += 4) terms(j, Four{}, std::false_type{});
+        for (; j < j0; ++j) terms(j, One{}, std::false_type{});
+        for (; j + 4 <= m; j += 4) terms(j, Four{}, std::true_type{});
+        for (; j < m; ++j) terms(j, One{}, std::true_type{});
+#pragma unroll
+        for (int u = 0; u < QQ; ++u)
+            if (u < q) {
+                reinterpret_cast<double2*>(out + static_cast<int64_t>(ld_uniform_i(idx_out, u)) * n)[i2] =
+                    double2{ax[u], ay[u]};
+                reinterpret_cast<double2*>(out + static_cast<int64_t>(ld_uniform_i(idx_out2, u)) * n)[i2] =
+                    double2{bx[u], by[u]};
+            }
     }
 }
 
@@ -4405,11 +4752,114 @@ int blk_gram_groups(int64_t n)
     return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kBlkGramGroups, (n + 31) / 32)));
 }
 
+// The Gram partials part[G][mu mv] of launch_blk_gram (G returned), no reduction.
+static hipError_t blk_gram_partials(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib,
+                                    int mv, int64_t n, double* part, hipStream_t s, bool same, int* Gout);
+
 hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib, int mv,
-                           int64_t n, double* part, double* out, hipStream_t s)
+                           int64_t n, double* part, double* out, hipStream_t s, bool same, double* yproj)
+{
+    if ((same && mu != mv) || (yproj && mu < mv)) return hipErrorInvalidValue;
+    int G = 0;
+    hipError_t e = blk_gram_partials(A, ia, mu, B, ib, mv, n, part, s, same, &G);
+    if (e != hipSuccess) return e;
+    const int np = mu * mv;
+    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), dim3(kBlock), 0, s, part, G, np, out, yproj, mv);
+    return hipGetLastError();
+}
+
+hipError_t launch_blk_gram_orth(const double* A, const int32_t* ia, int w, int64_t n, double* part, double* gram,
+                                bool scale, double pivot, double* flag, double* T, hipStream_t s)
+{
+    if (w < 1 || w > kCoefMax) return hipErrorInvalidValue;
+    hipError_t e = launch_blk_gram(A, ia, w, A, ia, w, n, part, gram, s, true);
+    if (e != hipSuccess) return e;
+    SLA_LAUNCH(k_blk_orth_coef, dim3(1), dim3(64), 0, s, gram, w, scale ? 1 : 0, pivot, flag, T);
+    return hipGetLastError();
+}
+
+static hipError_t blk_gram_partials(const double* A, const int32_t* ia, int mu, const double* B, const int32_t* ib,
+                                    int mv, int64_t n, double* part, hipStream_t s, bool same, int* Gout)
 {
     if (mu < 1 || mv < 1 || mu > kBlkMaxCols || mv > kBlkMaxCols || n < 1) return hipErrorInvalidValue;
+    if (same && mu != mv) return hipErrorInvalidValue;
     const int np = mu * mv;
+    const bool pieces = n % 2 == 0 && !(reinterpret_cast<uintptr_t>(A) & 15) && !(reinterpret_cast<uintptr_t>(B) & 15);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+        ncu = 1;
+    if (pieces) {
+        // at most 8 register tiles of 4 x 4 (1 wide where a side is narrower than 4): the
+        // products stream from registers like the combinations
+        const int TA = mu >= 4 ? 4 : 1, TB = mv >= 4 ? 4 : 1;
+        const int ntile = ((mu + TA - 1) / TA) * ((mv + TB - 1) / TB);
+        int ntp = 1;
+        while (ntp < ntile) ntp *= 2;
+        // wider blocks of at most 24 x 24 columns: 6 x 6 tiles, at most 16
+        const bool wide = ntp > 8 && mu <= 24 && mv <= 24;
+        if (wide) ntp = ((mu + 5) / 6) * ((mv + 5) / 6) <= 4 ? 4 : 16;
+        if (ntp <= 8 || wide) {
+            const double* Bs = same ? A : B;
+            const int32_t* ibs = same ? ia : ib;
+            using RtKernel = void (*)(const double*, const int32_t*, int, const double*, const int32_t*, int, int64_t,
+                                      double*);
+            RtKernel f = nullptr;
+#define SLA_GRAM_RT(ta, tb)                                                                                \
+    f = ntp == 1 ? k_blk_gram_rt<ta, tb, 1> : ntp == 2 ? k_blk_gram_rt<ta, tb, 2>                         \
+        : ntp == 4 ? k_blk_gram_rt<ta, tb, 4> : k_blk_gram_rt<ta, tb, 8>
+            if (wide) f = ntp == 4 ? k_blk_gram_rt<6, 6, 4> : k_blk_gram_rt<6, 6, 16>;
+            else if (TA == 1 && TB == 1) SLA_GRAM_RT(1, 1);
+            else if (TA == 4 && TB == 1) SLA_GRAM_RT(4, 1);
+            else if (TA == 1) SLA_GRAM_RT(1, 4);
+            else SLA_GRAM_RT(4, 4);
+#undef SLA_GRAM_RT
+            int occ = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f, kBlock, 0) != hipSuccess || occ < 1) occ = 1;
+            const int64_t per_block = (kBlock / 64) * (64 / ntp);   // row pairs per grid step of a workgroup
+            const int G = static_cast<int>(std::min<int64_t>(
+                {static_cast<int64_t>(blk_gram_groups(n)), (n / 2 + per_block - 1) / per_block,
+                 static_cast<int64_t>(occ) * ncu}));
+            SLA_LAUNCH(f, dim3(static_cast<unsigned>(G)), dim3(kBlock), 0, s, A, ia, mu, Bs, ibs, mv, n, part);
+            *Gout = G;
+            return hipGetLastError();
+        }
+    }
+    if (pieces) {
+        // pipelined slices of 16-byte pieces: ncol R <= 4096 doubles (32 KiB of LDS)
+        const int ncol = same ? mu : mu + mv;
+        int R = 4096;
+        while (ncol * R > 4096) R /= 2;
+        int lgh = 0;
+        while ((2 << lgh) < R) ++lgh;
+        const int64_t nslices = (n + R - 1) / R;
+        const size_t lds = sizeof(double) * std::max<size_t>(static_cast<size_t>(ncol) * (R + 2), kBlock);
+        const int TA = mu >= 4 ? 4 : 1, TB = mv >= 4 ? 4 : 1;
+        const int ntile = ((mu + TA - 1) / TA) * ((mv + TB - 1) / TB);
+        int tpt = 1;   // threads per tile: a power of 2 with ntile tpt <= kBlock
+        while (ntile * tpt * 2 <= kBlock) tpt *= 2;
+        const int pt = (ntile + kBlock / tpt - 1) / (kBlock / tpt);
+        const int sm = same ? 1 : 0;
+        using GramKernel = void (*)(const double*, const int32_t*, int, const double*, const int32_t*, int, int,
+                                    int64_t, int, int, double*);
+        GramKernel f = (TA == 1 && TB == 1) ? k_blk_gram_pipe<1, 1, 1, 8>
+                       : (TA == 4 && TB == 1) ? k_blk_gram_pipe<4, 1, 1, 8>
+                       : (TA == 1)           ? k_blk_gram_pipe<1, 4, 1, 8>
+                       : (pt <= 1)           ? k_blk_gram_pipe<4, 4, 1, 8>
+                       : (pt <= 2)           ? k_blk_gram_pipe<4, 4, 2, 8>
+                                             : k_blk_gram_pipe<4, 4, 3, 8>;
+        // one resident round of workgroups (a second, partial round would run on part of
+        // the GPU), each taking slices grid-stride
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, f, kBlock, lds) != hipSuccess || occ < 1) occ = 1;
+        const int G = static_cast<int>(std::min<int64_t>({static_cast<int64_t>(blk_gram_groups(n)), nslices,
+                                                          static_cast<int64_t>(occ) * ncu}));
+        const dim3 grid(static_cast<unsigned>(G)), blk(kBlock);
+        SLA_LAUNCH(f, grid, blk, lds, s, A, ia, mu, B, ib, mv, sm, n, lgh, tpt, part);
+        *Gout = G;
+        return hipGetLastError();
+    }
+    if (same) B = A, ib = ia;
     // slice rows: (mu + mv) (R + 1) doubles within 32 KiB of LDS (five workgroups per
     // CU keep loads in flight while others compute), R a multiple of 32
     constexpr int kStage = 4000;
@@ -4427,9 +4877,7 @@ hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const dou
         if (pt <= 1) SLA_LAUNCH(k_blk_gram_tiled<1>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, tpt, part);
         else if (pt <= 2) SLA_LAUNCH(k_blk_gram_tiled<2>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, tpt, part);
         else SLA_LAUNCH(k_blk_gram_tiled<3>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, tpt, part);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), blk, 0, s, part, G, np, out);
+        *Gout = G;
         return hipGetLastError();
     }
     int tpp = 1;   // threads per pair: a power of 2 with np tpp <= kBlock
@@ -4442,16 +4890,14 @@ hipError_t launch_blk_gram(const double* A, const int32_t* ia, int mu, const dou
     else if (pp <= 16) SLA_LAUNCH(k_blk_gram<16>, grid, blk, lds, s, A, ia, mu, B, ib, mv, n, R, 1, part);
     else SLA_LAUNCH(k_blk_gram<(kBlkMaxCols * kBlkMaxCols + kBlock - 1) / kBlock>, grid, blk, lds, s, A, ia, mu, B,
                     ib, mv, n, R, 1, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), blk, 0, s, part, G, np, out);
+    *Gout = G;
     return hipGetLastError();
 }
 
 hipError_t launch_blk_reduce(const double* part, int G, int np, double* out, hipStream_t s)
 {
     if (G < 1 || np < 1) return hipErrorInvalidValue;
-    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), dim3(kBlock), 0, s, part, G, np, out);
+    SLA_LAUNCH(k_blk_reduce, dim3(static_cast<unsigned>(np)), dim3(kBlock), 0, s, part, G, np, out, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -4463,6 +4909,23 @@ hipError_t launch_blk_diag_inv(const void* rp, int rp_bits, const int32_t* col, 
         SLA_LAUNCH(k_blk_diag_inv<int64_t>, grid, blk, 0, s, static_cast<const int64_t*>(rp), col, vals, n, tinv, part);
     else
         SLA_LAUNCH(k_blk_diag_inv<int32_t>, grid, blk, 0, s, static_cast<const int32_t*>(rp), col, vals, n, tinv, part);
+    return hipGetLastError();
+}
+
+hipError_t launch_blk_comb_dual(const double* in, const int32_t* idx_in, int m, int j0, const double* Y,
+                                double* out, const int32_t* idx_out, const int32_t* idx_out2, int q, int64_t n,
+                                hipStream_t s)
+{
+    if (m < 1 || j0 < 0 || j0 >= m || q < 1 || q > 32 || n < 1) return hipErrorInvalidValue;
+    if ((n & 1) || (reinterpret_cast<uintptr_t>(in) & 15) || (reinterpret_cast<uintptr_t>(out) & 15))
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blk_comb_groups(n))), blk(kBlock);
+    if (q <= 1) SLA_LAUNCH(k_blk_comb2d<1>, grid, blk, 0, s, in, idx_in, m, j0, Y, out, idx_out, idx_out2, q, n);
+    else if (q <= 2) SLA_LAUNCH(k_blk_comb2d<2>, grid, blk, 0, s, in, idx_in, m, j0, Y, out, idx_out, idx_out2, q, n);
+    else if (q <= 4) SLA_LAUNCH(k_blk_comb2d<4>, grid, blk, 0, s, in, idx_in, m, j0, Y, out, idx_out, idx_out2, q, n);
+    else if (q <= 8) SLA_LAUNCH(k_blk_comb2d<8>, grid, blk, 0, s, in, idx_in, m, j0, Y, out, idx_out, idx_out2, q, n);
+    else if (q <= 16) SLA_LAUNCH(k_blk_comb2d<16>, grid, blk, 0, s, in, idx_in, m, j0, Y, out, idx_out, idx_out2, q, n);
+    else SLA_LAUNCH(k_blk_comb2d<32>, grid, blk, 0, s, in, idx_in, m, j0, Y, out, idx_out, idx_out2, q, n);
     return hipGetLastError();
 }
 
