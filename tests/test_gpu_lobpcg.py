@@ -134,10 +134,20 @@ def test_lobpcg_varcoef_40(S):
 
 
 def test_lobpcg_varcoef_300(S):
-    # 90,000 rows: 352 Gram workgroups of 32-row slices, ragged combination grid
+    # 90,000 rows: register-tile Gram products (4 x 4 and, for the Rayleigh-Ritz matrix of
+    # 24 columns, 6 x 6 tiles) over many workgroups, ragged combination grid
     A, _, _ = W.varcoef_poisson5(300, seed=2)
     ev, U, info, r = compare(S, A, 8, "largest", 1e-8, g=np.linspace(1.0, 2.0, 8))
     assert info["iterations"] > 20
+
+
+@pytest.mark.parametrize("N,k,tol", [(15, 4, 1e-10), (301, 8, 1e-8)])
+def test_lobpcg_odd_rows(S, N, k, tol):
+    # an odd row count: columns start at odd multiples of 8 bytes, so the Gram products,
+    # the combinations and the Ritz step take their row-by-row kernels
+    A, _, _ = W.varcoef_poisson5(N, seed=5)
+    assert A.n_rows % 2 == 1
+    compare(S, A, k, "largest", tol, g=np.linspace(1.0, 2.0, k))
 
 
 def test_lobpcg_invariant_start_block(S):
