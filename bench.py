@@ -773,6 +773,10 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
     ceiling = measure_ceiling(S, torch, dev) if not args.no_ceiling else None
+    if not args.no_ceiling and cache_resident(r["w"]) and not r["bicg"] and not r["an"]["split"]:
+        rf0 = iteration_roofline(r)
+        r["ceiling_resident"] = measure_ceiling_resident(S, torch, dev, rf0["bm"]["cg_spmv"],
+                                                         rf0["bm"]["cg_update"])
     big = None
     if args.workload == "poisson1024" and not args.no_big and args.fixed_iters == 0 and not args.jacobi:
         # the metric's second configuration, 169M DOF (500 + 500 fixed iterations), timed
@@ -918,6 +922,11 @@ def iteration_roofline(r) -> dict:
                 moved_gbps=gbps(bm["iteration"], iter_ms), spmv_gbps=gbps(spmv_bytes, spmv_ms))
 
 
+def cache_resident(w) -> bool:
+    """Whether one iteration's working set fits the 256 MB Infinity Cache."""
+    return (12 * w["nnz"] + 52 * w["n"]) * w["batch"] < 200e6
+
+
 def cg_summary(r, ceiling, args) -> dict:
     """The measured numbers of one CG workload (headline fields and its roofline)."""
     w = r["w"]
@@ -925,7 +934,7 @@ def cg_summary(r, ceiling, args) -> dict:
     rf = iteration_roofline(r)
     traffic, traffic_src = read_traffic(w["name"], "bytes_per_iteration")
     ms_step = 1e3 * r["wall"] / r["steps"]
-    resident = (12 * w["nnz"] + 52 * w["n"]) * B < 200e6   # fits the 256 MB Infinity Cache
+    resident = cache_resident(w)
     roof = {"bound": "hbm",
             "kernel": ("one BiCGStab iteration (two products, three streaming kernels)" if r["bicg"] else
                        "one CG iteration: " + r["spmv_kernel"] + " + k_cg_update"
@@ -950,6 +959,13 @@ def cg_summary(r, ceiling, args) -> dict:
             t_ceil = (rf["bm"]["cg_spmv"] / ceiling["spmv_mix"]["gbps"] +
                       rf["bm"]["cg_update"] / ceiling["triad"]["gbps"]) / 1e9
             roof["frac_of_ceiling"] = round(t_ceil / (rf["iter_ms"] * 1e-3), 4)
+    cr = r.get("ceiling_resident")
+    if cr:
+        # a cache-resident iteration against plain streams of its own sizes: the SpMV
+        # mix moving the SpMV's bytes plus the triad moving the update's, each launch timed
+        roof["resident_ceiling"] = cr
+        roof["frac_of_resident_ceiling"] = round(
+            (cr["spmv_mix"]["us"] + cr["triad"]["us"]) / (1e3 * rf["iter_ms"]), 4)
     return {"workload": w["desc"], "n": w["n"], "nnz": w["nnz"], "batch": B,
             "row_ptr": f"int{8 * r['rp_stated']} (kernels read int{8 * r['rp_bytes']})",
             "col_idx_read": ("none (diagonal layout)" if r["dia_nd"] else f"int{8 * r['col_bytes']}"),
@@ -1017,12 +1033,36 @@ CEILING_MIXES = {"read": (1, 0), "write": (0, 1), "copy": (1, 1), "triad": (2, 1
 CEILING_SWEEP = [(u, nt, bpc) for u in (1, 2, 4) for nt in (1, 0) for bpc in (1, 2, 4, 8)]
 
 
+def _probe_best(lib, L, bufs, part, stream, torch, nr: int, nw: int, n: int, sweep: bool) -> dict:
+    """Best rate of one read/write mix over n doubles per array, over the variants."""
+    import ctypes as C
+    ins = (C.c_void_p * max(nr, 1))(*[bufs[i].data_ptr() for i in range(nr)])
+    outs = (C.c_void_p * max(nw, 1))(*[bufs[nr + i].data_ptr() for i in range(nw)])
+    best = None
+    for (u, nt, bpc) in (CEILING_SWEEP if sweep else CEILING_SWEEP[:1]):
+        def launch():
+            L.check(lib.sla_probe_stream(nr, nw, ins, outs, n, u, nt, bpc, part.data_ptr(), stream.cuda_stream))
+        launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbps = 8.0 * n * (nr + nw) / (ms * 1e-3) / 1e9
+        if best is None or gbps > best["gbps"]:
+            best = {"gbps": round(gbps, 1), "unroll": u, "nontemporal": nt, "blocks_per_cu": bpc,
+                    "us": round(1e3 * ms, 2), "bytes": 8 * n * (nr + nw)}
+    return best
+
+
 def measure_ceiling(S, torch, dev, sweep: bool = True, elems: int = 1 << 26) -> dict:
     """Bandwidth of plain coalesced streams on this GPU, in this run: for each mix the
     best rate (bytes read + written / event-timed launch) over the variants.  Arrays of
     `elems` doubles (512 MiB each by default: every mix streams far past the 256 MB
     Infinity Cache); the SpMV mix uses arrays a quarter as long (13 of them)."""
-    import ctypes as C
     from differentiable_sparse_linear_spmv_amd import _lib as L
     lib = L.load()
     bufs = [torch.empty(elems, dtype=torch.float64, device=dev) for _ in range(13)]
@@ -1033,30 +1073,31 @@ def measure_ceiling(S, torch, dev, sweep: bool = True, elems: int = 1 << 26) -> 
     out = {}
     for name, (nr, nw) in CEILING_MIXES.items():
         n = elems // 4 if nr + nw > 4 else elems
-        ins = (C.c_void_p * max(nr, 1))(*[bufs[i].data_ptr() for i in range(nr)])
-        outs = (C.c_void_p * max(nw, 1))(*[bufs[nr + i].data_ptr() for i in range(nw)])
-        best = None
-        for (u, nt, bpc) in (CEILING_SWEEP if sweep else CEILING_SWEEP[:1]):
-            def launch():
-                L.check(lib.sla_probe_stream(nr, nw, ins, outs, n, u, nt, bpc, part.data_ptr(),
-                                             stream.cuda_stream))
-            launch()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5
-            e0.record(stream)
-            for _ in range(reps):
-                launch()
-            e1.record(stream)
-            e1.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            gbps = 8.0 * n * (nr + nw) / (ms * 1e-3) / 1e9
-            if best is None or gbps > best["gbps"]:
-                best = {"gbps": round(gbps, 1), "unroll": u, "nontemporal": nt, "blocks_per_cu": bpc,
-                        "us": round(1e3 * ms, 2), "bytes": 8 * n * (nr + nw)}
-        out[name] = best
+        out[name] = _probe_best(lib, L, bufs, part, stream, torch, nr, nw, n, sweep)
     del bufs, part
     torch.cuda.empty_cache()
     out["frac_of_peak"] = {k: round(v["gbps"] / HBM_PEAK_GBPS, 4) for k, v in out.items()}
+    return out
+
+
+def measure_ceiling_resident(S, torch, dev, spmv_bytes: int, update_bytes: int) -> dict:
+    """The same probes at the sizes of one cache-resident CG iteration: the SpMV mix (10
+    arrays read, 3 written) moving the SpMV's bytes, and the triad moving the update's.
+    The arrays fit the Infinity Cache, as the iteration's working set does, so this is
+    the rate plain streams of that size reach (launch and ramp included), not HBM's."""
+    from differentiable_sparse_linear_spmv_amd import _lib as L
+    lib = L.load()
+    n_spmv = max(1024, int(spmv_bytes) // (8 * 13)) & ~1   # the probes take an even length
+    n_upd = max(1024, int(update_bytes) // (8 * 3)) & ~1
+    bufs = [torch.empty(max(n_spmv, n_upd), dtype=torch.float64, device=dev) for _ in range(13)]
+    for bb in bufs:
+        bb.fill_(1.0)
+    part = torch.zeros(8 * 1024, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {"spmv_mix": _probe_best(lib, L, bufs, part, stream, torch, 10, 3, n_spmv, True),
+           "triad": _probe_best(lib, L, bufs, part, stream, torch, 2, 1, n_upd, True)}
+    del bufs, part
+    torch.cuda.empty_cache()
     return out
 
 if __name__ == "__main__":

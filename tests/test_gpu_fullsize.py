@@ -4,7 +4,9 @@
   oracle's values stored in tests/golden/*.json (written by
   tests/golden/make_golden.py, which calls only the oracle): iteration counts within
   2 % (every system of the FEM batch), x within 1e-9, lambda and dL/dvals within 1e-8
-  (relative, on seeded samples and on the norms).
+  (relative, on seeded samples and on the norms); and on whole vectors (every system of
+  the batch), the oracle's SpMV and gradient scatter applied to the GPU's x and lambda:
+  true residuals of the solve and of the adjoint within 2 rtol, dL/dvals bit for bit.
 * convdiff1024: BiCGStab and its adjoint on A^T, by the bounds its stop test fixes
   (see the test's docstring).
 * poisson13000 (169M unknowns, int64 row pointers), in the launch configuration the
@@ -112,6 +114,21 @@ def test_fullsize_single_system(S, name):
     out = dict(x=x, lam=lam, gvals=gv, iterations=info[0]["iterations"], state=info[0]["state"],
                adj_iterations=binfo[0]["iterations"], rhs_norm=info[0]["rhs_norm"])
     check_system(out, g, name, ITER_BAR[name])
+    gx = 2.0 * (x - c["x_target"]) if c["loss"] == "sq_target" else x
+    check_whole_vectors(A, A.vals, c["b"], gx, x, lam, gv, c["rtol"], name)
+
+
+def check_whole_vectors(A, vals, b, gx, x, lam, gv, rtol, tag):
+    """Every entry, by what any correct run satisfies (the oracle's SpMV and gradient
+    scatter on the GPU's vectors): the true residuals |b - A x| and |g - A lambda| within
+    2 rtol of |b| and |g| (the stop tests hold the recurrence residuals to rtol; on these
+    systems the two differ by far less), and dL/dvals = -lambda_i x_j bit for bit."""
+    nb, ng = np.linalg.norm(b), np.linalg.norm(gx)
+    res = np.linalg.norm(b - O.spmv(A, x, vals=vals))
+    assert res <= 2 * rtol * nb, (tag, res / nb)
+    ares = np.linalg.norm(gx - O.spmv(A, lam, vals=vals))
+    assert ares <= 2 * rtol * ng, (tag, ares / ng)
+    assert np.array_equal(gv, O.pattern_outer(A, lam, x, sign=-1.0)), tag
 
 
 def test_fullsize_fem_batched(S):
@@ -131,6 +148,8 @@ def test_fullsize_fem_batched(S):
         out = dict(x=x[s], lam=lam[s], gvals=gv[s], iterations=its[s], state=info[s]["state"],
                    adj_iterations=adj[s], rhs_norm=info[s]["rhs_norm"])
         check_system(out, gs, f"system {s}", bar)
+    for s in range(A.batch):   # every system, every entry
+        check_whole_vectors(A, A.vals[s], c["b"][s], x[s], x[s], lam[s], gv[s], c["rtol"], f"system {s}")
 
 
 # ------------------------------------------------------------------------------ 169M rows
