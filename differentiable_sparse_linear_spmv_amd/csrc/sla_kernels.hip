@@ -3955,13 +3955,21 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         if (tid < kGroup) a.part_sigma[static_cast<int64_t>(sys0 + tid) * a.G + gc.lb] = sig;
         return;
     }
-    GStage<CAPG> SA, SB;
-    int32_t k0a = tk0(t), k1a = tk1(t), k0b = 0, k1b = 0;
+    // Three stage buffers in rotation: while tile t is summed, tiles t + ts and t + 2 ts
+    // are loading, so each tile's loads have two tile times to arrive (with one tile
+    // ahead the kernel waited on memory once per tile).
+    GStage<CAPG> SA, SB, SC;
+    int32_t k0a = tk0(t), k1a = tk1(t), k0b = 0, k1b = 0, k0c = 0, k1c = 0;
+    if (t + ts < te) {
+        k0b = tk0(t + ts);
+        k1b = tk1(t + ts);
+    }
     stage(SA, t, k0a, k1a);
+    stage(SB, t + ts, k0b, k1b);   // past the end: clamped loads
     if constexpr (WIN) {
-        // the ring's first fill: chunks t - hc ... t + hc - 1 (stage brought t + hc),
-        // every load issued before the first store (unconditional: past 2 hc they
-        // repeat the last chunk)
+        // the ring's first fill: chunks t - hc ... t + hc - 1 (the stages bring t + hc
+        // and t + hc + 1), every load issued before the first store (unconditional: past
+        // 2 hc they repeat the last chunk)
         double fill[2 * kGWinHaloChunks];
 #pragma unroll
         for (int u = 0; u < 2 * kGWinHaloChunks; ++u) fill[u] = chunk_ld(t - hc + min(u, max(2 * hc - 1, 0)));
@@ -3969,19 +3977,20 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         for (int u = 0; u < 2 * kGWinHaloChunks; ++u)
             if (u < 2 * hc) chunk_st(t - hc + u, fill[u]);
     }
-    if (t + ts < te) {
-        k0b = tk0(t + ts);
-        k1b = tk1(t + ts);
+    if (t + 2 * ts < te) {
+        k0c = tk0(t + 2 * ts);
+        k1c = tk1(t + 2 * ts);
     }
     commit(SA, t, k0a, k1a);
     __syncthreads();
-#define SLA_GCG_TILE(nxt)                                                                                  \
+    // stg: the buffer that takes tile t + 2 ts; cmt: the buffer holding tile t + ts
+#define SLA_GCG_TILE(stg, cmt)                                                                             \
     {                                                                                                      \
-        stage(nxt, t + ts, k0b, k1b); /* past the end: clamped loads, keeps the wait counts exact */      \
-        int32_t k0c = 0, k1c = 0;                                                                          \
-        if (t + 2 * ts < te) {                                                                             \
-            k0c = tk0(t + 2 * ts);                                                                         \
-            k1c = tk1(t + 2 * ts);                                                                         \
+        stage(stg, t + 2 * ts, k0c, k1c); /* past the end: clamped loads, keeps the wait counts exact */  \
+        int32_t k0d = 0, k1d = 0;                                                                          \
+        if (t + 3 * ts < te) {                                                                             \
+            k0d = tk0(t + 3 * ts);                                                                         \
+            k1d = tk1(t + 3 * ts);                                                                         \
         }                                                                                                  \
         const int rs = s_rs[tid], re = s_re[tid];                                                          \
         double sum = 0.0;                                                                                  \
@@ -4006,7 +4015,11 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         const int32_t k0n = k0b, k1n = k1b;                                                                \
         k0b = k0c;                                                                                         \
         k1b = k1c;                                                                                         \
-        if (t < te) commit(nxt, t, k0n, k1n);                                                              \
+        k0c = k0d;                                                                                         \
+        k1c = k1d;                                                                                         \
+        /* unconditional (past the end it commits an empty tile nothing reads), so no */                \
+        /* staged load is left unconsumed on a path                                   */                \
+        commit(cmt, t, k0n, k1n);                                                                          \
         if (run && i < n) {                                                                                \
             const int64_t e = static_cast<int64_t>(i) * kGroup + sy;                                      \
             qg[e] = sum;                                                                                   \
@@ -4018,8 +4031,9 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
     }
 #pragma unroll 1
     while (true) {
-        SLA_GCG_TILE(SB)
-        SLA_GCG_TILE(SA)
+        SLA_GCG_TILE(SC, SB)
+        SLA_GCG_TILE(SA, SC)
+        SLA_GCG_TILE(SB, SA)
     }
 #undef SLA_GCG_TILE
     sig = group_block_sum(sig, s_red);

@@ -5,8 +5,9 @@
   tests/golden/make_golden.py, which calls only the oracle): iteration counts within
   2 % (every system of the FEM batch), x within 1e-9, lambda and dL/dvals within 1e-8
   (relative, on seeded samples and on the norms); and on whole vectors (every system of
-  the batch), the oracle's SpMV and gradient scatter applied to the GPU's x and lambda:
-  true residuals of the solve and of the adjoint within 2 rtol, dL/dvals bit for bit.
+  the batch), the oracle's gradient scatter applied to the GPU's x and lambda gives
+  dL/dvals bit for bit, and on the 1M Poisson grid the true residuals of the solve and
+  of the adjoint are within 2 rtol (see RES_BAR for why not elsewhere).
 * convdiff1024: BiCGStab and its adjoint on A^T, by the bounds its stop test fixes
   (see the test's docstring).
 * poisson13000 (169M unknowns, int64 row pointers), in the launch configuration the
@@ -115,20 +116,36 @@ def test_fullsize_single_system(S, name):
                adj_iterations=binfo[0]["iterations"], rhs_norm=info[0]["rhs_norm"])
     check_system(out, g, name, ITER_BAR[name])
     gx = 2.0 * (x - c["x_target"]) if c["loss"] == "sq_target" else x
-    check_whole_vectors(A, A.vals, c["b"], gx, x, lam, gv, c["rtol"], name)
+    bar = RES_BAR[name]
+    check_whole_vectors(A, A.vals, c["b"], gx, x, lam, gv, None if bar is None else bar * c["rtol"], name)
 
 
-def check_whole_vectors(A, vals, b, gx, x, lam, gv, rtol, tag):
+# True-residual bars, in units of rtol (None: not asserted).  The stop test holds the
+# recurrence residual to rtol; the true residual |b - A x| departs from it by the
+# rounding CG accumulates, which grows with the iteration count and |A| |x| / |b| (the
+# attainable accuracy of fp64 CG).  On the 1M Poisson grid (2,892 iterations) the
+# oracle's own two residuals agree to 1e-15 relative, so 2 rtol is a tight bar.  On the
+# FEM systems the mass term (1e-3) barely controls the constant mode: |x| reaches 1e8
+# and the oracle's own adjoint ends with a true residual of 1.4e-6 relative (system 0)
+# while its recurrence residual is 1e-8; the variable-coefficient grid drifts to
+# 2.4 rtol over 46,530 iterations.  There the true residual measures fp64 CG, not this
+# implementation, and parity rests on the agreement with the oracle's vectors.
+RES_BAR = {"poisson1024": 2.0, "fem256x256": None, "varcoef2048": None}
+
+
+def check_whole_vectors(A, vals, b, gx, x, lam, gv, bar, tag):
     """Every entry, by what any correct run satisfies (the oracle's SpMV and gradient
-    scatter on the GPU's vectors): the true residuals |b - A x| and |g - A lambda| within
-    2 rtol of |b| and |g| (the stop tests hold the recurrence residuals to rtol; on these
-    systems the two differ by far less), and dL/dvals = -lambda_i x_j bit for bit."""
+    scatter on the GPU's vectors): dL/dvals = -lambda_i x_j bit for bit, and where `bar`
+    is given the true residuals |b - A x| and |g - A lambda| within `bar` of |b| and
+    |g|."""
+    assert np.array_equal(gv, O.pattern_outer(A, lam, x, sign=-1.0)), tag
+    if bar is None:
+        return
     nb, ng = np.linalg.norm(b), np.linalg.norm(gx)
     res = np.linalg.norm(b - O.spmv(A, x, vals=vals))
-    assert res <= 2 * rtol * nb, (tag, res / nb)
+    assert res <= bar * nb, (tag, res / nb)
     ares = np.linalg.norm(gx - O.spmv(A, lam, vals=vals))
-    assert ares <= 2 * rtol * ng, (tag, ares / ng)
-    assert np.array_equal(gv, O.pattern_outer(A, lam, x, sign=-1.0)), tag
+    assert ares <= bar * ng, (tag, ares / ng)
 
 
 def test_fullsize_fem_batched(S):
@@ -149,7 +166,7 @@ def test_fullsize_fem_batched(S):
                    adj_iterations=adj[s], rhs_norm=info[s]["rhs_norm"])
         check_system(out, gs, f"system {s}", bar)
     for s in range(A.batch):   # every system, every entry
-        check_whole_vectors(A, A.vals[s], c["b"][s], x[s], x[s], lam[s], gv[s], c["rtol"], f"system {s}")
+        check_whole_vectors(A, A.vals[s], c["b"][s], x[s], x[s], lam[s], gv[s], None, f"system {s}")
 
 
 # ------------------------------------------------------------------------------ 169M rows
