@@ -3925,19 +3925,16 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
             for (int u = 0; u < UC; ++u) S.c[u] = cb[min(tid + u * kBlock, lastc)];
         }
     };
+    // Every staged register is written to LDS on every path (slots past the tile's
+    // entries take the clamped loads' copies and are never read), so no load is left
+    // unconsumed on a branch, which would make the compiler drain the loads in flight.
     auto commit = [&](const GStage<CAPG>& S, int32_t t, int32_t k0, int32_t k1) __attribute__((always_inline)) {
-        const int32_t cnt = k1 - k0;
+        (void)k1;
 #pragma unroll
-        for (int u = 0; u < UV; ++u) {
-            const int e = tid + u * kBlock;
-            if (e < cnt * kGroup) s_val[e] = S.v[u];
-        }
+        for (int u = 0; u < UV; ++u) s_val[tid + u * kBlock] = S.v[u];
         const int32_t cbase = WIN ? t * kGRows : 0;
 #pragma unroll
-        for (int u = 0; u < UC; ++u) {
-            const int e = tid + u * kBlock;
-            if (e < cnt) s_col[e] = S.c[u] + cbase;
-        }
+        for (int u = 0; u < UC; ++u) s_col[tid + u * kBlock] = S.c[u] + cbase;
         const bool has = t * kGRows + tid / kGroup < n;
         s_rs[tid] = S.a0 - k0;
         s_re[tid] = has ? S.a1 - k0 : S.a0 - k0;
@@ -3965,7 +3962,6 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         k1b = tk1(t + ts);
     }
     stage(SA, t, k0a, k1a);
-    stage(SB, t + ts, k0b, k1b);   // past the end: clamped loads
     if constexpr (WIN) {
         // the ring's first fill: chunks t - hc ... t + hc - 1 (the stages bring t + hc
         // and t + hc + 1), every load issued before the first store (unconditional: past
@@ -3982,6 +3978,9 @@ __global__ __launch_bounds__(kBlock) void k_gcg_spmv(CgArgs a, int64_t k)
         k1c = tk1(t + 2 * ts);
     }
     commit(SA, t, k0a, k1a);
+    // staged after the first commit, so the loop starts with its loads the only ones in
+    // flight
+    stage(SB, t + ts, k0b, k1b);   // past the end: clamped loads
     __syncthreads();
     // stg: the buffer that takes tile t + 2 ts; cmt: the buffer holding tile t + ts
 #define SLA_GCG_TILE(stg, cmt)                                                                             \
