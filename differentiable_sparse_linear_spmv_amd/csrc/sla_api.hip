@@ -697,6 +697,17 @@ sla_status ensure_reorder(sla_csr* A, hipStream_t s)
     return SLA_OK;
 }
 
+// A pattern with no stored entries: the staged SpMV still issues its (clamped) entry
+// loads on every path, so it gets readable stand-ins for the entry arrays (b, whose
+// length n is nonzero whenever there is a tile to stage); nothing read is ever used.
+void no_entries_standins(CgArgs& a, int64_t nnz)
+{
+    if (nnz > 0) return;
+    a.vals = a.b;
+    a.col = reinterpret_cast<const int32_t*>(a.b);
+    a.col16 = reinterpret_cast<const int16_t*>(a.b);
+}
+
 // Grouped batch (kGroup systems interleaved per element): values into the grouped
 // layout, then init / (p update, SpMV, update) per iteration / x back to the caller's
 // layout.  The polling is run_cg's.  With the reordering on, the grouped kernels run on
@@ -919,6 +930,7 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     if (band > 0) a.col16 = A->colb16;   // the banded SpMV's window-relative offsets, or none
     a.vals = vals;
     a.b = b;
+    no_entries_standins(a, A->nnz);
     a.x = x;
     a.r = w.r;
     a.p0 = w.p0;
@@ -1024,6 +1036,7 @@ sla_status run_bicgstab(sla_csr* A, const void* row_ptr, const int32_t* col, int
     a.col16 = (col == A->col && row_ptr == A->krp) ? A->col16 : (col == A->col_t ? A->col16_t : nullptr);
     a.vals = vals;
     a.b = b;
+    no_entries_standins(a, A->nnz);
     a.x = x;
     a.r = w.r;
     a.p0 = w.p0;   // p

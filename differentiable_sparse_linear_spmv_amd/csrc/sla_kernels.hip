@@ -748,13 +748,16 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
                                            const double* __restrict__ vals,
                                            const double* __restrict__ rin, const double* __restrict__ pprev,
                                            const double* __restrict__ x, int64_t t, int64_t n, int64_t k0,
-                                           int64_t k1)
+                                           int64_t k1, bool live = true)
 {
     constexpr int U = CAP / kBlock;
     const int tid = threadIdx.x;
     const int64_t row0 = t * kTile;
     const int nr = static_cast<int>(min(static_cast<int64_t>(kTile), n - row0));
-    const int64_t i = row0 + min(tid, nr - 1);
+    // live = false: a stand-in stage past the workgroup's last tile (loads issued, never
+    // used), every lane at the tile's first row and (k0 = k1) its first entry, so it
+    // costs a few cache lines
+    const int64_t i = row0 + (live ? min(tid, nr - 1) : 0);
     S.a0 = rp[i];
     S.a1 = rp[i + 1];
     S.ri = ldv<OFF32>(rin, i);   // with SPLIT: p_k (rin is the formed operand)
@@ -764,11 +767,16 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
     }
     const int64_t cnt = k1 - k0;
     // (the products-first variant reads its entries itself, chunk by chunk)
-    if (CAP != kCapSkew && cnt <= CAP && cnt > 0) {
-        const double* __restrict__ vb = vals + k0;
-        const int last = static_cast<int>(cnt) - 1;
+    // Unconditional: an empty or over-cap tile loads clamped copies of stored entries
+    // (never read), so every staged register is written on every path and no load in
+    // flight is drained where paths join.  (A pattern with no stored entries gets
+    // readable stand-in pointers from the host.)
+    if constexpr (CAP != kCapSkew) {
+        const int64_t kb = cnt > 0 ? k0 : (k0 > 0 ? k0 - 1 : 0);
+        const double* __restrict__ vb = vals + kb;
+        const int last = static_cast<int>(min(max(cnt, static_cast<int64_t>(1)), static_cast<int64_t>(CAP))) - 1;
         if constexpr (C16) {
-            const int16_t* __restrict__ cb = col16 + k0;
+            const int16_t* __restrict__ cb = col16 + kb;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = min(tid + u * kBlock, last);
@@ -776,7 +784,7 @@ __device__ __forceinline__ void stage_tile(TileStage<RP, CAP / kBlock>& S, const
                 S.c[u] = cb[j];
             }
         } else {
-            const int32_t* __restrict__ cb = col + k0;
+            const int32_t* __restrict__ cb = col + kb;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = min(tid + u * kBlock, last);
@@ -917,62 +925,65 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(CgArgs a, int64_t k)
             if (tn < ntiles)
                 stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x,
                                                        tile_of(tn), n, k0n, k1n);
-        } else if (cnt <= CAP) {
+        } else {
+            // Every staged entry register goes to LDS (slots past the tile's entries are
+            // never read), on both paths; the next tile is staged unconditionally (past the
+            // workgroup's last tile: a clamped copy of it, never used).
             const int32_t cbase = C16 ? static_cast<int32_t>(row0) : 0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = tid + u * kBlock;
-                if (j < cnt) {
-                    s_val[j] = cur.v[u];
-                    s_col[j] = cbase + cur.c[u];
-                }
+                s_val[j] = cur.v[u];
+                s_col[j] = cbase + cur.c[u];
             }
-            const int rs = static_cast<int>(static_cast<int64_t>(cur.a0) - k0);
-            const int re = (tid < nr) ? static_cast<int>(static_cast<int64_t>(cur.a1) - k0) : rs;
-            __syncthreads();
-            // Gathers of the row's first RC entries are issued before the next tile's
-            // prefetch: the vector-memory counter completes in order, so waiting for
-            // them does not wait for the prefetch.  Slots past the row's end gather
-            // the lane's own row (a valid address) and are masked below.
-            double pv[RC];
-#pragma unroll
-            for (int u = 0; u < RC; ++u) {
-                const int64_t c = (rs + u < re) ? static_cast<int64_t>(s_col[rs + u]) : i;
-                pv[u] = g(c);
-            }
-            if (tn < ntiles)
-                stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
-                                                  k0n, k1n);
-#pragma unroll
-            for (int u = 0; u < RC; ++u) {
-                const bool ok = rs + u < re;
-                const double tt = s_val[ok ? rs + u : rs] * pv[u];
-                const double sn = s + tt;
-                s = ok ? sn : s;
-            }
-#pragma unroll 1
-            for (int j0 = rs + RC; j0 < re; j0 += RC) {   // rows longer than RC entries
-                double pw[RC];
+            const int64_t tstg = tile_of(min(tn, ntiles - 1));
+            if (cnt <= CAP) {
+                const int rs = static_cast<int>(static_cast<int64_t>(cur.a0) - k0);
+                const int re = (tid < nr) ? static_cast<int>(static_cast<int64_t>(cur.a1) - k0) : rs;
+                __syncthreads();
+                // Gathers of the row's first RC entries are issued before the next tile's
+                // prefetch: the vector-memory counter completes in order, so waiting for
+                // them does not wait for the prefetch.  Slots past the row's end gather
+                // the lane's own row (a valid address) and are masked below.
+                double pv[RC];
 #pragma unroll
                 for (int u = 0; u < RC; ++u) {
-                    const int j = (j0 + u < re) ? j0 + u : j0;
-                    pw[u] = g(s_col[j]);
+                    const int64_t c = (rs + u < re) ? static_cast<int64_t>(s_col[rs + u]) : i;
+                    pv[u] = g(c);
                 }
+                stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tstg, n,
+                                                       k0n, k1n, tn < ntiles);
 #pragma unroll
                 for (int u = 0; u < RC; ++u) {
-                    const bool ok = j0 + u < re;
-                    const int j = ok ? j0 + u : j0;
-                    const double tt = s_val[j] * pw[u];
+                    const bool ok = rs + u < re;
+                    const double tt = s_val[ok ? rs + u : rs] * pv[u];
                     const double sn = s + tt;
                     s = ok ? sn : s;
                 }
+#pragma unroll 1
+                for (int j0 = rs + RC; j0 < re; j0 += RC) {   // rows longer than RC entries
+                    double pw[RC];
+#pragma unroll
+                    for (int u = 0; u < RC; ++u) {
+                        const int j = (j0 + u < re) ? j0 + u : j0;
+                        pw[u] = g(s_col[j]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < RC; ++u) {
+                        const bool ok = j0 + u < re;
+                        const int j = ok ? j0 + u : j0;
+                        const double tt = s_val[j] * pw[u];
+                        const double sn = s + tt;
+                        s = ok ? sn : s;
+                    }
+                }
+                __syncthreads();
+            } else {
+                __syncthreads();   // the long-row path reuses s_val and s_col
+                s = tile_rowsum_long<RP, RC>(rp, col, vals, row0, nr, g, s_val, s_col);
+                stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tstg, n,
+                                                       k0n, k1n, tn < ntiles);
             }
-            __syncthreads();
-        } else {
-            s = tile_rowsum_long<RP, RC>(rp, col, vals, row0, nr, g, s_val, s_col);
-            if (tn < ntiles)
-                stage_tile<RP, CAP, OFF32, SPLIT, C16>(nxt, rp, col, col16, vals, SPLIT ? partner : rin, pprev, x, tile_of(tn), n,
-                                                  k0n, k1n);
         }
         if (tid < nr) {
             if constexpr (SPLIT) {
