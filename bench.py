@@ -545,7 +545,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
             fams[fam] = dict(kernels=names, fetch_kib_total=tf, write_kib_total=tw,
                              bytes_per_run=(tf * kib * sf / runs + tw * kib * sw / runs_w) if runs and runs_w else None)
         cmd = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o p --output-format csv -- "
-               f"python -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
+               f"python3 -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline --no-ceiling "
                "--calibrate-copy; then python bench.py --workload "
                f"{workload} --summarize-pmc <fetch dir> <write dir>")
         out = dict(workload=workload, command=cmd, kernel_source_hash=kernel_source_hash(), unit="run",
@@ -571,7 +571,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
         runs_w = sum(1 for _, name, _ in wr if per[0] in name) / per[1]
         tf, tw = total(fr), total(wr)
         cmd = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o p --output-format csv -- "
-               f"python -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
+               f"python3 -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline --no-ceiling "
                "--calibrate-copy; then python bench.py --workload "
                f"{workload} --summarize-pmc <fetch dir> <write dir>")
         out = dict(workload=workload, command=cmd, kernel_source_hash=kernel_source_hash(), kernels=names,
@@ -595,7 +595,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
         upd_f, _ = pick(fr, ["k_bs_update"])
         upd_w, _ = pick(wr, ["k_bs_update"])
     cmd = ("rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d <dir> -o p --output-format csv -- "
-           f"python -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline "
+           f"python3 -u bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu-baseline --no-ceiling "
            "--calibrate-copy --fixed-iters 12; then python bench.py --workload "
            f"{workload} --summarize-pmc <fetch dir> <write dir>")
     out = dict(workload=workload, command=cmd, kernel_source_hash=kernel_source_hash(),
