@@ -889,14 +889,15 @@ sla_status run_cg(sla_csr* A, const void* row_ptr, const int32_t* col, int cap, 
     }
     // The 16-byte update kernel (k_cg_update_wide) serves every per-system solve whose
     // vectors are 16-byte aligned: one system, or an even n (the caller's b, read as r_0,
-    // must be aligned too).  Systems that stream from HBM give it 3 workgroups per CU:
-    // at 169M rows 684 us per launch against 782 us for the 8-tile kernel on one box
-    // (1024 workgroups: 701 us; 2048: 810 us); at 1M rows the 8-tile grid stays best for
-    // it too (6.6 us against 7.2 us for the 8-tile kernel).
+    // must be aligned too).  Systems that stream from HBM give it exactly 3 workgroups
+    // per CU, whatever the plain SpMV's occupancy: at 169M rows 684 us per launch against
+    // 782 us for the 8-tile kernel on one box (1024 workgroups: 701 us; 2048: 810 us); at
+    // 1M rows the 8-tile grid stays best for it too (6.6 us against 7.2 us for the
+    // 8-tile kernel).
     const bool wide = !list && !(batch >= 8 && batch % 8 == 0) && (batch == 1 || n % 2 == 0) &&
                       (reinterpret_cast<uintptr_t>(b) & 15) == 0;
     const bool streaming = (12 * A->nnz + 52 * n) * batch > kBandStreamBytes;
-    if (wide && streaming && batch == 1) Gu = std::max(Gu, 3 * A->n_cu);
+    if (wide && streaming && batch == 1) Gu = 3 * A->n_cu;
     if (list) G = Gu = list->total_wg;   // one grid and one partial slot per workgroup
     Workspace w;
     sla_status st = ensure_workspace(A, batch, std::max(G, Gu), &w, jacobi ? kMethodJacobi : kMethodCG,
