@@ -807,7 +807,13 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     n, nnz, B = w["n"], w["nnz"], w["batch"]
     method = w["method"]
     bicg = method == "bicgstab"
+    # csr_create (device validation and analysis of the pattern) is timed on its own,
+    # outside the steps
+    torch.cuda.synchronize()
+    tc0 = time.perf_counter()
     h = S.csr_create(w["rp"], w["col"], symmetric=w["symmetric"])
+    torch.cuda.synchronize()
+    create_ms = 1e3 * (time.perf_counter() - tc0)
     an = S.csr_analysis(h)
     if bicg:
         spmv_kernel = "k_cg_spmv (BiCGStab modes: v = A p, t = A s)"
@@ -885,7 +891,7 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
         schedule += "; operand in an LDS window, 16-bit column offsets"
     del x, h
     return dict(w=w, an=an, bicg=bicg, spmv_kernel=spmv_kernel, schedule=schedule, col_bytes=col_bytes, dia_nd=dia_nd,
-                rp_bytes=rp_bytes, rp_stated=rp_stated, steps=steps, warmup=warmup, wall=wall,
+                rp_bytes=rp_bytes, rp_stated=rp_stated, steps=steps, warmup=warmup, wall=wall, create_ms=create_ms,
                 event_ms=e0.elapsed_time(e1) / steps, fwd_it=fwd_it, bwd_it=bwd_it, total_it=total_it, tq=tq)
 
 
@@ -972,6 +978,7 @@ def cg_summary(r, ceiling, args) -> dict:
             "rtol": w["rtol"], "fixed_iterations": w["fixed"],
             "cg_schedule": r["schedule"], "steps": r["steps"], "warmup": r["warmup"],
             "ms_per_step": round(ms_step, 4), "solve_adjoint_ms": round(ms_step, 4),
+            "csr_create_ms": round(r["create_ms"], 3),
             "iterations_per_step": {"forward": r["fwd_it"][-1], "adjoint": r["bwd_it"][-1]},
             "iters_per_s": round(r["total_it"] / r["wall"], 2),
             "hbm_gbps_per_iteration": round(rf["achieved"], 1),
@@ -1005,7 +1012,8 @@ def cg_line(r, args, ceiling, cpu) -> dict:
                    "cg_schedule": r["schedule"], "preconditioner": "jacobi" if args.jacobi else "none",
                    "method": w["method"]},
     }
-    for k in ("iterations_per_step", "solve_adjoint_ms", "hbm_gbps_per_iteration", "hbm_gbps_moved_per_iteration",
+    for k in ("iterations_per_step", "solve_adjoint_ms", "csr_create_ms", "hbm_gbps_per_iteration",
+              "hbm_gbps_moved_per_iteration",
               "event_ms_per_step", "kernels", "bytes_model", "roofline"):
         out[k] = sm[k]
     if ceiling:
