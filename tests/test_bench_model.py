@@ -107,3 +107,30 @@ def test_diagonal_layout_model():
     assert m["cg_update"] == 24 * n
     m9 = bench.bytes_model(1000, 8000, 2, 4, dia_nd=9)
     assert m9["cg_spmv"] == 8 * 9 * 1000 * 2 + 2 * 1000 + 48 * 1000 * 2
+
+
+def test_iteration_roofline_and_resident_ceiling_fields():
+    # the bench line's roofline fields from synthetic kernel timings: the V=9 fraction
+    # over the whole iteration (SpMV + update), the bytes-moved fraction, and the
+    # fraction of same-size streaming probes for a cache-resident workload
+    w = dict(name="poisson1024", desc="synthetic", n=N, nnz=NNZ, batch=1, rtol=1e-8, fixed=False, method="cg")
+    spmv_ms, upd_ms, launches = 0.022, 0.007, 100
+    tq = {"cg_spmv": {"launches": launches, "total_ms": spmv_ms * launches},
+          "cg_update": {"launches": launches, "total_ms": upd_ms * launches},
+          "cg_pupd": {"launches": 0, "total_ms": 0.0}}
+    cr = {"spmv_mix": {"us": 16.0, "gbps": 6500.0}, "triad": {"us": 5.0, "gbps": 5000.0}}
+    r = dict(w=w, tq=tq, bicg=False, an={"split": False}, rp_bytes=4, rp_stated=4, col_bytes=2, dia_nd=0,
+             spmv_kernel="k_cg_spmv", schedule="fused", steps=1, warmup=0, wall=1.0, event_ms=1.0,
+             fwd_it=[1], bwd_it=[1], total_it=2, create_ms=1.0, ceiling_resident=cr)
+    assert bench.cache_resident(w)
+    roof = bench.cg_summary(r, None, None)["roofline"]
+    it_s = spmv_ms * 1e-3 + upd_ms * 1e-3
+    v9 = bench.bytes_model_v9(N, NNZ, 1, 4)
+    moved = bench.bytes_model(N, NNZ, 1, 4, col_bytes=2)["iteration"]
+    assert roof["bytes_per_iteration"] == v9
+    assert abs(roof["frac"] - v9 / it_s / 8e12) < 1e-4
+    assert abs(roof["frac_bytes_moved"] - moved / it_s / 8e12) < 1e-4
+    assert abs(roof["frac_of_resident_ceiling"] - (16.0 + 5.0) / (1e6 * it_s)) < 1e-4
+    assert roof["cache_resident"]
+    # 169M rows do not fit the Infinity Cache
+    assert not bench.cache_resident(dict(w, n=169_000_000, nnz=844_948_000))
