@@ -31,6 +31,7 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -858,13 +859,17 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    infos = []
+    infos, marks = [], []
     for _ in range(steps):
         _, _, _, info, binfo = step()
         infos.append((info, binfo))
+        em = torch.cuda.Event(enable_timing=True)   # per-step marks on the stream, no sync
+        em.record(stream)
+        marks.append(em)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, len(marks))]
     fwd_it = [sum(s["iterations"] for s in S.read_info(i)) for i, _ in infos]
     bwd_it = [sum(s["iterations"] for s in S.read_info(bi)) for _, bi in infos]
     max_fwd = max(s["iterations"] for s in S.read_info(infos[-1][0]))
@@ -892,6 +897,7 @@ def measure_cg(args, w, S, torch, steps: int, warmup: int) -> dict:
     del x, h
     return dict(w=w, an=an, bicg=bicg, spmv_kernel=spmv_kernel, schedule=schedule, col_bytes=col_bytes, dia_nd=dia_nd,
                 rp_bytes=rp_bytes, rp_stated=rp_stated, steps=steps, warmup=warmup, wall=wall, create_ms=create_ms,
+                step_ms=step_ms,
                 event_ms=e0.elapsed_time(e1) / steps, fwd_it=fwd_it, bwd_it=bwd_it, total_it=total_it, tq=tq)
 
 
@@ -979,6 +985,7 @@ def cg_summary(r, ceiling, args) -> dict:
             "cg_schedule": r["schedule"], "steps": r["steps"], "warmup": r["warmup"],
             "ms_per_step": round(ms_step, 4), "solve_adjoint_ms": round(ms_step, 4),
             "csr_create_ms": round(r["create_ms"], 3),
+            "step_ms_median": (round(statistics.median(r["step_ms"]), 4) if r.get("step_ms") else None),
             "iterations_per_step": {"forward": r["fwd_it"][-1], "adjoint": r["bwd_it"][-1]},
             "iters_per_s": round(r["total_it"] / r["wall"], 2),
             "hbm_gbps_per_iteration": round(rf["achieved"], 1),
@@ -1012,7 +1019,7 @@ def cg_line(r, args, ceiling, cpu) -> dict:
                    "cg_schedule": r["schedule"], "preconditioner": "jacobi" if args.jacobi else "none",
                    "method": w["method"]},
     }
-    for k in ("iterations_per_step", "solve_adjoint_ms", "csr_create_ms", "hbm_gbps_per_iteration",
+    for k in ("iterations_per_step", "solve_adjoint_ms", "step_ms_median", "csr_create_ms", "hbm_gbps_per_iteration",
               "hbm_gbps_moved_per_iteration",
               "event_ms_per_step", "kernels", "bytes_model", "roofline"):
         out[k] = sm[k]
