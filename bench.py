@@ -452,12 +452,32 @@ def cpu_baseline(w, iters: int, single_iters: int = 100) -> dict:
     t0 = time.perf_counter()
     r = O.cg_timing(A, b, iters, host["threads"], adjoint=True, vals=vals)
     dt = time.perf_counter() - t0
-    return dict(value=round(2 * iters / dt, 3), unit=unit, cores=r["threads"], kind="oracle",
+    rows = dict(value=round(2 * iters / dt, 3), unit=unit, cores=r["threads"], kind="oracle",
                 mode="timing mode: the oracle's CG steps with OpenMP over rows (and over the inner "
                      "products' slices)",
                 sample=f"oracle {name} on {what}, {iters} fixed iterations + {iters} adjoint iterations "
                        f"on {r['threads']} threads", seconds=round(dt, 2),
                 nproc=host["nproc"], host_model=host["model"], single_thread=single)
+    if w["host"] is None or A.batch == 1:
+        return rows
+    # A batch of systems: the timing mode over systems, one host thread per system (each
+    # runs the oracle's CG steps on one OpenMP thread; the C calls release the GIL), on
+    # as many systems as there are threads; iterations summed over the systems.
+    from concurrent.futures import ThreadPoolExecutor
+    nsys = min(host["threads"], A.batch)
+    bs = w["host"]["b"].reshape(A.batch, A.n_rows)
+    vs = A.vals.reshape(A.batch, A.nnz)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nsys) as ex:
+        list(ex.map(lambda s_: O.cg_timing(A, bs[s_], iters, 1, adjoint=True, vals=vs[s_]), range(nsys)))
+    dt = time.perf_counter() - t0
+    return dict(value=round(2 * iters * nsys / dt, 3), unit=unit + " (summed over systems)", cores=nsys,
+                kind="oracle",
+                mode="timing mode over systems: one thread per system, each the oracle's CG steps on one "
+                     "OpenMP thread",
+                sample=f"oracle {name} on systems 0..{nsys - 1} of this workload, {iters} fixed iterations "
+                       f"+ {iters} adjoint iterations each, {nsys} systems at once", seconds=round(dt, 2),
+                nproc=host["nproc"], host_model=host["model"], rows_parallel=rows, single_thread=single)
 
 
 # ------------------------------------------------------------------------------ traffic
