@@ -243,16 +243,24 @@ def run_lobpcg(args, c, S, torch, dev) -> dict:
 
 
 def cpu_baseline_lobpcg(c, iters: int) -> dict:
-    """The oracle's LOBPCG (one thread) for a bounded number of iterations."""
+    """The oracle's LOBPCG for a bounded number of iterations: with its library calls on
+    every host thread (the value), and on one thread beside it."""
     import oracle.lobpcg as OL
     from threadpoolctl import threadpool_limits
-    t0 = time.perf_counter()
-    with threadpool_limits(1):
-        OL.lobpcg(c["A"], c["k"], c["X0"], which=c["which"], tol=1e-300, max_iter=iters)
-    dt = time.perf_counter() - t0
-    return dict(value=round(iters / dt, 3), unit="LOBPCG iterations/s", cores=1, kind="oracle",
-                sample=f"oracle LOBPCG on this workload, the first {iters} iterations, single thread",
-                seconds=round(dt, 2))
+    host = host_cpu()
+    out = {}
+    for nt in (host["threads"], 1):
+        t0 = time.perf_counter()
+        with threadpool_limits(nt):
+            OL.lobpcg(c["A"], c["k"], c["X0"], which=c["which"], tol=1e-300, max_iter=iters)
+        dt = time.perf_counter() - t0
+        out[nt] = dict(value=round(iters / dt, 3), unit="LOBPCG iterations/s", cores=nt, kind="oracle",
+                       sample=f"oracle LOBPCG on this workload, the first {iters} iterations, its numpy "
+                              f"calls on {nt} thread(s)", seconds=round(dt, 2))
+    r = dict(out[host["threads"]], nproc=host["nproc"], host_model=host["model"])
+    if host["threads"] != 1:
+        r["single_thread"] = out[1]
+    return r
 
 
 def run_list(args, c, S, torch, dev) -> dict:
@@ -299,37 +307,61 @@ def run_list(args, c, S, torch, dev) -> dict:
 
 
 def cpu_baseline_list(c, iters: int) -> dict:
-    """The oracle's CG (one thread) on every item of the list, a fixed number of iterations each."""
+    """The oracle on every item of the list, a fixed number of iterations each.
+
+    The value: the oracle's timing mode over items, one host thread per item at a time
+    (each the CG steps on one OpenMP thread; the C calls release Python's lock), on all
+    host threads.  Beside it, the parity oracle on one thread."""
     import oracle as O
+    from concurrent.futures import ThreadPoolExecutor
+    host = host_cpu()
+    k = len(c["items"])
     t0 = time.perf_counter()
     for A, b in zip(c["items"], c["b"]):
         f = O.cg(A, b, rtol=0.0, max_iter=iters, fixed=True)
         O.solve_backward(A, f["x"], f["x"], symmetric=True, rtol=0.0, max_iter=iters, fixed=True)
+    dt1 = time.perf_counter() - t0
+    single = dict(value=round(2 * iters * k / dt1, 3), unit="CG iters/s (summed over items)", cores=1,
+                  kind="oracle", sample=f"parity mode (sequential oracle) on each of the {k} items, {iters} fixed "
+                                        f"iterations + {iters} adjoint", seconds=round(dt1, 2))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=host["threads"]) as ex:
+        list(ex.map(lambda ab: O.cg_timing(ab[0], ab[1], iters, 1, adjoint=True), zip(c["items"], c["b"])))
     dt = time.perf_counter() - t0
-    k = len(c["items"])
-    return dict(value=round(2 * iters * k / dt, 3), unit="CG iters/s (summed over items)", cores=1, kind="oracle",
-                sample=f"oracle CG on each of the {k} items, {iters} fixed iterations + {iters} adjoint "
-                       f"(single thread)", seconds=round(dt, 2))
+    return dict(value=round(2 * iters * k / dt, 3), unit="CG iters/s (summed over items)", cores=host["threads"],
+                kind="oracle", mode="timing mode over items: one host thread per item, each the oracle's CG steps "
+                                    "on one OpenMP thread",
+                sample=f"oracle CG on each of the {k} items, {iters} fixed iterations + {iters} adjoint, "
+                       f"{host['threads']} items at once", seconds=round(dt, 2), nproc=host["nproc"],
+                host_model=host["model"], single_thread=single)
 
 
 def cpu_baseline_eigsh(w, steps: int) -> dict:
-    """The oracle's Lanczos (one thread) for a bounded number of steps of the same problem."""
+    """The oracle's Lanczos for a bounded number of steps of the same problem: with its
+    library calls on every host thread (the value), and on one thread beside it."""
     import oracle.eigsh as OE
     from threadpoolctl import threadpool_limits
     A = w["host"]["A"]
-    t0 = time.perf_counter()
-    with threadpool_limits(1):
-        if w["max_dim"] and w["max_dim"] < steps:
-            OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=w["max_dim"],
-                     max_iter=steps, keep=w["keep"] or None)
-            how = f"step budget, basis of {w['max_dim']} with thick restart"
-        else:
-            OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=steps)
-            how = "dimension cap"
-    dt = time.perf_counter() - t0
-    return dict(value=round(steps / dt, 3), unit="Lanczos steps/s", cores=1, kind="oracle",
-                sample=f"oracle Lanczos on this workload, the first {steps} steps ({how}), "
-                       f"single thread", seconds=round(dt, 2))
+    host = host_cpu()
+    out = {}
+    for nt in (host["threads"], 1):
+        t0 = time.perf_counter()
+        with threadpool_limits(nt):
+            if w["max_dim"] and w["max_dim"] < steps:
+                OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=w["max_dim"],
+                         max_iter=steps, keep=w["keep"] or None)
+                how = f"step budget, basis of {w['max_dim']} with thick restart"
+            else:
+                OE.eigsh(A, w["k"], w["host"]["v0"], which=w["which"], tol=1e-300, max_dim=steps)
+                how = "dimension cap"
+        dt = time.perf_counter() - t0
+        out[nt] = dict(value=round(steps / dt, 3), unit="Lanczos steps/s", cores=nt, kind="oracle",
+                       sample=f"oracle Lanczos on this workload, the first {steps} steps ({how}), its numpy "
+                              f"calls on {nt} thread(s)", seconds=round(dt, 2))
+    r = dict(out[host["threads"]], nproc=host["nproc"], host_model=host["model"])
+    if host["threads"] != 1:
+        r["single_thread"] = out[1]
+    return r
 
 
 # ------------------------------------------------------------------------------ workloads
