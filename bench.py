@@ -450,7 +450,7 @@ def cpu_baseline(w, iters: int, single_iters: int = 100) -> dict:
     and inner products split over OpenMP threads (orc_cg_timing), `iters` fixed
     iterations forward and `iters` in the adjoint.  Parity mode beside it: the
     single-threaded oracle itself (orc_cg + orc_solve_backward), `single_iters` + `single_iters`.
-    BiCGStab workloads have the parity mode only."""
+    BiCGStab workloads: orc_bicgstab_timing (the adjoint on the transpose), parity mode beside it."""
     import oracle as O
     import workloads as W
 
@@ -478,6 +478,18 @@ def cpu_baseline(w, iters: int, single_iters: int = 100) -> dict:
     single = dict(value=round(2 * si / dt1, 3), unit=unit, cores=1, kind="oracle",
                   sample=f"parity mode (sequential oracle) on {what}, {si} fixed iterations + {si} adjoint",
                   seconds=round(dt1, 2))
+    if method == "bicgstab":
+        # the BiCGStab timing mode: orc_bicgstab's steps over OpenMP threads, the adjoint
+        # on the transpose
+        t0 = time.perf_counter()
+        r = O.bicgstab_timing(A, b, iters, host["threads"], adjoint=True, vals=vals)
+        dt = time.perf_counter() - t0
+        return dict(value=round(2 * iters / dt, 3), unit=unit, cores=r["threads"], kind="oracle",
+                    mode="timing mode: the oracle's BiCGStab steps with OpenMP over rows (and over the inner "
+                         "products' slices), the adjoint on the transpose",
+                    sample=f"oracle {name} on {what}, {iters} fixed iterations + {iters} adjoint iterations "
+                           f"on {r['threads']} threads", seconds=round(dt, 2),
+                    nproc=host["nproc"], host_model=host["model"], single_thread=single)
     if method != "cg" or not w.get("symmetric", True):
         single.update(nproc=host["nproc"], host_model=host["model"])
         return single

@@ -73,6 +73,8 @@ def lib():
         L.orc_solve_backward.restype = i32
         L.orc_cg_timing.argtypes = [i64, P, P, P, P, P, i64, i32, P, P, P, i32]
         L.orc_cg_timing.restype = i32
+        L.orc_bicgstab_timing.argtypes = [i64, P, P, P, P, P, i64, i32, P, P, P, P, P, P, i32]
+        L.orc_bicgstab_timing.restype = i32
         _lib = L
     return _lib
 
@@ -213,4 +215,24 @@ def cg_timing(A, b, iters, threads, adjoint=True, vals=None):
     work = np.empty(4 * max(n, 1), np.float64)
     nt = lib().orc_cg_timing(n, _p(rp), _p(col), _p(v), _p(b), _p(x), int(iters), 1 if adjoint else 0,
                              _p(lam), _p(gv), _p(work), int(threads))
+    return dict(x=x, lam=lam, gvals=gv[:A.nnz], threads=int(nt))
+
+
+def bicgstab_timing(A, b, iters, threads, adjoint=True, vals=None):
+    """The CPU baseline's BiCGStab timing mode (orc_bicgstab_timing): `iters` fixed
+    iterations of orc_bicgstab's steps on `threads` OpenMP threads, then (adjoint) the
+    same on A^T with right-hand side x and the gradient on A's pattern.  Returns
+    dict(x, lam, gvals, threads)."""
+    rp, col = _pattern(A)
+    v = _f64(A.vals if vals is None else vals)
+    b = _f64(b)
+    n = A.n_rows
+    rpt, ct, perm = transpose(A)
+    vt = np.ascontiguousarray(v[perm]) if A.nnz > 0 else np.zeros(1)
+    x = np.empty(n, np.float64)
+    lam = np.empty(n, np.float64)
+    gv = np.empty(max(A.nnz, 1), np.float64)
+    work = np.empty(6 * max(n, 1), np.float64)
+    nt = lib().orc_bicgstab_timing(n, _p(rp), _p(col), _p(v), _p(b), _p(x), int(iters), 1 if adjoint else 0,
+                                   _p(rpt), _p(ct), _p(vt), _p(lam), _p(gv), _p(work), int(threads))
     return dict(x=x, lam=lam, gvals=gv[:A.nnz], threads=int(nt))

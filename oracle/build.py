@@ -17,8 +17,8 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
-    # -fopenmp serves orc_cg_timing (the CPU baseline's timing mode) only; the parity
-    # functions have no OpenMP pragmas and run sequentially
+    # -fopenmp serves orc_cg_timing and orc_bicgstab_timing (the CPU baseline's timing
+    # modes) only; the parity functions have no OpenMP pragmas and run sequentially
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99", "-Wall", "-fopenmp",
            "-shared", "-fPIC", SRC, "-o", tmp, "-lm"]
     subprocess.check_call(cmd)

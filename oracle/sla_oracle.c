@@ -519,6 +519,103 @@ static void cg_fixed_threads(int64_t n, const int64_t* row_ptr, const int32_t* c
     }
 }
 
+/* The same BiCGStab steps as orc_bicgstab (no stop test in fixed mode; the breakdown
+   guards end the run early), split over nt OpenMP threads: rows of the products and
+   of the vector updates, slices of the inner products.  Timing mode only. */
+static void spmv_threads(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val, const double* in,
+                         double* out, int nt)
+{
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            double t = val[e] * in[col[e]];
+            s = s + t;
+        }
+        out[i] = s;
+    }
+}
+
+static void bicgstab_fixed_threads(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
+                                   const double* b, double* x, int64_t iters, double* work, double* part, int nt)
+{
+    double* r = work;
+    double* p = work + n;
+    double* v = work + 2 * n;
+    double* s = work + 3 * n;
+    double* t = work + 4 * n;
+    const double* rh = b;
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; p[i] = b[i]; v[i] = 0.0; }
+    double rho = dot_threads(n, rh, r, part, nt);
+    double alpha = 0.0, omega = 0.0;
+    for (int64_t k = 0; k < iters; ++k) {
+        if (k > 0) {
+            double rho1 = dot_threads(n, rh, r, part, nt);
+            if (rho1 == 0.0 || omega == 0.0) return;
+            double beta = (rho1 / rho) * (alpha / omega);
+#pragma omp parallel for num_threads(nt) schedule(static)
+            for (int64_t i = 0; i < n; ++i) {
+                double tv = omega * v[i];
+                double d = p[i] - tv;
+                double tb = beta * d;
+                p[i] = r[i] + tb;
+            }
+            rho = rho1;
+        }
+        spmv_threads(n, row_ptr, col, val, p, v, nt);
+        double rv = dot_threads(n, rh, v, part, nt);
+        if (!(rv == rv) || rv == 0.0) return;
+        alpha = rho / rv;
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            double tv = alpha * v[i];
+            s[i] = r[i] - tv;
+        }
+        spmv_threads(n, row_ptr, col, val, s, t, nt);
+        double ts = dot_threads(n, t, s, part, nt);
+        double tt = dot_threads(n, t, t, part, nt);
+        if (!(tt == tt) || !(ts == ts) || tt == 0.0) return;
+        omega = ts / tt;
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            double tp = alpha * p[i];
+            double x1 = x[i] + tp;
+            double ts_ = omega * s[i];
+            x[i] = x1 + ts_;
+            double tt_ = omega * t[i];
+            r[i] = s[i] - tt_;
+        }
+    }
+}
+
+/* The CPU baseline's BiCGStab timing mode: iters fixed iterations on A, then (adjoint)
+   the same on A^T (row_ptr_t, col_t, val_t: the transposed pattern and values) with
+   right-hand side x (L = 0.5 |x|^2), and the gradient -lam_i x_j on A's pattern.
+   work holds 6 n doubles. */
+int orc_bicgstab_timing(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val,
+                        const double* b, double* x, int64_t iters, int adjoint, const int64_t* row_ptr_t,
+                        const int32_t* col_t, const double* val_t, double* lam, double* gvals, double* work,
+                        int threads)
+{
+    int nt = threads > 0 ? threads : 1;
+    if (nt > 1024) nt = 1024;
+    double part[1024];
+    bicgstab_fixed_threads(n, row_ptr, col, val, b, x, iters, work, part, nt);
+    if (adjoint) {
+        double* g = work + 5 * n;
+        memcpy(g, x, sizeof(double) * (size_t)n);
+        bicgstab_fixed_threads(n, row_ptr_t, col_t, val_t, g, lam, iters, work, part, nt);
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+                double tg = lam[i] * x[col[e]];
+                gvals[e] = -1.0 * tg;
+            }
+    }
+    return nt;
+}
+
 int orc_cg_timing(int64_t n, const int64_t* row_ptr, const int32_t* col, const double* val, const double* b,
                   double* x, int64_t iters, int adjoint, double* lam, double* gvals, double* work, int threads)
 {

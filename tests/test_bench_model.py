@@ -134,3 +134,22 @@ def test_iteration_roofline_and_resident_ceiling_fields():
     assert roof["cache_resident"]
     # 169M rows do not fit the Infinity Cache
     assert not bench.cache_resident(dict(w, n=169_000_000, nnz=844_948_000))
+
+
+def test_oracle_bicgstab_timing_mode_follows_the_parity_oracle():
+    # the BiCGStab timing mode runs orc_bicgstab's steps over OpenMP threads, its
+    # adjoint on the transpose: on a small nonsymmetric grid the iterates agree with
+    # the sequential oracle to rounding
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    A = W.convdiff5(30, shift=1.0)
+    b = W.rhs_normal(A.n_rows, 0)
+    K = 12
+    r = O.bicgstab_timing(A, b, K, 3)
+    f = O.bicgstab(A, b, rtol=0.0, max_iter=K, fixed=True)
+    bw = O.solve_backward(A, f["x"], f["x"], symmetric=False, rtol=0.0, max_iter=K, fixed=True, method="bicgstab")
+    rel = lambda a, c: np.linalg.norm(a - c) / np.linalg.norm(c)
+    assert r["threads"] == 3
+    assert rel(r["x"], f["x"]) < 1e-12 and rel(r["lam"], bw["lam"]) < 1e-12
+    assert rel(r["gvals"], bw["gvals"]) < 1e-12
